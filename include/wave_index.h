@@ -1,0 +1,153 @@
+/*
+ * wave_index.h -- C ABI of the MI355X (gfx950) wave-index library (libwave_index.so).
+ *
+ * The wave index is the attention-aware vector index of RetroInfer ("RetroInfer: A Vector Storage
+ * Engine for Scalable Long-Context LLM Inference"; technical summaries on gist.science, Spanish
+ * page section 2.A and Arabic page section 2.a).  Each decode query's attention is split into
+ *   - a steady zone: the first `sink` and the last `window` positions, attended exactly;
+ *   - a retrieval zone: the tokens of the top_k clusters of a spherical-k-means index whose
+ *     centroids score highest against the query, attended exactly;
+ *   - an estimation zone: every other non-empty cluster c, approximated from its mean key mu_c,
+ *     its size n_c and its value sum SV_c: numerator += n_c * exp(s_c) * SV_c / n_c,
+ *     denominator += n_c * exp(s_c), with s_c = <q, mu_c> * scale;
+ * and the three partial softmax states are merged with log-sum-exp.  The index is built at
+ * prefill by spherical k-means run separately on consecutive segments of the sequence (Spanish
+ * page section 3, "Clustering Segmentado"; Arabic page section 2.a, last paragraph).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless marked (host).  All device buffers are caller-allocated
+ *     and caller-owned; the library never allocates or frees device memory and keeps no device
+ *     state between calls.
+ *   - Layout is row-major and contiguous, heads-major: [B, H, tokens, d].  Query head h reads KV
+ *     head h / (Hq / Hkv).
+ *   - `stream` is a hipStream_t (0 = the null stream).  Calls enqueue work and return; they never
+ *     synchronise.  Asynchronous faults surface at the caller's next synchronisation.
+ *   - d must be 128.  Element types are fp32 (WI_F32) or bfloat16 (WI_BF16); arithmetic is fp32
+ *     (fast paths) and fp64 (every decision that must be reproducible: k-means assignments and
+ *     sums, top-k ties).
+ *   - Invalid arguments are rejected on the host before anything is enqueued: the call returns a
+ *     negative wi_status, sets the thread-local wi_last_error() string and has no side effect.
+ *   - NaN or Inf inputs are not checked; they propagate to the outputs.
+ */
+#ifndef WAVE_INDEX_H_
+#define WAVE_INDEX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WI_OK = 0,
+  WI_ERR_INVALID_ARG = -1, /* bad shape, null required pointer, inconsistent parameters      */
+  WI_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement (d != 128, ...)     */
+  WI_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_bytes figure   */
+  WI_ERR_HIP = -4          /* a HIP launch or query failed; see wi_last_error()               */
+} wi_status;
+
+typedef enum { WI_F32 = 0, WI_BF16 = 1 } wi_dtype;
+
+/* Parameters of an index build.  The clustered range of each (b, g) is positions
+ * [sink, N - window) (empty when sink + window >= N); it is cut into consecutive segments of
+ * seg_len tokens (the last may be shorter; seg_len = 0 means one segment), and segment s owns
+ * cluster ids [s * clusters_per_seg, (s + 1) * clusters_per_seg).  Segments hold at most 65536
+ * tokens.  iters >= 1 Lloyd iterations (assign, then update) run on every segment. */
+typedef struct {
+  int32_t B, Hkv, N, d;
+  int32_t sink, window;
+  int32_t seg_len;
+  int32_t clusters_per_seg;
+  int32_t iters;
+  int32_t dtype;   /* wi_dtype of K, V and of the stored index */
+  uint64_t seed;   /* seeds the per-segment initialisation     */
+} wi_build_params;
+
+/* The index: every pointer is caller-allocated device memory, sized by wi_index_shapes_for().
+ *   centroids   [B,Hkv,C,d]   dtype  mean key of each cluster (0 for an empty cluster)
+ *   value_sums  [B,Hkv,C,d]   dtype  sum of member values (0 for an empty cluster)
+ *   sizes       [B,Hkv,C]     int32  member count n_c
+ *   offsets     [B,Hkv,C+1]   int32  exclusive prefix sum of sizes: cluster c owns rows
+ *                                    [offsets[c], offsets[c+1]) of k_perm / v_perm
+ *   perm        [B,Hkv,Nc]    int32  absolute token position of each k_perm row
+ *   k_perm      [B,Hkv,Nc,d]  dtype  clustered keys, cluster after cluster, ascending position
+ *   v_perm      [B,Hkv,Nc,d]  dtype  the matching values
+ *   k_steady    [B,Hkv,NS,d]  dtype  keys of the steady zone, ascending position
+ *   v_steady    [B,Hkv,NS,d]  dtype  the matching values
+ * where C = nseg * clusters_per_seg, Nc = clustered tokens, NS = min(N, sink + window).
+ * wi_decode only reads an index, so several streams may decode the same index concurrently. */
+typedef struct {
+  void *centroids, *value_sums;
+  int32_t *sizes, *offsets, *perm;
+  void *k_perm, *v_perm;
+  void *k_steady, *v_steady;
+} wi_index_view;
+
+/* Sizes (in elements, except build_workspace_bytes) of every index buffer. */
+typedef struct {
+  int64_t C, Nc, n_steady, nseg;
+  int64_t centroids, value_sums, sizes, offsets, perm, k_perm, v_perm, k_steady, v_steady;
+  int64_t build_workspace_bytes;
+} wi_index_shapes;
+
+/* Parameters of one batched GQA decode step over an index built with matching B, Hkv, d and
+ * dtype.  n_steady, C and Nc are the figures wi_index_shapes_for() returned.  top_k >= 0 clusters
+ * are retrieved per query head (clamped to the head's number of non-empty clusters).  scale
+ * multiplies every logit (1/sqrt(d) for standard attention). */
+typedef struct {
+  int32_t B, Hq, Hkv, d;
+  int32_t n_steady, C, Nc;
+  int32_t top_k;
+  float scale;
+  int32_t dtype;
+} wi_decode_params;
+
+/* (host) Fill *out with the buffer sizes of an index for *p.  Host only; enqueues nothing.
+ * Errors: WI_ERR_INVALID_ARG for null pointers or out-of-range fields, WI_ERR_UNSUPPORTED for
+ * d != 128, a segment longer than 65536 tokens, more than 4096 clusters per segment or more
+ * than 2^31 rows in one index buffer. */
+wi_status wi_index_shapes_for(const wi_build_params *p, wi_index_shapes *out);
+
+/* Build the wave index of K, V ([B,Hkv,N,d], dtype) into *out (segmented spherical k-means;
+ * RetroInfer Spanish summary section 3 and Arabic summary section 2.a).
+ * Per segment: initial centroid directions are unit-normalised key rows chosen by a partial
+ * Fisher-Yates shuffle driven by SplitMix64 (Steele, Lea, Flood, OOPSLA 2014) seeded from
+ * (seed, b, g, s); then `iters` times: assign every key to the centroid direction of highest
+ * inner product (ties to the lower id; decided in fp64), and replace every non-empty cluster's
+ * direction by its normalised fp64 member sum (kept when the cluster is empty).  The last
+ * assignment defines sizes, offsets, perm, the copies, centroids (mean key) and value sums.
+ * The result is a deterministic function of (K, V, parameters).  `workspace` must hold
+ * build_workspace_bytes (256-byte aligned).  K and V may be freed once the build completes. */
+wi_status wi_build_index(const wi_build_params *p, const void *k, const void *v,
+                         const wi_index_view *out, void *workspace, size_t ws_bytes,
+                         void *stream);
+
+/* (host) Workspace bytes wi_decode needs for *p.  Host only. */
+wi_status wi_decode_workspace_bytes(const wi_decode_params *p, size_t *bytes);
+
+/* One decode step for every (b, query head) (RetroInfer Spanish summary section 2.A items 1-3,
+ * Arabic summary section 2.a):
+ *   q        [B,Hq,d]      dtype  the queries
+ *   out      [B,Hq,d]      fp32   attention output
+ *   lse      [B,Hq]        fp32   log-sum-exp of the merged softmax state (nullable)
+ *   sel_ids  [B,Hq,top_k]  int32  retrieved cluster ids in ascending order, -1 padded (nullable)
+ * The retrieval zone of a head is the min(top_k, #non-empty) non-empty clusters that come first
+ * in the order (-sigma_c, c), sigma_c = <q, mu_c> with exact products summed in fp64 in ascending
+ * coordinate order: higher score first, lower id on equal scores.  `workspace` must hold
+ * wi_decode_workspace_bytes (256-byte aligned); calls that share a workspace must not overlap. */
+wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const void *q,
+                    float *out, float *lse, int32_t *sel_ids, void *workspace, size_t ws_bytes,
+                    void *stream);
+
+/* (host) Static description of a status code. */
+const char *wi_status_string(wi_status s);
+
+/* (host) Detail of the last error raised on the calling thread ("" if none). */
+const char *wi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVE_INDEX_H_ */

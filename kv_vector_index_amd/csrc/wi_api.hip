@@ -1,0 +1,254 @@
+// C ABI of the wave-index library: host-side validation, buffer sizing, workspace carving and
+// launch order.  No device memory is allocated here; every buffer comes from the caller.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "wave_index.h"
+#include "wi_device.h"
+#include "wi_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wi_status fail(wi_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool sync_debug() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("WI_SYNC_DEBUG");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+wi_status check_hip(hipError_t e, const char* what, hipStream_t s) {
+  if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(WI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return WI_OK;
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;   // rows (of d elements) per buffer
+
+struct Derived {
+  int64_t NS, Nc, lo, L, nseg, C;
+};
+
+wi_status derive_build(const wi_build_params* p, Derived* d) {
+  if (!p) return fail(WI_ERR_INVALID_ARG, "params is null");
+  if (p->B < 1 || p->Hkv < 1 || p->N < 1)
+    return fail(WI_ERR_INVALID_ARG, "B, Hkv and N must be >= 1 (got %d, %d, %d)", p->B, p->Hkv, p->N);
+  if (p->d != wi::kD) return fail(WI_ERR_UNSUPPORTED, "head dim %d unsupported (only 128)", p->d);
+  if (p->sink < 0 || p->window < 0 || p->seg_len < 0)
+    return fail(WI_ERR_INVALID_ARG, "sink, window and seg_len must be >= 0");
+  if (p->clusters_per_seg < 1) return fail(WI_ERR_INVALID_ARG, "clusters_per_seg must be >= 1");
+  if (p->clusters_per_seg > wi::kMaxClustersPerSeg)
+    return fail(WI_ERR_UNSUPPORTED, "clusters_per_seg %d > %d", p->clusters_per_seg, wi::kMaxClustersPerSeg);
+  if (p->iters < 1) return fail(WI_ERR_INVALID_ARG, "iters must be >= 1");
+  if (p->dtype != WI_F32 && p->dtype != WI_BF16) return fail(WI_ERR_INVALID_ARG, "bad dtype %d", p->dtype);
+  const int64_t N = p->N;
+  d->NS = std::min<int64_t>(N, (int64_t)p->sink + p->window);
+  if ((int64_t)p->sink + p->window >= N) { d->Nc = 0; d->lo = N; }
+  else { d->Nc = N - p->sink - p->window; d->lo = p->sink; }
+  d->L = (p->seg_len == 0) ? d->Nc : p->seg_len;
+  if (d->L > wi::kMaxSegLen)
+    return fail(WI_ERR_UNSUPPORTED, "segment length %lld > %d", (long long)d->L, wi::kMaxSegLen);
+  d->nseg = d->Nc > 0 ? wi::ceil_div(d->Nc, d->L) : 0;
+  d->C = d->nseg * p->clusters_per_seg;
+  const int64_t BG = (int64_t)p->B * p->Hkv;
+  if (BG * N >= kMaxRows || BG * (d->C + 1) >= kMaxRows)
+    return fail(WI_ERR_UNSUPPORTED, "an index buffer would exceed 2^31 rows");
+  return WI_OK;
+}
+
+}  // namespace
+
+namespace wi {
+
+BuildLayout build_layout(const wi_build_params& p) {
+  BuildLayout L{};
+  Derived d{};
+  derive_build(&p, &d);
+  L.C = d.C; L.Nc = d.Nc; L.NS = d.NS; L.nseg = d.nseg; L.L = d.L;
+  const int64_t BG = (int64_t)p.B * p.Hkv;
+  const size_t e = p.dtype == WI_BF16 ? 2 : 4;
+  size_t o = 0;
+  L.off_mhat = o;      o = align256(o + (size_t)BG * d.C * kD * e);
+  L.off_assign = o;    o = align256(o + (size_t)BG * d.Nc * 4);
+  L.off_knorm = o;     o = align256(o + (size_t)BG * d.Nc * 4);
+  L.off_flag_cnt = o;  o = align256(o + (size_t)p.iters * 4);
+  L.off_flag_list = o; o = align256(o + (size_t)BG * d.Nc * 4);
+  L.total = o;
+  return L;
+}
+
+DecodeLayout decode_layout(const wi_decode_params& p) {
+  DecodeLayout L{};
+  L.BG = p.B * p.Hkv;
+  L.BH = p.B * p.Hq;
+  L.G = p.Hq / p.Hkv;
+  L.W32 = (int)ceil_div(p.C, 32);
+  L.Umax = (int)std::min<int64_t>(p.C, (int64_t)L.G * p.top_k);
+  L.max_chunks_g = (int)ceil_div((int64_t)p.n_steady + p.Nc, kChunkTokens);
+  L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
+  L.n_est = L.BG * L.est_tiles_g;
+  L.max_chunks = L.BG * L.max_chunks_g;
+  L.n_counters = 2 * L.BG + 2;
+  const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G;
+  const size_t items = (size_t)L.n_est + (size_t)L.max_chunks;
+  size_t o = 0;
+  L.off_counters = o; o = align256(o + (size_t)L.n_counters * 4);
+  L.off_scores = o;   o = align256(o + BH * C * 4);
+  L.off_mu_norm = o;  o = align256(o + BG * C * 4);
+  L.off_keys32 = o;   o = align256(o + BH * C * 4);
+  L.off_sel_bits = o; o = align256(o + BH * L.W32 * 4);
+  L.off_band_ids = o; o = align256(o + BH * C * 4);
+  L.off_band_key = o; o = align256(o + BH * C * 8);
+  L.off_wl_row0 = o;  o = align256(o + BG * L.Umax * 4);
+  L.off_wl_mask = o;  o = align256(o + BG * L.Umax * 4);
+  L.off_wl_pre = o;   o = align256(o + BG * (L.Umax + 1) * 4);
+  L.off_grp = o;      o = align256(o + BG * 4 * 4);
+  L.off_chunk_e0 = o; o = align256(o + BG * L.max_chunks_g * 4);
+  L.off_part_md = o;  o = align256(o + items * G * 2 * 4);
+  L.off_part_num = o; o = align256(o + items * G * kD * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace wi
+
+extern "C" {
+
+wi_status wi_index_shapes_for(const wi_build_params* p, wi_index_shapes* out) {
+  if (!out) return fail(WI_ERR_INVALID_ARG, "out is null");
+  Derived d{};
+  wi_status s = derive_build(p, &d);
+  if (s != WI_OK) return s;
+  const int64_t BG = (int64_t)p->B * p->Hkv;
+  out->C = d.C;
+  out->Nc = d.Nc;
+  out->n_steady = d.NS;
+  out->nseg = d.nseg;
+  out->centroids = BG * d.C * wi::kD;
+  out->value_sums = BG * d.C * wi::kD;
+  out->sizes = BG * d.C;
+  out->offsets = BG * (d.C + 1);
+  out->perm = BG * d.Nc;
+  out->k_perm = BG * d.Nc * wi::kD;
+  out->v_perm = BG * d.Nc * wi::kD;
+  out->k_steady = BG * d.NS * wi::kD;
+  out->v_steady = BG * d.NS * wi::kD;
+  out->build_workspace_bytes = (int64_t)wi::build_layout(*p).total;
+  return WI_OK;
+}
+
+wi_status wi_build_index(const wi_build_params* p, const void* k, const void* v,
+                         const wi_index_view* out, void* workspace, size_t ws_bytes, void* stream) {
+  Derived d{};
+  wi_status s = derive_build(p, &d);
+  if (s != WI_OK) return s;
+  if (!k || !v) return fail(WI_ERR_INVALID_ARG, "k and v must be non-null");
+  if (!out) return fail(WI_ERR_INVALID_ARG, "index view is null");
+  if (!out->offsets || (d.NS > 0 && (!out->k_steady || !out->v_steady)))
+    return fail(WI_ERR_INVALID_ARG, "index view has a null offsets or steady-zone pointer");
+  if (d.Nc > 0 && (!out->centroids || !out->value_sums || !out->sizes || !out->perm ||
+                   !out->k_perm || !out->v_perm))
+    return fail(WI_ERR_INVALID_ARG, "index view has a null pointer");
+  const wi::BuildLayout L = wi::build_layout(*p);
+  if (L.total > 0 && (!workspace || ws_bytes < L.total))
+    return fail(WI_ERR_WORKSPACE, "build workspace of %zu bytes given, %zu needed", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(WI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return check_hip(wi::launch_build(*p, L, k, v, *out, workspace, st), "wi_build_index launch", st);
+}
+
+wi_status wi_decode_workspace_bytes(const wi_decode_params* p, size_t* bytes) {
+  if (!p || !bytes) return fail(WI_ERR_INVALID_ARG, "null argument");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
+    return fail(WI_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and Hkv dividing Hq");
+  if (p->C < 0 || p->Nc < 0 || p->n_steady < 0 || p->top_k < 0)
+    return fail(WI_ERR_INVALID_ARG, "negative C, Nc, n_steady or top_k");
+  *bytes = wi::decode_layout(*p).total;
+  return WI_OK;
+}
+
+wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
+                    float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream) {
+  if (!p || !idx || !q || !out) return fail(WI_ERR_INVALID_ARG, "params, index, q and out must be non-null");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
+    return fail(WI_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and Hkv dividing Hq");
+  if (p->d != wi::kD) return fail(WI_ERR_UNSUPPORTED, "head dim %d unsupported (only 128)", p->d);
+  if (p->dtype != WI_F32 && p->dtype != WI_BF16) return fail(WI_ERR_INVALID_ARG, "bad dtype %d", p->dtype);
+  const int G = p->Hq / p->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(WI_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+  if ((int64_t)p->B * p->Hkv > wi::kMaxGroupsPerDecode)
+    return fail(WI_ERR_UNSUPPORTED, "B * Hkv = %lld > %d", (long long)p->B * p->Hkv, wi::kMaxGroupsPerDecode);
+  if (p->C < 0 || p->Nc < 0 || p->n_steady < 0 || p->top_k < 0)
+    return fail(WI_ERR_INVALID_ARG, "negative C, Nc, n_steady or top_k");
+  if ((int64_t)p->n_steady + p->Nc < 1) return fail(WI_ERR_INVALID_ARG, "empty context");
+  if ((p->C == 0) != (p->Nc == 0)) return fail(WI_ERR_INVALID_ARG, "C and Nc must be both zero or both positive");
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(WI_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const int64_t BG = (int64_t)p->B * p->Hkv;
+  if (BG * ((int64_t)p->Nc + p->n_steady) >= kMaxRows || (int64_t)p->B * p->Hq * ((int64_t)p->C + 1) >= kMaxRows)
+    return fail(WI_ERR_UNSUPPORTED, "a buffer would exceed 2^31 rows");
+  if (!idx->offsets || (p->n_steady > 0 && (!idx->k_steady || !idx->v_steady)))
+    return fail(WI_ERR_INVALID_ARG, "index view has a null offsets or steady-zone pointer");
+  if (p->C > 0 && (!idx->centroids || !idx->value_sums || !idx->k_perm || !idx->v_perm))
+    return fail(WI_ERR_INVALID_ARG, "index view has a null pointer");
+  if (sel_ids && p->top_k == 0) sel_ids = nullptr;
+  const wi::DecodeLayout L = wi::decode_layout(*p);
+  if (!workspace || ws_bytes < L.total)
+    return fail(WI_ERR_WORKSPACE, "decode workspace of %zu bytes given, %zu needed", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(WI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  wi::DecodeArgs a{};
+  a.mu = idx->centroids; a.sv = idx->value_sums; a.offsets = idx->offsets;
+  a.k_perm = idx->k_perm; a.v_perm = idx->v_perm; a.k_steady = idx->k_steady; a.v_steady = idx->v_steady;
+  a.q = q; a.out = out; a.lse = lse; a.sel_ids = sel_ids;
+  char* base = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(base + L.off_counters);
+  a.scores = reinterpret_cast<float*>(base + L.off_scores);
+  a.mu_norm = reinterpret_cast<float*>(base + L.off_mu_norm);
+  a.keys32 = reinterpret_cast<uint32_t*>(base + L.off_keys32);
+  a.sel_bits = reinterpret_cast<uint32_t*>(base + L.off_sel_bits);
+  a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
+  a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
+  a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
+  a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
+  a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
+  a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
+  a.chunk_e0 = reinterpret_cast<int32_t*>(base + L.off_chunk_e0);
+  a.part_md = reinterpret_cast<float*>(base + L.off_part_md);
+  a.part_num = reinterpret_cast<float*>(base + L.off_part_num);
+  a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
+  a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.max_chunks_g = L.max_chunks_g;
+  a.est_tiles_g = L.est_tiles_g; a.n_est = L.n_est; a.n_counters = L.n_counters; a.scale = p->scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);
+}
+
+const char* wi_status_string(wi_status s) {
+  switch (s) {
+    case WI_OK: return "ok";
+    case WI_ERR_INVALID_ARG: return "invalid argument";
+    case WI_ERR_UNSUPPORTED: return "unsupported configuration";
+    case WI_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case WI_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* wi_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,695 @@
+// Wave-index decode step on gfx950: score -> select -> exact attention + estimation -> LSE merge.
+//
+// Method: RetroInfer's tripartite attention (technical summary, gist.science Spanish page,
+// section 2.A items 1-3; Arabic page section 2.a).  Per query head, the steady zone (sinks and
+// local window) and the retrieval zone (all tokens of the top_k clusters by <q, mu_c>) are
+// attended exactly; every other non-empty cluster contributes n_c * exp(s_c) to the softmax
+// denominator and n_c * exp(s_c) * SV_c / n_c to the numerator; the partial softmax states are
+// merged with log-sum-exp.
+//
+// Kernels (one stream, in order):
+//   k_score   grid (ceil(C/128), B*Hkv): MFMA product of the group's query heads with 128
+//             centroids per block; writes fp32 scores and fp32 centroid norms.  One pass over mu
+//             per KV head serves all of its query heads.
+//   k_select  grid (B*Hq): exact top-k per head.  Radix select over the fp32 scores finds the
+//             k-th value; every cluster whose fp32 score lies within the certified error band of
+//             it is re-scored with the canonical fp64 sum, and the set is completed by
+//             (-sigma, id).  The last head of a KV group to finish builds the group's union work
+//             list (cluster rows with a per-head mask, token prefix sums, chunk starts); the last
+//             group sets the global chunk numbering.
+//   k_attend  persistent grid: work items are estimation tiles (128 clusters) and exact-attention
+//             chunks (128 tokens of steady + retrieved rows, loaded once per KV group and shared
+//             by its query heads).  Each item writes one partial softmax state per head; the last
+//             item of a KV group merges that group's partials into out and lse.
+#include "wi_device.h"
+#include "wi_internal.h"
+
+namespace wi {
+
+// ============================================================================ k_score
+template <typename T>
+__global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
+  const int bg = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int G = a.G, C = a.C;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0u;
+  if (C == 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int cbase = blockIdx.x * 128 + w * 32;
+  const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
+  const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+
+  if constexpr (sizeof(T) == 2) {
+    // A = query heads (row = lane&15), B = centroids (column = lane&15).  Along k, lane group lg
+    // owns dims [32*lg, 32*lg+32); MFMA step s consumes dims 32*lg + 8s .. +8 on both operands.
+    bf16x8_t qa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * lg + 8 * s);
+      else qa[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = cbase + 16 * t + lr;
+      bf16x8_t mb[4];
+      if (c < C) {
+        const T* row = mu + (size_t)c * kD + 32 * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mb[s] = *reinterpret_cast<const bf16x8_t*>(row + 8 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mb[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], mb[s], acc, 0, 0, 0);
+      float n2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float x = (float)mb[s][e]; n2 += x * x; }
+      n2 += __shfl_xor(n2, 16);
+      n2 += __shfl_xor(n2, 32);
+      if (c < C) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * lg + r;
+          if (h < G) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+        }
+        if (lg == 0) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
+      }
+    }
+  } else {
+    // fp32: 16x16x4 MFMA, 32 steps; step s consumes dim 32*lg + s on both operands.
+    float qa[32];
+#pragma unroll
+    for (int s = 0; s < 32; s += 8) {
+      float tmp[8];
+      if (lr < G) St<float>::load8(reinterpret_cast<const float*>(qg) + (size_t)lr * kD + 32 * lg + s, tmp);
+      else for (int e = 0; e < 8; ++e) tmp[e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qa[s + e] = tmp[e];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = cbase + 16 * t + lr;
+      float mb[32];
+      if (c < C) {
+        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 32 * lg;
+#pragma unroll
+        for (int s = 0; s < 32; s += 8) {
+          float tmp[8];
+          St<float>::load8(row + s, tmp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mb[s + e] = tmp[e];
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 32; ++s) mb[s] = 0.f;
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], mb[s], acc, 0, 0, 0);
+      float n2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < 32; ++s) n2 += mb[s] * mb[s];
+      n2 += __shfl_xor(n2, 16);
+      n2 += __shfl_xor(n2, 32);
+      if (c < C) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * lg + r;
+          if (h < G) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+        }
+        if (lg == 0) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
+      }
+    }
+  }
+}
+
+// ============================================================================ k_select
+constexpr int kSelThreads = 512;
+
+// Threshold key of the k-th largest of n keys (1 <= k <= n): after the call, exactly
+// k - *rem_out keys are strictly greater than the returned key and at least *rem_out are equal.
+template <typename K, typename Get>
+__device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, K* shk, int* shi,
+                                int* rem_out) {
+  K prefix = 0, mask = 0;
+  int rem = k;
+  for (int shift = (int)sizeof(K) * 8 - 8; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const K key = get(i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cum = 0, sel = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        const int hb = (int)hist[bin];
+        if (cum + hb >= rem) { sel = bin; break; }
+        cum += hb;
+      }
+      shk[0] = prefix | ((K)sel << shift);
+      shi[0] = rem - cum;
+    }
+    __syncthreads();
+    prefix = shk[0];
+    rem = shi[0];
+    mask |= (K)255 << shift;
+    __syncthreads();
+  }
+  *rem_out = rem;
+  return prefix;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
+  extern __shared__ uint32_t dyn[];           // selected-cluster bitmap [W32] (+ keys if cached)
+  __shared__ uint32_t hist[256];
+  __shared__ int iscr[32];
+  __shared__ float fscr[32];
+  __shared__ uint64_t shk64[2];
+  __shared__ uint32_t shk32[2];
+  __shared__ double qd[kD];
+
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int G = a.G, g = h / G, bg = b * a.Hkv + g;
+  const int C = a.C, W32 = a.W32;
+  uint32_t* bits = dyn;
+  const bool keys_in_lds = (size_t)C * 4 + (size_t)W32 * 4 <= 65536;
+  uint32_t* keys = keys_in_lds ? dyn + W32 : a.keys32 + (size_t)bh * C;
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const float* sc = a.scores + (size_t)bh * C;
+  const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
+  const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
+
+  // query norm (fp32) and the fp64 copy used for canonical rescoring
+  float qv = 0.f;
+  if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
+  const float qn = sqrtf(block_sum(qv * qv, fscr));
+
+  for (int w = tid; w < W32; w += NT) bits[w] = 0u;
+  // order keys (0 = empty cluster), non-empty count, largest centroid norm
+  int cnt = 0;
+  float mxn = 0.f;
+  for (int c = tid; c < C; c += NT) {
+    const int sz = off[c + 1] - off[c];
+    uint32_t key = 0u;
+    if (sz > 0) {
+      ++cnt;
+      mxn = fmaxf(mxn, a.mu_norm[(size_t)bg * C + c]);
+      key = f32_order_key(sc[c]);
+    }
+    keys[c] = key;
+  }
+  const int n_ne = block_isum(cnt, iscr);
+  mxn = block_max(mxn, fscr);
+  const int k_eff = min(a.top_k, n_ne);
+  __syncthreads();
+
+  if (k_eff > 0 && k_eff == n_ne) {
+    for (int c = tid; c < C; c += NT)
+      if (keys[c] != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31));
+  } else if (k_eff > 0) {
+    int rem;
+    const uint32_t thr = block_radix_select<uint32_t>(
+        C, k_eff, [&](int i) { return keys[i]; }, hist, shk32, iscr, &rem);
+    // Certified band: |fp32 score - canonical fp64 score| <= delta for every cluster
+    // (fp32 accumulation of d exact-or-rounded products, times 2 for an unspecified MFMA order).
+    const double that = (double)f32_from_order_key(thr);
+    const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qn * (1.0 + 1.0 / 1024) *
+                             (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
+    const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
+    // classify in id order: each thread owns a contiguous id range
+    const int per = (C + NT - 1) / NT;
+    const int c0 = min(C, tid * per), c1 = min(C, c0 + per);
+    int nb = 0, nin = 0;
+    for (int c = c0; c < c1; ++c) {
+      if (keys[c] == 0u) continue;
+      const double v = (double)sc[c];
+      if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
+      else if (v >= lo) ++nb;
+    }
+    int n_band;
+    int pos = block_exclusive_scan(nb, iscr, &n_band);
+    const int n_in = block_isum(nin, iscr);
+    const int need = k_eff - n_in;
+    int32_t* band = a.band_ids + (size_t)bh * C;
+    for (int c = c0; c < c1; ++c) {
+      if (keys[c] == 0u) continue;
+      const double v = (double)sc[c];
+      if (!(v > hi) && v >= lo) band[pos++] = c;
+    }
+    __syncthreads();
+    if (need >= n_band) {
+      for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+    } else if (need > 0) {
+      uint64_t* bkey = a.band_key + (size_t)bh * C;
+      for (int i = tid; i < n_band; i += NT) {
+        const int c = band[i];
+        // canonical score: exact products summed in fp64, ascending coordinate order
+        double acc = 0.0;
+        {
+#pragma clang fp contract(off)
+          const T* row = mu + (size_t)c * kD;
+          for (int j = 0; j < kD; ++j) {
+            const double p = qd[j] * (double)St<T>::f(row[j]);
+            acc = acc + p;
+          }
+        }
+        bkey[i] = f64_order_key(acc);
+      }
+      __syncthreads();
+      int rem2;
+      const uint64_t t64 = block_radix_select<uint64_t>(
+          n_band, need, [&](int i) { return bkey[i]; }, hist, shk64, iscr, &rem2);
+      // keys above the threshold are in; among keys equal to it the lowest ids (band order) fill
+      const int per2 = (n_band + NT - 1) / NT;
+      const int i0 = min(n_band, tid * per2), i1 = min(n_band, i0 + per2);
+      int neq = 0;
+      for (int i = i0; i < i1; ++i) neq += (bkey[i] == t64);
+      int tot_eq;
+      int r = block_exclusive_scan(neq, iscr, &tot_eq);
+      for (int i = i0; i < i1; ++i) {
+        const uint64_t kk = bkey[i];
+        bool take = kk > t64;
+        if (kk == t64) { take = r < rem2; ++r; }
+        if (take) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+      }
+    }
+  }
+  __syncthreads();
+
+  // publish the bitmap; ascending ids to sel_ids
+  uint32_t* gbits = a.sel_bits + (size_t)bh * W32;
+  for (int w = tid; w < W32; w += NT) gbits[w] = bits[w];
+  if (a.sel_ids) {
+    const int perw = (W32 + NT - 1) / NT;
+    const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+    int n = 0;
+    for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
+    int tot;
+    int p = block_exclusive_scan(n, iscr, &tot);
+    int32_t* out = a.sel_ids + (size_t)bh * a.top_k;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t m = bits[w];
+      while (m) { const int bit = __ffs(m) - 1; m &= m - 1; if (p < a.top_k) out[p] = w * 32 + bit; ++p; }
+    }
+    for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
+  }
+
+  // ---- the last query head of the KV group to arrive builds the group's work list
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) iscr[20] = (atomicAdd(&a.counters[bg], 1u) == (uint32_t)(G - 1));
+  __syncthreads();
+  if (!iscr[20]) return;
+  __threadfence();
+
+  const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
+  const int perw = (W32 + NT - 1) / NT;
+  const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+  int ne = 0, nt = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t u = 0u;
+    for (int j = 0; j < G; ++j) u |= __builtin_nontemporal_load(hb + (size_t)j * W32 + w);
+    ne += __popc(u);
+    while (u) { const int bit = __ffs(u) - 1; u &= u - 1; const int c = w * 32 + bit; nt += off[c + 1] - off[c]; }
+  }
+  int n_entries, n_utok;
+  int e = block_exclusive_scan(ne, iscr, &n_entries);
+  int t = block_exclusive_scan(nt, iscr, &n_utok);
+  const int NS = a.NS;
+  const int n_tok = NS + n_utok;
+  int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
+  int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
+  int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
+  int32_t* ce0 = a.chunk_e0 + (size_t)bg * a.max_chunks_g;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t hw[kMaxGroup];
+    uint32_t u = 0u;
+    for (int j = 0; j < G; ++j) { hw[j] = __builtin_nontemporal_load(hb + (size_t)j * W32 + w); u |= hw[j]; }
+    while (u) {
+      const int bit = __ffs(u) - 1;
+      u &= u - 1;
+      const int c = w * 32 + bit;
+      int m = 0;
+      for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
+      const int r0 = off[c], sz = off[c + 1] - r0;
+      const int start = NS + t;
+      row0[e] = r0;
+      msk[e] = m;
+      pre[e] = start;
+      // chunks whose first token falls inside this cluster's token range start at entry e
+      for (int j = (start + kChunkTokens - 1) / kChunkTokens; j * kChunkTokens < start + sz; ++j) ce0[j] = e;
+      ++e;
+      t += sz;
+    }
+  }
+  if (tid == 0) {
+    pre[n_entries] = n_tok;
+    // chunks that start inside the steady zone begin with entry 0
+    for (int j = 0; j * kChunkTokens < min(NS, n_tok); ++j) ce0[j] = 0;
+    const int n_chunks = (n_tok + kChunkTokens - 1) / kChunkTokens;
+    int32_t* gd = a.grp + (size_t)bg * 4;
+    gd[0] = n_entries;
+    gd[1] = n_tok;
+    gd[2] = n_chunks;
+  }
+  // ---- the last group to arrive numbers every group's chunks
+  __threadfence();
+  __syncthreads();
+  const int BG = a.B * a.Hkv;
+  if (tid == 0) iscr[21] = (atomicAdd(&a.counters[2 * BG], 1u) == (uint32_t)(BG - 1));
+  __syncthreads();
+  if (!iscr[21]) return;
+  __threadfence();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < BG; ++i) {
+      int32_t* gd = a.grp + (size_t)i * 4;
+      const int nc = __builtin_nontemporal_load(gd + 2);
+      gd[3] = run;
+      run += nc;
+    }
+    a.counters[2 * BG + 1] = (uint32_t)run;
+  }
+}
+
+// ============================================================================ k_attend
+constexpr int kAttThreads = 256;
+
+// Rows of a work item: wave w owns rows w*32 + 4*i + (lane>>4), i = 0..7; lane&15 owns dims
+// [8*(lane&15), +8).  Given per-row logits (identical across the 16 lanes of a row) and the row
+// values, form the item's partial softmax state per head and write it to `slot`.
+template <int G>
+__device__ __forceinline__ void finish_partial(const float (&l)[8][G], const float (&v)[8][8],
+                                               const float (&wden)[8], int slot, const DecodeArgs& a,
+                                               float* sh_m, float* sh_num, float* sh_den) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15;
+  float M[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = l[0][h];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, l[i][h]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane == 0) sh_m[w * G + h] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = sh_m[h];
+    for (int ww = 1; ww < kAttThreads / 64; ++ww) m = fmaxf(m, sh_m[ww * G + h]);
+    M[h] = m;
+  }
+  float den[G], num[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    den[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = (l[i][h] == -INFINITY) ? 0.f : __expf(l[i][h] - M[h]);
+      den[h] += wden[i] * p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[h][e] += p * v[i][e];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    den[h] += __shfl_xor(den[h], 16);
+    den[h] += __shfl_xor(den[h], 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      num[h][e] += __shfl_xor(num[h][e], 16);
+      num[h][e] += __shfl_xor(num[h][e], 32);
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh_num[(w * G + h) * kD + 8 * lr + e] = num[h][e];
+      if (lr == 0) sh_den[w * G + h] = den[h];
+    }
+  }
+  __syncthreads();
+  float* pn = a.part_num + (size_t)slot * G * kD;
+  for (int i = threadIdx.x; i < G * kD; i += kAttThreads) {
+    float s = 0.f;
+    for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_num[ww * G * kD + i];
+    pn[i] = s;
+  }
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    float s = 0.f;
+    for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_den[ww * G + hh];
+    a.part_md[((size_t)slot * G + hh) * 2 + 0] = M[hh];
+    a.part_md[((size_t)slot * G + hh) * 2 + 1] = s;
+  }
+  __syncthreads();
+}
+
+template <typename T, int G>
+__device__ void est_tile(const DecodeArgs& a, int bg, int tile, int slot, float* sh_m,
+                         float* sh_num, float* sh_den) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv, C = a.C;
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * C * kD;
+  const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
+  float l[8][G], v[8][8], wden[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tile * kEstTile + w * 32 + 4 * i + rg;
+    bool live = c < C;
+    int sz = 0;
+    if (live) { sz = off[c + 1] - off[c]; live = sz > 0; }
+    wden[i] = (float)sz;
+    if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
+    else for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x = -INFINITY;
+      if (live) {
+        const uint32_t sel = a.sel_bits[(hbase + h) * a.W32 + (c >> 5)];
+        if (!((sel >> (c & 31)) & 1u)) x = a.scores[(hbase + h) * C + c] * a.scale;
+      }
+      l[i][h] = x;
+    }
+  }
+  finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
+}
+
+template <typename T, int G>
+__device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int slot, float* sh_m,
+                             float* sh_num, float* sh_den, int* sh_row, int* sh_mask) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int NS = a.NS;
+  const int32_t* gd = a.grp + (size_t)bg * 4;
+  const int n_entries = gd[0], n_tok = gd[1];
+  const int t0 = jl * kChunkTokens;
+  const int t1 = min(n_tok, t0 + kChunkTokens);
+  const int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
+  const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
+  const int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
+  const int e0 = a.chunk_e0[(size_t)bg * a.max_chunks_g + jl];
+
+  // token -> (row, head mask); row >= 0 indexes k_perm, row < 0 is steady row (-1 - row)
+  for (int i = threadIdx.x; i < kChunkTokens; i += kAttThreads) { sh_row[i] = 0; sh_mask[i] = 0; }
+  __syncthreads();
+  for (int t = t0 + threadIdx.x; t < min(t1, NS); t += kAttThreads) {
+    sh_row[t - t0] = -1 - t;
+    sh_mask[t - t0] = (1 << G) - 1;
+  }
+  for (int e = e0 + threadIdx.x; e < n_entries; e += kAttThreads) {
+    const int s = pre[e];
+    if (s >= t1) break;
+    const int s1 = pre[e + 1];
+    const int r0 = row0[e], m = msk[e];
+    for (int t = max(s, t0); t < min(s1, t1); ++t) { sh_row[t - t0] = r0 + (t - s); sh_mask[t - t0] = m; }
+  }
+  __syncthreads();
+
+  const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
+  const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
+  const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * NS * kD;
+  const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * NS * kD;
+  const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) St<T>::load8(qg + (size_t)h * kD + 8 * lr, qf[h]);
+
+  float kr[8][8], v[8][8], wden[8];
+  int mk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = w * 32 + 4 * i + rg;
+    const int t = t0 + r;
+    wden[i] = 1.f;
+    mk[i] = 0;
+    if (t < t1) {
+      const int row = sh_row[r];
+      mk[i] = sh_mask[r];
+      const T* kq = row >= 0 ? kp + (size_t)row * kD : ks + (size_t)(-1 - row) * kD;
+      const T* vq = row >= 0 ? vp + (size_t)row * kD : vs + (size_t)(-1 - row) * kD;
+      St<T>::load8(kq + 8 * lr, kr[i]);
+      St<T>::load8(vq + 8 * lr, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kr[i][e] = 0.f; v[i][e] = 0.f; }
+    }
+  }
+  float l[8][G];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += qf[h][e] * kr[i][e];
+      s += __shfl_xor(s, 8);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 1);
+      l[i][h] = ((mk[i] >> h) & 1) ? s * a.scale : -INFINITY;
+    }
+  }
+  finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
+}
+
+template <int G>
+__device__ void merge_group(const DecodeArgs& a, int bg) {
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int32_t* gd = a.grp + (size_t)bg * 4;
+  const int n_chunks = __builtin_nontemporal_load(gd + 2), cbase = __builtin_nontemporal_load(gd + 3);
+  const int P = a.est_tiles_g + n_chunks;
+  for (int idx = threadIdx.x; idx < G * kD; idx += kAttThreads) {
+    const int h = idx / kD, dd = idx - h * kD;
+    float M = -INFINITY;
+    for (int p = 0; p < P; ++p) {
+      const size_t slot = p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
+      const float den = __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2 + 1);
+      if (den > 0.f) M = fmaxf(M, __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2));
+    }
+    float den = 0.f, num = 0.f;
+    for (int p = 0; p < P; ++p) {
+      const size_t slot = p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
+      const float dp = __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2 + 1);
+      if (dp > 0.f) {
+        const float f = __expf(__builtin_nontemporal_load(a.part_md + (slot * G + h) * 2) - M);
+        den += f * dp;
+        num += f * __builtin_nontemporal_load(a.part_num + (slot * G + h) * kD + dd);
+      }
+    }
+    const size_t oh = (size_t)b * a.Hq + (size_t)g * G + h;
+    a.out[oh * kD + dd] = num / den;
+    if (dd == 0 && a.lse) a.lse[oh] = M + __logf(den);
+  }
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
+  __shared__ float sh_m[4 * G];
+  __shared__ float sh_den[4 * G];
+  __shared__ float sh_num[4 * G * kD];
+  __shared__ int sh_row[kChunkTokens];
+  __shared__ int sh_mask[kChunkTokens];
+  __shared__ int sh_flag;
+  __shared__ int sh_base[kMaxGroupsPerDecode];
+  const int BG = a.B * a.Hkv;
+  const int total = (int)__builtin_nontemporal_load(a.counters + 2 * BG + 1);
+  for (int i = threadIdx.x; i < BG; i += kAttThreads) sh_base[i] = a.grp[(size_t)i * 4 + 3];
+  __syncthreads();
+  for (int item = blockIdx.x; item < a.n_est + total; item += gridDim.x) {
+    int bg;
+    if (item < a.n_est) {
+      bg = item / a.est_tiles_g;
+      est_tile<T, G>(a, bg, item - bg * a.est_tiles_g, item, sh_m, sh_num, sh_den);
+    } else {
+      const int j = item - a.n_est;
+      // group owning global chunk j: the last group whose chunk base is <= j (a group with no
+      // chunks shares its base with the next one, so the last such group always covers j)
+      int lo = 0, hi = BG - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh_base[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      bg = lo;
+      const int jl = j - sh_base[bg];
+      attend_chunk<T, G>(a, bg, jl, item, sh_m, sh_num, sh_den, sh_row, sh_mask);
+    }
+    // completion: the last item of the group merges it
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t expected = (uint32_t)(a.est_tiles_g + __builtin_nontemporal_load(a.grp + (size_t)bg * 4 + 2));
+      sh_flag = (atomicAdd(&a.counters[BG + bg], 1u) == expected - 1u);
+    }
+    __syncthreads();
+    if (sh_flag) {
+      __threadfence();
+      merge_group<G>(a, bg);
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================================ launcher
+template <typename T, int G>
+static hipError_t launch_attend(const DecodeArgs& a, hipStream_t s, int grid) {
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(grid), dim3(kAttThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
+  hipLaunchKernelGGL(k_score<T>, dim3((unsigned)std::max<int64_t>(1, ceil_div(a.C, 128)), BG),
+                     dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool keys_in_lds = (size_t)a.C * 4 + (size_t)a.W32 * 4 <= 65536;
+  const size_t dyn = (size_t)a.W32 * 4 + (keys_in_lds ? (size_t)a.C * 4 : 0);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), dyn, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int max_items = a.n_est + BG * a.max_chunks_g;
+  const int grid = std::max(1, std::min(max_items, 2048));
+  switch (a.G) {
+    case 1: return launch_attend<T, 1>(a, s, grid);
+    case 2: return launch_attend<T, 2>(a, s, grid);
+    case 4: return launch_attend<T, 4>(a, s, grid);
+    case 8: return launch_attend<T, 8>(a, s, grid);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+    attr_set = true;
+  }
+  return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);
+}
+
+}  // namespace wi

@@ -1,0 +1,162 @@
+// Device-side helpers shared by the wave-index kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wi {
+
+constexpr int kD = 128;     // head dimension the kernels are written for
+constexpr int kWave = 64;   // CDNA wavefront width
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ element conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Storage traits: float (fp32) or uint16_t (bf16 bits).
+template <typename T> struct St;
+template <> struct St<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float f(float x) { return x; }
+  // fp64 -> fp32 by round-to-nearest-even
+  __device__ __forceinline__ static float from_f64(double x) { return (float)x; }
+  // 8 consecutive elements starting at p (32-byte aligned)
+  __device__ __forceinline__ static void load8(const float* p, float (&o)[8]) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 4);
+    o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
+    o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
+    o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y);
+    o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
+  }
+};
+template <> struct St<uint16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float f(uint16_t x) { return bf16_bits_to_f32(x); }
+  // fp64 -> fp32 (RNE) -> bf16 (RNE): two rounding steps
+  __device__ __forceinline__ static uint16_t from_f64(double x) { return f32_to_bf16_bits((float)x); }
+  __device__ __forceinline__ static void load8(const uint16_t* p, float (&o)[8]) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+    o[0] = __uint_as_float(a.x << 16); o[1] = __uint_as_float(a.x & 0xffff0000u);
+    o[2] = __uint_as_float(a.y << 16); o[3] = __uint_as_float(a.y & 0xffff0000u);
+    o[4] = __uint_as_float(a.z << 16); o[5] = __uint_as_float(a.z & 0xffff0000u);
+    o[6] = __uint_as_float(a.w << 16); o[7] = __uint_as_float(a.w & 0xffff0000u);
+  }
+};
+
+// fp32 -> uint32 whose unsigned order is the float order (-NaN < -Inf < ... < +Inf < +NaN).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ uint64_t f64_order_key(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Canonical fp64 score: sum over j ascending of x_j * y_j, each product exact (both operands
+// carry at most 24 significant bits), one rounding per addition, no contraction into FMA.
+template <typename T>
+__device__ __noinline__ double canonical_dot(const T* __restrict__ x, const T* __restrict__ y) {
+#pragma clang fp contract(off)
+  double acc = 0.0;
+  for (int j = 0; j < kD; ++j) {
+    const double p = (double)St<T>::f(x[j]) * (double)St<T>::f(y[j]);
+    acc = acc + p;
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------------ wave / block reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive prefix sum within a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).  `scratch` holds
+// >= 17 ints of LDS.  Returns this thread's exclusive prefix; *total receives the block sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) { const int t = scratch[i]; scratch[i] = run; run += t; }
+    scratch[16] = run;
+  }
+  __syncthreads();
+  const int res = scratch[w] + inc - v;
+  *total = scratch[16];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < nw; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ int block_isum(int v, int* scratch) {
+  v = wave_isum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  int r = 0;
+  for (int i = 0; i < nw; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace wi

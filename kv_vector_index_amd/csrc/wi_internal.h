@@ -1,0 +1,80 @@
+// Internal host/device declarations of the wave-index library: workspace layouts and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <cmath>
+#include <stdint.h>
+
+#include "wave_index.h"
+
+namespace wi {
+
+constexpr int kChunkTokens = 128;   // tokens per exact-attention work item
+constexpr int kEstTile = 128;       // clusters per estimation work item
+constexpr int kMaxGroup = 8;        // query heads per KV head supported by the decode kernels
+constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
+constexpr int kMaxClustersPerSeg = 4096;
+constexpr int kMaxGroupsPerDecode = 4096;  // B * Hkv of one decode call
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------------ decode workspace
+struct DecodeLayout {
+  int BG, BH, G, W32, Umax, max_chunks_g, est_tiles_g, n_est, max_chunks;
+  int n_counters;          // [0,BG) select arrivals, [BG,2BG) attend arrivals, 2BG all, 2BG+1 total
+  size_t off_counters, off_scores, off_mu_norm, off_keys32, off_sel_bits, off_band_ids,
+      off_band_key, off_wl_row0, off_wl_mask, off_wl_pre, off_grp, off_chunk_e0, off_part_md,
+      off_part_num, total;
+};
+DecodeLayout decode_layout(const wi_decode_params& p);
+
+// Device pointers of one decode call.
+struct DecodeArgs {
+  const void* mu;          // [BG, C, d]
+  const void* sv;          // [BG, C, d]
+  const int32_t* offsets;  // [BG, C+1]
+  const void* k_perm;      // [BG, Nc, d]
+  const void* v_perm;
+  const void* k_steady;    // [BG, NS, d]
+  const void* v_steady;
+  const void* q;           // [BH, d]
+  float* out;              // [BH, d]
+  float* lse;              // [BH] or null
+  int32_t* sel_ids;        // [BH, top_k] or null
+  // workspace
+  uint32_t* counters;
+  float* scores;           // [BH, C]
+  float* mu_norm;          // [BG, C]
+  uint32_t* keys32;        // [BH, C]
+  uint32_t* sel_bits;      // [BH, W32]
+  int32_t* band_ids;       // [BH, C]
+  uint64_t* band_key;      // [BH, C]
+  int32_t* wl_row0;        // [BG, Umax]
+  int32_t* wl_mask;        // [BG, Umax]
+  int32_t* wl_pre;         // [BG, Umax+1]
+  int32_t* grp;            // [BG, 4]: n_entries, n_tok, n_chunks, chunk_base
+  int32_t* chunk_e0;       // [BG, max_chunks_g]
+  float* part_md;          // [(n_est + max_chunks), G, 2]
+  float* part_num;         // [(n_est + max_chunks), G, d]
+  // shapes
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, max_chunks_g, est_tiles_g, n_est, n_counters;
+  float scale;
+};
+
+hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ build workspace
+struct BuildLayout {
+  int64_t C, Nc, NS, nseg, L;
+  size_t off_mhat, off_assign, off_knorm, off_flag_cnt, off_flag_list, total;
+};
+BuildLayout build_layout(const wi_build_params& p);
+
+hipError_t launch_build(const wi_build_params& p, const BuildLayout& L, const void* k,
+                        const void* v, const wi_index_view& out, void* ws, hipStream_t s);
+
+}  // namespace wi

@@ -1,0 +1,244 @@
+"""Python binding of libwave_index.so (the C ABI declared in include/wave_index.h).
+
+Argument marshalling only: every step of the build and of the decode runs in the HIP kernels of
+the library.  torch supplies device memory and the HIP stream handle.  The binding fails loudly
+when the library is missing; there is no fallback path.
+
+Functions with the C names (``wi_index_shapes_for``, ``wi_build_index``,
+``wi_decode_workspace_bytes``, ``wi_decode``, ``wi_status_string``, ``wi_last_error``) take and
+return ctypes structures; ``build_index`` and ``decode`` wrap them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwave_index.so")
+
+WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0, -1, -2, -3, -4
+WI_F32, WI_BF16 = 0, 1
+EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode",
+            "wi_status_string", "wi_last_error")
+
+
+class WaveIndexError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"wave-index status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class BuildParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("seg_len", ctypes.c_int32), ("clusters_per_seg", ctypes.c_int32),
+                ("iters", ctypes.c_int32), ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class IndexView(ctypes.Structure):
+    _fields_ = [("centroids", ctypes.c_void_p), ("value_sums", ctypes.c_void_p),
+                ("sizes", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("k_perm", ctypes.c_void_p),
+                ("v_perm", ctypes.c_void_p), ("k_steady", ctypes.c_void_p),
+                ("v_steady", ctypes.c_void_p)]
+
+
+class IndexShapes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "C", "Nc", "n_steady", "nseg", "centroids", "value_sums", "sizes", "offsets", "perm",
+        "k_perm", "v_perm", "k_steady", "v_steady", "build_workspace_bytes")]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("n_steady", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("Nc", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.wi_index_shapes_for.argtypes = [ctypes.POINTER(BuildParams), ctypes.POINTER(IndexShapes)]
+        L.wi_build_index.argtypes = [ctypes.POINTER(BuildParams), vp, vp, ctypes.POINTER(IndexView),
+                                     vp, sz, vp]
+        L.wi_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
+        L.wi_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
+                                vp, vp, sz, vp]
+        L.wi_status_string.argtypes = [ctypes.c_int]
+        for name in ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode"):
+            getattr(L, name).restype = ctypes.c_int
+        L.wi_status_string.restype = ctypes.c_char_p
+        L.wi_last_error.restype = ctypes.c_char_p
+        L.wi_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def wi_status_string(status: int) -> str:
+    return lib().wi_status_string(int(status)).decode()
+
+
+def wi_last_error() -> str:
+    return lib().wi_last_error().decode()
+
+
+def _check(status: int) -> int:
+    if status != WI_OK:
+        raise WaveIndexError(status, f"{wi_status_string(status)}: {wi_last_error()}")
+    return status
+
+
+def wi_index_shapes_for(p: BuildParams) -> IndexShapes:
+    out = IndexShapes()
+    _check(lib().wi_index_shapes_for(ctypes.byref(p), ctypes.byref(out)))
+    return out
+
+
+def wi_build_index(p: BuildParams, k_ptr: int, v_ptr: int, view: IndexView, ws_ptr: int,
+                   ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_build_index(ctypes.byref(p), k_ptr, v_ptr, ctypes.byref(view), ws_ptr,
+                                       ws_bytes, stream))
+
+
+def wi_decode_workspace_bytes(p: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().wi_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def wi_decode(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_ptr: Optional[int],
+              sel_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_decode(ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr,
+                                  sel_ptr, ws_ptr, ws_bytes, stream))
+
+
+# ---------------------------------------------------------------------------- torch convenience
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return WI_BF16
+    if t.dtype == torch.float32:
+        return WI_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclasses.dataclass
+class Index:
+    """Device tensors of a built wave index (layouts as in include/wave_index.h)."""
+    centroids: object
+    value_sums: object
+    sizes: object
+    offsets: object
+    perm: object
+    k_perm: object
+    v_perm: object
+    k_steady: object
+    v_steady: object
+    C: int
+    Nc: int
+    n_steady: int
+
+    def view(self) -> IndexView:
+        return IndexView(*[_ptr(getattr(self, f)) for f in (
+            "centroids", "value_sums", "sizes", "offsets", "perm", "k_perm", "v_perm",
+            "k_steady", "v_steady")])
+
+    def clone(self) -> "Index":
+        return dataclasses.replace(self, **{f: getattr(self, f).clone() for f in (
+            "centroids", "value_sums", "sizes", "offsets", "perm", "k_perm", "v_perm",
+            "k_steady", "v_steady")})
+
+
+def allocate_index(B: int, Hkv: int, N: int, sink: int, window: int, seg_len: int,
+                   clusters_per_seg: int, dtype, device) -> tuple:
+    """Index tensors (uninitialised) and the BuildParams skeleton for the given shape."""
+    import torch
+    p = BuildParams(B, Hkv, N, 128, sink, window, seg_len, clusters_per_seg, 1,
+                    WI_BF16 if dtype == torch.bfloat16 else WI_F32, 0)
+    sh = wi_index_shapes_for(p)
+    C, Nc, NS = sh.C, sh.Nc, sh.n_steady
+    e = dict(device=device)
+    idx = Index(
+        centroids=torch.empty((B, Hkv, C, 128), dtype=dtype, **e),
+        value_sums=torch.empty((B, Hkv, C, 128), dtype=dtype, **e),
+        sizes=torch.empty((B, Hkv, C), dtype=torch.int32, **e),
+        offsets=torch.empty((B, Hkv, C + 1), dtype=torch.int32, **e),
+        perm=torch.empty((B, Hkv, Nc), dtype=torch.int32, **e),
+        k_perm=torch.empty((B, Hkv, Nc, 128), dtype=dtype, **e),
+        v_perm=torch.empty((B, Hkv, Nc, 128), dtype=dtype, **e),
+        k_steady=torch.empty((B, Hkv, NS, 128), dtype=dtype, **e),
+        v_steady=torch.empty((B, Hkv, NS, 128), dtype=dtype, **e),
+        C=C, Nc=Nc, n_steady=NS)
+    return idx, p, sh
+
+
+def build_index(K, V, sink: int, window: int, seg_len: int, clusters_per_seg: int, iters: int,
+                seed: int, workspace=None) -> Index:
+    """Build the wave index of K, V ([B,Hkv,N,128] device tensors, fp32 or bf16)."""
+    import torch
+    assert K.is_cuda and K.shape == V.shape and K.dtype == V.dtype and K.is_contiguous() and V.is_contiguous()
+    B, Hkv, N, d = K.shape
+    idx, p, sh = allocate_index(B, Hkv, N, sink, window, seg_len, clusters_per_seg, K.dtype, K.device)
+    p.d = d
+    p.iters = iters
+    p.seed = seed & ((1 << 64) - 1)
+    p.dtype = _dtype_code(K)
+    need = max(int(sh.build_workspace_bytes), 256)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=K.device)
+    wi_build_index(p, K.data_ptr(), V.data_ptr(), idx.view(), workspace.data_ptr(), workspace.numel(),
+                   _stream(K.device))
+    return idx
+
+
+def decode_params(index: Index, B: int, Hq: int, Hkv: int, top_k: int, dtype,
+                  scale: Optional[float] = None) -> DecodeParams:
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    return DecodeParams(B, Hq, Hkv, 128, index.n_steady, index.C, index.Nc, top_k, scale,
+                        WI_BF16 if dtype == torch.bfloat16 else WI_F32)
+
+
+def decode(index: Index, q, top_k: int, scale: Optional[float] = None, workspace=None,
+           want_lse: bool = True, want_sel: bool = True, out=None):
+    """One decode step: q [B,Hq,128] -> (out fp32 [B,Hq,128], lse [B,Hq] or None, sel [B,Hq,k])."""
+    import torch
+    assert q.is_cuda and q.is_contiguous()
+    B, Hq, d = q.shape
+    Hkv = index.centroids.shape[1]
+    p = decode_params(index, B, Hq, Hkv, top_k, q.dtype, scale)
+    p.d = d
+    p.dtype = _dtype_code(q)
+    need = wi_decode_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    sel = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device) if want_sel else None
+    wi_decode(p, index.view(), q.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(sel),
+              workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    return out, lse, sel

@@ -1,0 +1,165 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, its structs match
+the header's layout, and host-side validation rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_vector_index_amd import wave_index as wi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wave_index.h")
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wi_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(wi.EXPORTED)
+    L = wi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", wi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (wi_[a-z_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "wave_index.h"
+#define P(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
+int main(void) {
+  printf("wi_build_params %zu\n", sizeof(wi_build_params));
+  printf("wi_index_view %zu\n", sizeof(wi_index_view));
+  printf("wi_index_shapes %zu\n", sizeof(wi_index_shapes));
+  printf("wi_decode_params %zu\n", sizeof(wi_decode_params));
+  P(wi_build_params, seed); P(wi_build_params, dtype); P(wi_build_params, iters);
+  P(wi_index_view, v_steady); P(wi_index_shapes, build_workspace_bytes);
+  P(wi_decode_params, scale); P(wi_decode_params, dtype); P(wi_decode_params, top_k);
+  return 0;
+}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    assert int(got["wi_build_params"]) == ctypes.sizeof(wi.BuildParams)
+    assert int(got["wi_index_view"]) == ctypes.sizeof(wi.IndexView)
+    assert int(got["wi_index_shapes"]) == ctypes.sizeof(wi.IndexShapes)
+    assert int(got["wi_decode_params"]) == ctypes.sizeof(wi.DecodeParams)
+    assert int(got["wi_build_params.seed"]) == wi.BuildParams.seed.offset
+    assert int(got["wi_build_params.dtype"]) == wi.BuildParams.dtype.offset
+    assert int(got["wi_build_params.iters"]) == wi.BuildParams.iters.offset
+    assert int(got["wi_index_view.v_steady"]) == wi.IndexView.v_steady.offset
+    assert int(got["wi_index_shapes.build_workspace_bytes"]) == wi.IndexShapes.build_workspace_bytes.offset
+    assert int(got["wi_decode_params.scale"]) == wi.DecodeParams.scale.offset
+    assert int(got["wi_decode_params.dtype"]) == wi.DecodeParams.dtype.offset
+    assert int(got["wi_decode_params.top_k"]) == wi.DecodeParams.top_k.offset
+
+
+@pytest.mark.parametrize("N,S,W,L,Cs,want", [
+    (8192, 4, 256, 0, 64, dict(C=64, Nc=7932, n_steady=260, nseg=1)),
+    (131072, 4, 64, 8192, 512, dict(C=8192, Nc=131004, n_steady=68, nseg=16)),
+    (1048576, 4, 64, 8192, 512, dict(C=65536, Nc=1048508, n_steady=68, nseg=128)),
+    (131072, 0, 0, 8192, 512, dict(C=8192, Nc=131072, n_steady=0, nseg=16)),
+    (50, 30, 30, 8, 4, dict(C=0, Nc=0, n_steady=50, nseg=0)),
+    (100, 10, 10, 30, 7, dict(C=21, Nc=80, n_steady=20, nseg=3)),
+])
+def test_index_shapes(N, S, W, L, Cs, want):
+    p = wi.BuildParams(2, 8, N, 128, S, W, L, Cs, 10, wi.WI_BF16, 0)
+    sh = wi.wi_index_shapes_for(p)
+    for k, v in want.items():
+        assert getattr(sh, k) == v, k
+    BG = 16
+    assert sh.centroids == BG * want["C"] * 128 and sh.offsets == BG * (want["C"] + 1)
+    assert sh.perm == BG * want["Nc"] and sh.k_steady == BG * want["n_steady"] * 128
+    assert sh.build_workspace_bytes >= BG * want["Nc"] * 12
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d", 64, wi.WI_ERR_UNSUPPORTED), ("B", 0, wi.WI_ERR_INVALID_ARG),
+    ("N", 0, wi.WI_ERR_INVALID_ARG), ("seg_len", 70000, wi.WI_ERR_UNSUPPORTED),
+    ("clusters_per_seg", 5000, wi.WI_ERR_UNSUPPORTED), ("clusters_per_seg", 0, wi.WI_ERR_INVALID_ARG),
+    ("iters", 0, wi.WI_ERR_INVALID_ARG), ("dtype", 7, wi.WI_ERR_INVALID_ARG),
+    ("sink", -1, wi.WI_ERR_INVALID_ARG),
+])
+def test_shapes_rejects(field, value, status):
+    p = wi.BuildParams(1, 8, 131072, 128, 4, 64, 8192, 512, 10, wi.WI_BF16, 0)
+    setattr(p, field, value)
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_index_shapes_for(p)
+    assert e.value.status == status
+    assert wi.wi_last_error()
+
+
+FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation first
+
+
+def _view():
+    return wi.IndexView(*([FAKE] * 9))
+
+
+def _dparams(**kw):
+    p = wi.DecodeParams(1, 32, 8, 128, 68, 8192, 131004, 164, 0.0883883, wi.WI_BF16)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), wi.WI_ERR_UNSUPPORTED), (dict(Hq=12), wi.WI_ERR_INVALID_ARG),
+    (dict(Hq=24), wi.WI_ERR_UNSUPPORTED), (dict(top_k=-1), wi.WI_ERR_INVALID_ARG),
+    (dict(C=0), wi.WI_ERR_INVALID_ARG), (dict(scale=0.0), wi.WI_ERR_INVALID_ARG),
+    (dict(n_steady=0, C=0, Nc=0), wi.WI_ERR_INVALID_ARG), (dict(dtype=3), wi.WI_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_params(kw, status):
+    p = _dparams(**kw)
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode(p, _view(), FAKE, FAKE, None, None, FAKE, 1 << 40, 0)
+    assert e.value.status == status
+
+
+def test_decode_rejects_null_pointers_and_small_workspace():
+    p = _dparams()
+    need = wi.wi_decode_workspace_bytes(p)
+    assert need > 0
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode(p, _view(), None, FAKE, None, None, FAKE, need, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    v = _view()
+    v.k_perm = None
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode(p, v, FAKE, FAKE, None, None, FAKE, need, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode(p, _view(), FAKE, FAKE, None, None, FAKE, need - 1, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode(p, _view(), FAKE, FAKE, None, None, FAKE + 8, need, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+
+
+def test_build_rejects_null_inputs_and_small_workspace():
+    p = wi.BuildParams(1, 8, 4096, 128, 4, 64, 1024, 64, 3, wi.WI_BF16, 1)
+    need = wi.wi_index_shapes_for(p).build_workspace_bytes
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_build_index(p, None, FAKE, _view(), FAKE, need, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_build_index(p, FAKE, FAKE, _view(), FAKE, need - 1, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+
+
+def test_status_strings():
+    for s in (wi.WI_OK, wi.WI_ERR_INVALID_ARG, wi.WI_ERR_UNSUPPORTED, wi.WI_ERR_WORKSPACE, wi.WI_ERR_HIP):
+        assert wi.wi_status_string(s)
+    assert wi.wi_status_string(-99) == "unknown status"

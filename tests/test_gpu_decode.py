@@ -1,0 +1,155 @@
+"""GPU parity of wi_decode against the CPU oracle (decode side only, on oracle-built indexes).
+
+Gates: selected cluster ids bit-exact (ascending, -1 padded); max |o - oracle| <= 1e-4 (fp32) or
+1e-2 (bf16 inputs, fp32 accumulation); |lse - oracle| <= 1e-4; relative RMS error of o <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_vector_index_amd import synth
+from kv_vector_index_amd import wave_index as wi
+from wi_testutil import assert_decode_parity, device, inputs, upload_index
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(**kw):
+    # several score tiles (C = 6 x 48 = 288), a ragged last segment, several attention chunks
+    w = synth.Workload("small", 2, 8, 2, 128, 6000, "bf16", 40, 4, 32, 1024, 48, 3, 7)
+    return w.replace(**kw)
+
+
+def _run(w, seed, top_k=None, q_scale_override=None, build_seed=5):
+    dev = device()
+    Kt, Vt, Qt, K64, V64, Q64 = inputs(w, seed, dev)
+    idx = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters,
+                             build_seed, w.dtype)
+    k = w.top_k if top_k is None else top_k
+    gi = upload_index(idx, w.dtype, dev)
+    o, lse, sel = wi.decode(gi, Qt, k)
+    torch.cuda.synchronize()
+    ro, rl, rs = oracle.decode(Q64, idx, w.Hq, k, 1 / math.sqrt(w.d))
+    return assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_parity_small(dtype, G):
+    _run(_small(dtype=dtype, Hq=2 * G), seed=10 + G)
+
+
+@pytest.mark.parametrize("top_k", [0, 1, 13, 287, 288, 400])
+def test_decode_parity_top_k_range(top_k):
+    _run(_small(B=1, Hq=8), seed=3, top_k=top_k)
+
+
+def test_decode_sharpened_queries_bf16():
+    # a query scale of 12 concentrates attention (max logit ~ 12) so that the 1e-2 gate bites
+    _run(_small(q_scale=12.0, q_noise=0.5), seed=4)
+
+
+def test_decode_all_retrieved_equals_dense_attention():
+    dev = device()
+    w = _small(B=1, Hq=4, dtype="f32")
+    Kt, Vt, Qt, K64, V64, Q64 = inputs(w, 21, dev)
+    idx = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1, "f32")
+    gi = upload_index(idx, "f32", dev)
+    o, lse, _ = wi.decode(gi, Qt, idx.C)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(128)
+    for h in range(w.Hq):
+        g = h // (w.Hq // w.Hkv)
+        q = torch.from_numpy(Q64[0, h])
+        Kd, Vd = torch.from_numpy(K64[0, g]), torch.from_numpy(V64[0, g])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[None, None, None], Kd[None, None], Vd[None, None], scale=scale)[0, 0, 0].numpy()
+        assert np.abs(o[0, h].cpu().numpy() - ref).max() <= 1e-5
+        assert abs(float(lse[0, h]) - float(torch.logsumexp(Kd @ q * scale, 0))) <= 1e-5
+
+
+def test_decode_ties_broken_by_lower_id():
+    dev = device()
+    rng = np.random.default_rng(7)
+    C, d = 300, 128
+    mu = oracle.round_to_dtype(rng.standard_normal((C, d)) * 0.1, "bf16")
+    for c in range(0, C, 3):
+        mu[c + 1] = mu[c]          # every score appears at least twice
+    mu[10:40] = mu[9]
+    sizes = rng.integers(1, 5, C)
+    sizes[::17] = 0                # some empty clusters (never selectable)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    Nc = int(off[-1])
+    kp = oracle.round_to_dtype(rng.standard_normal((Nc, d)) * 0.1, "bf16")
+    vp = oracle.round_to_dtype(rng.standard_normal((Nc, d)), "bf16")
+    sv = np.zeros((C, d))
+    for c in range(C):
+        if sizes[c]:
+            sv[c] = oracle.round_to_dtype(vp[off[c]:off[c + 1]].sum(0), "bf16")
+    ks = oracle.round_to_dtype(rng.standard_normal((3, d)) * 0.1, "bf16")
+    vs = oracle.round_to_dtype(rng.standard_normal((3, d)), "bf16")
+    idx = oracle.Index(centroids=mu[None, None], value_sums=sv[None, None], sizes=sizes[None, None],
+                       offsets=off[None, None], perm=np.arange(Nc)[None, None] + 3,
+                       k_perm=kp[None, None], v_perm=vp[None, None], k_steady=ks[None, None],
+                       v_steady=vs[None, None], C=C, Nc=Nc)
+    Q64 = oracle.round_to_dtype(rng.standard_normal((1, 4, d)), "bf16")
+    Q64[0, 3] = mu[9] * 4          # the 31 tied clusters 9..39 top this head's ranking
+    gi = upload_index(idx, "bf16", dev)
+    Qt = synth.cast(Q64, "bf16", dev)
+    for k in (1, 5, 20, 31, 45, 150):
+        o, lse, sel = wi.decode(gi, Qt, k)
+        torch.cuda.synchronize()
+        ro, rl, rs = oracle.decode(Q64, idx, 4, k, 1 / math.sqrt(d))
+        assert_decode_parity(o, lse, sel, ro, rl, rs, "bf16")
+
+
+def test_decode_steady_only_context():
+    dev = device()
+    w = _small(B=1, Hq=4, N=50, sink=8, window=64)
+    Kt, Vt, Qt, K64, V64, Q64 = inputs(w, 2, dev)
+    idx = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1, "bf16")
+    assert idx.C == 0
+    gi = upload_index(idx, "bf16", dev)
+    o, lse, sel = wi.decode(gi, Qt, 4)
+    torch.cuda.synchronize()
+    ro, rl, rs = oracle.decode(Q64, idx, w.Hq, 4, 1 / math.sqrt(128))
+    assert_decode_parity(o, lse, sel, ro, rl, rs, "bf16")
+
+
+def test_decode_single_head_8k_f32_workload():
+    # one head, fp32, 8192 keys from 64 blobs, 64 clusters, 10 iterations, top 8, 4 + 256 steady
+    w = synth.WORKLOADS["single_head_8k_f32"]
+    _run(w, seed=0, build_seed=0)
+
+
+def test_decode_gqa_128k_bf16_full_size_sampled_heads():
+    """The benchmarked launch (B=1, 32/8 heads, 128K, top 164 of 8192 clusters), on an index the
+    oracle finalizes from the generator's blob labels (folded into 512 clusters per segment);
+    the oracle checks a sample of query heads one by one."""
+    dev = device()
+    w = synth.WORKLOADS["gqa_128k_bf16"]
+    Kt, Vt, Qt, K64, V64, Q64, labels = inputs(w, 0, dev, with_labels=True)
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    ci = np.arange(hi - lo)
+    lab = (ci // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    idx = oracle.finalize_index(K64, V64, lab, w.sink, w.window, C, w.dtype)
+    gi = upload_index(idx, w.dtype, dev)
+    o, lse, sel = wi.decode(gi, Qt, w.top_k)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 5), (0, 14), (0, 31)]
+    G = w.Hq // w.Hkv
+    res = [oracle.decode_head(Q64[b, h], idx, b, h // G, w.top_k, 1 / math.sqrt(w.d)) for b, h in heads]
+    ro = np.stack([r[0] for r in res])
+    rl = np.array([r[1] for r in res])
+    rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
+    assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
+    # every head: the selected ids are ascending, distinct, non-empty clusters
+    s = sel.cpu().numpy()
+    sizes = idx.sizes
+    for h in range(w.Hq):
+        ids = s[0, h][s[0, h] >= 0]
+        assert ids.size == w.top_k and np.all(np.diff(ids) > 0) and np.all(sizes[0, h // G, ids] > 0)
