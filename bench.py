@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the wave-index decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_128k_bf16]
+
+Workload (default): one Llama-3-8B-shaped GQA attention layer (32 query heads, 8 KV heads, head
+dim 128, bf16), batch 1, 131072 tokens of context, segmented spherical k-means index with 8192
+clusters (16 segments x 512), top 164 clusters (2%) retrieved per query head, 4 sink + 64 window
+tokens in the steady zone.  Synthetic seeded blob-mixture keys (see kv_vector_index_amd/synth.py).
+
+A step is one wi_decode call: scores, top-k, exact attention over steady + retrieved tokens,
+estimation of every other cluster, LSE merge, for all B x Hq query heads.  The index is built
+once beforehand (its build is timed separately and reported under "build").  To keep steps from
+hitting in the 256 MB Infinity Cache, the timed steps cycle through `--instances` copies of the
+index placed at different HBM addresses.  Steps are captured in a HIP graph and replayed, so the
+timed region measures GPU work rather than Python launch overhead.  Inputs are resident in HBM
+before the timed region starts.
+
+Prints one JSON line (rank 0) with the throughput, the roofline position of the dominant kernel
+(per-kernel HIP-event timing over a second, eager pass), and the CPU oracle timed on the host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "wave-index decode steps/s at 128K ctx (batch·heads); achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_MFMA_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_gqa_128k_bf16.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_kernel_source_hash() -> str:
+    with open(os.path.join(ROOT, "kv_vector_index_amd", "csrc", "wi_decode.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, idx_offsets_np, sel_np):
+    """Bytes the method must touch per step: index rows read once (mu, SV, offsets, steady rows,
+    union of the rows retrieved by a KV group's query heads), queries, outputs."""
+    import numpy as np
+    e = 2 if w.dtype == "bf16" else 4
+    d = w.d
+    G = w.Hq // w.Hkv
+    C = idx_offsets_np.shape[-1] - 1
+    NS = min(w.N, w.sink + w.window)
+    per = {"score": 0, "attend": 0, "select": 0}
+    union_rows = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            off = idx_offsets_np[b, g]
+            ids = np.unique(sel_np[b, g * G:(g + 1) * G].ravel())
+            ids = ids[ids >= 0]
+            u = int((off[ids + 1] - off[ids]).sum())
+            union_rows += u
+            per["score"] += C * d * e                       # centroids
+            per["select"] += 4 * (C + 1)                    # offsets (cluster sizes)
+            per["attend"] += C * d * e + 4 * (C + 1) + NS * 2 * d * e + u * 2 * d * e
+    per["score"] += w.B * w.Hq * d * e                      # queries
+    per["attend"] += w.B * w.Hq * (4 * d + 4)               # outputs + lse
+    per["select"] += w.B * w.Hq * w.top_k * 4               # selected ids
+    return per, union_rows
+
+
+def cpu_baseline(w, seed, budget_s):
+    """The oracle's decode on the host: one full step (all query heads) on an oracle-finalized
+    index of the same workload, repeated within the time budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from kv_vector_index_amd import synth
+
+    K, V, Q, labels = synth.make_instance(w, seed, with_labels=True)
+    K = synth.as_float64(synth.cast(K, w.dtype))
+    V = synth.as_float64(synth.cast(V, w.dtype))
+    Q = synth.as_float64(synth.cast(Q, w.dtype))
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    ci = np.arange(hi - lo)
+    lab = (ci // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    idx = oracle.finalize_index(K, V, lab, w.sink, w.window, C, w.dtype)
+    G = w.Hq // w.Hkv
+    scale = 1 / math.sqrt(w.d)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        heads = 0
+        while True:
+            for b in range(w.B):
+                for h in range(w.Hq):
+                    oracle.decode_head(Q[b, h], idx, b, h // G, w.top_k, scale)
+                    heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        steps = heads / (w.B * w.Hq)
+        # build: one segment of spherical k-means, scaled to every segment of every (b, g)
+        segs = oracle.segment_bounds(hi - lo, w.seg_len)
+        t1 = time.perf_counter()
+        a0, a1 = segs[0]
+        oracle.spherical_kmeans_segment(K[0, 0, lo + a0:lo + a1], w.clusters_per_seg, w.iters,
+                                        w.dtype, oracle.segment_state(1, 0, 0, 0))
+        seg_s = time.perf_counter() - t1
+    return {
+        "value": steps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+        "sample": f"{steps:.2f} decode steps (all {w.B * w.Hq} query heads each) of {w.name} on an "
+                  f"oracle-finalized index, NumPy float64, BLAS pinned to 1 thread, {dt:.1f} s",
+        "build_s_estimate": seg_s * len(segs) * w.B * w.Hkv,
+        "build_sample": f"one {a1 - a0}-token segment x {w.iters} iterations in {seg_s:.1f} s, "
+                        f"scaled to {len(segs) * w.B * w.Hkv} segments",
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="gqa_128k_bf16")
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would hold its "
+              "own sequences and KV heads with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_vector_index_amd import synth
+    from kv_vector_index_amd import wave_index as wi
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: generating inputs")
+    K, V, Q = synth.make_instance(w, args.seed)
+    Kt, Vt = synth.cast(K, w.dtype, dev), synth.cast(V, w.dtype, dev)
+    Qt = synth.cast(Q, w.dtype, dev)
+    del K, V
+
+    # ---- index build (timed on its own, with per-kernel events)
+    log("[bench] building the index")
+    idx = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    torch.cuda.synchronize()
+    wi.wi_profile_enable(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    idx = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    t1.record()
+    torch.cuda.synchronize()
+    build_stages = wi.wi_profile_read()
+    wi.wi_profile_enable(False)
+    build_ms = t0.elapsed_time(t1)
+    n_keys = w.B * w.Hkv * idx.Nc
+    assign_flops = 2.0 * n_keys * w.clusters_per_seg * w.d * w.iters
+    assign_ms = build_stages["assign"][0]
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    del Kt, Vt
+
+    # ---- instances at distinct HBM addresses
+    insts = [idx] + [idx.clone() for _ in range(args.instances - 1)]
+    qs = [Qt.clone() for _ in insts]
+    p = wi.decode_params(idx, w.B, w.Hq, w.Hkv, w.top_k, Qt.dtype)
+    ws_bytes = wi.wi_decode_workspace_bytes(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    sel = torch.empty((w.B, w.Hq, w.top_k), dtype=torch.int32, device=dev)
+    views = [i.view() for i in insts]
+
+    def step(i):
+        j = i % len(insts)
+        wi.wi_decode(p, views[j], qs[j].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
+                     ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
+
+    log("[bench] warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    off_np = idx.offsets.cpu().numpy()
+    per_bytes, union_rows = algorithmic_bytes(w, off_np, sel_np)
+    step_bytes = sum(per_bytes.values())
+
+    # ---- timed region: K steps
+    K_steps = args.steps
+    if args.no_graph:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K_steps):
+            step(i)
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+    else:
+        per_graph = min(K_steps, 8 * len(insts))
+        while K_steps % per_graph:
+            per_graph -= 1
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(per_graph):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(K_steps // per_graph):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K_steps
+
+    # ---- per-kernel timing (eager, HIP events around every kernel on the launch stream).  A
+    # long matrix product heads the queue so the host enqueues every step before the GPU reaches
+    # them: the events then time the kernels, not the Python launch gaps.
+    log("[bench] per-kernel timing pass")
+    prof_steps = min(K_steps, 200)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    wi.wi_profile_enable(True)
+    for _ in range(30):
+        a = a @ a
+        a = a / a.abs().max()
+    for i in range(prof_steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = wi.wi_profile_read()
+    wi.wi_profile_enable(False)
+    del a
+    avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items() if k in ("score", "select", "attend")}
+    attend_s = avg_ms["attend"] / 1e3
+    achieved = per_bytes["attend"] / attend_s / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == decode_kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "context": w.N, "clusters": idx.C, "top_k": w.top_k,
+                   "sink": w.sink, "window": w.window, "instances": len(insts),
+                   "timing": "eager" if args.no_graph else "hip-graph replay"},
+        "head_steps_per_s": 1e3 / ms_per_step * w.B * w.Hq,
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms_per_step / 1e3) / 1e9,
+        "step_frac_of_hbm_peak": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "retrieved_union_rows": union_rows,
+        "kernel_avg_us": {k: (v * 1e3 if v is not None else None) for k, v in avg_ms.items()},
+        "kernel_algorithmic_bytes": per_bytes,
+        "roofline": {"kernel": "k_attend", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+        "build": {"ms": build_ms,
+                  "stage_ms": {k: v[0] for k, v in build_stages.items() if v[1]},
+                  "assign_tflops": assign_flops / (assign_ms / 1e3) / 1e12 if assign_ms else None,
+                  "assign_mfma_frac": (assign_flops / (assign_ms / 1e3) / 1e12 / mfma_peak) if assign_ms else None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

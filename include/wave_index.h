@@ -140,6 +140,33 @@ wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const v
                     float *out, float *lse, int32_t *sel_ids, void *workspace, size_t ws_bytes,
                     void *stream);
 
+/* Stages timed by the profiling hook below (one entry per kernel of the two entry points). */
+typedef enum {
+  WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA)                          */
+  WI_STAGE_SELECT = 1,    /* decode: per-head top-k and the per-group work lists            */
+  WI_STAGE_ATTEND = 2,    /* decode: exact attention over steady + retrieved rows,
+                             estimation over the other clusters, log-sum-exp merge          */
+  WI_STAGE_PREP = 3,      /* build: steady-zone copies, key norms                           */
+  WI_STAGE_INIT = 4,      /* build: seeded initial centroid directions                      */
+  WI_STAGE_ASSIGN = 5,    /* build: k-means assignment (MFMA), all iterations               */
+  WI_STAGE_RESCORE = 6,   /* build: fp64 re-decision of uncertain assignments               */
+  WI_STAGE_CSR = 7,       /* build: sizes, offsets, permutation                             */
+  WI_STAGE_UPDATE = 8,    /* build: centroid directions from member sums                    */
+  WI_STAGE_FINAL = 9,     /* build: mean keys, value sums, cluster-major copies             */
+  WI_NUM_STAGES = 10
+} wi_stage;
+
+/* (host) Profiling hook for measurement tools.  While enabled, wi_decode and wi_build_index
+ * record a pair of HIP events around each kernel they launch, on the call's stream (this adds
+ * event records between the kernels; leave it disabled for production timing).  Enabling clears
+ * the accumulated figures.  Not thread-safe against concurrent calls on several threads. */
+wi_status wi_profile_enable(int enable);
+
+/* (host) Wait for the recorded events and return, per stage, the summed kernel time in
+ * milliseconds and the number of launches since the hook was enabled.  Both arrays hold
+ * WI_NUM_STAGES entries.  Synchronises on the recorded events only. */
+wi_status wi_profile_read(double *total_ms, int64_t *launches);
+
 /* (host) Static description of a status code. */
 const char *wi_status_string(wi_status s);
 

@@ -4,6 +4,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "wave_index.h"
 #include "wi_device.h"
@@ -72,6 +74,33 @@ wi_status derive_build(const wi_build_params* p, Derived* d) {
 }  // namespace
 
 namespace wi {
+
+bool g_prof_on = false;
+
+namespace {
+struct ProfRec {
+  int stage;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_recs;
+hipEvent_t g_prof_open[WI_NUM_STAGES] = {};
+}  // namespace
+
+void prof_record(int stage, bool begin, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  (void)hipEventRecord(ev, s);
+  if (begin) {
+    g_prof_open[stage] = ev;
+  } else if (g_prof_open[stage]) {
+    g_prof_recs.push_back({stage, g_prof_open[stage], ev});
+    g_prof_open[stage] = nullptr;
+  } else {
+    (void)hipEventDestroy(ev);
+  }
+}
 
 BuildLayout build_layout(const wi_build_params& p) {
   BuildLayout L{};
@@ -250,5 +279,37 @@ const char* wi_status_string(wi_status s) {
 }
 
 const char* wi_last_error(void) { return g_err; }
+
+static void prof_clear() {
+  for (auto& r : wi::g_prof_recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  wi::g_prof_recs.clear();
+  for (auto& e : wi::g_prof_open)
+    if (e) { (void)hipEventDestroy(e); e = nullptr; }
+}
+
+wi_status wi_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(wi::g_prof_mu);
+  if (enable) prof_clear();
+  wi::g_prof_on = enable != 0;
+  return WI_OK;
+}
+
+wi_status wi_profile_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(WI_ERR_INVALID_ARG, "null output array");
+  std::lock_guard<std::mutex> lk(wi::g_prof_mu);
+  for (int i = 0; i < WI_NUM_STAGES; ++i) { total_ms[i] = 0.0; launches[i] = 0; }
+  for (auto& r : wi::g_prof_recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(WI_ERR_HIP, "profiling events: %s", hipGetErrorString(e));
+    total_ms[r.stage] += ms;
+    launches[r.stage] += 1;
+  }
+  return WI_OK;
+}
 
 }  // extern "C"

@@ -542,28 +542,43 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   {
     const int rows = a.NS + a.Nc;
     const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(rows, 4), 4096));
+    prof_begin(WI_STAGE_PREP, st);
     hipLaunchKernelGGL(k_prep<T>, dim3(gx, BG), dim3(256), 0, st, a);
+    prof_end(WI_STAGE_PREP, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.Nc == 0) return hipSuccess;
   {
     const size_t lds = (size_t)a.Cs * 4 + (((size_t)a.L * 2 + 3) & ~size_t(3));
+    prof_begin(WI_STAGE_INIT, st);
     hipLaunchKernelGGL(k_init<T>, dim3(a.nseg, BG), dim3(kInitThreads), lds, st, a);
+    prof_end(WI_STAGE_INIT, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const size_t alds = (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride;
   const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs;
   for (int it = 0; it < a.iters; ++it) {
+    prof_begin(WI_STAGE_ASSIGN, st);
     hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, kAssignKeys), a.nseg, BG), dim3(256),
                        alds, st, a, it);
+    prof_end(WI_STAGE_ASSIGN, st);
+    prof_begin(WI_STAGE_RESCORE, st);
     hipLaunchKernelGGL(k_rescore<T>, dim3(1024), dim3(256), 0, st, a, it);
+    prof_end(WI_STAGE_RESCORE, st);
+    prof_begin(WI_STAGE_CSR, st);
     hipLaunchKernelGGL(k_csr, dim3(a.nseg, BG), dim3(kCsrThreads), clds, st, a);
-    if (it + 1 < a.iters)
+    prof_end(WI_STAGE_CSR, st);
+    if (it + 1 < a.iters) {
+      prof_begin(WI_STAGE_UPDATE, st);
       hipLaunchKernelGGL((k_sums<T, false>), dim3((unsigned)ceil_div(a.Cs, 8), a.nseg, BG), dim3(512), 0, st, a);
-    else
+      prof_end(WI_STAGE_UPDATE, st);
+    } else {
+      prof_begin(WI_STAGE_FINAL, st);
       hipLaunchKernelGGL((k_sums<T, true>), dim3((unsigned)ceil_div(a.Cs, 8), a.nseg, BG), dim3(512), 0, st, a);
+      prof_end(WI_STAGE_FINAL, st);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -660,24 +660,31 @@ static hipError_t launch_attend(const DecodeArgs& a, hipStream_t s, int grid) {
 template <typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
+  prof_begin(WI_STAGE_SCORE, s);
   hipLaunchKernelGGL(k_score<T>, dim3((unsigned)std::max<int64_t>(1, ceil_div(a.C, 128)), BG),
                      dim3(256), 0, s, a);
+  prof_end(WI_STAGE_SCORE, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool keys_in_lds = (size_t)a.C * 4 + (size_t)a.W32 * 4 <= 65536;
   const size_t dyn = (size_t)a.W32 * 4 + (keys_in_lds ? (size_t)a.C * 4 : 0);
+  prof_begin(WI_STAGE_SELECT, s);
   hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), dyn, s, a);
+  prof_end(WI_STAGE_SELECT, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_items = a.n_est + BG * a.max_chunks_g;
   const int grid = std::max(1, std::min(max_items, 2048));
+  prof_begin(WI_STAGE_ATTEND, s);
   switch (a.G) {
-    case 1: return launch_attend<T, 1>(a, s, grid);
-    case 2: return launch_attend<T, 2>(a, s, grid);
-    case 4: return launch_attend<T, 4>(a, s, grid);
-    case 8: return launch_attend<T, 8>(a, s, grid);
-    default: return hipErrorInvalidValue;
+    case 1: e = launch_attend<T, 1>(a, s, grid); break;
+    case 2: e = launch_attend<T, 2>(a, s, grid); break;
+    case 4: e = launch_attend<T, 4>(a, s, grid); break;
+    case 8: e = launch_attend<T, 8>(a, s, grid); break;
+    default: e = hipErrorInvalidValue;
   }
+  prof_end(WI_STAGE_ATTEND, s);
+  return e;
 }
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {

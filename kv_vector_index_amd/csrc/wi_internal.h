@@ -67,6 +67,12 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
 
+// ------------------------------------------------------------------ profiling hook
+extern bool g_prof_on;
+void prof_record(int stage, bool begin, hipStream_t s);
+inline void prof_begin(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, true, s); }
+inline void prof_end(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, false, s); }
+
 // ------------------------------------------------------------------ build workspace
 struct BuildLayout {
   int64_t C, Nc, NS, nseg, L;

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libwave_index.so")
 WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0, -1, -2, -3, -4
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode",
-            "wi_status_string", "wi_last_error")
+            "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
+STAGES = ("score", "select", "attend", "prep", "init", "assign", "rescore", "csr", "update", "final")
 
 
 class WaveIndexError(RuntimeError):
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.wi_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
                                 vp, vp, sz, vp]
         L.wi_status_string.argtypes = [ctypes.c_int]
+        L.wi_profile_enable.argtypes = [ctypes.c_int]
+        L.wi_profile_enable.restype = ctypes.c_int
+        L.wi_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode"):
             getattr(L, name).restype = ctypes.c_int
         L.wi_status_string.restype = ctypes.c_char_p
@@ -123,6 +128,19 @@ def wi_decode(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_pt
               sel_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_decode(ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr,
                                   sel_ptr, ws_ptr, ws_bytes, stream))
+
+
+def wi_profile_enable(enable: bool) -> int:
+    return _check(lib().wi_profile_enable(1 if enable else 0))
+
+
+def wi_profile_read() -> dict:
+    """{stage name: (total kernel ms, launches)} accumulated since wi_profile_enable(True)."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().wi_profile_read(ms, cnt))
+    return {STAGES[i]: (ms[i], cnt[i]) for i in range(n)}
 
 
 # ---------------------------------------------------------------------------- torch convenience

@@ -153,3 +153,47 @@ def test_decode_gqa_128k_bf16_full_size_sampled_heads():
     for h in range(w.Hq):
         ids = s[0, h][s[0, h] >= 0]
         assert ids.size == w.top_k and np.all(np.diff(ids) > 0) and np.all(sizes[0, h // G, ids] > 0)
+
+
+def test_decode_graph_replay_matches_eager():
+    """Decode steps captured in a HIP graph and replayed several times, with eager work and
+    synchronisations between replays, give the eager result every time (the kernels zero their
+    own counters, so nothing in the graph is a memset)."""
+    dev = device()
+    w = _small(B=2, Hq=8)
+    Kt, Vt, Qt, K64, V64, Q64 = inputs(w, 31, dev)
+    idx = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 2, w.dtype)
+    gi = upload_index(idx, w.dtype, dev)
+    q2 = (Qt.float() * 1.3).to(Qt.dtype)
+    p = wi.decode_params(gi, w.B, w.Hq, w.Hkv, w.top_k, Qt.dtype)
+    ws = torch.empty(wi.wi_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device=dev) for _ in range(2)]
+    lses = [torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev) for _ in range(2)]
+    sels = [torch.empty((w.B, w.Hq, w.top_k), dtype=torch.int32, device=dev) for _ in range(2)]
+    view = gi.view()
+
+    def steps():
+        for j, q in enumerate((Qt, q2)):
+            wi.wi_decode(p, view, q.data_ptr(), outs[j].data_ptr(), lses[j].data_ptr(), sels[j].data_ptr(),
+                         ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+
+    steps()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), l.clone(), s.clone()) for o, l, s in zip(outs, lses, sels)]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            steps()
+    torch.cuda.current_stream().wait_stream(st)
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        _ = (torch.randn(1000, device=dev) * 2).sum()     # eager work between replays
+        torch.cuda.synchronize()
+        for (o, l, s), (ro, rl, rs) in zip(zip(outs, lses, sels), ref):
+            assert torch.equal(s, rs)
+            assert torch.equal(o, ro) and torch.equal(l, rl)
