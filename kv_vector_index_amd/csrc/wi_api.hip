@@ -232,7 +232,7 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
     return fail(WI_ERR_UNSUPPORTED, "a buffer would exceed 2^31 rows");
   if (!idx->offsets || (p->n_steady > 0 && (!idx->k_steady || !idx->v_steady)))
     return fail(WI_ERR_INVALID_ARG, "index view has a null offsets or steady-zone pointer");
-  if (p->C > 0 && (!idx->centroids || !idx->value_sums || !idx->k_perm || !idx->v_perm))
+  if (p->C > 0 && (!idx->centroids || !idx->value_sums || !idx->sizes || !idx->k_perm || !idx->v_perm))
     return fail(WI_ERR_INVALID_ARG, "index view has a null pointer");
   if (sel_ids && p->top_k == 0) sel_ids = nullptr;
   const wi::DecodeLayout L = wi::decode_layout(*p);
@@ -242,7 +242,7 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
     return fail(WI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   wi::DecodeArgs a{};
-  a.mu = idx->centroids; a.sv = idx->value_sums; a.offsets = idx->offsets;
+  a.mu = idx->centroids; a.sv = idx->value_sums; a.offsets = idx->offsets; a.sizes = idx->sizes;
   a.k_perm = idx->k_perm; a.v_perm = idx->v_perm; a.k_steady = idx->k_steady; a.v_steady = idx->v_steady;
   a.q = q; a.out = out; a.lse = lse; a.sel_ids = sel_ids;
   char* base = static_cast<char*>(workspace);

@@ -131,53 +131,85 @@ __global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
 
 // ============================================================================ k_select
 constexpr int kSelThreads = 512;
+constexpr int kSmallBand = 64;      // bands up to one wave are resolved by direct ranking
 
-// Threshold key of the k-th largest of n keys (1 <= k <= n): after the call, exactly
-// k - *rem_out keys are strictly greater than the returned key and at least *rem_out are equal.
+// Radix bin of the k-th largest key: threads 0..255 own the bins in descending order, so an
+// inclusive scan over them gives suffix counts; the one bin with excl < rem <= incl is chosen.
+__device__ __forceinline__ void radix_pick(const uint32_t* hist, int rem, int* scr, int* out_bin,
+                                           int* out_above) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bin = 255 - tid;
+  const int v = tid < 256 ? (int)hist[bin] : 0;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63 && w < 4) scr[w] = inc;
+  __syncthreads();
+  if (tid < 256) {
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += scr[i];
+    const int incl = base + inc, excl = incl - v;
+    if (excl < rem && rem <= incl) { *out_bin = bin; *out_above = excl; }
+  }
+  __syncthreads();
+}
+
+// Threshold key of the k-th largest of n keys (1 <= k <= n): afterwards exactly k - *rem_out keys
+// are strictly greater than the returned key and at least *rem_out keys equal it.
 template <typename K, typename Get>
-__device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, K* shk, int* shi,
-                                int* rem_out) {
+__device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, int* scr, int* rem_out) {
   K prefix = 0, mask = 0;
   int rem = k;
   for (int shift = (int)sizeof(K) * 8 - 8; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const K key = get(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, sel = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        const int hb = (int)hist[bin];
-        if (cum + hb >= rem) { sel = bin; break; }
-        cum += hb;
-      }
-      shk[0] = prefix | ((K)sel << shift);
-      shi[0] = rem - cum;
-    }
-    __syncthreads();
-    prefix = shk[0];
-    rem = shi[0];
+    radix_pick(hist, rem, scr, scr + 8, scr + 9);
+    prefix |= (K)scr[8] << shift;
+    rem -= scr[9];
     mask |= (K)255 << shift;
-    __syncthreads();
   }
   *rem_out = rem;
   return prefix;
 }
 
+// Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
+// summed in ascending coordinate order, no contraction.  The row is fetched in four batches.
+template <typename T>
+__device__ __forceinline__ double canonical_score_row(const double* qd, const T* row) {
+#pragma clang fp contract(off)
+  double acc = 0.0;
+#pragma unroll 1
+  for (int j0 = 0; j0 < kD; j0 += 32) {
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 32; u += 8) {
+      float t[8];
+      St<T>::load8(row + j0 + u, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[u + e] = t[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const double p = qd[j0 + e] * (double)x[e];
+      acc = acc + p;
+    }
+  }
+  return acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
-  extern __shared__ uint32_t dyn[];           // selected-cluster bitmap [W32] (+ keys if cached)
+  extern __shared__ uint32_t dyn[];           // bitmap [W32], then keys [C] when they fit
   __shared__ uint32_t hist[256];
-  __shared__ int iscr[32];
+  __shared__ int iscr[48];
   __shared__ float fscr[32];
-  __shared__ uint64_t shk64[2];
-  __shared__ uint32_t shk32[2];
   __shared__ double qd[kD];
+  __shared__ int band_lds[kSmallBand];
 
-  const int tid = threadIdx.x, NT = blockDim.x;
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, bg = b * a.Hkv + g;
@@ -186,28 +218,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   const bool keys_in_lds = (size_t)C * 4 + (size_t)W32 * 4 <= 65536;
   uint32_t* keys = keys_in_lds ? dyn + W32 : a.keys32 + (size_t)bh * C;
   const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const int32_t* sizes = a.sizes + (size_t)bg * C;
   const float* sc = a.scores + (size_t)bh * C;
+  const float* mnorm = a.mu_norm + (size_t)bg * C;
   const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
 
-  // query norm (fp32) and the fp64 copy used for canonical rescoring
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
   const float qn = sqrtf(block_sum(qv * qv, fscr));
 
   for (int w = tid; w < W32; w += NT) bits[w] = 0u;
-  // order keys (0 = empty cluster), non-empty count, largest centroid norm
+  // order keys (0 marks an empty cluster), non-empty count, largest centroid norm
   int cnt = 0;
   float mxn = 0.f;
-  for (int c = tid; c < C; c += NT) {
-    const int sz = off[c + 1] - off[c];
-    uint32_t key = 0u;
-    if (sz > 0) {
-      ++cnt;
-      mxn = fmaxf(mxn, a.mu_norm[(size_t)bg * C + c]);
-      key = f32_order_key(sc[c]);
+  for (int base = tid; base < C; base += 4 * NT) {
+    int sz[4];
+    float s[4], nm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = base + u * NT;
+      sz[u] = 0; s[u] = 0.f; nm[u] = 0.f;
+      if (c < C) { sz[u] = sizes[c]; s[u] = sc[c]; nm[u] = mnorm[c]; }
     }
-    keys[c] = key;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = base + u * NT;
+      if (c < C) {
+        uint32_t key = 0u;
+        if (sz[u] > 0) { ++cnt; mxn = fmaxf(mxn, nm[u]); key = f32_order_key(s[u]); }
+        keys[c] = key;
+      }
+    }
   }
   const int n_ne = block_isum(cnt, iscr);
   mxn = block_max(mxn, fscr);
@@ -219,21 +261,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       if (keys[c] != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31));
   } else if (k_eff > 0) {
     int rem;
-    const uint32_t thr = block_radix_select<uint32_t>(
-        C, k_eff, [&](int i) { return keys[i]; }, hist, shk32, iscr, &rem);
-    // Certified band: |fp32 score - canonical fp64 score| <= delta for every cluster
-    // (fp32 accumulation of d exact-or-rounded products, times 2 for an unspecified MFMA order).
+    const uint32_t thr = block_radix_select<uint32_t>(C, k_eff, [&](int i) { return keys[i]; }, hist, iscr, &rem);
+    // Certified band: |fp32 score - canonical fp64 score| <= delta for every cluster (fp32
+    // accumulation of d exact-or-rounded products, doubled for an unspecified MFMA order).
     const double that = (double)f32_from_order_key(thr);
     const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qn * (1.0 + 1.0 / 1024) *
                              (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
-    // classify in id order: each thread owns a contiguous id range
     const int per = (C + NT - 1) / NT;
     const int c0 = min(C, tid * per), c1 = min(C, c0 + per);
     int nb = 0, nin = 0;
     for (int c = c0; c < c1; ++c) {
-      if (keys[c] == 0u) continue;
-      const double v = (double)sc[c];
+      const uint32_t key = keys[c];
+      if (key == 0u) continue;
+      const double v = (double)f32_from_order_key(key);
       if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
       else if (v >= lo) ++nb;
     }
@@ -241,36 +282,37 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     int pos = block_exclusive_scan(nb, iscr, &n_band);
     const int n_in = block_isum(nin, iscr);
     const int need = k_eff - n_in;
-    int32_t* band = a.band_ids + (size_t)bh * C;
+    int32_t* band = n_band <= kSmallBand ? band_lds : a.band_ids + (size_t)bh * C;
     for (int c = c0; c < c1; ++c) {
-      if (keys[c] == 0u) continue;
-      const double v = (double)sc[c];
+      const uint32_t key = keys[c];
+      if (key == 0u) continue;
+      const double v = (double)f32_from_order_key(key);
       if (!(v > hi) && v >= lo) band[pos++] = c;
     }
     __syncthreads();
     if (need >= n_band) {
       for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
-    } else if (need > 0) {
-      uint64_t* bkey = a.band_key + (size_t)bh * C;
-      for (int i = tid; i < n_band; i += NT) {
-        const int c = band[i];
-        // canonical score: exact products summed in fp64, ascending coordinate order
-        double acc = 0.0;
-        {
-#pragma clang fp contract(off)
-          const T* row = mu + (size_t)c * kD;
-          for (int j = 0; j < kD; ++j) {
-            const double p = qd[j] * (double)St<T>::f(row[j]);
-            acc = acc + p;
-          }
+    } else if (n_band <= kSmallBand) {
+      // one wave: rescore, then rank by (-sigma, id); the band is in ascending id order
+      if (wv == 0) {
+        const bool live = lane < n_band;
+        const int c = live ? band[lane] : 0;
+        const uint64_t key = live ? f64_order_key(canonical_score_row<T>(qd, mu + (size_t)c * kD)) : 0ull;
+        int rank = 0;
+        for (int j = 0; j < n_band; ++j) {
+          const uint64_t kj = __shfl(key, j);
+          rank += (kj > key) || (kj == key && j < lane);
         }
-        bkey[i] = f64_order_key(acc);
+        if (live && rank < need) atomicOr(&bits[c >> 5], 1u << (c & 31));
       }
+    } else {
+      uint64_t* bkey = a.band_key + (size_t)bh * C;
+      for (int i = tid; i < n_band; i += NT)
+        bkey[i] = f64_order_key(canonical_score_row<T>(qd, mu + (size_t)band[i] * kD));
       __syncthreads();
       int rem2;
-      const uint64_t t64 = block_radix_select<uint64_t>(
-          n_band, need, [&](int i) { return bkey[i]; }, hist, shk64, iscr, &rem2);
-      // keys above the threshold are in; among keys equal to it the lowest ids (band order) fill
+      const uint64_t t64 = block_radix_select<uint64_t>(n_band, need, [&](int i) { return bkey[i]; }, hist, iscr, &rem2);
+      // above the threshold: in; equal to it: the lowest ids (band order) fill the rest
       const int per2 = (n_band + NT - 1) / NT;
       const int i0 = min(n_band, tid * per2), i1 = min(n_band, i0 + per2);
       int neq = 0;
@@ -308,56 +350,69 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   // ---- the last query head of the KV group to arrive builds the group's work list
   __threadfence();
   __syncthreads();
-  if (tid == 0) iscr[20] = (atomicAdd(&a.counters[bg], 1u) == (uint32_t)(G - 1));
+  if (tid == 0) iscr[40] = (atomicAdd(&a.counters[bg], 1u) == (uint32_t)(G - 1));
   __syncthreads();
-  if (!iscr[20]) return;
+  if (!iscr[40]) return;
   __threadfence();
 
+  // union of the group's selections, in ascending cluster id, with a per-head mask (LDS list;
+  // the bitmap area is reused since this head's bits are already published)
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
   const int perw = (W32 + NT - 1) / NT;
   const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-  int ne = 0, nt = 0;
+  int ne = 0;
   for (int w = w0; w < w1; ++w) {
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) u |= __builtin_nontemporal_load(hb + (size_t)j * W32 + w);
+    for (int j = 0; j < G; ++j) u |= hb[(size_t)j * W32 + w];
     ne += __popc(u);
-    while (u) { const int bit = __ffs(u) - 1; u &= u - 1; const int c = w * 32 + bit; nt += off[c + 1] - off[c]; }
   }
-  int n_entries, n_utok;
+  int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
+  int32_t* ucid = reinterpret_cast<int32_t*>(dyn);                 // [Umax] (Umax <= C)
+  int32_t* umask = a.wl_mask + (size_t)bg * a.Umax;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t hw[kMaxGroup];
+    uint32_t u = 0u;
+    for (int j = 0; j < G; ++j) { hw[j] = hb[(size_t)j * W32 + w]; u |= hw[j]; }
+    while (u) {
+      const int bit = __ffs(u) - 1;
+      u &= u - 1;
+      int m = 0;
+      for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
+      if (keys_in_lds) ucid[e] = w * 32 + bit;
+      else a.band_ids[(size_t)bh * C + e] = w * 32 + bit;
+      umask[e] = m;
+      ++e;
+    }
+  }
+  __syncthreads();
+  const int32_t* cid = keys_in_lds ? ucid : a.band_ids + (size_t)bh * C;
+  // token prefix over the entries (contiguous entry range per thread)
+  const int pe = (n_entries + NT - 1) / NT;
+  const int e0 = min(n_entries, tid * pe), e1 = min(n_entries, e0 + pe);
+  int nt = 0;
+  for (int i = e0; i < e1; ++i) nt += sizes[cid[i]];
+  int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
   const int NS = a.NS;
   const int n_tok = NS + n_utok;
   int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
-  int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
   int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
   int32_t* ce0 = a.chunk_e0 + (size_t)bg * a.max_chunks_g;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t hw[kMaxGroup];
-    uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) { hw[j] = __builtin_nontemporal_load(hb + (size_t)j * W32 + w); u |= hw[j]; }
-    while (u) {
-      const int bit = __ffs(u) - 1;
-      u &= u - 1;
-      const int c = w * 32 + bit;
-      int m = 0;
-      for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
-      const int r0 = off[c], sz = off[c + 1] - r0;
-      const int start = NS + t;
-      row0[e] = r0;
-      msk[e] = m;
-      pre[e] = start;
-      // chunks whose first token falls inside this cluster's token range start at entry e
-      for (int j = (start + kChunkTokens - 1) / kChunkTokens; j * kChunkTokens < start + sz; ++j) ce0[j] = e;
-      ++e;
-      t += sz;
-    }
+  for (int i = e0; i < e1; ++i) {
+    const int c = cid[i];
+    const int r0 = off[c], sz = sizes[c];
+    const int start = NS + t;
+    row0[i] = r0;
+    pre[i] = start;
+    // chunks whose first token falls inside this cluster's token range start at entry i
+    for (int j = (start + kChunkTokens - 1) / kChunkTokens; j * kChunkTokens < start + sz; ++j) ce0[j] = i;
+    t += sz;
   }
+  const int n_chunks = (n_tok + kChunkTokens - 1) / kChunkTokens;
+  for (int j = tid; j * kChunkTokens < min(NS, n_tok); j += NT) ce0[j] = 0;   // chunks in the steady zone
   if (tid == 0) {
     pre[n_entries] = n_tok;
-    // chunks that start inside the steady zone begin with entry 0
-    for (int j = 0; j * kChunkTokens < min(NS, n_tok); ++j) ce0[j] = 0;
-    const int n_chunks = (n_tok + kChunkTokens - 1) / kChunkTokens;
     int32_t* gd = a.grp + (size_t)bg * 4;
     gd[0] = n_entries;
     gd[1] = n_tok;
@@ -367,20 +422,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __threadfence();
   __syncthreads();
   const int BG = a.B * a.Hkv;
-  if (tid == 0) iscr[21] = (atomicAdd(&a.counters[2 * BG], 1u) == (uint32_t)(BG - 1));
+  if (tid == 0) iscr[41] = (atomicAdd(&a.counters[2 * BG], 1u) == (uint32_t)(BG - 1));
   __syncthreads();
-  if (!iscr[21]) return;
+  if (!iscr[41]) return;
   __threadfence();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < BG; ++i) {
-      int32_t* gd = a.grp + (size_t)i * 4;
-      const int nc = __builtin_nontemporal_load(gd + 2);
-      gd[3] = run;
-      run += nc;
-    }
-    a.counters[2 * BG + 1] = (uint32_t)run;
-  }
+  const int pg = (BG + NT - 1) / NT;
+  const int g0 = min(BG, tid * pg), g1 = min(BG, g0 + pg);
+  int nc = 0;
+  for (int i = g0; i < g1; ++i) nc += a.grp[(size_t)i * 4 + 2];
+  int total;
+  int run = block_exclusive_scan(nc, iscr, &total);
+  for (int i = g0; i < g1; ++i) { a.grp[(size_t)i * 4 + 3] = run; run += a.grp[(size_t)i * 4 + 2]; }
+  if (tid == 0) a.counters[2 * BG + 1] = (uint32_t)total;
 }
 
 // ============================================================================ k_attend
@@ -468,7 +521,7 @@ __device__ void est_tile(const DecodeArgs& a, int bg, int tile, int slot, float*
                          float* sh_num, float* sh_den) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv, C = a.C;
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * C * kD;
   const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
   float l[8][G], v[8][8], wden[8];
@@ -477,7 +530,7 @@ __device__ void est_tile(const DecodeArgs& a, int bg, int tile, int slot, float*
     const int c = tile * kEstTile + w * 32 + 4 * i + rg;
     bool live = c < C;
     int sz = 0;
-    if (live) { sz = off[c + 1] - off[c]; live = sz > 0; }
+    if (live) { sz = szs[c]; live = sz > 0; }
     wden[i] = (float)sz;
     if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
     else for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
@@ -573,34 +626,123 @@ __device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int slot, floa
   finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
 }
 
+constexpr int kMergeF = 8192;        // LDS slots for the per-partial scale factors
+
+// Log-sum-exp merge of a KV group's partial softmax states (estimation tiles, then exact
+// chunks, in that fixed order) into out and lse.  M_h = max m_p over partials with den_p > 0;
+// den = sum f_p den_p, num = sum f_p num_p with f_p = exp(m_p - M_h).  Every phase is parallel
+// over partials so the group's tail is a few memory round trips.
 template <int G>
-__device__ void merge_group(const DecodeArgs& a, int bg) {
+__device__ void merge_group(const DecodeArgs& a, int bg, float* sh_f, float* sh_red) {
+  const int tid = threadIdx.x;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int32_t* gd = a.grp + (size_t)bg * 4;
-  const int n_chunks = __builtin_nontemporal_load(gd + 2), cbase = __builtin_nontemporal_load(gd + 3);
+  const int n_chunks = gd[2], cbase = gd[3];
   const int P = a.est_tiles_g + n_chunks;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kAttThreads) {
-    const int h = idx / kD, dd = idx - h * kD;
-    float M = -INFINITY;
-    for (int p = 0; p < P; ++p) {
-      const size_t slot = p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
-      const float den = __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2 + 1);
-      if (den > 0.f) M = fmaxf(M, __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2));
+  auto slot_of = [&](int p) -> size_t {
+    return p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
+  };
+  const bool f_in_lds = P * G <= kMergeF;
+  // phase 1: per-head maximum
+  float mx[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
+  for (int i = tid; i < P * G; i += kAttThreads) {
+    const int p = i / G, h = i - p * G;
+    const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
+    if (md.y > 0.f) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) if (hh == h) mx[hh] = fmaxf(mx[hh], md.x);
     }
-    float den = 0.f, num = 0.f;
-    for (int p = 0; p < P; ++p) {
-      const size_t slot = p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
-      const float dp = __builtin_nontemporal_load(a.part_md + (slot * G + h) * 2 + 1);
-      if (dp > 0.f) {
-        const float f = __expf(__builtin_nontemporal_load(a.part_md + (slot * G + h) * 2) - M);
-        den += f * dp;
-        num += f * __builtin_nontemporal_load(a.part_num + (slot * G + h) * kD + dd);
-      }
-    }
-    const size_t oh = (size_t)b * a.Hq + (size_t)g * G + h;
-    a.out[oh * kD + dd] = num / den;
-    if (dd == 0 && a.lse) a.lse[oh] = M + __logf(den);
   }
+  float M[G], den[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = block_max(mx[h], sh_red);
+  // phase 2: scale factors and denominators
+  float dn[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) dn[h] = 0.f;
+  for (int i = tid; i < P * G; i += kAttThreads) {
+    const int p = i / G, h = i - p * G;
+    const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
+    float Mh = M[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) if (hh == h) Mh = M[hh];
+    const float f = md.y > 0.f ? __expf(md.x - Mh) : 0.f;
+    if (f_in_lds) sh_f[i] = f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) if (hh == h) dn[hh] += f * md.y;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) den[h] = block_sum(dn[h], sh_red);
+  __syncthreads();
+  // phase 3: numerators; a column is two dims of one head, replicas split the partials
+  constexpr int NCOL = G * 64;
+  constexpr int R = NCOL >= kAttThreads ? 1 : kAttThreads / NCOL;
+  constexpr int CPT = NCOL >= kAttThreads ? NCOL / kAttThreads : 1;
+  const int rep = tid / (kAttThreads / R);
+  float2 acc[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) acc[q] = make_float2(0.f, 0.f);
+  for (int p0 = rep; p0 < P; p0 += 16 * R) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int col = (tid % (kAttThreads / R)) + q * kAttThreads;
+      const int h = col >> 6, d2 = (col & 63) * 2;
+      float2 v[16];
+      float f[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int p = p0 + u * R;
+        v[u] = make_float2(0.f, 0.f);
+        f[u] = 0.f;
+        if (p < P) {
+          v[u] = *reinterpret_cast<const float2*>(a.part_num + (slot_of(p) * G + h) * kD + d2);
+          if (f_in_lds) f[u] = sh_f[p * G + h];
+          else {
+            const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
+            float Mh = M[0];
+#pragma unroll
+            for (int hh = 1; hh < G; ++hh) if (hh == h) Mh = M[hh];
+            f[u] = md.y > 0.f ? __expf(md.x - Mh) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) { acc[q].x += f[u] * v[u].x; acc[q].y += f[u] * v[u].y; }
+    }
+  }
+  if (R > 1) {
+    __syncthreads();   // every replica has finished reading the factors in sh_f
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int col = (tid % (kAttThreads / R)) + q * kAttThreads;
+      sh_f[rep * NCOL * 2 + col * 2] = acc[q].x;
+      sh_f[rep * NCOL * 2 + col * 2 + 1] = acc[q].y;
+    }
+    __syncthreads();
+  }
+  if (rep == 0) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int col = tid + q * kAttThreads;
+      float2 s = acc[q];
+      for (int r = 1; r < R; ++r) { s.x += sh_f[r * NCOL * 2 + col * 2]; s.y += sh_f[r * NCOL * 2 + col * 2 + 1]; }
+      const int h = col >> 6, d2 = (col & 63) * 2;
+      float dh = den[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) if (hh == h) dh = den[hh];
+      const size_t oh = (size_t)b * a.Hq + (size_t)g * G + h;
+      *reinterpret_cast<float2*>(a.out + oh * kD + d2) = make_float2(s.x / dh, s.y / dh);
+    }
+  }
+  if (tid < G && a.lse) {
+    float Mh = M[0], dh = den[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) if (hh == tid) { Mh = M[hh]; dh = den[hh]; }
+    a.lse[(size_t)b * a.Hq + (size_t)g * G + tid] = Mh + __logf(dh);
+  }
+  __syncthreads();
 }
 
 template <typename T, int G>
@@ -612,6 +754,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ int sh_mask[kChunkTokens];
   __shared__ int sh_flag;
   __shared__ int sh_base[kMaxGroupsPerDecode];
+  __shared__ float sh_f[kMergeF];
+  __shared__ float sh_red[32];
   const int BG = a.B * a.Hkv;
   const int total = (int)__builtin_nontemporal_load(a.counters + 2 * BG + 1);
   for (int i = threadIdx.x; i < BG; i += kAttThreads) sh_base[i] = a.grp[(size_t)i * 4 + 3];
@@ -644,7 +788,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     __syncthreads();
     if (sh_flag) {
       __threadfence();
-      merge_group<G>(a, bg);
+      merge_group<G>(a, bg, sh_f, sh_red);
     }
     __syncthreads();
   }

@@ -37,6 +37,7 @@ struct DecodeArgs {
   const void* mu;          // [BG, C, d]
   const void* sv;          // [BG, C, d]
   const int32_t* offsets;  // [BG, C+1]
+  const int32_t* sizes;    // [BG, C]
   const void* k_perm;      // [BG, Nc, d]
   const void* v_perm;
   const void* k_steady;    // [BG, NS, d]
