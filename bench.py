@@ -34,7 +34,8 @@ METRIC = "wave-index decode steps/s at 128K ctx (batch·heads); achieved HBM GB/
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_MFMA_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_gqa_128k_bf16.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa_128k_bf16.json")
+KERNEL_NAMES = {"score": "k_score_est", "select": "k_select+k_union", "attend": "k_attend", "merge": "k_merge"}
 
 
 def log(*a):
@@ -47,15 +48,19 @@ def decode_kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(w, idx_offsets_np, sel_np):
-    """Bytes the method must touch per step: index rows read once (mu, SV, offsets, steady rows,
-    union of the rows retrieved by a KV group's query heads), queries, outputs."""
+    """Bytes each decode kernel must move per step (every byte counted once):
+      score  : centroids, value sums and sizes of every cluster, queries
+      select : the retrieved ids it writes
+      attend : steady rows, the union of the rows retrieved by a KV group's query heads, and the
+               value sum of each retrieved cluster (for its estimation term)
+      merge  : outputs and lse"""
     import numpy as np
     e = 2 if w.dtype == "bf16" else 4
     d = w.d
     G = w.Hq // w.Hkv
     C = idx_offsets_np.shape[-1] - 1
     NS = min(w.N, w.sink + w.window)
-    per = {"score": 0, "attend": 0, "select": 0}
+    per = {"score": 0, "select": 0, "attend": 0, "merge": 0}
     union_rows = 0
     for b in range(w.B):
         for g in range(w.Hkv):
@@ -64,12 +69,11 @@ def algorithmic_bytes(w, idx_offsets_np, sel_np):
             ids = ids[ids >= 0]
             u = int((off[ids + 1] - off[ids]).sum())
             union_rows += u
-            per["score"] += C * d * e                       # centroids
-            per["select"] += 4 * (C + 1)                    # offsets (cluster sizes)
-            per["attend"] += C * d * e + 4 * (C + 1) + NS * 2 * d * e + u * 2 * d * e
-    per["score"] += w.B * w.Hq * d * e                      # queries
-    per["attend"] += w.B * w.Hq * (4 * d + 4)               # outputs + lse
-    per["select"] += w.B * w.Hq * w.top_k * 4               # selected ids
+            per["score"] += C * (2 * d * e + 4)
+            per["attend"] += NS * 2 * d * e + u * 2 * d * e + ids.size * (d * e + 4)
+    per["score"] += w.B * w.Hq * d * e
+    per["select"] += w.B * w.Hq * w.top_k * 4
+    per["merge"] += w.B * w.Hq * (4 * d + 4)
     return per, union_rows
 
 
@@ -262,16 +266,16 @@ def main():
     stages = wi.wi_profile_read()
     wi.wi_profile_enable(False)
     del a
-    avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items() if k in ("score", "select", "attend")}
-    attend_s = avg_ms["attend"] / 1e3
-    achieved = per_bytes["attend"] / attend_s / 1e9
+    avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items() if k in ("score", "select", "attend", "merge")}
+    dominant = max(("score", "attend"), key=lambda k: avg_ms[k] or 0.0)
+    achieved = {k: per_bytes[k] / (avg_ms[k] / 1e3) / 1e9 for k in ("score", "attend") if avg_ms[k]}
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha256_16") == decode_kernel_source_hash():
-            traffic = tr.get("hbm_bytes_per_launch")
+            traffic = tr.get("hbm_bytes_per_launch", {}).get(dominant)
 
     result = {
         "metric": METRIC,
@@ -297,9 +301,10 @@ def main():
         "retrieved_union_rows": union_rows,
         "kernel_avg_us": {k: (v * 1e3 if v is not None else None) for k, v in avg_ms.items()},
         "kernel_algorithmic_bytes": per_bytes,
-        "roofline": {"kernel": "k_attend", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+        "roofline": {"kernel": KERNEL_NAMES[dominant], "bound": "hbm", "achieved": achieved[dominant],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved[dominant] / HBM_PEAK_GBPS,
                      "traffic": traffic},
+        "kernel_hbm_gbps": achieved,
         "build": {"ms": build_ms,
                   "stage_ms": {k: v[0] for k, v in build_stages.items() if v[1]},
                   "assign_tflops": assign_flops / (assign_ms / 1e3) / 1e12 if assign_ms else None,

@@ -142,18 +142,20 @@ wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const v
 
 /* Stages timed by the profiling hook below (one entry per kernel of the two entry points). */
 typedef enum {
-  WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA)                          */
+  WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA) and the estimation over all
+                             non-empty clusters                                              */
   WI_STAGE_SELECT = 1,    /* decode: per-head top-k and the per-group work lists            */
-  WI_STAGE_ATTEND = 2,    /* decode: exact attention over steady + retrieved rows,
-                             estimation over the other clusters, log-sum-exp merge          */
-  WI_STAGE_PREP = 3,      /* build: steady-zone copies, key norms                           */
-  WI_STAGE_INIT = 4,      /* build: seeded initial centroid directions                      */
-  WI_STAGE_ASSIGN = 5,    /* build: k-means assignment (MFMA), all iterations               */
-  WI_STAGE_RESCORE = 6,   /* build: fp64 re-decision of uncertain assignments               */
-  WI_STAGE_CSR = 7,       /* build: sizes, offsets, permutation                             */
-  WI_STAGE_UPDATE = 8,    /* build: centroid directions from member sums                    */
-  WI_STAGE_FINAL = 9,     /* build: mean keys, value sums, cluster-major copies             */
-  WI_NUM_STAGES = 10
+  WI_STAGE_ATTEND = 2,    /* decode: exact attention over steady + retrieved rows and the
+                             retrieved clusters' estimation terms                            */
+  WI_STAGE_MERGE = 3,     /* decode: log-sum-exp merge into out and lse                      */
+  WI_STAGE_PREP = 4,      /* build: steady-zone copies, key norms                           */
+  WI_STAGE_INIT = 5,      /* build: seeded initial centroid directions                      */
+  WI_STAGE_ASSIGN = 6,    /* build: k-means assignment (MFMA), all iterations               */
+  WI_STAGE_RESCORE = 7,   /* build: fp64 re-decision of uncertain assignments               */
+  WI_STAGE_CSR = 8,       /* build: sizes, offsets, permutation                             */
+  WI_STAGE_UPDATE = 9,    /* build: centroid directions from member sums                    */
+  WI_STAGE_FINAL = 10,    /* build: mean keys, value sums, cluster-major copies             */
+  WI_NUM_STAGES = 11
 } wi_stage;
 
 /* (host) Profiling hook for measurement tools.  While enabled, wi_decode and wi_build_index

@@ -1,4 +1,5 @@
-// Wave-index decode step on gfx950: score -> select -> exact attention + estimation -> LSE merge.
+// Wave-index decode step on gfx950: score + estimate -> select -> work lists -> exact attention
+// -> LSE merge.
 //
 // Method: RetroInfer's tripartite attention (technical summary, gist.science Spanish page,
 // section 2.A items 1-3; Arabic page section 2.a).  Per query head, the steady zone (sinks and
@@ -7,39 +8,69 @@
 // denominator and n_c * exp(s_c) * SV_c / n_c to the numerator; the partial softmax states are
 // merged with log-sum-exp.
 //
-// Kernels (one stream, in order):
-//   k_score   grid (ceil(C/128), B*Hkv): MFMA product of the group's query heads with 128
-//             centroids per block; writes fp32 scores and fp32 centroid norms.  One pass over mu
-//             per KV head serves all of its query heads.
-//   k_select  grid (B*Hq): exact top-k per head.  Radix select over the fp32 scores finds the
-//             k-th value; every cluster whose fp32 score lies within the certified error band of
-//             it is re-scored with the canonical fp64 sum, and the set is completed by
-//             (-sigma, id).  The last head of a KV group to finish builds the group's union work
-//             list (cluster rows with a per-head mask, token prefix sums, chunk starts); the last
-//             group sets the global chunk numbering.
-//   k_attend  persistent grid: work items are estimation tiles (128 clusters) and exact-attention
-//             chunks (128 tokens of steady + retrieved rows, loaded once per KV group and shared
-//             by its query heads).  Each item writes one partial softmax state per head; the last
-//             item of a KV group merges that group's partials into out and lse.
+// The estimation is computed over *all* non-empty clusters in the same pass that scores them
+// (mu and SV stream together, before the selection is known), and the terms of the retrieved
+// clusters are subtracted at the merge: sum over E = sum over all - sum over R.  The subtracted
+// terms never exceed the exact mass of the same tokens (exp is convex, so n_c exp(mean logit) is
+// at most the sum of the members' exp(logit)), so the cancellation costs O(eps_fp32) relative to
+// the merged denominator.  When a head retrieves every non-empty cluster both terms are dropped.
+//
+// Kernels (one stream, in order; no kernel waits on another block of its own grid):
+//   k_score_est  grid (ceil(C/128), B*Hkv): MFMA scores of the KV group's query heads against 128
+//                centroids (one pass over mu serves all heads of the group), fp32 centroid norms,
+//                and the tile's estimation partial per head from SV and the sizes.
+//   k_select     grid (B*Hq): exact top-k per head (radix select on the fp32 scores, canonical
+//                fp64 re-scoring of the certified uncertainty band, ties to the lower id).
+//   k_union      grid (B*Hkv): union of the group's selections with a per-head mask, token
+//                prefix sums and chunk starts.
+//   k_attend     grid (S, B*Hkv): per KV group, items are 128-token chunks of steady + retrieved
+//                rows (each row loaded once and used by every head of the group that selected
+//                it) and 128-entry correction items (the retrieved clusters' estimation terms).
+//   k_merge      grid (B*Hq): log-sum-exp merge of the head's partials into out and lse.
 #include "wi_device.h"
 #include "wi_internal.h"
 
 namespace wi {
 
-// ============================================================================ k_score
-template <typename T>
-__global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
-  const int bg = blockIdx.y;
+constexpr int kScoreThreads = 256;
+
+// ============================================================================ k_score_est
+template <typename T, int G>
+__global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
+  __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
+  __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
+  __shared__ float sh_n[kEstTile];          // cluster sizes
+  __shared__ float sh_m[G], sh_den[G];
+  __shared__ float sh_num[4][G][kD];
+  const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int G = a.G, C = a.C;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0u;
-  if (C == 0) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int C = a.C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int cbase = blockIdx.x * 128 + w * 32;
+  const int cbase = tile * kEstTile + w * 32;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
+  const T* sv = static_cast<const T*>(a.sv) + ((size_t)bg * C + (size_t)tile * kEstTile) * kD;
+  const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+  const int nrows = min(kEstTile, C - tile * kEstTile);
+
+  // value sums of the tile: thread (w, lane) owns rows w + 4i and dims 2*lane, 2*lane+1.  The
+  // loads are issued first; they do not depend on the scores.
+  float2 svv[kEstTile / 4];
+#pragma unroll
+  for (int i = 0; i < kEstTile / 4; ++i) {
+    const int r = w + 4 * i;
+    svv[i] = make_float2(0.f, 0.f);
+    if (r < nrows) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + (size_t)r * kD + 2 * lane);
+        svv[i] = make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+      } else {
+        svv[i] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sv) + (size_t)r * kD + 2 * lane);
+      }
+    }
+  }
+  if (tid < kEstTile) sh_n[tid] = tid < nrows ? (float)szs[tile * kEstTile + tid] : 0.f;
 
   if constexpr (sizeof(T) == 2) {
     // A = query heads (row = lane&15), B = centroids (column = lane&15).  Along k, lane group lg
@@ -54,7 +85,9 @@ __global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
     for (int t = 0; t < 2; ++t) {
       const int c = cbase + 16 * t + lr;
       bf16x8_t mb[4];
+      int sz = 0;
       if (c < C) {
+        sz = szs[c];
         const T* row = mu + (size_t)c * kD + 32 * lg;
 #pragma unroll
         for (int s = 0; s < 4; ++s) mb[s] = *reinterpret_cast<const bf16x8_t*>(row + 8 * s);
@@ -72,14 +105,16 @@ __global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) { const float x = (float)mb[s][e]; n2 += x * x; }
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
-      if (c < C) {
+      const int cl = w * 32 + 16 * t + lr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * lg + r;
-          if (h < G) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * lg + r;
+        if (h < G) {
+          if (c < C) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+          sh_s[h][cl] = (c < C && sz > 0) ? acc[r] * a.scale : -INFINITY;
         }
-        if (lg == 0) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
       }
+      if (lg == 0 && c < C) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
     }
   } else {
     // fp32: 16x16x4 MFMA, 32 steps; step s consumes dim 32*lg + s on both operands.
@@ -96,7 +131,9 @@ __global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
     for (int t = 0; t < 2; ++t) {
       const int c = cbase + 16 * t + lr;
       float mb[32];
+      int sz = 0;
       if (c < C) {
+        sz = szs[c];
         const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 32 * lg;
 #pragma unroll
         for (int s = 0; s < 32; s += 8) {
@@ -117,15 +154,59 @@ __global__ __launch_bounds__(256) void k_score(DecodeArgs a) {
       for (int s = 0; s < 32; ++s) n2 += mb[s] * mb[s];
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
-      if (c < C) {
+      const int cl = w * 32 + 16 * t + lr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * lg + r;
-          if (h < G) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * lg + r;
+        if (h < G) {
+          if (c < C) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+          sh_s[h][cl] = (c < C && sz > 0) ? acc[r] * a.scale : -INFINITY;
         }
-        if (lg == 0) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
       }
+      if (lg == 0 && c < C) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
     }
+  }
+  __syncthreads();
+
+  // estimation partial of the tile: m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
+  for (int h = w; h < G; h += kScoreThreads / 64) {
+    const float x0 = sh_s[h][lane], x1 = sh_s[h][lane + 64];
+    const float m = wave_max(fmaxf(x0, x1));
+    const float w0 = x0 == -INFINITY ? 0.f : __expf(x0 - m);
+    const float w1 = x1 == -INFINITY ? 0.f : __expf(x1 - m);
+    sh_w[h][lane] = w0;
+    sh_w[h][lane + 64] = w1;
+    const float dn = wave_sum(w0 * sh_n[lane] + w1 * sh_n[lane + 64]);
+    if (lane == 0) { sh_m[h] = m; sh_den[h] = dn; }
+  }
+  __syncthreads();
+  float2 acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kEstTile / 4; ++i) {
+    const int r = w + 4 * i;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float wt = sh_w[h][r];
+      acc[h].x += wt * svv[i].x;
+      acc[h].y += wt * svv[i].y;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    sh_num[w][h][2 * lane] = acc[h].x;
+    sh_num[w][h][2 * lane + 1] = acc[h].y;
+  }
+  __syncthreads();
+  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
+  for (int i = tid; i < G * kD; i += kScoreThreads) {
+    const int h = i / kD, d = i - h * kD;
+    a.est_num[(slot * G + h) * kD + d] = sh_num[0][h][d] + sh_num[1][h][d] + sh_num[2][h][d] + sh_num[3][h][d];
+  }
+  if (tid < G) {
+    a.est_md[(slot * G + tid) * 2] = sh_m[tid];
+    a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
   }
 }
 
@@ -347,17 +428,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
   }
 
-  // ---- the last query head of the KV group to arrive builds the group's work list
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) iscr[40] = (atomicAdd(&a.counters[bg], 1u) == (uint32_t)(G - 1));
-  __syncthreads();
-  if (!iscr[40]) return;
-  __threadfence();
+  if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
+}
 
-  // union of the group's selections, in ascending cluster id, with a per-head mask (LDS list;
-  // the bitmap area is reused since this head's bits are already published)
+// ============================================================================ k_union
+constexpr int kUnionThreads = 512;
+constexpr int kUnionLds = 4096;
+
+// Union of the selections of a KV group's query heads, in ascending cluster id, with the mask of
+// the heads that selected each cluster; token prefix sums (the steady zone first) and the first
+// entry of every 128-token chunk.
+__global__ __launch_bounds__(kUnionThreads) void k_union(DecodeArgs a) {
+  __shared__ int iscr[48];
+  __shared__ int ucid_lds[kUnionLds];
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int bg = blockIdx.x;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int G = a.G, C = a.C, W32 = a.W32;
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const int32_t* sizes = a.sizes + (size_t)bg * C;
+  int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
+  int32_t* ucid = a.Umax <= kUnionLds ? ucid_lds : cidg;
+  int32_t* umask = a.wl_mask + (size_t)bg * a.Umax;
   const int perw = (W32 + NT - 1) / NT;
   const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
   int ne = 0;
@@ -368,8 +461,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
-  int32_t* ucid = reinterpret_cast<int32_t*>(dyn);                 // [Umax] (Umax <= C)
-  int32_t* umask = a.wl_mask + (size_t)bg * a.Umax;
   for (int w = w0; w < w1; ++w) {
     uint32_t hw[kMaxGroup];
     uint32_t u = 0u;
@@ -379,19 +470,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       u &= u - 1;
       int m = 0;
       for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
-      if (keys_in_lds) ucid[e] = w * 32 + bit;
-      else a.band_ids[(size_t)bh * C + e] = w * 32 + bit;
+      ucid[e] = w * 32 + bit;
       umask[e] = m;
       ++e;
     }
   }
   __syncthreads();
-  const int32_t* cid = keys_in_lds ? ucid : a.band_ids + (size_t)bh * C;
-  // token prefix over the entries (contiguous entry range per thread)
   const int pe = (n_entries + NT - 1) / NT;
   const int e0 = min(n_entries, tid * pe), e1 = min(n_entries, e0 + pe);
   int nt = 0;
-  for (int i = e0; i < e1; ++i) nt += sizes[cid[i]];
+  for (int i = e0; i < e1; ++i) nt += sizes[ucid[i]];
   int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
   const int NS = a.NS;
@@ -400,51 +488,37 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
   int32_t* ce0 = a.chunk_e0 + (size_t)bg * a.max_chunks_g;
   for (int i = e0; i < e1; ++i) {
-    const int c = cid[i];
+    const int c = ucid[i];
     const int r0 = off[c], sz = sizes[c];
     const int start = NS + t;
     row0[i] = r0;
     pre[i] = start;
+    if (ucid != cidg) cidg[i] = c;
     // chunks whose first token falls inside this cluster's token range start at entry i
     for (int j = (start + kChunkTokens - 1) / kChunkTokens; j * kChunkTokens < start + sz; ++j) ce0[j] = i;
     t += sz;
   }
-  const int n_chunks = (n_tok + kChunkTokens - 1) / kChunkTokens;
   for (int j = tid; j * kChunkTokens < min(NS, n_tok); j += NT) ce0[j] = 0;   // chunks in the steady zone
   if (tid == 0) {
     pre[n_entries] = n_tok;
     int32_t* gd = a.grp + (size_t)bg * 4;
     gd[0] = n_entries;
     gd[1] = n_tok;
-    gd[2] = n_chunks;
+    gd[2] = (n_tok + kChunkTokens - 1) / kChunkTokens;
+    gd[3] = (n_entries + kEstTile - 1) / kEstTile;
   }
-  // ---- the last group to arrive numbers every group's chunks
-  __threadfence();
-  __syncthreads();
-  const int BG = a.B * a.Hkv;
-  if (tid == 0) iscr[41] = (atomicAdd(&a.counters[2 * BG], 1u) == (uint32_t)(BG - 1));
-  __syncthreads();
-  if (!iscr[41]) return;
-  __threadfence();
-  const int pg = (BG + NT - 1) / NT;
-  const int g0 = min(BG, tid * pg), g1 = min(BG, g0 + pg);
-  int nc = 0;
-  for (int i = g0; i < g1; ++i) nc += a.grp[(size_t)i * 4 + 2];
-  int total;
-  int run = block_exclusive_scan(nc, iscr, &total);
-  for (int i = g0; i < g1; ++i) { a.grp[(size_t)i * 4 + 3] = run; run += a.grp[(size_t)i * 4 + 2]; }
-  if (tid == 0) a.counters[2 * BG + 1] = (uint32_t)total;
 }
 
 // ============================================================================ k_attend
 constexpr int kAttThreads = 256;
 
 // Rows of a work item: wave w owns rows w*32 + 4*i + (lane>>4), i = 0..7; lane&15 owns dims
-// [8*(lane&15), +8).  Given per-row logits (identical across the 16 lanes of a row) and the row
-// values, form the item's partial softmax state per head and write it to `slot`.
+// [8*(lane&15), +8).  Given per-row logits (identical across the 16 lanes of a row), the row
+// values and a per-row weight of the denominator, form the item's partial softmax state per head
+// (max logit m, den = sum wden e^(l-m), num = sum e^(l-m) v) and write it to `slot`.
 template <int G>
 __device__ __forceinline__ void finish_partial(const float (&l)[8][G], const float (&v)[8][8],
-                                               const float (&wden)[8], int slot, const DecodeArgs& a,
+                                               const float (&wden)[8], size_t slot, const DecodeArgs& a,
                                                float* sh_m, float* sh_num, float* sh_den) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15;
   float M[G];
@@ -500,7 +574,7 @@ __device__ __forceinline__ void finish_partial(const float (&l)[8][G], const flo
     }
   }
   __syncthreads();
-  float* pn = a.part_num + (size_t)slot * G * kD;
+  float* pn = a.att_num + slot * G * kD;
   for (int i = threadIdx.x; i < G * kD; i += kAttThreads) {
     float s = 0.f;
     for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_num[ww * G * kD + i];
@@ -510,51 +584,48 @@ __device__ __forceinline__ void finish_partial(const float (&l)[8][G], const flo
     const int hh = threadIdx.x;
     float s = 0.f;
     for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_den[ww * G + hh];
-    a.part_md[((size_t)slot * G + hh) * 2 + 0] = M[hh];
-    a.part_md[((size_t)slot * G + hh) * 2 + 1] = s;
+    a.att_md[(slot * G + hh) * 2 + 0] = M[hh];
+    a.att_md[(slot * G + hh) * 2 + 1] = s;
   }
   __syncthreads();
 }
 
+// The estimation terms of the retrieved clusters (entries [128 ci, 128 ci + 128) of the group's
+// union list), for the heads that retrieved each one; the merge subtracts them.
 template <typename T, int G>
-__device__ void est_tile(const DecodeArgs& a, int bg, int tile, int slot, float* sh_m,
-                         float* sh_num, float* sh_den) {
+__device__ void corr_item(const DecodeArgs& a, int bg, int ci, int n_entries, size_t slot,
+                          float* sh_m, float* sh_num, float* sh_den) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv, C = a.C;
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * C * kD;
+  const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
+  const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
   const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
   float l[8][G], v[8][8], wden[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = tile * kEstTile + w * 32 + 4 * i + rg;
-    bool live = c < C;
-    int sz = 0;
-    if (live) { sz = szs[c]; live = sz > 0; }
-    wden[i] = (float)sz;
+    const int e = ci * kEstTile + w * 32 + 4 * i + rg;
+    const bool live = e < n_entries;
+    const int c = live ? cid[e] : 0;
+    const int m = live ? msk[e] : 0;
+    wden[i] = live ? (float)szs[c] : 0.f;
     if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
-    else for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    else for (int x = 0; x < 8; ++x) v[i][x] = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = -INFINITY;
-      if (live) {
-        const uint32_t sel = a.sel_bits[(hbase + h) * a.W32 + (c >> 5)];
-        if (!((sel >> (c & 31)) & 1u)) x = a.scores[(hbase + h) * C + c] * a.scale;
-      }
-      l[i][h] = x;
-    }
+    for (int h = 0; h < G; ++h)
+      l[i][h] = ((m >> h) & 1) ? a.scores[(hbase + h) * C + c] * a.scale : -INFINITY;
   }
   finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
 }
 
 template <typename T, int G>
-__device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int slot, float* sh_m,
-                             float* sh_num, float* sh_den, int* sh_row, int* sh_mask) {
+__device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int n_entries, int n_tok,
+                             size_t slot, float* sh_m, float* sh_num, float* sh_den, int* sh_row,
+                             int* sh_mask) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int NS = a.NS;
-  const int32_t* gd = a.grp + (size_t)bg * 4;
-  const int n_entries = gd[0], n_tok = gd[1];
   const int t0 = jl * kChunkTokens;
   const int t1 = min(n_tok, t0 + kChunkTokens);
   const int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
@@ -563,8 +634,6 @@ __device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int slot, floa
   const int e0 = a.chunk_e0[(size_t)bg * a.max_chunks_g + jl];
 
   // token -> (row, head mask); row >= 0 indexes k_perm, row < 0 is steady row (-1 - row)
-  for (int i = threadIdx.x; i < kChunkTokens; i += kAttThreads) { sh_row[i] = 0; sh_mask[i] = 0; }
-  __syncthreads();
   for (int t = t0 + threadIdx.x; t < min(t1, NS); t += kAttThreads) {
     sh_row[t - t0] = -1 - t;
     sh_mask[t - t0] = (1 << G) - 1;
@@ -626,125 +695,6 @@ __device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int slot, floa
   finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
 }
 
-constexpr int kMergeF = 8192;        // LDS slots for the per-partial scale factors
-
-// Log-sum-exp merge of a KV group's partial softmax states (estimation tiles, then exact
-// chunks, in that fixed order) into out and lse.  M_h = max m_p over partials with den_p > 0;
-// den = sum f_p den_p, num = sum f_p num_p with f_p = exp(m_p - M_h).  Every phase is parallel
-// over partials so the group's tail is a few memory round trips.
-template <int G>
-__device__ void merge_group(const DecodeArgs& a, int bg, float* sh_f, float* sh_red) {
-  const int tid = threadIdx.x;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int32_t* gd = a.grp + (size_t)bg * 4;
-  const int n_chunks = gd[2], cbase = gd[3];
-  const int P = a.est_tiles_g + n_chunks;
-  auto slot_of = [&](int p) -> size_t {
-    return p < a.est_tiles_g ? (size_t)bg * a.est_tiles_g + p : (size_t)a.n_est + cbase + (p - a.est_tiles_g);
-  };
-  const bool f_in_lds = P * G <= kMergeF;
-  // phase 1: per-head maximum
-  float mx[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
-  for (int i = tid; i < P * G; i += kAttThreads) {
-    const int p = i / G, h = i - p * G;
-    const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
-    if (md.y > 0.f) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) if (hh == h) mx[hh] = fmaxf(mx[hh], md.x);
-    }
-  }
-  float M[G], den[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = block_max(mx[h], sh_red);
-  // phase 2: scale factors and denominators
-  float dn[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) dn[h] = 0.f;
-  for (int i = tid; i < P * G; i += kAttThreads) {
-    const int p = i / G, h = i - p * G;
-    const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
-    float Mh = M[0];
-#pragma unroll
-    for (int hh = 1; hh < G; ++hh) if (hh == h) Mh = M[hh];
-    const float f = md.y > 0.f ? __expf(md.x - Mh) : 0.f;
-    if (f_in_lds) sh_f[i] = f;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) if (hh == h) dn[hh] += f * md.y;
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) den[h] = block_sum(dn[h], sh_red);
-  __syncthreads();
-  // phase 3: numerators; a column is two dims of one head, replicas split the partials
-  constexpr int NCOL = G * 64;
-  constexpr int R = NCOL >= kAttThreads ? 1 : kAttThreads / NCOL;
-  constexpr int CPT = NCOL >= kAttThreads ? NCOL / kAttThreads : 1;
-  const int rep = tid / (kAttThreads / R);
-  float2 acc[CPT];
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) acc[q] = make_float2(0.f, 0.f);
-  for (int p0 = rep; p0 < P; p0 += 16 * R) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int col = (tid % (kAttThreads / R)) + q * kAttThreads;
-      const int h = col >> 6, d2 = (col & 63) * 2;
-      float2 v[16];
-      float f[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int p = p0 + u * R;
-        v[u] = make_float2(0.f, 0.f);
-        f[u] = 0.f;
-        if (p < P) {
-          v[u] = *reinterpret_cast<const float2*>(a.part_num + (slot_of(p) * G + h) * kD + d2);
-          if (f_in_lds) f[u] = sh_f[p * G + h];
-          else {
-            const float2 md = *reinterpret_cast<const float2*>(a.part_md + (slot_of(p) * G + h) * 2);
-            float Mh = M[0];
-#pragma unroll
-            for (int hh = 1; hh < G; ++hh) if (hh == h) Mh = M[hh];
-            f[u] = md.y > 0.f ? __expf(md.x - Mh) : 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) { acc[q].x += f[u] * v[u].x; acc[q].y += f[u] * v[u].y; }
-    }
-  }
-  if (R > 1) {
-    __syncthreads();   // every replica has finished reading the factors in sh_f
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int col = (tid % (kAttThreads / R)) + q * kAttThreads;
-      sh_f[rep * NCOL * 2 + col * 2] = acc[q].x;
-      sh_f[rep * NCOL * 2 + col * 2 + 1] = acc[q].y;
-    }
-    __syncthreads();
-  }
-  if (rep == 0) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int col = tid + q * kAttThreads;
-      float2 s = acc[q];
-      for (int r = 1; r < R; ++r) { s.x += sh_f[r * NCOL * 2 + col * 2]; s.y += sh_f[r * NCOL * 2 + col * 2 + 1]; }
-      const int h = col >> 6, d2 = (col & 63) * 2;
-      float dh = den[0];
-#pragma unroll
-      for (int hh = 1; hh < G; ++hh) if (hh == h) dh = den[hh];
-      const size_t oh = (size_t)b * a.Hq + (size_t)g * G + h;
-      *reinterpret_cast<float2*>(a.out + oh * kD + d2) = make_float2(s.x / dh, s.y / dh);
-    }
-  }
-  if (tid < G && a.lse) {
-    float Mh = M[0], dh = den[0];
-#pragma unroll
-    for (int hh = 1; hh < G; ++hh) if (hh == tid) { Mh = M[hh]; dh = den[hh]; }
-    a.lse[(size_t)b * a.Hq + (size_t)g * G + tid] = Mh + __logf(dh);
-  }
-  __syncthreads();
-}
-
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ float sh_m[4 * G];
@@ -752,92 +702,154 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ float sh_num[4 * G * kD];
   __shared__ int sh_row[kChunkTokens];
   __shared__ int sh_mask[kChunkTokens];
-  __shared__ int sh_flag;
-  __shared__ int sh_base[kMaxGroupsPerDecode];
-  __shared__ float sh_f[kMergeF];
-  __shared__ float sh_red[32];
-  const int BG = a.B * a.Hkv;
-  const int total = (int)__builtin_nontemporal_load(a.counters + 2 * BG + 1);
-  for (int i = threadIdx.x; i < BG; i += kAttThreads) sh_base[i] = a.grp[(size_t)i * 4 + 3];
-  __syncthreads();
-  for (int item = blockIdx.x; item < a.n_est + total; item += gridDim.x) {
-    int bg;
-    if (item < a.n_est) {
-      bg = item / a.est_tiles_g;
-      est_tile<T, G>(a, bg, item - bg * a.est_tiles_g, item, sh_m, sh_num, sh_den);
-    } else {
-      const int j = item - a.n_est;
-      // group owning global chunk j: the last group whose chunk base is <= j (a group with no
-      // chunks shares its base with the next one, so the last such group always covers j)
-      int lo = 0, hi = BG - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sh_base[mid] <= j) lo = mid; else hi = mid - 1;
-      }
-      bg = lo;
-      const int jl = j - sh_base[bg];
-      attend_chunk<T, G>(a, bg, jl, item, sh_m, sh_num, sh_den, sh_row, sh_mask);
-    }
-    // completion: the last item of the group merges it
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t expected = (uint32_t)(a.est_tiles_g + __builtin_nontemporal_load(a.grp + (size_t)bg * 4 + 2));
-      sh_flag = (atomicAdd(&a.counters[BG + bg], 1u) == expected - 1u);
-    }
-    __syncthreads();
-    if (sh_flag) {
-      __threadfence();
-      merge_group<G>(a, bg, sh_f, sh_red);
-    }
-    __syncthreads();
+  const int bg = blockIdx.y;
+  const int32_t* gd = a.grp + (size_t)bg * 4;
+  const int n_entries = gd[0], n_tok = gd[1], n_chunks = gd[2], n_corr = gd[3];
+  for (int it = blockIdx.x; it < n_chunks + n_corr; it += gridDim.x) {
+    const size_t slot = (size_t)bg * a.att_items_g + it;
+    if (it < n_chunks)
+      attend_chunk<T, G>(a, bg, it, n_entries, n_tok, slot, sh_m, sh_num, sh_den, sh_row, sh_mask);
+    else
+      corr_item<T, G>(a, bg, it - n_chunks, n_entries, slot, sh_m, sh_num, sh_den);
   }
+}
+
+// ============================================================================ k_merge
+constexpr int kMergeThreads = 256;
+constexpr int kMergeLds = 8192;
+
+// out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
+// num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact chunks (+1),
+// retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
+// only its exact chunks.
+__global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
+  __shared__ float sh_f[kMergeLds];
+  __shared__ float sh_red[32];
+  __shared__ float4 sh_acc[kMergeThreads / 32][32];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
+  const int32_t* gd = a.grp + (size_t)bg * 4;
+  const int n_chunks = gd[2], n_corr = gd[3];
+  const bool use_est = a.all_sel[bh] == 0;
+  const int PE = use_est ? a.est_tiles_g : 0;
+  const int PC = use_est ? n_corr : 0;
+  const int P = PE + n_chunks + PC;
+  // partial p: [0, PE) estimation tiles, [PE, PE + n_chunks) chunks, then corrections
+  auto md_of = [&](int p) -> const float* {
+    if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
+    return a.att_md + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * 2;
+  };
+  auto num_of = [&](int p) -> const float* {
+    if (p < PE) return a.est_num + (((size_t)bg * a.est_tiles_g + p) * G + hi) * kD;
+    return a.att_num + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * kD;
+  };
+  float mx = -INFINITY;
+  for (int p = tid; p < PE + n_chunks; p += kMergeThreads) {
+    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
+    if (md.y > 0.f) mx = fmaxf(mx, md.x);
+  }
+  const float M = block_max(mx, sh_red);
+  const bool f_lds = P <= kMergeLds;
+  float dn = 0.f;
+  for (int p = tid; p < P; p += kMergeThreads) {
+    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
+    float f = md.y > 0.f ? __expf(md.x - M) : 0.f;
+    if (p >= PE + n_chunks) f = -f;
+    if (f_lds) sh_f[p] = f;
+    dn += f * md.y;
+  }
+  const float den = block_sum(dn, sh_red);
+  __syncthreads();
+  // numerators: 32 float4 columns cover the head's 128 dims; 8 replicas split the partials
+  const int col = tid & 31, rep = tid >> 5;
+  constexpr int R = kMergeThreads / 32;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = rep; p0 < P; p0 += 8 * R) {
+    float4 v[8];
+    float f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * R;
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      f[u] = 0.f;
+      if (p < P) {
+        v[u] = *reinterpret_cast<const float4*>(num_of(p) + 4 * col);
+        if (f_lds) {
+          f[u] = sh_f[p];
+        } else {
+          const float2 md = *reinterpret_cast<const float2*>(md_of(p));
+          f[u] = md.y > 0.f ? __expf(md.x - M) : 0.f;
+          if (p >= PE + n_chunks) f[u] = -f[u];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x += f[u] * v[u].x; acc.y += f[u] * v[u].y; acc.z += f[u] * v[u].z; acc.w += f[u] * v[u].w;
+    }
+  }
+  sh_acc[rep][col] = acc;
+  __syncthreads();
+  if (tid < 32) {
+    float4 s = sh_acc[0][tid];
+    for (int r = 1; r < R; ++r) {
+      const float4 t = sh_acc[r][tid];
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * tid) = make_float4(s.x / den, s.y / den, s.z / den, s.w / den);
+  }
+  if (tid == 0 && a.lse) a.lse[bh] = M + __logf(den);
 }
 
 // ============================================================================ launcher
 template <typename T, int G>
-static hipError_t launch_attend(const DecodeArgs& a, hipStream_t s, int grid) {
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(grid), dim3(kAttThreads), 0, s, a);
+static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
+  const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
+  hipError_t e;
+  if (a.C > 0) {
+    prof_begin(WI_STAGE_SCORE, s);
+    hipLaunchKernelGGL((k_score_est<T, G>), dim3(a.est_tiles_g, BG), dim3(kScoreThreads), 0, s, a);
+    prof_end(WI_STAGE_SCORE, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const bool keys_in_lds = (size_t)a.C * 4 + (size_t)a.W32 * 4 <= 65536;
+  const size_t dyn = (size_t)a.W32 * 4 + (keys_in_lds ? (size_t)a.C * 4 : 0);
+  prof_begin(WI_STAGE_SELECT, s);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), dyn, s, a);
+  hipLaunchKernelGGL(k_union, dim3(BG), dim3(kUnionThreads), 0, s, a);
+  prof_end(WI_STAGE_SELECT, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int S = (int)std::max<int64_t>(1, std::min<int64_t>(a.att_items_g, ceil_div(1024, BG)));
+  prof_begin(WI_STAGE_ATTEND, s);
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(S, BG), dim3(kAttThreads), 0, s, a);
+  prof_end(WI_STAGE_ATTEND, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin(WI_STAGE_MERGE, s);
+  hipLaunchKernelGGL(k_merge, dim3(BH), dim3(kMergeThreads), 0, s, a);
+  prof_end(WI_STAGE_MERGE, s);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
-  prof_begin(WI_STAGE_SCORE, s);
-  hipLaunchKernelGGL(k_score<T>, dim3((unsigned)std::max<int64_t>(1, ceil_div(a.C, 128)), BG),
-                     dim3(256), 0, s, a);
-  prof_end(WI_STAGE_SCORE, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const bool keys_in_lds = (size_t)a.C * 4 + (size_t)a.W32 * 4 <= 65536;
-  const size_t dyn = (size_t)a.W32 * 4 + (keys_in_lds ? (size_t)a.C * 4 : 0);
-  prof_begin(WI_STAGE_SELECT, s);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), dyn, s, a);
-  prof_end(WI_STAGE_SELECT, s);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int max_items = a.n_est + BG * a.max_chunks_g;
-  const int grid = std::max(1, std::min(max_items, 2048));
-  prof_begin(WI_STAGE_ATTEND, s);
   switch (a.G) {
-    case 1: e = launch_attend<T, 1>(a, s, grid); break;
-    case 2: e = launch_attend<T, 2>(a, s, grid); break;
-    case 4: e = launch_attend<T, 4>(a, s, grid); break;
-    case 8: e = launch_attend<T, 8>(a, s, grid); break;
-    default: e = hipErrorInvalidValue;
+    case 1: return launch_groups<T, 1>(a, s);
+    case 2: return launch_groups<T, 2>(a, s);
+    case 4: return launch_groups<T, 4>(a, s);
+    case 8: return launch_groups<T, 8>(a, s);
+    default: return hipErrorInvalidValue;
   }
-  prof_end(WI_STAGE_ATTEND, s);
-  return e;
 }
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
     attr_set = true;
   }
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);

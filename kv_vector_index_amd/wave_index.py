@@ -23,7 +23,8 @@ WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0,
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
-STAGES = ("score", "select", "attend", "prep", "init", "assign", "rescore", "csr", "update", "final")
+STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
+          "final")
 
 
 class WaveIndexError(RuntimeError):
