@@ -126,24 +126,24 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.G = p.Hq / p.Hkv;
   L.W32 = (int)ceil_div(p.C, 32);
   L.Umax = (int)std::min<int64_t>(p.C, (int64_t)L.G * p.top_k);
-  L.max_chunks_g = (int)ceil_div((int64_t)p.n_steady + p.Nc, kChunkTokens);
   L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
-  L.att_items_g = L.max_chunks_g + (int)ceil_div(L.Umax, kEstTile);
+  // about 1024 exact-attention workgroups in all, none with less than 64 tokens of context
+  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(1024, L.BG),
+                                                            ceil_div((int64_t)p.n_steady + p.Nc, 64)));
+  L.att_items_g = L.att_split + (int)ceil_div(L.Umax, kEstTile);
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G;
   size_t o = 0;
+  L.off_counters = o; o = align256(o + BG * 4);
   L.off_scores = o;   o = align256(o + BH * C * 4);
   L.off_mu_norm = o;  o = align256(o + BG * C * 4);
-  L.off_keys32 = o;   o = align256(o + BH * C * 4);
   L.off_sel_bits = o; o = align256(o + BH * L.W32 * 4);
   L.off_band_ids = o; o = align256(o + BH * C * 4);
   L.off_band_key = o; o = align256(o + BH * C * 8);
   L.off_all_sel = o;  o = align256(o + BH * 4);
   L.off_wl_cid = o;   o = align256(o + BG * L.Umax * 4);
-  L.off_wl_row0 = o;  o = align256(o + BG * L.Umax * 4);
   L.off_wl_mask = o;  o = align256(o + BG * L.Umax * 4);
-  L.off_wl_pre = o;   o = align256(o + BG * (L.Umax + 1) * 4);
+  L.off_rowmap = o;   o = align256(o + BG * ((size_t)p.n_steady + p.Nc) * 4);
   L.off_grp = o;      o = align256(o + BG * 4 * 4);
-  L.off_chunk_e0 = o; o = align256(o + BG * L.max_chunks_g * 4);
   L.off_est_md = o;   o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
   L.off_est_num = o;  o = align256(o + BG * L.est_tiles_g * G * kD * 4);
   L.off_att_md = o;   o = align256(o + BG * L.att_items_g * G * 2 * 4);
@@ -226,6 +226,8 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
     return fail(WI_ERR_INVALID_ARG, "negative C, Nc, n_steady or top_k");
   if ((int64_t)p->n_steady + p->Nc < 1) return fail(WI_ERR_INVALID_ARG, "empty context");
   if ((p->C == 0) != (p->Nc == 0)) return fail(WI_ERR_INVALID_ARG, "C and Nc must be both zero or both positive");
+  if (p->Nc >= (1 << 23) || p->n_steady >= (1 << 23))
+    return fail(WI_ERR_UNSUPPORTED, "more than 2^23 clustered or steady tokens per KV head");
   if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(WI_ERR_INVALID_ARG, "scale must be finite and > 0");
   const int64_t BG = (int64_t)p->B * p->Hkv;
   if (BG * ((int64_t)p->Nc + p->n_steady) >= kMaxRows || (int64_t)p->B * p->Hq * ((int64_t)p->C + 1) >= kMaxRows)
@@ -246,26 +248,24 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.k_perm = idx->k_perm; a.v_perm = idx->v_perm; a.k_steady = idx->k_steady; a.v_steady = idx->v_steady;
   a.q = q; a.out = out; a.lse = lse; a.sel_ids = sel_ids;
   char* base = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(base + L.off_counters);
   a.scores = reinterpret_cast<float*>(base + L.off_scores);
   a.mu_norm = reinterpret_cast<float*>(base + L.off_mu_norm);
-  a.keys32 = reinterpret_cast<uint32_t*>(base + L.off_keys32);
   a.sel_bits = reinterpret_cast<uint32_t*>(base + L.off_sel_bits);
   a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
   a.wl_cid = reinterpret_cast<int32_t*>(base + L.off_wl_cid);
-  a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
   a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
-  a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
+  a.rowmap = reinterpret_cast<uint32_t*>(base + L.off_rowmap);
   a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
-  a.chunk_e0 = reinterpret_cast<int32_t*>(base + L.off_chunk_e0);
   a.est_md = reinterpret_cast<float*>(base + L.off_est_md);
   a.est_num = reinterpret_cast<float*>(base + L.off_est_num);
   a.att_md = reinterpret_cast<float*>(base + L.off_att_md);
   a.att_num = reinterpret_cast<float*>(base + L.off_att_num);
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
-  a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.max_chunks_g = L.max_chunks_g;
-  a.est_tiles_g = L.est_tiles_g; a.att_items_g = L.att_items_g; a.scale = p->scale;
+  a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.est_tiles_g = L.est_tiles_g;
+  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);
 }

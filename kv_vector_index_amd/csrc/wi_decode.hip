@@ -15,17 +15,17 @@
 // at most the sum of the members' exp(logit)), so the cancellation costs O(eps_fp32) relative to
 // the merged denominator.  When a head retrieves every non-empty cluster both terms are dropped.
 //
-// Kernels (one stream, in order; no kernel waits on another block of its own grid):
+// Kernels (one stream, in order):
 //   k_score_est  grid (ceil(C/128), B*Hkv): MFMA scores of the KV group's query heads against 128
 //                centroids (one pass over mu serves all heads of the group), fp32 centroid norms,
 //                and the tile's estimation partial per head from SV and the sizes.
-//   k_select     grid (B*Hq): exact top-k per head (radix select on the fp32 scores, canonical
-//                fp64 re-scoring of the certified uncertainty band, ties to the lower id).
-//   k_union      grid (B*Hkv): union of the group's selections with a per-head mask, token
-//                prefix sums and chunk starts.
-//   k_attend     grid (S, B*Hkv): per KV group, items are 128-token chunks of steady + retrieved
-//                rows (each row loaded once and used by every head of the group that selected
-//                it) and 128-entry correction items (the retrieved clusters' estimation terms).
+//   k_select     grid (B*Hq): exact top-k per head (histogram threshold on the fp32 scores,
+//                canonical fp64 re-scoring of the certified uncertainty band, ties to the lower
+//                id).  The last head of each KV group to finish builds the group's work list.
+//   k_attend     grid (S + Sc, B*Hkv): S workgroups per KV group split its token list (steady
+//                zone, then the union of the rows its heads retrieved, each row loaded once for
+//                all heads that want it) with an online softmax; Sc workgroups fold the retrieved
+//                clusters' estimation terms.
 //   k_merge      grid (B*Hq): log-sum-exp merge of the head's partials into out and lse.
 #include "wi_device.h"
 #include "wi_internal.h"
@@ -52,6 +52,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   const T* sv = static_cast<const T*>(a.sv) + ((size_t)bg * C + (size_t)tile * kEstTile) * kD;
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+  if (tile == 0 && tid == 0) a.counters[bg] = 0u;    // arrivals of the group's heads in k_select
+  if (C == 0) return;
   const int nrows = min(kEstTile, C - tile * kEstTile);
 
   // value sums of the tile: thread (w, lane) owns rows w + 4i and dims 2*lane, 2*lane+1.  The
@@ -281,100 +283,252 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
   return acc;
 }
 
+
+// Hand-off between workgroups of one grid.  An agent-scope fence on this GPU writes back and
+// invalidates the whole L2 of the XCD, and those serialise across the chip; instead the data a
+// later workgroup reads is stored with agent-scope relaxed atomic stores (coherent at device
+// level), the writer waits for their completion before it bumps the arrival counter, and the
+// last arriving workgroup reads with agent-scope relaxed atomic loads.
+__device__ __forceinline__ void coherent_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns true in exactly one workgroup: the last of `expected` to arrive at `counter`.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);                         // this thread's stores have completed
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomicAdd(counter, 1u) == expected - 1u;
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return last;
+}
+
+constexpr int kSelKPT = 16;         // clusters per thread per register round
+constexpr int kBins = 2048;         // histogram bins over [min score, max score]
+constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
+
+// Per query head: the retrieval zone is the k_eff = min(top_k, #non-empty) non-empty clusters
+// first in the order (-sigma_c, c).  1) the k_eff-th largest fp32 score t is found with a
+// 2048-bin histogram over [min, max] and a rank count inside the threshold bin (a radix select
+// over the order keys covers bins too full to rank); 2) clusters above t + 2 delta are in, those
+// below t - 2 delta are out (delta bounds |fp32 score - canonical fp64 score|); 3) the band in
+// between is re-scored canonically and ranked by (-sigma, id).  The last head of a KV group to
+// finish builds the group's work list: the union of the heads' clusters with a head mask, a
+// token -> row map (steady zone first), and the list the estimation corrections run over.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
-  extern __shared__ uint32_t dyn[];           // bitmap [W32], then keys [C] when they fit
-  __shared__ uint32_t hist[256];
+  extern __shared__ uint32_t bits[];                 // [W32] retrieved-cluster bitmap
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t cand[kCandMax];
   __shared__ int iscr[48];
-  __shared__ float fscr[32];
+  __shared__ float fred[8][4];
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
+  __shared__ int sh_i[8];
 
   const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, bg = b * a.Hkv + g;
   const int C = a.C, W32 = a.W32;
-  uint32_t* bits = dyn;
-  const bool keys_in_lds = (size_t)C * 4 + (size_t)W32 * 4 <= 65536;
-  uint32_t* keys = keys_in_lds ? dyn + W32 : a.keys32 + (size_t)bh * C;
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
   const int32_t* sizes = a.sizes + (size_t)bg * C;
   const float* sc = a.scores + (size_t)bh * C;
   const float* mnorm = a.mu_norm + (size_t)bg * C;
   const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
+  // thread t owns clusters [t*KPT, (t+1)*KPT), visited kSelKPT at a time
+  const int KPT = (C + NT - 1) / NT;
+  const int R = (KPT + kSelKPT - 1) / kSelKPT;
+  const bool cached = R <= 1;
+  const int cbeg = min(C, tid * KPT), cend = min(C, cbeg + KPT);
 
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
-  const float qn = sqrtf(block_sum(qv * qv, fscr));
-
   for (int w = tid; w < W32; w += NT) bits[w] = 0u;
-  // order keys (0 marks an empty cluster), non-empty count, largest centroid norm
-  int cnt = 0;
-  float mxn = 0.f;
-  for (int base = tid; base < C; base += 4 * NT) {
-    int sz[4];
-    float s[4], nm[4];
+
+  uint32_t kc[kSelKPT];
+  auto load_keys = [&](int r, uint32_t (&k)[kSelKPT]) {
+    if (cached) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = base + u * NT;
-      sz[u] = 0; s[u] = 0.f; nm[u] = 0.f;
-      if (c < C) { sz[u] = sizes[c]; s[u] = sc[c]; nm[u] = mnorm[c]; }
+      for (int i = 0; i < kSelKPT; ++i) k[i] = kc[i];
+      return;
+    }
+    int n[kSelKPT];
+    float s[kSelKPT];
+#pragma unroll
+    for (int i = 0; i < kSelKPT; ++i) {
+      const int c = cbeg + r * kSelKPT + i;
+      n[i] = 0; s[i] = 0.f;
+      if (c < cend) { n[i] = sizes[c]; s[i] = sc[c]; }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = base + u * NT;
-      if (c < C) {
-        uint32_t key = 0u;
-        if (sz[u] > 0) { ++cnt; mxn = fmaxf(mxn, nm[u]); key = f32_order_key(s[u]); }
-        keys[c] = key;
+    for (int i = 0; i < kSelKPT; ++i) k[i] = n[i] > 0 ? f32_order_key(s[i]) : 0u;
+  };
+
+  // ---- pass 1: non-empty count, score range, largest centroid norm (and the key cache)
+  int cnt = 0;
+  float smax = -INFINITY, smin = INFINITY, mxn = 0.f;
+  for (int r = 0; r < R; ++r) {
+    int n[kSelKPT];
+    float s[kSelKPT], nm[kSelKPT];
+#pragma unroll
+    for (int i = 0; i < kSelKPT; ++i) {
+      const int c = cbeg + r * kSelKPT + i;
+      n[i] = 0; s[i] = 0.f; nm[i] = 0.f;
+      if (c < cend) { n[i] = sizes[c]; s[i] = sc[c]; nm[i] = mnorm[c]; }
+    }
+#pragma unroll
+    for (int i = 0; i < kSelKPT; ++i) {
+      uint32_t key = 0u;
+      if (n[i] > 0) {
+        ++cnt;
+        smax = fmaxf(smax, s[i]);
+        smin = fminf(smin, s[i]);
+        mxn = fmaxf(mxn, nm[i]);
+        key = f32_order_key(s[i]);
       }
+      if (cached) kc[i] = key;
     }
   }
-  const int n_ne = block_isum(cnt, iscr);
-  mxn = block_max(mxn, fscr);
+  {
+    float v0 = (float)cnt, v1 = smax, v2 = -smin, v3 = fmaxf(mxn, 0.f);
+    float q2 = qv * qv;
+    v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_max(v2); v3 = wave_max(v3); q2 = wave_sum(q2);
+    if (lane == 0) { fred[wv][0] = v0; fred[wv][1] = v1; fred[wv][2] = v2; fred[wv][3] = v3; iscr[32 + wv] = __float_as_int(q2); }
+    __syncthreads();
+    float r0 = 0.f, r1 = -INFINITY, r2 = -INFINITY, r3 = 0.f, r4 = 0.f;
+    for (int i = 0; i < NT / 64; ++i) {
+      r0 += fred[i][0]; r1 = fmaxf(r1, fred[i][1]); r2 = fmaxf(r2, fred[i][2]); r3 = fmaxf(r3, fred[i][3]);
+      r4 += __int_as_float(iscr[32 + i]);
+    }
+    cnt = (int)r0; smax = r1; smin = -r2; mxn = r3; qv = sqrtf(r4);
+    __syncthreads();
+  }
+  const int n_ne = cnt;
+  const float qn = qv;
   const int k_eff = min(a.top_k, n_ne);
-  __syncthreads();
 
   if (k_eff > 0 && k_eff == n_ne) {
-    for (int c = tid; c < C; c += NT)
-      if (keys[c] != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31));
+    for (int r = 0; r < R; ++r) {
+      uint32_t k[kSelKPT];
+      load_keys(r, k);
+#pragma unroll
+      for (int i = 0; i < kSelKPT; ++i) {
+        const int c = cbeg + r * kSelKPT + i;
+        if (k[i] != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31));
+      }
+    }
   } else if (k_eff > 0) {
-    int rem;
-    const uint32_t thr = block_radix_select<uint32_t>(C, k_eff, [&](int i) { return keys[i]; }, hist, iscr, &rem);
-    // Certified band: |fp32 score - canonical fp64 score| <= delta for every cluster (fp32
-    // accumulation of d exact-or-rounded products, doubled for an unspecified MFMA order).
+    // ---- pass 2: histogram over [smin, smax] (monotone binning, so higher bins hold higher scores)
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    const float span = smax - smin;
+    const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
+    auto bin_of = [&](uint32_t key) -> int {
+      const float s = f32_from_order_key(key);
+      return min(kBins - 1, max(0, (int)((s - smin) * inv)));
+    };
+    for (int r = 0; r < R; ++r) {
+      uint32_t k[kSelKPT];
+      load_keys(r, k);
+#pragma unroll
+      for (int i = 0; i < kSelKPT; ++i)
+        if (k[i] != 0u) atomicAdd(&hist[bin_of(k[i])], 1u);
+    }
+    __syncthreads();
+    // threshold bin: thread t owns bins kBins-1-4t .. kBins-4-4t (descending)
+    {
+      constexpr int BPT = kBins / kSelThreads;
+      int v = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) v += (int)hist[kBins - 1 - BPT * tid - j];
+      int tot;
+      int run = block_exclusive_scan(v, iscr, &tot);
+      if (run < k_eff && k_eff <= run + v) {
+        for (int j = 0; j < BPT; ++j) {
+          const int bin = kBins - 1 - BPT * tid - j;
+          const int hb = (int)hist[bin];
+          if (run + hb >= k_eff) { sh_i[0] = bin; sh_i[1] = run; break; }
+          run += hb;
+        }
+      }
+      __syncthreads();
+    }
+    const int bstar = sh_i[0];
+    const int rem = k_eff - sh_i[1];
+    const int ncand = (int)hist[bstar];
+    uint32_t thr;
+    if (ncand <= kCandMax) {
+      if (tid == 0) sh_i[2] = 0;
+      __syncthreads();
+      for (int r = 0; r < R; ++r) {
+        uint32_t k[kSelKPT];
+        load_keys(r, k);
+#pragma unroll
+        for (int i = 0; i < kSelKPT; ++i)
+          if (k[i] != 0u && bin_of(k[i]) == bstar) cand[atomicAdd(&sh_i[2], 1)] = k[i];
+      }
+      __syncthreads();
+      // the rem-th largest candidate: gt < rem <= ge
+      for (int i = tid; i < ncand; i += NT) {
+        const uint32_t ki = cand[i];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < ncand; ++j) { const uint32_t kj = cand[j]; gt += kj > ki; ge += kj >= ki; }
+        if (gt < rem && rem <= ge) sh_i[3] = (int)ki;
+      }
+      __syncthreads();
+      thr = (uint32_t)sh_i[3];
+    } else {
+      int rr;
+      thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) {
+        return sizes[c] > 0 ? f32_order_key(sc[c]) : 0u; }, hist, iscr, &rr);
+    }
+    // ---- pass 3: in / band / out.  delta bounds |fp32 score - canonical fp64 score| for every
+    // cluster: fp32 accumulation of d exact-or-rounded products, doubled for an unspecified
+    // MFMA summation order.
     const double that = (double)f32_from_order_key(thr);
     const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qn * (1.0 + 1.0 / 1024) *
                              (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
-    const int per = (C + NT - 1) / NT;
-    const int c0 = min(C, tid * per), c1 = min(C, c0 + per);
     int nb = 0, nin = 0;
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t key = keys[c];
-      if (key == 0u) continue;
-      const double v = (double)f32_from_order_key(key);
-      if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
-      else if (v >= lo) ++nb;
+    for (int r = 0; r < R; ++r) {
+      uint32_t k[kSelKPT];
+      load_keys(r, k);
+#pragma unroll
+      for (int i = 0; i < kSelKPT; ++i) {
+        if (k[i] == 0u) continue;
+        const int c = cbeg + r * kSelKPT + i;
+        const double v = (double)f32_from_order_key(k[i]);
+        if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
+        else if (v >= lo) ++nb;
+      }
     }
     int n_band;
     int pos = block_exclusive_scan(nb, iscr, &n_band);
     const int n_in = block_isum(nin, iscr);
     const int need = k_eff - n_in;
     int32_t* band = n_band <= kSmallBand ? band_lds : a.band_ids + (size_t)bh * C;
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t key = keys[c];
-      if (key == 0u) continue;
-      const double v = (double)f32_from_order_key(key);
-      if (!(v > hi) && v >= lo) band[pos++] = c;
+    if (nb > 0) {
+      for (int r = 0; r < R; ++r) {
+        uint32_t k[kSelKPT];
+        load_keys(r, k);
+#pragma unroll
+        for (int i = 0; i < kSelKPT; ++i) {
+          if (k[i] == 0u) continue;
+          const double v = (double)f32_from_order_key(k[i]);
+          if (!(v > hi) && v >= lo) band[pos++] = cbeg + r * kSelKPT + i;
+        }
+      }
     }
     __syncthreads();
     if (need >= n_band) {
       for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
     } else if (n_band <= kSmallBand) {
-      // one wave: rescore, then rank by (-sigma, id); the band is in ascending id order
+      // one wave: canonical scores, then rank by (-sigma, id); the band is in ascending id order
       if (wv == 0) {
         const bool live = lane < n_band;
         const int c = live ? band[lane] : 0;
@@ -399,20 +553,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       int neq = 0;
       for (int i = i0; i < i1; ++i) neq += (bkey[i] == t64);
       int tot_eq;
-      int r = block_exclusive_scan(neq, iscr, &tot_eq);
+      int rk = block_exclusive_scan(neq, iscr, &tot_eq);
       for (int i = i0; i < i1; ++i) {
         const uint64_t kk = bkey[i];
         bool take = kk > t64;
-        if (kk == t64) { take = r < rem2; ++r; }
+        if (kk == t64) { take = rk < rem2; ++rk; }
         if (take) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
       }
     }
   }
   __syncthreads();
 
-  // publish the bitmap; ascending ids to sel_ids
-  uint32_t* gbits = a.sel_bits + (size_t)bh * W32;
-  for (int w = tid; w < W32; w += NT) gbits[w] = bits[w];
+  // ---- publish: bitmap (coherent, read by the group's last head), ascending ids, flag
+  for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
   if (a.sel_ids) {
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
@@ -427,51 +580,36 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
     for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
   }
-
   if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
-}
+  if (!arrive_last(a.counters + bg, (uint32_t)G, &sh_i[4])) return;
 
-// ============================================================================ k_union
-constexpr int kUnionThreads = 512;
-constexpr int kUnionLds = 4096;
-
-// Union of the selections of a KV group's query heads, in ascending cluster id, with the mask of
-// the heads that selected each cluster; token prefix sums (the steady zone first) and the first
-// entry of every 128-token chunk.
-__global__ __launch_bounds__(kUnionThreads) void k_union(DecodeArgs a) {
-  __shared__ int iscr[48];
-  __shared__ int ucid_lds[kUnionLds];
-  const int tid = threadIdx.x, NT = blockDim.x;
-  const int bg = blockIdx.x;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int G = a.G, C = a.C, W32 = a.W32;
+  // ---- the group's work list (last head only)
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
-  const int32_t* sizes = a.sizes + (size_t)bg * C;
-  int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
-  int32_t* ucid = a.Umax <= kUnionLds ? ucid_lds : cidg;
-  int32_t* umask = a.wl_mask + (size_t)bg * a.Umax;
   const int perw = (W32 + NT - 1) / NT;
   const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
   int ne = 0;
   for (int w = w0; w < w1; ++w) {
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) u |= hb[(size_t)j * W32 + w];
+    for (int j = 0; j < G; ++j) u |= coherent_load(hb + (size_t)j * W32 + w);
     ne += __popc(u);
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
+  int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
+  int32_t* mskg = a.wl_mask + (size_t)bg * a.Umax;
+  int32_t* ucid = n_entries <= kCandMax ? reinterpret_cast<int32_t*>(cand) : cidg;
+  int32_t* umsk = n_entries <= kCandMax ? reinterpret_cast<int32_t*>(hist) : mskg;
   for (int w = w0; w < w1; ++w) {
     uint32_t hw[kMaxGroup];
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) { hw[j] = hb[(size_t)j * W32 + w]; u |= hw[j]; }
+    for (int j = 0; j < G; ++j) { hw[j] = coherent_load(hb + (size_t)j * W32 + w); u |= hw[j]; }
     while (u) {
       const int bit = __ffs(u) - 1;
       u &= u - 1;
       int m = 0;
       for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
       ucid[e] = w * 32 + bit;
-      umask[e] = m;
+      umsk[e] = m;
       ++e;
     }
   }
@@ -484,234 +622,209 @@ __global__ __launch_bounds__(kUnionThreads) void k_union(DecodeArgs a) {
   int t = block_exclusive_scan(nt, iscr, &n_utok);
   const int NS = a.NS;
   const int n_tok = NS + n_utok;
-  int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
-  int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
-  int32_t* ce0 = a.chunk_e0 + (size_t)bg * a.max_chunks_g;
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  uint32_t* rmap = a.rowmap + (size_t)bg * (NS + a.Nc);
   for (int i = e0; i < e1; ++i) {
-    const int c = ucid[i];
+    const int c = ucid[i], m = umsk[i];
     const int r0 = off[c], sz = sizes[c];
-    const int start = NS + t;
-    row0[i] = r0;
-    pre[i] = start;
-    if (ucid != cidg) cidg[i] = c;
-    // chunks whose first token falls inside this cluster's token range start at entry i
-    for (int j = (start + kChunkTokens - 1) / kChunkTokens; j * kChunkTokens < start + sz; ++j) ce0[j] = i;
+    if (ucid != cidg) { cidg[i] = c; mskg[i] = m; }
+    const uint32_t tag = (uint32_t)m << 24;
+    for (int j = 0; j < sz; ++j) rmap[NS + t + j] = (uint32_t)(r0 + j) | tag;
     t += sz;
   }
-  for (int j = tid; j * kChunkTokens < min(NS, n_tok); j += NT) ce0[j] = 0;   // chunks in the steady zone
+  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
+  for (int s = tid; s < NS; s += NT) rmap[s] = (uint32_t)s | stag;
   if (tid == 0) {
-    pre[n_entries] = n_tok;
-    int32_t* gd = a.grp + (size_t)bg * 4;
-    gd[0] = n_entries;
-    gd[1] = n_tok;
-    gd[2] = (n_tok + kChunkTokens - 1) / kChunkTokens;
-    gd[3] = (n_entries + kEstTile - 1) / kEstTile;
+    a.grp[(size_t)bg * 4 + 0] = n_entries;
+    a.grp[(size_t)bg * 4 + 1] = n_tok;
   }
 }
 
 // ============================================================================ k_attend
 constexpr int kAttThreads = 256;
+constexpr int kRowsPerLane = 4;                       // rows per lane group per sub-chunk
+constexpr int kSubChunk = 4 * 4 * kRowsPerLane;       // 4 waves x 4 lane groups x rows
 
-// Rows of a work item: wave w owns rows w*32 + 4*i + (lane>>4), i = 0..7; lane&15 owns dims
-// [8*(lane&15), +8).  Given per-row logits (identical across the 16 lanes of a row), the row
-// values and a per-row weight of the denominator, form the item's partial softmax state per head
-// (max logit m, den = sum wden e^(l-m), num = sum e^(l-m) v) and write it to `slot`.
+// Online softmax state of one lane group (16 lanes share a row; lane&15 owns 8 dims).
 template <int G>
-__device__ __forceinline__ void finish_partial(const float (&l)[8][G], const float (&v)[8][8],
-                                               const float (&wden)[8], size_t slot, const DecodeArgs& a,
-                                               float* sh_m, float* sh_num, float* sh_den) {
+struct OState {
+  float m[G], den[G], num[G][8];
+  __device__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY; den[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[h][e] = 0.f;
+    }
+  }
+  // fold rows with logits l (-inf = absent), denominator weights wd and values v
+  __device__ void add(const float (&l)[kRowsPerLane][G], const float (&wd)[kRowsPerLane],
+                      const float (&v)[kRowsPerLane][8]) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = m[h];
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) mx = fmaxf(mx, l[i][h]);
+      if (mx == -INFINITY) continue;
+      const float sc = m[h] == -INFINITY ? 0.f : __expf(m[h] - mx);
+      den[h] *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[h][e] *= sc;
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        const float p = l[i][h] == -INFINITY ? 0.f : __expf(l[i][h] - mx);
+        den[h] += wd[i] * p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[h][e] += p * v[i][e];
+      }
+      m[h] = mx;
+    }
+  }
+};
+
+// Combine the 16 lane-group states of the block and write one partial per head to `slot`.
+template <int G>
+__device__ void write_partial(OState<G>& st, size_t slot, float* md_out, float* num_out,
+                              float* sh_m, float* sh_den, float* sh_num) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15;
-  float M[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float m = l[0][h];
+    // across the four lane groups of the wave
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = fmaxf(m, l[i][h]);
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (lane == 0) sh_m[w * G + h] = m;
-  }
-  __syncthreads();
+    for (int x = 16; x <= 32; x <<= 1) {
+      const float om = __shfl_xor(st.m[h], x);
+      const float mx = fmaxf(st.m[h], om);
+      const float s0 = st.m[h] == -INFINITY ? 0.f : __expf(st.m[h] - mx);
+      const float s1 = om == -INFINITY ? 0.f : __expf(om - mx);
+      st.den[h] = st.den[h] * s0 + __shfl_xor(st.den[h], x) * s1;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = sh_m[h];
-    for (int ww = 1; ww < kAttThreads / 64; ++ww) m = fmaxf(m, sh_m[ww * G + h]);
-    M[h] = m;
-  }
-  float den[G], num[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    den[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) num[h][e] = 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = (l[i][h] == -INFINITY) ? 0.f : __expf(l[i][h] - M[h]);
-      den[h] += wden[i] * p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) num[h][e] += p * v[i][e];
+      for (int e = 0; e < 8; ++e) st.num[h][e] = st.num[h][e] * s0 + __shfl_xor(st.num[h][e], x) * s1;
+      st.m[h] = mx;
     }
-  }
+    if (lane < 16) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    den[h] += __shfl_xor(den[h], 16);
-    den[h] += __shfl_xor(den[h], 32);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      num[h][e] += __shfl_xor(num[h][e], 16);
-      num[h][e] += __shfl_xor(num[h][e], 32);
-    }
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sh_num[(w * G + h) * kD + 8 * lr + e] = num[h][e];
-      if (lr == 0) sh_den[w * G + h] = den[h];
+      for (int e = 0; e < 8; ++e) sh_num[(w * G + h) * kD + 8 * lr + e] = st.num[h][e];
+      if (lr == 0) { sh_m[w * G + h] = st.m[h]; sh_den[w * G + h] = st.den[h]; }
     }
   }
   __syncthreads();
-  float* pn = a.att_num + slot * G * kD;
   for (int i = threadIdx.x; i < G * kD; i += kAttThreads) {
+    const int h = i / kD;
+    float mx = -INFINITY;
+    for (int ww = 0; ww < 4; ++ww) mx = fmaxf(mx, sh_m[ww * G + h]);
     float s = 0.f;
-    for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_num[ww * G * kD + i];
-    pn[i] = s;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sh_m[ww * G + h];
+      if (mw != -INFINITY) s += __expf(mw - mx) * sh_num[ww * G * kD + i];
+    }
+    num_out[slot * G * kD + i] = s;
   }
   if (threadIdx.x < G) {
-    const int hh = threadIdx.x;
-    float s = 0.f;
-    for (int ww = 0; ww < kAttThreads / 64; ++ww) s += sh_den[ww * G + hh];
-    a.att_md[(slot * G + hh) * 2 + 0] = M[hh];
-    a.att_md[(slot * G + hh) * 2 + 1] = s;
+    const int h = threadIdx.x;
+    float mx = -INFINITY;
+    for (int ww = 0; ww < 4; ++ww) mx = fmaxf(mx, sh_m[ww * G + h]);
+    float d = 0.f;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sh_m[ww * G + h];
+      if (mw != -INFINITY) d += __expf(mw - mx) * sh_den[ww * G + h];
+    }
+    md_out[(slot * G + h) * 2] = mx;
+    md_out[(slot * G + h) * 2 + 1] = d;
   }
   __syncthreads();
 }
 
-// The estimation terms of the retrieved clusters (entries [128 ci, 128 ci + 128) of the group's
-// union list), for the heads that retrieved each one; the merge subtracts them.
-template <typename T, int G>
-__device__ void corr_item(const DecodeArgs& a, int bg, int ci, int n_entries, size_t slot,
-                          float* sh_m, float* sh_num, float* sh_den) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv, C = a.C;
-  const int32_t* szs = a.sizes + (size_t)bg * C;
-  const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * C * kD;
-  const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
-  const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
-  const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
-  float l[8][G], v[8][8], wden[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = ci * kEstTile + w * 32 + 4 * i + rg;
-    const bool live = e < n_entries;
-    const int c = live ? cid[e] : 0;
-    const int m = live ? msk[e] : 0;
-    wden[i] = live ? (float)szs[c] : 0.f;
-    if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
-    else for (int x = 0; x < 8; ++x) v[i][x] = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      l[i][h] = ((m >> h) & 1) ? a.scores[(hbase + h) * C + c] * a.scale : -INFINITY;
-  }
-  finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
-}
-
-template <typename T, int G>
-__device__ void attend_chunk(const DecodeArgs& a, int bg, int jl, int n_entries, int n_tok,
-                             size_t slot, float* sh_m, float* sh_num, float* sh_den, int* sh_row,
-                             int* sh_mask) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int NS = a.NS;
-  const int t0 = jl * kChunkTokens;
-  const int t1 = min(n_tok, t0 + kChunkTokens);
-  const int32_t* row0 = a.wl_row0 + (size_t)bg * a.Umax;
-  const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
-  const int32_t* pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
-  const int e0 = a.chunk_e0[(size_t)bg * a.max_chunks_g + jl];
-
-  // token -> (row, head mask); row >= 0 indexes k_perm, row < 0 is steady row (-1 - row)
-  for (int t = t0 + threadIdx.x; t < min(t1, NS); t += kAttThreads) {
-    sh_row[t - t0] = -1 - t;
-    sh_mask[t - t0] = (1 << G) - 1;
-  }
-  for (int e = e0 + threadIdx.x; e < n_entries; e += kAttThreads) {
-    const int s = pre[e];
-    if (s >= t1) break;
-    const int s1 = pre[e + 1];
-    const int r0 = row0[e], m = msk[e];
-    for (int t = max(s, t0); t < min(s1, t1); ++t) { sh_row[t - t0] = r0 + (t - s); sh_mask[t - t0] = m; }
-  }
-  __syncthreads();
-
-  const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
-  const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
-  const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * NS * kD;
-  const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * NS * kD;
-  const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
-
-  float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) St<T>::load8(qg + (size_t)h * kD + 8 * lr, qf[h]);
-
-  float kr[8][8], v[8][8], wden[8];
-  int mk[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 32 + 4 * i + rg;
-    const int t = t0 + r;
-    wden[i] = 1.f;
-    mk[i] = 0;
-    if (t < t1) {
-      const int row = sh_row[r];
-      mk[i] = sh_mask[r];
-      const T* kq = row >= 0 ? kp + (size_t)row * kD : ks + (size_t)(-1 - row) * kD;
-      const T* vq = row >= 0 ? vp + (size_t)row * kD : vs + (size_t)(-1 - row) * kD;
-      St<T>::load8(kq + 8 * lr, kr[i]);
-      St<T>::load8(vq + 8 * lr, v[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kr[i][e] = 0.f; v[i][e] = 0.f; }
-    }
-  }
-  float l[8][G];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += qf[h][e] * kr[i][e];
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 1);
-      l[i][h] = ((mk[i] >> h) & 1) ? s * a.scale : -INFINITY;
-    }
-  }
-  finish_partial<G>(l, v, wden, slot, a, sh_m, sh_num, sh_den);
-}
-
+// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
+// of its KV group's list (steady zone, then the retrieved clusters); workgroup S + j folds the
+// estimation terms of union entries [128 j, 128 j + 128) (the merge subtracts them).
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
-  __shared__ float sh_m[4 * G];
-  __shared__ float sh_den[4 * G];
+  __shared__ float sh_m[4 * G], sh_den[4 * G];
   __shared__ float sh_num[4 * G * kD];
-  __shared__ int sh_row[kChunkTokens];
-  __shared__ int sh_mask[kChunkTokens];
-  const int bg = blockIdx.y;
-  const int32_t* gd = a.grp + (size_t)bg * 4;
-  const int n_entries = gd[0], n_tok = gd[1], n_chunks = gd[2], n_corr = gd[3];
-  for (int it = blockIdx.x; it < n_chunks + n_corr; it += gridDim.x) {
-    const size_t slot = (size_t)bg * a.att_items_g + it;
-    if (it < n_chunks)
-      attend_chunk<T, G>(a, bg, it, n_entries, n_tok, slot, sh_m, sh_num, sh_den, sh_row, sh_mask);
-    else
-      corr_item<T, G>(a, bg, it - n_chunks, n_entries, slot, sh_m, sh_num, sh_den);
+  const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
+  const int n_entries = a.grp[(size_t)bg * 4 + 0], n_tok = a.grp[(size_t)bg * 4 + 1];
+  const size_t slot = (size_t)bg * a.att_items_g + s;
+  const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+  OState<G> st;
+  st.init();
+  if (s < S) {
+    const int t0 = (int)(((int64_t)s * n_tok) / S), t1 = (int)(((int64_t)(s + 1) * n_tok) / S);
+    const uint32_t* rmap = a.rowmap + (size_t)bg * (a.NS + a.Nc);
+    const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
+    const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
+    const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
+    const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * a.NS * kD;
+    float qf[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) St<T>::load8(qg + (size_t)h * kD + 8 * lr, qf[h]);
+    for (int c0 = t0; c0 < t1; c0 += kSubChunk) {
+      uint32_t ent[kRowsPerLane];
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        const int t = c0 + w * 16 + 4 * i + rg;
+        ent[i] = t < t1 ? rmap[t] : 0u;
+      }
+      float kr[kRowsPerLane][8], v[kRowsPerLane][8], wd[kRowsPerLane], l[kRowsPerLane][G];
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        const uint32_t en = ent[i];
+        const int row = (int)(en & 0x7fffffu);
+        const T* kq = (en & (1u << 23)) ? ks + (size_t)row * kD : kp + (size_t)row * kD;
+        const T* vq = (en & (1u << 23)) ? vs + (size_t)row * kD : vp + (size_t)row * kD;
+        if ((en >> 24) != 0u) {
+          St<T>::load8(kq + 8 * lr, kr[i]);
+          St<T>::load8(vq + 8 * lr, v[i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { kr[i][e] = 0.f; v[i][e] = 0.f; }
+        }
+        wd[i] = 1.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        const uint32_t mk = ent[i] >> 24;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float x = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x += qf[h][e] * kr[i][e];
+          x += __shfl_xor(x, 8);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 1);
+          l[i][h] = ((mk >> h) & 1u) ? x * a.scale : -INFINITY;
+        }
+      }
+      st.add(l, wd, v);
+    }
+  } else {
+    const int e0 = (s - S) * kEstTile;
+    const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
+    const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
+    const int32_t* szs = a.sizes + (size_t)bg * a.C;
+    const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
+    const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
+    for (int c0 = e0; c0 < min(n_entries, e0 + kEstTile); c0 += kSubChunk) {
+      float v[kRowsPerLane][8], wd[kRowsPerLane], l[kRowsPerLane][G];
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        const int e = c0 + w * 16 + 4 * i + rg;
+        const bool live = e < min(n_entries, e0 + kEstTile);
+        const int c = live ? cid[e] : 0;
+        const int m = live ? msk[e] : 0;
+        wd[i] = live ? (float)szs[c] : 0.f;
+        if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
+        else for (int x = 0; x < 8; ++x) v[i][x] = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          l[i][h] = ((m >> h) & 1) ? a.scores[(hbase + h) * a.C + c] * a.scale : -INFINITY;
+      }
+      st.add(l, wd, v);
+    }
   }
+  write_partial<G>(st, slot, a.att_md, a.att_num, sh_m, sh_den, sh_num);
 }
 
 // ============================================================================ k_merge
@@ -719,9 +832,9 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeLds = 8192;
 
 // out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
-// num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact chunks (+1),
+// num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact splits (+1),
 // retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
-// only its exact chunks.
+// only its exact splits.
 __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   __shared__ float sh_f[kMergeLds];
   __shared__ float sh_red[32];
@@ -730,13 +843,11 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
-  const int32_t* gd = a.grp + (size_t)bg * 4;
-  const int n_chunks = gd[2], n_corr = gd[3];
   const bool use_est = a.all_sel[bh] == 0;
   const int PE = use_est ? a.est_tiles_g : 0;
-  const int PC = use_est ? n_corr : 0;
-  const int P = PE + n_chunks + PC;
-  // partial p: [0, PE) estimation tiles, [PE, PE + n_chunks) chunks, then corrections
+  const int S = a.att_split;
+  const int PC = use_est ? a.att_items_g - S : 0;
+  const int P = PE + S + PC;
   auto md_of = [&](int p) -> const float* {
     if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
     return a.att_md + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * 2;
@@ -746,7 +857,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     return a.att_num + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * kD;
   };
   float mx = -INFINITY;
-  for (int p = tid; p < PE + n_chunks; p += kMergeThreads) {
+  for (int p = tid; p < PE + S; p += kMergeThreads) {
     const float2 md = *reinterpret_cast<const float2*>(md_of(p));
     if (md.y > 0.f) mx = fmaxf(mx, md.x);
   }
@@ -756,7 +867,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   for (int p = tid; p < P; p += kMergeThreads) {
     const float2 md = *reinterpret_cast<const float2*>(md_of(p));
     float f = md.y > 0.f ? __expf(md.x - M) : 0.f;
-    if (p >= PE + n_chunks) f = -f;
+    if (p >= PE + S) f = -f;
     if (f_lds) sh_f[p] = f;
     dn += f * md.y;
   }
@@ -781,7 +892,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
         } else {
           const float2 md = *reinterpret_cast<const float2*>(md_of(p));
           f[u] = md.y > 0.f ? __expf(md.x - M) : 0.f;
-          if (p >= PE + n_chunks) f[u] = -f[u];
+          if (p >= PE + S) f[u] = -f[u];
         }
       }
     }
@@ -808,22 +919,16 @@ template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
   hipError_t e;
-  if (a.C > 0) {
-    prof_begin(WI_STAGE_SCORE, s);
-    hipLaunchKernelGGL((k_score_est<T, G>), dim3(a.est_tiles_g, BG), dim3(kScoreThreads), 0, s, a);
-    prof_end(WI_STAGE_SCORE, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const bool keys_in_lds = (size_t)a.C * 4 + (size_t)a.W32 * 4 <= 65536;
-  const size_t dyn = (size_t)a.W32 * 4 + (keys_in_lds ? (size_t)a.C * 4 : 0);
+  prof_begin(WI_STAGE_SCORE, s);
+  hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, a);
+  prof_end(WI_STAGE_SCORE, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), dyn, s, a);
-  hipLaunchKernelGGL(k_union, dim3(BG), dim3(kUnionThreads), 0, s, a);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 4, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int S = (int)std::max<int64_t>(1, std::min<int64_t>(a.att_items_g, ceil_div(1024, BG)));
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(S, BG), dim3(kAttThreads), 0, s, a);
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
@@ -847,9 +952,9 @@ hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStre
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 98304);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
     attr_set = true;
   }
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);

@@ -24,10 +24,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
-  int BG, BH, G, W32, Umax, max_chunks_g, est_tiles_g, att_items_g;
-  size_t off_scores, off_mu_norm, off_keys32, off_sel_bits, off_band_ids, off_band_key,
-      off_all_sel, off_wl_cid, off_wl_row0, off_wl_mask, off_wl_pre, off_grp, off_chunk_e0,
-      off_est_md, off_est_num, off_att_md, off_att_num, total;
+  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g;
+  size_t off_counters, off_scores, off_mu_norm, off_sel_bits, off_band_ids, off_band_key,
+      off_all_sel, off_wl_cid, off_wl_mask, off_rowmap, off_grp, off_est_md, off_est_num,
+      off_att_md, off_att_num, total;
 };
 DecodeLayout decode_layout(const wi_decode_params& p);
 
@@ -46,25 +46,23 @@ struct DecodeArgs {
   float* lse;              // [BH] or null
   int32_t* sel_ids;        // [BH, top_k] or null
   // workspace
+  uint32_t* counters;      // [BG] arrivals of a group's heads in k_select
   float* scores;           // [BH, C] fp32 <q, mu_c>
   float* mu_norm;          // [BG, C]
-  uint32_t* keys32;        // [BH, C] order keys when they do not fit in LDS
   uint32_t* sel_bits;      // [BH, W32] retrieved-cluster bitmap
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
   int32_t* wl_cid;         // [BG, Umax] union entries: cluster id
-  int32_t* wl_row0;        // [BG, Umax]           first k_perm row
-  int32_t* wl_mask;        // [BG, Umax]           heads that retrieved it
-  int32_t* wl_pre;         // [BG, Umax+1]         first token (steady zone first)
-  int32_t* grp;            // [BG, 4]: n_entries, n_tok, n_chunks, n_corr
-  int32_t* chunk_e0;       // [BG, max_chunks_g]   first entry of each chunk
+  int32_t* wl_mask;        // [BG, Umax]             heads that retrieved it
+  uint32_t* rowmap;        // [BG, NS + Nc] token -> row | steady flag (bit 23) | head mask << 24
+  int32_t* grp;            // [BG, 4]: n_entries, n_tok
   float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
   float* est_num;          // [BG, est_tiles_g, G, d]
   float* att_md;           // [BG, att_items_g, G, 2]
   float* att_num;          // [BG, att_items_g, G, d]
   // shapes
-  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, max_chunks_g, est_tiles_g, att_items_g;
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g;
   float scale;
 };
 
