@@ -142,6 +142,8 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_all_sel = o;  o = align256(o + BH * 4);
   L.off_wl_cid = o;   o = align256(o + BG * L.Umax * 4);
   L.off_wl_mask = o;  o = align256(o + BG * L.Umax * 4);
+  L.off_wl_row0 = o;  o = align256(o + BG * L.Umax * 4);
+  L.off_wl_pre = o;   o = align256(o + BG * (L.Umax + 1) * 4);
   L.off_rowmap = o;   o = align256(o + BG * ((size_t)p.n_steady + p.Nc) * 4);
   L.off_grp = o;      o = align256(o + BG * 4 * 4);
   L.off_est_md = o;   o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
@@ -257,6 +259,8 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
   a.wl_cid = reinterpret_cast<int32_t*>(base + L.off_wl_cid);
   a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
+  a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
+  a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
   a.rowmap = reinterpret_cast<uint32_t*>(base + L.off_rowmap);
   a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
   a.est_md = reinterpret_cast<float*>(base + L.off_est_md);

@@ -35,6 +35,8 @@ namespace wi {
 constexpr int kScoreThreads = 256;
 
 // ============================================================================ k_score_est
+// grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid or value
+// sum row (256 B in bf16) is read as four 64-byte pieces by four lanes in one instruction.
 template <typename T, int G>
 __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
@@ -47,64 +49,68 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   const int C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
+  if (tile == 0 && tid == 0) a.counters[bg] = 0u;    // arrivals of the group's heads in k_select
+  if (C == 0) return;
+  const int nrows = min(kEstTile, C - tile * kEstTile);
   const int cbase = tile * kEstTile + w * 32;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
   const T* sv = static_cast<const T*>(a.sv) + ((size_t)bg * C + (size_t)tile * kEstTile) * kD;
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
-  if (tile == 0 && tid == 0) a.counters[bg] = 0u;    // arrivals of the group's heads in k_select
-  if (C == 0) return;
-  const int nrows = min(kEstTile, C - tile * kEstTile);
 
-  // value sums of the tile: thread (w, lane) owns rows w + 4i and dims 2*lane, 2*lane+1.  The
-  // loads are issued first; they do not depend on the scores.
-  float2 svv[kEstTile / 4];
+  // value sums: lane (lr, rg = lg) of wave w owns rows w*32 + 4i + rg and dims [8 lr, 8 lr + 8).
+  // Issued first: they do not depend on the scores.
+  u32x4_t svr[8];
+  [[maybe_unused]] u32x4_t svr_hi[8];
 #pragma unroll
-  for (int i = 0; i < kEstTile / 4; ++i) {
-    const int r = w + 4 * i;
-    svv[i] = make_float2(0.f, 0.f);
+  for (int i = 0; i < 8; ++i) {
+    const int r = w * 32 + 4 * i + lg;
+    svr[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (sizeof(T) == 4) svr_hi[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (r < nrows) {
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(sv + (size_t)r * kD + 2 * lane);
-        svv[i] = make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
-      } else {
-        svv[i] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sv) + (size_t)r * kD + 2 * lane);
-      }
+      const T* p = sv + (size_t)r * kD + 8 * lr;
+      svr[i] = *reinterpret_cast<const u32x4_t*>(p);
+      if constexpr (sizeof(T) == 4) svr_hi[i] = *reinterpret_cast<const u32x4_t*>(p + 4);
     }
   }
   if (tid < kEstTile) sh_n[tid] = tid < nrows ? (float)szs[tile * kEstTile + tid] : 0.f;
 
   if constexpr (sizeof(T) == 2) {
-    // A = query heads (row = lane&15), B = centroids (column = lane&15).  Along k, lane group lg
-    // owns dims [32*lg, 32*lg+32); MFMA step s consumes dims 32*lg + 8s .. +8 on both operands.
+    // A = query heads (row = lane&15), B = centroids (column = lane&15).  MFMA step s consumes
+    // dims 32 s + 8 lg .. +8 on both operands, so the four lanes of a row read 64 contiguous bytes.
     bf16x8_t qa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * lg + 8 * s);
+      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
       else qa[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    bf16x8_t mb[2][4];
+    int sz[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = cbase + 16 * t + lr;
+      sz[t] = 0;
+      if (c < C) {
+        sz[t] = szs[c];
+        const T* row = mu + (size_t)c * kD + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mb[t][s] = *reinterpret_cast<const bf16x8_t*>(row + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mb[t][s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int c = cbase + 16 * t + lr;
-      bf16x8_t mb[4];
-      int sz = 0;
-      if (c < C) {
-        sz = szs[c];
-        const T* row = mu + (size_t)c * kD + 32 * lg;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) mb[s] = *reinterpret_cast<const bf16x8_t*>(row + 8 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) mb[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      }
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], mb[s], acc, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], mb[t][s], acc, 0, 0, 0);
       float n2 = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { const float x = (float)mb[s][e]; n2 += x * x; }
+        for (int e = 0; e < 8; ++e) { const float x = (float)mb[t][s][e]; n2 += x * x; }
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
       const int cl = w * 32 + 16 * t + lr;
@@ -113,21 +119,21 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
         const int h = 4 * lg + r;
         if (h < G) {
           if (c < C) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
-          sh_s[h][cl] = (c < C && sz > 0) ? acc[r] * a.scale : -INFINITY;
+          sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
         }
       }
       if (lg == 0 && c < C) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
     }
   } else {
-    // fp32: 16x16x4 MFMA, 32 steps; step s consumes dim 32*lg + s on both operands.
+    // fp32: 16x16x4 MFMA, 32 steps; lane (lr, lg) loads dims 16 j + 4 lg .. +4 (j = 0..7) and step
+    // 4 j + e consumes dim 16 j + 4 lg + e on both operands.
     float qa[32];
 #pragma unroll
-    for (int s = 0; s < 32; s += 8) {
-      float tmp[8];
-      if (lr < G) St<float>::load8(reinterpret_cast<const float*>(qg) + (size_t)lr * kD + 32 * lg + s, tmp);
-      else for (int e = 0; e < 8; ++e) tmp[e] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qa[s + e] = tmp[e];
+    for (int j = 0; j < 8; ++j) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (lr < G) v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(qg) + (size_t)lr * kD + 16 * j + 4 * lg);
+      qa[4 * j] = __uint_as_float(v.x); qa[4 * j + 1] = __uint_as_float(v.y);
+      qa[4 * j + 2] = __uint_as_float(v.z); qa[4 * j + 3] = __uint_as_float(v.w);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -136,13 +142,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
       int sz = 0;
       if (c < C) {
         sz = szs[c];
-        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 32 * lg;
+        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 4 * lg;
 #pragma unroll
-        for (int s = 0; s < 32; s += 8) {
-          float tmp[8];
-          St<float>::load8(row + s, tmp);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mb[s + e] = tmp[e];
+        for (int j = 0; j < 8; ++j) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + 16 * j);
+          mb[4 * j] = __uint_as_float(v.x); mb[4 * j + 1] = __uint_as_float(v.y);
+          mb[4 * j + 2] = __uint_as_float(v.z); mb[4 * j + 3] = __uint_as_float(v.w);
         }
       } else {
 #pragma unroll
@@ -182,23 +187,46 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     if (lane == 0) { sh_m[h] = m; sh_den[h] = dn; }
   }
   __syncthreads();
-  float2 acc[G];
+  float acc[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = make_float2(0.f, 0.f);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-  for (int i = 0; i < kEstTile / 4; ++i) {
-    const int r = w + 4 * i;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = w * 32 + 4 * i + lg;
+    float v[8];
+    if constexpr (sizeof(T) == 2) {
+      const u32x4_t u = svr[i];
+      v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+      v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+      v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+      v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+    } else {
+      v[0] = __uint_as_float(svr[i].x); v[1] = __uint_as_float(svr[i].y);
+      v[2] = __uint_as_float(svr[i].z); v[3] = __uint_as_float(svr[i].w);
+      v[4] = __uint_as_float(svr_hi[i].x); v[5] = __uint_as_float(svr_hi[i].y);
+      v[6] = __uint_as_float(svr_hi[i].z); v[7] = __uint_as_float(svr_hi[i].w);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float wt = sh_w[h][r];
-      acc[h].x += wt * svv[i].x;
-      acc[h].y += wt * svv[i].y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += wt * v[e];
     }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    sh_num[w][h][2 * lane] = acc[h].x;
-    sh_num[w][h][2 * lane + 1] = acc[h].y;
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[h][e] += __shfl_xor(acc[h][e], 16);
+      acc[h][e] += __shfl_xor(acc[h][e], 32);
+    }
+  if (lg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh_num[w][h][8 * lr + e] = acc[h][e];
   }
   __syncthreads();
   const size_t slot = (size_t)bg * a.est_tiles_g + tile;
@@ -307,7 +335,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   return last;
 }
 
-constexpr int kSelKPT = 16;         // clusters per thread per register round
+constexpr int kSelKPT = 16;         // clusters per thread held in registers
 constexpr int kBins = 2048;         // histogram bins over [min score, max score]
 constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
 
@@ -316,16 +344,20 @@ constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ra
 // 2048-bin histogram over [min, max] and a rank count inside the threshold bin (a radix select
 // over the order keys covers bins too full to rank); 2) clusters above t + 2 delta are in, those
 // below t - 2 delta are out (delta bounds |fp32 score - canonical fp64 score|); 3) the band in
-// between is re-scored canonically and ranked by (-sigma, id).  The last head of a KV group to
-// finish builds the group's work list: the union of the heads' clusters with a head mask, a
-// token -> row map (steady zone first), and the list the estimation corrections run over.
+// between is re-scored canonically and ranked by (-sigma, id).  Thread t visits clusters
+// t, t + NT, t + 2 NT, ... so every global access is coalesced; id-ordered lists come from
+// bitmaps.  The last head of a KV group to finish builds the group's work list: the union of the
+// heads' clusters with a head mask, a token -> row map (steady zone first) and the list the
+// estimation corrections run over.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
-  extern __shared__ uint32_t bits[];                 // [W32] retrieved-cluster bitmap
+  extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t cand[kCandMax];
+  __shared__ int32_t u_row0[kCandMax];
+  __shared__ int32_t u_msk[kCandMax];
   __shared__ int iscr[48];
-  __shared__ float fred[8][4];
+  __shared__ float fred[8][5];
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
   __shared__ int sh_i[8];
@@ -335,51 +367,59 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, bg = b * a.Hkv + g;
   const int C = a.C, W32 = a.W32;
+  uint32_t* bits = dynl;
+  uint32_t* bbits = dynl + W32;
   const int32_t* sizes = a.sizes + (size_t)bg * C;
   const float* sc = a.scores + (size_t)bh * C;
   const float* mnorm = a.mu_norm + (size_t)bg * C;
   const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
-  // thread t owns clusters [t*KPT, (t+1)*KPT), visited kSelKPT at a time
-  const int KPT = (C + NT - 1) / NT;
-  const int R = (KPT + kSelKPT - 1) / kSelKPT;
-  const bool cached = R <= 1;
-  const int cbeg = min(C, tid * KPT), cend = min(C, cbeg + KPT);
+  const int KPT = (C + NT - 1) / NT;          // thread t owns clusters j * NT + t, j < KPT
+  const bool cached = KPT <= kSelKPT;
 
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
-  for (int w = tid; w < W32; w += NT) bits[w] = 0u;
+  for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
 
   uint32_t kc[kSelKPT];
-  auto load_keys = [&](int r, uint32_t (&k)[kSelKPT]) {
-    if (cached) {
+  // fn(c, key) for every cluster of this thread, keys from registers or re-read in batches
+  auto visit = [&](auto&& fn) {
+    for (int j0 = 0; j0 < KPT; j0 += kSelKPT) {
+      uint32_t k[kSelKPT];
+      if (cached) {
 #pragma unroll
-      for (int i = 0; i < kSelKPT; ++i) k[i] = kc[i];
-      return;
+        for (int i = 0; i < kSelKPT; ++i) k[i] = kc[i];
+      } else {
+        int n[kSelKPT];
+        float s[kSelKPT];
+#pragma unroll
+        for (int i = 0; i < kSelKPT; ++i) {
+          const int c = (j0 + i) * NT + tid;
+          n[i] = 0; s[i] = 0.f;
+          if (c < C) { n[i] = sizes[c]; s[i] = sc[c]; }
+        }
+#pragma unroll
+        for (int i = 0; i < kSelKPT; ++i) k[i] = n[i] > 0 ? f32_order_key(s[i]) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kSelKPT; ++i) {
+        const int c = (j0 + i) * NT + tid;
+        if (c < C) fn(c, k[i]);
+      }
     }
-    int n[kSelKPT];
-    float s[kSelKPT];
-#pragma unroll
-    for (int i = 0; i < kSelKPT; ++i) {
-      const int c = cbeg + r * kSelKPT + i;
-      n[i] = 0; s[i] = 0.f;
-      if (c < cend) { n[i] = sizes[c]; s[i] = sc[c]; }
-    }
-#pragma unroll
-    for (int i = 0; i < kSelKPT; ++i) k[i] = n[i] > 0 ? f32_order_key(s[i]) : 0u;
   };
 
   // ---- pass 1: non-empty count, score range, largest centroid norm (and the key cache)
   int cnt = 0;
   float smax = -INFINITY, smin = INFINITY, mxn = 0.f;
-  for (int r = 0; r < R; ++r) {
+  for (int j0 = 0; j0 < KPT; j0 += kSelKPT) {
     int n[kSelKPT];
     float s[kSelKPT], nm[kSelKPT];
 #pragma unroll
     for (int i = 0; i < kSelKPT; ++i) {
-      const int c = cbeg + r * kSelKPT + i;
+      const int c = (j0 + i) * NT + tid;
       n[i] = 0; s[i] = 0.f; nm[i] = 0.f;
-      if (c < cend) { n[i] = sizes[c]; s[i] = sc[c]; nm[i] = mnorm[c]; }
+      if (c < C) { n[i] = sizes[c]; s[i] = sc[c]; nm[i] = mnorm[c]; }
     }
 #pragma unroll
     for (int i = 0; i < kSelKPT; ++i) {
@@ -395,35 +435,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   }
   {
-    float v0 = (float)cnt, v1 = smax, v2 = -smin, v3 = fmaxf(mxn, 0.f);
-    float q2 = qv * qv;
-    v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_max(v2); v3 = wave_max(v3); q2 = wave_sum(q2);
-    if (lane == 0) { fred[wv][0] = v0; fred[wv][1] = v1; fred[wv][2] = v2; fred[wv][3] = v3; iscr[32 + wv] = __float_as_int(q2); }
+    float v0 = (float)cnt, v1 = smax, v2 = -smin, v3 = mxn, v4 = qv * qv;
+    v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_max(v2); v3 = wave_max(v3); v4 = wave_sum(v4);
+    if (lane == 0) { fred[wv][0] = v0; fred[wv][1] = v1; fred[wv][2] = v2; fred[wv][3] = v3; fred[wv][4] = v4; }
     __syncthreads();
     float r0 = 0.f, r1 = -INFINITY, r2 = -INFINITY, r3 = 0.f, r4 = 0.f;
     for (int i = 0; i < NT / 64; ++i) {
-      r0 += fred[i][0]; r1 = fmaxf(r1, fred[i][1]); r2 = fmaxf(r2, fred[i][2]); r3 = fmaxf(r3, fred[i][3]);
-      r4 += __int_as_float(iscr[32 + i]);
+      r0 += fred[i][0]; r1 = fmaxf(r1, fred[i][1]); r2 = fmaxf(r2, fred[i][2]);
+      r3 = fmaxf(r3, fred[i][3]); r4 += fred[i][4];
     }
     cnt = (int)r0; smax = r1; smin = -r2; mxn = r3; qv = sqrtf(r4);
-    __syncthreads();
   }
   const int n_ne = cnt;
   const float qn = qv;
   const int k_eff = min(a.top_k, n_ne);
 
   if (k_eff > 0 && k_eff == n_ne) {
-    for (int r = 0; r < R; ++r) {
-      uint32_t k[kSelKPT];
-      load_keys(r, k);
-#pragma unroll
-      for (int i = 0; i < kSelKPT; ++i) {
-        const int c = cbeg + r * kSelKPT + i;
-        if (k[i] != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31));
-      }
-    }
+    visit([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
-    // ---- pass 2: histogram over [smin, smax] (monotone binning, so higher bins hold higher scores)
+    // ---- pass 2: histogram over [smin, smax] (monotone binning: higher bins, higher scores)
     for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
     const float span = smax - smin;
@@ -432,16 +462,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       const float s = f32_from_order_key(key);
       return min(kBins - 1, max(0, (int)((s - smin) * inv)));
     };
-    for (int r = 0; r < R; ++r) {
-      uint32_t k[kSelKPT];
-      load_keys(r, k);
-#pragma unroll
-      for (int i = 0; i < kSelKPT; ++i)
-        if (k[i] != 0u) atomicAdd(&hist[bin_of(k[i])], 1u);
-    }
+    visit([&](int c, uint32_t k) { if (k != 0u) atomicAdd(&hist[bin_of(k)], 1u); });
     __syncthreads();
-    // threshold bin: thread t owns bins kBins-1-4t .. kBins-4-4t (descending)
     {
+      // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
       constexpr int BPT = kBins / kSelThreads;
       int v = 0;
 #pragma unroll
@@ -456,6 +480,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
           run += hb;
         }
       }
+      if (tid == 0) sh_i[2] = 0;
       __syncthreads();
     }
     const int bstar = sh_i[0];
@@ -463,15 +488,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     const int ncand = (int)hist[bstar];
     uint32_t thr;
     if (ncand <= kCandMax) {
-      if (tid == 0) sh_i[2] = 0;
-      __syncthreads();
-      for (int r = 0; r < R; ++r) {
-        uint32_t k[kSelKPT];
-        load_keys(r, k);
-#pragma unroll
-        for (int i = 0; i < kSelKPT; ++i)
-          if (k[i] != 0u && bin_of(k[i]) == bstar) cand[atomicAdd(&sh_i[2], 1)] = k[i];
-      }
+      visit([&](int c, uint32_t k) { if (k != 0u && bin_of(k) == bstar) cand[atomicAdd(&sh_i[2], 1)] = k; });
       __syncthreads();
       // the rem-th largest candidate: gt < rem <= ge
       for (int i = tid; i < ncand; i += NT) {
@@ -494,35 +511,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qn * (1.0 + 1.0 / 1024) *
                              (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
-    int nb = 0, nin = 0;
-    for (int r = 0; r < R; ++r) {
-      uint32_t k[kSelKPT];
-      load_keys(r, k);
-#pragma unroll
-      for (int i = 0; i < kSelKPT; ++i) {
-        if (k[i] == 0u) continue;
-        const int c = cbeg + r * kSelKPT + i;
-        const double v = (double)f32_from_order_key(k[i]);
-        if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
-        else if (v >= lo) ++nb;
-      }
-    }
+    int nin = 0;
+    visit([&](int c, uint32_t k) {
+      if (k == 0u) return;
+      const double v = (double)f32_from_order_key(k);
+      if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
+      else if (v >= lo) atomicOr(&bbits[c >> 5], 1u << (c & 31));
+    });
+    const int n_in = block_isum(nin, iscr);          // includes a barrier
+    const int need = k_eff - n_in;
+    // band list in ascending id order from the band bitmap
+    const int perw = (W32 + NT - 1) / NT;
+    const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+    int nb = 0;
+    for (int w = w0; w < w1; ++w) nb += __popc(bbits[w]);
     int n_band;
     int pos = block_exclusive_scan(nb, iscr, &n_band);
-    const int n_in = block_isum(nin, iscr);
-    const int need = k_eff - n_in;
     int32_t* band = n_band <= kSmallBand ? band_lds : a.band_ids + (size_t)bh * C;
-    if (nb > 0) {
-      for (int r = 0; r < R; ++r) {
-        uint32_t k[kSelKPT];
-        load_keys(r, k);
-#pragma unroll
-        for (int i = 0; i < kSelKPT; ++i) {
-          if (k[i] == 0u) continue;
-          const double v = (double)f32_from_order_key(k[i]);
-          if (!(v > hi) && v >= lo) band[pos++] = cbeg + r * kSelKPT + i;
-        }
-      }
+    for (int w = w0; w < w1; ++w) {
+      uint32_t m = bbits[w];
+      while (m) { const int bit = __ffs(m) - 1; m &= m - 1; band[pos++] = w * 32 + bit; }
     }
     __syncthreads();
     if (need >= n_band) {
@@ -595,10 +603,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
+  const bool ul = n_entries <= kCandMax;           // entry tables in LDS
   int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
   int32_t* mskg = a.wl_mask + (size_t)bg * a.Umax;
-  int32_t* ucid = n_entries <= kCandMax ? reinterpret_cast<int32_t*>(cand) : cidg;
-  int32_t* umsk = n_entries <= kCandMax ? reinterpret_cast<int32_t*>(hist) : mskg;
+  int32_t* ucid = ul ? reinterpret_cast<int32_t*>(cand) : cidg;
+  int32_t* umsk = ul ? u_msk : mskg;
+  int32_t* urow = ul ? u_row0 : a.wl_row0 + (size_t)bg * a.Umax;
+  int32_t* upre = ul ? reinterpret_cast<int32_t*>(hist) : a.wl_pre + (size_t)bg * (a.Umax + 1);
   for (int w = w0; w < w1; ++w) {
     uint32_t hw[kMaxGroup];
     uint32_t u = 0u;
@@ -614,38 +625,87 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   }
   __syncthreads();
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
   const int pe = (n_entries + NT - 1) / NT;
   const int e0 = min(n_entries, tid * pe), e1 = min(n_entries, e0 + pe);
   int nt = 0;
-  for (int i = e0; i < e1; ++i) nt += sizes[ucid[i]];
+  for (int i = e0; i < e1; ++i) {
+    const int c = ucid[i];
+    const int sz = sizes[c];
+    urow[i] = off[c];
+    upre[i] = sz;                                   // sizes for now, prefix below
+    nt += sz;
+  }
   int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
   const int NS = a.NS;
   const int n_tok = NS + n_utok;
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
-  uint32_t* rmap = a.rowmap + (size_t)bg * (NS + a.Nc);
   for (int i = e0; i < e1; ++i) {
-    const int c = ucid[i], m = umsk[i];
-    const int r0 = off[c], sz = sizes[c];
-    if (ucid != cidg) { cidg[i] = c; mskg[i] = m; }
-    const uint32_t tag = (uint32_t)m << 24;
-    for (int j = 0; j < sz; ++j) rmap[NS + t + j] = (uint32_t)(r0 + j) | tag;
+    const int sz = upre[i];
+    upre[i] = NS + t;
     t += sz;
+    if (ul) { cidg[i] = ucid[i]; mskg[i] = umsk[i]; }
   }
-  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
-  for (int s = tid; s < NS; s += NT) rmap[s] = (uint32_t)s | stag;
   if (tid == 0) {
+    upre[n_entries] = n_tok;
     a.grp[(size_t)bg * 4 + 0] = n_entries;
     a.grp[(size_t)bg * 4 + 1] = n_tok;
+  }
+  __syncthreads();
+  // token -> row map, written coalesced: row | steady flag (bit 23) | head mask << 24
+  uint32_t* rmap = a.rowmap + (size_t)bg * (NS + a.Nc);
+  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
+  for (int tk = tid; tk < n_tok; tk += NT) {
+    uint32_t v;
+    if (tk < NS) {
+      v = (uint32_t)tk | stag;
+    } else {
+      int lo2 = 0, hi2 = n_entries - 1;           // last entry with upre[e] <= tk
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2 + 1) >> 1;
+        if (upre[mid] <= tk) lo2 = mid; else hi2 = mid - 1;
+      }
+      v = (uint32_t)(urow[lo2] + (tk - upre[lo2])) | ((uint32_t)umsk[lo2] << 24);
+    }
+    rmap[tk] = v;
   }
 }
 
 // ============================================================================ k_attend
 constexpr int kAttThreads = 256;
-constexpr int kRowsPerLane = 4;                       // rows per lane group per sub-chunk
-constexpr int kSubChunk = 4 * 4 * kRowsPerLane;       // 4 waves x 4 lane groups x rows
+constexpr int kAttStage = 512;      // row-map entries staged in LDS at a time
 
-// Online softmax state of one lane group (16 lanes share a row; lane&15 owns 8 dims).
+// Rows per lane group per pass (a lane group is 16 lanes sharing a row, lane&15 owns 8 dims).
+template <typename T> struct AttRows { static constexpr int R = 4; };
+template <> struct AttRows<float> { static constexpr int R = 2; };
+
+// Packed row piece: 8 elements of one row (16 B of bf16 or 32 B of fp32).
+template <typename T> struct Piece;
+template <> struct Piece<uint16_t> {
+  u32x4_t v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ void zero() { v = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+};
+template <> struct Piece<float> {
+  u32x4_t v0, v1;
+  __device__ void load(const float* p) {
+    v0 = *reinterpret_cast<const u32x4_t*>(p);
+    v1 = *reinterpret_cast<const u32x4_t*>(p + 4);
+  }
+  __device__ void zero() { v0 = u32x4_t{0u, 0u, 0u, 0u}; v1 = v0; }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v0.x); o[1] = __uint_as_float(v0.y); o[2] = __uint_as_float(v0.z); o[3] = __uint_as_float(v0.w);
+    o[4] = __uint_as_float(v1.x); o[5] = __uint_as_float(v1.y); o[6] = __uint_as_float(v1.z); o[7] = __uint_as_float(v1.w);
+  }
+};
+
+// Online softmax state of one lane group.
 template <int G>
 struct OState {
   float m[G], den[G], num[G][8];
@@ -657,27 +717,35 @@ struct OState {
       for (int e = 0; e < 8; ++e) num[h][e] = 0.f;
     }
   }
-  // fold rows with logits l (-inf = absent), denominator weights wd and values v
-  __device__ void add(const float (&l)[kRowsPerLane][G], const float (&wd)[kRowsPerLane],
-                      const float (&v)[kRowsPerLane][8]) {
+  // fold R rows with logits l (-inf = absent), denominator weights wd and packed values v
+  template <int R, typename P>
+  __device__ void add(const float (&l)[R][G], const float (&wd)[R], const P (&v)[R]) {
+    float mx[G], sc[G];
+    bool any = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = m[h];
+      mx[h] = m[h];
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) mx = fmaxf(mx, l[i][h]);
-      if (mx == -INFINITY) continue;
-      const float sc = m[h] == -INFINITY ? 0.f : __expf(m[h] - mx);
-      den[h] *= sc;
+      for (int i = 0; i < R; ++i) mx[h] = fmaxf(mx[h], l[i][h]);
+      any |= mx[h] != -INFINITY;
+      sc[h] = (m[h] == -INFINITY || mx[h] == -INFINITY) ? 0.f : __expf(m[h] - mx[h]);
+      den[h] *= sc[h];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) num[h][e] *= sc;
+      for (int e = 0; e < 8; ++e) num[h][e] *= sc[h];
+      m[h] = mx[h];
+    }
+    if (!any) return;
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        const float p = l[i][h] == -INFINITY ? 0.f : __expf(l[i][h] - mx);
+    for (int i = 0; i < R; ++i) {
+      float vf[8];
+      v[i].unpack(vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = l[i][h] == -INFINITY ? 0.f : __expf(l[i][h] - mx[h]);
         den[h] += wd[i] * p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) num[h][e] += p * v[i][e];
+        for (int e = 0; e < 8; ++e) num[h][e] += p * vf[e];
       }
-      m[h] = mx;
     }
   }
 };
@@ -689,7 +757,6 @@ __device__ void write_partial(OState<G>& st, size_t slot, float* md_out, float* 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    // across the four lane groups of the wave
 #pragma unroll
     for (int x = 16; x <= 32; x <<= 1) {
       const float om = __shfl_xor(st.m[h], x);
@@ -731,7 +798,31 @@ __device__ void write_partial(OState<G>& st, size_t slot, float* md_out, float* 
     md_out[(slot * G + h) * 2] = mx;
     md_out[(slot * G + h) * 2 + 1] = d;
   }
-  __syncthreads();
+}
+
+// q . k for 8 dims held by this lane, completed across the 16 lanes of the row
+template <typename T>
+__device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t qa[4] = {qp.v.x, qp.v.y, qp.v.z, qp.v.w};
+    const uint32_t ka[4] = {kp.v.x, kp.v.y, kp.v.z, kp.v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qa[j]), __builtin_bit_cast(bf16x2_t, ka[j]), s, false);
+  } else {
+    float qf[8], kf[8];
+    qp.unpack(qf);
+    kp.unpack(kf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += qf[e] * kf[e];
+  }
+  s += __shfl_xor(s, 8);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
 }
 
 // grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
@@ -739,102 +830,103 @@ __device__ void write_partial(OState<G>& st, size_t slot, float* md_out, float* 
 // estimation terms of union entries [128 j, 128 j + 128) (the merge subtracts them).
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
+  constexpr int R = AttRows<T>::R;
+  constexpr int PASS = 16 * R;                 // 4 waves x 4 lane groups x R rows
   __shared__ float sh_m[4 * G], sh_den[4 * G];
   __shared__ float sh_num[4 * G * kD];
+  __shared__ uint32_t sh_ent[kAttStage];
   const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
   const int n_entries = a.grp[(size_t)bg * 4 + 0], n_tok = a.grp[(size_t)bg * 4 + 1];
   const size_t slot = (size_t)bg * a.att_items_g + s;
-  const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
   OState<G> st;
   st.init();
   if (s < S) {
+    const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+    Piece<T> qp[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qp[h].load(qg + (size_t)h * kD + 8 * lr);
     const int t0 = (int)(((int64_t)s * n_tok) / S), t1 = (int)(((int64_t)(s + 1) * n_tok) / S);
     const uint32_t* rmap = a.rowmap + (size_t)bg * (a.NS + a.Nc);
     const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
     const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
     const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * a.NS * kD;
-    float qf[G][8];
+    for (int z0 = t0; z0 < t1; z0 += kAttStage) {
+      const int z1 = min(t1, z0 + kAttStage);
+      __syncthreads();
+      for (int i = threadIdx.x; i < z1 - z0; i += kAttThreads) sh_ent[i] = rmap[z0 + i];
+      __syncthreads();
+      for (int c0 = z0; c0 < z1; c0 += PASS) {
+        uint32_t ent[R];
+        Piece<T> kr[R], vr[R];
 #pragma unroll
-    for (int h = 0; h < G; ++h) St<T>::load8(qg + (size_t)h * kD + 8 * lr, qf[h]);
-    for (int c0 = t0; c0 < t1; c0 += kSubChunk) {
-      uint32_t ent[kRowsPerLane];
-#pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        const int t = c0 + w * 16 + 4 * i + rg;
-        ent[i] = t < t1 ? rmap[t] : 0u;
-      }
-      float kr[kRowsPerLane][8], v[kRowsPerLane][8], wd[kRowsPerLane], l[kRowsPerLane][G];
-#pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        const uint32_t en = ent[i];
-        const int row = (int)(en & 0x7fffffu);
-        const T* kq = (en & (1u << 23)) ? ks + (size_t)row * kD : kp + (size_t)row * kD;
-        const T* vq = (en & (1u << 23)) ? vs + (size_t)row * kD : vp + (size_t)row * kD;
-        if ((en >> 24) != 0u) {
-          St<T>::load8(kq + 8 * lr, kr[i]);
-          St<T>::load8(vq + 8 * lr, v[i]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { kr[i][e] = 0.f; v[i][e] = 0.f; }
+        for (int i = 0; i < R; ++i) {
+          const int t = c0 + w * (4 * R) + 4 * i + rg;
+          ent[i] = t < z1 ? sh_ent[t - z0] : 0u;
+          const int row = (int)(ent[i] & 0x7fffffu);
+          const bool stdy = (ent[i] >> 23) & 1u;
+          if ((ent[i] >> 24) != 0u) {
+            kr[i].load((stdy ? ks : kp) + (size_t)row * kD + 8 * lr);
+            vr[i].load((stdy ? vs : vp) + (size_t)row * kD + 8 * lr);
+          } else {
+            kr[i].zero();
+            vr[i].zero();
+          }
         }
-        wd[i] = 1.f;
-      }
+        float l[R][G], wd[R];
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        const uint32_t mk = ent[i] >> 24;
+        for (int i = 0; i < R; ++i) {
+          const uint32_t mk = ent[i] >> 24;
+          wd[i] = 1.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float x = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x += qf[h][e] * kr[i][e];
-          x += __shfl_xor(x, 8);
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 2);
-          x += __shfl_xor(x, 1);
-          l[i][h] = ((mk >> h) & 1u) ? x * a.scale : -INFINITY;
+          for (int h = 0; h < G; ++h) {
+            const float x = row_dot<T>(qp[h], kr[i]);
+            l[i][h] = ((mk >> h) & 1u) ? x * a.scale : -INFINITY;
+          }
         }
+        st.template add<R>(l, wd, vr);
       }
-      st.add(l, wd, v);
     }
   } else {
-    const int e0 = (s - S) * kEstTile;
+    const int e0 = (s - S) * kEstTile, e1 = min(n_entries, e0 + kEstTile);
     const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
     const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
     const int32_t* szs = a.sizes + (size_t)bg * a.C;
     const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
     const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
-    for (int c0 = e0; c0 < min(n_entries, e0 + kEstTile); c0 += kSubChunk) {
-      float v[kRowsPerLane][8], wd[kRowsPerLane], l[kRowsPerLane][G];
+    for (int c0 = e0; c0 < e1; c0 += PASS) {
+      Piece<T> vr[R];
+      float wd[R], l[R][G];
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        const int e = c0 + w * 16 + 4 * i + rg;
-        const bool live = e < min(n_entries, e0 + kEstTile);
+      for (int i = 0; i < R; ++i) {
+        const int e = c0 + w * (4 * R) + 4 * i + rg;
+        const bool live = e < e1;
         const int c = live ? cid[e] : 0;
         const int m = live ? msk[e] : 0;
         wd[i] = live ? (float)szs[c] : 0.f;
-        if (live) St<T>::load8(sv + (size_t)c * kD + 8 * lr, v[i]);
-        else for (int x = 0; x < 8; ++x) v[i][x] = 0.f;
+        if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
+        else vr[i].zero();
 #pragma unroll
         for (int h = 0; h < G; ++h)
           l[i][h] = ((m >> h) & 1) ? a.scores[(hbase + h) * a.C + c] * a.scale : -INFINITY;
       }
-      st.add(l, wd, v);
+      st.template add<R>(l, wd, vr);
     }
   }
   write_partial<G>(st, slot, a.att_md, a.att_num, sh_m, sh_den, sh_num);
 }
 
 // ============================================================================ k_merge
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;
 constexpr int kMergeLds = 8192;
+constexpr int kMergeU = 16;
 
 // out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
 // num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact splits (+1),
 // retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
-// only its exact splits.
+// only its exact splits.  The first batch of numerators is fetched before the maximum is known.
 __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   __shared__ float sh_f[kMergeLds];
   __shared__ float sh_red[32];
@@ -856,6 +948,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     if (p < PE) return a.est_num + (((size_t)bg * a.est_tiles_g + p) * G + hi) * kD;
     return a.att_num + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * kD;
   };
+  const int col = tid & 31, rep = tid >> 5;
+  constexpr int RP = kMergeThreads / 32;
+  float4 v[kMergeU];
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) {
+    const int p = rep + u * RP;
+    v[u] = p < P ? *reinterpret_cast<const float4*>(num_of(p) + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float mx = -INFINITY;
   for (int p = tid; p < PE + S; p += kMergeThreads) {
     const float2 md = *reinterpret_cast<const float2*>(md_of(p));
@@ -873,39 +973,41 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   }
   const float den = block_sum(dn, sh_red);
   __syncthreads();
-  // numerators: 32 float4 columns cover the head's 128 dims; 8 replicas split the partials
-  const int col = tid & 31, rep = tid >> 5;
-  constexpr int R = kMergeThreads / 32;
+  auto factor = [&](int p) -> float {
+    if (f_lds) return sh_f[p];
+    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
+    const float f = md.y > 0.f ? __expf(md.x - M) : 0.f;
+    return p >= PE + S ? -f : f;
+  };
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p0 = rep; p0 < P; p0 += 8 * R) {
-    float4 v[8];
-    float f[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int p = p0 + u * R;
-      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      f[u] = 0.f;
-      if (p < P) {
-        v[u] = *reinterpret_cast<const float4*>(num_of(p) + 4 * col);
-        if (f_lds) {
-          f[u] = sh_f[p];
-        } else {
-          const float2 md = *reinterpret_cast<const float2*>(md_of(p));
-          f[u] = md.y > 0.f ? __expf(md.x - M) : 0.f;
-          if (p >= PE + S) f[u] = -f[u];
-        }
-      }
+  for (int u = 0; u < kMergeU; ++u) {
+    const int p = rep + u * RP;
+    if (p < P) {
+      const float f = factor(p);
+      acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+    }
+  }
+  for (int p0 = rep + kMergeU * RP; p0 < P; p0 += kMergeU * RP) {
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) {
+      const int p = p0 + u * RP;
+      v[u] = p < P ? *reinterpret_cast<const float4*>(num_of(p) + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc.x += f[u] * v[u].x; acc.y += f[u] * v[u].y; acc.z += f[u] * v[u].z; acc.w += f[u] * v[u].w;
+    for (int u = 0; u < kMergeU; ++u) {
+      const int p = p0 + u * RP;
+      if (p < P) {
+        const float f = factor(p);
+        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+      }
     }
   }
   sh_acc[rep][col] = acc;
   __syncthreads();
   if (tid < 32) {
     float4 s = sh_acc[0][tid];
-    for (int r = 1; r < R; ++r) {
+    for (int r = 1; r < RP; ++r) {
       const float4 t = sh_acc[r][tid];
       s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
     }
@@ -924,7 +1026,7 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 4, s, a);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_ATTEND, s);

@@ -26,7 +26,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct DecodeLayout {
   int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g;
   size_t off_counters, off_scores, off_mu_norm, off_sel_bits, off_band_ids, off_band_key,
-      off_all_sel, off_wl_cid, off_wl_mask, off_rowmap, off_grp, off_est_md, off_est_num,
+      off_all_sel, off_wl_cid, off_wl_mask, off_wl_row0, off_wl_pre, off_rowmap, off_grp, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
 };
 DecodeLayout decode_layout(const wi_decode_params& p);
@@ -55,6 +55,8 @@ struct DecodeArgs {
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
   int32_t* wl_cid;         // [BG, Umax] union entries: cluster id
   int32_t* wl_mask;        // [BG, Umax]             heads that retrieved it
+  int32_t* wl_row0;        // [BG, Umax]             first k_perm row (when not held in LDS)
+  int32_t* wl_pre;         // [BG, Umax+1]           first token (when not held in LDS)
   uint32_t* rowmap;        // [BG, NS + Nc] token -> row | steady flag (bit 23) | head mask << 24
   int32_t* grp;            // [BG, 4]: n_entries, n_tok
   float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
