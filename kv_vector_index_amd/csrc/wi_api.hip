@@ -127,10 +127,11 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.W32 = (int)ceil_div(p.C, 32);
   L.Umax = (int)std::min<int64_t>(p.C, (int64_t)L.G * p.top_k);
   L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
-  // about 1024 exact-attention workgroups in all, none with less than 64 tokens of context
-  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(1024, L.BG),
+  // about 1024 exact-attention workgroups in all (every one resident at once on 256 CUs),
+  // none with less than 64 tokens of context; each writes an exact and a correction partial
+  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(1024 / std::max(1, L.BG),
                                                             ceil_div((int64_t)p.n_steady + p.Nc, 64)));
-  L.att_items_g = L.att_split + (int)ceil_div(L.Umax, kEstTile);
+  L.att_items_g = 2 * L.att_split;
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G;
   size_t o = 0;
   L.off_counters = o; o = align256(o + BG * 4);

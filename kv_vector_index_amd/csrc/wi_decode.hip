@@ -32,6 +32,10 @@
 
 namespace wi {
 
+#ifdef WI_TRACE
+__device__ unsigned long long g_trace[64][8192];
+#endif
+
 constexpr int kScoreThreads = 256;
 
 // ============================================================================ k_score_est
@@ -39,6 +43,7 @@ constexpr int kScoreThreads = 256;
 // sum row (256 B in bf16) is read as four 64-byte pieces by four lanes in one instruction.
 template <typename T, int G>
 __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
+  WI_TP(30);
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
   __shared__ float sh_n[kEstTile];          // cluster sizes
@@ -74,6 +79,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     }
   }
   if (tid < kEstTile) sh_n[tid] = tid < nrows ? (float)szs[tile * kEstTile + tid] : 0.f;
+  WI_TP(31);
 
   if constexpr (sizeof(T) == 2) {
     // A = query heads (row = lane&15), B = centroids (column = lane&15).  MFMA step s consumes
@@ -174,6 +180,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     }
   }
   __syncthreads();
+  WI_TP(32);
 
   // estimation partial of the tile: m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
   for (int h = w; h < G; h += kScoreThreads / 64) {
@@ -338,6 +345,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 constexpr int kSelKPT = 16;         // clusters per thread held in registers
 constexpr int kBins = 2048;         // histogram bins over [min score, max score]
 constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
+constexpr int kSelStage = 8192;     // cluster sizes and offsets kept in LDS up to this many clusters
 
 // Per query head: the retrieval zone is the k_eff = min(top_k, #non-empty) non-empty clusters
 // first in the order (-sigma_c, c).  1) the k_eff-th largest fp32 score t is found with a
@@ -351,7 +359,9 @@ constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ra
 // estimation corrections run over.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
-  extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
+  WI_TP(0);
+  extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap,
+                                                     // then sizes [C] and offsets [C] if C <= kSelStage
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t cand[kCandMax];
   __shared__ int32_t u_row0[kCandMax];
@@ -369,6 +379,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   const int C = a.C, W32 = a.W32;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
+  const bool staged = C <= kSelStage;
+  int32_t* lsz = reinterpret_cast<int32_t*>(dynl + 2 * W32);
+  int32_t* loff = lsz + C;
   const int32_t* sizes = a.sizes + (size_t)bg * C;
   const float* sc = a.scores + (size_t)bh * C;
   const float* mnorm = a.mu_norm + (size_t)bg * C;
@@ -380,6 +393,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
+  WI_TP(1);
 
   uint32_t kc[kSelKPT];
   // fn(c, key) for every cluster of this thread, keys from registers or re-read in batches
@@ -421,6 +435,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       n[i] = 0; s[i] = 0.f; nm[i] = 0.f;
       if (c < C) { n[i] = sizes[c]; s[i] = sc[c]; nm[i] = mnorm[c]; }
     }
+    if (staged) {
+#pragma unroll
+      for (int i = 0; i < kSelKPT; ++i) {
+        const int c = (j0 + i) * NT + tid;
+        if (c < C) { lsz[c] = n[i]; loff[c] = a.offsets[(size_t)bg * (C + 1) + c]; }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kSelKPT; ++i) {
       uint32_t key = 0u;
@@ -446,6 +467,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
     cnt = (int)r0; smax = r1; smin = -r2; mxn = r3; qv = sqrtf(r4);
   }
+  WI_TP(3);
   const int n_ne = cnt;
   const float qn = qv;
   const int k_eff = min(a.top_k, n_ne);
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     };
     visit([&](int c, uint32_t k) { if (k != 0u) atomicAdd(&hist[bin_of(k)], 1u); });
     __syncthreads();
+  WI_TP(4);
     {
       // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
       constexpr int BPT = kBins / kSelThreads;
@@ -484,6 +507,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       __syncthreads();
     }
     const int bstar = sh_i[0];
+  WI_TP(5);
     const int rem = k_eff - sh_i[1];
     const int ncand = (int)hist[bstar];
     uint32_t thr;
@@ -499,6 +523,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       }
       __syncthreads();
       thr = (uint32_t)sh_i[3];
+  WI_TP(6);
     } else {
       int rr;
       thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) {
@@ -520,6 +545,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     });
     const int n_in = block_isum(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
+  WI_TP(7);
     // band list in ascending id order from the band bitmap
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
@@ -573,6 +599,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __syncthreads();
 
   // ---- publish: bitmap (coherent, read by the group's last head), ascending ids, flag
+  WI_TP(8);
   for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
   if (a.sel_ids) {
     const int perw = (W32 + NT - 1) / NT;
@@ -589,7 +616,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
   }
   if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
+  WI_TP(9);
   if (!arrive_last(a.counters + bg, (uint32_t)G, &sh_i[4])) return;
+  WI_TP(10);
 
   // ---- the group's work list (last head only)
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
@@ -603,6 +632,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
+  WI_TP(11);
   const bool ul = n_entries <= kCandMax;           // entry tables in LDS
   int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
   int32_t* mskg = a.wl_mask + (size_t)bg * a.Umax;
@@ -631,13 +661,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   int nt = 0;
   for (int i = e0; i < e1; ++i) {
     const int c = ucid[i];
-    const int sz = sizes[c];
-    urow[i] = off[c];
+    const int sz = staged ? lsz[c] : sizes[c];
+    urow[i] = staged ? loff[c] : off[c];
     upre[i] = sz;                                   // sizes for now, prefix below
     nt += sz;
   }
   int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
+  WI_TP(12);
   const int NS = a.NS;
   const int n_tok = NS + n_utok;
   for (int i = e0; i < e1; ++i) {
@@ -652,23 +683,35 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     a.grp[(size_t)bg * 4 + 1] = n_tok;
   }
   __syncthreads();
-  // token -> row map, written coalesced: row | steady flag (bit 23) | head mask << 24
+  // token -> row map: row | steady flag (bit 23) | head mask << 24.  Thread t writes tokens
+  // [t*per, (t+1)*per): one search for its first entry, then a walk along the entries.
   uint32_t* rmap = a.rowmap + (size_t)bg * (NS + a.Nc);
   const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
-  for (int tk = tid; tk < n_tok; tk += NT) {
-    uint32_t v;
-    if (tk < NS) {
-      v = (uint32_t)tk | stag;
-    } else {
-      int lo2 = 0, hi2 = n_entries - 1;           // last entry with upre[e] <= tk
-      while (lo2 < hi2) {
-        const int mid = (lo2 + hi2 + 1) >> 1;
-        if (upre[mid] <= tk) lo2 = mid; else hi2 = mid - 1;
-      }
-      v = (uint32_t)(urow[lo2] + (tk - upre[lo2])) | ((uint32_t)umsk[lo2] << 24);
+  const int per = (n_tok + NT - 1) / NT;
+  const int tb = min(n_tok, tid * per), te = min(n_tok, tb + per);
+  int tk = tb;
+  for (; tk < min(te, NS); ++tk) rmap[tk] = (uint32_t)tk | stag;
+  if (tk < te) {
+    int lo2 = 0, hi2 = n_entries - 1;              // last entry with upre[e] <= tk
+    while (lo2 < hi2) {
+      const int mid = (lo2 + hi2 + 1) >> 1;
+      if (upre[mid] <= tk) lo2 = mid; else hi2 = mid - 1;
     }
-    rmap[tk] = v;
+    int en = lo2;
+    int base = upre[en], nxt = upre[en + 1];
+    uint32_t r0 = (uint32_t)urow[en], tag = (uint32_t)umsk[en] << 24;
+    for (; tk < te; ++tk) {
+      while (tk >= nxt) {
+        ++en;
+        base = nxt;
+        nxt = upre[en + 1];
+        r0 = (uint32_t)urow[en];
+        tag = (uint32_t)umsk[en] << 24;
+      }
+      rmap[tk] = (r0 + (uint32_t)(tk - base)) | tag;
+    }
   }
+  WI_TP(13);
 }
 
 // ============================================================================ k_attend
@@ -825,9 +868,10 @@ __device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp)
   return s;
 }
 
-// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
-// of its KV group's list (steady zone, then the retrieved clusters); workgroup S + j folds the
-// estimation terms of union entries [128 j, 128 j + 128) (the merge subtracts them).
+// grid (S, B*Hkv).  Workgroup s attends exactly over tokens [s n_tok / S, (s+1) n_tok / S) of its
+// KV group's list (steady zone, then the retrieved clusters) and folds the estimation terms of
+// union entries [s n_entries / S, (s+1) n_entries / S) into a second partial (the merge
+// subtracts it).
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
@@ -835,14 +879,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ float sh_m[4 * G], sh_den[4 * G];
   __shared__ float sh_num[4 * G * kD];
   __shared__ uint32_t sh_ent[kAttStage];
+  WI_TP(20);
   const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
   const int n_entries = a.grp[(size_t)bg * 4 + 0], n_tok = a.grp[(size_t)bg * 4 + 1];
-  const size_t slot = (size_t)bg * a.att_items_g + s;
+  WI_TP(21);
   OState<G> st;
   st.init();
-  if (s < S) {
+  {
     const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
     Piece<T> qp[G];
 #pragma unroll
@@ -889,8 +934,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
         st.template add<R>(l, wd, vr);
       }
     }
-  } else {
-    const int e0 = (s - S) * kEstTile, e1 = min(n_entries, e0 + kEstTile);
+  }
+  WI_TP(22);
+  write_partial<G>(st, (size_t)bg * a.att_items_g + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
+  // estimation terms of this workgroup's share of the retrieved clusters
+  st.init();
+  {
+    const int e0 = (int)(((int64_t)s * n_entries) / S), e1 = (int)(((int64_t)(s + 1) * n_entries) / S);
     const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
     const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
     const int32_t* szs = a.sizes + (size_t)bg * a.C;
@@ -915,7 +965,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
       st.template add<R>(l, wd, vr);
     }
   }
-  write_partial<G>(st, slot, a.att_md, a.att_num, sh_m, sh_den, sh_num);
+  __syncthreads();
+  write_partial<G>(st, (size_t)bg * a.att_items_g + S + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
+  WI_TP(23);
 }
 
 // ============================================================================ k_merge
@@ -928,6 +980,7 @@ constexpr int kMergeU = 16;
 // retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
 // only its exact splits.  The first batch of numerators is fetched before the maximum is known.
 __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
+  WI_TP(40);
   __shared__ float sh_f[kMergeLds];
   __shared__ float sh_red[32];
   __shared__ float4 sh_acc[kMergeThreads / 32][32];
@@ -1014,6 +1067,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * tid) = make_float4(s.x / den, s.y / den, s.z / den, s.w / den);
   }
   if (tid == 0 && a.lse) a.lse[bh] = M + __logf(den);
+  WI_TP(41);
 }
 
 // ============================================================================ launcher
@@ -1026,11 +1080,12 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
+  const size_t sel_lds = (size_t)a.W32 * 8 + (a.C <= kSelStage ? (size_t)a.C * 8 : 0);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), sel_lds, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_split, BG), dim3(kAttThreads), 0, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
@@ -1054,12 +1109,18 @@ hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStre
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
     attr_set = true;
   }
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);
 }
 
 }  // namespace wi
+
+#ifdef WI_TRACE
+extern "C" int wi_trace_read(void* dst, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(wi::g_trace), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif

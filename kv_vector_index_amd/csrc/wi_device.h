@@ -6,6 +6,15 @@
 
 namespace wi {
 
+// Phase timestamps for development builds (-DWI_TRACE): thread 0 of every block records the
+// constant-rate wall clock at each marker; wi_trace_read() copies the table out.
+#ifdef WI_TRACE
+extern __device__ unsigned long long g_trace[64][8192];
+#define WI_TP(ev) do { if (threadIdx.x == 0) ::wi::g_trace[ev][blockIdx.x + blockIdx.y * gridDim.x] = wall_clock64(); } while (0)
+#else
+#define WI_TP(ev) do { } while (0)
+#endif
+
 constexpr int kD = 128;     // head dimension the kernels are written for
 constexpr int kWave = 64;   // CDNA wavefront width
 
