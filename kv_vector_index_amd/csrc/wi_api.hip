@@ -127,30 +127,36 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.W32 = (int)ceil_div(p.C, 32);
   L.Umax = (int)std::min<int64_t>(p.C, (int64_t)L.G * p.top_k);
   L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
-  // about 1024 exact-attention workgroups in all (every one resident at once on 256 CUs),
-  // none with less than 64 tokens of context; each writes an exact and a correction partial
-  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(1024 / std::max(1, L.BG),
-                                                            ceil_div((int64_t)p.n_steady + p.Nc, 64)));
-  L.att_items_g = 2 * L.att_split;
+  // about 1024 attention workgroups in all, so that every one is resident at once on 256 CUs:
+  // S split the token list (none with less than 64 tokens of context), Sc ~ 1/32 of them fold
+  // the retrieved clusters' estimation terms
+  const int64_t ntok_max = (int64_t)p.n_steady + p.Nc;
+  const int total = (int)std::max<int64_t>(2, std::min<int64_t>(1024 / std::max(1, L.BG), ceil_div(ntok_max, 64) + 1));
+  const int Sc = (int)std::max<int64_t>(1, ceil_div(total, 32));
+  L.att_split = std::max(1, total - Sc);
+  L.att_items_g = L.att_split + Sc;
+  L.part_cap = (int)std::max<int64_t>(1, ceil_div(ntok_max, L.att_split));
+  L.corr_cap = (int)std::max<int64_t>(1, ceil_div(L.Umax, Sc));
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G;
   size_t o = 0;
-  L.off_counters = o; o = align256(o + BG * 4);
-  L.off_scores = o;   o = align256(o + BH * C * 4);
-  L.off_mu_norm = o;  o = align256(o + BG * C * 4);
-  L.off_sel_bits = o; o = align256(o + BH * L.W32 * 4);
-  L.off_band_ids = o; o = align256(o + BH * C * 4);
-  L.off_band_key = o; o = align256(o + BH * C * 8);
-  L.off_all_sel = o;  o = align256(o + BH * 4);
-  L.off_wl_cid = o;   o = align256(o + BG * L.Umax * 4);
-  L.off_wl_mask = o;  o = align256(o + BG * L.Umax * 4);
-  L.off_wl_row0 = o;  o = align256(o + BG * L.Umax * 4);
-  L.off_wl_pre = o;   o = align256(o + BG * (L.Umax + 1) * 4);
-  L.off_rowmap = o;   o = align256(o + BG * ((size_t)p.n_steady + p.Nc) * 4);
-  L.off_grp = o;      o = align256(o + BG * 4 * 4);
-  L.off_est_md = o;   o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
-  L.off_est_num = o;  o = align256(o + BG * L.est_tiles_g * G * kD * 4);
-  L.off_att_md = o;   o = align256(o + BG * L.att_items_g * G * 2 * 4);
-  L.off_att_num = o;  o = align256(o + BG * L.att_items_g * G * kD * 4);
+  L.off_counters = o;  o = align256(o + BG * 4);
+  L.off_keys = o;      o = align256(o + BH * C * 4);
+  L.off_tile_norm = o; o = align256(o + BG * L.est_tiles_g * 4);
+  L.off_sel_bits = o;  o = align256(o + BH * L.W32 * 4);
+  L.off_band_ids = o;  o = align256(o + BH * C * 4);
+  L.off_band_key = o;  o = align256(o + BH * C * 8);
+  L.off_all_sel = o;   o = align256(o + BH * 4);
+  L.off_wl_cid = o;    o = align256(o + BG * L.Umax * 4);
+  L.off_wl_mask = o;   o = align256(o + BG * L.Umax * 4);
+  L.off_wl_row0 = o;   o = align256(o + BG * L.Umax * 4);
+  L.off_wl_pre = o;    o = align256(o + BG * (L.Umax + 1) * 4);
+  L.off_part_tok = o;  o = align256(o + BG * L.att_split * (size_t)L.part_cap * 4);
+  L.off_part_corr = o; o = align256(o + BG * Sc * (size_t)L.corr_cap * 8);
+  L.off_part_hdr = o;  o = align256(o + BG * L.att_items_g * 4);
+  L.off_est_md = o;    o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
+  L.off_est_num = o;   o = align256(o + BG * L.est_tiles_g * G * kD * 4);
+  L.off_att_md = o;    o = align256(o + BG * L.att_items_g * G * 2 * 4);
+  L.off_att_num = o;   o = align256(o + BG * L.att_items_g * G * kD * 4);
   L.total = o;
   return L;
 }
@@ -229,8 +235,8 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
     return fail(WI_ERR_INVALID_ARG, "negative C, Nc, n_steady or top_k");
   if ((int64_t)p->n_steady + p->Nc < 1) return fail(WI_ERR_INVALID_ARG, "empty context");
   if ((p->C == 0) != (p->Nc == 0)) return fail(WI_ERR_INVALID_ARG, "C and Nc must be both zero or both positive");
-  if (p->Nc >= (1 << 23) || p->n_steady >= (1 << 23))
-    return fail(WI_ERR_UNSUPPORTED, "more than 2^23 clustered or steady tokens per KV head");
+  if (p->Nc >= (1 << 23) || p->n_steady >= (1 << 23) || p->C >= (1 << 24))
+    return fail(WI_ERR_UNSUPPORTED, "more than 2^23 clustered or steady tokens, or 2^24 clusters, per KV head");
   if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(WI_ERR_INVALID_ARG, "scale must be finite and > 0");
   const int64_t BG = (int64_t)p->B * p->Hkv;
   if (BG * ((int64_t)p->Nc + p->n_steady) >= kMaxRows || (int64_t)p->B * p->Hq * ((int64_t)p->C + 1) >= kMaxRows)
@@ -252,8 +258,8 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.q = q; a.out = out; a.lse = lse; a.sel_ids = sel_ids;
   char* base = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<uint32_t*>(base + L.off_counters);
-  a.scores = reinterpret_cast<float*>(base + L.off_scores);
-  a.mu_norm = reinterpret_cast<float*>(base + L.off_mu_norm);
+  a.keys = reinterpret_cast<uint32_t*>(base + L.off_keys);
+  a.tile_norm = reinterpret_cast<float*>(base + L.off_tile_norm);
   a.sel_bits = reinterpret_cast<uint32_t*>(base + L.off_sel_bits);
   a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
@@ -262,15 +268,17 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
   a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
   a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
-  a.rowmap = reinterpret_cast<uint32_t*>(base + L.off_rowmap);
-  a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
+  a.part_tok = reinterpret_cast<uint32_t*>(base + L.off_part_tok);
+  a.part_corr = reinterpret_cast<uint32_t*>(base + L.off_part_corr);
+  a.part_hdr = reinterpret_cast<int32_t*>(base + L.off_part_hdr);
   a.est_md = reinterpret_cast<float*>(base + L.off_est_md);
   a.est_num = reinterpret_cast<float*>(base + L.off_est_num);
   a.att_md = reinterpret_cast<float*>(base + L.off_att_md);
   a.att_num = reinterpret_cast<float*>(base + L.off_att_num);
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
   a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.est_tiles_g = L.est_tiles_g;
-  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.scale = p->scale;
+  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.part_cap = L.part_cap;
+  a.corr_cap = L.corr_cap; a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);
 }

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
   __shared__ float sh_n[kEstTile];          // cluster sizes
-  __shared__ float sh_m[G], sh_den[G];
+  __shared__ float sh_m[G], sh_den[G], sh_nm[4];
   __shared__ float sh_num[4][G][kD];
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     }
   }
   if (tid < kEstTile) sh_n[tid] = tid < nrows ? (float)szs[tile * kEstTile + tid] : 0.f;
+  float nmax = 0.f;                 // largest centroid norm among the tile's non-empty clusters
   WI_TP(31);
 
   if constexpr (sizeof(T) == 2) {
@@ -124,11 +125,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * lg + r;
         if (h < G) {
-          if (c < C) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
           sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
         }
       }
-      if (lg == 0 && c < C) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
+      if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
     }
   } else {
     // fp32: 16x16x4 MFMA, 32 steps; lane (lr, lg) loads dims 16 j + 4 lg .. +4 (j = 0..7) and step
@@ -172,16 +173,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * lg + r;
         if (h < G) {
-          if (c < C) a.scores[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = acc[r];
+          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz > 0 ? f32_order_key(acc[r]) : 0u;
           sh_s[h][cl] = (c < C && sz > 0) ? acc[r] * a.scale : -INFINITY;
         }
       }
-      if (lg == 0 && c < C) a.mu_norm[(size_t)bg * C + c] = sqrtf(n2);
+      if (c < C && sz > 0) nmax = fmaxf(nmax, sqrtf(n2));
     }
   }
   __syncthreads();
   WI_TP(32);
 
+  nmax = wave_max(nmax);
+  if (lane == 0) sh_nm[w] = nmax;
   // estimation partial of the tile: m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
   for (int h = w; h < G; h += kScoreThreads / 64) {
     const float x0 = sh_s[h][lane], x1 = sh_s[h][lane + 64];
@@ -245,6 +248,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
     a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
   }
+  if (tid == 0) a.tile_norm[slot] = fmaxf(fmaxf(sh_nm[0], sh_nm[1]), fmaxf(sh_nm[2], sh_nm[3]));
 }
 
 // ============================================================================ k_select
@@ -345,7 +349,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 constexpr int kSelKPT = 16;         // clusters per thread held in registers
 constexpr int kBins = 2048;         // histogram bins over [min score, max score]
 constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
-constexpr int kSelStage = 8192;     // cluster sizes and offsets kept in LDS up to this many clusters
 
 // Per query head: the retrieval zone is the k_eff = min(top_k, #non-empty) non-empty clusters
 // first in the order (-sigma_c, c).  1) the k_eff-th largest fp32 score t is found with a
@@ -354,14 +357,12 @@ constexpr int kSelStage = 8192;     // cluster sizes and offsets kept in LDS up 
 // below t - 2 delta are out (delta bounds |fp32 score - canonical fp64 score|); 3) the band in
 // between is re-scored canonically and ranked by (-sigma, id).  Thread t visits clusters
 // t, t + NT, t + 2 NT, ... so every global access is coalesced; id-ordered lists come from
-// bitmaps.  The last head of a KV group to finish builds the group's work list: the union of the
-// heads' clusters with a head mask, a token -> row map (steady zone first) and the list the
-// estimation corrections run over.
+// bitmaps.  The last head of a KV group to finish builds the group's work: the union of the
+// heads' clusters in id order with a head mask, cut into one slice of the token -> row map per
+// exact-attention workgroup and one slice of the retrieved clusters per correction workgroup.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
-  WI_TP(0);
-  extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap,
-                                                     // then sizes [C] and offsets [C] if C <= kSelStage
+  extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t cand[kCandMax];
   __shared__ int32_t u_row0[kCandMax];
@@ -371,6 +372,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
   __shared__ int sh_i[8];
+  WI_TP(0);
 
   const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
@@ -379,12 +381,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   const int C = a.C, W32 = a.W32;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
-  const bool staged = C <= kSelStage;
-  int32_t* lsz = reinterpret_cast<int32_t*>(dynl + 2 * W32);
-  int32_t* loff = lsz + C;
-  const int32_t* sizes = a.sizes + (size_t)bg * C;
-  const float* sc = a.scores + (size_t)bh * C;
-  const float* mnorm = a.mu_norm + (size_t)bg * C;
+  const uint32_t* keys = a.keys + (size_t)bh * C;
   const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
   const int KPT = (C + NT - 1) / NT;          // thread t owns clusters j * NT + t, j < KPT
@@ -392,8 +389,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
 
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
+  float mxn = 0.f;
+  for (int i = tid; i < a.est_tiles_g; i += NT) mxn = fmaxf(mxn, a.tile_norm[(size_t)bg * a.est_tiles_g + i]);
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
-  WI_TP(1);
 
   uint32_t kc[kSelKPT];
   // fn(c, key) for every cluster of this thread, keys from registers or re-read in batches
@@ -404,16 +402,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < kSelKPT; ++i) k[i] = kc[i];
       } else {
-        int n[kSelKPT];
-        float s[kSelKPT];
 #pragma unroll
         for (int i = 0; i < kSelKPT; ++i) {
           const int c = (j0 + i) * NT + tid;
-          n[i] = 0; s[i] = 0.f;
-          if (c < C) { n[i] = sizes[c]; s[i] = sc[c]; }
+          k[i] = c < C ? keys[c] : 0u;
         }
-#pragma unroll
-        for (int i = 0; i < kSelKPT; ++i) k[i] = n[i] > 0 ? f32_order_key(s[i]) : 0u;
       }
 #pragma unroll
       for (int i = 0; i < kSelKPT; ++i) {
@@ -423,36 +416,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   };
 
-  // ---- pass 1: non-empty count, score range, largest centroid norm (and the key cache)
+  // ---- pass 1: non-empty count and score range (and the key cache)
   int cnt = 0;
-  float smax = -INFINITY, smin = INFINITY, mxn = 0.f;
+  float smax = -INFINITY, smin = INFINITY;
   for (int j0 = 0; j0 < KPT; j0 += kSelKPT) {
-    int n[kSelKPT];
-    float s[kSelKPT], nm[kSelKPT];
+    uint32_t k[kSelKPT];
 #pragma unroll
     for (int i = 0; i < kSelKPT; ++i) {
       const int c = (j0 + i) * NT + tid;
-      n[i] = 0; s[i] = 0.f; nm[i] = 0.f;
-      if (c < C) { n[i] = sizes[c]; s[i] = sc[c]; nm[i] = mnorm[c]; }
-    }
-    if (staged) {
-#pragma unroll
-      for (int i = 0; i < kSelKPT; ++i) {
-        const int c = (j0 + i) * NT + tid;
-        if (c < C) { lsz[c] = n[i]; loff[c] = a.offsets[(size_t)bg * (C + 1) + c]; }
-      }
+      k[i] = c < C ? keys[c] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kSelKPT; ++i) {
-      uint32_t key = 0u;
-      if (n[i] > 0) {
+      if (k[i] != 0u) {
         ++cnt;
-        smax = fmaxf(smax, s[i]);
-        smin = fminf(smin, s[i]);
-        mxn = fmaxf(mxn, nm[i]);
-        key = f32_order_key(s[i]);
+        const float s = f32_from_order_key(k[i]);
+        smax = fmaxf(smax, s);
+        smin = fminf(smin, s);
       }
-      if (cached) kc[i] = key;
+      if (cached) kc[i] = k[i];
     }
   }
   {
@@ -486,7 +468,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     };
     visit([&](int c, uint32_t k) { if (k != 0u) atomicAdd(&hist[bin_of(k)], 1u); });
     __syncthreads();
-  WI_TP(4);
+    WI_TP(4);
     {
       // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
       constexpr int BPT = kBins / kSelThreads;
@@ -507,7 +489,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       __syncthreads();
     }
     const int bstar = sh_i[0];
-  WI_TP(5);
     const int rem = k_eff - sh_i[1];
     const int ncand = (int)hist[bstar];
     uint32_t thr;
@@ -523,12 +504,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       }
       __syncthreads();
       thr = (uint32_t)sh_i[3];
-  WI_TP(6);
     } else {
       int rr;
-      thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) {
-        return sizes[c] > 0 ? f32_order_key(sc[c]) : 0u; }, hist, iscr, &rr);
+      thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
     }
+    WI_TP(6);
     // ---- pass 3: in / band / out.  delta bounds |fp32 score - canonical fp64 score| for every
     // cluster: fp32 accumulation of d exact-or-rounded products, doubled for an unspecified
     // MFMA summation order.
@@ -545,7 +525,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     });
     const int n_in = block_isum(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
-  WI_TP(7);
     // band list in ascending id order from the band bitmap
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
@@ -559,6 +538,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
       while (m) { const int bit = __ffs(m) - 1; m &= m - 1; band[pos++] = w * 32 + bit; }
     }
     __syncthreads();
+    WI_TP(7);
     if (need >= n_band) {
       for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
     } else if (n_band <= kSmallBand) {
@@ -597,9 +577,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   }
   __syncthreads();
+  WI_TP(8);
 
   // ---- publish: bitmap (coherent, read by the group's last head), ascending ids, flag
-  WI_TP(8);
   for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
   if (a.sel_ids) {
     const int perw = (W32 + NT - 1) / NT;
@@ -620,95 +600,127 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   if (!arrive_last(a.counters + bg, (uint32_t)G, &sh_i[4])) return;
   WI_TP(10);
 
-  // ---- the group's work list (last head only)
+  // ---- the group's work (last head only): union entries in ascending cluster id
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
   const int perw = (W32 + NT - 1) / NT;
   const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+  uint32_t hw[kMaxGroup][2];
+  const bool hold = perw <= 2;                     // this thread's words stay in registers
   int ne = 0;
   for (int w = w0; w < w1; ++w) {
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) u |= coherent_load(hb + (size_t)j * W32 + w);
+    for (int j = 0; j < G; ++j) {
+      const uint32_t x = coherent_load(hb + (size_t)j * W32 + w);
+      if (hold) hw[j][w - w0] = x;
+      u |= x;
+    }
     ne += __popc(u);
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
-  WI_TP(11);
   const bool ul = n_entries <= kCandMax;           // entry tables in LDS
-  int32_t* cidg = a.wl_cid + (size_t)bg * a.Umax;
-  int32_t* mskg = a.wl_mask + (size_t)bg * a.Umax;
-  int32_t* ucid = ul ? reinterpret_cast<int32_t*>(cand) : cidg;
-  int32_t* umsk = ul ? u_msk : mskg;
+  int32_t* ucid = ul ? reinterpret_cast<int32_t*>(cand) : a.wl_cid + (size_t)bg * a.Umax;
+  int32_t* umsk = ul ? u_msk : a.wl_mask + (size_t)bg * a.Umax;
   int32_t* urow = ul ? u_row0 : a.wl_row0 + (size_t)bg * a.Umax;
   int32_t* upre = ul ? reinterpret_cast<int32_t*>(hist) : a.wl_pre + (size_t)bg * (a.Umax + 1);
   for (int w = w0; w < w1; ++w) {
-    uint32_t hw[kMaxGroup];
+    uint32_t x[kMaxGroup];
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) { hw[j] = coherent_load(hb + (size_t)j * W32 + w); u |= hw[j]; }
+    for (int j = 0; j < G; ++j) {
+      x[j] = hold ? hw[j][w - w0] : coherent_load(hb + (size_t)j * W32 + w);
+      u |= x[j];
+    }
     while (u) {
       const int bit = __ffs(u) - 1;
       u &= u - 1;
       int m = 0;
-      for (int j = 0; j < G; ++j) m |= (int)((hw[j] >> bit) & 1u) << j;
+      for (int j = 0; j < G; ++j) m |= (int)((x[j] >> bit) & 1u) << j;
       ucid[e] = w * 32 + bit;
       umsk[e] = m;
       ++e;
     }
   }
   __syncthreads();
+  WI_TP(11);
+  // sizes and first rows of the entries, token prefix sums (steady zone first)
   const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const int32_t* sizes = a.sizes + (size_t)bg * C;
   const int pe = (n_entries + NT - 1) / NT;
   const int e0 = min(n_entries, tid * pe), e1 = min(n_entries, e0 + pe);
   int nt = 0;
   for (int i = e0; i < e1; ++i) {
     const int c = ucid[i];
-    const int sz = staged ? lsz[c] : sizes[c];
-    urow[i] = staged ? loff[c] : off[c];
+    const int sz = sizes[c];
+    urow[i] = off[c];
     upre[i] = sz;                                   // sizes for now, prefix below
     nt += sz;
   }
   int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
-  WI_TP(12);
   const int NS = a.NS;
   const int n_tok = NS + n_utok;
   for (int i = e0; i < e1; ++i) {
     const int sz = upre[i];
     upre[i] = NS + t;
     t += sz;
-    if (ul) { cidg[i] = ucid[i]; mskg[i] = umsk[i]; }
   }
-  if (tid == 0) {
-    upre[n_entries] = n_tok;
-    a.grp[(size_t)bg * 4 + 0] = n_entries;
-    a.grp[(size_t)bg * 4 + 1] = n_tok;
-  }
+  if (tid == 0) upre[n_entries] = n_tok;
   __syncthreads();
-  // token -> row map: row | steady flag (bit 23) | head mask << 24.  Thread t writes tokens
-  // [t*per, (t+1)*per): one search for its first entry, then a walk along the entries.
-  uint32_t* rmap = a.rowmap + (size_t)bg * (NS + a.Nc);
+  WI_TP(12);
+  // slices: exact-attention workgroup s takes tokens [s n_tok / S, (s+1) n_tok / S) (entries:
+  // row | steady flag (bit 23) | head mask << 24); correction workgroup j takes entries
+  // [j n / Sc, (j+1) n / Sc) (cluster id | head mask << 24, then the size).  Thread t writes
+  // tokens [t per, (t+1) per): one search for its first entry, then a walk.
+  const int S = a.att_split, Sc = a.att_items_g - a.att_split;
   const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
+  uint32_t* ptok = a.part_tok + (size_t)bg * S * a.part_cap;
+  for (int sl = tid; sl < S; sl += NT)
+    a.part_hdr[(size_t)bg * (S + Sc) + sl] = (int)(((int64_t)(sl + 1) * n_tok) / S) - (int)(((int64_t)sl * n_tok) / S);
   const int per = (n_tok + NT - 1) / NT;
   const int tb = min(n_tok, tid * per), te = min(n_tok, tb + per);
-  int tk = tb;
-  for (; tk < min(te, NS); ++tk) rmap[tk] = (uint32_t)tk | stag;
-  if (tk < te) {
-    int lo2 = 0, hi2 = n_entries - 1;              // last entry with upre[e] <= tk
-    while (lo2 < hi2) {
-      const int mid = (lo2 + hi2 + 1) >> 1;
-      if (upre[mid] <= tk) lo2 = mid; else hi2 = mid - 1;
-    }
-    int en = lo2;
-    int base = upre[en], nxt = upre[en + 1];
-    uint32_t r0 = (uint32_t)urow[en], tag = (uint32_t)umsk[en] << 24;
-    for (; tk < te; ++tk) {
-      while (tk >= nxt) {
-        ++en;
-        base = nxt;
-        nxt = upre[en + 1];
-        r0 = (uint32_t)urow[en];
-        tag = (uint32_t)umsk[en] << 24;
+  if (tb < te) {
+    int sl = (int)((((int64_t)tb + 1) * S - 1) / n_tok);          // slice of token tb
+    int s_beg = (int)(((int64_t)sl * n_tok) / S), s_end = (int)(((int64_t)(sl + 1) * n_tok) / S);
+    int en = 0, base = 0, nxt = 0;
+    uint32_t r0 = 0u, tag = 0u;
+    if (te > NS && n_entries > 0) {
+      const int t1st = max(tb, NS);
+      int lo2 = 0, hi2 = n_entries - 1;            // last entry with upre[e] <= t1st
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2 + 1) >> 1;
+        if (upre[mid] <= t1st) lo2 = mid; else hi2 = mid - 1;
       }
-      rmap[tk] = (r0 + (uint32_t)(tk - base)) | tag;
+      en = lo2; base = upre[en]; nxt = upre[en + 1];
+      r0 = (uint32_t)urow[en]; tag = (uint32_t)umsk[en] << 24;
+    }
+    for (int tk = tb; tk < te; ++tk) {
+      while (tk >= s_end) { ++sl; s_beg = s_end; s_end = (int)(((int64_t)(sl + 1) * n_tok) / S); }
+      uint32_t v;
+      if (tk < NS) {
+        v = (uint32_t)tk | stag;
+      } else {
+        while (tk >= nxt) {
+          ++en;
+          base = nxt;
+          nxt = upre[en + 1];
+          r0 = (uint32_t)urow[en];
+          tag = (uint32_t)umsk[en] << 24;
+        }
+        v = (r0 + (uint32_t)(tk - base)) | tag;
+      }
+      ptok[(size_t)sl * a.part_cap + (tk - s_beg)] = v;
+    }
+  }
+  if (Sc > 0) {
+    for (int j = tid; j < Sc; j += NT)
+      a.part_hdr[(size_t)bg * (S + Sc) + S + j] = (int)(((int64_t)(j + 1) * n_entries) / Sc) - (int)(((int64_t)j * n_entries) / Sc);
+    uint32_t* pc = a.part_corr + (size_t)bg * Sc * a.corr_cap * 2;
+    for (int i = e0; i < e1; ++i) {
+      const int j = (int)((((int64_t)i + 1) * Sc - 1) / n_entries);
+      const int k = i - (int)(((int64_t)j * n_entries) / Sc);
+      uint32_t* d = pc + ((size_t)j * a.corr_cap + k) * 2;
+      d[0] = (uint32_t)ucid[i] | ((uint32_t)umsk[i] << 24);
+      d[1] = (uint32_t)(upre[i + 1] - upre[i]);
     }
   }
   WI_TP(13);
@@ -868,10 +880,11 @@ __device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp)
   return s;
 }
 
-// grid (S, B*Hkv).  Workgroup s attends exactly over tokens [s n_tok / S, (s+1) n_tok / S) of its
-// KV group's list (steady zone, then the retrieved clusters) and folds the estimation terms of
-// union entries [s n_entries / S, (s+1) n_entries / S) into a second partial (the merge
-// subtracts it).
+// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over slice s of its KV group's token list
+// (steady zone, then the retrieved clusters' rows, each row loaded once for every head of the
+// group that retrieved it); workgroup S + j folds the estimation terms of slice j of the
+// retrieved clusters into a partial the merge subtracts.  Slice contents and counts are read in
+// one round, the rows in the next.
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
@@ -880,29 +893,33 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ float sh_num[4 * G * kD];
   __shared__ uint32_t sh_ent[kAttStage];
   WI_TP(20);
-  const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split;
+  const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split, Sc = a.att_items_g - a.att_split;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
-  const int n_entries = a.grp[(size_t)bg * 4 + 0], n_tok = a.grp[(size_t)bg * 4 + 1];
-  WI_TP(21);
   OState<G> st;
   st.init();
-  {
+  if (s < S) {
+    const uint32_t* src = a.part_tok + ((size_t)bg * S + s) * a.part_cap;
+    const int stage0 = min(a.part_cap, kAttStage);
+    for (int i = threadIdx.x; i < stage0; i += kAttThreads) sh_ent[i] = src[i];
+    const int n = a.part_hdr[(size_t)bg * (S + Sc) + s];
     const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
     Piece<T> qp[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) qp[h].load(qg + (size_t)h * kD + 8 * lr);
-    const int t0 = (int)(((int64_t)s * n_tok) / S), t1 = (int)(((int64_t)(s + 1) * n_tok) / S);
-    const uint32_t* rmap = a.rowmap + (size_t)bg * (a.NS + a.Nc);
     const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
     const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
     const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * a.NS * kD;
-    for (int z0 = t0; z0 < t1; z0 += kAttStage) {
-      const int z1 = min(t1, z0 + kAttStage);
-      __syncthreads();
-      for (int i = threadIdx.x; i < z1 - z0; i += kAttThreads) sh_ent[i] = rmap[z0 + i];
-      __syncthreads();
+    __syncthreads();
+    WI_TP(21);
+    for (int z0 = 0; z0 < n; z0 += kAttStage) {
+      const int z1 = min(n, z0 + kAttStage);
+      if (z0 > 0) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < z1 - z0; i += kAttThreads) sh_ent[i] = src[z0 + i];
+        __syncthreads();
+      }
       for (int c0 = z0; c0 < z1; c0 += PASS) {
         uint32_t ent[R];
         Piece<T> kr[R], vr[R];
@@ -934,39 +951,45 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
         st.template add<R>(l, wd, vr);
       }
     }
+  } else {
+    const int j = s - S;
+    const uint32_t* src = a.part_corr + ((size_t)bg * Sc + j) * a.corr_cap * 2;
+    const int stage0 = min(2 * a.corr_cap, kAttStage);
+    for (int i = threadIdx.x; i < stage0; i += kAttThreads) sh_ent[i] = src[i];
+    const int n = a.part_hdr[(size_t)bg * (S + Sc) + S + j];
+    const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
+    const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
+    __syncthreads();
+    for (int z0 = 0; z0 < n; z0 += kAttStage / 2) {
+      const int z1 = min(n, z0 + kAttStage / 2);
+      if (z0 > 0) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < 2 * (z1 - z0); i += kAttThreads) sh_ent[i] = src[2 * z0 + i];
+        __syncthreads();
+      }
+      for (int c0 = z0; c0 < z1; c0 += PASS) {
+        Piece<T> vr[R];
+        float wd[R], l[R][G];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int e = c0 + w * (4 * R) + 4 * i + rg;
+          const bool live = e < z1;
+          const uint32_t en = live ? sh_ent[2 * (e - z0)] : 0u;
+          const int c = (int)(en & 0xffffffu);
+          const uint32_t m = en >> 24;
+          wd[i] = live ? (float)sh_ent[2 * (e - z0) + 1] : 0.f;
+          if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
+          else vr[i].zero();
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            l[i][h] = ((m >> h) & 1u) ? f32_from_order_key(a.keys[(hbase + h) * a.C + c]) * a.scale : -INFINITY;
+        }
+        st.template add<R>(l, wd, vr);
+      }
+    }
   }
   WI_TP(22);
   write_partial<G>(st, (size_t)bg * a.att_items_g + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
-  // estimation terms of this workgroup's share of the retrieved clusters
-  st.init();
-  {
-    const int e0 = (int)(((int64_t)s * n_entries) / S), e1 = (int)(((int64_t)(s + 1) * n_entries) / S);
-    const int32_t* cid = a.wl_cid + (size_t)bg * a.Umax;
-    const int32_t* msk = a.wl_mask + (size_t)bg * a.Umax;
-    const int32_t* szs = a.sizes + (size_t)bg * a.C;
-    const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
-    const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
-    for (int c0 = e0; c0 < e1; c0 += PASS) {
-      Piece<T> vr[R];
-      float wd[R], l[R][G];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int e = c0 + w * (4 * R) + 4 * i + rg;
-        const bool live = e < e1;
-        const int c = live ? cid[e] : 0;
-        const int m = live ? msk[e] : 0;
-        wd[i] = live ? (float)szs[c] : 0.f;
-        if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
-        else vr[i].zero();
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          l[i][h] = ((m >> h) & 1) ? a.scores[(hbase + h) * a.C + c] * a.scale : -INFINITY;
-      }
-      st.template add<R>(l, wd, vr);
-    }
-  }
-  __syncthreads();
-  write_partial<G>(st, (size_t)bg * a.att_items_g + S + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
   WI_TP(23);
 }
 
@@ -1080,12 +1103,11 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  const size_t sel_lds = (size_t)a.W32 * 8 + (a.C <= kSelStage ? (size_t)a.C * 8 : 0);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), sel_lds, s, a);
+  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_split, BG), dim3(kAttThreads), 0, s, a);
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);

@@ -24,10 +24,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
-  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g;
-  size_t off_counters, off_scores, off_mu_norm, off_sel_bits, off_band_ids, off_band_key,
-      off_all_sel, off_wl_cid, off_wl_mask, off_wl_row0, off_wl_pre, off_rowmap, off_grp, off_est_md, off_est_num,
-      off_att_md, off_att_num, total;
+  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g, part_cap, corr_cap;
+  size_t off_counters, off_keys, off_tile_norm, off_sel_bits, off_band_ids, off_band_key,
+      off_all_sel, off_wl_cid, off_wl_mask, off_wl_row0, off_wl_pre, off_part_tok, off_part_corr,
+      off_part_hdr, off_est_md, off_est_num, off_att_md, off_att_num, total;
 };
 DecodeLayout decode_layout(const wi_decode_params& p);
 
@@ -47,24 +47,26 @@ struct DecodeArgs {
   int32_t* sel_ids;        // [BH, top_k] or null
   // workspace
   uint32_t* counters;      // [BG] arrivals of a group's heads in k_select
-  float* scores;           // [BH, C] fp32 <q, mu_c>
-  float* mu_norm;          // [BG, C]
+  uint32_t* keys;          // [BH, C] order key of the fp32 score <q, mu_c> (0: empty cluster)
+  float* tile_norm;        // [BG, est_tiles_g] largest centroid norm of each 128-cluster tile
   uint32_t* sel_bits;      // [BH, W32] retrieved-cluster bitmap
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
-  int32_t* wl_cid;         // [BG, Umax] union entries: cluster id
-  int32_t* wl_mask;        // [BG, Umax]             heads that retrieved it
-  int32_t* wl_row0;        // [BG, Umax]             first k_perm row (when not held in LDS)
-  int32_t* wl_pre;         // [BG, Umax+1]           first token (when not held in LDS)
-  uint32_t* rowmap;        // [BG, NS + Nc] token -> row | steady flag (bit 23) | head mask << 24
-  int32_t* grp;            // [BG, 4]: n_entries, n_tok
+  int32_t* wl_cid;         // [BG, Umax] union entry tables when they exceed LDS
+  int32_t* wl_mask;        // [BG, Umax]
+  int32_t* wl_row0;        // [BG, Umax]
+  int32_t* wl_pre;         // [BG, Umax+1]
+  uint32_t* part_tok;      // [BG, S, part_cap] token slices: row | steady (bit 23) | mask << 24
+  uint32_t* part_corr;     // [BG, Sc, corr_cap, 2] correction slices: (cid | mask << 24, size)
+  int32_t* part_hdr;       // [BG, S + Sc] slice lengths
   float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
   float* est_num;          // [BG, est_tiles_g, G, d]
-  float* att_md;           // [BG, att_items_g, G, 2]
-  float* att_num;          // [BG, att_items_g, G, d]
+  float* att_md;           // [BG, S + Sc, G, 2]
+  float* att_num;          // [BG, S + Sc, G, d]
   // shapes
-  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g;
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g, part_cap,
+      corr_cap;
   float scale;
 };
 
