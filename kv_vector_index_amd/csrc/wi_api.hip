@@ -135,9 +135,10 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   const int Sc = (int)std::max<int64_t>(1, ceil_div(total, 32));
   L.att_split = std::max(1, total - Sc);
   L.att_items_g = L.att_split + Sc;
-  L.part_cap = (int)std::max<int64_t>(1, ceil_div(ntok_max, L.att_split));
-  L.corr_cap = (int)std::max<int64_t>(1, ceil_div(L.Umax, Sc));
-  const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G;
+  // list mode: every attention workgroup rebuilds the group's union in LDS from the heads' lists
+  const int64_t list_lds = ((int64_t)2 * L.W32 + (int64_t)4 * L.G * p.top_k + 1) * 4;
+  L.list_mode = ((int64_t)L.G * p.top_k <= 4096 && list_lds <= kAttListLds) ? 1 : 0;
+  const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G, K = p.top_k;
   size_t o = 0;
   L.off_counters = o;  o = align256(o + BG * 4);
   L.off_keys = o;      o = align256(o + BH * C * 4);
@@ -146,13 +147,15 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_band_ids = o;  o = align256(o + BH * C * 4);
   L.off_band_key = o;  o = align256(o + BH * C * 8);
   L.off_all_sel = o;   o = align256(o + BH * 4);
+  L.off_hl_cid = o;    o = align256(o + BH * K * 4);
+  L.off_hl_sz = o;     o = align256(o + BH * K * 4);
+  L.off_hl_row = o;    o = align256(o + BH * K * 4);
+  L.off_hl_n = o;      o = align256(o + BH * 4);
   L.off_wl_cid = o;    o = align256(o + BG * L.Umax * 4);
   L.off_wl_mask = o;   o = align256(o + BG * L.Umax * 4);
   L.off_wl_row0 = o;   o = align256(o + BG * L.Umax * 4);
   L.off_wl_pre = o;    o = align256(o + BG * (L.Umax + 1) * 4);
-  L.off_part_tok = o;  o = align256(o + BG * L.att_split * (size_t)L.part_cap * 4);
-  L.off_part_corr = o; o = align256(o + BG * Sc * (size_t)L.corr_cap * 8);
-  L.off_part_hdr = o;  o = align256(o + BG * L.att_items_g * 4);
+  L.off_grp = o;       o = align256(o + BG * 2 * 4);
   L.off_est_md = o;    o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
   L.off_est_num = o;   o = align256(o + BG * L.est_tiles_g * G * kD * 4);
   L.off_att_md = o;    o = align256(o + BG * L.att_items_g * G * 2 * 4);
@@ -264,21 +267,23 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
+  a.hl_cid = reinterpret_cast<int32_t*>(base + L.off_hl_cid);
+  a.hl_sz = reinterpret_cast<int32_t*>(base + L.off_hl_sz);
+  a.hl_row = reinterpret_cast<int32_t*>(base + L.off_hl_row);
+  a.hl_n = reinterpret_cast<int32_t*>(base + L.off_hl_n);
   a.wl_cid = reinterpret_cast<int32_t*>(base + L.off_wl_cid);
   a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
   a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
   a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
-  a.part_tok = reinterpret_cast<uint32_t*>(base + L.off_part_tok);
-  a.part_corr = reinterpret_cast<uint32_t*>(base + L.off_part_corr);
-  a.part_hdr = reinterpret_cast<int32_t*>(base + L.off_part_hdr);
+  a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
   a.est_md = reinterpret_cast<float*>(base + L.off_est_md);
   a.est_num = reinterpret_cast<float*>(base + L.off_est_num);
   a.att_md = reinterpret_cast<float*>(base + L.off_att_md);
   a.att_num = reinterpret_cast<float*>(base + L.off_att_num);
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
   a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.est_tiles_g = L.est_tiles_g;
-  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.part_cap = L.part_cap;
-  a.corr_cap = L.corr_cap; a.scale = p->scale;
+  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.list_mode = L.list_mode;
+  a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);
 }

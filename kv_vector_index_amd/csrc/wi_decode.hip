@@ -365,8 +365,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t cand[kCandMax];
-  __shared__ int32_t u_row0[kCandMax];
-  __shared__ int32_t u_msk[kCandMax];
   __shared__ int iscr[48];
   __shared__ float fred[8][5];
   __shared__ double qd[kD];
@@ -579,149 +577,94 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __syncthreads();
   WI_TP(8);
 
-  // ---- publish: bitmap (coherent, read by the group's last head), ascending ids, flag
-  for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
-  if (a.sel_ids) {
+  // ---- publish: ascending retrieved ids (to sel_ids and, in list mode, to this head's list with
+  // each cluster's size and first row)
+  const bool list_mode = a.list_mode != 0;
+  {
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
     int n = 0;
     for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
     int tot;
     int p = block_exclusive_scan(n, iscr, &tot);
-    int32_t* out = a.sel_ids + (size_t)bh * a.top_k;
+    int32_t* out = a.sel_ids ? a.sel_ids + (size_t)bh * a.top_k : nullptr;
+    const size_t lbase = (size_t)bh * a.top_k;
+    const int32_t* sizes = a.sizes + (size_t)bg * C;
+    const int32_t* off = a.offsets + (size_t)bg * (C + 1);
     for (int w = w0; w < w1; ++w) {
       uint32_t m = bits[w];
-      while (m) { const int bit = __ffs(m) - 1; m &= m - 1; if (p < a.top_k) out[p] = w * 32 + bit; ++p; }
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        const int c = w * 32 + bit;
+        if (p < a.top_k) {
+          if (out) out[p] = c;
+          if (list_mode) { a.hl_cid[lbase + p] = c; a.hl_sz[lbase + p] = sizes[c]; a.hl_row[lbase + p] = off[c]; }
+        }
+        ++p;
+      }
     }
-    for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
+    if (out) for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
+    if (tid == 0) a.hl_n[bh] = min(tot, a.top_k);
   }
   if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
   WI_TP(9);
+  if (list_mode) return;
+
+  // ---- table mode (unions too large for the attention kernel's LDS): the last head of the group
+  // builds the union table in global memory
+  for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
   if (!arrive_last(a.counters + bg, (uint32_t)G, &sh_i[4])) return;
   WI_TP(10);
-
-  // ---- the group's work (last head only): union entries in ascending cluster id
   const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
   const int perw = (W32 + NT - 1) / NT;
   const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-  uint32_t hw[kMaxGroup][2];
-  const bool hold = perw <= 2;                     // this thread's words stay in registers
   int ne = 0;
   for (int w = w0; w < w1; ++w) {
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) {
-      const uint32_t x = coherent_load(hb + (size_t)j * W32 + w);
-      if (hold) hw[j][w - w0] = x;
-      u |= x;
-    }
+    for (int j = 0; j < G; ++j) u |= coherent_load(hb + (size_t)j * W32 + w);
     ne += __popc(u);
   }
   int n_entries;
   int e = block_exclusive_scan(ne, iscr, &n_entries);
-  const bool ul = n_entries <= kCandMax;           // entry tables in LDS
-  int32_t* ucid = ul ? reinterpret_cast<int32_t*>(cand) : a.wl_cid + (size_t)bg * a.Umax;
-  int32_t* umsk = ul ? u_msk : a.wl_mask + (size_t)bg * a.Umax;
-  int32_t* urow = ul ? u_row0 : a.wl_row0 + (size_t)bg * a.Umax;
-  int32_t* upre = ul ? reinterpret_cast<int32_t*>(hist) : a.wl_pre + (size_t)bg * (a.Umax + 1);
+  int32_t* ucid = a.wl_cid + (size_t)bg * a.Umax;
+  int32_t* umsk = a.wl_mask + (size_t)bg * a.Umax;
+  int32_t* urow = a.wl_row0 + (size_t)bg * a.Umax;
+  int32_t* upre = a.wl_pre + (size_t)bg * (a.Umax + 1);
+  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+  const int32_t* sizes = a.sizes + (size_t)bg * C;
+  int nt = 0;
+  const int e_first = e;
   for (int w = w0; w < w1; ++w) {
     uint32_t x[kMaxGroup];
     uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) {
-      x[j] = hold ? hw[j][w - w0] : coherent_load(hb + (size_t)j * W32 + w);
-      u |= x[j];
-    }
+    for (int j = 0; j < G; ++j) { x[j] = coherent_load(hb + (size_t)j * W32 + w); u |= x[j]; }
     while (u) {
       const int bit = __ffs(u) - 1;
       u &= u - 1;
       int m = 0;
       for (int j = 0; j < G; ++j) m |= (int)((x[j] >> bit) & 1u) << j;
-      ucid[e] = w * 32 + bit;
+      const int c = w * 32 + bit;
+      ucid[e] = c;
       umsk[e] = m;
+      urow[e] = off[c];
+      upre[e] = sizes[c];
+      nt += sizes[c];
       ++e;
     }
-  }
-  __syncthreads();
-  WI_TP(11);
-  // sizes and first rows of the entries, token prefix sums (steady zone first)
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
-  const int32_t* sizes = a.sizes + (size_t)bg * C;
-  const int pe = (n_entries + NT - 1) / NT;
-  const int e0 = min(n_entries, tid * pe), e1 = min(n_entries, e0 + pe);
-  int nt = 0;
-  for (int i = e0; i < e1; ++i) {
-    const int c = ucid[i];
-    const int sz = sizes[c];
-    urow[i] = off[c];
-    upre[i] = sz;                                   // sizes for now, prefix below
-    nt += sz;
   }
   int n_utok;
   int t = block_exclusive_scan(nt, iscr, &n_utok);
   const int NS = a.NS;
-  const int n_tok = NS + n_utok;
-  for (int i = e0; i < e1; ++i) {
+  for (int i = e_first; i < e; ++i) {
     const int sz = upre[i];
     upre[i] = NS + t;
     t += sz;
   }
-  if (tid == 0) upre[n_entries] = n_tok;
-  __syncthreads();
-  WI_TP(12);
-  // slices: exact-attention workgroup s takes tokens [s n_tok / S, (s+1) n_tok / S) (entries:
-  // row | steady flag (bit 23) | head mask << 24); correction workgroup j takes entries
-  // [j n / Sc, (j+1) n / Sc) (cluster id | head mask << 24, then the size).  Thread t writes
-  // tokens [t per, (t+1) per): one search for its first entry, then a walk.
-  const int S = a.att_split, Sc = a.att_items_g - a.att_split;
-  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
-  uint32_t* ptok = a.part_tok + (size_t)bg * S * a.part_cap;
-  for (int sl = tid; sl < S; sl += NT)
-    a.part_hdr[(size_t)bg * (S + Sc) + sl] = (int)(((int64_t)(sl + 1) * n_tok) / S) - (int)(((int64_t)sl * n_tok) / S);
-  const int per = (n_tok + NT - 1) / NT;
-  const int tb = min(n_tok, tid * per), te = min(n_tok, tb + per);
-  if (tb < te) {
-    int sl = (int)((((int64_t)tb + 1) * S - 1) / n_tok);          // slice of token tb
-    int s_beg = (int)(((int64_t)sl * n_tok) / S), s_end = (int)(((int64_t)(sl + 1) * n_tok) / S);
-    int en = 0, base = 0, nxt = 0;
-    uint32_t r0 = 0u, tag = 0u;
-    if (te > NS && n_entries > 0) {
-      const int t1st = max(tb, NS);
-      int lo2 = 0, hi2 = n_entries - 1;            // last entry with upre[e] <= t1st
-      while (lo2 < hi2) {
-        const int mid = (lo2 + hi2 + 1) >> 1;
-        if (upre[mid] <= t1st) lo2 = mid; else hi2 = mid - 1;
-      }
-      en = lo2; base = upre[en]; nxt = upre[en + 1];
-      r0 = (uint32_t)urow[en]; tag = (uint32_t)umsk[en] << 24;
-    }
-    for (int tk = tb; tk < te; ++tk) {
-      while (tk >= s_end) { ++sl; s_beg = s_end; s_end = (int)(((int64_t)(sl + 1) * n_tok) / S); }
-      uint32_t v;
-      if (tk < NS) {
-        v = (uint32_t)tk | stag;
-      } else {
-        while (tk >= nxt) {
-          ++en;
-          base = nxt;
-          nxt = upre[en + 1];
-          r0 = (uint32_t)urow[en];
-          tag = (uint32_t)umsk[en] << 24;
-        }
-        v = (r0 + (uint32_t)(tk - base)) | tag;
-      }
-      ptok[(size_t)sl * a.part_cap + (tk - s_beg)] = v;
-    }
-  }
-  if (Sc > 0) {
-    for (int j = tid; j < Sc; j += NT)
-      a.part_hdr[(size_t)bg * (S + Sc) + S + j] = (int)(((int64_t)(j + 1) * n_entries) / Sc) - (int)(((int64_t)j * n_entries) / Sc);
-    uint32_t* pc = a.part_corr + (size_t)bg * Sc * a.corr_cap * 2;
-    for (int i = e0; i < e1; ++i) {
-      const int j = (int)((((int64_t)i + 1) * Sc - 1) / n_entries);
-      const int k = i - (int)(((int64_t)j * n_entries) / Sc);
-      uint32_t* d = pc + ((size_t)j * a.corr_cap + k) * 2;
-      d[0] = (uint32_t)ucid[i] | ((uint32_t)umsk[i] << 24);
-      d[1] = (uint32_t)(upre[i + 1] - upre[i]);
-    }
+  if (tid == 0) {
+    upre[n_entries] = NS + n_utok;
+    a.grp[(size_t)bg * 2 + 0] = n_entries;
+    a.grp[(size_t)bg * 2 + 1] = NS + n_utok;
   }
   WI_TP(13);
 }
@@ -880,29 +823,141 @@ __device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp)
   return s;
 }
 
-// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over slice s of its KV group's token list
-// (steady zone, then the retrieved clusters' rows, each row loaded once for every head of the
-// group that retrieved it); workgroup S + j folds the estimation terms of slice j of the
-// retrieved clusters into a partial the merge subtracts.  Slice contents and counts are read in
-// one round, the rows in the next.
+// The group's work list as the attention workgroups see it: entry e (ascending cluster id) has a
+// cluster id, the mask of the heads that retrieved it, its first row in k_perm/v_perm and its
+// first token (the steady zone's tokens come first).  List mode keeps a copy in LDS, rebuilt by
+// every workgroup from the heads' sorted lists; table mode reads the table the group's last head
+// wrote to global memory.
+struct WorkList {
+  const uint32_t* cm;    // cid | mask << 24 (list mode)
+  const int32_t* cid;    // table mode
+  const int32_t* msk;    // table mode
+  const int32_t* row;
+  const int32_t* pre;    // [n + 1]
+  int n, n_tok;
+  bool lds;
+  __device__ int cid_of(int e) const { return lds ? (int)(cm[e] & 0xffffffu) : cid[e]; }
+  __device__ uint32_t mask_of(int e) const { return lds ? (cm[e] >> 24) : (uint32_t)msk[e]; }
+};
+
+// Union of the G heads' sorted lists in LDS: a bitmap over cluster ids gives each cluster's rank
+// (word prefix + popcount); every list entry ORs its head bit into the rank's slot.
+template <int G>
+__device__ WorkList build_union(const DecodeArgs& a, int b, int g, uint32_t* lds, int* iscr) {
+  const int tid = threadIdx.x, NT = kAttThreads;
+  const int W32 = a.W32, K = a.top_k, L = G * K;
+  uint32_t* ubm = lds;                     // [W32]
+  int32_t* wp = reinterpret_cast<int32_t*>(lds + W32);            // [W32]
+  uint32_t* tcm = lds + 2 * W32;           // [L]
+  int32_t* tsz = reinterpret_cast<int32_t*>(tcm + L);             // [L]
+  int32_t* trow = tsz + L;                 // [L]
+  int32_t* tpre = trow + L;                // [L + 1]
+  const size_t hb = ((size_t)b * a.Hq + (size_t)g * G);
+  for (int i = tid; i < W32; i += NT) ubm[i] = 0u;
+  for (int i = tid; i < L; i += NT) tcm[i] = 0u;
+  __syncthreads();
+  for (int x = tid; x < L; x += NT) {
+    const int j = x / K, i = x - j * K;
+    if (i < a.hl_n[hb + j]) {
+      const int c = a.hl_cid[(hb + j) * K + i];
+      atomicOr(&ubm[c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  const int pw = (W32 + NT - 1) / NT;
+  const int w0 = min(W32, tid * pw), w1 = min(W32, w0 + pw);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(ubm[w]);
+  int n;
+  int run = block_exclusive_scan(cnt, iscr, &n);
+  for (int w = w0; w < w1; ++w) { wp[w] = run; run += __popc(ubm[w]); }
+  __syncthreads();
+  for (int x = tid; x < L; x += NT) {
+    const int j = x / K, i = x - j * K;
+    if (i < a.hl_n[hb + j]) {
+      const size_t li = (hb + j) * K + i;
+      const int c = a.hl_cid[li];
+      const int r = wp[c >> 5] + __popc(ubm[c >> 5] & ((1u << (c & 31)) - 1u));
+      atomicOr(&tcm[r], (uint32_t)c | (1u << (24 + j)));
+      tsz[r] = a.hl_sz[li];
+      trow[r] = a.hl_row[li];
+    }
+  }
+  __syncthreads();
+  const int pe = (n + NT - 1) / NT;
+  const int e0 = min(n, tid * pe), e1 = min(n, e0 + pe);
+  int nt = 0;
+  for (int e = e0; e < e1; ++e) nt += tsz[e];
+  int tot;
+  int t = block_exclusive_scan(nt, iscr, &tot);
+  for (int e = e0; e < e1; ++e) { tpre[e] = a.NS + t; t += tsz[e]; }
+  if (tid == 0) tpre[n] = a.NS + tot;
+  __syncthreads();
+  WorkList wl;
+  wl.cm = tcm; wl.cid = nullptr; wl.msk = nullptr; wl.row = trow; wl.pre = tpre;
+  wl.n = n; wl.n_tok = a.NS + tot; wl.lds = true;
+  return wl;
+}
+
+// sh_ent[t - z0] for tokens [z0, z1): row | steady flag (bit 23) | head mask << 24.
+template <int G>
+__device__ void fill_tokens(const DecodeArgs& a, const WorkList& wl, int z0, int z1, uint32_t* sh_ent,
+                            int* sh_e0) {
+  const int tid = threadIdx.x, NT = kAttThreads, NS = a.NS;
+  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
+  for (int t = z0 + tid; t < min(z1, NS); t += NT) sh_ent[t - z0] = (uint32_t)t | stag;
+  const int u0 = max(z0, NS);
+  if (u0 < z1) {
+    for (int e = tid; e < wl.n; e += NT)
+      if (wl.pre[e] <= u0 && u0 < wl.pre[e + 1]) *sh_e0 = e;
+    __syncthreads();
+    for (int e = *sh_e0 + tid; e < wl.n; e += NT) {
+      const int p0 = wl.pre[e];
+      if (p0 >= z1) break;
+      const int p1 = min(wl.pre[e + 1], z1);
+      const uint32_t r0 = (uint32_t)wl.row[e], tag = wl.mask_of(e) << 24;
+      for (int t = max(p0, u0); t < p1; ++t) sh_ent[t - z0] = (r0 + (uint32_t)(t - p0)) | tag;
+    }
+  }
+  __syncthreads();
+}
+
+// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
+// of its KV group's list (steady zone, then the retrieved clusters' rows, each row loaded once
+// for every head of the group that retrieved it); workgroup S + j folds the estimation terms of
+// union entries [j n / Sc, (j+1) n / Sc) into a partial the merge subtracts.
 template <typename T, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
   constexpr int PASS = 16 * R;                 // 4 waves x 4 lane groups x R rows
+  extern __shared__ uint32_t att_dyn[];        // list mode: the group's union table
   __shared__ float sh_m[4 * G], sh_den[4 * G];
   __shared__ float sh_num[4 * G * kD];
   __shared__ uint32_t sh_ent[kAttStage];
+  __shared__ int iscr[24];
+  __shared__ int sh_e0;
   WI_TP(20);
   const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split, Sc = a.att_items_g - a.att_split;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
+  WorkList wl;
+  if (a.list_mode) {
+    wl = build_union<G>(a, b, g, att_dyn, iscr);
+  } else {
+    wl.cm = nullptr;
+    wl.cid = a.wl_cid + (size_t)bg * a.Umax;
+    wl.msk = a.wl_mask + (size_t)bg * a.Umax;
+    wl.row = a.wl_row0 + (size_t)bg * a.Umax;
+    wl.pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
+    wl.n = a.grp[(size_t)bg * 2];
+    wl.n_tok = a.grp[(size_t)bg * 2 + 1];
+    wl.lds = false;
+  }
+  WI_TP(21);
   OState<G> st;
   st.init();
   if (s < S) {
-    const uint32_t* src = a.part_tok + ((size_t)bg * S + s) * a.part_cap;
-    const int stage0 = min(a.part_cap, kAttStage);
-    for (int i = threadIdx.x; i < stage0; i += kAttThreads) sh_ent[i] = src[i];
-    const int n = a.part_hdr[(size_t)bg * (S + Sc) + s];
+    const int t0 = (int)(((int64_t)s * wl.n_tok) / S), t1 = (int)(((int64_t)(s + 1) * wl.n_tok) / S);
     const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
     Piece<T> qp[G];
 #pragma unroll
@@ -911,15 +966,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
     const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * a.NS * kD;
-    __syncthreads();
-    WI_TP(21);
-    for (int z0 = 0; z0 < n; z0 += kAttStage) {
-      const int z1 = min(n, z0 + kAttStage);
-      if (z0 > 0) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < z1 - z0; i += kAttThreads) sh_ent[i] = src[z0 + i];
-        __syncthreads();
-      }
+    for (int z0 = t0; z0 < t1; z0 += kAttStage) {
+      const int z1 = min(t1, z0 + kAttStage);
+      if (z0 > t0) __syncthreads();
+      fill_tokens<G>(a, wl, z0, z1, sh_ent, &sh_e0);
       for (int c0 = z0; c0 < z1; c0 += PASS) {
         uint32_t ent[R];
         Piece<T> kr[R], vr[R];
@@ -953,39 +1003,26 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     }
   } else {
     const int j = s - S;
-    const uint32_t* src = a.part_corr + ((size_t)bg * Sc + j) * a.corr_cap * 2;
-    const int stage0 = min(2 * a.corr_cap, kAttStage);
-    for (int i = threadIdx.x; i < stage0; i += kAttThreads) sh_ent[i] = src[i];
-    const int n = a.part_hdr[(size_t)bg * (S + Sc) + S + j];
+    const int e0 = (int)(((int64_t)j * wl.n) / Sc), e1 = (int)(((int64_t)(j + 1) * wl.n) / Sc);
     const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
     const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
-    __syncthreads();
-    for (int z0 = 0; z0 < n; z0 += kAttStage / 2) {
-      const int z1 = min(n, z0 + kAttStage / 2);
-      if (z0 > 0) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < 2 * (z1 - z0); i += kAttThreads) sh_ent[i] = src[2 * z0 + i];
-        __syncthreads();
-      }
-      for (int c0 = z0; c0 < z1; c0 += PASS) {
-        Piece<T> vr[R];
-        float wd[R], l[R][G];
+    for (int c0 = e0; c0 < e1; c0 += PASS) {
+      Piece<T> vr[R];
+      float wd[R], l[R][G];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int e = c0 + w * (4 * R) + 4 * i + rg;
-          const bool live = e < z1;
-          const uint32_t en = live ? sh_ent[2 * (e - z0)] : 0u;
-          const int c = (int)(en & 0xffffffu);
-          const uint32_t m = en >> 24;
-          wd[i] = live ? (float)sh_ent[2 * (e - z0) + 1] : 0.f;
-          if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
-          else vr[i].zero();
+      for (int i = 0; i < R; ++i) {
+        const int e = c0 + w * (4 * R) + 4 * i + rg;
+        const bool live = e < e1;
+        const int c = live ? wl.cid_of(e) : 0;
+        const uint32_t m = live ? wl.mask_of(e) : 0u;
+        wd[i] = live ? (float)(wl.pre[e + 1] - wl.pre[e]) : 0.f;
+        if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
+        else vr[i].zero();
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            l[i][h] = ((m >> h) & 1u) ? f32_from_order_key(a.keys[(hbase + h) * a.C + c]) * a.scale : -INFINITY;
-        }
-        st.template add<R>(l, wd, vr);
+        for (int h = 0; h < G; ++h)
+          l[i][h] = ((m >> h) & 1u) ? f32_from_order_key(a.keys[(hbase + h) * a.C + c]) * a.scale : -INFINITY;
       }
+      st.template add<R>(l, wd, vr);
     }
   }
   WI_TP(22);
@@ -1106,8 +1143,15 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attend<T, G>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttListLds);
+    attr_set = true;
+  }
+  const size_t att_lds = a.list_mode ? ((size_t)2 * a.W32 + (size_t)4 * G * a.top_k + 1) * 4 : 0;
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
+  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), att_lds, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);

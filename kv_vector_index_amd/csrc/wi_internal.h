@@ -18,16 +18,17 @@ constexpr int kMaxGroup = 8;        // query heads per KV head supported by the 
 constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
 constexpr int kMaxClustersPerSeg = 4096;
 constexpr int kMaxGroupsPerDecode = 4096;  // B * Hkv of one decode call
+constexpr int kAttListLds = 96 * 1024;     // LDS the attention kernel may spend on a group's union
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
-  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g, part_cap, corr_cap;
+  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g, list_mode;
   size_t off_counters, off_keys, off_tile_norm, off_sel_bits, off_band_ids, off_band_key,
-      off_all_sel, off_wl_cid, off_wl_mask, off_wl_row0, off_wl_pre, off_part_tok, off_part_corr,
-      off_part_hdr, off_est_md, off_est_num, off_att_md, off_att_num, total;
+      off_all_sel, off_hl_cid, off_hl_sz, off_hl_row, off_hl_n, off_wl_cid, off_wl_mask,
+      off_wl_row0, off_wl_pre, off_grp, off_est_md, off_est_num, off_att_md, off_att_num, total;
 };
 DecodeLayout decode_layout(const wi_decode_params& p);
 
@@ -53,20 +54,21 @@ struct DecodeArgs {
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
-  int32_t* wl_cid;         // [BG, Umax] union entry tables when they exceed LDS
-  int32_t* wl_mask;        // [BG, Umax]
-  int32_t* wl_row0;        // [BG, Umax]
-  int32_t* wl_pre;         // [BG, Umax+1]
-  uint32_t* part_tok;      // [BG, S, part_cap] token slices: row | steady (bit 23) | mask << 24
-  uint32_t* part_corr;     // [BG, Sc, corr_cap, 2] correction slices: (cid | mask << 24, size)
-  int32_t* part_hdr;       // [BG, S + Sc] slice lengths
+  int32_t* hl_cid;         // [BH, top_k] list mode: the head's retrieved clusters, ascending
+  int32_t* hl_sz;          // [BH, top_k]            their sizes
+  int32_t* hl_row;         // [BH, top_k]            their first k_perm rows
+  int32_t* hl_n;           // [BH]                   list lengths
+  int32_t* wl_cid;         // [BG, Umax] table mode: the group's union, ascending cluster id
+  int32_t* wl_mask;        // [BG, Umax]             heads that retrieved each
+  int32_t* wl_row0;        // [BG, Umax]             first k_perm row
+  int32_t* wl_pre;         // [BG, Umax+1]           first token (steady zone first)
+  int32_t* grp;            // [BG, 2]                union length, token count
   float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
   float* est_num;          // [BG, est_tiles_g, G, d]
   float* att_md;           // [BG, S + Sc, G, 2]
   float* att_num;          // [BG, S + Sc, G, d]
   // shapes
-  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g, part_cap,
-      corr_cap;
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g, list_mode;
   float scale;
 };
 
