@@ -20,7 +20,6 @@ Prints one JSON line (rank 0) with the throughput, the roofline position of the 
 (per-kernel HIP-event timing over a second, eager pass), and the CPU oracle timed on the host.
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -35,16 +34,11 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_MFMA_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa_128k_bf16.json")
-KERNEL_NAMES = {"score": "k_score_est", "select": "k_select+k_union", "attend": "k_attend", "merge": "k_merge"}
+KERNEL_NAMES = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def decode_kernel_source_hash() -> str:
-    with open(os.path.join(ROOT, "kv_vector_index_amd", "csrc", "wi_decode.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def algorithmic_bytes(w, idx_offsets_np, sel_np):
@@ -274,7 +268,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_sha256_16") == decode_kernel_source_hash():
+        from kv_vector_index_amd.traffic import decode_source_hash
+        if tr.get("kernel_source_sha256_16") == decode_source_hash():
             traffic = tr.get("hbm_bytes_per_launch", {}).get(dominant)
 
     result = {

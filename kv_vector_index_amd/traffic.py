@@ -1,0 +1,127 @@
+"""HBM traffic records from rocprofv3 counter runs.
+
+Two sub-commands:
+
+    python -m kv_vector_index_amd.traffic copy --mib 512 --reps 4
+        runs a plain device-to-device copy of a known size, the calibration kernel for the
+        FETCH_SIZE / WRITE_SIZE counters;
+
+    python -m kv_vector_index_amd.traffic record --fetch DIR --write DIR \\
+            --copy-fetch DIR --copy-write DIR --copy-mib 512 --out FILE
+        reads the counter CSVs that `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` wrote
+        for a decode run and for the copy run, scales every kernel's per-dispatch KiB by the
+        factor that makes the copy kernel read and write exactly its known size, and writes a
+        JSON record of HBM bytes per launch for the decode kernels, tagged with a hash of the
+        decode kernels' source so that a record taken from older kernels is not reported.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECODE_KERNELS = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
+
+
+def decode_source_hash() -> str:
+    with open(os.path.join(ROOT, "kv_vector_index_amd", "csrc", "wi_decode.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def per_kernel_kib(directory: str, counter: str) -> dict:
+    """Average per-dispatch value of `counter` for every kernel name in a rocprofv3 CSV run."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    per_dispatch = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (fn, row["Dispatch_Id"])
+                name = row["Kernel_Name"]
+                v = float(row["Counter_Value"])
+                if key in per_dispatch:
+                    per_dispatch[key] = (name, per_dispatch[key][1] + v)
+                else:
+                    per_dispatch[key] = (name, v)
+    sums = {}
+    for name, v in per_dispatch.values():
+        s, n = sums.get(name, (0.0, 0))
+        sums[name] = (s + v, n + 1)
+    return {name: {"kib": s / n, "dispatches": n} for name, (s, n) in sums.items()}
+
+
+def match(table: dict, fragment: str) -> dict:
+    hits = {k: v for k, v in table.items() if fragment in k}
+    if not hits:
+        raise KeyError(f"no kernel matching {fragment!r}")
+    kib = sum(v["kib"] * v["dispatches"] for v in hits.values())
+    n = sum(v["dispatches"] for v in hits.values())
+    return {"kib": kib / n, "dispatches": n, "names": sorted(hits)}
+
+
+def cmd_copy(args):
+    import torch
+    n = args.mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": args.reps}), flush=True)
+
+
+def cmd_record(args):
+    nbytes = args.copy_mib << 20
+    cf = per_kernel_kib(args.copy_fetch, "FETCH_SIZE")
+    cw = per_kernel_kib(args.copy_write, "WRITE_SIZE")
+    # the calibration kernel: the one that moved the most bytes in the copy run
+    copy_name = max(cf, key=lambda k: cf[k]["kib"])
+    f_fetch = nbytes / (cf[copy_name]["kib"] * 1024.0)
+    f_write = nbytes / (cw[copy_name]["kib"] * 1024.0)
+    df = per_kernel_kib(args.fetch, "FETCH_SIZE")
+    dw = per_kernel_kib(args.write, "WRITE_SIZE")
+    out = {"kernel_source_sha256_16": decode_source_hash(),
+           "calibration": {"kernel": copy_name, "bytes": nbytes,
+                           "fetch_kib": cf[copy_name]["kib"], "write_kib": cw[copy_name]["kib"],
+                           "fetch_factor": f_fetch, "write_factor": f_write},
+           "hbm_bytes_per_launch": {}, "raw": {}}
+    for key, frag in DECODE_KERNELS.items():
+        try:
+            a, b = match(df, frag), match(dw, frag)
+        except KeyError:
+            continue
+        fetch_b = a["kib"] * 1024.0 * f_fetch
+        write_b = b["kib"] * 1024.0 * f_write
+        out["hbm_bytes_per_launch"][key] = fetch_b + write_b
+        out["raw"][key] = {"fetch_kib": a["kib"], "write_kib": b["kib"], "dispatches": a["dispatches"],
+                           "fetch_bytes": fetch_b, "write_bytes": write_b, "kernels": a["names"]}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out["hbm_bytes_per_launch"]))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=512)
+    c.add_argument("--reps", type=int, default=4)
+    r = sub.add_parser("record")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    r.add_argument("--copy-mib", type=int, default=512)
+    r.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    return cmd_copy(args) if args.cmd == "copy" else cmd_record(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
