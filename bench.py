@@ -33,7 +33,7 @@ METRIC = "wave-index decode steps/s at 128K ctx (batch·heads); achieved HBM GB/
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_MFMA_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa_128k_bf16.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_{}.json")   # per workload
 KERNEL_NAMES = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
@@ -72,15 +72,19 @@ def algorithmic_bytes(w, idx_offsets_np, sel_np):
 
 
 def cpu_baseline(w, seed, budget_s):
-    """The oracle's decode on the host: one full step (all query heads) on an oracle-finalized
-    index of the same workload, repeated within the time budget."""
+    """The oracle's decode on the host, on a bounded sample of the workload: the query heads of one
+    KV group of sequence 0 (the seeded generator draws that group exactly as in the full
+    workload), on an oracle-finalized index of that group, repeated within the time budget and
+    scaled to whole steps (B x Hq heads)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     from kv_vector_index_amd import synth
 
-    K, V, Q, labels = synth.make_instance(w, seed, with_labels=True)
+    G = w.Hq // w.Hkv
+    ws = w.replace(B=1, Hkv=1, Hq=G, steps=1)
+    K, V, Q, labels = synth.make_instance(ws, seed, with_labels=True)
     K = synth.as_float64(synth.cast(K, w.dtype))
     V = synth.as_float64(synth.cast(V, w.dtype))
     Q = synth.as_float64(synth.cast(Q, w.dtype))
@@ -89,16 +93,14 @@ def cpu_baseline(w, seed, budget_s):
     lab = (ci // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
     C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
     idx = oracle.finalize_index(K, V, lab, w.sink, w.window, C, w.dtype)
-    G = w.Hq // w.Hkv
     scale = 1 / math.sqrt(w.d)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         heads = 0
         while True:
-            for b in range(w.B):
-                for h in range(w.Hq):
-                    oracle.decode_head(Q[b, h], idx, b, h // G, w.top_k, scale)
-                    heads += 1
+            for h in range(G):
+                oracle.decode_head(Q[0, h], idx, 0, 0, w.top_k, scale)
+                heads += 1
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
@@ -112,8 +114,9 @@ def cpu_baseline(w, seed, budget_s):
         seg_s = time.perf_counter() - t1
     return {
         "value": steps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
-        "sample": f"{steps:.2f} decode steps (all {w.B * w.Hq} query heads each) of {w.name} on an "
-                  f"oracle-finalized index, NumPy float64, BLAS pinned to 1 thread, {dt:.1f} s",
+        "sample": f"{heads} query-head decodes ({G} heads of KV group 0, sequence 0) of {w.name} on an "
+                  f"oracle-finalized index, NumPy float64, BLAS pinned to 1 thread, {dt:.1f} s; "
+                  f"value = heads/s / ({w.B} x {w.Hq} heads per step)",
         "build_s_estimate": seg_s * len(segs) * w.B * w.Hkv,
         "build_sample": f"one {a1 - a0}-token segment x {w.iters} iterations in {seg_s:.1f} s, "
                         f"scaled to {len(segs) * w.B * w.Hkv} segments",
@@ -138,7 +141,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="gqa_128k_bf16")
-    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--instances", type=int, default=0, help="index copies cycled through (0: by footprint)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,12 +159,12 @@ def main():
     from kv_vector_index_amd import wave_index as wi
 
     w = synth.WORKLOADS[args.workload]
+    if w.top_k <= 0:
+        print(f"workload {w.name} has no decode step (build only)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
-    log(f"[bench] workload {w.name}: generating inputs")
-    K, V, Q = synth.make_instance(w, args.seed)
-    Kt, Vt = synth.cast(K, w.dtype, dev), synth.cast(V, w.dtype, dev)
-    Qt = synth.cast(Q, w.dtype, dev)
-    del K, V
+    log(f"[bench] workload {w.name}: generating inputs on the device")
+    Kt, Vt, Qt = synth.make_instance_device(w, args.seed, dev)
 
     # ---- index build (timed on its own, with per-kernel events)
     log("[bench] building the index")
@@ -183,9 +186,16 @@ def main():
     mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     del Kt, Vt
 
-    # ---- instances at distinct HBM addresses
-    insts = [idx] + [idx.clone() for _ in range(args.instances - 1)]
-    qs = [Qt.clone() for _ in insts]
+    # ---- instances at distinct HBM addresses (so that a step's bytes miss the 256 MB MALL) and
+    # the queries of the steps (a drifting sequence for multi-step workloads)
+    n_inst = args.instances if args.instances else (8 if w.B * w.Hkv * idx.C * w.d * 4 < (64 << 20) else 2 if w.B == 1 else 1)
+    insts = [idx] + [idx.clone() for _ in range(n_inst - 1)]
+    if w.steps > 1:
+        qm = synth.drift_queries_device(Qt, w.steps, w.drift, args.seed)
+        qs = [qm[t].to(torch.float32).to(Qt.dtype).contiguous() for t in range(w.steps)]
+        del qm
+    else:
+        qs = [Qt.clone() for _ in insts]
     p = wi.decode_params(idx, w.B, w.Hq, w.Hkv, w.top_k, Qt.dtype)
     ws_bytes = wi.wi_decode_workspace_bytes(p)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -196,7 +206,7 @@ def main():
 
     def step(i):
         j = i % len(insts)
-        wi.wi_decode(p, views[j], qs[j].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
+        wi.wi_decode(p, views[j], qs[i % len(qs)].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
                      ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
 
     log("[bench] warmup")
@@ -220,7 +230,7 @@ def main():
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
     else:
-        per_graph = min(K_steps, 8 * len(insts))
+        per_graph = min(K_steps, max(8 * len(insts), len(qs)))
         while K_steps % per_graph:
             per_graph -= 1
         g = torch.cuda.CUDAGraph()
@@ -265,8 +275,8 @@ def main():
     achieved = {k: per_bytes[k] / (avg_ms[k] / 1e3) / 1e9 for k in ("score", "attend") if avg_ms[k]}
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    if os.path.exists(TRAFFIC_FILE.format(w.name)):
+        with open(TRAFFIC_FILE.format(w.name)) as f:
             tr = json.load(f)
         from kv_vector_index_amd.traffic import decode_source_hash
         if tr.get("kernel_source_sha256_16") == decode_source_hash():
@@ -306,6 +316,19 @@ def main():
                   "assign_mfma_frac": (assign_flops / (assign_ms / 1e3) / 1e12 / mfma_peak) if assign_ms else None},
         "cpu_baseline": None,
     }
+    # streaming-copy bandwidth of this HBM, as context for the nominal 8 TB/s
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    result["hbm_copy_gbps"] = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_budget)

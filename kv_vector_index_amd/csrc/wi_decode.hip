@@ -41,8 +41,12 @@ constexpr int kScoreThreads = 256;
 // ============================================================================ k_score_est
 // grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid or value
 // sum row (256 B in bf16) is read as four 64-byte pieces by four lanes in one instruction.
+// Four waves per SIMD where the tile's registers fit in 128 VGPRs without spilling (bf16, up to
+// four heads per group); otherwise the compiler's choice.
+template <typename T, int G> struct ScoreWaves { static constexpr int v = (sizeof(T) == 2 && G <= 4) ? 4 : 1; };
+
 template <typename T, int G>
-__global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(ScoreWaves<T, G>::v))) void k_score_est(DecodeArgs a) {
   WI_TP(30);
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
@@ -63,8 +67,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
 
-  // value sums: lane (lr, rg = lg) of wave w owns rows w*32 + 4i + rg and dims [8 lr, 8 lr + 8).
-  // Issued first: they do not depend on the scores.
+  // Every global load of the tile is issued before the first wait: the value sums (lane (lr, lg)
+  // of wave w owns rows w*32 + 4i + lg and dims [8 lr, 8 lr + 8)), the sizes, the queries and
+  // the centroids, so the tile costs one memory round trip.
   u32x4_t svr[8];
   [[maybe_unused]] u32x4_t svr_hi[8];
 #pragma unroll
@@ -74,23 +79,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
     if constexpr (sizeof(T) == 4) svr_hi[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (r < nrows) {
       const T* p = sv + (size_t)r * kD + 8 * lr;
-      svr[i] = *reinterpret_cast<const u32x4_t*>(p);
-      if constexpr (sizeof(T) == 4) svr_hi[i] = *reinterpret_cast<const u32x4_t*>(p + 4);
+      svr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+      if constexpr (sizeof(T) == 4) svr_hi[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
     }
   }
-  if (tid < kEstTile) sh_n[tid] = tid < nrows ? (float)szs[tile * kEstTile + tid] : 0.f;
+  const int n_own = (tid < nrows) ? szs[tile * kEstTile + tid] : 0;   // sh_n, stored later
   float nmax = 0.f;                 // largest centroid norm among the tile's non-empty clusters
-  WI_TP(31);
 
   if constexpr (sizeof(T) == 2) {
     // A = query heads (row = lane&15), B = centroids (column = lane&15).  MFMA step s consumes
     // dims 32 s + 8 lg .. +8 on both operands, so the four lanes of a row read 64 contiguous bytes.
     bf16x8_t qa[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
-      else qa[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    }
     bf16x8_t mb[2][4];
     int sz[2];
 #pragma unroll
@@ -101,12 +100,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
         sz[t] = szs[c];
         const T* row = mu + (size_t)c * kD + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mb[t][s] = *reinterpret_cast<const bf16x8_t*>(row + 32 * s);
+        for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(row + 32 * s));
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) mb[t][s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
+      else qa[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int c = cbase + 16 * t + lr;
@@ -134,6 +139,22 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
   } else {
     // fp32: 16x16x4 MFMA, 32 steps; lane (lr, lg) loads dims 16 j + 4 lg .. +4 (j = 0..7) and step
     // 4 j + e consumes dim 16 j + 4 lg + e on both operands.
+    u32x4_t mraw[2][8];
+    int sz[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = cbase + 16 * t + lr;
+      sz[t] = 0;
+      if (c < C) {
+        sz[t] = szs[c];
+        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 4 * lg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mraw[t][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 16 * j));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mraw[t][j] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
     float qa[32];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -142,23 +163,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
       qa[4 * j] = __uint_as_float(v.x); qa[4 * j + 1] = __uint_as_float(v.y);
       qa[4 * j + 2] = __uint_as_float(v.z); qa[4 * j + 3] = __uint_as_float(v.w);
     }
+    WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int c = cbase + 16 * t + lr;
       float mb[32];
-      int sz = 0;
-      if (c < C) {
-        sz = szs[c];
-        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 4 * lg;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + 16 * j);
-          mb[4 * j] = __uint_as_float(v.x); mb[4 * j + 1] = __uint_as_float(v.y);
-          mb[4 * j + 2] = __uint_as_float(v.z); mb[4 * j + 3] = __uint_as_float(v.w);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 32; ++s) mb[s] = 0.f;
+      for (int j = 0; j < 8; ++j) {
+        mb[4 * j] = __uint_as_float(mraw[t][j].x); mb[4 * j + 1] = __uint_as_float(mraw[t][j].y);
+        mb[4 * j + 2] = __uint_as_float(mraw[t][j].z); mb[4 * j + 3] = __uint_as_float(mraw[t][j].w);
       }
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -173,13 +186,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_est(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * lg + r;
         if (h < G) {
-          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz > 0 ? f32_order_key(acc[r]) : 0u;
-          sh_s[h][cl] = (c < C && sz > 0) ? acc[r] * a.scale : -INFINITY;
+          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
+          sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
         }
       }
-      if (c < C && sz > 0) nmax = fmaxf(nmax, sqrtf(n2));
+      if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
     }
   }
+  if (tid < kEstTile) sh_n[tid] = (float)n_own;
   __syncthreads();
   WI_TP(32);
 
@@ -825,42 +839,68 @@ __device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp)
 
 // The group's work list as the attention workgroups see it: entry e (ascending cluster id) has a
 // cluster id, the mask of the heads that retrieved it, its first row in k_perm/v_perm and its
-// first token (the steady zone's tokens come first).  List mode keeps a copy in LDS, rebuilt by
-// every workgroup from the heads' sorted lists; table mode reads the table the group's last head
-// wrote to global memory.
+// first token (the steady zone's tokens come first).  List mode (kList) keeps it in LDS, rebuilt
+// by every workgroup from the heads' sorted lists; table mode reads the table the group's last
+// head wrote to global memory.
+template <bool kList>
 struct WorkList {
-  const uint32_t* cm;    // cid | mask << 24 (list mode)
+  const uint32_t* lds;   // list mode: [cm: n][row: n][pre: n + 1] at offsets 0, L, 2L
+  int L;
   const int32_t* cid;    // table mode
-  const int32_t* msk;    // table mode
+  const int32_t* msk;
   const int32_t* row;
-  const int32_t* pre;    // [n + 1]
+  const int32_t* pre;
   int n, n_tok;
-  bool lds;
-  __device__ int cid_of(int e) const { return lds ? (int)(cm[e] & 0xffffffu) : cid[e]; }
-  __device__ uint32_t mask_of(int e) const { return lds ? (cm[e] >> 24) : (uint32_t)msk[e]; }
+  __device__ int cid_of(int e) const { if constexpr (kList) return (int)(lds[e] & 0xffffffu); else return cid[e]; }
+  __device__ uint32_t mask_of(int e) const { if constexpr (kList) return lds[e] >> 24; else return (uint32_t)msk[e]; }
+  __device__ int row_of(int e) const { if constexpr (kList) return (int)lds[L + e]; else return row[e]; }
+  __device__ int pre_of(int e) const { if constexpr (kList) return (int)lds[2 * L + e]; else return pre[e]; }
 };
 
-// Union of the G heads' sorted lists in LDS: a bitmap over cluster ids gives each cluster's rank
-// (word prefix + popcount); every list entry ORs its head bit into the rank's slot.
+constexpr int kListPerThread = 16;   // list entries per thread in the union build (G * top_k <= 4096)
+
+// Union of the G heads' sorted lists in LDS.  All global loads (list lengths, ids, sizes, first
+// rows) are issued in one round; a bitmap over cluster ids then gives each cluster's rank (word
+// prefix + popcount) and every list entry ORs its head bit into the rank's slot.
+// LDS: ubm[W32] | wp[W32] | tcm[L] | trow[L] | tpre[L+1] | tsz[L]
 template <int G>
-__device__ WorkList build_union(const DecodeArgs& a, int b, int g, uint32_t* lds, int* iscr) {
+__device__ WorkList<true> build_union(const DecodeArgs& a, int b, int g, uint32_t* lds, int* iscr) {
   const int tid = threadIdx.x, NT = kAttThreads;
   const int W32 = a.W32, K = a.top_k, L = G * K;
-  uint32_t* ubm = lds;                     // [W32]
-  int32_t* wp = reinterpret_cast<int32_t*>(lds + W32);            // [W32]
-  uint32_t* tcm = lds + 2 * W32;           // [L]
-  int32_t* tsz = reinterpret_cast<int32_t*>(tcm + L);             // [L]
-  int32_t* trow = tsz + L;                 // [L]
-  int32_t* tpre = trow + L;                // [L + 1]
-  const size_t hb = ((size_t)b * a.Hq + (size_t)g * G);
+  uint32_t* ubm = lds;
+  int32_t* wp = reinterpret_cast<int32_t*>(lds + W32);
+  uint32_t* tab = lds + 2 * W32;
+  uint32_t* tcm = tab;
+  int32_t* trow = reinterpret_cast<int32_t*>(tab + L);
+  int32_t* tpre = reinterpret_cast<int32_t*>(tab + 2 * L);
+  int32_t* tsz = reinterpret_cast<int32_t*>(tab + 3 * L + 1);
+  const size_t hb = (size_t)b * a.Hq + (size_t)g * G;
+  int hn[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) hn[j] = a.hl_n[hb + j];
+  int c_[kListPerThread], sz_[kListPerThread], rw_[kListPerThread];
+#pragma unroll
+  for (int k = 0; k < kListPerThread; ++k) {
+    const int x = tid + k * NT;
+    c_[k] = -1; sz_[k] = 0; rw_[k] = 0;
+    if (x < L) {
+      const size_t li = hb * K + x;          // head j = x / K, entry x % K of that head's list
+      c_[k] = a.hl_cid[li]; sz_[k] = a.hl_sz[li]; rw_[k] = a.hl_row[li];
+    }
+  }
   for (int i = tid; i < W32; i += NT) ubm[i] = 0u;
   for (int i = tid; i < L; i += NT) tcm[i] = 0u;
   __syncthreads();
-  for (int x = tid; x < L; x += NT) {
-    const int j = x / K, i = x - j * K;
-    if (i < a.hl_n[hb + j]) {
-      const int c = a.hl_cid[(hb + j) * K + i];
-      atomicOr(&ubm[c >> 5], 1u << (c & 31));
+#pragma unroll
+  for (int k = 0; k < kListPerThread; ++k) {
+    const int x = tid + k * NT;
+    if (x < L) {
+      const int j = x / K, i = x - j * K;
+      int n = hn[0];
+#pragma unroll
+      for (int jj = 1; jj < G; ++jj) if (j == jj) n = hn[jj];
+      if (i >= n) c_[k] = -1;
+      if (c_[k] >= 0) atomicOr(&ubm[c_[k] >> 5], 1u << (c_[k] & 31));
     }
   }
   __syncthreads();
@@ -872,15 +912,15 @@ __device__ WorkList build_union(const DecodeArgs& a, int b, int g, uint32_t* lds
   int run = block_exclusive_scan(cnt, iscr, &n);
   for (int w = w0; w < w1; ++w) { wp[w] = run; run += __popc(ubm[w]); }
   __syncthreads();
-  for (int x = tid; x < L; x += NT) {
-    const int j = x / K, i = x - j * K;
-    if (i < a.hl_n[hb + j]) {
-      const size_t li = (hb + j) * K + i;
-      const int c = a.hl_cid[li];
+#pragma unroll
+  for (int k = 0; k < kListPerThread; ++k) {
+    const int x = tid + k * NT;
+    if (x < L && c_[k] >= 0) {
+      const int c = c_[k], j = x / K;
       const int r = wp[c >> 5] + __popc(ubm[c >> 5] & ((1u << (c & 31)) - 1u));
       atomicOr(&tcm[r], (uint32_t)c | (1u << (24 + j)));
-      tsz[r] = a.hl_sz[li];
-      trow[r] = a.hl_row[li];
+      tsz[r] = sz_[k];
+      trow[r] = rw_[k];
     }
   }
   __syncthreads();
@@ -893,65 +933,153 @@ __device__ WorkList build_union(const DecodeArgs& a, int b, int g, uint32_t* lds
   for (int e = e0; e < e1; ++e) { tpre[e] = a.NS + t; t += tsz[e]; }
   if (tid == 0) tpre[n] = a.NS + tot;
   __syncthreads();
-  WorkList wl;
-  wl.cm = tcm; wl.cid = nullptr; wl.msk = nullptr; wl.row = trow; wl.pre = tpre;
-  wl.n = n; wl.n_tok = a.NS + tot; wl.lds = true;
+  WorkList<true> wl;
+  wl.lds = tab; wl.L = L;
+  wl.cid = wl.msk = wl.row = wl.pre = nullptr;
+  wl.n = n; wl.n_tok = a.NS + tot;
   return wl;
 }
 
 // sh_ent[t - z0] for tokens [z0, z1): row | steady flag (bit 23) | head mask << 24.
-template <int G>
-__device__ void fill_tokens(const DecodeArgs& a, const WorkList& wl, int z0, int z1, uint32_t* sh_ent,
-                            int* sh_e0) {
+template <int G, bool kList>
+__device__ void fill_tokens(const DecodeArgs& a, const WorkList<kList>& wl, int z0, int z1,
+                            uint32_t* sh_ent, int* sh_e0) {
   const int tid = threadIdx.x, NT = kAttThreads, NS = a.NS;
   const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
   for (int t = z0 + tid; t < min(z1, NS); t += NT) sh_ent[t - z0] = (uint32_t)t | stag;
   const int u0 = max(z0, NS);
   if (u0 < z1) {
     for (int e = tid; e < wl.n; e += NT)
-      if (wl.pre[e] <= u0 && u0 < wl.pre[e + 1]) *sh_e0 = e;
+      if (wl.pre_of(e) <= u0 && u0 < wl.pre_of(e + 1)) *sh_e0 = e;
     __syncthreads();
     for (int e = *sh_e0 + tid; e < wl.n; e += NT) {
-      const int p0 = wl.pre[e];
+      const int p0 = wl.pre_of(e);
       if (p0 >= z1) break;
-      const int p1 = min(wl.pre[e + 1], z1);
-      const uint32_t r0 = (uint32_t)wl.row[e], tag = wl.mask_of(e) << 24;
+      const int p1 = min(wl.pre_of(e + 1), z1);
+      const uint32_t r0 = (uint32_t)wl.row_of(e), tag = wl.mask_of(e) << 24;
       for (int t = max(p0, u0); t < p1; ++t) sh_ent[t - z0] = (r0 + (uint32_t)(t - p0)) | tag;
     }
   }
   __syncthreads();
 }
 
+// Max over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));  // row half mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));  // row mirror
+  return v;
+}
+
+// Orders this wave's LDS writes before its later LDS reads (and the reverse) without a block
+// barrier: the lanes of one wave hand values to each other through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Scores of the group's query heads against 16 key rows on MFMA: A = queries (row = head,
+// padded to 16 with zeros), B = keys (column = the 16 tokens).  Lane (lr = lane & 15, lg =
+// lane >> 4) supplies token lr; the result lane holds heads 4 lg + r (r = 0..3) of token lr.
+template <typename T> struct QkTile;
+template <> struct QkTile<uint16_t> {
+  bf16x8_t q[4], k[4];
+  // MFMA step s consumes dims 32 s + 8 lg .. +8 of both operands (64 contiguous bytes per row
+  // across the four lanes of a lane column)
+  __device__ void load_q(const uint16_t* qg, int G, int lr, int lg) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (lr < G) q[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
+      else q[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  __device__ void load_k(const uint16_t* row, int lg) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k[s] = *reinterpret_cast<const bf16x8_t*>(row + 32 * s + 8 * lg);
+  }
+  __device__ void zero_k() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __device__ f32x4_t scores() const {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[s], k[s], acc, 0, 0, 0);
+    return acc;
+  }
+};
+template <> struct QkTile<float> {
+  float q[32];
+  u32x4_t k[8];
+  // MFMA step 4 j + e consumes dim 16 j + 4 lg + e of both operands
+  __device__ void load_q(const float* qg, int G, int lr, int lg) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (lr < G) v = *reinterpret_cast<const u32x4_t*>(qg + (size_t)lr * kD + 16 * j + 4 * lg);
+      q[4 * j] = __uint_as_float(v.x); q[4 * j + 1] = __uint_as_float(v.y);
+      q[4 * j + 2] = __uint_as_float(v.z); q[4 * j + 3] = __uint_as_float(v.w);
+    }
+  }
+  __device__ void load_k(const float* row, int lg) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k[j] = *reinterpret_cast<const u32x4_t*>(row + 16 * j + 4 * lg);
+  }
+  __device__ void zero_k() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k[j] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __device__ f32x4_t scores() const {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q[4 * j], __uint_as_float(k[j].x), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q[4 * j + 1], __uint_as_float(k[j].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q[4 * j + 2], __uint_as_float(k[j].z), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q[4 * j + 3], __uint_as_float(k[j].w), acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
 // grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
 // of its KV group's list (steady zone, then the retrieved clusters' rows, each row loaded once
 // for every head of the group that retrieved it); workgroup S + j folds the estimation terms of
 // union entries [j n / Sc, (j+1) n / Sc) into a partial the merge subtracts.
-template <typename T, int G>
+//
+// Token workgroups: each wave takes 16-token steps.  The group's query heads are scored against
+// the 16 key rows on MFMA; each head's running max comes from a DPP row reduction; the
+// probabilities go through a 256-byte LDS slot of the wave to the lanes that hold the value
+// rows (lane (lr, lg) holds dims 8 lr .. 8 lr + 7 of tokens 4 i + lg), which accumulate P V.
+template <typename T, int G, bool kList>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
-  constexpr int PASS = 16 * R;                 // 4 waves x 4 lane groups x R rows
+  constexpr int PASS = 16 * R;                 // corrections: 4 waves x 4 lane groups x R rows
+  constexpr int PG = G <= 4 ? 4 : 8;           // probabilities per token in the LDS slot
   extern __shared__ uint32_t att_dyn[];        // list mode: the group's union table
   __shared__ float sh_m[4 * G], sh_den[4 * G];
   __shared__ float sh_num[4 * G * kD];
   __shared__ uint32_t sh_ent[kAttStage];
+  __shared__ float sh_p[4][16][PG];
   __shared__ int iscr[24];
   __shared__ int sh_e0;
   WI_TP(20);
   const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split, Sc = a.att_items_g - a.att_split;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, rg = lane >> 4;
-  WorkList wl;
-  if (a.list_mode) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
+  WorkList<kList> wl;
+  if constexpr (kList) {
     wl = build_union<G>(a, b, g, att_dyn, iscr);
   } else {
-    wl.cm = nullptr;
+    wl.lds = nullptr; wl.L = 0;
     wl.cid = a.wl_cid + (size_t)bg * a.Umax;
     wl.msk = a.wl_mask + (size_t)bg * a.Umax;
     wl.row = a.wl_row0 + (size_t)bg * a.Umax;
     wl.pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
     wl.n = a.grp[(size_t)bg * 2];
     wl.n_tok = a.grp[(size_t)bg * 2 + 1];
-    wl.lds = false;
   }
   WI_TP(21);
   OState<G> st;
@@ -959,9 +1087,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   if (s < S) {
     const int t0 = (int)(((int64_t)s * wl.n_tok) / S), t1 = (int)(((int64_t)(s + 1) * wl.n_tok) / S);
     const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
-    Piece<T> qp[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qp[h].load(qg + (size_t)h * kD + 8 * lr);
+    QkTile<T> qk;
+    qk.load_q(qg, G, lr, lg);
     const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
     const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
@@ -969,36 +1096,87 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     for (int z0 = t0; z0 < t1; z0 += kAttStage) {
       const int z1 = min(t1, z0 + kAttStage);
       if (z0 > t0) __syncthreads();
-      fill_tokens<G>(a, wl, z0, z1, sh_ent, &sh_e0);
-      for (int c0 = z0; c0 < z1; c0 += PASS) {
-        uint32_t ent[R];
-        Piece<T> kr[R], vr[R];
+      fill_tokens<G, kList>(a, wl, z0, z1, sh_ent, &sh_e0);
+      const int nsteps = (z1 - z0 + 15) >> 4;
+      for (int j = w; j < nsteps; j += 4) {
+        const int base = z0 + 16 * j;
+        // key row of token base + lr (MFMA operand), value rows of tokens base + 4 i + lg
+        const int tk = base + lr;
+        const uint32_t eK = tk < z1 ? sh_ent[tk - z0] : 0u;
+        if ((eK >> 24) != 0u) {
+          const uint32_t row = eK & 0x7fffffu;
+          qk.load_k((((eK >> 23) & 1u) ? ks : kp) + (size_t)row * kD, lg);
+        } else {
+          qk.zero_k();
+        }
+        Piece<T> vr[4];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int t = c0 + w * (4 * R) + 4 * i + rg;
-          ent[i] = t < z1 ? sh_ent[t - z0] : 0u;
-          const int row = (int)(ent[i] & 0x7fffffu);
-          const bool stdy = (ent[i] >> 23) & 1u;
-          if ((ent[i] >> 24) != 0u) {
-            kr[i].load((stdy ? ks : kp) + (size_t)row * kD + 8 * lr);
-            vr[i].load((stdy ? vs : vp) + (size_t)row * kD + 8 * lr);
+        for (int i = 0; i < 4; ++i) {
+          const int tv = base + 4 * i + lg;
+          const uint32_t eV = tv < z1 ? sh_ent[tv - z0] : 0u;
+          if ((eV >> 24) != 0u) {
+            const uint32_t row = eV & 0x7fffffu;
+            vr[i].load((((eV >> 23) & 1u) ? vs : vp) + (size_t)row * kD + 8 * lr);
           } else {
-            kr[i].zero();
             vr[i].zero();
           }
         }
-        float l[R][G], wd[R];
+        const f32x4_t acc = qk.scores();
+        // logits of heads 4 lg + r for token lr; -inf where the head did not retrieve it
+        float sc[4], mx[4];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const uint32_t mk = ent[i] >> 24;
-          wd[i] = 1.f;
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * lg + r;
+          const bool ok = h < G && ((eK >> (24 + (h & 7))) & 1u);
+          sc[r] = ok ? acc[r] * a.scale : -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < (G < 4 ? G : 4); ++r) mx[r] = row16_max(sc[r]);
+        float alpha[G];
+        bool rescale = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float hm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx[h & 3]), 16 * (h >> 2)));
+          const float mn = fmaxf(st.m[h], hm);
+          alpha[h] = (st.m[h] == mn) ? 1.f : __expf(st.m[h] - mn);
+          rescale |= st.m[h] != mn;
+          st.m[h] = mn;
+        }
+        // probabilities of the lane's heads for token lr, handed to the value lanes through LDS
+        wave_lds_sync();
+        if (4 * lg < G) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float mh = st.m[r & (G - 1)];
+            if constexpr (G > 4) mh = lg ? st.m[4 + r] : st.m[r];
+            p[r] = sc[r] == -INFINITY ? 0.f : __expf(sc[r] - mh);
+          }
+          *reinterpret_cast<f32x4_t*>(&sh_p[w][lr][4 * lg]) = f32x4_t{p[0], p[1], p[2], p[3]};
+        }
+        wave_lds_sync();
+        if (rescale) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float x = row_dot<T>(qp[h], kr[i]);
-            l[i][h] = ((mk >> h) & 1u) ? x * a.scale : -INFINITY;
+            st.den[h] *= alpha[h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.num[h][e] *= alpha[h];
           }
         }
-        st.template add<R>(l, wd, vr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float pv[PG];
+          *reinterpret_cast<f32x4_t*>(&pv[0]) = *reinterpret_cast<const f32x4_t*>(&sh_p[w][4 * i + lg][0]);
+          if constexpr (PG > 4) *reinterpret_cast<f32x4_t*>(&pv[4]) = *reinterpret_cast<const f32x4_t*>(&sh_p[w][4 * i + lg][4]);
+          float vf[8];
+          vr[i].unpack(vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            st.den[h] += pv[h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.num[h][e] += pv[h] * vf[e];
+          }
+        }
       }
     }
   } else {
@@ -1006,6 +1184,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     const int e0 = (int)(((int64_t)j * wl.n) / Sc), e1 = (int)(((int64_t)(j + 1) * wl.n) / Sc);
     const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
     const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
+    const int rg = lg;
     for (int c0 = e0; c0 < e1; c0 += PASS) {
       Piece<T> vr[R];
       float wd[R], l[R][G];
@@ -1015,7 +1194,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
         const bool live = e < e1;
         const int c = live ? wl.cid_of(e) : 0;
         const uint32_t m = live ? wl.mask_of(e) : 0u;
-        wd[i] = live ? (float)(wl.pre[e + 1] - wl.pre[e]) : 0.f;
+        wd[i] = live ? (float)(wl.pre_of(e + 1) - wl.pre_of(e)) : 0.f;
         if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
         else vr[i].zero();
 #pragma unroll
@@ -1145,13 +1324,17 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attend<T, G>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attend<T, G, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kAttListLds);
     attr_set = true;
   }
-  const size_t att_lds = a.list_mode ? ((size_t)2 * a.W32 + (size_t)4 * G * a.top_k + 1) * 4 : 0;
+  // list mode LDS: bitmap and word prefix (2 W32) + the union table (4 L + 1)
+  const size_t att_lds = ((size_t)2 * a.W32 + (size_t)4 * G * a.top_k + 1) * 4;
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL((k_attend<T, G>), dim3(a.att_items_g, BG), dim3(kAttThreads), att_lds, s, a);
+  if (a.list_mode)
+    hipLaunchKernelGGL((k_attend<T, G, true>), dim3(a.att_items_g, BG), dim3(kAttThreads), att_lds, s, a);
+  else
+    hipLaunchKernelGGL((k_attend<T, G, false>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);

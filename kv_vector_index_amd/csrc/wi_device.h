@@ -10,7 +10,7 @@ namespace wi {
 // constant-rate wall clock at each marker; wi_trace_read() copies the table out.
 #ifdef WI_TRACE
 extern __device__ unsigned long long g_trace[64][8192];
-#define WI_TP(ev) do { if (threadIdx.x == 0) ::wi::g_trace[ev][blockIdx.x + blockIdx.y * gridDim.x] = wall_clock64(); } while (0)
+#define WI_TP(ev) do { const unsigned wi_tp_i = blockIdx.x + blockIdx.y * gridDim.x; if (threadIdx.x == 0 && wi_tp_i < 8192u) ::wi::g_trace[ev][wi_tp_i] = wall_clock64(); } while (0)
 #else
 #define WI_TP(ev) do { } while (0)
 #endif

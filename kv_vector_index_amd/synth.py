@@ -29,7 +29,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "blob_mixture_head", "make_instance", "drift_queries",
-           "cast", "as_float64"]
+           "cast", "as_float64", "make_instance_device", "drift_queries_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -143,6 +143,59 @@ def cast(x: np.ndarray, dtype: str, device=None):
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return t if device is None else t.to(device)
+
+
+def _device_generator(device, seed: int, b: int, g: int, stream: int = 0):
+    import torch
+    key = np.random.SeedSequence([int(seed), int(b), int(g), int(stream)]).generate_state(1, np.uint64)[0]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(key) & ((1 << 63) - 1))
+    return gen
+
+
+def make_instance_device(w: Workload, seed: int, device, n_override: Optional[int] = None):
+    """The same recipe as make_instance, drawn on the device with torch's generator (a different
+    random stream, so not the same numbers): K, V [B,Hkv,N,d] and q [B,Hq,d] in the storage
+    dtype.  For throughput runs whose sizes make host-side float64 generation slow; parity tests
+    use make_instance."""
+    import torch
+    N = w.N if n_override is None else int(n_override)
+    G = w.Hq // w.Hkv
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    K = torch.empty((w.B, w.Hkv, N, w.d), dtype=tdt, device=device)
+    V = torch.empty_like(K)
+    Q = torch.empty((w.B, w.Hq, w.d), dtype=tdt, device=device)
+    chunk = 1 << 16
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            gen = _device_generator(device, seed, b, g)
+            centres = torch.randn((w.n_blobs, w.d), generator=gen, device=device, dtype=torch.float64)
+            for t0 in range(0, N, chunk):
+                n = min(chunk, N - t0)
+                lab = torch.randint(0, w.n_blobs, (n,), generator=gen, device=device)
+                k = centres[lab] + w.key_noise * torch.randn((n, w.d), generator=gen, device=device,
+                                                             dtype=torch.float64)
+                k /= torch.linalg.vector_norm(k, dim=1, keepdim=True)
+                K[b, g, t0:t0 + n] = k.to(torch.float32).to(tdt)
+                v = torch.randn((n, w.d), generator=gen, device=device, dtype=torch.float64)
+                V[b, g, t0:t0 + n] = v.to(torch.float32).to(tdt)
+            u = torch.randint(0, w.n_blobs, (G,), generator=gen, device=device)
+            q = w.q_scale * centres[u] + w.q_noise * torch.randn((G, w.d), generator=gen, device=device,
+                                                                 dtype=torch.float64)
+            Q[b, g * G:(g + 1) * G] = q.to(torch.float32).to(tdt)
+    return K, V, Q
+
+
+def drift_queries_device(q0, steps: int, drift: float, seed: int = 0):
+    """[steps, *q0.shape] float64 device master copies: q_0 = q0, q_{t+1} = q_t + drift * N(0, I)."""
+    import torch
+    gen = _device_generator(q0.device, seed, 1 << 20, 0, 7)
+    out = torch.empty((steps,) + tuple(q0.shape), dtype=torch.float64, device=q0.device)
+    out[0] = q0.to(torch.float64)
+    for t in range(1, steps):
+        out[t] = out[t - 1] + drift * torch.randn(tuple(q0.shape), generator=gen, device=q0.device,
+                                                  dtype=torch.float64)
+    return out
 
 
 def as_float64(t) -> np.ndarray:
