@@ -125,41 +125,33 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.BH = p.B * p.Hq;
   L.G = p.Hq / p.Hkv;
   L.W32 = (int)ceil_div(p.C, 32);
-  L.Umax = (int)std::min<int64_t>(p.C, (int64_t)L.G * p.top_k);
   L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
-  // about 1024 attention workgroups in all, so that every one is resident at once on 256 CUs:
-  // S split the token list (none with less than 64 tokens of context), Sc ~ 1/32 of them fold
-  // the retrieved clusters' estimation terms
-  const int64_t ntok_max = (int64_t)p.n_steady + p.Nc;
-  const int total = (int)std::max<int64_t>(2, std::min<int64_t>(1024 / std::max(1, L.BG), ceil_div(ntok_max, 64) + 1));
-  const int Sc = (int)std::max<int64_t>(1, ceil_div(total, 32));
-  L.att_split = std::max(1, total - Sc);
-  L.att_items_g = L.att_split + Sc;
-  // list mode: every attention workgroup rebuilds the group's union in LDS from the heads' lists
-  const int64_t list_lds = ((int64_t)2 * L.W32 + (int64_t)4 * L.G * p.top_k + 1) * 4;
-  L.list_mode = ((int64_t)L.G * p.top_k <= 4096 && list_lds <= kAttListLds) ? 1 : 0;
+  // Attention workgroups per query head: Sc fold the retrieved clusters' estimation terms (64
+  // each); S split the head's exact tokens (steady zone + retrieved clusters, estimated from
+  // the mean cluster size).  S fills about one resident wave of the grid (kAttTarget in all)
+  // but gives no workgroup fewer than 64 or, when the grid must queue anyway, 512 tokens.
+  const int Sc = p.top_k > 0 ? (int)ceil_div(p.top_k, kCorrEntries) : 0;
+  const int64_t tok_est = (int64_t)p.n_steady + (p.C > 0 ? ceil_div((int64_t)p.top_k * p.Nc, p.C) : 0);
+  const int64_t fill = (int64_t)kAttTarget / L.BH - Sc;
+  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(tok_est, 64), std::max<int64_t>(ceil_div(tok_est, 512), fill)));
+  L.att_items = L.att_split + Sc;
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G, K = p.top_k;
   size_t o = 0;
-  L.off_counters = o;  o = align256(o + BG * 4);
-  L.off_keys = o;      o = align256(o + BH * C * 4);
-  L.off_tile_norm = o; o = align256(o + BG * L.est_tiles_g * 4);
-  L.off_sel_bits = o;  o = align256(o + BH * L.W32 * 4);
-  L.off_band_ids = o;  o = align256(o + BH * C * 4);
-  L.off_band_key = o;  o = align256(o + BH * C * 8);
-  L.off_all_sel = o;   o = align256(o + BH * 4);
-  L.off_hl_cid = o;    o = align256(o + BH * K * 4);
-  L.off_hl_sz = o;     o = align256(o + BH * K * 4);
-  L.off_hl_row = o;    o = align256(o + BH * K * 4);
-  L.off_hl_n = o;      o = align256(o + BH * 4);
-  L.off_wl_cid = o;    o = align256(o + BG * L.Umax * 4);
-  L.off_wl_mask = o;   o = align256(o + BG * L.Umax * 4);
-  L.off_wl_row0 = o;   o = align256(o + BG * L.Umax * 4);
-  L.off_wl_pre = o;    o = align256(o + BG * (L.Umax + 1) * 4);
-  L.off_grp = o;       o = align256(o + BG * 2 * 4);
-  L.off_est_md = o;    o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
-  L.off_est_num = o;   o = align256(o + BG * L.est_tiles_g * G * kD * 4);
-  L.off_att_md = o;    o = align256(o + BG * L.att_items_g * G * 2 * 4);
-  L.off_att_num = o;   o = align256(o + BG * L.att_items_g * G * kD * 4);
+  L.off_keys = o;       o = align256(o + BH * C * 4);
+  L.off_tile_norm = o;  o = align256(o + BG * L.est_tiles_g * 4);
+  L.off_sel_bits = o;   o = align256(o + BH * L.W32 * 4);
+  L.off_band_ids = o;   o = align256(o + BH * C * 4);
+  L.off_band_key = o;   o = align256(o + BH * C * 8);
+  L.off_all_sel = o;    o = align256(o + BH * 4);
+  L.off_hl_cid = o;     o = align256(o + BH * K * 4);
+  L.off_hl_row = o;     o = align256(o + BH * K * 4);
+  L.off_hl_pre = o;     o = align256(o + BH * (K + 1) * 4);
+  L.off_hl_key = o;     o = align256(o + BH * K * 4);
+  L.off_att_bounds = o; o = align256(o + BH * L.att_split * 4);
+  L.off_est_md = o;     o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
+  L.off_est_num = o;    o = align256(o + BG * L.est_tiles_g * G * kD * 4);
+  L.off_att_md = o;     o = align256(o + BH * L.att_items * 2 * 4);
+  L.off_att_num = o;    o = align256(o + BH * L.att_items * kD * 4);
   L.total = o;
   return L;
 }
@@ -260,7 +252,6 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.k_perm = idx->k_perm; a.v_perm = idx->v_perm; a.k_steady = idx->k_steady; a.v_steady = idx->v_steady;
   a.q = q; a.out = out; a.lse = lse; a.sel_ids = sel_ids;
   char* base = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(base + L.off_counters);
   a.keys = reinterpret_cast<uint32_t*>(base + L.off_keys);
   a.tile_norm = reinterpret_cast<float*>(base + L.off_tile_norm);
   a.sel_bits = reinterpret_cast<uint32_t*>(base + L.off_sel_bits);
@@ -268,21 +259,17 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
   a.hl_cid = reinterpret_cast<int32_t*>(base + L.off_hl_cid);
-  a.hl_sz = reinterpret_cast<int32_t*>(base + L.off_hl_sz);
   a.hl_row = reinterpret_cast<int32_t*>(base + L.off_hl_row);
-  a.hl_n = reinterpret_cast<int32_t*>(base + L.off_hl_n);
-  a.wl_cid = reinterpret_cast<int32_t*>(base + L.off_wl_cid);
-  a.wl_mask = reinterpret_cast<int32_t*>(base + L.off_wl_mask);
-  a.wl_row0 = reinterpret_cast<int32_t*>(base + L.off_wl_row0);
-  a.wl_pre = reinterpret_cast<int32_t*>(base + L.off_wl_pre);
-  a.grp = reinterpret_cast<int32_t*>(base + L.off_grp);
+  a.hl_pre = reinterpret_cast<int32_t*>(base + L.off_hl_pre);
+  a.hl_key = reinterpret_cast<uint32_t*>(base + L.off_hl_key);
+  a.att_bounds = reinterpret_cast<int32_t*>(base + L.off_att_bounds);
   a.est_md = reinterpret_cast<float*>(base + L.off_est_md);
   a.est_num = reinterpret_cast<float*>(base + L.off_est_num);
   a.att_md = reinterpret_cast<float*>(base + L.off_att_md);
   a.att_num = reinterpret_cast<float*>(base + L.off_att_num);
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
-  a.top_k = p->top_k; a.W32 = L.W32; a.Umax = L.Umax; a.est_tiles_g = L.est_tiles_g;
-  a.att_split = L.att_split; a.att_items_g = L.att_items_g; a.list_mode = L.list_mode;
+  a.top_k = p->top_k; a.W32 = L.W32; a.est_tiles_g = L.est_tiles_g;
+  a.att_split = L.att_split; a.att_items = L.att_items;
   a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   const int C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  if (tile == 0 && tid == 0) a.counters[bg] = 0u;    // arrivals of the group's heads in k_select
   if (C == 0) return;
   const int nrows = min(kEstTile, C - tile * kEstTile);
   const int cbase = tile * kEstTile + w * 32;
@@ -337,29 +336,6 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
 }
 
 
-// Hand-off between workgroups of one grid.  An agent-scope fence on this GPU writes back and
-// invalidates the whole L2 of the XCD, and those serialise across the chip; instead the data a
-// later workgroup reads is stored with agent-scope relaxed atomic stores (coherent at device
-// level), the writer waits for their completion before it bumps the arrival counter, and the
-// last arriving workgroup reads with agent-scope relaxed atomic loads.
-__device__ __forceinline__ void coherent_store(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Returns true in exactly one workgroup: the last of `expected` to arrive at `counter`.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* flag) {
-  __builtin_amdgcn_s_waitcnt(0);                         // this thread's stores have completed
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = atomicAdd(counter, 1u) == expected - 1u;
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  return last;
-}
-
 constexpr int kSelKPT = 16;         // clusters per thread held in registers
 constexpr int kBins = 2048;         // histogram bins over [min score, max score]
 constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
@@ -591,96 +567,59 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __syncthreads();
   WI_TP(8);
 
-  // ---- publish: ascending retrieved ids (to sel_ids and, in list mode, to this head's list with
-  // each cluster's size and first row)
-  const bool list_mode = a.list_mode != 0;
+  // ---- publish, in ascending id: sel_ids and the head's list (id, first k_perm row, first
+  // token after the steady zone, score key), padded to top_k; then, for every token workgroup
+  // of the attention kernel, the list entry that holds its first retrieved token
   {
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-    int n = 0;
-    for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
-    int tot;
-    int p = block_exclusive_scan(n, iscr, &tot);
-    int32_t* out = a.sel_ids ? a.sel_ids + (size_t)bh * a.top_k : nullptr;
-    const size_t lbase = (size_t)bh * a.top_k;
     const int32_t* sizes = a.sizes + (size_t)bg * C;
     const int32_t* off = a.offsets + (size_t)bg * (C + 1);
+    int n = 0, nt = 0;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t m = bits[w];
+      n += __popc(m);
+      while (m) { const int c = w * 32 + __ffs(m) - 1; m &= m - 1; nt += sizes[c]; }
+    }
+    int tot, ttot;
+    int p = block_exclusive_scan(n, iscr, &tot);
+    int t = a.NS + block_exclusive_scan(nt, iscr, &ttot);
+    const int K = a.top_k, S = a.att_split;
+    const int64_t ntok = (int64_t)a.NS + ttot;
+    int32_t* out = a.sel_ids ? a.sel_ids + (size_t)bh * K : nullptr;
+    const size_t lb = (size_t)bh * K, pb = (size_t)bh * (K + 1);
+    int32_t* bounds = a.att_bounds + (size_t)bh * S;
     for (int w = w0; w < w1; ++w) {
       uint32_t m = bits[w];
       while (m) {
-        const int bit = __ffs(m) - 1;
+        const int c = w * 32 + __ffs(m) - 1;
         m &= m - 1;
-        const int c = w * 32 + bit;
-        if (p < a.top_k) {
+        const int sz = sizes[c];
+        if (p < K) {
           if (out) out[p] = c;
-          if (list_mode) { a.hl_cid[lbase + p] = c; a.hl_sz[lbase + p] = sizes[c]; a.hl_row[lbase + p] = off[c]; }
+          a.hl_cid[lb + p] = c;
+          a.hl_row[lb + p] = off[c];
+          a.hl_pre[pb + p] = t;
+          a.hl_key[lb + p] = keys[c];
+          // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); its first
+          // retrieved token max(that start, NS) lies in [t, t + sz) for s in [s_a, s_b]
+          const int64_t s_a = p == 0 ? 0 : ((int64_t)t * S + ntok - 1) / ntok;
+          const int64_t s_b = min((int64_t)S - 1, ((int64_t)(t + sz) * S + ntok - 1) / ntok - 1);
+          for (int64_t x = s_a; x <= s_b; ++x) bounds[x] = p;
         }
         ++p;
+        t += sz;
       }
     }
-    if (out) for (int i = tot + tid; i < a.top_k; i += NT) out[i] = -1;
-    if (tid == 0) a.hl_n[bh] = min(tot, a.top_k);
+    for (int i = tot + tid; i < K; i += NT) {
+      if (out) out[i] = -1;
+      a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok;
+    }
+    if (tid == 0) a.hl_pre[pb + K] = (int)ntok;
+    if (tot == 0) for (int x = tid; x < S; x += NT) bounds[x] = 0;
   }
   if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
   WI_TP(9);
-  if (list_mode) return;
-
-  // ---- table mode (unions too large for the attention kernel's LDS): the last head of the group
-  // builds the union table in global memory
-  for (int w = tid; w < W32; w += NT) coherent_store(a.sel_bits + (size_t)bh * W32 + w, bits[w]);
-  if (!arrive_last(a.counters + bg, (uint32_t)G, &sh_i[4])) return;
-  WI_TP(10);
-  const uint32_t* hb = a.sel_bits + ((size_t)b * a.Hq + (size_t)g * G) * W32;
-  const int perw = (W32 + NT - 1) / NT;
-  const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-  int ne = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) u |= coherent_load(hb + (size_t)j * W32 + w);
-    ne += __popc(u);
-  }
-  int n_entries;
-  int e = block_exclusive_scan(ne, iscr, &n_entries);
-  int32_t* ucid = a.wl_cid + (size_t)bg * a.Umax;
-  int32_t* umsk = a.wl_mask + (size_t)bg * a.Umax;
-  int32_t* urow = a.wl_row0 + (size_t)bg * a.Umax;
-  int32_t* upre = a.wl_pre + (size_t)bg * (a.Umax + 1);
-  const int32_t* off = a.offsets + (size_t)bg * (C + 1);
-  const int32_t* sizes = a.sizes + (size_t)bg * C;
-  int nt = 0;
-  const int e_first = e;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t x[kMaxGroup];
-    uint32_t u = 0u;
-    for (int j = 0; j < G; ++j) { x[j] = coherent_load(hb + (size_t)j * W32 + w); u |= x[j]; }
-    while (u) {
-      const int bit = __ffs(u) - 1;
-      u &= u - 1;
-      int m = 0;
-      for (int j = 0; j < G; ++j) m |= (int)((x[j] >> bit) & 1u) << j;
-      const int c = w * 32 + bit;
-      ucid[e] = c;
-      umsk[e] = m;
-      urow[e] = off[c];
-      upre[e] = sizes[c];
-      nt += sizes[c];
-      ++e;
-    }
-  }
-  int n_utok;
-  int t = block_exclusive_scan(nt, iscr, &n_utok);
-  const int NS = a.NS;
-  for (int i = e_first; i < e; ++i) {
-    const int sz = upre[i];
-    upre[i] = NS + t;
-    t += sz;
-  }
-  if (tid == 0) {
-    upre[n_entries] = NS + n_utok;
-    a.grp[(size_t)bg * 2 + 0] = n_entries;
-    a.grp[(size_t)bg * 2 + 1] = NS + n_utok;
-  }
-  WI_TP(13);
 }
 
 // ============================================================================ k_attend
@@ -837,132 +776,6 @@ __device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp)
   return s;
 }
 
-// The group's work list as the attention workgroups see it: entry e (ascending cluster id) has a
-// cluster id, the mask of the heads that retrieved it, its first row in k_perm/v_perm and its
-// first token (the steady zone's tokens come first).  List mode (kList) keeps it in LDS, rebuilt
-// by every workgroup from the heads' sorted lists; table mode reads the table the group's last
-// head wrote to global memory.
-template <bool kList>
-struct WorkList {
-  const uint32_t* lds;   // list mode: [cm: n][row: n][pre: n + 1] at offsets 0, L, 2L
-  int L;
-  const int32_t* cid;    // table mode
-  const int32_t* msk;
-  const int32_t* row;
-  const int32_t* pre;
-  int n, n_tok;
-  __device__ int cid_of(int e) const { if constexpr (kList) return (int)(lds[e] & 0xffffffu); else return cid[e]; }
-  __device__ uint32_t mask_of(int e) const { if constexpr (kList) return lds[e] >> 24; else return (uint32_t)msk[e]; }
-  __device__ int row_of(int e) const { if constexpr (kList) return (int)lds[L + e]; else return row[e]; }
-  __device__ int pre_of(int e) const { if constexpr (kList) return (int)lds[2 * L + e]; else return pre[e]; }
-};
-
-constexpr int kListPerThread = 16;   // list entries per thread in the union build (G * top_k <= 4096)
-
-// Union of the G heads' sorted lists in LDS.  All global loads (list lengths, ids, sizes, first
-// rows) are issued in one round; a bitmap over cluster ids then gives each cluster's rank (word
-// prefix + popcount) and every list entry ORs its head bit into the rank's slot.
-// LDS: ubm[W32] | wp[W32] | tcm[L] | trow[L] | tpre[L+1] | tsz[L]
-template <int G>
-__device__ WorkList<true> build_union(const DecodeArgs& a, int b, int g, uint32_t* lds, int* iscr) {
-  const int tid = threadIdx.x, NT = kAttThreads;
-  const int W32 = a.W32, K = a.top_k, L = G * K;
-  uint32_t* ubm = lds;
-  int32_t* wp = reinterpret_cast<int32_t*>(lds + W32);
-  uint32_t* tab = lds + 2 * W32;
-  uint32_t* tcm = tab;
-  int32_t* trow = reinterpret_cast<int32_t*>(tab + L);
-  int32_t* tpre = reinterpret_cast<int32_t*>(tab + 2 * L);
-  int32_t* tsz = reinterpret_cast<int32_t*>(tab + 3 * L + 1);
-  const size_t hb = (size_t)b * a.Hq + (size_t)g * G;
-  int hn[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) hn[j] = a.hl_n[hb + j];
-  int c_[kListPerThread], sz_[kListPerThread], rw_[kListPerThread];
-#pragma unroll
-  for (int k = 0; k < kListPerThread; ++k) {
-    const int x = tid + k * NT;
-    c_[k] = -1; sz_[k] = 0; rw_[k] = 0;
-    if (x < L) {
-      const size_t li = hb * K + x;          // head j = x / K, entry x % K of that head's list
-      c_[k] = a.hl_cid[li]; sz_[k] = a.hl_sz[li]; rw_[k] = a.hl_row[li];
-    }
-  }
-  for (int i = tid; i < W32; i += NT) ubm[i] = 0u;
-  for (int i = tid; i < L; i += NT) tcm[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kListPerThread; ++k) {
-    const int x = tid + k * NT;
-    if (x < L) {
-      const int j = x / K, i = x - j * K;
-      int n = hn[0];
-#pragma unroll
-      for (int jj = 1; jj < G; ++jj) if (j == jj) n = hn[jj];
-      if (i >= n) c_[k] = -1;
-      if (c_[k] >= 0) atomicOr(&ubm[c_[k] >> 5], 1u << (c_[k] & 31));
-    }
-  }
-  __syncthreads();
-  const int pw = (W32 + NT - 1) / NT;
-  const int w0 = min(W32, tid * pw), w1 = min(W32, w0 + pw);
-  int cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(ubm[w]);
-  int n;
-  int run = block_exclusive_scan(cnt, iscr, &n);
-  for (int w = w0; w < w1; ++w) { wp[w] = run; run += __popc(ubm[w]); }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kListPerThread; ++k) {
-    const int x = tid + k * NT;
-    if (x < L && c_[k] >= 0) {
-      const int c = c_[k], j = x / K;
-      const int r = wp[c >> 5] + __popc(ubm[c >> 5] & ((1u << (c & 31)) - 1u));
-      atomicOr(&tcm[r], (uint32_t)c | (1u << (24 + j)));
-      tsz[r] = sz_[k];
-      trow[r] = rw_[k];
-    }
-  }
-  __syncthreads();
-  const int pe = (n + NT - 1) / NT;
-  const int e0 = min(n, tid * pe), e1 = min(n, e0 + pe);
-  int nt = 0;
-  for (int e = e0; e < e1; ++e) nt += tsz[e];
-  int tot;
-  int t = block_exclusive_scan(nt, iscr, &tot);
-  for (int e = e0; e < e1; ++e) { tpre[e] = a.NS + t; t += tsz[e]; }
-  if (tid == 0) tpre[n] = a.NS + tot;
-  __syncthreads();
-  WorkList<true> wl;
-  wl.lds = tab; wl.L = L;
-  wl.cid = wl.msk = wl.row = wl.pre = nullptr;
-  wl.n = n; wl.n_tok = a.NS + tot;
-  return wl;
-}
-
-// sh_ent[t - z0] for tokens [z0, z1): row | steady flag (bit 23) | head mask << 24.
-template <int G, bool kList>
-__device__ void fill_tokens(const DecodeArgs& a, const WorkList<kList>& wl, int z0, int z1,
-                            uint32_t* sh_ent, int* sh_e0) {
-  const int tid = threadIdx.x, NT = kAttThreads, NS = a.NS;
-  const uint32_t stag = (1u << 23) | ((uint32_t)((1 << G) - 1) << 24);
-  for (int t = z0 + tid; t < min(z1, NS); t += NT) sh_ent[t - z0] = (uint32_t)t | stag;
-  const int u0 = max(z0, NS);
-  if (u0 < z1) {
-    for (int e = tid; e < wl.n; e += NT)
-      if (wl.pre_of(e) <= u0 && u0 < wl.pre_of(e + 1)) *sh_e0 = e;
-    __syncthreads();
-    for (int e = *sh_e0 + tid; e < wl.n; e += NT) {
-      const int p0 = wl.pre_of(e);
-      if (p0 >= z1) break;
-      const int p1 = min(wl.pre_of(e + 1), z1);
-      const uint32_t r0 = (uint32_t)wl.row_of(e), tag = wl.mask_of(e) << 24;
-      for (int t = max(p0, u0); t < p1; ++t) sh_ent[t - z0] = (r0 + (uint32_t)(t - p0)) | tag;
-    }
-  }
-  __syncthreads();
-}
-
 // Max over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), in every lane of the row.
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
@@ -980,18 +793,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Scores of the group's query heads against 16 key rows on MFMA: A = queries (row = head,
-// padded to 16 with zeros), B = keys (column = the 16 tokens).  Lane (lr = lane & 15, lg =
-// lane >> 4) supplies token lr; the result lane holds heads 4 lg + r (r = 0..3) of token lr.
+// Scores of a query against 16 key rows on MFMA: A = the query (row 0; rows 1-15 zero), B = the
+// keys (column = token).  Lane (lr = lane & 15, lg = lane >> 4) supplies token lr; the result
+// lane (lr, lg = 0) holds the score of token lr in register 0.
 template <typename T> struct QkTile;
 template <> struct QkTile<uint16_t> {
   bf16x8_t q[4], k[4];
   // MFMA step s consumes dims 32 s + 8 lg .. +8 of both operands (64 contiguous bytes per row
   // across the four lanes of a lane column)
-  __device__ void load_q(const uint16_t* qg, int G, int lr, int lg) {
+  __device__ void load_q(const uint16_t* qh, int lr, int lg) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (lr < G) q[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
+      if (lr == 0) q[s] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * s + 8 * lg);
       else q[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
@@ -1014,11 +827,11 @@ template <> struct QkTile<float> {
   float q[32];
   u32x4_t k[8];
   // MFMA step 4 j + e consumes dim 16 j + 4 lg + e of both operands
-  __device__ void load_q(const float* qg, int G, int lr, int lg) {
+  __device__ void load_q(const float* qh, int lr, int lg) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (lr < G) v = *reinterpret_cast<const u32x4_t*>(qg + (size_t)lr * kD + 16 * j + 4 * lg);
+      if (lr == 0) v = *reinterpret_cast<const u32x4_t*>(qh + 16 * j + 4 * lg);
       q[4 * j] = __uint_as_float(v.x); q[4 * j + 1] = __uint_as_float(v.y);
       q[4 * j + 2] = __uint_as_float(v.z); q[4 * j + 3] = __uint_as_float(v.w);
     }
@@ -1044,168 +857,138 @@ template <> struct QkTile<float> {
   }
 };
 
-// grid (S + Sc, B*Hkv).  Workgroup s < S attends exactly over tokens [s n_tok / S, (s+1) n_tok / S)
-// of its KV group's list (steady zone, then the retrieved clusters' rows, each row loaded once
-// for every head of the group that retrieved it); workgroup S + j folds the estimation terms of
-// union entries [j n / Sc, (j+1) n / Sc) into a partial the merge subtracts.
+// grid (B*Hq * (S + Sc)): workgroup (bh, s).  For s < S it attends exactly over tokens
+// [s n_tok / S, (s+1) n_tok / S) of query head bh's list: the steady zone, then the rows of the
+// head's retrieved clusters in ascending cluster id.  Workgroup S + j folds the estimation terms
+// of entries [64 j, 64 j + 64) of the head's retrieved list into a partial the merge subtracts.
 //
-// Token workgroups: each wave takes 16-token steps.  The group's query heads are scored against
-// the 16 key rows on MFMA; each head's running max comes from a DPP row reduction; the
-// probabilities go through a 256-byte LDS slot of the wave to the lanes that hold the value
-// rows (lane (lr, lg) holds dims 8 lr .. 8 lr + 7 of tokens 4 i + lg), which accumulate P V.
-template <typename T, int G, bool kList>
+// Token workgroups map their tokens to rows through the list (first token of every entry, in
+// LDS, binary-searched per token), then each wave takes 16-token steps: the query is scored
+// against the 16 key rows on MFMA, the running max comes from a DPP row reduction, and the
+// probabilities go through a 64-byte LDS slot of the wave to the lanes that hold the value rows
+// (lane (lr, lg) holds dims 8 lr .. 8 lr + 7 of tokens 4 i + lg), which accumulate P V.
+template <typename T>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
   constexpr int PASS = 16 * R;                 // corrections: 4 waves x 4 lane groups x R rows
-  constexpr int PG = G <= 4 ? 4 : 8;           // probabilities per token in the LDS slot
-  extern __shared__ uint32_t att_dyn[];        // list mode: the group's union table
-  __shared__ float sh_m[4 * G], sh_den[4 * G];
-  __shared__ float sh_num[4 * G * kD];
-  __shared__ uint32_t sh_ent[kAttStage];
-  __shared__ float sh_p[4][16][PG];
-  __shared__ int iscr[24];
-  __shared__ int sh_e0;
+  __shared__ float sh_m[4], sh_den[4];
+  __shared__ float sh_num[4 * kD];
+  __shared__ uint32_t sh_ent[kAttStage];       // token -> row | steady flag (bit 23) | valid (bit 24)
+  __shared__ int spre[kAttStage + 1];          // first token of list entries e_cur + x
+  __shared__ int srow[kAttStage];              // first k_perm row of list entries e_cur + x
+  __shared__ float sh_p[4][16];
+  __shared__ int sh_next;
   WI_TP(20);
-  const int bg = blockIdx.y, s = blockIdx.x, S = a.att_split, Sc = a.att_items_g - a.att_split;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
-  WorkList<kList> wl;
-  if constexpr (kList) {
-    wl = build_union<G>(a, b, g, att_dyn, iscr);
-  } else {
-    wl.lds = nullptr; wl.L = 0;
-    wl.cid = a.wl_cid + (size_t)bg * a.Umax;
-    wl.msk = a.wl_mask + (size_t)bg * a.Umax;
-    wl.row = a.wl_row0 + (size_t)bg * a.Umax;
-    wl.pre = a.wl_pre + (size_t)bg * (a.Umax + 1);
-    wl.n = a.grp[(size_t)bg * 2];
-    wl.n_tok = a.grp[(size_t)bg * 2 + 1];
-  }
-  WI_TP(21);
-  OState<G> st;
+  const int items = a.att_items, S = a.att_split, K = a.top_k;
+  const int bh = blockIdx.x / items, s = blockIdx.x - bh * items;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, bg = b * a.Hkv + h / a.G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int NS = a.NS;
+  const int32_t* pre = a.hl_pre + (size_t)bh * (K + 1);
+  OState<1> st;
   st.init();
   if (s < S) {
-    const int t0 = (int)(((int64_t)s * wl.n_tok) / S), t1 = (int)(((int64_t)(s + 1) * wl.n_tok) / S);
-    const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
+    const int ntok = pre[K];
+    int e_cur = K > 0 ? a.att_bounds[(size_t)bh * S + s] : 0;
+    const int t0 = (int)(((int64_t)s * ntok) / S), t1 = (int)(((int64_t)(s + 1) * ntok) / S);
+    const int32_t* rowl = a.hl_row + (size_t)bh * K;
     QkTile<T> qk;
-    qk.load_q(qg, G, lr, lg);
+    qk.load_q(static_cast<const T*>(a.q) + (size_t)bh * kD, lr, lg);
     const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
     const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
-    const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * a.NS * kD;
-    const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * a.NS * kD;
+    const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * NS * kD;
+    const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * NS * kD;
+    WI_TP(21);
     for (int z0 = t0; z0 < t1; z0 += kAttStage) {
       const int z1 = min(t1, z0 + kAttStage);
-      if (z0 > t0) __syncthreads();
-      fill_tokens<G, kList>(a, wl, z0, z1, sh_ent, &sh_e0);
+      if (z0 > t0) __syncthreads();            // the previous chunk's map is no longer read
+      for (int t = z0 + tid; t < min(z1, NS); t += kAttThreads) sh_ent[t - z0] = (uint32_t)t | (3u << 23);
+      const int u0 = max(z0, NS);
+      if (u0 < z1) {
+        // the at most z1 - u0 <= kAttStage entries that hold tokens [u0, z1) start at e_cur
+        for (int x = tid; x <= kAttStage; x += kAttThreads) {
+          const int e = e_cur + x;
+          spre[x] = e <= K ? pre[e] : ntok;
+          if (x < kAttStage) srow[x] = e < K ? rowl[e] : 0;
+        }
+        __syncthreads();
+        for (int t = u0 + tid; t < z1; t += kAttThreads) {
+          int lo = 0, hi = kAttStage;            // spre[lo] <= t < spre[hi]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (spre[mid] <= t) lo = mid; else hi = mid;
+          }
+          sh_ent[t - z0] = (uint32_t)(srow[lo] + (t - spre[lo])) | (1u << 24);
+          if (t == z1 - 1) sh_next = e_cur + lo;
+        }
+      }
+      __syncthreads();
+      if (u0 < z1) e_cur = sh_next;
       const int nsteps = (z1 - z0 + 15) >> 4;
       for (int j = w; j < nsteps; j += 4) {
         const int base = z0 + 16 * j;
         // key row of token base + lr (MFMA operand), value rows of tokens base + 4 i + lg
         const int tk = base + lr;
         const uint32_t eK = tk < z1 ? sh_ent[tk - z0] : 0u;
-        if ((eK >> 24) != 0u) {
-          const uint32_t row = eK & 0x7fffffu;
-          qk.load_k((((eK >> 23) & 1u) ? ks : kp) + (size_t)row * kD, lg);
-        } else {
-          qk.zero_k();
-        }
+        if ((eK >> 24) != 0u) qk.load_k((((eK >> 23) & 1u) ? ks : kp) + (size_t)(eK & 0x7fffffu) * kD, lg);
+        else qk.zero_k();
         Piece<T> vr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tv = base + 4 * i + lg;
           const uint32_t eV = tv < z1 ? sh_ent[tv - z0] : 0u;
-          if ((eV >> 24) != 0u) {
-            const uint32_t row = eV & 0x7fffffu;
-            vr[i].load((((eV >> 23) & 1u) ? vs : vp) + (size_t)row * kD + 8 * lr);
-          } else {
-            vr[i].zero();
-          }
+          if ((eV >> 24) != 0u) vr[i].load((((eV >> 23) & 1u) ? vs : vp) + (size_t)(eV & 0x7fffffu) * kD + 8 * lr);
+          else vr[i].zero();
         }
         const f32x4_t acc = qk.scores();
-        // logits of heads 4 lg + r for token lr; -inf where the head did not retrieve it
-        float sc[4], mx[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * lg + r;
-          const bool ok = h < G && ((eK >> (24 + (h & 7))) & 1u);
-          sc[r] = ok ? acc[r] * a.scale : -INFINITY;
-        }
-#pragma unroll
-        for (int r = 0; r < (G < 4 ? G : 4); ++r) mx[r] = row16_max(sc[r]);
-        float alpha[G];
-        bool rescale = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float hm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx[h & 3]), 16 * (h >> 2)));
-          const float mn = fmaxf(st.m[h], hm);
-          alpha[h] = (st.m[h] == mn) ? 1.f : __expf(st.m[h] - mn);
-          rescale |= st.m[h] != mn;
-          st.m[h] = mn;
-        }
-        // probabilities of the lane's heads for token lr, handed to the value lanes through LDS
+        const float sc = (lg == 0 && (eK >> 24) != 0u) ? acc[0] * a.scale : -INFINITY;
+        const float hm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_max(sc)), 0));
+        const float mn = fmaxf(st.m[0], hm);
+        const float alpha = (st.m[0] == mn) ? 1.f : __expf(st.m[0] - mn);
+        const bool rescale = st.m[0] != mn;
+        st.m[0] = mn;
         wave_lds_sync();
-        if (4 * lg < G) {
-          float p[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float mh = st.m[r & (G - 1)];
-            if constexpr (G > 4) mh = lg ? st.m[4 + r] : st.m[r];
-            p[r] = sc[r] == -INFINITY ? 0.f : __expf(sc[r] - mh);
-          }
-          *reinterpret_cast<f32x4_t*>(&sh_p[w][lr][4 * lg]) = f32x4_t{p[0], p[1], p[2], p[3]};
-        }
+        if (lg == 0) sh_p[w][lr] = sc == -INFINITY ? 0.f : __expf(sc - mn);
         wave_lds_sync();
         if (rescale) {
+          st.den[0] *= alpha;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            st.den[h] *= alpha[h];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.num[h][e] *= alpha[h];
-          }
+          for (int e = 0; e < 8; ++e) st.num[0][e] *= alpha;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float pv[PG];
-          *reinterpret_cast<f32x4_t*>(&pv[0]) = *reinterpret_cast<const f32x4_t*>(&sh_p[w][4 * i + lg][0]);
-          if constexpr (PG > 4) *reinterpret_cast<f32x4_t*>(&pv[4]) = *reinterpret_cast<const f32x4_t*>(&sh_p[w][4 * i + lg][4]);
+          const float p = sh_p[w][4 * i + lg];
           float vf[8];
           vr[i].unpack(vf);
+          st.den[0] += p;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            st.den[h] += pv[h];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.num[h][e] += pv[h] * vf[e];
-          }
+          for (int e = 0; e < 8; ++e) st.num[0][e] += p * vf[e];
         }
       }
     }
   } else {
-    const int j = s - S;
-    const int e0 = (int)(((int64_t)j * wl.n) / Sc), e1 = (int)(((int64_t)(j + 1) * wl.n) / Sc);
+    const int e0 = (s - S) * kCorrEntries, e1 = min(K, e0 + kCorrEntries);
     const T* sv = static_cast<const T*>(a.sv) + (size_t)bg * a.C * kD;
-    const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
-    const int rg = lg;
+    const size_t lb = (size_t)bh * K;
     for (int c0 = e0; c0 < e1; c0 += PASS) {
       Piece<T> vr[R];
-      float wd[R], l[R][G];
+      float wd[R], l[R][1];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int e = c0 + w * (4 * R) + 4 * i + rg;
+        const int e = c0 + w * (4 * R) + 4 * i + lg;
         const bool live = e < e1;
-        const int c = live ? wl.cid_of(e) : 0;
-        const uint32_t m = live ? wl.mask_of(e) : 0u;
-        wd[i] = live ? (float)(wl.pre_of(e + 1) - wl.pre_of(e)) : 0.f;
-        if (live) vr[i].load(sv + (size_t)c * kD + 8 * lr);
+        const int c = live ? a.hl_cid[lb + e] : 0;
+        const uint32_t key = live ? a.hl_key[lb + e] : 0u;
+        wd[i] = live ? (float)(pre[e + 1] - pre[e]) : 0.f;
+        if (key != 0u) vr[i].load(sv + (size_t)c * kD + 8 * lr);
         else vr[i].zero();
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          l[i][h] = ((m >> h) & 1u) ? f32_from_order_key(a.keys[(hbase + h) * a.C + c]) * a.scale : -INFINITY;
+        l[i][0] = key != 0u ? f32_from_order_key(key) * a.scale : -INFINITY;
       }
       st.template add<R>(l, wd, vr);
     }
   }
   WI_TP(22);
-  write_partial<G>(st, (size_t)bg * a.att_items_g + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
+  write_partial<1>(st, (size_t)bh * items + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
   WI_TP(23);
 }
 
@@ -1229,16 +1012,16 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
   const bool use_est = a.all_sel[bh] == 0;
   const int PE = use_est ? a.est_tiles_g : 0;
-  const int S = a.att_split;
-  const int PC = use_est ? a.att_items_g - S : 0;
+  const int S = a.att_split, items = a.att_items;
+  const int PC = use_est ? items - S : 0;
   const int P = PE + S + PC;
   auto md_of = [&](int p) -> const float* {
     if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
-    return a.att_md + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * 2;
+    return a.att_md + ((size_t)bh * items + (p - PE)) * 2;
   };
   auto num_of = [&](int p) -> const float* {
     if (p < PE) return a.est_num + (((size_t)bg * a.est_tiles_g + p) * G + hi) * kD;
-    return a.att_num + (((size_t)bg * a.att_items_g + (p - PE)) * G + hi) * kD;
+    return a.att_num + ((size_t)bh * items + (p - PE)) * kD;
   };
   const int col = tid & 31, rep = tid >> 5;
   constexpr int RP = kMergeThreads / 32;
@@ -1322,19 +1105,8 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attend<T, G, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttListLds);
-    attr_set = true;
-  }
-  // list mode LDS: bitmap and word prefix (2 W32) + the union table (4 L + 1)
-  const size_t att_lds = ((size_t)2 * a.W32 + (size_t)4 * G * a.top_k + 1) * 4;
   prof_begin(WI_STAGE_ATTEND, s);
-  if (a.list_mode)
-    hipLaunchKernelGGL((k_attend<T, G, true>), dim3(a.att_items_g, BG), dim3(kAttThreads), att_lds, s, a);
-  else
-    hipLaunchKernelGGL((k_attend<T, G, false>), dim3(a.att_items_g, BG), dim3(kAttThreads), 0, s, a);
+  hipLaunchKernelGGL(k_attend<T>, dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);

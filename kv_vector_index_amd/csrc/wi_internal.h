@@ -12,23 +12,23 @@
 
 namespace wi {
 
-constexpr int kChunkTokens = 128;   // tokens per exact-attention work item
 constexpr int kEstTile = 128;       // clusters per estimation work item
 constexpr int kMaxGroup = 8;        // query heads per KV head supported by the decode kernels
 constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
 constexpr int kMaxClustersPerSeg = 4096;
-constexpr int kMaxGroupsPerDecode = 4096;  // B * Hkv of one decode call
-constexpr int kAttListLds = 96 * 1024;     // LDS the attention kernel may spend on a group's union
+constexpr int kMaxGroupsPerDecode = 65535;  // B * Hkv of one decode call (a grid dimension)
+constexpr int kCorrEntries = 64;    // retrieved clusters per correction workgroup
+constexpr int kAttTarget = 1024;    // attention workgroups one wave of the grid holds (4 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
-  int BG, BH, G, W32, Umax, est_tiles_g, att_split, att_items_g, list_mode;
-  size_t off_counters, off_keys, off_tile_norm, off_sel_bits, off_band_ids, off_band_key,
-      off_all_sel, off_hl_cid, off_hl_sz, off_hl_row, off_hl_n, off_wl_cid, off_wl_mask,
-      off_wl_row0, off_wl_pre, off_grp, off_est_md, off_est_num, off_att_md, off_att_num, total;
+  int BG, BH, G, W32, est_tiles_g, att_split, att_items;
+  size_t off_keys, off_tile_norm, off_sel_bits, off_band_ids, off_band_key, off_all_sel,
+      off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
+      off_att_md, off_att_num, total;
 };
 DecodeLayout decode_layout(const wi_decode_params& p);
 
@@ -47,28 +47,26 @@ struct DecodeArgs {
   float* lse;              // [BH] or null
   int32_t* sel_ids;        // [BH, top_k] or null
   // workspace
-  uint32_t* counters;      // [BG] arrivals of a group's heads in k_select
   uint32_t* keys;          // [BH, C] order key of the fp32 score <q, mu_c> (0: empty cluster)
   float* tile_norm;        // [BG, est_tiles_g] largest centroid norm of each 128-cluster tile
-  uint32_t* sel_bits;      // [BH, W32] retrieved-cluster bitmap
+  uint32_t* sel_bits;      // [BH, W32] retrieved-cluster bitmap (band bitmap beside it in LDS)
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
-  int32_t* hl_cid;         // [BH, top_k] list mode: the head's retrieved clusters, ascending
-  int32_t* hl_sz;          // [BH, top_k]            their sizes
-  int32_t* hl_row;         // [BH, top_k]            their first k_perm rows
-  int32_t* hl_n;           // [BH]                   list lengths
-  int32_t* wl_cid;         // [BG, Umax] table mode: the group's union, ascending cluster id
-  int32_t* wl_mask;        // [BG, Umax]             heads that retrieved each
-  int32_t* wl_row0;        // [BG, Umax]             first k_perm row
-  int32_t* wl_pre;         // [BG, Umax+1]           first token (steady zone first)
-  int32_t* grp;            // [BG, 2]                union length, token count
+  // the head's retrieval zone, ascending cluster id, padded to top_k (cid 0, row 0, key 0 and
+  // first token = n_tok past the list)
+  int32_t* hl_cid;         // [BH, top_k]
+  int32_t* hl_row;         // [BH, top_k]    first k_perm row
+  int32_t* hl_pre;         // [BH, top_k+1]  first token (steady zone first); [top_k] = n_tok
+  uint32_t* hl_key;        // [BH, top_k]    order key of the fp32 score
+  int32_t* att_bounds;     // [BH, S]        list entry holding the first retrieved token of
+                           //                token workgroup s
   float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
   float* est_num;          // [BG, est_tiles_g, G, d]
-  float* att_md;           // [BG, S + Sc, G, 2]
-  float* att_num;          // [BG, S + Sc, G, d]
+  float* att_md;           // [BH, S + Sc, 2]
+  float* att_num;          // [BH, S + Sc, d]
   // shapes
-  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, Umax, est_tiles_g, att_split, att_items_g, list_mode;
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, est_tiles_g, att_split, att_items;
   float scale;
 };
 
