@@ -135,7 +135,11 @@ wi_status wi_decode_workspace_bytes(const wi_decode_params *p, size_t *bytes);
  * The retrieval zone of a head is the min(top_k, #non-empty) non-empty clusters that come first
  * in the order (-sigma_c, c), sigma_c = <q, mu_c> with exact products summed in fp64 in ascending
  * coordinate order: higher score first, lower id on equal scores.  `workspace` must hold
- * wi_decode_workspace_bytes (256-byte aligned); calls that share a workspace must not overlap. */
+ * wi_decode_workspace_bytes (256-byte aligned); calls that share a workspace must not overlap.
+ * Errors: WI_ERR_INVALID_ARG for inconsistent parameters or null required pointers,
+ * WI_ERR_WORKSPACE for a short or misaligned workspace, WI_ERR_UNSUPPORTED for d != 128, a
+ * group size other than 1, 2, 4 or 8, more than 262144 clusters or 2^23 tokens per KV head, or
+ * B * Hkv above 65535. */
 wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const void *q,
                     float *out, float *lse, int32_t *sel_ids, void *workspace, size_t ws_bytes,
                     void *stream);

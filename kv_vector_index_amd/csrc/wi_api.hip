@@ -139,7 +139,9 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   size_t o = 0;
   L.off_keys = o;       o = align256(o + BH * C * 4);
   L.off_tile_norm = o;  o = align256(o + BG * L.est_tiles_g * 4);
-  L.off_sel_bits = o;   o = align256(o + BH * L.W32 * 4);
+  L.off_tile_cnt = o;   o = align256(o + BG * L.est_tiles_g * 4);
+  L.off_tile_top = o;   o = align256(o + BH * L.est_tiles_g * kTileTop * 4);
+  L.off_tile_top_id = o; o = align256(o + BH * L.est_tiles_g * kTileTop * 4);
   L.off_band_ids = o;   o = align256(o + BH * C * 4);
   L.off_band_key = o;   o = align256(o + BH * C * 8);
   L.off_all_sel = o;    o = align256(o + BH * 4);
@@ -230,8 +232,10 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
     return fail(WI_ERR_INVALID_ARG, "negative C, Nc, n_steady or top_k");
   if ((int64_t)p->n_steady + p->Nc < 1) return fail(WI_ERR_INVALID_ARG, "empty context");
   if ((p->C == 0) != (p->Nc == 0)) return fail(WI_ERR_INVALID_ARG, "C and Nc must be both zero or both positive");
-  if (p->Nc >= (1 << 23) || p->n_steady >= (1 << 23) || p->C >= (1 << 24))
-    return fail(WI_ERR_UNSUPPORTED, "more than 2^23 clustered or steady tokens, or 2^24 clusters, per KV head");
+  if (p->Nc >= (1 << 23) || p->n_steady >= (1 << 23))
+    return fail(WI_ERR_UNSUPPORTED, "more than 2^23 clustered or steady tokens per KV head");
+  if (p->C > wi::kMaxDecodeClusters)
+    return fail(WI_ERR_UNSUPPORTED, "more than %d clusters per KV head", wi::kMaxDecodeClusters);
   if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(WI_ERR_INVALID_ARG, "scale must be finite and > 0");
   const int64_t BG = (int64_t)p->B * p->Hkv;
   if (BG * ((int64_t)p->Nc + p->n_steady) >= kMaxRows || (int64_t)p->B * p->Hq * ((int64_t)p->C + 1) >= kMaxRows)
@@ -254,7 +258,9 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   char* base = static_cast<char*>(workspace);
   a.keys = reinterpret_cast<uint32_t*>(base + L.off_keys);
   a.tile_norm = reinterpret_cast<float*>(base + L.off_tile_norm);
-  a.sel_bits = reinterpret_cast<uint32_t*>(base + L.off_sel_bits);
+  a.tile_cnt = reinterpret_cast<int32_t*>(base + L.off_tile_cnt);
+  a.tile_top = reinterpret_cast<uint32_t*>(base + L.off_tile_top);
+  a.tile_top_id = reinterpret_cast<int32_t*>(base + L.off_tile_top_id);
   a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);

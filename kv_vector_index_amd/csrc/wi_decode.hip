@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
   __shared__ float sh_n[kEstTile];          // cluster sizes
+  __shared__ uint32_t sh_k[G][kEstTile];    // order keys of the raw scores, 0 for empty clusters
   __shared__ float sh_m[G], sh_den[G], sh_nm[4];
   __shared__ float sh_num[4][G][kD];
   const int tile = blockIdx.x, bg = blockIdx.y;
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
         if (h < G) {
           if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
           sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
+          sh_k[h][cl] = (c < C && sz[t] > 0) ? f32_order_key(acc[r]) : 0u;
         }
       }
       if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
@@ -187,6 +189,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
         if (h < G) {
           if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
           sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
+          sh_k[h][cl] = (c < C && sz[t] > 0) ? f32_order_key(acc[r]) : 0u;
         }
       }
       if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
@@ -208,6 +211,35 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     sh_w[h][lane + 64] = w1;
     const float dn = wave_sum(w0 * sh_n[lane] + w1 * sh_n[lane + 64]);
     if (lane == 0) { sh_m[h] = m; sh_den[h] = dn; }
+    // the head's 8 best scores of the tile (key 0 past the non-empty clusters) with their cluster
+    // ids: lane r keeps the r-th, found by repeated wave maxima, each time clearing the holder
+    // with the lowest id
+    uint32_t k0 = sh_k[h][lane], k1 = sh_k[h][lane + 64], best = 0u;
+    int best_id = 0;
+#pragma unroll
+    for (int r = 0; r < kTileTop; ++r) {
+      const uint32_t m8 = wave_umax(k0 > k1 ? k0 : k1);
+      const uint64_t b0 = __ballot(k0 == m8);
+      int holder;
+      if (b0 != 0ull) {
+        holder = __ffsll((unsigned long long)b0) - 1;
+        if (lane == holder) k0 = 0u;
+      } else {
+        const uint64_t b1 = __ballot(k1 == m8);
+        holder = __ffsll((unsigned long long)b1) - 1 + 64;
+        if (lane == holder - 64) k1 = 0u;
+      }
+      if (lane == r) { best = m8; best_id = tile * kEstTile + holder; }
+    }
+    if (lane < kTileTop) {
+      const size_t ti = (((size_t)b * a.Hq + (size_t)g * G + h) * a.est_tiles_g + tile) * kTileTop + lane;
+      a.tile_top[ti] = best;
+      a.tile_top_id[ti] = best_id;
+    }
+  }
+  if (w == 0) {
+    const int nc = __popcll(__ballot(sh_n[lane] > 0.f)) + __popcll(__ballot(sh_n[lane + 64] > 0.f));
+    if (lane == 0) a.tile_cnt[(size_t)bg * a.est_tiles_g + tile] = nc;
   }
   __syncthreads();
   float acc[G][8];
@@ -265,8 +297,13 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 }
 
 // ============================================================================ k_select
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSmallBand = 64;      // bands up to one wave are resolved by direct ranking
+constexpr int kSumCap = 4096;       // tile summaries (8 per 128-cluster tile) staged in LDS
+constexpr int kCandCap = 2048;      // candidate clusters ranked in LDS
+constexpr int kFullCap = 256;       // tiles scanned in full
+constexpr int kBins = 2048;         // histogram bins over [min, max] of the ranked scores
+constexpr int kPubPT = 8;           // retrieved clusters per thread in one publishing round
 
 // Radix bin of the k-th largest key: threads 0..255 own the bins in descending order, so an
 // inclusive scan over them gives suffix counts; the one bin with excl < rem <= incl is chosen.
@@ -310,6 +347,118 @@ __device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, int* scr,
   return prefix;
 }
 
+// k-th largest (1 <= k <= n) of n score order keys (all non-zero): a kBins histogram over
+// [min, max] of the scores gives the bin of the k-th largest, whose keys are then ranked by one
+// wave (a radix select over the keys covers a bin of more than 64).  `bl` holds >= 64 keys.
+// Histogram stage shared by the threshold searches below: over the non-zero ones of n score
+// order keys (0 marks an empty cluster and is skipped), kBins bins over [min, max] of their
+// scores; returns the bin holding the k-th largest (1 <= k <= #non-zero) and how many keys lie in
+// higher bins.
+struct KthBin { int bin, above; float mn, inv; };   // bin -1: fewer than k non-zero keys
+template <typename Get>
+__device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, float* fred, int* sh_i) {
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  float mx = -INFINITY, mn = INFINITY;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t key = get(i);
+    if (key == 0u) continue;
+    const float s = f32_from_order_key(key);
+    mx = fmaxf(mx, s);
+    mn = fminf(mn, s);
+  }
+  mx = wave_max(mx);
+  mn = -wave_max(-mn);
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+  if (lane == 0) { fred[2 * wv] = mx; fred[2 * wv + 1] = mn; }
+  __syncthreads();
+  for (int i = 0; i < NT / 64; ++i) { mx = fmaxf(mx, fred[2 * i]); mn = fminf(mn, fred[2 * i + 1]); }
+  KthBin r;
+  r.mn = mn;
+  r.inv = mx > mn ? (float)(kBins - 1) / (mx - mn) : 0.f;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t key = get(i);
+    if (key == 0u) continue;
+    const float s = f32_from_order_key(key);
+    atomicAdd(&hist[min(kBins - 1, max(0, (int)((s - r.mn) * r.inv)))], 1u);
+  }
+  __syncthreads();
+  // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
+  constexpr int BPT = (kBins + kSelThreads - 1) / kSelThreads;
+  int v = 0;
+  for (int j = 0; j < BPT; ++j) { const int bin = kBins - 1 - BPT * tid - j; if (bin >= 0) v += (int)hist[bin]; }
+  int tot;
+  int run = block_exclusive_scan(v, iscr, &tot);
+  if (run < k && k <= run + v) {
+    for (int j = 0; j < BPT; ++j) {
+      const int bin = kBins - 1 - BPT * tid - j;
+      const int hb = (int)hist[bin];
+      if (run + hb >= k) { sh_i[0] = bin; sh_i[1] = run; break; }
+      run += hb;
+    }
+  }
+  __syncthreads();
+  r.bin = tot >= k ? sh_i[0] : -1;
+  r.above = sh_i[1];
+  return r;
+}
+
+__device__ __forceinline__ int bin_of(const KthBin& kb, uint32_t key) {
+  return min(kBins - 1, max(0, (int)((f32_from_order_key(key) - kb.mn) * kb.inv)));
+}
+
+// k-th largest (1 <= k <= n) of n score order keys (all non-zero): the histogram bin of the
+// k-th largest, whose keys are then ranked by one wave (a radix select over the keys covers a bin
+// of more than 64).  `bl` holds >= 64 keys.
+template <typename Get>
+__device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint32_t* bl, int* iscr,
+                                    float* fred, int* sh_i) {
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  const KthBin kb = kth_bin(n, k, get, hist, iscr, fred, sh_i);
+  const int rem = k - kb.above;
+  const int nb = (int)hist[kb.bin];
+  if (nb <= 64) {
+    if (tid == 0) sh_i[4] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = get(i);
+      if (key != 0u && bin_of(kb, key) == kb.bin) bl[atomicAdd(&sh_i[4], 1)] = key;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const uint32_t key = lane < nb ? bl[lane] : 0u;
+      int gt = 0, ge = 0;
+      for (int j = 0; j < nb; ++j) { const uint32_t kj = bl[j]; gt += kj > key; ge += kj >= key; }
+      if (lane < nb && gt < rem && rem <= ge) sh_i[3] = (int)key;
+    }
+    __syncthreads();
+    return (uint32_t)sh_i[3];
+  }
+  int rr;
+  return block_radix_select<uint32_t>(n, k, get, hist, iscr, &rr);
+}
+
+// A lower bound of the k-th largest (1 <= k <= n) of n score order keys (some may be 0, which
+// rank last): the smallest non-zero key of the histogram bin that holds the k-th largest
+// non-zero key; 0 when fewer than k keys are non-zero.
+template <typename Get>
+__device__ uint32_t kth_lower_bound(int n, int k, Get get, uint32_t* hist, int* iscr, float* fred, int* sh_i) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const KthBin kb = kth_bin(n, k, get, hist, iscr, fred, sh_i);
+  if (kb.bin < 0) return 0u;
+  uint32_t lo = 0xffffffffu;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t x = get(i);
+    if (x != 0u && bin_of(kb, x) == kb.bin) lo = min(lo, x);
+  }
+  lo = ~wave_umax(~lo);
+  if ((threadIdx.x & 63) == 0) hist[threadIdx.x >> 6] = lo;
+  __syncthreads();
+  uint32_t r = 0xffffffffu;
+  for (int i = 0; i < NT / 64; ++i) r = min(r, hist[i]);
+  __syncthreads();
+  return r;
+}
+
 // Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
 // summed in ascending coordinate order, no contraction.  The row is fetched in four batches.
 template <typename T>
@@ -335,182 +484,185 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
   return acc;
 }
 
-
-constexpr int kSelKPT = 16;         // clusters per thread held in registers
-constexpr int kBins = 2048;         // histogram bins over [min score, max score]
-constexpr int kCandMax = 1024;      // candidates (keys of the threshold bin) ranked in LDS
-
 // Per query head: the retrieval zone is the k_eff = min(top_k, #non-empty) non-empty clusters
-// first in the order (-sigma_c, c).  1) the k_eff-th largest fp32 score t is found with a
-// 2048-bin histogram over [min, max] and a rank count inside the threshold bin (a radix select
-// over the order keys covers bins too full to rank); 2) clusters above t + 2 delta are in, those
-// below t - 2 delta are out (delta bounds |fp32 score - canonical fp64 score|); 3) the band in
-// between is re-scored canonically and ranked by (-sigma, id).  Thread t visits clusters
-// t, t + NT, t + 2 NT, ... so every global access is coalesced; id-ordered lists come from
-// bitmaps.  The last head of a KV group to finish builds the group's work: the union of the
-// heads' clusters in id order with a head mask, cut into one slice of the token -> row map per
-// exact-attention workgroup and one slice of the retrieved clusters per correction workgroup.
+// first in the order (-sigma_c, c).  With t the k_eff-th largest fp32 score and delta a bound on
+// |fp32 score - canonical fp64 score|, clusters above t + 2 delta are in, those below t - 2 delta
+// are out, and the band in between is re-scored canonically and ranked by (-sigma, id).
+//
+// One pass over the head's scores: the score kernel kept the 8 best scores of every 128-cluster
+// tile, and the k_eff-th largest of those is a lower bound L <= t; the pass collects every
+// cluster scoring >= L - 2 delta (t, the band and everything above it) into LDS, and t, the
+// in/band split and the band ranking then run on that short list.  If the list overflows (ties
+// or a head whose best clusters crowd a few tiles) t is found by a radix select over all scores
+// and the split by a second pass.  The head's list (ascending id: cluster, first row, first
+// token, score key) and the entry of every attention workgroup's first token are published last.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
+  __shared__ uint32_t skey[kSumCap];                 // tile summaries: score keys
+  __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
+                                                     // ascending retrieved list
+  __shared__ uint32_t ckey[kCandCap];                // candidates: score keys
+  __shared__ int cidl[kCandCap];                     // candidates: cluster ids
+  __shared__ int tfull[kFullCap];                    // tiles whose 8 best pass the threshold
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t cand[kCandMax];
   __shared__ int iscr[48];
-  __shared__ float fred[8][5];
+  __shared__ float fred[2 * kSelThreads / 64];
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
   __shared__ int sh_i[8];
   WI_TP(0);
 
-  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, NT = kSelThreads, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
-  const int G = a.G, g = h / G, bg = b * a.Hkv + g;
-  const int C = a.C, W32 = a.W32;
+  const int g = h / a.G, bg = b * a.Hkv + g;
+  const int C = a.C, W32 = a.W32, tiles = a.est_tiles_g;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
   const uint32_t* keys = a.keys + (size_t)bh * C;
   const T* qh = static_cast<const T*>(a.q) + (size_t)bh * kD;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
-  const int KPT = (C + NT - 1) / NT;          // thread t owns clusters j * NT + t, j < KPT
-  const bool cached = KPT <= kSelKPT;
+  const int KPT = (C + NT - 1) / NT;          // thread t visits clusters j * NT + t, j < KPT
 
+  // ---- set-up: query, largest centroid norm, non-empty count, tile summaries
   float qv = 0.f;
   if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
   float mxn = 0.f;
-  for (int i = tid; i < a.est_tiles_g; i += NT) mxn = fmaxf(mxn, a.tile_norm[(size_t)bg * a.est_tiles_g + i]);
+  int ne = 0;
+  for (int i = tid; i < tiles; i += NT) {
+    mxn = fmaxf(mxn, a.tile_norm[(size_t)bg * tiles + i]);
+    ne += a.tile_cnt[(size_t)bg * tiles + i];
+  }
+  const int nsum = tiles * kTileTop;
+  const bool use_sum = nsum <= kSumCap;
+  if (use_sum)
+    for (int i = tid; i < nsum; i += NT) {
+      skey[i] = a.tile_top[(size_t)bh * nsum + i];
+      sid[i] = a.tile_top_id[(size_t)bh * nsum + i];
+    }
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
+  {
+    float v0 = (float)ne, v1 = mxn, v2 = qv * qv;
+    v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_sum(v2);
+    if (lane == 0) { fred[wv] = v0; fred[16 + wv] = v1; hist[wv] = __float_as_uint(v2); }
+    __syncthreads();
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f;
+    for (int i = 0; i < NT / 64; ++i) { r0 += fred[i]; r1 = fmaxf(r1, fred[16 + i]); r2 += __uint_as_float(hist[i]); }
+    ne = (int)r0; mxn = r1; qv = sqrtf(r2);
+    __syncthreads();
+  }
+  WI_TP(3);
+  const int n_ne = ne;
+  const int k_eff = min(a.top_k, n_ne);
 
-  uint32_t kc[kSelKPT];
-  // fn(c, key) for every cluster of this thread, keys from registers or re-read in batches
-  auto visit = [&](auto&& fn) {
-    for (int j0 = 0; j0 < KPT; j0 += kSelKPT) {
-      uint32_t k[kSelKPT];
-      if (cached) {
+  auto visit_keys = [&](auto&& fn) {           // fn(c, key) for every cluster of this thread
+    for (int j0 = 0; j0 < KPT; j0 += 16) {
+      uint32_t k[16];
 #pragma unroll
-        for (int i = 0; i < kSelKPT; ++i) k[i] = kc[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < kSelKPT; ++i) {
-          const int c = (j0 + i) * NT + tid;
-          k[i] = c < C ? keys[c] : 0u;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int c = (j0 + i) * NT + tid;
+        k[i] = c < C ? keys[c] : 0u;
       }
 #pragma unroll
-      for (int i = 0; i < kSelKPT; ++i) {
+      for (int i = 0; i < 16; ++i) {
         const int c = (j0 + i) * NT + tid;
         if (c < C) fn(c, k[i]);
       }
     }
   };
 
-  // ---- pass 1: non-empty count and score range (and the key cache)
-  int cnt = 0;
-  float smax = -INFINITY, smin = INFINITY;
-  for (int j0 = 0; j0 < KPT; j0 += kSelKPT) {
-    uint32_t k[kSelKPT];
-#pragma unroll
-    for (int i = 0; i < kSelKPT; ++i) {
-      const int c = (j0 + i) * NT + tid;
-      k[i] = c < C ? keys[c] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kSelKPT; ++i) {
-      if (k[i] != 0u) {
-        ++cnt;
-        const float s = f32_from_order_key(k[i]);
-        smax = fmaxf(smax, s);
-        smin = fminf(smin, s);
-      }
-      if (cached) kc[i] = k[i];
-    }
-  }
-  {
-    float v0 = (float)cnt, v1 = smax, v2 = -smin, v3 = mxn, v4 = qv * qv;
-    v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_max(v2); v3 = wave_max(v3); v4 = wave_sum(v4);
-    if (lane == 0) { fred[wv][0] = v0; fred[wv][1] = v1; fred[wv][2] = v2; fred[wv][3] = v3; fred[wv][4] = v4; }
-    __syncthreads();
-    float r0 = 0.f, r1 = -INFINITY, r2 = -INFINITY, r3 = 0.f, r4 = 0.f;
-    for (int i = 0; i < NT / 64; ++i) {
-      r0 += fred[i][0]; r1 = fmaxf(r1, fred[i][1]); r2 = fmaxf(r2, fred[i][2]);
-      r3 = fmaxf(r3, fred[i][3]); r4 += fred[i][4];
-    }
-    cnt = (int)r0; smax = r1; smin = -r2; mxn = r3; qv = sqrtf(r4);
-  }
-  WI_TP(3);
-  const int n_ne = cnt;
-  const float qn = qv;
-  const int k_eff = min(a.top_k, n_ne);
-
   if (k_eff > 0 && k_eff == n_ne) {
-    visit([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
+    visit_keys([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
-    // ---- pass 2: histogram over [smin, smax] (monotone binning: higher bins, higher scores)
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
-    __syncthreads();
-    const float span = smax - smin;
-    const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
-    auto bin_of = [&](uint32_t key) -> int {
-      const float s = f32_from_order_key(key);
-      return min(kBins - 1, max(0, (int)((s - smin) * inv)));
-    };
-    visit([&](int c, uint32_t k) { if (k != 0u) atomicAdd(&hist[bin_of(k)], 1u); });
+    // delta bounds |fp32 score - canonical fp64 score| for every cluster: fp32 accumulation of d
+    // exact-or-rounded products, doubled for an unspecified MFMA summation order
+    const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qv * (1.0 + 1.0 / 1024) *
+                             (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
+    // ---- lower bound L of the k_eff-th largest score from the tile summaries
+    float thr_f = -INFINITY;
+    if (use_sum) {
+      const uint32_t L = kth_lower_bound(nsum, k_eff, [&](int i) { return skey[i]; }, hist, iscr, fred, sh_i);
+      if (L != 0u) {
+        const double thr_d = (double)f32_from_order_key(L) - 2.0 * delta;
+        thr_f = (float)thr_d;
+        if ((double)thr_f > thr_d) thr_f = nextafterf(thr_f, -INFINITY);
+      }
+    }
+    if (tid == 0) { sh_i[2] = 0; sh_i[5] = 0; }
     __syncthreads();
     WI_TP(4);
-    {
-      // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
-      constexpr int BPT = kBins / kSelThreads;
-      int v = 0;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) v += (int)hist[kBins - 1 - BPT * tid - j];
-      int tot;
-      int run = block_exclusive_scan(v, iscr, &tot);
-      if (run < k_eff && k_eff <= run + v) {
-        for (int j = 0; j < BPT; ++j) {
-          const int bin = kBins - 1 - BPT * tid - j;
-          const int hb = (int)hist[bin];
-          if (run + hb >= k_eff) { sh_i[0] = bin; sh_i[1] = run; break; }
-          run += hb;
+    // ---- candidates: the non-empty clusters scoring >= L - 2 delta (appends wave-aggregated)
+    auto append = [&](bool take, uint32_t key, int id) {
+      const uint64_t m = __ballot(take);
+      if (m == 0ull) return;
+      const int leader = __ffsll((unsigned long long)m) - 1;
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&sh_i[2], __popcll(m));
+      base = __builtin_amdgcn_readlane(base, leader);
+      if (take) {
+        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (pos < kCandCap) { ckey[pos] = key; cidl[pos] = id; }
+      }
+    };
+    auto passes = [&](uint32_t k) { return k != 0u && f32_from_order_key(k) >= thr_f; };
+    bool scan_all = !use_sum;
+    if (use_sum) {
+      // a tile whose 8th best score is below the threshold has all its candidates among its 8
+      // best; the others are scanned in full
+      for (int i = tid; i < nsum; i += NT) {
+        const int t = i / kTileTop;
+        const bool full = passes(skey[t * kTileTop + kTileTop - 1]);
+        append(!full && passes(skey[i]), skey[i], sid[i]);
+        if (full && i == t * kTileTop) {
+          const int q = atomicAdd(&sh_i[5], 1);
+          if (q < kFullCap) tfull[q] = t;
         }
       }
-      if (tid == 0) sh_i[2] = 0;
       __syncthreads();
-    }
-    const int bstar = sh_i[0];
-    const int rem = k_eff - sh_i[1];
-    const int ncand = (int)hist[bstar];
-    uint32_t thr;
-    if (ncand <= kCandMax) {
-      visit([&](int c, uint32_t k) { if (k != 0u && bin_of(k) == bstar) cand[atomicAdd(&sh_i[2], 1)] = k; });
-      __syncthreads();
-      // the rem-th largest candidate: gt < rem <= ge
-      for (int i = tid; i < ncand; i += NT) {
-        const uint32_t ki = cand[i];
-        int gt = 0, ge = 0;
-        for (int j = 0; j < ncand; ++j) { const uint32_t kj = cand[j]; gt += kj > ki; ge += kj >= ki; }
-        if (gt < rem && rem <= ge) sh_i[3] = (int)ki;
+      const int n_full = sh_i[5];
+      if (n_full > kFullCap) {
+        scan_all = true;
+        __syncthreads();
+        if (tid == 0) sh_i[2] = 0;
+        __syncthreads();
+      } else {
+        for (int j = wv; j < n_full; j += NT / 64) {
+          const int t = tfull[j];
+          for (int r = lane; r < kEstTile; r += 64) {
+            const int c = t * kEstTile + r;
+            const uint32_t key = c < C ? keys[c] : 0u;
+            append(passes(key), key, c);
+          }
+        }
       }
-      __syncthreads();
-      thr = (uint32_t)sh_i[3];
+    }
+    if (scan_all) visit_keys([&](int c, uint32_t k) { append(passes(k), k, c); });
+    __syncthreads();
+    const int n_c = sh_i[2];
+    const bool listed = n_c <= kCandCap;
+    WI_TP(5);
+    // ---- t = k_eff-th largest score: from the candidates, else over all scores
+    uint32_t thr;
+    if (listed) {
+      thr = kth_largest_key(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
     } else {
       int rr;
       thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
     }
     WI_TP(6);
-    // ---- pass 3: in / band / out.  delta bounds |fp32 score - canonical fp64 score| for every
-    // cluster: fp32 accumulation of d exact-or-rounded products, doubled for an unspecified
-    // MFMA summation order.
+    // ---- in / band / out
     const double that = (double)f32_from_order_key(thr);
-    const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qn * (1.0 + 1.0 / 1024) *
-                             (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
     int nin = 0;
-    visit([&](int c, uint32_t k) {
+    auto classify = [&](int c, uint32_t k) {
       if (k == 0u) return;
       const double v = (double)f32_from_order_key(k);
       if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
       else if (v >= lo) atomicOr(&bbits[c >> 5], 1u << (c & 31));
-    });
+    };
+    if (listed) for (int i = tid; i < n_c; i += NT) classify(cidl[i], ckey[i]);
+    else visit_keys(classify);
     const int n_in = block_isum(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
     // band list in ascending id order from the band bitmap
@@ -537,7 +689,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
         const uint64_t key = live ? f64_order_key(canonical_score_row<T>(qd, mu + (size_t)c * kD)) : 0ull;
         int rank = 0;
         for (int j = 0; j < n_band; ++j) {
-          const uint64_t kj = __shfl(key, j);
+          const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, j);
           rank += (kj > key) || (kj == key && j < lane);
         }
         if (live && rank < need) atomicOr(&bits[c >> 5], 1u << (c & 31));
@@ -571,44 +724,84 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   // token after the steady zone, score key), padded to top_k; then, for every token workgroup
   // of the attention kernel, the list entry that holds its first retrieved token
   {
+    const int K = a.top_k, S = a.att_split;
+    // ascending retrieved ids (LDS when they fit)
+    int32_t* rl = K <= kSumCap ? sid : a.band_ids + (size_t)bh * C;
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-    const int32_t* sizes = a.sizes + (size_t)bg * C;
-    const int32_t* off = a.offsets + (size_t)bg * (C + 1);
-    int n = 0, nt = 0;
+    int n = 0;
+    for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
+    int tot;
+    int p = block_exclusive_scan(n, iscr, &tot);
     for (int w = w0; w < w1; ++w) {
       uint32_t m = bits[w];
-      n += __popc(m);
-      while (m) { const int c = w * 32 + __ffs(m) - 1; m &= m - 1; nt += sizes[c]; }
+      while (m) { const int c = w * 32 + __ffs(m) - 1; m &= m - 1; rl[p++] = c; }
     }
-    int tot, ttot;
-    int p = block_exclusive_scan(n, iscr, &tot);
-    int t = a.NS + block_exclusive_scan(nt, iscr, &ttot);
-    const int K = a.top_k, S = a.att_split;
-    const int64_t ntok = (int64_t)a.NS + ttot;
+    tot = min(tot, K);
+    __syncthreads();
+    WI_TP(10);
+    const int32_t* off = a.offsets + (size_t)bg * (C + 1);
     int32_t* out = a.sel_ids ? a.sel_ids + (size_t)bh * K : nullptr;
     const size_t lb = (size_t)bh * K, pb = (size_t)bh * (K + 1);
     int32_t* bounds = a.att_bounds + (size_t)bh * S;
-    for (int w = w0; w < w1; ++w) {
-      uint32_t m = bits[w];
-      while (m) {
-        const int c = w * 32 + __ffs(m) - 1;
-        m &= m - 1;
-        const int sz = sizes[c];
-        if (p < K) {
-          if (out) out[p] = c;
-          a.hl_cid[lb + p] = c;
-          a.hl_row[lb + p] = off[c];
-          a.hl_pre[pb + p] = t;
-          a.hl_key[lb + p] = keys[c];
-          // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); its first
-          // retrieved token max(that start, NS) lies in [t, t + sz) for s in [s_a, s_b]
-          const int64_t s_a = p == 0 ? 0 : ((int64_t)t * S + ntok - 1) / ntok;
-          const int64_t s_b = min((int64_t)S - 1, ((int64_t)(t + sz) * S + ntok - 1) / ntok - 1);
-          for (int64_t x = s_a; x <= s_b; ++x) bounds[x] = p;
+    // token total first when the list takes several rounds
+    int64_t ntok = a.NS;
+    const int chunk = NT * kPubPT;
+    if (tot > chunk) {
+      int sum = 0;
+      for (int i = tid; i < tot; i += NT) { const int c = rl[i]; sum += off[c + 1] - off[c]; }
+      ntok += block_isum(sum, iscr);
+    }
+    int t_run = a.NS;
+    for (int base = 0; base < tot; base += chunk) {
+      const int i0 = base + tid * kPubPT;
+      int c_[kPubPT], r_[kPubPT], z_[kPubPT];
+      uint32_t k_[kPubPT];
+      int ssum = 0;
+#pragma unroll
+      for (int u = 0; u < kPubPT; ++u) {
+        const int i = i0 + u;
+        c_[u] = 0; r_[u] = 0; z_[u] = 0; k_[u] = 0u;
+        if (i < tot) {
+          c_[u] = rl[i];
+          r_[u] = off[c_[u]];
+          z_[u] = off[c_[u] + 1] - r_[u];
+          k_[u] = keys[c_[u]];
+          ssum += z_[u];
         }
-        ++p;
-        t += sz;
+      }
+      int csum;
+      int t = t_run + block_exclusive_scan(ssum, iscr, &csum);
+      WI_TP(11);
+      if (tot <= chunk) ntok = (int64_t)a.NS + csum;
+#pragma unroll
+      for (int u = 0; u < kPubPT; ++u) {
+        const int i = i0 + u;
+        if (i < tot) {
+          if (out) out[i] = c_[u];
+          a.hl_cid[lb + i] = c_[u];
+          a.hl_row[lb + i] = r_[u];
+          a.hl_pre[pb + i] = t;
+          a.hl_key[lb + i] = k_[u];
+          if (tot <= kSumCap) skey[i] = (uint32_t)t;
+          t += z_[u];
+        }
+      }
+      t_run += csum;
+    }
+    // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); the entry holding its
+    // first retrieved token max(that start, NS): the last entry whose first token is <= it
+    __syncthreads();
+    if (tot > 0) {
+      for (int x = tid; x < S; x += NT) {
+        const int u = max((int)(((int64_t)x * ntok) / S), a.NS);
+        int lo = 0, hi = tot;                      // first token of entry lo <= u < that of hi
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          const int pm = tot <= kSumCap ? (int)skey[mid] : a.hl_pre[pb + mid];
+          if (pm <= u) lo = mid; else hi = mid;
+        }
+        bounds[x] = lo;
       }
     }
     for (int i = tot + tid; i < K; i += NT) {
@@ -751,30 +944,6 @@ __device__ void write_partial(OState<G>& st, size_t slot, float* md_out, float* 
   }
 }
 
-// q . k for 8 dims held by this lane, completed across the 16 lanes of the row
-template <typename T>
-__device__ __forceinline__ float row_dot(const Piece<T>& qp, const Piece<T>& kp) {
-  float s = 0.f;
-  if constexpr (sizeof(T) == 2) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const uint32_t qa[4] = {qp.v.x, qp.v.y, qp.v.z, qp.v.w};
-    const uint32_t ka[4] = {kp.v.x, kp.v.y, kp.v.z, kp.v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qa[j]), __builtin_bit_cast(bf16x2_t, ka[j]), s, false);
-  } else {
-    float qf[8], kf[8];
-    qp.unpack(qf);
-    kp.unpack(kf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += qf[e] * kf[e];
-  }
-  s += __shfl_xor(s, 8);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 1);
-  return s;
-}
 
 // Max over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), in every lane of the row.
 __device__ __forceinline__ float row16_max(float v) {
@@ -1129,10 +1298,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+    // the select kernel's two cluster bitmaps (2 * ceil(C / 32) words) live in dynamic LDS
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);

@@ -91,31 +91,61 @@ __device__ __noinline__ double canonical_dot(const T* __restrict__ x, const T* _
 }
 
 // ------------------------------------------------------------------ wave / block reductions
+// Lane exchanges inside a DPP row of 16 lanes (VALU operand modifiers, no LDS traffic):
+// quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_shr:n = 0x110 + n (lanes shifted in from outside the row read 0).
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, true); }
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) { return __int_as_float(dpp_i<kCtrl>(__float_as_int(v))); }
+__device__ __forceinline__ float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+// All-lane reductions: a butterfly inside each row, then the four row results combined in a
+// fixed order ((row 0, row 1), (row 2, row 3)).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ int wave_isum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  v += dpp_i<0x140>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  int x = (int)v;
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<0xB1>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x4E>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x141>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x140>(x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
 }
 
-// Inclusive prefix sum within a wave.
+// Inclusive prefix sum within a wave: Hillis-Steele inside each row (shifts 1, 2, 4, 8), then
+// the totals of the lower rows added.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += dpp_i<0x111>(v);
+  v += dpp_i<0x112>(v);
+  v += dpp_i<0x114>(v);
+  v += dpp_i<0x118>(v);
+  const int s1 = __builtin_amdgcn_readlane(v, 15);
+  const int s2 = __builtin_amdgcn_readlane(v, 31);
+  const int s3 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? s1 : 0) + (row >= 2 ? s2 : 0) + (row >= 3 ? s3 : 0);
 }
 
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).  `scratch` holds

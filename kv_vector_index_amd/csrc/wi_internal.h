@@ -13,11 +13,14 @@
 namespace wi {
 
 constexpr int kEstTile = 128;       // clusters per estimation work item
+constexpr int kTileTop = 8;         // best scores per head the score kernel keeps of each tile
 constexpr int kMaxGroup = 8;        // query heads per KV head supported by the decode kernels
 constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
 constexpr int kMaxClustersPerSeg = 4096;
 constexpr int kMaxGroupsPerDecode = 65535;  // B * Hkv of one decode call (a grid dimension)
 constexpr int kCorrEntries = 64;    // retrieved clusters per correction workgroup
+constexpr int kSelectBitmapLds = 65536;   // dynamic LDS of the select kernel: 2 bitmaps over C
+constexpr int kMaxDecodeClusters = kSelectBitmapLds / 8 * 32;   // C per KV head (262144)
 constexpr int kAttTarget = 1024;    // attention workgroups one wave of the grid holds (4 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -26,7 +29,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
   int BG, BH, G, W32, est_tiles_g, att_split, att_items;
-  size_t off_keys, off_tile_norm, off_sel_bits, off_band_ids, off_band_key, off_all_sel,
+  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel,
       off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
 };
@@ -49,7 +52,9 @@ struct DecodeArgs {
   // workspace
   uint32_t* keys;          // [BH, C] order key of the fp32 score <q, mu_c> (0: empty cluster)
   float* tile_norm;        // [BG, est_tiles_g] largest centroid norm of each 128-cluster tile
-  uint32_t* sel_bits;      // [BH, W32] retrieved-cluster bitmap (band bitmap beside it in LDS)
+  int32_t* tile_cnt;       // [BG, est_tiles_g] non-empty clusters of each tile
+  uint32_t* tile_top;      // [BH, est_tiles_g, kTileTop] best score keys of each tile, descending
+  int32_t* tile_top_id;    // [BH, est_tiles_g, kTileTop] their cluster ids
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
