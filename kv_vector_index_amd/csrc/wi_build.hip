@@ -19,6 +19,8 @@
 //     k_csr     per segment: counts, offsets and a stable counting scatter -> sizes/offsets/perm
 //     k_update  (all but the last iteration) fp64 member sums -> new unit directions
 //     k_final   (last iteration) mean keys, value sums, cluster-major K/V copies
+#include <type_traits>
+
 #include "wi_device.h"
 #include "wi_internal.h"
 
@@ -170,36 +172,51 @@ __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
 }
 
 // ============================================================================ k_assign
-constexpr int kAssignKeys = 256;    // keys per block: 4 waves x 4 tiles of 16
+constexpr int kAssignWaves = 8;
+constexpr int kAssignThreads = 64 * kAssignWaves;
+constexpr int kAssignKeys = 64 * kAssignWaves;     // keys per block: 4 tiles of 16 per wave
 
 template <typename T> struct AssignCfg;
 template <> struct AssignCfg<uint16_t> { static constexpr int kChunk = 512; static constexpr int kStride = 272; };
 template <> struct AssignCfg<float> { static constexpr int kChunk = 256; static constexpr int kStride = 528; };
 
-struct Top2 {
+// Running top-2 of one key's fp32 scores and the 4-centroid group that holds the best one.
+struct Best2 {
   float b1, b2;
-  int i1;
+  int grp;
 };
 
-__device__ __forceinline__ void top2_push(Top2& t, float v, int id) {
-  if (v > t.b1) { t.b2 = t.b1; t.b1 = v; t.i1 = id; }
-  else if (v > t.b2) { t.b2 = v; }
+// Fold the scores of centroids 4 grp .. 4 grp + 3: the exact two largest values so far, and the
+// group of the largest (an equal later group does not replace it: lower ids win ties).
+__device__ __forceinline__ void best2_fold4(Best2& t, float a0, float a1, float a2, float a3, int grp) {
+  const float m = fmaxf(fmaxf(a0, a1), a2);                 // largest of a0..a2
+  const float md = __builtin_amdgcn_fmed3f(a0, a1, a2);     // second largest of a0..a2
+  const float g1 = fmaxf(m, a3);
+  const float g2 = fmaxf(md, fminf(m, a3));
+  const bool nw = g1 > t.b1;
+  t.b2 = fmaxf(fmaxf(fminf(t.b1, g1), t.b2), g2);
+  t.b1 = fmaxf(t.b1, g1);
+  t.grp = nw ? grp : t.grp;
 }
 
-__device__ __forceinline__ void top2_merge_xor(Top2& t, int m) {
+// Merge the state of lane (lane ^ m): the union's two largest values, the lower group on ties.
+__device__ __forceinline__ void best2_merge_xor(Best2& t, int m) {
   const float o1 = __shfl_xor(t.b1, m), o2 = __shfl_xor(t.b2, m);
-  const int oi = __shfl_xor(t.i1, m);
-  if (o1 > t.b1 || (o1 == t.b1 && oi < t.i1)) {
-    t.b2 = fmaxf(o2, t.b1);
-    t.b1 = o1;
-    t.i1 = oi;
-  } else {
-    t.b2 = fmaxf(t.b2, o1);
-  }
+  const int og = __shfl_xor(t.grp, m);
+  const bool take = o1 > t.b1 || (o1 == t.b1 && og < t.grp);
+  t.b2 = fmaxf(fmaxf(fminf(t.b1, o1), t.b2), o2);
+  if (take) { t.b1 = o1; t.grp = og; }
 }
 
+// Keys are the MFMA B operand (column = key), held in registers; the segment's centroid
+// directions are staged in LDS in chunks and fed as the A operand (row = centroid).  Lane (lr,
+// lg) of an output tile holds centroids 4 lg .. 4 lg + 3 of the 16-centroid tile for key lr; each
+// lane folds them into a running top-2 (values exact, best group only).  At the end the four
+// scores of the winning group are recomputed, which names the best centroid; the choice is
+// certified when it leads the second best by more than twice the fp32 error bound, otherwise the
+// key goes to the fp64 re-decision list.
 template <typename T>
-__global__ __launch_bounds__(256) void k_assign(BuildArgs a, int it) {
+__global__ __launch_bounds__(kAssignThreads) void k_assign(BuildArgs a, int it) {
   extern __shared__ __attribute__((aligned(16))) unsigned char clds[];
   constexpr int CH = AssignCfg<T>::kChunk, STR = AssignCfg<T>::kStride;
   const int s = blockIdx.y, bg = blockIdx.z;
@@ -211,57 +228,24 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, int it) {
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
   const T* mh = static_cast<const T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
 
-  Top2 tk[4];
+  Best2 tk[4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) { tk[kt].b1 = -INFINITY; tk[kt].b2 = -INFINITY; tk[kt].i1 = 0; }
+  for (int kt = 0; kt < 4; ++kt) { tk[kt].b1 = -INFINITY; tk[kt].b2 = -INFINITY; tk[kt].grp = 0; }
 
-  if constexpr (sizeof(T) == 2) {
-    // B operand = keys: key (lane & 15) of tile kt, dims 32*lg + 8*st .. +8 at MFMA step st
-    bf16x8_t kb[4][4];
+  // key (lane & 15) of tile kt; lane group lg holds dims 32 lg .. 32 lg + 31
+  constexpr int KE = sizeof(T) == 2 ? 4 : 32;      // bf16: 4 x 8 elements; fp32: 32 elements
+  typedef typename std::conditional<sizeof(T) == 2, bf16x8_t, float>::type KElem;
+  KElem kb[4][KE];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int i = key0 + w * 64 + kt * 16 + lr;
+  for (int kt = 0; kt < 4; ++kt) {
+    const int i = key0 + w * 64 + kt * 16 + lr;
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         if (i < n_s) kb[kt][st] = *reinterpret_cast<const bf16x8_t*>(K + (size_t)i * kD + 32 * lg + 8 * st);
         else kb[kt][st] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
-    }
-    for (int c0 = 0; c0 < cs_eff; c0 += CH) {
-      const int ch = min(CH, cs_eff - c0);
-      const int ch16 = (ch + 15) & ~15;
-      __syncthreads();
-      // stage centroid rows [c0, c0 + ch16) into LDS (rows past cs_eff are zero)
-      for (int idx = threadIdx.x; idx < ch16 * 16; idx += blockDim.x) {
-        const int r = idx >> 4, q = idx & 15;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (r < ch) val = *reinterpret_cast<const u32x4_t*>(mh + (size_t)(c0 + r) * kD + q * 8);
-        *reinterpret_cast<u32x4_t*>(clds + r * STR + q * 16) = val;
-      }
-      __syncthreads();
-      for (int ct = 0; ct < ch16 / 16; ++ct) {
-        bf16x8_t ca[4];
-        const unsigned char* rp = clds + (ct * 16 + lr) * STR + 64 * lg;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) ca[st] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * st);
-        const int cidb = c0 + ct * 16 + 4 * lg;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[st], kb[kt][st], acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (cidb + r < cs_eff) top2_push(tk[kt], acc[r], cidb + r);
-        }
-      }
-    }
-  } else {
-    // fp32: 16x16x4 MFMA; step st (0..31) consumes dim 32*lg + st on both operands
-    float kb[4][32];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int i = key0 + w * 64 + kt * 16 + lr;
+    } else {
 #pragma unroll
       for (int st = 0; st < 32; st += 8) {
         float tmp[8];
@@ -271,21 +255,39 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, int it) {
         for (int e = 0; e < 8; ++e) kb[kt][st + e] = tmp[e];
       }
     }
-    for (int c0 = 0; c0 < cs_eff; c0 += CH) {
-      const int ch = min(CH, cs_eff - c0);
-      const int ch16 = (ch + 15) & ~15;
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < ch16 * 32; idx += blockDim.x) {
-        const int r = idx >> 5, q = idx & 31;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (r < ch) val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(mh) + (size_t)(c0 + r) * kD + q * 4);
-        *reinterpret_cast<u32x4_t*>(clds + r * STR + q * 16) = val;
-      }
-      __syncthreads();
-      for (int ct = 0; ct < ch16 / 16; ++ct) {
+  }
+
+  for (int c0 = 0; c0 < cs_eff; c0 += CH) {
+    const int ch = min(CH, cs_eff - c0);
+    const int ch16 = (ch + 15) & ~15;
+    __syncthreads();
+    // stage centroid rows [c0, c0 + ch16) into LDS (rows past cs_eff are zero)
+    constexpr int Q = kD * (int)sizeof(T) / 16;      // 16-byte pieces per row
+    for (int idx = threadIdx.x; idx < ch16 * Q; idx += kAssignThreads) {
+      const int r = idx / Q, q = idx - r * Q;
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (r < ch) val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(mh + (size_t)(c0 + r) * kD) + q * 16);
+      *reinterpret_cast<u32x4_t*>(clds + r * STR + q * 16) = val;
+    }
+    __syncthreads();
+    const int nct = ch16 / 16;
+    for (int ct = 0; ct < nct; ++ct) {
+      const int grp = (c0 + ct * 16) / 4 + lg;
+      const bool ragged = c0 + ct * 16 + 16 > cs_eff;
+      f32x4_t acc[4];
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_t ca[4];
+        const unsigned char* rp = clds + (ct * 16 + lr) * STR + 64 * lg;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) ca[st] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * st);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[st], kb[kt][st], acc[kt], 0, 0, 0);
+        }
+      } else {
         const float* rp = reinterpret_cast<const float*>(clds + (ct * 16 + lr) * STR) + 32 * lg;
-        const int cidb = c0 + ct * 16 + 4 * lg;
-        f32x4_t acc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -298,31 +300,73 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, int it) {
             for (int kt = 0; kt < 4; ++kt)
               acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[e], kb[kt][st + e], acc[kt], 0, 0, 0);
         }
+      }
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt) {
+        float v[4] = {acc[kt][0], acc[kt][1], acc[kt][2], acc[kt][3]};
+        if (ragged) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (cidb + r < cs_eff) top2_push(tk[kt], acc[kt][r], cidb + r);
+          for (int r = 0; r < 4; ++r) if (4 * grp + r >= cs_eff) v[r] = -INFINITY;
+        }
+        best2_fold4(tk[kt], v[0], v[1], v[2], v[3], grp);
       }
     }
   }
 
   // combine the four lane groups holding disjoint centroid subsets of the same key
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) { top2_merge_xor(tk[kt], 16); top2_merge_xor(tk[kt], 32); }
+  for (int kt = 0; kt < 4; ++kt) { best2_merge_xor(tk[kt], 16); best2_merge_xor(tk[kt], 32); }
 
-  // certify: the fp32 winner is the exact winner if its lead exceeds twice the error bound
+  // the winning group's four scores, recomputed on the vector units (each lane its 32 dims, then
+  // summed over the four lane groups), name the best centroid; certify it against the best of
+  // the rest: the group's other three and the exact second-best fp32 score overall
+  const bool resident = cs_eff <= CH;             // the last staged chunk holds every centroid
   int flagged[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
+    const int grp = tk[kt].grp;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = min(4 * grp + r, cs_eff - 1);
+      float acc = 0.f;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          u32x4_t cv;
+          if (resident) cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * lg + 16 * st);
+          else cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * lg + 8 * st);
+          const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc += __uint_as_float(cw[e] << 16) * (float)kb[kt][st][2 * e];
+            acc += __uint_as_float(cw[e] & 0xffff0000u) * (float)kb[kt][st][2 * e + 1];
+          }
+        }
+      } else {
+        const float* cr = resident ? reinterpret_cast<const float*>(clds + c * STR) + 32 * lg
+                                   : reinterpret_cast<const float*>(mh) + (size_t)c * kD + 32 * lg;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) acc += cr[e] * kb[kt][e];
+      }
+      acc += __shfl_xor(acc, 16);
+      acc += __shfl_xor(acc, 32);
+      p[r] = 4 * grp + r < cs_eff ? acc : -INFINITY;
+    }
+    int rb = 0;
+#pragma unroll
+    for (int r = 1; r < 4; ++r) if (p[r] > p[rb]) rb = r;
+    float b2 = tk[kt].b2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) if (r != rb) b2 = fmaxf(b2, p[r]);
     const int i = key0 + w * 64 + kt * 16 + lr;
     flagged[kt] = 0;
     if (lg == 0 && i < n_s) {
       const size_t gi = (size_t)bg * a.Nc + (size_t)s * a.L + i;
       const double kn = (double)a.knorm[gi] * (1.0 + 1.0 / 1024);
       const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * kn * 1.01 + 1e-30;
-      a.assign[gi] = tk[kt].i1;
-      flagged[kt] = !((double)tk[kt].b1 - (double)tk[kt].b2 > 2.0 * delta);
+      a.assign[gi] = 4 * grp + rb;
+      flagged[kt] = !((double)p[rb] - (double)b2 > 2.0 * delta);
     }
   }
 #pragma unroll
@@ -331,7 +375,7 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, int it) {
     if (m == 0) continue;
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&a.flag_cnt[it], (uint32_t)__popcll(m));
-    base = __shfl(base, 0);
+    base = __builtin_amdgcn_readlane(base, 0);
     if (flagged[kt]) {
       const uint32_t pos = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
       const int i = key0 + w * 64 + kt * 16 + lr;
@@ -561,7 +605,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs;
   for (int it = 0; it < a.iters; ++it) {
     prof_begin(WI_STAGE_ASSIGN, st);
-    hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, kAssignKeys), a.nseg, BG), dim3(256),
+    hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, kAssignKeys), a.nseg, BG), dim3(kAssignThreads),
                        alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
