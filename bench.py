@@ -135,6 +135,51 @@ def _cpu_model():
     return "unknown"
 
 
+def bench_build(w, args, dev):
+    """Index build only: K warm-up builds, then `steps` timed builds with per-kernel events."""
+    import torch
+
+    from kv_vector_index_amd import synth
+    from kv_vector_index_amd import wave_index as wi
+
+    log(f"[bench] workload {w.name}: generating inputs on the device")
+    Kt, Vt, _ = synth.make_instance_device(w, args.seed, dev)
+    steps = max(1, min(args.steps, 20))
+    for _ in range(max(1, min(args.warmup, 3))):
+        idx = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        idx = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    t1.record()
+    torch.cuda.synchronize()
+    build_ms = t0.elapsed_time(t1) / steps
+    wi.wi_profile_enable(True)
+    for _ in range(steps):
+        idx = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    torch.cuda.synchronize()
+    stages = wi.wi_profile_read()
+    wi.wi_profile_enable(False)
+    n_keys = w.B * w.Hkv * idx.Nc
+    assign_flops = 2.0 * n_keys * w.clusters_per_seg * w.d * w.iters
+    assign_ms = stages["assign"][0] / steps
+    peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    tflops = assign_flops / (assign_ms / 1e3) / 1e12
+    result = {
+        "metric": "wave-index build (segmented spherical k-means) time", "value": build_ms, "unit": "ms",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": build_ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "kv_heads": w.Hkv, "head_dim": w.d, "context": w.N,
+                   "segment": w.seg_len, "clusters_per_segment": w.clusters_per_seg, "iterations": w.iters},
+        "stage_ms": {k: v[0] / steps for k, v in stages.items() if v[1]},
+        "roofline": {"kernel": "k_assign", "bound": "mfma", "achieved": tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +191,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--build-only", action="store_true",
+                    help="time the index build (segmented spherical k-means) instead of the decode step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would hold its "
@@ -159,10 +206,9 @@ def main():
     from kv_vector_index_amd import wave_index as wi
 
     w = synth.WORKLOADS[args.workload]
-    if w.top_k <= 0:
-        print(f"workload {w.name} has no decode step (build only)", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.build_only or w.top_k <= 0:
+        return bench_build(w, args, dev)
     log(f"[bench] workload {w.name}: generating inputs on the device")
     Kt, Vt, Qt = synth.make_instance_device(w, args.seed, dev)
 

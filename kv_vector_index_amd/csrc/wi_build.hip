@@ -172,13 +172,22 @@ __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
 }
 
 // ============================================================================ k_assign
-constexpr int kAssignWaves = 8;
-constexpr int kAssignThreads = 64 * kAssignWaves;
-constexpr int kAssignKeys = 64 * kAssignWaves;     // keys per block: 4 tiles of 16 per wave
-
+// Per element type: centroid rows per LDS chunk, LDS row stride (bytes, padded against bank
+// conflicts) and waves per block (each wave scores 4 tiles of 16 keys).  bf16 keys fit 128
+// VGPRs, so 16 waves (4 per SIMD) share one staged chunk; fp32 keys take twice the registers.
 template <typename T> struct AssignCfg;
-template <> struct AssignCfg<uint16_t> { static constexpr int kChunk = 512; static constexpr int kStride = 272; };
-template <> struct AssignCfg<float> { static constexpr int kChunk = 256; static constexpr int kStride = 528; };
+template <> struct AssignCfg<uint16_t> { static constexpr int kChunk = 512, kStride = 272, kWaves = 16; };
+template <> struct AssignCfg<float> { static constexpr int kChunk = 256, kStride = 528, kWaves = 8; };
+template <typename T> constexpr int assign_threads() { return 64 * AssignCfg<T>::kWaves; }
+
+// a.lo * b.lo + a.hi * b.hi + c for packed bfloat16 pairs: both products are exact in fp32, the
+// sums round as fp32 additions.  Emitted directly: the compiler's builtin for this instruction
+// picks the wrong 32-bit pieces of a 128-bit register here.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 
 // Running top-2 of one key's fp32 scores and the 4-centroid group that holds the best one.
 struct Best2 {
@@ -216,13 +225,14 @@ __device__ __forceinline__ void best2_merge_xor(Best2& t, int m) {
 // certified when it leads the second best by more than twice the fp32 error bound, otherwise the
 // key goes to the fp64 re-decision list.
 template <typename T>
-__global__ __launch_bounds__(kAssignThreads) void k_assign(BuildArgs a, int it) {
+__global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int it) {
   extern __shared__ __attribute__((aligned(16))) unsigned char clds[];
   constexpr int CH = AssignCfg<T>::kChunk, STR = AssignCfg<T>::kStride;
   const int s = blockIdx.y, bg = blockIdx.z;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
-  const int key0 = blockIdx.x * kAssignKeys;
+  constexpr int NT = assign_threads<T>();
+  const int key0 = blockIdx.x * NT;                 // 64 keys per wave
   if (key0 >= n_s) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(kAssignThreads) void k_assign(BuildArgs a, int it) 
     __syncthreads();
     // stage centroid rows [c0, c0 + ch16) into LDS (rows past cs_eff are zero)
     constexpr int Q = kD * (int)sizeof(T) / 16;      // 16-byte pieces per row
-    for (int idx = threadIdx.x; idx < ch16 * Q; idx += kAssignThreads) {
+    for (int idx = threadIdx.x; idx < ch16 * Q; idx += NT) {
       const int r = idx / Q, q = idx - r * Q;
       u32x4_t val = {0u, 0u, 0u, 0u};
       if (r < ch) val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(mh + (size_t)(c0 + r) * kD) + q * 16);
@@ -336,12 +346,11 @@ __global__ __launch_bounds__(kAssignThreads) void k_assign(BuildArgs a, int it) 
           u32x4_t cv;
           if (resident) cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * lg + 16 * st);
           else cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * lg + 8 * st);
-          const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc += __uint_as_float(cw[e] << 16) * (float)kb[kt][st][2 * e];
-            acc += __uint_as_float(cw[e] & 0xffff0000u) * (float)kb[kt][st][2 * e + 1];
-          }
+          const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
+          acc = dot2_bf16(cv.x, kw.x, acc);
+          acc = dot2_bf16(cv.y, kw.y, acc);
+          acc = dot2_bf16(cv.z, kw.z, acc);
+          acc = dot2_bf16(cv.w, kw.w, acc);
         }
       } else {
         const float* cr = resident ? reinterpret_cast<const float*>(clds + c * STR) + 32 * lg
@@ -605,7 +614,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs;
   for (int it = 0; it < a.iters; ++it) {
     prof_begin(WI_STAGE_ASSIGN, st);
-    hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, kAssignKeys), a.nseg, BG), dim3(kAssignThreads),
+    hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, assign_threads<T>()), a.nseg, BG), dim3(assign_threads<T>()),
                        alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
