@@ -179,6 +179,7 @@ template <typename T> struct AssignCfg;
 template <> struct AssignCfg<uint16_t> { static constexpr int kChunk = 512, kStride = 272, kWaves = 16; };
 template <> struct AssignCfg<float> { static constexpr int kChunk = 256, kStride = 528, kWaves = 8; };
 template <typename T> constexpr int assign_threads() { return 64 * AssignCfg<T>::kWaves; }
+constexpr int64_t kAssignBlocksTarget = 256;       // one block per CU
 
 // a.lo * b.lo + a.hi * b.hi + c for packed bfloat16 pairs: both products are exact in fp32, the
 // sums round as fp32 additions.  Emitted directly: the compiler's builtin for this instruction
@@ -189,26 +190,26 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return d;
 }
 
-// Running top-2 of one key's fp32 scores and the 4-centroid group that holds the best one.
+// Running state of one key over the 4-centroid groups seen so far: the largest and second-largest
+// group maximum of the fp32 scores, and the group holding the largest.  Every centroid outside
+// the best group scores at most b2; the best group's own four scores are recomputed at the end.
 struct Best2 {
   float b1, b2;
   int grp;
 };
 
-// Fold the scores of centroids 4 grp .. 4 grp + 3: the exact two largest values so far, and the
-// group of the largest (an equal later group does not replace it: lower ids win ties).
+// Fold the group of centroids 4 grp .. 4 grp + 3 (an equal later group does not replace the
+// best: lower ids win ties, and b2 then equals b1 so that the key is re-decided exactly).
 __device__ __forceinline__ void best2_fold4(Best2& t, float a0, float a1, float a2, float a3, int grp) {
-  const float m = fmaxf(fmaxf(a0, a1), a2);                 // largest of a0..a2
-  const float md = __builtin_amdgcn_fmed3f(a0, a1, a2);     // second largest of a0..a2
-  const float g1 = fmaxf(m, a3);
-  const float g2 = fmaxf(md, fminf(m, a3));
-  const bool nw = g1 > t.b1;
-  t.b2 = fmaxf(fmaxf(fminf(t.b1, g1), t.b2), g2);
-  t.b1 = fmaxf(t.b1, g1);
+  const float g = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+  const bool nw = g > t.b1;
+  t.b2 = __builtin_amdgcn_fmed3f(t.b1, t.b2, g);            // b1 >= b2: the new second largest
+  t.b1 = fmaxf(t.b1, g);
   t.grp = nw ? grp : t.grp;
 }
 
-// Merge the state of lane (lane ^ m): the union's two largest values, the lower group on ties.
+// Merge the state of lane (lane ^ m): the two largest group maxima of the union, the lower group
+// on ties.
 __device__ __forceinline__ void best2_merge_xor(Best2& t, int m) {
   const float o1 = __shfl_xor(t.b1, m), o2 = __shfl_xor(t.b2, m);
   const int og = __shfl_xor(t.grp, m);
@@ -219,29 +220,46 @@ __device__ __forceinline__ void best2_merge_xor(Best2& t, int m) {
 
 // Keys are the MFMA B operand (column = key), held in registers; the segment's centroid
 // directions are staged in LDS in chunks and fed as the A operand (row = centroid).  Lane (lr,
-// lg) of an output tile holds centroids 4 lg .. 4 lg + 3 of the 16-centroid tile for key lr; each
-// lane folds them into a running top-2 (values exact, best group only).  At the end the four
-// scores of the winning group are recomputed, which names the best centroid; the choice is
-// certified when it leads the second best by more than twice the fp32 error bound, otherwise the
-// key goes to the fp64 re-decision list.
-template <typename T>
+// lg) of an output tile holds centroids 4 lg .. 4 lg + 3 of the 16-centroid tile for key lr and
+// folds their maximum into the key's running best two group maxima.  At the end the four scores
+// of the best group are recomputed, which names the best centroid; the choice is certified when
+// it leads every other centroid (the group's other three, and the second-best group maximum) by
+// more than twice the fp32 error bound, otherwise the key goes to the fp64 re-decision list.
+template <typename T, bool kResident>
 __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int it) {
   extern __shared__ __attribute__((aligned(16))) unsigned char clds[];
   constexpr int CH = AssignCfg<T>::kChunk, STR = AssignCfg<T>::kStride;
+  constexpr int NT = assign_threads<T>();          // 64 keys per wave and pass
   const int s = blockIdx.y, bg = blockIdx.z;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
-  constexpr int NT = assign_threads<T>();
-  const int key0 = blockIdx.x * NT;                 // 64 keys per wave
-  if (key0 >= n_s) return;
+  if (blockIdx.x * NT >= n_s) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
   const T* mh = static_cast<const T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
+  constexpr bool resident = kResident;            // one staged chunk holds every centroid
+  constexpr int Q = kD * (int)sizeof(T) / 16;      // 16-byte pieces per centroid row
+  // stage centroid rows [c0, c0 + ch16) into LDS (rows past cs_eff are zero)
+  auto stage = [&](int c0, int ch, int ch16) {
+    for (int idx = threadIdx.x; idx < ch16 * Q; idx += NT) {
+      const int r = idx / Q, q = idx - r * Q;
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (r < ch) val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(mh + (size_t)(c0 + r) * kD) + q * 16);
+      *reinterpret_cast<u32x4_t*>(clds + r * STR + q * 16) = val;
+    }
+  };
+  if constexpr (resident) {
+    stage(0, cs_eff, (cs_eff + 15) & ~15);
+    __syncthreads();
+  }
 
+  // The block's passes: keys [p NT, (p + 1) NT) for p = blockIdx.x, blockIdx.x + gridDim.x, ...
+  // With every centroid resident there is no barrier between passes, so the waves drift apart
+  // and one wave's loads and list updates overlap the others' matrix work.
+  for (int key0 = blockIdx.x * NT; key0 < n_s; key0 += gridDim.x * NT) {
   Best2 tk[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) { tk[kt].b1 = -INFINITY; tk[kt].b2 = -INFINITY; tk[kt].grp = 0; }
-
   // key (lane & 15) of tile kt; lane group lg holds dims 32 lg .. 32 lg + 31
   constexpr int KE = sizeof(T) == 2 ? 4 : 32;      // bf16: 4 x 8 elements; fp32: 32 elements
   typedef typename std::conditional<sizeof(T) == 2, bf16x8_t, float>::type KElem;
@@ -270,16 +288,11 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   for (int c0 = 0; c0 < cs_eff; c0 += CH) {
     const int ch = min(CH, cs_eff - c0);
     const int ch16 = (ch + 15) & ~15;
-    __syncthreads();
-    // stage centroid rows [c0, c0 + ch16) into LDS (rows past cs_eff are zero)
-    constexpr int Q = kD * (int)sizeof(T) / 16;      // 16-byte pieces per row
-    for (int idx = threadIdx.x; idx < ch16 * Q; idx += NT) {
-      const int r = idx / Q, q = idx - r * Q;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (r < ch) val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(mh + (size_t)(c0 + r) * kD) + q * 16);
-      *reinterpret_cast<u32x4_t*>(clds + r * STR + q * 16) = val;
+    if constexpr (!resident) {
+      __syncthreads();
+      stage(c0, ch, ch16);
+      __syncthreads();
     }
-    __syncthreads();
     const int nct = ch16 / 16;
     for (int ct = 0; ct < nct; ++ct) {
       const int grp = (c0 + ct * 16) / 4 + lg;
@@ -323,6 +336,13 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     }
   }
 
+  // key norms for the error bound, loaded while the winners are recomputed
+  float knorm[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int i = key0 + w * 64 + kt * 16 + lr;
+    knorm[kt] = (lg == 0 && i < n_s) ? a.knorm[(size_t)bg * a.Nc + (size_t)s * a.L + i] : 0.f;
+  }
   // combine the four lane groups holding disjoint centroid subsets of the same key
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) { best2_merge_xor(tk[kt], 16); best2_merge_xor(tk[kt], 32); }
@@ -330,8 +350,46 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   // the winning group's four scores, recomputed on the vector units (each lane its 32 dims, then
   // summed over the four lane groups), name the best centroid; certify it against the best of
   // the rest: the group's other three and the exact second-best fp32 score overall
-  const bool resident = cs_eff <= CH;             // the last staged chunk holds every centroid
   int flagged[4];
+  // lane's 32-dim part of <key of tile kt, centroid c>; rows from LDS when resident, else global
+  auto part_dot = [&](int kt, int c) -> float {
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * lg + 16 * st);
+        const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
+        acc = dot2_bf16(cv.x, kw.x, acc);
+        acc = dot2_bf16(cv.y, kw.y, acc);
+        acc = dot2_bf16(cv.z, kw.z, acc);
+        acc = dot2_bf16(cv.w, kw.w, acc);
+      }
+    } else {
+      const float* cr = reinterpret_cast<const float*>(clds + c * STR) + 32 * lg;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc += cr[e] * kb[kt][e];
+    }
+    return acc;
+  };
+  auto part_dot_global = [&](int kt, int c) -> float {
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * lg + 8 * st);
+        const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
+        acc = dot2_bf16(cv.x, kw.x, acc);
+        acc = dot2_bf16(cv.y, kw.y, acc);
+        acc = dot2_bf16(cv.z, kw.z, acc);
+        acc = dot2_bf16(cv.w, kw.w, acc);
+      }
+    } else {
+      const float* cr = reinterpret_cast<const float*>(mh) + (size_t)c * kD + 32 * lg;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc += cr[e] * kb[kt][e];
+    }
+    return acc;
+  };
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int grp = tk[kt].grp;
@@ -339,25 +397,9 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = min(4 * grp + r, cs_eff - 1);
-      float acc = 0.f;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          u32x4_t cv;
-          if (resident) cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * lg + 16 * st);
-          else cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * lg + 8 * st);
-          const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
-          acc = dot2_bf16(cv.x, kw.x, acc);
-          acc = dot2_bf16(cv.y, kw.y, acc);
-          acc = dot2_bf16(cv.z, kw.z, acc);
-          acc = dot2_bf16(cv.w, kw.w, acc);
-        }
-      } else {
-        const float* cr = resident ? reinterpret_cast<const float*>(clds + c * STR) + 32 * lg
-                                   : reinterpret_cast<const float*>(mh) + (size_t)c * kD + 32 * lg;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) acc += cr[e] * kb[kt][e];
-      }
+      float acc;
+      if constexpr (resident) acc = part_dot(kt, c);
+      else acc = part_dot_global(kt, c);
       acc += __shfl_xor(acc, 16);
       acc += __shfl_xor(acc, 32);
       p[r] = 4 * grp + r < cs_eff ? acc : -INFINITY;
@@ -372,7 +414,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     flagged[kt] = 0;
     if (lg == 0 && i < n_s) {
       const size_t gi = (size_t)bg * a.Nc + (size_t)s * a.L + i;
-      const double kn = (double)a.knorm[gi] * (1.0 + 1.0 / 1024);
+      const double kn = (double)knorm[kt] * (1.0 + 1.0 / 1024);
       const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * kn * 1.01 + 1e-30;
       a.assign[gi] = 4 * grp + rb;
       flagged[kt] = !((double)p[rb] - (double)b2 > 2.0 * delta);
@@ -391,6 +433,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
       a.flag_list[pos] = (int32_t)((size_t)bg * a.Nc + (size_t)s * a.L + i);
     }
   }
+  }  // passes
 }
 
 // ============================================================================ k_rescore
@@ -612,10 +655,18 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   }
   const size_t alds = (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride;
   const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs;
+  // assignment blocks per segment: about one block per CU in all (each stages the segment's
+  // centroids once and loops over 64-key-per-wave passes), at least one pass each
+  const unsigned assign_px = (unsigned)std::max<int64_t>(1, std::min<int64_t>(
+      ceil_div(a.L, assign_threads<T>()), ceil_div(kAssignBlocksTarget, (int64_t)a.nseg * BG)));
   for (int it = 0; it < a.iters; ++it) {
     prof_begin(WI_STAGE_ASSIGN, st);
-    hipLaunchKernelGGL(k_assign<T>, dim3((unsigned)ceil_div(a.L, assign_threads<T>()), a.nseg, BG), dim3(assign_threads<T>()),
-                       alds, st, a, it);
+    if (a.Cs <= AssignCfg<T>::kChunk)
+      hipLaunchKernelGGL((k_assign<T, true>), dim3(assign_px, a.nseg, BG), dim3(assign_threads<T>()),
+                         alds, st, a, it);
+    else
+      hipLaunchKernelGGL((k_assign<T, false>), dim3(assign_px, a.nseg, BG), dim3(assign_threads<T>()),
+                         alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
     hipLaunchKernelGGL(k_rescore<T>, dim3(1024), dim3(256), 0, st, a, it);
@@ -644,8 +695,10 @@ static void set_lds_limits() {
   const int big = 160 * 1024 - 8192;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_init<float>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_init<uint16_t>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<float>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<uint16_t>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<float, true>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<float, false>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<uint16_t, true>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_assign<uint16_t, false>), hipFuncAttributeMaxDynamicSharedMemorySize, big);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_csr), hipFuncAttributeMaxDynamicSharedMemorySize, big);
   done = true;
 }

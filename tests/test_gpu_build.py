@@ -51,6 +51,21 @@ def test_build_parity_one_segment_and_many_clusters():
     _assert_index_equal(index_to_numpy(gi), ref)
 
 
+def test_build_parity_chunked_centroids_f32():
+    # 300 clusters per segment: more than one LDS chunk of fp32 centroid directions
+    w = synth.Workload("b", 1, 1, 1, 128, 2000, "f32", 40, 0, 0, 0, 300, 3, 5)
+    gi, ref, _, _ = _build_both(w, 4, 11)
+    _assert_index_equal(index_to_numpy(gi), ref)
+
+
+def test_build_parity_many_segments_several_passes_per_block():
+    # 8 KV heads x 64 segments: more segments than one assignment block each can cover with a
+    # single pass, so every block loops over several key passes
+    w = synth.Workload("b", 1, 8, 8, 128, 64 * 1100 + 12, "f32", 30, 4, 8, 1100, 20, 2, 5)
+    gi, ref, _, _ = _build_both(w, 6, 21)
+    _assert_index_equal(index_to_numpy(gi), ref)
+
+
 def test_build_parity_duplicate_keys_force_ties():
     dev = device()
     w = synth.Workload("b", 1, 2, 1, 128, 1200, "bf16", 8, 2, 2, 400, 24, 4, 3)
