@@ -406,14 +406,15 @@ __device__ __forceinline__ int bin_of(const KthBin& kb, uint32_t key) {
   return min(kBins - 1, max(0, (int)((f32_from_order_key(key) - kb.mn) * kb.inv)));
 }
 
-// k-th largest (1 <= k <= n) of n score order keys (all non-zero): the histogram bin of the
-// k-th largest, whose keys are then ranked by one wave (a radix select over the keys covers a bin
-// of more than 64).  `bl` holds >= 64 keys.
+// k-th largest (k >= 1) of the non-zero ones of n score order keys, 0 when fewer than k are
+// non-zero: the histogram bin of the k-th largest, whose keys are then ranked by one wave (a radix
+// select over the keys covers a bin of more than 64).  `bl` holds >= 64 keys.
 template <typename Get>
 __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint32_t* bl, int* iscr,
                                     float* fred, int* sh_i) {
   const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const KthBin kb = kth_bin(n, k, get, hist, iscr, fred, sh_i);
+  if (kb.bin < 0) return 0u;
   const int rem = k - kb.above;
   const int nb = (int)hist[kb.bin];
   if (nb <= 64) {
@@ -435,28 +436,6 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
   }
   int rr;
   return block_radix_select<uint32_t>(n, k, get, hist, iscr, &rr);
-}
-
-// A lower bound of the k-th largest (1 <= k <= n) of n score order keys (some may be 0, which
-// rank last): the smallest non-zero key of the histogram bin that holds the k-th largest
-// non-zero key; 0 when fewer than k keys are non-zero.
-template <typename Get>
-__device__ uint32_t kth_lower_bound(int n, int k, Get get, uint32_t* hist, int* iscr, float* fred, int* sh_i) {
-  const int tid = threadIdx.x, NT = blockDim.x;
-  const KthBin kb = kth_bin(n, k, get, hist, iscr, fred, sh_i);
-  if (kb.bin < 0) return 0u;
-  uint32_t lo = 0xffffffffu;
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t x = get(i);
-    if (x != 0u && bin_of(kb, x) == kb.bin) lo = min(lo, x);
-  }
-  lo = ~wave_umax(~lo);
-  if ((threadIdx.x & 63) == 0) hist[threadIdx.x >> 6] = lo;
-  __syncthreads();
-  uint32_t r = 0xffffffffu;
-  for (int i = 0; i < NT / 64; ++i) r = min(r, hist[i]);
-  __syncthreads();
-  return r;
 }
 
 // Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
@@ -505,6 +484,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __shared__ uint32_t ckey[kCandCap];                // candidates: score keys
   __shared__ int cidl[kCandCap];                     // candidates: cluster ids
   __shared__ int tfull[kFullCap];                    // tiles whose 8 best pass the threshold
+  __shared__ int rl_off[kCandCap];                   // retrieved list, by rank: first row, size
+  __shared__ int rl_sz[kCandCap];
   __shared__ uint32_t hist[kBins];
   __shared__ int iscr[48];
   __shared__ float fred[2 * kSelThreads / 64];
@@ -572,6 +553,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   };
 
+  bool fast_pub = false;            // the retrieved clusters are all LDS candidates
+  int co[kCandCap / kSelThreads], ce[kCandCap / kSelThreads];
   if (k_eff > 0 && k_eff == n_ne) {
     visit_keys([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
@@ -579,10 +562,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     // exact-or-rounded products, doubled for an unspecified MFMA summation order
     const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qv * (1.0 + 1.0 / 1024) *
                              (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
-    // ---- lower bound L of the k_eff-th largest score from the tile summaries
+    // ---- L = the k_eff-th largest of the tile summaries: a lower bound of t, and t itself
+    // when no tile has its 8th best within 2 delta of L (every score >= L is then a summary)
     float thr_f = -INFINITY;
+    uint32_t L = 0u;
     if (use_sum) {
-      const uint32_t L = kth_lower_bound(nsum, k_eff, [&](int i) { return skey[i]; }, hist, iscr, fred, sh_i);
+      L = kth_largest_key(nsum, k_eff, [&](int i) { return skey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
       if (L != 0u) {
         const double thr_d = (double)f32_from_order_key(L) - 2.0 * delta;
         thr_f = (float)thr_d;
@@ -641,10 +626,22 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     __syncthreads();
     const int n_c = sh_i[2];
     const bool listed = n_c <= kCandCap;
-    WI_TP(5);
-    // ---- t = k_eff-th largest score: from the candidates, else over all scores
-    uint32_t thr;
+    fast_pub = listed;
+    // first rows and sizes of the candidates, fetched now and used when publishing
     if (listed) {
+#pragma unroll
+      for (int j = 0; j < kCandCap / kSelThreads; ++j) {
+        const int i = tid + j * NT;
+        if (i < n_c) { const int c = cidl[i]; co[j] = a.offsets[(size_t)bg * (C + 1) + c]; ce[j] = a.offsets[(size_t)bg * (C + 1) + c + 1]; }
+      }
+    }
+    WI_TP(5);
+    // ---- t = k_eff-th largest score: L itself when no tile was scanned in full, else from the
+    // candidates, else over all scores
+    uint32_t thr;
+    if (listed && !scan_all && sh_i[5] == 0 && L != 0u) {
+      thr = L;
+    } else if (listed) {
       thr = kth_largest_key(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
     } else {
       int rr;
@@ -725,7 +722,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   // of the attention kernel, the list entry that holds its first retrieved token
   {
     const int K = a.top_k, S = a.att_split;
-    // ascending retrieved ids (LDS when they fit)
+    // ascending retrieved ids (LDS when they fit); on the candidate path each retrieved
+    // candidate also drops its prefetched first row, size and key at its rank
     int32_t* rl = K <= kSumCap ? sid : a.band_ids + (size_t)bh * C;
     const int perw = (W32 + NT - 1) / NT;
     const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
@@ -733,9 +731,27 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
     int tot;
     int p = block_exclusive_scan(n, iscr, &tot);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t m = bits[w];
-      while (m) { const int c = w * 32 + __ffs(m) - 1; m &= m - 1; rl[p++] = c; }
+    if (fast_pub) {
+      int* wpre = reinterpret_cast<int*>(bbits);      // the band bitmap is no longer needed
+      for (int w = w0; w < w1; ++w) { wpre[w] = p; p += __popc(bits[w]); }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kCandCap / kSelThreads; ++j) {
+        const int i = tid + j * NT;
+        if (i < sh_i[2]) {
+          const int c = cidl[i];
+          const uint32_t wb = bits[c >> 5];
+          if ((wb >> (c & 31)) & 1u) {
+            const int r = wpre[c >> 5] + __popc(wb & ((1u << (c & 31)) - 1u));
+            sid[r] = c; skey[r] = ckey[i]; rl_off[r] = co[j]; rl_sz[r] = ce[j] - co[j];
+          }
+        }
+      }
+    } else {
+      for (int w = w0; w < w1; ++w) {
+        uint32_t m = bits[w];
+        while (m) { const int c = w * 32 + __ffs(m) - 1; m &= m - 1; rl[p++] = c; }
+      }
     }
     tot = min(tot, K);
     __syncthreads();
@@ -763,10 +779,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
         const int i = i0 + u;
         c_[u] = 0; r_[u] = 0; z_[u] = 0; k_[u] = 0u;
         if (i < tot) {
-          c_[u] = rl[i];
-          r_[u] = off[c_[u]];
-          z_[u] = off[c_[u] + 1] - r_[u];
-          k_[u] = keys[c_[u]];
+          if (fast_pub) {
+            c_[u] = sid[i]; r_[u] = rl_off[i]; z_[u] = rl_sz[i]; k_[u] = skey[i];
+          } else {
+            c_[u] = rl[i];
+            r_[u] = off[c_[u]];
+            z_[u] = off[c_[u] + 1] - r_[u];
+            k_[u] = keys[c_[u]];
+          }
           ssum += z_[u];
         }
       }
