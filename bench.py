@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_MFMA_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_{}.json")   # per workload
+PROF_REPS = 20                  # launches of each decode kernel between its timing events
 KERNEL_NAMES = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
@@ -299,14 +300,15 @@ def main():
         total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K_steps
 
-    # ---- per-kernel timing (eager, HIP events around every kernel on the launch stream).  A
-    # long matrix product heads the queue so the host enqueues every step before the GPU reaches
-    # them: the events then time the kernels, not the Python launch gaps.
+    # ---- per-kernel timing (eager, HIP events on the launch stream around PROF_REPS back-to-back
+    # launches of each kernel, so that the event records themselves do not count).  A long matrix
+    # product heads the queue so the host enqueues every step before the GPU reaches them: the
+    # events then time the kernels, not the Python launch gaps.
     log("[bench] per-kernel timing pass")
-    prof_steps = min(K_steps, 200)
+    prof_steps = min(K_steps, 20)
     a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    wi.wi_profile_enable(True)
+    wi.wi_profile_enable(True, PROF_REPS)
     for _ in range(30):
         a = a @ a
         a = a / a.abs().max()

@@ -165,11 +165,16 @@ typedef enum {
 /* (host) Profiling hook for measurement tools.  While enabled, wi_decode and wi_build_index
  * record a pair of HIP events around each kernel they launch, on the call's stream (this adds
  * event records between the kernels; leave it disabled for production timing).  Enabling clears
- * the accumulated figures.  Not thread-safe against concurrent calls on several threads. */
+ * the accumulated figures.  Not thread-safe against concurrent calls on several threads.
+ * enable = 0 turns the hook off, 1 times every launch once; enable = R > 1 additionally launches
+ * each decode kernel R times back to back between its two events (the decode kernels are pure
+ * functions of their inputs, so the repeats leave the results unchanged), which measures the
+ * per-launch duration without the cost of the event records themselves.  Negative values:
+ * WI_ERR_INVALID_ARG. */
 wi_status wi_profile_enable(int enable);
 
 /* (host) Wait for the recorded events and return, per stage, the summed kernel time in
- * milliseconds and the number of launches since the hook was enabled.  Both arrays hold
+ * milliseconds and the number of launches (repeats included) since the hook was enabled.  Both arrays hold
  * WI_NUM_STAGES entries.  Synchronises on the recorded events only. */
 wi_status wi_profile_read(double *total_ms, int64_t *launches);
 

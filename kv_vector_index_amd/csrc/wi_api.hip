@@ -76,11 +76,13 @@ wi_status derive_build(const wi_build_params* p, Derived* d) {
 namespace wi {
 
 bool g_prof_on = false;
+int g_prof_reps = 1;
 
 namespace {
 struct ProfRec {
   int stage;
   hipEvent_t a, b;
+  int reps;            // launches of the stage between a and b
 };
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof_recs;
@@ -95,7 +97,7 @@ void prof_record(int stage, bool begin, hipStream_t s) {
   if (begin) {
     g_prof_open[stage] = ev;
   } else if (g_prof_open[stage]) {
-    g_prof_recs.push_back({stage, g_prof_open[stage], ev});
+    g_prof_recs.push_back({stage, g_prof_open[stage], ev, g_prof_reps});
     g_prof_open[stage] = nullptr;
   } else {
     (void)hipEventDestroy(ev);
@@ -306,8 +308,10 @@ static void prof_clear() {
 
 wi_status wi_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(wi::g_prof_mu);
+  if (enable < 0) return fail(WI_ERR_INVALID_ARG, "negative profiling mode %d", enable);
   if (enable) prof_clear();
   wi::g_prof_on = enable != 0;
+  wi::g_prof_reps = enable > 1 ? enable : 1;
   return WI_OK;
 }
 
@@ -320,8 +324,10 @@ wi_status wi_profile_read(double* total_ms, int64_t* launches) {
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
     if (e != hipSuccess) return fail(WI_ERR_HIP, "profiling events: %s", hipGetErrorString(e));
+    // a decode stage launched `reps` times back to back between its events counts as that many
+    const int reps = r.stage <= WI_STAGE_MERGE ? r.reps : 1;
     total_ms[r.stage] += ms;
-    launches[r.stage] += 1;
+    launches[r.stage] += reps;
   }
   return WI_OK;
 }

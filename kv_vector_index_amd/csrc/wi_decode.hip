@@ -1287,19 +1287,28 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
-  hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, a);
+  // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent)
+  for (int r = 0; r < prof_reps(); ++r) {
+    hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, a);
+  }
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
+  for (int r = 0; r < prof_reps(); ++r) {
+    hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
+  }
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_ATTEND, s);
-  hipLaunchKernelGGL(k_attend<T>, dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
+  for (int r = 0; r < prof_reps(); ++r) {
+    hipLaunchKernelGGL(k_attend<T>, dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
+  }
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
-  hipLaunchKernelGGL(k_merge, dim3(BH), dim3(kMergeThreads), 0, s, a);
+  for (int r = 0; r < prof_reps(); ++r) {
+    hipLaunchKernelGGL(k_merge, dim3(BH), dim3(kMergeThreads), 0, s, a);
+  }
   prof_end(WI_STAGE_MERGE, s);
   return hipGetLastError();
 }

@@ -79,6 +79,8 @@ hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStre
 
 // ------------------------------------------------------------------ profiling hook
 extern bool g_prof_on;
+extern int g_prof_reps;   // decode kernels launched this many times back to back while profiling
+inline int prof_reps() { return g_prof_on ? g_prof_reps : 1; }
 void prof_record(int stage, bool begin, hipStream_t s);
 inline void prof_begin(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, true, s); }
 inline void prof_end(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, false, s); }

@@ -131,8 +131,10 @@ def wi_decode(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_pt
                                   sel_ptr, ws_ptr, ws_bytes, stream))
 
 
-def wi_profile_enable(enable: bool) -> int:
-    return _check(lib().wi_profile_enable(1 if enable else 0))
+def wi_profile_enable(enable, repeats: int = 1) -> int:
+    """Turn the per-kernel timing hook on or off; with repeats > 1 every decode kernel is
+    launched that many times back to back between its events."""
+    return _check(lib().wi_profile_enable(max(1, int(repeats)) if enable else 0))
 
 
 def wi_profile_read() -> dict:

@@ -163,3 +163,12 @@ def test_status_strings():
     for s in (wi.WI_OK, wi.WI_ERR_INVALID_ARG, wi.WI_ERR_UNSUPPORTED, wi.WI_ERR_WORKSPACE, wi.WI_ERR_HIP):
         assert wi.wi_status_string(s)
     assert wi.wi_status_string(-99) == "unknown status"
+
+
+def test_profile_hook_modes():
+    L = wi.lib()
+    assert L.wi_profile_enable(-1) == wi.WI_ERR_INVALID_ARG
+    assert L.wi_profile_enable(5) == wi.WI_OK           # five back-to-back launches per decode kernel
+    stages = wi.wi_profile_read()                         # nothing recorded yet
+    assert all(v == (0.0, 0) for v in stages.values())
+    assert L.wi_profile_enable(0) == wi.WI_OK
