@@ -305,22 +305,28 @@ constexpr int kFullCap = 256;       // tiles scanned in full
 constexpr int kBins = 2048;         // histogram bins over [min, max] of the ranked scores
 constexpr int kPubPT = 8;           // retrieved clusters per thread in one publishing round
 
-// Radix bin of the k-th largest key: threads 0..255 own the bins in descending order, so an
-// inclusive scan over them gives suffix counts; the one bin with excl < rem <= incl is chosen.
+// Radix bin of the k-th largest key: each thread owns 256 / blockDim.x consecutive bins in
+// descending order, so an exclusive scan over the threads gives the count above each thread's
+// bins; the one bin with excl < rem <= incl is chosen.
 __device__ __forceinline__ void radix_pick(const uint32_t* hist, int rem, int* scr, int* out_bin,
                                            int* out_above) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bin = 255 - tid;
-  const int v = tid < 256 ? (int)hist[bin] : 0;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == 63 && w < 4) scr[w] = inc;
-  __syncthreads();
-  if (tid < 256) {
-    int base = 0;
-    for (int i = 0; i < w; ++i) base += scr[i];
-    const int incl = base + inc, excl = incl - v;
-    if (excl < rem && rem <= incl) { *out_bin = bin; *out_above = excl; }
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int per = (256 + NT - 1) / NT;
+  int v = 0;
+  for (int j = 0; j < per; ++j) { const int bin = 255 - per * tid - j; if (bin >= 0) v += (int)hist[bin]; }
+  int tot;
+  int run = block_exclusive_scan(v, scr, &tot);
+  if (run < rem && rem <= run + v) {
+    for (int j = 0; j < per; ++j) {
+      const int bin = 255 - per * tid - j;
+      const int hb = (int)hist[bin];
+      if (run + hb >= rem) { scr[20] = bin; scr[21] = run; break; }
+      run += hb;
+    }
   }
+  __syncthreads();
+  *out_bin = scr[20];
+  *out_above = scr[21];
   __syncthreads();
 }
 
@@ -331,16 +337,17 @@ __device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, int* scr,
   K prefix = 0, mask = 0;
   int rem = k;
   for (int shift = (int)sizeof(K) * 8 - 8; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const K key = get(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    radix_pick(hist, rem, scr, scr + 8, scr + 9);
-    prefix |= (K)scr[8] << shift;
-    rem -= scr[9];
+    int bin, above;
+    radix_pick(hist, rem, scr, &bin, &above);
+    prefix |= (K)bin << shift;
+    rem -= above;
     mask |= (K)255 << shift;
   }
   *rem_out = rem;
@@ -383,7 +390,7 @@ __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, floa
   }
   __syncthreads();
   // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
-  constexpr int BPT = (kBins + kSelThreads - 1) / kSelThreads;
+  const int BPT = (kBins + NT - 1) / NT;
   int v = 0;
   for (int j = 0; j < BPT; ++j) { const int bin = kBins - 1 - BPT * tid - j; if (bin >= 0) v += (int)hist[bin]; }
   int tot;
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __shared__ int rl_sz[kCandCap];
   __shared__ uint32_t hist[kBins];
   __shared__ int iscr[48];
-  __shared__ float fred[2 * kSelThreads / 64];
+  __shared__ float fred[32];
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
   __shared__ int sh_i[8];
@@ -507,8 +514,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   const int KPT = (C + NT - 1) / NT;          // thread t visits clusters j * NT + t, j < KPT
 
   // ---- set-up: query, largest centroid norm, non-empty count, tile summaries
-  float qv = 0.f;
-  if (tid < kD) { qv = St<T>::f(qh[tid]); qd[tid] = (double)qv; }
+  float qv = 0.f;                             // this thread's part of |q|^2
+  for (int i = tid; i < kD; i += NT) { const float x = St<T>::f(qh[i]); qd[i] = (double)x; qv += x * x; }
   float mxn = 0.f;
   int ne = 0;
   for (int i = tid; i < tiles; i += NT) {
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     }
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
   {
-    float v0 = (float)ne, v1 = mxn, v2 = qv * qv;
+    float v0 = (float)ne, v1 = mxn, v2 = qv;
     v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_sum(v2);
     if (lane == 0) { fred[wv] = v0; fred[16 + wv] = v1; hist[wv] = __float_as_uint(v2); }
     __syncthreads();
