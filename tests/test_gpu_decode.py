@@ -155,6 +155,46 @@ def test_decode_gqa_128k_bf16_full_size_sampled_heads():
         assert ids.size == w.top_k and np.all(np.diff(ids) > 0) and np.all(sizes[0, h // G, ids] > 0)
 
 
+def _oracle_index_slice(gi, b, g):
+    """The oracle's view of KV group (b, g) of a device index: exact float64 copies of its arrays
+    with leading dimensions of one."""
+    f = lambda t: t[b:b + 1, g:g + 1].detach().cpu().to(torch.float64).numpy()
+    i = lambda t: t[b:b + 1, g:g + 1].detach().cpu().numpy().astype(np.int64)
+    return oracle.Index(centroids=f(gi.centroids), value_sums=f(gi.value_sums), sizes=i(gi.sizes),
+                        offsets=i(gi.offsets), perm=i(gi.perm), k_perm=f(gi.k_perm), v_perm=f(gi.v_perm),
+                        k_steady=f(gi.k_steady), v_steady=f(gi.v_steady), C=gi.C, Nc=gi.Nc)
+
+
+def test_decode_gqa_128k_b16_drifting_steps_sampled_heads():
+    """Batch 16 at 128K context, 100 decode steps whose queries drift by N(0, 0.1) per step, on
+    the device-built index of the full batch; the oracle checks sampled query heads at the first,
+    a middle and the last step, on the same index (build parity is tested on its own)."""
+    dev = device()
+    w = synth.WORKLOADS["gqa_128k_b16_bf16"]
+    Kt, Vt, Qt = synth.make_instance_device(w, 0, dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    del Kt, Vt
+    qm = synth.drift_queries_device(Qt, w.steps, w.drift, 0)
+    G = w.Hq // w.Hkv
+    heads = [(0, 0), (7, 13), (15, 31)]
+    checks = {0: None, 50: None, w.steps - 1: None}
+    for t in range(w.steps):
+        q = qm[t].to(torch.float32).to(Qt.dtype)
+        o, lse, sel = wi.decode(gi, q, w.top_k)
+        if t in checks:
+            checks[t] = (q.clone(), o.clone(), lse.clone(), sel.clone())
+    torch.cuda.synchronize()
+    slices = {(b, h // G): _oracle_index_slice(gi, b, h // G) for b, h in heads}
+    for t, (q, o, lse, sel) in checks.items():
+        Q64 = synth.as_float64(q)
+        res = [oracle.decode_head(Q64[b, h], slices[(b, h // G)], 0, 0, w.top_k, 1 / math.sqrt(w.d))
+               for b, h in heads]
+        ro = np.stack([r[0] for r in res])
+        rl = np.array([r[1] for r in res])
+        rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
+        assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
+
+
 def test_decode_graph_replay_matches_eager():
     """Decode steps captured in a HIP graph and replayed several times, with eager work and
     synchronisations between replays, give the eager result every time (the kernels zero their
