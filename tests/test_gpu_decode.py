@@ -195,6 +195,27 @@ def test_decode_gqa_128k_b16_drifting_steps_sampled_heads():
         assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
 
 
+def test_decode_gqa_1m_bf16_sampled_heads():
+    """One million tokens per KV head (65536 clusters, top 656): the device-built index decoded
+    once, sampled query heads checked against the oracle on the same index."""
+    dev = device()
+    w = synth.WORKLOADS["gqa_1m_bf16"]
+    Kt, Vt, Qt = synth.make_instance_device(w, 0, dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
+    del Kt, Vt
+    o, lse, sel = wi.decode(gi, Qt, w.top_k)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    heads = [(0, 0), (0, 9), (0, 30)]
+    Q64 = synth.as_float64(Qt)
+    res = [oracle.decode_head(Q64[b, h], _oracle_index_slice(gi, b, h // G), 0, 0, w.top_k, 1 / math.sqrt(w.d))
+           for b, h in heads]
+    ro = np.stack([r[0] for r in res])
+    rl = np.array([r[1] for r in res])
+    rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
+    assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
+
+
 def test_decode_graph_replay_matches_eager():
     """Decode steps captured in a HIP graph and replayed several times, with eager work and
     synchronisations between replays, give the eager result every time (the kernels zero their
