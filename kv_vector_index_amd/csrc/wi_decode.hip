@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   __shared__ float sh_n[kEstTile];          // cluster sizes
   __shared__ uint32_t sh_k[G][kEstTile];    // order keys of the raw scores, 0 for empty clusters
   __shared__ float sh_m[G], sh_den[G], sh_nm[4];
-  __shared__ float sh_num[4][G][kD];
+  __shared__ float sh_num[G <= 4 ? 1 : 4][G][kD];          // G > 4: per-wave numerators
+  __shared__ __attribute__((aligned(16))) float sh_part[G <= 4 ? 16 : 1][G][kD];  // G <= 4: per lane group
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int C = a.C;
@@ -270,24 +271,43 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       for (int e = 0; e < 8; ++e) acc[h][e] += wt * v[e];
     }
   }
+  // sum over the 16 lane groups of the block (4 waves x 4 row groups) that hold the same dims
+  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
+  if constexpr (G <= 4) {
+    // every lane group writes its partial numerators to LDS; 16-way sums read them back
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16);
-      acc[h][e] += __shfl_xor(acc[h][e], 32);
+    for (int h = 0; h < G; ++h) {
+      float* dst = &sh_part[w * 4 + lg][h][8 * lr];
+      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
     }
-  if (lg == 0) {
+    __syncthreads();
+    for (int i = tid; i < G * kD; i += kScoreThreads) {
+      const int h = i / kD, d = i - h * kD;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += sh_part[j][h][d];
+      a.est_num[(slot * G + h) * kD + d] = sum;
+    }
+  } else {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sh_num[w][h][8 * lr + e] = acc[h][e];
-  }
-  __syncthreads();
-  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
-  for (int i = tid; i < G * kD; i += kScoreThreads) {
-    const int h = i / kD, d = i - h * kD;
-    a.est_num[(slot * G + h) * kD + d] = sh_num[0][h][d] + sh_num[1][h][d] + sh_num[2][h][d] + sh_num[3][h][d];
+      for (int e = 0; e < 8; ++e) {
+        acc[h][e] += __shfl_xor(acc[h][e], 16);
+        acc[h][e] += __shfl_xor(acc[h][e], 32);
+      }
+    if (lg == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sh_num[w][h][8 * lr + e] = acc[h][e];
+    }
+    __syncthreads();
+    for (int i = tid; i < G * kD; i += kScoreThreads) {
+      const int h = i / kD, d = i - h * kD;
+      a.est_num[(slot * G + h) * kD + d] = sh_num[0][h][d] + sh_num[1][h][d] + sh_num[2][h][d] + sh_num[3][h][d];
+    }
   }
   if (tid < G) {
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
