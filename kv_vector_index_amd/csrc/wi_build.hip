@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_prep(BuildArgs a) {
   const int bg = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (blockIdx.x == 0 && bg == 0)
-    for (int i = threadIdx.x; i < a.iters; i += blockDim.x) a.flag_cnt[i] = 0u;
+    for (int i = threadIdx.x; i < a.iters; i += 256) a.flag_cnt[i] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.offsets[(size_t)bg * (a.C + 1) + a.C] = a.Nc;
   const T* K = static_cast<const T*>(a.k) + (size_t)bg * a.N * kD;
   const T* V = static_cast<const T*>(a.v) + (size_t)bg * a.N * kD;
@@ -143,9 +143,9 @@ __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
   uint16_t* rows = reinterpret_cast<uint16_t*>(init_lds + a.Cs);
   const uint64_t st0 = segment_state0(a.seed, b, g, s);
   // the draws do not depend on the shuffle state: j_r = r + (x_r mod (n_s - r))
-  for (int r = threadIdx.x; r < cs_eff; r += blockDim.x)
+  for (int r = threadIdx.x; r < cs_eff; r += kInitThreads)
     draw[r] = (uint32_t)r + (uint32_t)(splitmix64_nth(st0, (uint64_t)r) % (uint64_t)(n_s - r));
-  for (int i = threadIdx.x; i < n_s; i += blockDim.x) rows[i] = (uint16_t)i;
+  for (int i = threadIdx.x; i < n_s; i += kInitThreads) rows[i] = (uint16_t)i;
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int r = 0; r < cs_eff; ++r) {
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
   int my = 0;
   for (int j = j0; j < j1; ++j) my += (int)cnt[j];
   int tot;
-  int ex = block_exclusive_scan(my, iscr, &tot);
+  int ex = block_exclusive_scan<kCsrThreads>(my, iscr, &tot);
   for (int j = j0; j < j1; ++j) { loc[j] = (uint32_t)ex; ex += (int)cnt[j]; }
   __syncthreads();
   const int cbase = s * Cs;

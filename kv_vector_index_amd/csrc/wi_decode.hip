@@ -317,7 +317,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 }
 
 // ============================================================================ k_select
-constexpr int kSelThreads = 1024;
+// Block size of the select: 1024 threads while every head has a CU to itself, 512 beyond that
+// (two heads per CU then run at once).
+constexpr int kSelThreadsFew = 1024, kSelThreadsMany = 512;
+constexpr int kSelHeadsPerRound = 256;
 constexpr int kSmallBand = 64;      // bands up to one wave are resolved by direct ranking
 constexpr int kSumCap = 4096;       // tile summaries (8 per 128-cluster tile) staged in LDS
 constexpr int kCandCap = 2048;      // candidate clusters ranked in LDS
@@ -325,17 +328,18 @@ constexpr int kFullCap = 256;       // tiles scanned in full
 constexpr int kBins = 2048;         // histogram bins over [min, max] of the ranked scores
 constexpr int kPubPT = 8;           // retrieved clusters per thread in one publishing round
 
-// Radix bin of the k-th largest key: each thread owns 256 / blockDim.x consecutive bins in
+// Radix bin of the k-th largest key: each thread owns 256 / NT consecutive bins in
 // descending order, so an exclusive scan over the threads gives the count above each thread's
 // bins; the one bin with excl < rem <= incl is chosen.
+template <int NT>
 __device__ __forceinline__ void radix_pick(const uint32_t* hist, int rem, int* scr, int* out_bin,
                                            int* out_above) {
-  const int tid = threadIdx.x, NT = blockDim.x;
-  const int per = (256 + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  constexpr int per = (256 + NT - 1) / NT;
   int v = 0;
   for (int j = 0; j < per; ++j) { const int bin = 255 - per * tid - j; if (bin >= 0) v += (int)hist[bin]; }
   int tot;
-  int run = block_exclusive_scan(v, scr, &tot);
+  int run = block_exclusive_scan<NT>(v, scr, &tot);
   if (run < rem && rem <= run + v) {
     for (int j = 0; j < per; ++j) {
       const int bin = 255 - per * tid - j;
@@ -352,20 +356,20 @@ __device__ __forceinline__ void radix_pick(const uint32_t* hist, int rem, int* s
 
 // Threshold key of the k-th largest of n keys (1 <= k <= n): afterwards exactly k - *rem_out keys
 // are strictly greater than the returned key and at least *rem_out keys equal it.
-template <typename K, typename Get>
+template <int NT, typename K, typename Get>
 __device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, int* scr, int* rem_out) {
   K prefix = 0, mask = 0;
   int rem = k;
   for (int shift = (int)sizeof(K) * 8 - 8; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += NT) {
       const K key = get(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     int bin, above;
-    radix_pick(hist, rem, scr, &bin, &above);
+    radix_pick<NT>(hist, rem, scr, &bin, &above);
     prefix |= (K)bin << shift;
     rem -= above;
     mask |= (K)255 << shift;
@@ -382,9 +386,9 @@ __device__ K block_radix_select(int n, int k, Get get, uint32_t* hist, int* scr,
 // scores; returns the bin holding the k-th largest (1 <= k <= #non-zero) and how many keys lie in
 // higher bins.
 struct KthBin { int bin, above; float mn, inv; };   // bin -1: fewer than k non-zero keys
-template <typename Get>
+template <int NT, typename Get>
 __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, float* fred, int* sh_i) {
-  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   float mx = -INFINITY, mn = INFINITY;
   for (int i = tid; i < n; i += NT) {
     const uint32_t key = get(i);
@@ -397,7 +401,10 @@ __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, floa
   mn = -wave_max(-mn);
   for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
   if (lane == 0) { fred[2 * wv] = mx; fred[2 * wv + 1] = mn; }
+  if (tid == 0) sh_i[4] = 0;                       // key counter of kth_largest_key's small bin
   __syncthreads();
+  WI_TP(12);
+#pragma unroll
   for (int i = 0; i < NT / 64; ++i) { mx = fmaxf(mx, fred[2 * i]); mn = fminf(mn, fred[2 * i + 1]); }
   KthBin r;
   r.mn = mn;
@@ -409,12 +416,14 @@ __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, floa
     atomicAdd(&hist[min(kBins - 1, max(0, (int)((s - r.mn) * r.inv)))], 1u);
   }
   __syncthreads();
+  WI_TP(13);
   // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
-  const int BPT = (kBins + NT - 1) / NT;
+  constexpr int BPT = (kBins + NT - 1) / NT;
   int v = 0;
   for (int j = 0; j < BPT; ++j) { const int bin = kBins - 1 - BPT * tid - j; if (bin >= 0) v += (int)hist[bin]; }
   int tot;
-  int run = block_exclusive_scan(v, iscr, &tot);
+  int run = block_exclusive_scan<NT>(v, iscr, &tot);
+  WI_TP(14);
   if (run < k && k <= run + v) {
     for (int j = 0; j < BPT; ++j) {
       const int bin = kBins - 1 - BPT * tid - j;
@@ -436,22 +445,22 @@ __device__ __forceinline__ int bin_of(const KthBin& kb, uint32_t key) {
 // k-th largest (k >= 1) of the non-zero ones of n score order keys, 0 when fewer than k are
 // non-zero: the histogram bin of the k-th largest, whose keys are then ranked by one wave (a radix
 // select over the keys covers a bin of more than 64).  `bl` holds >= 64 keys.
-template <typename Get>
+template <int NT, typename Get>
 __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint32_t* bl, int* iscr,
                                     float* fred, int* sh_i) {
-  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
-  const KthBin kb = kth_bin(n, k, get, hist, iscr, fred, sh_i);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const KthBin kb = kth_bin<NT>(n, k, get, hist, iscr, fred, sh_i);
+  WI_TP(15);
   if (kb.bin < 0) return 0u;
   const int rem = k - kb.above;
   const int nb = (int)hist[kb.bin];
   if (nb <= 64) {
-    if (tid == 0) sh_i[4] = 0;
-    __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t key = get(i);
       if (key != 0u && bin_of(kb, key) == kb.bin) bl[atomicAdd(&sh_i[4], 1)] = key;
     }
     __syncthreads();
+    WI_TP(16);
     if (wv == 0) {
       const uint32_t key = lane < nb ? bl[lane] : 0u;
       int gt = 0, ge = 0;
@@ -462,7 +471,7 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
     return (uint32_t)sh_i[3];
   }
   int rr;
-  return block_radix_select<uint32_t>(n, k, get, hist, iscr, &rr);
+  return block_radix_select<NT, uint32_t>(n, k, get, hist, iscr, &rr);
 }
 
 // Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
@@ -502,8 +511,8 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
 // or a head whose best clusters crowd a few tiles) t is found by a radix select over all scores
 // and the split by a second pass.  The head's list (ascending id: cluster, first row, first
 // token, score key) and the entry of every attention workgroup's first token are published last.
-template <typename T>
-__global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ uint32_t skey[kSumCap];                 // tile summaries: score keys
   __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
@@ -521,7 +530,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   __shared__ int sh_i[8];
   WI_TP(0);
 
-  const int tid = threadIdx.x, NT = kSelThreads, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / a.G, bg = b * a.Hkv + g;
@@ -581,7 +590,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
   };
 
   bool fast_pub = false;            // the retrieved clusters are all LDS candidates
-  int co[kCandCap / kSelThreads], ce[kCandCap / kSelThreads];
+  int co[kCandCap / NT], ce[kCandCap / NT];
   if (k_eff > 0 && k_eff == n_ne) {
     visit_keys([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
@@ -594,7 +603,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     float thr_f = -INFINITY;
     uint32_t L = 0u;
     if (use_sum) {
-      L = kth_largest_key(nsum, k_eff, [&](int i) { return skey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
+      L = kth_largest_key<NT>(nsum, k_eff, [&](int i) { return skey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
       if (L != 0u) {
         const double thr_d = (double)f32_from_order_key(L) - 2.0 * delta;
         thr_f = (float)thr_d;
@@ -657,7 +666,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     // first rows and sizes of the candidates, fetched now and used when publishing
     if (listed) {
 #pragma unroll
-      for (int j = 0; j < kCandCap / kSelThreads; ++j) {
+      for (int j = 0; j < kCandCap / NT; ++j) {
         const int i = tid + j * NT;
         if (i < n_c) { const int c = cidl[i]; co[j] = a.offsets[(size_t)bg * (C + 1) + c]; ce[j] = a.offsets[(size_t)bg * (C + 1) + c + 1]; }
       }
@@ -669,10 +678,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     if (listed && !scan_all && sh_i[5] == 0 && L != 0u) {
       thr = L;
     } else if (listed) {
-      thr = kth_largest_key(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
+      thr = kth_largest_key<NT>(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
     } else {
       int rr;
-      thr = block_radix_select<uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
+      thr = block_radix_select<NT, uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
     }
     WI_TP(6);
     // ---- in / band / out
@@ -687,7 +696,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     };
     if (listed) for (int i = tid; i < n_c; i += NT) classify(cidl[i], ckey[i]);
     else visit_keys(classify);
-    const int n_in = block_isum(nin, iscr);          // includes a barrier
+    const int n_in = block_isum<NT>(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
     // band list in ascending id order from the band bitmap
     const int perw = (W32 + NT - 1) / NT;
@@ -695,7 +704,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     int nb = 0;
     for (int w = w0; w < w1; ++w) nb += __popc(bbits[w]);
     int n_band;
-    int pos = block_exclusive_scan(nb, iscr, &n_band);
+    int pos = block_exclusive_scan<NT>(nb, iscr, &n_band);
     int32_t* band = n_band <= kSmallBand ? band_lds : a.band_ids + (size_t)bh * C;
     for (int w = w0; w < w1; ++w) {
       uint32_t m = bbits[w];
@@ -725,14 +734,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
         bkey[i] = f64_order_key(canonical_score_row<T>(qd, mu + (size_t)band[i] * kD));
       __syncthreads();
       int rem2;
-      const uint64_t t64 = block_radix_select<uint64_t>(n_band, need, [&](int i) { return bkey[i]; }, hist, iscr, &rem2);
+      const uint64_t t64 = block_radix_select<NT, uint64_t>(n_band, need, [&](int i) { return bkey[i]; }, hist, iscr, &rem2);
       // above the threshold: in; equal to it: the lowest ids (band order) fill the rest
       const int per2 = (n_band + NT - 1) / NT;
       const int i0 = min(n_band, tid * per2), i1 = min(n_band, i0 + per2);
       int neq = 0;
       for (int i = i0; i < i1; ++i) neq += (bkey[i] == t64);
       int tot_eq;
-      int rk = block_exclusive_scan(neq, iscr, &tot_eq);
+      int rk = block_exclusive_scan<NT>(neq, iscr, &tot_eq);
       for (int i = i0; i < i1; ++i) {
         const uint64_t kk = bkey[i];
         bool take = kk > t64;
@@ -757,13 +766,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     int n = 0;
     for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
     int tot;
-    int p = block_exclusive_scan(n, iscr, &tot);
+    int p = block_exclusive_scan<NT>(n, iscr, &tot);
     if (fast_pub) {
       int* wpre = reinterpret_cast<int*>(bbits);      // the band bitmap is no longer needed
       for (int w = w0; w < w1; ++w) { wpre[w] = p; p += __popc(bits[w]); }
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kCandCap / kSelThreads; ++j) {
+      for (int j = 0; j < kCandCap / NT; ++j) {
         const int i = tid + j * NT;
         if (i < sh_i[2]) {
           const int c = cidl[i];
@@ -793,7 +802,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
     if (tot > chunk) {
       int sum = 0;
       for (int i = tid; i < tot; i += NT) { const int c = rl[i]; sum += off[c + 1] - off[c]; }
-      ntok += block_isum(sum, iscr);
+      ntok += block_isum<NT>(sum, iscr);
     }
     int t_run = a.NS;
     for (int base = 0; base < tot; base += chunk) {
@@ -818,7 +827,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(DecodeArgs a) {
         }
       }
       int csum;
-      int t = t_run + block_exclusive_scan(ssum, iscr, &csum);
+      int t = t_run + block_exclusive_scan<NT>(ssum, iscr, &csum);
       WI_TP(11);
       if (tot <= chunk) ntok = (int64_t)a.NS + csum;
 #pragma unroll
@@ -1212,6 +1221,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
 constexpr int kMergeThreads = 512;
 constexpr int kMergeLds = 8192;
 constexpr int kMergeU = 16;
+constexpr int kMergeMdU = 2;   // md pairs per thread loaded in the first round
 
 // out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
 // num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact splits (+1),
@@ -1226,11 +1236,13 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
-  const bool use_est = a.all_sel[bh] == 0;
-  const int PE = use_est ? a.est_tiles_g : 0;
+  // Partials in order: PE estimation tiles, S token workgroups, PC correction workgroups.  All
+  // of them are loaded at once, before the head's all-retrieved flag is known; when it is set
+  // the estimation and correction partials are dead (not used, whatever they hold).
+  const int all_sel = a.all_sel[bh];
+  const int PE = a.est_tiles_g;
   const int S = a.att_split, items = a.att_items;
-  const int PC = use_est ? items - S : 0;
-  const int P = PE + S + PC;
+  const int P = PE + items;
   auto md_of = [&](int p) -> const float* {
     if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
     return a.att_md + ((size_t)bh * items + (p - PE)) * 2;
@@ -1247,28 +1259,53 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     const int p = rep + u * RP;
     v[u] = p < P ? *reinterpret_cast<const float4*>(num_of(p) + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float mx = -INFINITY;
-  for (int p = tid; p < PE + S; p += kMergeThreads) {
-    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
-    if (md.y > 0.f) mx = fmaxf(mx, md.x);
+  float2 md[kMergeMdU];
+#pragma unroll
+  for (int u = 0; u < kMergeMdU; ++u) {
+    const int p = tid + u * kMergeThreads;
+    md[u] = p < P ? *reinterpret_cast<const float2*>(md_of(p)) : make_float2(0.f, 0.f);
   }
-  const float M = block_max(mx, sh_red);
+  const bool use_est = all_sel == 0;
+  auto live = [&](int p, float den) { return den > 0.f && (use_est || (p >= PE && p < PE + S)); };
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMergeMdU; ++u) {
+    const int p = tid + u * kMergeThreads;
+    if (p < PE + S && live(p, md[u].y)) mx = fmaxf(mx, md[u].x);
+  }
+  for (int p = tid + kMergeMdU * kMergeThreads; p < PE + S; p += kMergeThreads) {
+    const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
+    if (live(p, m2.y)) mx = fmaxf(mx, m2.x);
+  }
+  const float M = block_max<kMergeThreads>(mx, sh_red);
+  // merge factor of a live partial, negated for the corrections; 0 for a dead one
+  auto factor_of = [&](int p, float2 m2) -> float {
+    if (!live(p, m2.y)) return 0.f;
+    const float f = __expf(m2.x - M);
+    return p >= PE + S ? -f : f;
+  };
   const bool f_lds = P <= kMergeLds;
   float dn = 0.f;
-  for (int p = tid; p < P; p += kMergeThreads) {
-    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
-    float f = md.y > 0.f ? __expf(md.x - M) : 0.f;
-    if (p >= PE + S) f = -f;
-    if (f_lds) sh_f[p] = f;
-    dn += f * md.y;
+#pragma unroll
+  for (int u = 0; u < kMergeMdU; ++u) {
+    const int p = tid + u * kMergeThreads;
+    if (p < P) {
+      const float f = factor_of(p, md[u]);
+      if (f_lds) sh_f[p] = f;
+      if (f != 0.f) dn += f * md[u].y;
+    }
   }
-  const float den = block_sum(dn, sh_red);
+  for (int p = tid + kMergeMdU * kMergeThreads; p < P; p += kMergeThreads) {
+    const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
+    const float f = factor_of(p, m2);
+    if (f_lds) sh_f[p] = f;
+    if (f != 0.f) dn += f * m2.y;
+  }
+  const float den = block_sum<kMergeThreads>(dn, sh_red);
   __syncthreads();
   auto factor = [&](int p) -> float {
     if (f_lds) return sh_f[p];
-    const float2 md = *reinterpret_cast<const float2*>(md_of(p));
-    const float f = md.y > 0.f ? __expf(md.x - M) : 0.f;
-    return p >= PE + S ? -f : f;
+    return factor_of(p, *reinterpret_cast<const float2*>(md_of(p)));
   };
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1276,7 +1313,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     const int p = rep + u * RP;
     if (p < P) {
       const float f = factor(p);
-      acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+      if (f != 0.f) { acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w; }
     }
   }
   for (int p0 = rep + kMergeU * RP; p0 < P; p0 += kMergeU * RP) {
@@ -1290,7 +1327,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
       const int p = p0 + u * RP;
       if (p < P) {
         const float f = factor(p);
-        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+        if (f != 0.f) { acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w; }
       }
     }
   }
@@ -1322,7 +1359,10 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
   for (int r = 0; r < prof_reps(); ++r) {
-    hipLaunchKernelGGL(k_select<T>, dim3(BH), dim3(kSelThreads), (size_t)a.W32 * 8, s, a);
+    if (BH > kSelHeadsPerRound)
+      hipLaunchKernelGGL((k_select<T, kSelThreadsMany>), dim3(BH), dim3(kSelThreadsMany), (size_t)a.W32 * 8, s, a);
+    else
+      hipLaunchKernelGGL((k_select<T, kSelThreadsFew>), dim3(BH), dim3(kSelThreadsFew), (size_t)a.W32 * 8, s, a);
   }
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1355,12 +1395,14 @@ hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStre
   static bool attr_set = false;
   if (!attr_set) {
     // the select kernel's two cluster bitmaps (2 * ceil(C / 32) words) live in dynamic LDS
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<float>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<uint16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
-    if (e != hipSuccess) return e;
+    const void* fns[4] = {reinterpret_cast<const void*>(k_select<float, kSelThreadsFew>),
+                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);

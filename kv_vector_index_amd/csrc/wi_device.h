@@ -148,51 +148,65 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v + (row >= 1 ? s1 : 0) + (row >= 2 ? s2 : 0) + (row >= 3 ? s3 : 0);
 }
 
-// Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).  `scratch` holds
-// >= 17 ints of LDS.  Returns this thread's exclusive prefix; *total receives the block sum.
+// Block-wide scans and reductions over NT threads (a multiple of 64, <= 1024; NT is the launch
+// block size, a compile-time constant so that no work-group size is read at run time).  `scratch`
+// holds >= NT / 64 entries of LDS; every thread reads all per-wave partials itself.
+
+// Exclusive prefix sum: returns this thread's exclusive prefix; *total receives the block sum.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int inc = wave_inclusive_scan(v);
   if (lane == 63) scratch[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) { const int t = scratch[i]; scratch[i] = run; run += t; }
-    scratch[16] = run;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < nw; ++i) {
+    const int t = scratch[i];
+    before += i < w ? t : 0;
+    tot += t;
   }
+  *total = tot;
   __syncthreads();
-  const int res = scratch[w] + inc - v;
-  *total = scratch[16];
-  __syncthreads();
-  return res;
+  return before + inc - v;
 }
 
+template <int NT>
 __device__ __forceinline__ float block_max(float v, float* scratch) {
+  constexpr int nw = NT / 64;
   v = wave_max(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) scratch[w] = v;
   __syncthreads();
   float r = scratch[0];
+#pragma unroll
   for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
   __syncthreads();
   return r;
 }
+template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
+  constexpr int nw = NT / 64;
   v = wave_sum(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) scratch[w] = v;
   __syncthreads();
   float r = 0.f;
+#pragma unroll
   for (int i = 0; i < nw; ++i) r += scratch[i];
   __syncthreads();
   return r;
 }
+template <int NT>
 __device__ __forceinline__ int block_isum(int v, int* scratch) {
+  constexpr int nw = NT / 64;
   v = wave_isum(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) scratch[w] = v;
   __syncthreads();
   int r = 0;
+#pragma unroll
   for (int i = 0; i < nw; ++i) r += scratch[i];
   __syncthreads();
   return r;

@@ -7,6 +7,8 @@ more than 256 tiles need a full scan, or when the summaries themselves do not fi
 below forces one of those branches; all are checked against the oracle to the same gates as the
 other decode tests (ids bit-exact, outputs to the dtype tolerance).
 
+The last two cases run more than 256 query heads, where the select runs at half the block size.
+
 Indexes come from oracle.finalize_index on random labels (no k-means), so that cluster counts,
 empty clusters and crowding can be chosen directly.
 """
@@ -116,3 +118,17 @@ def test_select_crowded_heads_with_all_retrieved_neighbour():
                          crowd_heads=2)
     _check(idx, Qt, Q64, Hq=8, k=30, dtype="bf16")
     _check(idx, Qt, Q64, Hq=8, k=256, dtype="bf16")
+
+
+def test_select_half_size_blocks_crowded_and_empty():
+    # 272 query heads: the select runs two heads per CU at 512 threads; crowded first tiles for
+    # two heads of every group, 10% empty clusters
+    idx, Qt, Q64 = _case(C=1024, tokens_per_cluster=3, Hq=272, Hkv=34, dtype="bf16", seed=8, crowd=40,
+                         crowd_heads=2)
+    _check(idx, Qt, Q64, Hq=272, k=50, dtype="bf16")
+
+
+def test_select_half_size_blocks_radix_fallback():
+    # 264 query heads with more candidates than the LDS list holds (radix select over all scores)
+    idx, Qt, Q64 = _case(C=4096, tokens_per_cluster=1, Hq=264, Hkv=33, dtype="f32", seed=9)
+    _check(idx, Qt, Q64, Hq=264, k=2500, dtype="f32")
