@@ -50,9 +50,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   WI_TP(30);
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
-  __shared__ float sh_n[kEstTile];          // cluster sizes
+  __shared__ float sh_n[kScoreThreads];     // cluster sizes (entries >= nrows are 0)
+  __shared__ float sh_nrm[kEstTile];        // centroid norms
   __shared__ uint32_t sh_k[G][kEstTile];    // order keys of the raw scores, 0 for empty clusters
-  __shared__ float sh_m[G], sh_den[G], sh_nm[4];
+  __shared__ float sh_m[G], sh_den[G];
   __shared__ float sh_num[G <= 4 ? 1 : 4][G][kD];          // G > 4: per-wave numerators
   __shared__ __attribute__((aligned(16))) float sh_part[G <= 4 ? 16 : 1][G][kD];  // G <= 4: per lane group
   const int tile = blockIdx.x, bg = blockIdx.y;
@@ -68,54 +69,60 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
 
-  // Every global load of the tile is issued before the first wait: the value sums (lane (lr, lg)
-  // of wave w owns rows w*32 + 4i + lg and dims [8 lr, 8 lr + 8)), the sizes, the queries and
-  // the centroids, so the tile costs one memory round trip.
+  // Every global load of the tile is issued before the first wait: the sizes, the centroids and
+  // the queries, then the value sums (lane (lr, lg) of wave w owns rows w*32 + 4i + lg and dims
+  // [8 lr, 8 lr + 8)), so the tile costs one memory round trip and the scores, keys and
+  // summaries are computed while the value sums are still arriving.  The loads are unconditional
+  // (row indices clamped into the tile, query rows into the group) so that the wait before the
+  // first MFMA counts only the loads issued ahead of it; rows past the tile get weight 0 and
+  // query rows past the group are never read back.  Empty clusters are masked by their size in
+  // the per-head pass.
+  const int n_raw = szs[tile * kEstTile + min(tid, nrows - 1)];
   u32x4_t svr[8];
   [[maybe_unused]] u32x4_t svr_hi[8];
+  auto load_sv = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 32 + 4 * i + lg;
-    svr[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (sizeof(T) == 4) svr_hi[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (r < nrows) {
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(w * 32 + 4 * i + lg, nrows - 1);
       const T* p = sv + (size_t)r * kD + 8 * lr;
       svr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
       if constexpr (sizeof(T) == 4) svr_hi[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
     }
-  }
-  const int n_own = (tid < nrows) ? szs[tile * kEstTile + tid] : 0;   // sh_n, stored later
-  float nmax = 0.f;                 // largest centroid norm among the tile's non-empty clusters
+  };
+  // raw score of query head h (row h of the MFMA tile) against cluster row cl, and the norm of
+  // that centroid
+  auto put_scores = [&](const f32x4_t& acc, float n2, int t) {
+    const int cl = w * 32 + 16 * t + lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * lg + r;
+      if (h < G) {
+        sh_s[h][cl] = acc[r];
+        sh_k[h][cl] = f32_order_key(acc[r]);
+      }
+    }
+    if (lg == 0) sh_nrm[cl] = sqrtf(n2);
+  };
 
   if constexpr (sizeof(T) == 2) {
     // A = query heads (row = lane&15), B = centroids (column = lane&15).  MFMA step s consumes
     // dims 32 s + 8 lg .. +8 on both operands, so the four lanes of a row read 64 contiguous bytes.
     bf16x8_t qa[4];
     bf16x8_t mb[2][4];
-    int sz[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int c = cbase + 16 * t + lr;
-      sz[t] = 0;
-      if (c < C) {
-        sz[t] = szs[c];
-        const T* row = mu + (size_t)c * kD + 8 * lg;
+      const T* row = mu + (size_t)min(cbase + 16 * t + lr, C - 1) * kD + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(row + 32 * s));
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) mb[t][s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(row + 32 * s));
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (lr < G) qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)lr * kD + 32 * s + 8 * lg);
-      else qa[s] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int s = 0; s < 4; ++s)
+      qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)min(lr, G - 1) * kD + 32 * s + 8 * lg);
+    load_sv();
+    __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
     WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int c = cbase + 16 * t + lr;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], mb[t][s], acc, 0, 0, 0);
@@ -126,49 +133,30 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
         for (int e = 0; e < 8; ++e) { const float x = (float)mb[t][s][e]; n2 += x * x; }
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
-      const int cl = w * 32 + 16 * t + lr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * lg + r;
-        if (h < G) {
-          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
-          sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
-          sh_k[h][cl] = (c < C && sz[t] > 0) ? f32_order_key(acc[r]) : 0u;
-        }
-      }
-      if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
+      put_scores(acc, n2, t);
     }
   } else {
     // fp32: 16x16x4 MFMA, 32 steps; lane (lr, lg) loads dims 16 j + 4 lg .. +4 (j = 0..7) and step
     // 4 j + e consumes dim 16 j + 4 lg + e on both operands.
     u32x4_t mraw[2][8];
-    int sz[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int c = cbase + 16 * t + lr;
-      sz[t] = 0;
-      if (c < C) {
-        sz[t] = szs[c];
-        const float* row = reinterpret_cast<const float*>(mu) + (size_t)c * kD + 4 * lg;
+      const float* row = reinterpret_cast<const float*>(mu) + (size_t)min(cbase + 16 * t + lr, C - 1) * kD + 4 * lg;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mraw[t][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 16 * j));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mraw[t][j] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < 8; ++j) mraw[t][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 16 * j));
     }
     float qa[32];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (lr < G) v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(qg) + (size_t)lr * kD + 16 * j + 4 * lg);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(qg) + (size_t)min(lr, G - 1) * kD + 16 * j + 4 * lg);
       qa[4 * j] = __uint_as_float(v.x); qa[4 * j + 1] = __uint_as_float(v.y);
       qa[4 * j + 2] = __uint_as_float(v.z); qa[4 * j + 3] = __uint_as_float(v.w);
     }
+    load_sv();
+    __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
     WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int c = cbase + 16 * t + lr;
       float mb[32];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -183,28 +171,31 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       for (int s = 0; s < 32; ++s) n2 += mb[s] * mb[s];
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
-      const int cl = w * 32 + 16 * t + lr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * lg + r;
-        if (h < G) {
-          if (c < C) a.keys[((size_t)b * a.Hq + (size_t)g * G + h) * C + c] = sz[t] > 0 ? f32_order_key(acc[r]) : 0u;
-          sh_s[h][cl] = (c < C && sz[t] > 0) ? acc[r] * a.scale : -INFINITY;
-          sh_k[h][cl] = (c < C && sz[t] > 0) ? f32_order_key(acc[r]) : 0u;
-        }
-      }
-      if (c < C && sz[t] > 0) nmax = fmaxf(nmax, sqrtf(n2));
+      put_scores(acc, n2, t);
     }
   }
-  if (tid < kEstTile) sh_n[tid] = (float)n_own;
+  sh_n[tid] = tid < nrows ? (float)n_raw : 0.f;
   __syncthreads();
   WI_TP(32);
 
-  nmax = wave_max(nmax);
-  if (lane == 0) sh_nm[w] = nmax;
-  // estimation partial of the tile: m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
+  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
+  if (w == 0) {
+    // largest norm among the tile's non-empty centroids, and how many are non-empty
+    const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
+    const float nm = wave_max(fmaxf(e0 ? sh_nrm[lane] : 0.f, e1 ? sh_nrm[lane + 64] : 0.f));
+    const int nc = __popcll(__ballot(e0)) + __popcll(__ballot(e1));
+    if (lane == 0) { a.tile_norm[slot] = nm; a.tile_cnt[slot] = nc; }
+  }
+  // per head: the raw-score keys (0 for empty clusters), then the estimation partial of the tile:
+  // m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
   for (int h = w; h < G; h += kScoreThreads / 64) {
-    const float x0 = sh_s[h][lane], x1 = sh_s[h][lane + 64];
+    const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
+    const uint32_t k0 = e0 ? sh_k[h][lane] : 0u, k1 = e1 ? sh_k[h][lane + 64] : 0u;
+    uint32_t* keys_h = a.keys + ((size_t)b * a.Hq + (size_t)g * G + h) * C + (size_t)tile * kEstTile;
+    if (lane < nrows) keys_h[lane] = k0;
+    if (lane + 64 < nrows) keys_h[lane + 64] = k1;
+    const float x0 = e0 ? sh_s[h][lane] * a.scale : -INFINITY;
+    const float x1 = e1 ? sh_s[h][lane + 64] * a.scale : -INFINITY;
     const float m = wave_max(fmaxf(x0, x1));
     const float w0 = x0 == -INFINITY ? 0.f : __expf(x0 - m);
     const float w1 = x1 == -INFINITY ? 0.f : __expf(x1 - m);
@@ -215,20 +206,20 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     // the head's 8 best scores of the tile (key 0 past the non-empty clusters) with their cluster
     // ids: lane r keeps the r-th, found by repeated wave maxima, each time clearing the holder
     // with the lowest id
-    uint32_t k0 = sh_k[h][lane], k1 = sh_k[h][lane + 64], best = 0u;
+    uint32_t c0 = k0, c1 = k1, best = 0u;
     int best_id = 0;
 #pragma unroll
     for (int r = 0; r < kTileTop; ++r) {
-      const uint32_t m8 = wave_umax(k0 > k1 ? k0 : k1);
-      const uint64_t b0 = __ballot(k0 == m8);
+      const uint32_t m8 = wave_umax(c0 > c1 ? c0 : c1);
+      const uint64_t b0 = __ballot(c0 == m8);
       int holder;
       if (b0 != 0ull) {
         holder = __ffsll((unsigned long long)b0) - 1;
-        if (lane == holder) k0 = 0u;
+        if (lane == holder) c0 = 0u;
       } else {
-        const uint64_t b1 = __ballot(k1 == m8);
+        const uint64_t b1 = __ballot(c1 == m8);
         holder = __ffsll((unsigned long long)b1) - 1 + 64;
-        if (lane == holder - 64) k1 = 0u;
+        if (lane == holder - 64) c1 = 0u;
       }
       if (lane == r) { best = m8; best_id = tile * kEstTile + holder; }
     }
@@ -237,10 +228,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       a.tile_top[ti] = best;
       a.tile_top_id[ti] = best_id;
     }
-  }
-  if (w == 0) {
-    const int nc = __popcll(__ballot(sh_n[lane] > 0.f)) + __popcll(__ballot(sh_n[lane + 64] > 0.f));
-    if (lane == 0) a.tile_cnt[(size_t)bg * a.est_tiles_g + tile] = nc;
   }
   __syncthreads();
   float acc[G][8];
@@ -272,7 +259,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     }
   }
   // sum over the 16 lane groups of the block (4 waves x 4 row groups) that hold the same dims
-  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
   if constexpr (G <= 4) {
     // every lane group writes its partial numerators to LDS; 16-way sums read them back
 #pragma unroll
@@ -313,7 +299,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
     a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
   }
-  if (tid == 0) a.tile_norm[slot] = fmaxf(fmaxf(sh_nm[0], sh_nm[1]), fmaxf(sh_nm[2], sh_nm[3]));
 }
 
 // ============================================================================ k_select
