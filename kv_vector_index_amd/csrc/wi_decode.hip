@@ -17,15 +17,16 @@
 //
 // Kernels (one stream, in order):
 //   k_score_est  grid (ceil(C/128), B*Hkv): MFMA scores of the KV group's query heads against 128
-//                centroids (one pass over mu serves all heads of the group), fp32 centroid norms,
-//                and the tile's estimation partial per head from SV and the sizes.
-//   k_select     grid (B*Hq): exact top-k per head (histogram threshold on the fp32 scores,
-//                canonical fp64 re-scoring of the certified uncertainty band, ties to the lower
-//                id).  The last head of each KV group to finish builds the group's work list.
-//   k_attend     grid (S + Sc, B*Hkv): S workgroups per KV group split its token list (steady
-//                zone, then the union of the rows its heads retrieved, each row loaded once for
-//                all heads that want it) with an online softmax; Sc workgroups fold the retrieved
-//                clusters' estimation terms.
+//                centroids (one pass over mu serves all heads of the group), the score keys, the
+//                tile's 8 best keys per head, fp32 centroid norms, and the tile's estimation
+//                partial per head from SV and the sizes.
+//   k_select     grid (B*Hq): exact top-k per head (a threshold bounded from the tile summaries
+//                and found on the fp32 scores, canonical fp64 re-scoring of the certified
+//                uncertainty band, ties to the lower id), published as the head's ascending list
+//                of clusters with their first rows and token offsets.
+//   k_attend     grid (B*Hq * (S + Sc)): S workgroups per head split its token list (steady zone,
+//                then the rows of its retrieved clusters) with an online softmax; Sc workgroups
+//                fold the retrieved clusters' estimation terms.
 //   k_merge      grid (B*Hq): log-sum-exp merge of the head's partials into out and lse.
 #include "wi_device.h"
 #include "wi_internal.h"
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       a.tile_top_id[ti] = best_id;
     }
   }
+  WI_TP(33);
   __syncthreads();
   float acc[G][8];
 #pragma unroll
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   if (tid < G) {
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
     a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
-  }
+  }  WI_TP(34);
 }
 
 // ============================================================================ k_select
