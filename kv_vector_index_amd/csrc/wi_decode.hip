@@ -1205,20 +1205,24 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
 }
 
 // ============================================================================ k_merge
-constexpr int kMergeThreads = 512;
+// Block size of the merge: 512 threads, or 1024 when every head has a CU to itself and has more
+// partials than 512 threads fetch in one round.  Each thread keeps kMergeU numerator columns in
+// flight (12 fits either size without spills).
+constexpr int kMergeThreadsFew = 1024, kMergeThreadsMany = 512;
 constexpr int kMergeLds = 8192;
-constexpr int kMergeU = 16;
-constexpr int kMergeMdU = 2;   // md pairs per thread loaded in the first round
+constexpr int kMergeU = 12;
 
 // out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
 // num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact splits (+1),
 // retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
 // only its exact splits.  The first batch of numerators is fetched before the maximum is known.
-__global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
+  constexpr int kMergeMdU = NT >= 1024 ? 1 : 2;   // md pairs per thread loaded in the first round
   WI_TP(40);
   __shared__ float sh_f[kMergeLds];
   __shared__ float sh_red[32];
-  __shared__ float4 sh_acc[kMergeThreads / 32][32];
+  __shared__ float4 sh_acc[NT / 32][32];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
@@ -1234,37 +1238,35 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
     if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
     return a.att_md + ((size_t)bh * items + (p - PE)) * 2;
   };
-  auto num_of = [&](int p) -> const float* {
-    if (p < PE) return a.est_num + (((size_t)bg * a.est_tiles_g + p) * G + hi) * kD;
-    return a.att_num + ((size_t)bh * items + (p - PE)) * kD;
-  };
   const int col = tid & 31, rep = tid >> 5;
-  constexpr int RP = kMergeThreads / 32;
+  constexpr int RP = NT / 32;
+  // numerator columns [4 col, 4 col + 4) of partial p; past P the last partial is read and unused
+  const float* est_col = a.est_num + ((size_t)bg * a.est_tiles_g * G + hi) * kD + 4 * col;
+  const float* att_col = a.att_num + (size_t)bh * items * kD + 4 * col;
+  auto num_col = [&](int p) -> float4 {
+    p = min(p, P - 1);
+    const float* q = p < PE ? est_col + (size_t)p * G * kD : att_col + (size_t)(p - PE) * kD;
+    return *reinterpret_cast<const float4*>(q);
+  };
   float4 v[kMergeU];
 #pragma unroll
-  for (int u = 0; u < kMergeU; ++u) {
-    const int p = rep + u * RP;
-    v[u] = p < P ? *reinterpret_cast<const float4*>(num_of(p) + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int u = 0; u < kMergeU; ++u) v[u] = num_col(rep + u * RP);
   float2 md[kMergeMdU];
 #pragma unroll
-  for (int u = 0; u < kMergeMdU; ++u) {
-    const int p = tid + u * kMergeThreads;
-    md[u] = p < P ? *reinterpret_cast<const float2*>(md_of(p)) : make_float2(0.f, 0.f);
-  }
+  for (int u = 0; u < kMergeMdU; ++u) md[u] = *reinterpret_cast<const float2*>(md_of(min(tid + u * NT, P - 1)));
   const bool use_est = all_sel == 0;
   auto live = [&](int p, float den) { return den > 0.f && (use_est || (p >= PE && p < PE + S)); };
   float mx = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kMergeMdU; ++u) {
-    const int p = tid + u * kMergeThreads;
+    const int p = tid + u * NT;
     if (p < PE + S && live(p, md[u].y)) mx = fmaxf(mx, md[u].x);
   }
-  for (int p = tid + kMergeMdU * kMergeThreads; p < PE + S; p += kMergeThreads) {
+  for (int p = tid + kMergeMdU * NT; p < PE + S; p += NT) {
     const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
     if (live(p, m2.y)) mx = fmaxf(mx, m2.x);
   }
-  const float M = block_max<kMergeThreads>(mx, sh_red);
+  const float M = block_max<NT>(mx, sh_red);
   // merge factor of a live partial, negated for the corrections; 0 for a dead one
   auto factor_of = [&](int p, float2 m2) -> float {
     if (!live(p, m2.y)) return 0.f;
@@ -1275,20 +1277,20 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   float dn = 0.f;
 #pragma unroll
   for (int u = 0; u < kMergeMdU; ++u) {
-    const int p = tid + u * kMergeThreads;
+    const int p = tid + u * NT;
     if (p < P) {
       const float f = factor_of(p, md[u]);
       if (f_lds) sh_f[p] = f;
       if (f != 0.f) dn += f * md[u].y;
     }
   }
-  for (int p = tid + kMergeMdU * kMergeThreads; p < P; p += kMergeThreads) {
+  for (int p = tid + kMergeMdU * NT; p < P; p += NT) {
     const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
     const float f = factor_of(p, m2);
     if (f_lds) sh_f[p] = f;
     if (f != 0.f) dn += f * m2.y;
   }
-  const float den = block_sum<kMergeThreads>(dn, sh_red);
+  const float den = block_sum<NT>(dn, sh_red);
   __syncthreads();
   auto factor = [&](int p) -> float {
     if (f_lds) return sh_f[p];
@@ -1305,10 +1307,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
   }
   for (int p0 = rep + kMergeU * RP; p0 < P; p0 += kMergeU * RP) {
 #pragma unroll
-    for (int u = 0; u < kMergeU; ++u) {
-      const int p = p0 + u * RP;
-      v[u] = p < P ? *reinterpret_cast<const float4*>(num_of(p) + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int u = 0; u < kMergeU; ++u) v[u] = num_col(p0 + u * RP);
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u) {
       const int p = p0 + u * RP;
@@ -1336,6 +1335,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeArgs a) {
 template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
+  const bool merge_big = BH <= kSelHeadsPerRound &&
+                         a.est_tiles_g + a.att_items > (kMergeThreadsMany / 32) * kMergeU;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
   // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent)
@@ -1361,7 +1362,8 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
   for (int r = 0; r < prof_reps(); ++r) {
-    hipLaunchKernelGGL(k_merge, dim3(BH), dim3(kMergeThreads), 0, s, a);
+    if (merge_big) hipLaunchKernelGGL(k_merge<kMergeThreadsFew>, dim3(BH), dim3(kMergeThreadsFew), 0, s, a);
+    else hipLaunchKernelGGL(k_merge<kMergeThreadsMany>, dim3(BH), dim3(kMergeThreadsMany), 0, s, a);
   }
   prof_end(WI_STAGE_MERGE, s);
   return hipGetLastError();
