@@ -114,7 +114,6 @@ BuildLayout build_layout(const wi_build_params& p) {
   size_t o = 0;
   L.off_mhat = o;      o = align256(o + (size_t)BG * d.C * kD * e);
   L.off_assign = o;    o = align256(o + (size_t)BG * d.Nc * 4);
-  L.off_knorm = o;     o = align256(o + (size_t)BG * d.Nc * 4);
   L.off_flag_cnt = o;  o = align256(o + (size_t)p.iters * 4);
   L.off_flag_list = o; o = align256(o + (size_t)BG * d.Nc * 4);
   L.total = o;

@@ -40,7 +40,6 @@ struct BuildArgs {
   void* vs;
   void* mhat;         // [BG, C, d] centroid directions (workspace)
   int32_t* assign;    // [BG, Nc] local cluster id per clustered token
-  float* knorm;       // [BG, Nc]
   uint32_t* flag_cnt; // [iters]
   int32_t* flag_list; // [BG * Nc]
   int Hkv, N, sink, window, NS, lo, Nc, L, nseg, Cs, C, BG, iters;
@@ -61,22 +60,12 @@ __global__ __launch_bounds__(256) void k_prep(BuildArgs a) {
   const T* V = static_cast<const T*>(a.v) + (size_t)bg * a.N * kD;
   T* ks = static_cast<T*>(a.ks) + (size_t)bg * a.NS * kD;
   T* vs = static_cast<T*>(a.vs) + (size_t)bg * a.NS * kD;
-  const int rows = a.NS + a.Nc;
-  for (int r = blockIdx.x * 4 + w; r < rows; r += gridDim.x * 4) {
-    if (r < a.NS) {
-      // steady row r -> position: the first `sink` positions, then the last `window`
-      const int pos = (a.NS == a.N) ? r : (r < a.sink ? r : a.N - a.window + (r - a.sink));
-      for (int j = lane; j < kD; j += 64) {
-        ks[(size_t)r * kD + j] = K[(size_t)pos * kD + j];
-        vs[(size_t)r * kD + j] = V[(size_t)pos * kD + j];
-      }
-    } else {
-      const int i = r - a.NS;
-      const T* row = K + (size_t)(a.lo + i) * kD;
-      float s = 0.f;
-      for (int j = lane; j < kD; j += 64) { const float x = St<T>::f(row[j]); s += x * x; }
-      s = wave_sum(s);
-      if (lane == 0) a.knorm[(size_t)bg * a.Nc + i] = sqrtf(s);
+  for (int r = blockIdx.x * 4 + w; r < a.NS; r += gridDim.x * 4) {
+    // steady row r -> position: the first `sink` positions, then the last `window`
+    const int pos = (a.NS == a.N) ? r : (r < a.sink ? r : a.N - a.window + (r - a.sink));
+    for (int j = lane; j < kD; j += 64) {
+      ks[(size_t)r * kD + j] = K[(size_t)pos * kD + j];
+      vs[(size_t)r * kD + j] = V[(size_t)pos * kD + j];
     }
   }
 }
@@ -264,21 +253,18 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   constexpr int KE = sizeof(T) == 2 ? 4 : 32;      // bf16: 4 x 8 elements; fp32: 32 elements
   typedef typename std::conditional<sizeof(T) == 2, bf16x8_t, float>::type KElem;
   KElem kb[4][KE];
+  // keys past the segment read its last key (in bounds) and are never written back
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const int i = key0 + w * 64 + kt * 16 + lr;
+    const int i = min(key0 + w * 64 + kt * 16 + lr, n_s - 1);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (i < n_s) kb[kt][st] = *reinterpret_cast<const bf16x8_t*>(K + (size_t)i * kD + 32 * lg + 8 * st);
-        else kb[kt][st] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int st = 0; st < 4; ++st) kb[kt][st] = *reinterpret_cast<const bf16x8_t*>(K + (size_t)i * kD + 32 * lg + 8 * st);
     } else {
 #pragma unroll
       for (int st = 0; st < 32; st += 8) {
         float tmp[8];
-        if (i < n_s) St<float>::load8(reinterpret_cast<const float*>(K) + (size_t)i * kD + 32 * lg + st, tmp);
-        else for (int e = 0; e < 8; ++e) tmp[e] = 0.f;
+        St<float>::load8(reinterpret_cast<const float*>(K) + (size_t)i * kD + 32 * lg + st, tmp);
 #pragma unroll
         for (int e = 0; e < 8; ++e) kb[kt][st + e] = tmp[e];
       }
@@ -336,16 +322,28 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     }
   }
 
-  // key norms for the error bound, loaded while the winners are recomputed
-  float knorm[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int i = key0 + w * 64 + kt * 16 + lr;
-    knorm[kt] = (lg == 0 && i < n_s) ? a.knorm[(size_t)bg * a.Nc + (size_t)s * a.L + i] : 0.f;
-  }
   // combine the four lane groups holding disjoint centroid subsets of the same key
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) { best2_merge_xor(tk[kt], 16); best2_merge_xor(tk[kt], 32); }
+  // key norms for the error bound, from the key rows in registers (fp32 sum of the 128 exact
+  // squares; its relative error, under 128 * 2^-24, is covered by the 2^-10 inflation below)
+  float knorm[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    float q = 0.f;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float x = (float)kb[kt][st][e]; q += x * x; }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) q += kb[kt][e] * kb[kt][e];
+    }
+    q += __shfl_xor(q, 16);
+    q += __shfl_xor(q, 32);
+    knorm[kt] = sqrtf(q);
+  }
 
   // the winning group's four scores, recomputed on the vector units (each lane its 32 dims, then
   // summed over the four lane groups), name the best centroid; certify it against the best of
@@ -636,8 +634,7 @@ template <typename T>
 static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   const int BG = a.BG;
   {
-    const int rows = a.NS + a.Nc;
-    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(rows, 4), 4096));
+    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(a.NS, 4), 4096));
     prof_begin(WI_STAGE_PREP, st);
     hipLaunchKernelGGL(k_prep<T>, dim3(gx, BG), dim3(256), 0, st, a);
     prof_end(WI_STAGE_PREP, st);
@@ -714,7 +711,6 @@ hipError_t launch_build(const wi_build_params& p, const BuildLayout& L, const vo
   char* base = static_cast<char*>(ws);
   a.mhat = base + L.off_mhat;
   a.assign = reinterpret_cast<int32_t*>(base + L.off_assign);
-  a.knorm = reinterpret_cast<float*>(base + L.off_knorm);
   a.flag_cnt = reinterpret_cast<uint32_t*>(base + L.off_flag_cnt);
   a.flag_list = reinterpret_cast<int32_t*>(base + L.off_flag_list);
   a.Hkv = p.Hkv; a.N = p.N; a.sink = p.sink; a.window = p.window;

@@ -88,7 +88,7 @@ inline void prof_end(int stage, hipStream_t s) { if (g_prof_on) prof_record(stag
 // ------------------------------------------------------------------ build workspace
 struct BuildLayout {
   int64_t C, Nc, NS, nseg, L;
-  size_t off_mhat, off_assign, off_knorm, off_flag_cnt, off_flag_list, total;
+  size_t off_mhat, off_assign, off_flag_cnt, off_flag_list, total;
 };
 BuildLayout build_layout(const wi_build_params& p);
 
