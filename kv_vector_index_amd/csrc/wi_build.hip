@@ -280,20 +280,20 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
       __syncthreads();
     }
     const int nct = ch16 / 16;
-    for (int ct = 0; ct < nct; ++ct) {
+    // one 16-centroid tile: every tile but a ragged last one takes the unmasked path
+    auto tile = [&](int ct, bool ragged) {
       const int grp = (c0 + ct * 16) / 4 + lg;
-      const bool ragged = c0 + ct * 16 + 16 > cs_eff;
       f32x4_t acc[4];
       if constexpr (sizeof(T) == 2) {
-        bf16x8_t ca[4];
+        // one 32-dim slice of the 16 centroid rows at a time, against the four key tiles
         const unsigned char* rp = clds + (ct * 16 + lr) * STR + 64 * lg;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) ca[st] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * st);
+        for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8_t ca = *reinterpret_cast<const bf16x8_t*>(rp + 16 * st);
 #pragma unroll
-          for (int st = 0; st < 4; ++st) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[st], kb[kt][st], acc[kt], 0, 0, 0);
+          for (int kt = 0; kt < 4; ++kt) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca, kb[kt][st], acc[kt], 0, 0, 0);
         }
       } else {
         const float* rp = reinterpret_cast<const float*>(clds + (ct * 16 + lr) * STR) + 32 * lg;
@@ -319,35 +319,39 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
         }
         best2_fold4(tk[kt], v[0], v[1], v[2], v[3], grp);
       }
-    }
+    };
+    const int nfull = (c0 + ch16 <= cs_eff) ? nct : nct - 1;
+    for (int ct = 0; ct < nfull; ++ct) tile(ct, false);
+    if (nfull < nct) tile(nct - 1, true);
   }
 
   // combine the four lane groups holding disjoint centroid subsets of the same key
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) { best2_merge_xor(tk[kt], 16); best2_merge_xor(tk[kt], 32); }
-  // key norms for the error bound, from the key rows in registers (fp32 sum of the 128 exact
-  // squares; its relative error, under 128 * 2^-24, is covered by the 2^-10 inflation below)
-  float knorm[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    float q = 0.f;
+  // key norms for the error bound: the diagonal of K K^T for each 16-key tile, on the matrix
+  // cores from the key registers (fp32 sums of the exact squares; their relative error, under
+  // 128 * 2^-24, is covered by the 2^-10 inflation below).  D[i][i] sits in lane i + 16 (i / 4),
+  // component i % 4.
+  auto diag_of = [&](const f32x4_t& dd) -> float {
+    const float dg = (lr & 3) == 0 ? dd[0] : (lr & 3) == 1 ? dd[1] : (lr & 3) == 2 ? dd[2] : dd[3];
+    return __shfl(dg, lr + 16 * (lr >> 2));
+  };
+  auto knorm_of = [&](int kt) -> float {
+    f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { const float x = (float)kb[kt][st][e]; q += x * x; }
+      for (int st = 0; st < 4; ++st) dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kt][st], kb[kt][st], dd, 0, 0, 0);
     } else {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) q += kb[kt][e] * kb[kt][e];
+      for (int e = 0; e < 32; ++e) dd = __builtin_amdgcn_mfma_f32_16x16x4f32(kb[kt][e], kb[kt][e], dd, 0, 0, 0);
     }
-    q += __shfl_xor(q, 16);
-    q += __shfl_xor(q, 32);
-    knorm[kt] = sqrtf(q);
-  }
+    return sqrtf(diag_of(dd));
+  };
 
-  // the winning group's four scores, recomputed on the vector units (each lane its 32 dims, then
-  // summed over the four lane groups), name the best centroid; certify it against the best of
-  // the rest: the group's other three and the exact second-best fp32 score overall
+  // the winning group's four scores, recomputed (bf16 with resident centroids: on the matrix
+  // cores; otherwise on the vector units, each lane its 32 dims, then summed over the four lane
+  // groups), name the best centroid; certify it against the best of the rest: the group's other
+  // three and the exact second-best fp32 score overall
   int flagged[4];
   // lane's 32-dim part of <key of tile kt, centroid c>; rows from LDS when resident, else global
   auto part_dot = [&](int kt, int c) -> float {
@@ -392,15 +396,30 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   for (int kt = 0; kt < 4; ++kt) {
     const int grp = tk[kt].grp;
     float p[4];
+    if constexpr (resident && sizeof(T) == 2) {
+      // on the matrix cores: A row i = centroid 4 grp_i + r of key i (each lane gathers its own
+      // key's row from LDS), B = the key tile; the wanted scores are the diagonal of each product
+      // (after the merges every lane of key lr holds its group)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = min(4 * grp + r, cs_eff - 1);
-      float acc;
-      if constexpr (resident) acc = part_dot(kt, c);
-      else acc = part_dot_global(kt, c);
-      acc += __shfl_xor(acc, 16);
-      acc += __shfl_xor(acc, 32);
-      p[r] = 4 * grp + r < cs_eff ? acc : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const unsigned char* rp = clds + min(4 * grp + r, cs_eff - 1) * STR + 64 * lg;
+        f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(rp + 16 * st), kb[kt][st], dd, 0, 0, 0);
+        p[r] = 4 * grp + r < cs_eff ? diag_of(dd) : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = min(4 * grp + r, cs_eff - 1);
+        float acc;
+        if constexpr (resident) acc = part_dot(kt, c);
+        else acc = part_dot_global(kt, c);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        p[r] = 4 * grp + r < cs_eff ? acc : -INFINITY;
+      }
     }
     int rb = 0;
 #pragma unroll
@@ -408,11 +427,12 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     float b2 = tk[kt].b2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) if (r != rb) b2 = fmaxf(b2, p[r]);
+    const float kn_kt = knorm_of(kt);
     const int i = key0 + w * 64 + kt * 16 + lr;
     flagged[kt] = 0;
     if (lg == 0 && i < n_s) {
       const size_t gi = (size_t)bg * a.Nc + (size_t)s * a.L + i;
-      const double kn = (double)knorm[kt] * (1.0 + 1.0 / 1024);
+      const double kn = (double)kn_kt * (1.0 + 1.0 / 1024);
       const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * kn * 1.01 + 1e-30;
       a.assign[gi] = 4 * grp + rb;
       flagged[kt] = !((double)p[rb] - (double)b2 > 2.0 * delta);
