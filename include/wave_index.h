@@ -123,6 +123,25 @@ wi_status wi_build_index(const wi_build_params *p, const void *k, const void *v,
                          const wi_index_view *out, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/* Grow an index by one segment: the L = seg_len tokens that have left the local window since
+ * `prev` was built are clustered as a new segment (segmented clustering: RetroInfer Spanish
+ * summary section 3 "Clustering Segmentado", Arabic summary section 2.a last paragraph; the
+ * segments are clustered independently, each from its own seed).
+ *   p     the parameters of the grown context (N tokens); seg_len >= 1 and the clustered range
+ *         N - sink - window must be a positive multiple of seg_len.  `prev` is the index of the
+ *         first N - seg_len tokens with the same sink, window, seg_len, clusters_per_seg, iters,
+ *         seed and dtype (so it holds only full segments).
+ *   k, v  [B,Hkv,N,d] the grown context (the new segment's rows and the steady zone are read).
+ *   out   the index of the grown context, with the shapes of wi_index_shapes_for(p); it must not
+ *         overlap `prev`.  Its first segments are copied from `prev`, the last one is clustered,
+ *         and the steady-zone copies are taken from k, v.
+ * The result equals wi_build_index(p, k, v) bit for bit.  Workspace: build_workspace_bytes of p.
+ * Errors: as wi_build_index, and WI_ERR_INVALID_ARG for a clustered range that is not a positive
+ * multiple of seg_len, seg_len 0, null pointers in either view, or overlapping buffers. */
+wi_status wi_index_append_segment(const wi_build_params *p, const void *k, const void *v,
+                                  const wi_index_view *prev, const wi_index_view *out,
+                                  void *workspace, size_t ws_bytes, void *stream);
+
 /* (host) Workspace bytes wi_decode needs for *p.  Host only. */
 wi_status wi_decode_workspace_bytes(const wi_decode_params *p, size_t *bytes);
 

@@ -207,6 +207,52 @@ wi_status wi_build_index(const wi_build_params* p, const void* k, const void* v,
   return check_hip(wi::launch_build(*p, L, k, v, *out, workspace, st), "wi_build_index launch", st);
 }
 
+// [a, a + na) and [b, b + nb) share a byte (null ranges never do)
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+wi_status wi_index_append_segment(const wi_build_params* p, const void* k, const void* v,
+                                  const wi_index_view* prev, const wi_index_view* out,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  Derived d{};
+  wi_status s = derive_build(p, &d);
+  if (s != WI_OK) return s;
+  if (p->seg_len < 1) return fail(WI_ERR_INVALID_ARG, "appending a segment needs an explicit seg_len");
+  if (d.Nc < d.L || d.Nc % d.L != 0)
+    return fail(WI_ERR_INVALID_ARG, "the clustered range (%lld tokens) must be a positive multiple of seg_len (%lld)",
+                (long long)d.Nc, (long long)d.L);
+  if (!k || !v) return fail(WI_ERR_INVALID_ARG, "k and v must be non-null");
+  if (!prev || !out) return fail(WI_ERR_INVALID_ARG, "index view is null");
+  if (!out->offsets || (d.NS > 0 && (!out->k_steady || !out->v_steady)) || !out->centroids ||
+      !out->value_sums || !out->sizes || !out->perm || !out->k_perm || !out->v_perm)
+    return fail(WI_ERR_INVALID_ARG, "output index view has a null pointer");
+  const int64_t BG = (int64_t)p->B * p->Hkv, e = p->dtype == WI_BF16 ? 2 : 4;
+  const int64_t C0 = (d.nseg - 1) * p->clusters_per_seg, N0 = (d.nseg - 1) * d.L;
+  if (C0 > 0 && (!prev->centroids || !prev->value_sums || !prev->sizes || !prev->offsets ||
+                 !prev->perm || !prev->k_perm || !prev->v_perm))
+    return fail(WI_ERR_INVALID_ARG, "previous index view has a null pointer");
+  const size_t rowc = (size_t)(BG * C0 * wi::kD * e), rowc1 = (size_t)(BG * d.C * wi::kD * e);
+  const size_t rown = (size_t)(BG * N0 * wi::kD * e), rown1 = (size_t)(BG * d.Nc * wi::kD * e);
+  if (overlaps(prev->centroids, rowc, out->centroids, rowc1) ||
+      overlaps(prev->value_sums, rowc, out->value_sums, rowc1) ||
+      overlaps(prev->sizes, (size_t)(BG * C0 * 4), out->sizes, (size_t)(BG * d.C * 4)) ||
+      overlaps(prev->offsets, (size_t)(BG * (C0 + 1) * 4), out->offsets, (size_t)(BG * (d.C + 1) * 4)) ||
+      overlaps(prev->perm, (size_t)(BG * N0 * 4), out->perm, (size_t)(BG * d.Nc * 4)) ||
+      overlaps(prev->k_perm, rown, out->k_perm, rown1) || overlaps(prev->v_perm, rown, out->v_perm, rown1))
+    return fail(WI_ERR_INVALID_ARG, "the previous and the new index buffers overlap");
+  const wi::BuildLayout L = wi::build_layout(*p);
+  if (L.total > 0 && (!workspace || ws_bytes < L.total))
+    return fail(WI_ERR_WORKSPACE, "build workspace of %zu bytes given, %zu needed", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(WI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return check_hip(wi::launch_build(*p, L, k, v, *out, workspace, st, prev, (int)d.nseg - 1),
+                   "wi_index_append_segment launch", st);
+}
+
 wi_status wi_decode_workspace_bytes(const wi_decode_params* p, size_t* bytes) {
   if (!p || !bytes) return fail(WI_ERR_INVALID_ARG, "null argument");
   if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)

@@ -43,6 +43,7 @@ struct BuildArgs {
   uint32_t* flag_cnt; // [iters]
   int32_t* flag_list; // [BG * Nc]
   int Hkv, N, sink, window, NS, lo, Nc, L, nseg, Cs, C, BG, iters;
+  int seg0;           // segments [seg0, nseg) are built; the others are left as they are
   uint64_t seed;
 };
 
@@ -124,7 +125,7 @@ template <typename T>
 __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
   extern __shared__ uint32_t init_lds[];      // draws j_r [Cs], then the row array [n_s] (u16)
   __shared__ double buf[kInitThreads / 64][kD];
-  const int s = blockIdx.x, bg = blockIdx.y;
+  const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   extern __shared__ __attribute__((aligned(16))) unsigned char clds[];
   constexpr int CH = AssignCfg<T>::kChunk, STR = AssignCfg<T>::kStride;
   constexpr int NT = assign_threads<T>();          // 64 keys per wave and pass
-  const int s = blockIdx.y, bg = blockIdx.z;
+  const int s = a.seg0 + blockIdx.y, bg = blockIdx.z;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
   if (blockIdx.x * NT >= n_s) return;
@@ -506,7 +507,7 @@ constexpr int kCsrThreads = 1024;
 __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
   extern __shared__ uint32_t csr_lds[];   // cnt[Cs], loc[Cs], run[Cs], tbl[16][Cs] (u8)
   __shared__ int iscr[32];
-  const int s = blockIdx.x, bg = blockIdx.y;
+  const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int n_s = seg_len_of(a, s);
   const int Cs = a.Cs;
   uint32_t* cnt = csr_lds;
@@ -575,7 +576,7 @@ template <typename T, bool kFinal>
 __global__ __launch_bounds__(512) void k_sums(BuildArgs a) {
   __shared__ double buf[8][kD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int s = blockIdx.y, bg = blockIdx.z;
+  const int s = a.seg0 + blockIdx.y, bg = blockIdx.z;
   const int j = blockIdx.x * 8 + w;
   if (j >= a.Cs) return;
   const int n_s = seg_len_of(a, s);
@@ -661,11 +662,12 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.Nc == 0) return hipSuccess;
+  if (a.Nc == 0 || a.seg0 >= a.nseg) return hipSuccess;
+  const int nseg_b = a.nseg - a.seg0;        // segments built by this call
   {
     const size_t lds = (size_t)a.Cs * 4 + (((size_t)a.L * 2 + 3) & ~size_t(3));
     prof_begin(WI_STAGE_INIT, st);
-    hipLaunchKernelGGL(k_init<T>, dim3(a.nseg, BG), dim3(kInitThreads), lds, st, a);
+    hipLaunchKernelGGL(k_init<T>, dim3(nseg_b, BG), dim3(kInitThreads), lds, st, a);
     prof_end(WI_STAGE_INIT, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -675,29 +677,29 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   // assignment blocks per segment: about one block per CU in all (each stages the segment's
   // centroids once and loops over 64-key-per-wave passes), at least one pass each
   const unsigned assign_px = (unsigned)std::max<int64_t>(1, std::min<int64_t>(
-      ceil_div(a.L, assign_threads<T>()), ceil_div(kAssignBlocksTarget, (int64_t)a.nseg * BG)));
+      ceil_div(a.L, assign_threads<T>()), ceil_div(kAssignBlocksTarget, (int64_t)nseg_b * BG)));
   for (int it = 0; it < a.iters; ++it) {
     prof_begin(WI_STAGE_ASSIGN, st);
     if (a.Cs <= AssignCfg<T>::kChunk)
-      hipLaunchKernelGGL((k_assign<T, true>), dim3(assign_px, a.nseg, BG), dim3(assign_threads<T>()),
+      hipLaunchKernelGGL((k_assign<T, true>), dim3(assign_px, nseg_b, BG), dim3(assign_threads<T>()),
                          alds, st, a, it);
     else
-      hipLaunchKernelGGL((k_assign<T, false>), dim3(assign_px, a.nseg, BG), dim3(assign_threads<T>()),
+      hipLaunchKernelGGL((k_assign<T, false>), dim3(assign_px, nseg_b, BG), dim3(assign_threads<T>()),
                          alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
     hipLaunchKernelGGL(k_rescore<T>, dim3(1024), dim3(256), 0, st, a, it);
     prof_end(WI_STAGE_RESCORE, st);
     prof_begin(WI_STAGE_CSR, st);
-    hipLaunchKernelGGL(k_csr, dim3(a.nseg, BG), dim3(kCsrThreads), clds, st, a);
+    hipLaunchKernelGGL(k_csr, dim3(nseg_b, BG), dim3(kCsrThreads), clds, st, a);
     prof_end(WI_STAGE_CSR, st);
     if (it + 1 < a.iters) {
       prof_begin(WI_STAGE_UPDATE, st);
-      hipLaunchKernelGGL((k_sums<T, false>), dim3((unsigned)ceil_div(a.Cs, 8), a.nseg, BG), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_sums<T, false>), dim3((unsigned)ceil_div(a.Cs, 8), nseg_b, BG), dim3(512), 0, st, a);
       prof_end(WI_STAGE_UPDATE, st);
     } else {
       prof_begin(WI_STAGE_FINAL, st);
-      hipLaunchKernelGGL((k_sums<T, true>), dim3((unsigned)ceil_div(a.Cs, 8), a.nseg, BG), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_sums<T, true>), dim3((unsigned)ceil_div(a.Cs, 8), nseg_b, BG), dim3(512), 0, st, a);
       prof_end(WI_STAGE_FINAL, st);
     }
     hipError_t e = hipGetLastError();
@@ -720,8 +722,38 @@ static void set_lds_limits() {
   done = true;
 }
 
+// ============================================================================ k_copy_prefix
+// dst[g][0 .. bytes) = src[g][0 .. bytes) for g < G, rows of the source and destination `pitch`
+// bytes apart: the leading rows of every (b, KV head) block of an index buffer.  Words of 16 bytes
+// when every address and pitch allows, else 4.
+template <typename W>
+__global__ __launch_bounds__(256) void k_copy_prefix(const unsigned char* src, unsigned char* dst,
+                                                     size_t src_pitch, size_t dst_pitch, size_t bytes) {
+  const W* s = reinterpret_cast<const W*>(src + (size_t)blockIdx.y * src_pitch);
+  W* d = reinterpret_cast<W*>(dst + (size_t)blockIdx.y * dst_pitch);
+  const size_t n = bytes / sizeof(W);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) d[i] = s[i];
+}
+
+static hipError_t copy_prefix(const void* src, void* dst, size_t src_pitch, size_t dst_pitch, size_t bytes,
+                              int G, hipStream_t st) {
+  if (bytes == 0 || G == 0) return hipSuccess;
+  const bool wide = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | src_pitch |
+                      dst_pitch | bytes) & 15) == 0;
+  const size_t words = bytes / (wide ? 16 : 4);
+  const unsigned gx = (unsigned)std::max<size_t>(1, std::min<size_t>(ceil_div((int64_t)words, 256 * 4), 1024));
+  if (wide)
+    hipLaunchKernelGGL(k_copy_prefix<u32x4_t>, dim3(gx, G), dim3(256), 0, st,
+                       static_cast<const unsigned char*>(src), static_cast<unsigned char*>(dst), src_pitch, dst_pitch, bytes);
+  else
+    hipLaunchKernelGGL(k_copy_prefix<uint32_t>, dim3(gx, G), dim3(256), 0, st,
+                       static_cast<const unsigned char*>(src), static_cast<unsigned char*>(dst), src_pitch, dst_pitch, bytes);
+  return hipGetLastError();
+}
+
 hipError_t launch_build(const wi_build_params& p, const BuildLayout& L, const void* k, const void* v,
-                        const wi_index_view& out, void* ws, hipStream_t st) {
+                        const wi_index_view& out, void* ws, hipStream_t st, const wi_index_view* prev,
+                        int seg0) {
   set_lds_limits();
   BuildArgs a;
   a.k = k; a.v = v;
@@ -737,6 +769,23 @@ hipError_t launch_build(const wi_build_params& p, const BuildLayout& L, const vo
   a.NS = (int)L.NS; a.Nc = (int)L.Nc; a.lo = (L.Nc > 0) ? p.sink : p.N;
   a.L = (int)L.L; a.nseg = (int)L.nseg; a.Cs = p.clusters_per_seg; a.C = (int)L.C;
   a.BG = p.B * p.Hkv; a.iters = p.iters; a.seed = p.seed;
+  a.seg0 = seg0;
+  if (prev && seg0 > 0) {
+    // segments [0, seg0) of every (b, KV head) come from the previous index, whose C and Nc are
+    // those of its seg0 segments (the rows of a segment sit at the same places in both)
+    const size_t e = p.dtype == WI_BF16 ? 2 : 4;
+    const size_t C0 = (size_t)seg0 * p.clusters_per_seg, N0 = (size_t)seg0 * L.L;
+    const size_t C1 = (size_t)L.C, N1 = (size_t)L.Nc, d = kD;
+    const int G = a.BG;
+    hipError_t r;
+    if ((r = copy_prefix(prev->centroids, out.centroids, C0 * d * e, C1 * d * e, C0 * d * e, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->value_sums, out.value_sums, C0 * d * e, C1 * d * e, C0 * d * e, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->sizes, out.sizes, C0 * 4, C1 * 4, C0 * 4, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->offsets, out.offsets, (C0 + 1) * 4, (C1 + 1) * 4, C0 * 4, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->perm, out.perm, N0 * 4, N1 * 4, N0 * 4, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->k_perm, out.k_perm, N0 * d * e, N1 * d * e, N0 * d * e, G, st)) != hipSuccess) return r;
+    if ((r = copy_prefix(prev->v_perm, out.v_perm, N0 * d * e, N1 * d * e, N0 * d * e, G, st)) != hipSuccess) return r;
+  }
   return p.dtype == WI_BF16 ? launch_build_t<uint16_t>(a, st) : launch_build_t<float>(a, st);
 }
 

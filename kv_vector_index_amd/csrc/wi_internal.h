@@ -92,7 +92,10 @@ struct BuildLayout {
 };
 BuildLayout build_layout(const wi_build_params& p);
 
+// Build segments [seg0, nseg) of the index of *p into `out`; with seg0 > 0, segments [0, seg0)
+// are copied from `prev`, an index of the same parameters over seg0 full segments.
 hipError_t launch_build(const wi_build_params& p, const BuildLayout& L, const void* k,
-                        const void* v, const wi_index_view& out, void* ws, hipStream_t s);
+                        const void* v, const wi_index_view& out, void* ws, hipStream_t st,
+                        const wi_index_view* prev = nullptr, int seg0 = 0);
 
 }  // namespace wi

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libwave_index.so")
 
 WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0, -1, -2, -3, -4
 WI_F32, WI_BF16 = 0, 1
-EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode",
+EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
+            "wi_decode_workspace_bytes", "wi_decode",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
           "final")
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.wi_index_shapes_for.argtypes = [ctypes.POINTER(BuildParams), ctypes.POINTER(IndexShapes)]
         L.wi_build_index.argtypes = [ctypes.POINTER(BuildParams), vp, vp, ctypes.POINTER(IndexView),
                                      vp, sz, vp]
+        L.wi_index_append_segment.argtypes = [ctypes.POINTER(BuildParams), vp, vp, ctypes.POINTER(IndexView),
+                                              ctypes.POINTER(IndexView), vp, sz, vp]
         L.wi_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
         L.wi_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
                                 vp, vp, sz, vp]
@@ -84,7 +87,8 @@ def lib() -> ctypes.CDLL:
         L.wi_profile_enable.restype = ctypes.c_int
         L.wi_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.wi_profile_read.restype = ctypes.c_int
-        for name in ("wi_index_shapes_for", "wi_build_index", "wi_decode_workspace_bytes", "wi_decode"):
+        for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
+                     "wi_decode_workspace_bytes", "wi_decode"):
             getattr(L, name).restype = ctypes.c_int
         L.wi_status_string.restype = ctypes.c_char_p
         L.wi_last_error.restype = ctypes.c_char_p
@@ -117,6 +121,12 @@ def wi_build_index(p: BuildParams, k_ptr: int, v_ptr: int, view: IndexView, ws_p
                    ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_build_index(ctypes.byref(p), k_ptr, v_ptr, ctypes.byref(view), ws_ptr,
                                        ws_bytes, stream))
+
+
+def wi_index_append_segment(p: BuildParams, k_ptr: int, v_ptr: int, prev: IndexView, out: IndexView,
+                            ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_index_append_segment(ctypes.byref(p), k_ptr, v_ptr, ctypes.byref(prev),
+                                                ctypes.byref(out), ws_ptr, ws_bytes, stream))
 
 
 def wi_decode_workspace_bytes(p: DecodeParams) -> int:
@@ -231,6 +241,26 @@ def build_index(K, V, sink: int, window: int, seg_len: int, clusters_per_seg: in
         workspace = torch.empty(need, dtype=torch.uint8, device=K.device)
     wi_build_index(p, K.data_ptr(), V.data_ptr(), idx.view(), workspace.data_ptr(), workspace.numel(),
                    _stream(K.device))
+    return idx
+
+
+def append_segment(prev: Index, K, V, sink: int, window: int, seg_len: int, clusters_per_seg: int,
+                   iters: int, seed: int, workspace=None) -> Index:
+    """The index of K, V ([B,Hkv,N,128]) grown from `prev`, the index of their first N - seg_len
+    tokens built with the same parameters: the tokens that left the window form one new segment."""
+    import torch
+    assert K.is_cuda and K.shape == V.shape and K.dtype == V.dtype and K.is_contiguous() and V.is_contiguous()
+    B, Hkv, N, d = K.shape
+    idx, p, sh = allocate_index(B, Hkv, N, sink, window, seg_len, clusters_per_seg, K.dtype, K.device)
+    p.d = d
+    p.iters = iters
+    p.seed = seed & ((1 << 64) - 1)
+    p.dtype = _dtype_code(K)
+    need = max(int(sh.build_workspace_bytes), 256)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=K.device)
+    wi_index_append_segment(p, K.data_ptr(), V.data_ptr(), prev.view(), idx.view(), workspace.data_ptr(),
+                            workspace.numel(), _stream(K.device))
     return idx
 
 

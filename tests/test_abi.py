@@ -110,6 +110,43 @@ def _view():
     return wi.IndexView(*([FAKE] * 9))
 
 
+def _bparams(**kw):
+    # 4 sink + 64 window + 3 segments of 1024 tokens, 64 clusters each
+    p = wi.BuildParams(1, 8, 4 + 64 + 3 * 1024, 128, 4, 64, 1024, 64, 10, wi.WI_BF16, 0)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw", [dict(N=4 + 64 + 3 * 1024 + 100), dict(seg_len=0), dict(N=40)])
+def test_append_segment_rejects_ranges_that_are_not_whole_segments(kw):
+    # a clustered range that is not a positive multiple of seg_len (ragged, one implicit segment,
+    # or empty) has no previous index of full segments to grow from
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_index_append_segment(_bparams(**kw), FAKE, FAKE, _view(), _view(), FAKE, 1 << 40, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+
+
+def test_append_segment_rejects_null_overlap_and_small_workspace():
+    p = _bparams()
+    apart = wi.IndexView(*([FAKE + (1 << 38)] * 9))
+    with pytest.raises(wi.WaveIndexError) as e:       # null key rows
+        wi.wi_index_append_segment(p, None, FAKE, _view(), apart, FAKE, 1 << 40, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    prev = _view()
+    prev.k_perm = None
+    with pytest.raises(wi.WaveIndexError) as e:       # the previous index must be complete
+        wi.wi_index_append_segment(p, FAKE, FAKE, prev, apart, FAKE, 1 << 40, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:       # same buffers on both sides
+        wi.wi_index_append_segment(p, FAKE, FAKE, _view(), _view(), FAKE, 1 << 40, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    need = int(wi.wi_index_shapes_for(p).build_workspace_bytes)
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_index_append_segment(p, FAKE, FAKE, _view(), apart, FAKE, need - 1, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+
+
 def _dparams(**kw):
     p = wi.DecodeParams(1, 32, 8, 128, 68, 8192, 131004, 164, 0.0883883, wi.WI_BF16)
     for k, v in kw.items():
