@@ -167,6 +167,30 @@ def bench_build(w, args, dev):
     assign_ms = stages["assign"][0] / steps
     peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     tflops = assign_flops / (assign_ms / 1e3) / 1e12
+
+    # index maintenance: the same context one segment shorter, grown by that segment
+    append = None
+    L = w.seg_len
+    if L > 0 and idx.Nc >= 2 * L and idx.Nc % L == 0:
+        n0 = w.N - L
+        K0, V0 = Kt[:, :, :n0].contiguous(), Vt[:, :, :n0].contiguous()
+        prev = wi.build_index(K0, V0, w.sink, w.window, L, w.clusters_per_seg, w.iters, 1)
+        del K0, V0
+        for _ in range(2):
+            grown = wi.append_segment(prev, Kt, Vt, w.sink, w.window, L, w.clusters_per_seg, w.iters, 1)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            grown = wi.append_segment(prev, Kt, Vt, w.sink, w.window, L, w.clusters_per_seg, w.iters, 1)
+        t1.record()
+        torch.cuda.synchronize()
+        e = 2 if w.dtype == "bf16" else 4
+        # bytes the earlier segments' copy moves (read + write): centroids, value sums, sizes,
+        # offsets, perm, and the cluster-major K and V rows
+        copy_bytes = 2 * w.B * w.Hkv * (prev.C * (2 * w.d * e + 8) + prev.Nc * (2 * w.d * e + 4))
+        append = {"ms": t0.elapsed_time(t1) / steps, "tokens_appended": L, "context_before": n0,
+                  "copied_bytes": copy_bytes, "full_build_ms": build_ms}
+        del prev, grown
     result = {
         "metric": "wave-index build (segmented spherical k-means) time", "value": build_ms, "unit": "ms",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": build_ms,
@@ -177,6 +201,7 @@ def bench_build(w, args, dev):
         "stage_ms": {k: v[0] / steps for k, v in stages.items() if v[1]},
         "roofline": {"kernel": "k_assign", "bound": "mfma", "achieved": tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None},
+        "append_segment": append,
     }
     print(json.dumps(result), flush=True)
 
