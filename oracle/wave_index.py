@@ -11,6 +11,9 @@ Sources, cited as [tag section]:
   [SM64]   Steele, Lea, Flood, "Fast Splittable Pseudorandom Number Generators", OOPSLA 2014
   [DM01]   Dhillon, Modha, "Concept Decompositions for Large Sparse Text Data using Clustering",
            Machine Learning 42, 2001 (spherical k-means)
+  [FKV-es] "FreeKV: Boosting KV Cache Retrieval for Efficient LLM Inference", technical summary
+           (gist.science/es), section A items 1-2 (speculative retrieval, correction by a
+           cosine threshold between consecutive queries)
 
 What the pages fix: each decode query's attention is split into a steady zone (sink tokens and the
 local window, exact), a retrieval zone (the clusters of a spherical-k-means index most similar to
@@ -38,6 +41,11 @@ Parity pins (tests/test_oracle.py), per function:
                           torch SDPA in float64); keys equal to centroids make the estimate exact;
                           one token per cluster makes the estimate exact for any k; top-k equals
                           brute-force ranking with forced ties
+  decode_gated .......... pinned: a threshold above 1 never reuses (equals decode); reusing a
+                          step's own selection equals decode; reusing "every cluster" equals
+                          dense attention; exact cosines of q with q, 2q and -q decide as
+                          their closed forms; one drifting head makes its whole KV group
+                          re-select
 Approximation quality against dense attention is "parity unpinned": the pages claim only
 comparable accuracy, with no figure.
 """
@@ -52,7 +60,8 @@ import numpy as np
 __all__ = [
     "round_to_dtype", "canonical_scores", "splitmix64", "segment_state", "init_rows",
     "steady_positions", "clustered_range", "segment_bounds", "spherical_kmeans_segment",
-    "Index", "finalize_index", "build_index", "decode", "decode_head",
+    "Index", "finalize_index", "build_index", "decode", "decode_head", "decode_gated",
+    "query_cosine",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -355,13 +364,16 @@ def _select(sigma: np.ndarray, sizes: np.ndarray, k: int) -> np.ndarray:
     return np.sort(cand[order[:k_eff]])
 
 
-def decode_head(q: np.ndarray, idx: Index, b: int, g: int, k: int, scale: float):
-    """One query head's decode step.  Returns (o [d], lse, sel_ids ascending)."""
+def decode_head(q: np.ndarray, idx: Index, b: int, g: int, k: int, scale: float,
+                R: Optional[np.ndarray] = None):
+    """One query head's decode step.  Returns (o [d], lse, sel_ids ascending).  The retrieval zone
+    is the head's top-k unless ``R`` (ascending cluster ids) is given."""
     mu = idx.centroids[b, g]
     sizes = idx.sizes[b, g]
     off = idx.offsets[b, g]
     sigma = canonical_scores(q[None, :], mu)[0] if idx.C > 0 else np.zeros(0)
-    R = _select(sigma, sizes, k)
+    if R is None:
+        R = _select(sigma, sizes, k)
 
     # exact part: steady rows and every row of the retrieved clusters [RI-es 2.A items 1-2]
     rows = [np.arange(off[c], off[c + 1]) for c in R]
@@ -421,3 +433,55 @@ def decode(Q: np.ndarray, idx: Index, Hq: int, k: int, scale: Optional[float] = 
             o[b, h], lse[b, h] = oh, lh
             sel[b, h, :R.size] = R
     return o, lse, sel
+
+
+# --------------------------------------------------------------------------------------------
+# Selection reuse across decode steps with a cosine gate [FKV-es A items 1-2].  Consecutive
+# queries are similar, so a KV head keeps the clusters its query heads retrieved at the previous
+# step unless the queries moved: the cosine C between the current and the previous query of a
+# head is computed, and a KV head whose query heads all have C >= tau reuses their previous
+# retrieval zones (reading R26); every other KV head selects afresh.  Scoring still runs for
+# every head, because the estimation zone (every non-empty cluster outside the reused zone)
+# needs the current query's scores (reading R27).
+# --------------------------------------------------------------------------------------------
+def query_cosine(q: np.ndarray, q_prev: np.ndarray) -> float:
+    """<q, q'> / (||q|| ||q'||) from canonical sums (ascending coordinate order, exact products),
+    IEEE float64 square roots and division; 0 when either query is zero (reading R26)."""
+    dot = canonical_scores(q[None, :], q_prev[None, :])[0, 0]
+    n1 = canonical_scores(q[None, :], q[None, :])[0, 0]
+    n2 = canonical_scores(q_prev[None, :], q_prev[None, :])[0, 0]
+    if n1 == 0.0 or n2 == 0.0:
+        return 0.0
+    return float(dot / (math.sqrt(n1) * math.sqrt(n2)))
+
+
+def decode_gated(Q: np.ndarray, Q_prev: np.ndarray, sel_prev: np.ndarray, idx: Index, Hq: int, k: int,
+                 tau: float, scale: Optional[float] = None):
+    """Batched decode with selection reuse: as ``decode``, except that a KV head whose query heads
+    all satisfy query_cosine(q, q_prev) >= tau takes each head's retrieval zone from ``sel_prev``
+    [B,Hq,k] (ascending ids, -1 padded).  Returns (o, lse, sel, reused [B,Hkv] bool)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    Q_prev = np.asarray(Q_prev, dtype=np.float64)
+    B, _, d = Q.shape
+    Hkv = idx.centroids.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    sel = np.full((B, Hq, k), -1, dtype=np.int64)
+    reused = np.zeros((B, Hkv), dtype=bool)
+    for b in range(B):
+        for g in range(Hkv):
+            heads = range(g * G, (g + 1) * G)
+            reuse = all(query_cosine(Q[b, h], Q_prev[b, h]) >= tau for h in heads)
+            reused[b, g] = reuse
+            for h in heads:
+                R = None
+                if reuse:
+                    prev = np.asarray(sel_prev[b, h])
+                    R = np.sort(prev[prev >= 0]).astype(np.int64)
+                oh, lh, Rh = decode_head(Q[b, h], idx, b, g, k, scale, R)
+                o[b, h], lse[b, h] = oh, lh
+                sel[b, h, :Rh.size] = Rh
+    return o, lse, sel, reused

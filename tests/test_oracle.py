@@ -403,3 +403,83 @@ def test_generator_is_seeded_and_shaped():
     np.testing.assert_allclose(np.linalg.norm(K, axis=-1), 1.0, rtol=1e-12)
     K3, _, _ = synth.make_instance(w, 6)
     assert not np.array_equal(K, K3)
+
+
+# ------------------------------------------------------------------ selection reuse (FreeKV)
+def _gated_setup(seed=0):
+    w = _small_workload()
+    K, V, Q = _inputs(w, seed)
+    idx = oracle.build_index(K, V, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 3, "bf16")
+    return w, K, V, Q, idx
+
+
+def test_query_cosine_closed_forms():
+    # cos(q, q) = 1 up to the rounding of sqrt(a) * sqrt(a) (within 1e-15); 2q and -q scale
+    # every product exactly; a zero query gives 0; e3 against e3 + e7 is 1/sqrt(2)
+    rng = np.random.default_rng(1)
+    q = oracle.round_to_dtype(rng.standard_normal(128), "bf16")
+    assert abs(oracle.query_cosine(q, q) - 1.0) <= 1e-15
+    assert abs(oracle.query_cosine(q, 2 * q) - 1.0) <= 1e-15
+    assert abs(oracle.query_cosine(q, -q) + 1.0) <= 1e-15
+    assert oracle.query_cosine(q, np.zeros(128)) == 0.0
+    e = np.zeros(128)
+    e[3] = 1.0
+    f = np.zeros(128)
+    f[3], f[7] = 1.0, 1.0
+    assert abs(oracle.query_cosine(e, f) - 1 / math.sqrt(2)) <= 1e-16
+
+
+def test_gated_threshold_above_one_never_reuses():
+    w, K, V, Q, idx = _gated_setup()
+    o, lse, sel = oracle.decode(Q, idx, w.Hq, w.top_k)
+    junk = np.zeros_like(sel)                     # cluster 0 only, never the real selection
+    go, gl, gs, reused = oracle.decode_gated(Q, Q, junk, idx, w.Hq, w.top_k, 1.5)
+    assert not reused.any()
+    np.testing.assert_array_equal(gs, sel)
+    np.testing.assert_array_equal(go, o)
+    np.testing.assert_array_equal(gl, lse)
+
+
+def test_gated_reusing_own_selection_equals_decode():
+    w, K, V, Q, idx = _gated_setup(1)
+    o, lse, sel = oracle.decode(Q, idx, w.Hq, w.top_k)
+    go, gl, gs, reused = oracle.decode_gated(Q, Q, sel, idx, w.Hq, w.top_k, 0.999)
+    assert reused.all()
+    np.testing.assert_array_equal(gs, sel)
+    np.testing.assert_allclose(go, o, rtol=0, atol=0)
+    np.testing.assert_array_equal(gl, lse)
+
+
+def test_gated_reusing_every_cluster_is_dense_attention():
+    w, K, V, Q, idx = _gated_setup(2)
+    G = w.Hq // w.Hkv
+    allc = np.full((w.B, w.Hq, idx.C), -1, dtype=np.int64)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            ne = np.nonzero(idx.sizes[b, h // G])[0]
+            allc[b, h, :ne.size] = ne
+    go, gl, gs, reused = oracle.decode_gated(Q, Q, allc, idx, w.Hq, idx.C, -2.0)
+    assert reused.all()
+    scale = 1 / math.sqrt(w.d)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            ro, rl = _dense(Q[b, h], K[b, h // G], V[b, h // G], scale)
+            np.testing.assert_allclose(go[b, h], ro, rtol=0, atol=1e-13)
+            assert abs(gl[b, h] - rl) < 1e-12
+
+
+def test_gated_one_drifting_head_reselects_its_whole_group():
+    w, K, V, Q, idx = _gated_setup(3)
+    G = w.Hq // w.Hkv
+    o, lse, sel = oracle.decode(Q, idx, w.Hq, w.top_k)
+    junk = np.full_like(sel, -1)
+    junk[..., 0] = 0                              # a stale one-cluster selection
+    Qp = Q.copy()
+    Qp[0, G] = -Q[0, G]                           # head G (first head of KV group 1) turns around
+    go, gl, gs, reused = oracle.decode_gated(Q, Qp, junk, idx, w.Hq, w.top_k, 0.5)
+    assert reused[0, 0] and not reused[0, 1]
+    # group 0 takes the stale zone, group 1 selects afresh for every one of its heads
+    for h in range(G):
+        assert list(gs[0, h][gs[0, h] >= 0]) == [0]
+    np.testing.assert_array_equal(gs[0, G:2 * G], sel[0, G:2 * G])
+    np.testing.assert_array_equal(go[0, G:2 * G], o[0, G:2 * G])
