@@ -16,6 +16,10 @@ index placed at different HBM addresses.  Steps are captured in a HIP graph and 
 timed region measures GPU work rather than Python launch overhead.  Inputs are resident in HBM
 before the timed region starts.
 
+With --gated TAU a step is one wi_decode_gated call over a drifting query stream (each step's
+queries and zones are the next step's q_prev and sel_prev), and with --refresh also the
+wi_select_refresh call that computes the postponed selection (FreeKV's scheme).
+
 Prints one JSON line (rank 0) with the throughput, the roofline position of the dominant kernel
 (per-kernel HIP-event timing over a second, eager pass), and the CPU oracle timed on the host.
 """
@@ -217,6 +221,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--gated", type=float, default=None, metavar="TAU",
+                    help="time wi_decode_gated over drifting queries: KV heads whose query heads all "
+                         "moved by a cosine >= TAU reuse the previous step's zones")
+    ap.add_argument("--refresh", action="store_true",
+                    help="with --gated: each step also runs wi_select_refresh (the postponed top-k of the "
+                         "reused groups, which the next step keeps), as in FreeKV")
     ap.add_argument("--build-only", action="store_true",
                     help="time the index build (segmented spherical k-means) instead of the decode step")
     args = ap.parse_args()
@@ -262,9 +272,10 @@ def main():
     # the queries of the steps (a drifting sequence for multi-step workloads)
     n_inst = args.instances if args.instances else (8 if w.B * w.Hkv * idx.C * w.d * 4 < (64 << 20) else 2 if w.B == 1 else 1)
     insts = [idx] + [idx.clone() for _ in range(n_inst - 1)]
-    if w.steps > 1:
-        qm = synth.drift_queries_device(Qt, w.steps, w.drift, args.seed)
-        qs = [qm[t].to(torch.float32).to(Qt.dtype).contiguous() for t in range(w.steps)]
+    if w.steps > 1 or args.gated is not None:
+        n_q, drift = (w.steps, w.drift) if w.steps > 1 else (64, 0.1)
+        qm = synth.drift_queries_device(Qt, n_q, drift, args.seed)
+        qs = [qm[t].to(torch.float32).to(Qt.dtype).contiguous() for t in range(n_q)]
         del qm
     else:
         qs = [Qt.clone() for _ in insts]
@@ -281,10 +292,35 @@ def main():
         wi.wi_decode(p, views[j], qs[i % len(qs)].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
                      ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
 
+    if args.gated is not None:
+        # step i reads the zones step i-1 wrote (two buffers: sel_prev and sel_ids may not alias)
+        sels = [sel, torch.empty_like(sel)]
+        reused = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+        reuse_log = []
+        step(0)
+        sels[1].copy_(sel)
+
+        def step(i):
+            j = i % len(insts)
+            st = torch.cuda.current_stream().cuda_stream
+            wi.wi_decode_gated(p, views[j], qs[i % len(qs)].data_ptr(), qs[(i - 1) % len(qs)].data_ptr(),
+                               sels[(i + 1) % 2].data_ptr(), args.gated, out.data_ptr(), lse.data_ptr(),
+                               sels[i % 2].data_ptr(), reused.data_ptr(), ws.data_ptr(), ws_bytes, st)
+            if args.refresh:
+                wi.wi_select_refresh(p, views[j], qs[i % len(qs)].data_ptr(), sels[i % 2].data_ptr(),
+                                     ws.data_ptr(), ws_bytes, st)
+            if reuse_log is not None:
+                reuse_log.append(reused.clone())
+
     log("[bench] warmup")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    reuse_frac = None
+    if args.gated is not None:
+        reuse_frac = float(torch.stack(reuse_log).float().mean()) if reuse_log else None
+        reuse_log = None
+        sel = sels[(args.warmup - 1) % 2]
     sel_np = sel.cpu().numpy()
     off_np = idx.offsets.cpu().numpy()
     per_bytes, union_rows = algorithmic_bytes(w, off_np, sel_np)
@@ -343,7 +379,8 @@ def main():
     stages = wi.wi_profile_read()
     wi.wi_profile_enable(False)
     del a
-    avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items() if k in ("score", "select", "attend", "merge")}
+    avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()
+              if k in ("score", "select", "attend", "merge") or (k == "refresh" and v[1])}
     dominant = max(("score", "attend"), key=lambda k: avg_ms[k] or 0.0)
     achieved = {k: per_bytes[k] / (avg_ms[k] / 1e3) / 1e9 for k in ("score", "attend") if avg_ms[k]}
 
@@ -372,6 +409,11 @@ def main():
                    "head_dim": w.d, "context": w.N, "clusters": idx.C, "top_k": w.top_k,
                    "sink": w.sink, "window": w.window, "instances": len(insts),
                    "timing": "eager" if args.no_graph else "hip-graph replay"},
+        "gated": None if args.gated is None else {"tau": args.gated, "refresh": args.refresh,
+                                                  "reused_kv_head_frac": reuse_frac,
+                                                  "out_ready_us": 1e3 * sum(avg_ms[k] for k in ("score", "select", "attend", "merge")),
+                                                  "refresh_us": 1e3 * avg_ms["refresh"] if avg_ms.get("refresh") else None,
+                                                  "query_drift_per_coord": 0.1 if w.steps == 1 else w.drift},
         "head_steps_per_s": 1e3 / ms_per_step * w.B * w.Hq,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms_per_step / 1e3) / 1e9,

@@ -163,7 +163,45 @@ wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const v
                     float *out, float *lse, int32_t *sel_ids, void *workspace, size_t ws_bytes,
                     void *stream);
 
-/* Stages timed by the profiling hook below (one entry per kernel of the two entry points). */
+/* One decode step that attends over the previous step's zones where the queries barely moved
+ * (FreeKV Spanish summary, section A items 1-2: speculative retrieval, and a fine-grained
+ * correction that selects again for the KV heads whose consecutive queries have a cosine below a
+ * threshold tau).  For every (b, KV head): if every one of its query heads has
+ * cos(q, q_prev) >= tau, where cos = <q, q'> / (|q| |q'|) from exact products summed in fp64 in
+ * ascending coordinate order, with IEEE fp64 square roots and division, and 0 when either query
+ * is zero, each of those heads takes its retrieval zone from sel_prev; otherwise the heads select
+ * as wi_decode does.  The scores of the current query are computed for every head either way: the
+ * estimation zone (every non-empty cluster outside the zone) uses them.
+ *   q_prev    [B,Hq,d]     dtype  the previous step's queries
+ *   sel_prev  [B,Hq,top_k] int32  the zones to keep; entries outside [0, C) are skipped and
+ *                                 repeats count once
+ *   tau                           the threshold (> 1 never reuses, <= 0 reuses any pair)
+ *   sel_ids   [B,Hq,top_k] int32  the zone each head attended over, ascending, -1 padded
+ *                                 (required when top_k > 0)
+ *   reused    [B,Hkv]      int32  1 where the KV head kept sel_prev (nullable)
+ * The call also keeps the reuse flags in the workspace for wi_select_refresh.  Feeding sel_ids
+ * to the next step keeps a zone for as long as the queries stay within tau of their predecessor;
+ * calling wi_select_refresh first gives FreeKV's scheme, in which a kept zone is one step old.
+ * Everything else, and the errors, as wi_decode; also WI_ERR_INVALID_ARG for a null q_prev or
+ * sel_prev, a NaN tau, a null sel_ids with top_k > 0, or sel_prev overlapping sel_ids. */
+wi_status wi_decode_gated(const wi_decode_params *p, const wi_index_view *idx, const void *q,
+                          const void *q_prev, const int32_t *sel_prev, float tau, float *out,
+                          float *lse, int32_t *sel_ids, int32_t *reused, void *workspace,
+                          size_t ws_bytes, void *stream);
+
+/* The selection that wi_decode_gated postponed (FreeKV Spanish summary, section A items 1-2: for
+ * the heads that were not corrected, retrieval is deferred and overlapped with other work for the
+ * next step).  For every (b, KV head) that the last wi_decode_gated call on this workspace
+ * marked reused, overwrites its heads' sel_ids rows with the top-k of the current queries, as
+ * wi_decode selects them; other rows are left as they are.  p, idx, q, sel_ids and the workspace
+ * must be those of that call, and the workspace must not have been used since; the call may be
+ * enqueued later or on another stream, ordered after that call.  After a wi_decode call on the
+ * workspace it does nothing.  Errors: as wi_decode for the shared arguments; WI_ERR_INVALID_ARG
+ * for a null sel_ids with top_k > 0. */
+wi_status wi_select_refresh(const wi_decode_params *p, const wi_index_view *idx, const void *q,
+                            int32_t *sel_ids, void *workspace, size_t ws_bytes, void *stream);
+
+/* Stages timed by the profiling hook below (one entry per kernel the entry points launch). */
 typedef enum {
   WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA) and the estimation over all
                              non-empty clusters                                              */
@@ -178,7 +216,8 @@ typedef enum {
   WI_STAGE_CSR = 8,       /* build: sizes, offsets, permutation                             */
   WI_STAGE_UPDATE = 9,    /* build: centroid directions from member sums                    */
   WI_STAGE_FINAL = 10,    /* build: mean keys, value sums, cluster-major copies             */
-  WI_NUM_STAGES = 11
+  WI_STAGE_REFRESH = 11,  /* wi_select_refresh: the postponed top-k of reused groups        */
+  WI_NUM_STAGES = 12
 } wi_stage;
 
 /* (host) Profiling hook for measurement tools.  While enabled, wi_decode and wi_build_index

@@ -146,6 +146,7 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_band_ids = o;   o = align256(o + BH * C * 4);
   L.off_band_key = o;   o = align256(o + BH * C * 8);
   L.off_all_sel = o;    o = align256(o + BH * 4);
+  L.off_gate = o;       o = align256(o + BG * 4);
   L.off_hl_cid = o;     o = align256(o + BH * K * 4);
   L.off_hl_row = o;     o = align256(o + BH * K * 4);
   L.off_hl_pre = o;     o = align256(o + BH * (K + 1) * 4);
@@ -263,8 +264,17 @@ wi_status wi_decode_workspace_bytes(const wi_decode_params* p, size_t* bytes) {
   return WI_OK;
 }
 
-wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
-                    float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream) {
+struct Gate {
+  const void* q_prev;
+  const int32_t* sel_prev;
+  int32_t* reused;
+  float tau;
+  bool refresh;            // select only, for the groups the last gated call reused
+};
+
+static wi_status decode_common(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
+                               float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream,
+                               const Gate* gate) {
   if (!p || !idx || !q || !out) return fail(WI_ERR_INVALID_ARG, "params, index, q and out must be non-null");
   if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
     return fail(WI_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and Hkv dividing Hq");
@@ -311,6 +321,7 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.band_ids = reinterpret_cast<int32_t*>(base + L.off_band_ids);
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
+  a.gate = reinterpret_cast<int32_t*>(base + L.off_gate);
   a.hl_cid = reinterpret_cast<int32_t*>(base + L.off_hl_cid);
   a.hl_row = reinterpret_cast<int32_t*>(base + L.off_hl_row);
   a.hl_pre = reinterpret_cast<int32_t*>(base + L.off_hl_pre);
@@ -325,7 +336,45 @@ wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const v
   a.att_split = L.att_split; a.att_items = L.att_items;
   a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return check_hip(wi::launch_decode(*p, a, st), "wi_decode launch", st);
+  if (gate && gate->refresh) {
+    a.refresh = 1;
+    return check_hip(wi::launch_refresh(*p, a, st), "wi_select_refresh launch", st);
+  }
+  if (gate) {
+    a.gated = 1; a.q_prev = gate->q_prev; a.sel_prev = gate->sel_prev; a.reused = gate->reused;
+    a.tau = gate->tau;
+  }
+  return check_hip(wi::launch_decode(*p, a, st), gate ? "wi_decode_gated launch" : "wi_decode launch", st);
+}
+
+wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
+                    float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, nullptr);
+}
+
+wi_status wi_decode_gated(const wi_decode_params* p, const wi_index_view* idx, const void* q,
+                          const void* q_prev, const int32_t* sel_prev, float tau, float* out, float* lse,
+                          int32_t* sel_ids, int32_t* reused, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_prev || !sel_prev) return fail(WI_ERR_INVALID_ARG, "q_prev and sel_prev must be non-null");
+  if (std::isnan(tau)) return fail(WI_ERR_INVALID_ARG, "tau is NaN");
+  if (p && p->top_k > 0 && !sel_ids)
+    return fail(WI_ERR_INVALID_ARG, "sel_ids must be non-null: it is the next step's sel_prev");
+  if (p && p->top_k > 0 && p->B > 0 && p->Hq > 0) {
+    const size_t nb = (size_t)p->B * p->Hq * p->top_k * sizeof(int32_t);
+    if (overlaps(sel_prev, nb, sel_ids, nb)) return fail(WI_ERR_INVALID_ARG, "sel_prev and sel_ids overlap");
+  }
+  const Gate gate{q_prev, sel_prev, reused, tau, false};
+  return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, &gate);
+}
+
+wi_status wi_select_refresh(const wi_decode_params* p, const wi_index_view* idx, const void* q,
+                            int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream) {
+  if (p && p->top_k > 0 && !sel_ids) return fail(WI_ERR_INVALID_ARG, "sel_ids must be non-null");
+  if (p && p->top_k == 0) return WI_OK;       // nothing to select
+  const Gate gate{nullptr, nullptr, nullptr, 0.f, true};
+  // out is not written; any non-null pointer passes the shared checks
+  return decode_common(p, idx, q, reinterpret_cast<float*>(workspace), nullptr, sel_ids, workspace, ws_bytes,
+                       stream, &gate);
 }
 
 const char* wi_status_string(wi_status s) {
@@ -370,7 +419,7 @@ wi_status wi_profile_read(double* total_ms, int64_t* launches) {
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
     if (e != hipSuccess) return fail(WI_ERR_HIP, "profiling events: %s", hipGetErrorString(e));
     // a decode stage launched `reps` times back to back between its events counts as that many
-    const int reps = r.stage <= WI_STAGE_MERGE ? r.reps : 1;
+    const int reps = (r.stage <= WI_STAGE_MERGE || r.stage == WI_STAGE_REFRESH) ? r.reps : 1;
     total_ms[r.stage] += ms;
     launches[r.stage] += reps;
   }

@@ -300,7 +300,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   if (tid < G) {
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
     a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
-  }  WI_TP(34);
+  }
+  WI_TP(34);
 }
 
 // ============================================================================ k_select
@@ -498,14 +499,15 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
 // or a head whose best clusters crowd a few tiles) t is found by a radix select over all scores
 // and the split by a second pass.  The head's list (ascending id: cluster, first row, first
 // token, score key) and the entry of every attention workgroup's first token are published last.
+static_assert(kMaxGroup * kD <= kCandCap, "a KV group's queries are staged in the candidate arrays");
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ uint32_t skey[kSumCap];                 // tile summaries: score keys
   __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
                                                      // ascending retrieved list
-  __shared__ uint32_t ckey[kCandCap];                // candidates: score keys
-  __shared__ int cidl[kCandCap];                     // candidates: cluster ids
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[kCandCap];   // candidates: score keys
+  __shared__ __attribute__((aligned(16))) int cidl[kCandCap];        // candidates: cluster ids
   __shared__ int tfull[kFullCap];                    // tiles whose 8 best pass the threshold
   __shared__ int rl_off[kCandCap];                   // retrieved list, by rank: first row, size
   __shared__ int rl_sz[kCandCap];
@@ -514,6 +516,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   __shared__ float fred[32];
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
+  __shared__ double gdd[3 * kMaxGroup];              // gated decode: <q, q'>, |q|^2, |q'|^2 per head
   __shared__ int sh_i[8];
   WI_TP(0);
 
@@ -521,6 +524,8 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / a.G, bg = b * a.Hkv + g;
+  // refresh: only the heads whose group attended over its previous zones select again
+  if (a.refresh && a.gate[bg] == 0) return;
   const int C = a.C, W32 = a.W32, tiles = a.est_tiles_g;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
@@ -546,6 +551,17 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       sid[i] = a.tile_top_id[(size_t)bh * nsum + i];
     }
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
+  // gated decode: the KV group's current and previous queries, staged (exact in fp32) in the
+  // candidate arrays, which are not used before the zone is decided
+  float* gq = reinterpret_cast<float*>(ckey);
+  float* gp = reinterpret_cast<float*>(cidl);
+  if (a.gated) {
+    const size_t row0 = ((size_t)b * a.Hq + (size_t)g * a.G) * kD;
+    for (int i = tid; i < a.G * kD; i += NT) {
+      gq[i] = St<T>::f(static_cast<const T*>(a.q)[row0 + i]);
+      gp[i] = St<T>::f(static_cast<const T*>(a.q_prev)[row0 + i]);
+    }
+  }
   {
     float v0 = (float)ne, v1 = mxn, v2 = qv;
     v0 = wave_sum(v0); v1 = wave_max(v1); v2 = wave_sum(v2);
@@ -559,6 +575,51 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   WI_TP(3);
   const int n_ne = ne;
   const int k_eff = min(a.top_k, n_ne);
+  // gated decode: the KV group keeps its heads' previous zones when every one of its query heads
+  // moved by a cosine of at least tau, <q, q'> / (|q| |q'|) from canonical fp64 sums (ascending
+  // coordinate order) with IEEE square roots and division, 0 when either query is zero.  Every
+  // head of the group takes the same decision from the same sums.
+  bool reuse = false;
+  if (a.gated) {
+    if (tid < 3 * a.G) {                      // thread 3 j + {0, 1, 2}: <q_j, q'_j>, |q_j|^2, |q'_j|^2
+      const int j = tid / 3, kind = tid - 3 * j;
+      const f32x4_t* x = reinterpret_cast<const f32x4_t*>((kind == 2 ? gp : gq) + j * kD);
+      const f32x4_t* y = reinterpret_cast<const f32x4_t*>((kind == 1 ? gq : gp) + j * kD);
+      // products of fp32 values are exact in fp64, so a fused multiply-add rounds as the sum does
+      double acc = 0.0;
+#pragma unroll 8
+      for (int e = 0; e < kD / 4; ++e) {
+        const f32x4_t u = x[e], v = y[e];
+        acc = acc + (double)u[0] * (double)v[0];
+        acc = acc + (double)u[1] * (double)v[1];
+        acc = acc + (double)u[2] * (double)v[2];
+        acc = acc + (double)u[3] * (double)v[3];
+      }
+      gdd[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      bool ok = true;
+      if (tid < a.G) {
+        const double dq = gdd[3 * tid], n1 = gdd[3 * tid + 1], n2 = gdd[3 * tid + 2];
+        const double cs = (n1 == 0.0 || n2 == 0.0) ? 0.0 : dq / (sqrt(n1) * sqrt(n2));
+        ok = cs >= (double)a.tau;
+      }
+      const bool all_ok = __ballot(!ok) == 0ull;
+      if (tid == 0) {
+        sh_i[6] = all_ok ? 1 : 0;
+        if (h == g * a.G) {
+          a.gate[bg] = all_ok ? 1 : 0;
+          if (a.reused) a.reused[bg] = all_ok ? 1 : 0;
+        }
+      }
+    }
+    __syncthreads();
+    reuse = sh_i[6] != 0;
+  } else if (!a.refresh && tid == 0 && h == g * a.G) {
+    a.gate[bg] = 0;                           // a refresh after a plain decode has nothing to do
+  }
+  int n_reused_ne = 0;              // non-empty clusters of a reused zone
 
   auto visit_keys = [&](auto&& fn) {           // fn(c, key) for every cluster of this thread
     for (int j0 = 0; j0 < KPT; j0 += 16) {
@@ -578,7 +639,19 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
 
   bool fast_pub = false;            // the retrieved clusters are all LDS candidates
   int co[kCandCap / NT], ce[kCandCap / NT];
-  if (k_eff > 0 && k_eff == n_ne) {
+  if (reuse) {
+    // the previous zone: its ids in [0, C), each once (the bitmap drops repeats)
+    const int32_t* sp = a.sel_prev + (size_t)bh * a.top_k;
+    int cnt = 0;
+    for (int i = tid; i < a.top_k; i += NT) {
+      const int c = sp[i];
+      if (c >= 0 && c < C) {
+        const uint32_t old = atomicOr(&bits[c >> 5], 1u << (c & 31));
+        if (!((old >> (c & 31)) & 1u) && keys[c] != 0u) ++cnt;
+      }
+    }
+    n_reused_ne = block_isum<NT>(cnt, iscr);
+  } else if (k_eff > 0 && k_eff == n_ne) {
     visit_keys([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
     // delta bounds |fp32 score - canonical fp64 score| for every cluster: fp32 accumulation of d
@@ -745,6 +818,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   // of the attention kernel, the list entry that holds its first retrieved token
   {
     const int K = a.top_k, S = a.att_split;
+    const bool lists = !a.refresh;            // refresh: sel_ids only (attention may read the lists)
     // ascending retrieved ids (LDS when they fit); on the candidate path each retrieved
     // candidate also drops its prefetched first row, size and key at its rank
     int32_t* rl = K <= kSumCap ? sid : a.band_ids + (size_t)bh * C;
@@ -822,10 +896,12 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
         const int i = i0 + u;
         if (i < tot) {
           if (out) out[i] = c_[u];
-          a.hl_cid[lb + i] = c_[u];
-          a.hl_row[lb + i] = r_[u];
-          a.hl_pre[pb + i] = t;
-          a.hl_key[lb + i] = k_[u];
+          if (lists) {
+            a.hl_cid[lb + i] = c_[u];
+            a.hl_row[lb + i] = r_[u];
+            a.hl_pre[pb + i] = t;
+            a.hl_key[lb + i] = k_[u];
+          }
           if (tot <= kSumCap) skey[i] = (uint32_t)t;
           t += z_[u];
         }
@@ -835,7 +911,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); the entry holding its
     // first retrieved token max(that start, NS): the last entry whose first token is <= it
     __syncthreads();
-    if (tot > 0) {
+    if (lists && tot > 0) {
       for (int x = tid; x < S; x += NT) {
         const int u = max((int)(((int64_t)x * ntok) / S), a.NS);
         int lo = 0, hi = tot;                      // first token of entry lo <= u < that of hi
@@ -849,12 +925,13 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
     for (int i = tot + tid; i < K; i += NT) {
       if (out) out[i] = -1;
-      a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok;
+      if (lists) { a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok; }
     }
+    if (!lists) return;
     if (tid == 0) a.hl_pre[pb + K] = (int)ntok;
     if (tot == 0) for (int x = tid; x < S; x += NT) bounds[x] = 0;
   }
-  if (tid == 0) a.all_sel[bh] = (k_eff == n_ne) ? 1 : 0;
+  if (tid == 0) a.all_sel[bh] = (reuse ? n_reused_ne == n_ne : k_eff == n_ne) ? 1 : 0;
   WI_TP(9);
 }
 
@@ -1370,6 +1447,20 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <typename T>
+static hipError_t launch_refresh_t(const DecodeArgs& a, hipStream_t s) {
+  const int BH = a.B * a.Hq;
+  prof_begin(WI_STAGE_REFRESH, s);
+  for (int r = 0; r < prof_reps(); ++r) {
+    if (BH > kSelHeadsPerRound)
+      hipLaunchKernelGGL((k_select<T, kSelThreadsMany>), dim3(BH), dim3(kSelThreadsMany), (size_t)a.W32 * 8, s, a);
+    else
+      hipLaunchKernelGGL((k_select<T, kSelThreadsFew>), dim3(BH), dim3(kSelThreadsFew), (size_t)a.W32 * 8, s, a);
+  }
+  prof_end(WI_STAGE_REFRESH, s);
+  return hipGetLastError();
+}
+
+template <typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   switch (a.G) {
     case 1: return launch_groups<T, 1>(a, s);
@@ -1380,7 +1471,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
-hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
+static hipError_t set_select_lds() {
   static bool attr_set = false;
   if (!attr_set) {
     // the select kernel's two cluster bitmaps (2 * ceil(C / 32) words) live in dynamic LDS
@@ -1394,7 +1485,19 @@ hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStre
     }
     attr_set = true;
   }
+  return hipSuccess;
+}
+
+hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
+  const hipError_t e = set_select_lds();
+  if (e != hipSuccess) return e;
   return p.dtype == WI_BF16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);
+}
+
+hipError_t launch_refresh(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s) {
+  const hipError_t e = set_select_lds();
+  if (e != hipSuccess) return e;
+  return p.dtype == WI_BF16 ? launch_refresh_t<uint16_t>(a, s) : launch_refresh_t<float>(a, s);
 }
 
 }  // namespace wi

@@ -77,19 +77,6 @@ __device__ __forceinline__ uint64_t f64_order_key(double x) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Canonical fp64 score: sum over j ascending of x_j * y_j, each product exact (both operands
-// carry at most 24 significant bits), one rounding per addition, no contraction into FMA.
-template <typename T>
-__device__ __noinline__ double canonical_dot(const T* __restrict__ x, const T* __restrict__ y) {
-#pragma clang fp contract(off)
-  double acc = 0.0;
-  for (int j = 0; j < kD; ++j) {
-    const double p = (double)St<T>::f(x[j]) * (double)St<T>::f(y[j]);
-    acc = acc + p;
-  }
-  return acc;
-}
-
 // ------------------------------------------------------------------ wave / block reductions
 // Lane exchanges inside a DPP row of 16 lanes (VALU operand modifiers, no LDS traffic):
 // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,

@@ -29,7 +29,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
   int BG, BH, G, W32, est_tiles_g, att_split, att_items;
-  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel,
+  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate,
       off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
 };
@@ -70,12 +70,21 @@ struct DecodeArgs {
   float* est_num;          // [BG, est_tiles_g, G, d]
   float* att_md;           // [BH, S + Sc, 2]
   float* att_num;          // [BH, S + Sc, d]
+  // selection reuse (gated decode; gated == 0 otherwise)
+  const void* q_prev;      // [BH, d] the previous step's queries
+  const int32_t* sel_prev; // [BH, top_k] the previous step's retrieved ids
+  int32_t* reused;         // [BG] or null: 1 where the KV head reused its heads' zones
+  int32_t* gate;           // [BG] workspace: the same flags, kept for a later refresh
+  float tau;
+  int gated;
+  int refresh;             // select only: fresh zones for the groups gate[] marks, into sel_ids
   // shapes
   int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, est_tiles_g, att_split, att_items;
   float scale;
 };
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_refresh(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ profiling hook
 extern bool g_prof_on;

@@ -22,10 +22,10 @@ LIB_PATH = os.path.join(_HERE, "libwave_index.so")
 WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0, -1, -2, -3, -4
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
-            "wi_decode_workspace_bytes", "wi_decode",
+            "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated", "wi_select_refresh",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
-          "final")
+          "final", "refresh")
 
 
 class WaveIndexError(RuntimeError):
@@ -82,13 +82,18 @@ def lib() -> ctypes.CDLL:
         L.wi_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
         L.wi_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
                                 vp, vp, sz, vp]
+        L.wi_decode_gated.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
+                                      ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+        L.wi_select_refresh.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, sz,
+                                        vp]
         L.wi_status_string.argtypes = [ctypes.c_int]
         L.wi_profile_enable.argtypes = [ctypes.c_int]
         L.wi_profile_enable.restype = ctypes.c_int
         L.wi_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
-                     "wi_decode_workspace_bytes", "wi_decode"):
+                     "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated",
+                     "wi_select_refresh"):
             getattr(L, name).restype = ctypes.c_int
         L.wi_status_string.restype = ctypes.c_char_p
         L.wi_last_error.restype = ctypes.c_char_p
@@ -139,6 +144,19 @@ def wi_decode(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_pt
               sel_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_decode(ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr,
                                   sel_ptr, ws_ptr, ws_bytes, stream))
+
+
+def wi_decode_gated(p: DecodeParams, view: IndexView, q_ptr: int, q_prev_ptr: int, sel_prev_ptr: int,
+                    tau: float, out_ptr: int, lse_ptr: Optional[int], sel_ptr: Optional[int],
+                    reused_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_decode_gated(ctypes.byref(p), ctypes.byref(view), q_ptr, q_prev_ptr, sel_prev_ptr,
+                                        tau, out_ptr, lse_ptr, sel_ptr, reused_ptr, ws_ptr, ws_bytes, stream))
+
+
+def wi_select_refresh(p: DecodeParams, view: IndexView, q_ptr: int, sel_ptr: Optional[int], ws_ptr: int,
+                      ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_select_refresh(ctypes.byref(p), ctypes.byref(view), q_ptr, sel_ptr, ws_ptr, ws_bytes,
+                                          stream))
 
 
 def wi_profile_enable(enable, repeats: int = 1) -> int:
@@ -293,3 +311,34 @@ def decode(index: Index, q, top_k: int, scale: Optional[float] = None, workspace
     wi_decode(p, index.view(), q.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(sel),
               workspace.data_ptr(), workspace.numel(), _stream(q.device))
     return out, lse, sel
+
+
+def decode_gated(index: Index, q, q_prev, sel_prev, top_k: int, tau: float, scale: Optional[float] = None,
+                 workspace=None, refresh: bool = False):
+    """Decode step attending over sel_prev ([B,Hq,k] int32) for every KV head whose query heads
+    all moved by a cosine >= tau.  Returns (out, lse, sel, reused [B,Hkv]): sel holds the zones
+    attended over, or with refresh=True the top-k of q for every head (wi_select_refresh)."""
+    import torch
+    assert q.is_cuda and q.is_contiguous() and q_prev.shape == q.shape and q_prev.dtype == q.dtype
+    assert q_prev.is_contiguous() and sel_prev.dtype == torch.int32 and sel_prev.is_contiguous()
+    B, Hq, d = q.shape
+    Hkv = index.centroids.shape[1]
+    assert tuple(sel_prev.shape) == (B, Hq, top_k)
+    p = decode_params(index, B, Hq, Hkv, top_k, q.dtype, scale)
+    p.d = d
+    p.dtype = _dtype_code(q)
+    need = wi_decode_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sel = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    reused = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    view = index.view()
+    wi_decode_gated(p, view, q.data_ptr(), q_prev.data_ptr(), sel_prev.data_ptr(), float(tau),
+                    out.data_ptr(), lse.data_ptr(), sel.data_ptr(), reused.data_ptr(), workspace.data_ptr(),
+                    workspace.numel(), _stream(q.device))
+    if refresh:
+        wi_select_refresh(p, view, q.data_ptr(), sel.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                          _stream(q.device))
+    return out, lse, sel, reused

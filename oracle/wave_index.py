@@ -45,7 +45,7 @@ Parity pins (tests/test_oracle.py), per function:
                           step's own selection equals decode; reusing "every cluster" equals
                           dense attention; exact cosines of q with q, 2q and -q decide as
                           their closed forms; one drifting head makes its whole KV group
-                          re-select
+                          re-select; the refreshed selection equals decode's for every head
 Approximation quality against dense attention is "parity unpinned": the pages claim only
 comparable accuracy, with no figure.
 """
@@ -442,7 +442,9 @@ def decode(Q: np.ndarray, idx: Index, Hq: int, k: int, scale: Optional[float] = 
 # head is computed, and a KV head whose query heads all have C >= tau reuses their previous
 # retrieval zones (reading R26); every other KV head selects afresh.  Scoring still runs for
 # every head, because the estimation zone (every non-empty cluster outside the reused zone)
-# needs the current query's scores (reading R27).
+# needs the current query's scores (reading R27).  For the heads that kept their zone, the
+# selection of the current query is not skipped but postponed past this step's attention: it is
+# what the next step reuses, so a kept zone is always one step old (``refresh``, reading R28).
 # --------------------------------------------------------------------------------------------
 def query_cosine(q: np.ndarray, q_prev: np.ndarray) -> float:
     """<q, q'> / (||q|| ||q'||) from canonical sums (ascending coordinate order, exact products),
@@ -456,10 +458,12 @@ def query_cosine(q: np.ndarray, q_prev: np.ndarray) -> float:
 
 
 def decode_gated(Q: np.ndarray, Q_prev: np.ndarray, sel_prev: np.ndarray, idx: Index, Hq: int, k: int,
-                 tau: float, scale: Optional[float] = None):
+                 tau: float, scale: Optional[float] = None, refresh: bool = False):
     """Batched decode with selection reuse: as ``decode``, except that a KV head whose query heads
     all satisfy query_cosine(q, q_prev) >= tau takes each head's retrieval zone from ``sel_prev``
-    [B,Hq,k] (ascending ids, -1 padded).  Returns (o, lse, sel, reused [B,Hkv] bool)."""
+    [B,Hq,k] (cluster ids; entries outside [0, C) are skipped and repeats count once).  Returns
+    (o, lse, sel, reused [B,Hkv] bool); sel is the zone each head attended over, or with
+    ``refresh`` the top-k of the current query for every head (the postponed selection)."""
     Q = np.asarray(Q, dtype=np.float64)
     Q_prev = np.asarray(Q_prev, dtype=np.float64)
     B, _, d = Q.shape
@@ -479,9 +483,13 @@ def decode_gated(Q: np.ndarray, Q_prev: np.ndarray, sel_prev: np.ndarray, idx: I
             for h in heads:
                 R = None
                 if reuse:
+                    # the previous zone: its ids in [0, C), each once (-1 pads the list)
                     prev = np.asarray(sel_prev[b, h])
-                    R = np.sort(prev[prev >= 0]).astype(np.int64)
+                    R = np.unique(prev[(prev >= 0) & (prev < idx.C)]).astype(np.int64)
                 oh, lh, Rh = decode_head(Q[b, h], idx, b, g, k, scale, R)
                 o[b, h], lse[b, h] = oh, lh
+                if refresh and reuse:
+                    sigma = canonical_scores(Q[b, h][None, :], idx.centroids[b, g])[0] if idx.C > 0 else np.zeros(0)
+                    Rh = _select(sigma, idx.sizes[b, g], k)
                 sel[b, h, :Rh.size] = Rh
     return o, lse, sel, reused

@@ -187,6 +187,41 @@ def test_decode_rejects_null_pointers_and_small_workspace():
     assert e.value.status == wi.WI_ERR_WORKSPACE
 
 
+def test_decode_gated_rejects_missing_gate_inputs_and_aliasing():
+    p = _dparams()
+    need = wi.wi_decode_workspace_bytes(p)
+    sel_bytes = p.B * p.Hq * p.top_k * 4
+    far = FAKE + (1 << 30)
+
+    def call(**kw):
+        a = dict(q_prev=FAKE + 4096, sel_prev=far, tau=0.9, sel=far + sel_bytes, ws=FAKE, ws_bytes=need, p=p)
+        a.update(kw)
+        with pytest.raises(wi.WaveIndexError) as e:
+            wi.wi_decode_gated(a["p"], _view(), FAKE, a["q_prev"], a["sel_prev"], a["tau"], FAKE, None,
+                               a["sel"], None, a["ws"], a["ws_bytes"], 0)
+        return e.value.status
+
+    assert call(q_prev=None) == wi.WI_ERR_INVALID_ARG
+    assert call(sel_prev=None) == wi.WI_ERR_INVALID_ARG
+    assert call(tau=float("nan")) == wi.WI_ERR_INVALID_ARG
+    assert call(sel=None) == wi.WI_ERR_INVALID_ARG
+    assert call(sel=far + sel_bytes - 4) == wi.WI_ERR_INVALID_ARG      # last row shared
+    assert call(ws_bytes=need - 1) == wi.WI_ERR_WORKSPACE
+    assert call(p=_dparams(Hq=12)) == wi.WI_ERR_INVALID_ARG              # same checks as wi_decode
+
+
+def test_select_refresh_rejects_null_sel_ids_and_does_nothing_for_top_k_zero():
+    p = _dparams()
+    need = wi.wi_decode_workspace_bytes(p)
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_select_refresh(p, _view(), FAKE, None, FAKE, need, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_select_refresh(p, _view(), FAKE, FAKE, FAKE, need - 1, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+    assert wi.wi_select_refresh(_dparams(top_k=0), _view(), FAKE, None, FAKE, need, 0) == wi.WI_OK
+
+
 def test_build_rejects_null_inputs_and_small_workspace():
     p = wi.BuildParams(1, 8, 4096, 128, 4, 64, 1024, 64, 3, wi.WI_BF16, 1)
     need = wi.wi_index_shapes_for(p).build_workspace_bytes

@@ -483,3 +483,22 @@ def test_gated_one_drifting_head_reselects_its_whole_group():
         assert list(gs[0, h][gs[0, h] >= 0]) == [0]
     np.testing.assert_array_equal(gs[0, G:2 * G], sel[0, G:2 * G])
     np.testing.assert_array_equal(go[0, G:2 * G], o[0, G:2 * G])
+
+
+def test_gated_refresh_postpones_rather_than_skips_the_selection():
+    # with refresh, every head's sel is the current query's own top-k (what the next step keeps),
+    # while the outputs still come from the kept stale zones
+    w, K, V, Q, idx = _gated_setup(4)
+    G = w.Hq // w.Hkv
+    o, lse, sel = oracle.decode(Q, idx, w.Hq, w.top_k)
+    junk = np.full_like(sel, -1)
+    junk[..., 0] = 0
+    Qp = Q.copy()
+    Qp[0, G] = -Q[0, G]
+    go, gl, gs, reused = oracle.decode_gated(Q, Qp, junk, idx, w.Hq, w.top_k, 0.5)
+    fo, fl, fs, freused = oracle.decode_gated(Q, Qp, junk, idx, w.Hq, w.top_k, 0.5, refresh=True)
+    np.testing.assert_array_equal(freused, reused)
+    np.testing.assert_array_equal(fo, go)
+    np.testing.assert_array_equal(fl, gl)
+    np.testing.assert_array_equal(fs, sel)
+    assert not np.array_equal(gs, sel)
