@@ -46,6 +46,15 @@ Parity pins (tests/test_oracle.py), per function:
                           dense attention; exact cosines of q with q, 2q and -q decide as
                           their closed forms; one drifting head makes its whole KV group
                           re-select; the refreshed selection equals decode's for every head
+  bound_data ............ pinned: numpy's own norms within one float32 ulp and never below them;
+                          a cluster of identical keys has radius 0
+  bound_terms,
+  prior_bounds,
+  decode_bounded ........ pinned: the a-posteriori bound covers the distance to dense softmax
+                          attention (textbook and torch SDPA) on random workloads and is
+                          nearly attained (within 2x) by a closed-form two-member cluster; the
+                          zone is the smallest meeting eps, A(k) is non-increasing, eps = 0
+                          gives dense attention with bound 0, a forced k reproduces decode
 Approximation quality against dense attention is "parity unpinned": the pages claim only
 comparable accuracy, with no figure.
 """
@@ -61,7 +70,8 @@ __all__ = [
     "round_to_dtype", "canonical_scores", "splitmix64", "segment_state", "init_rows",
     "steady_positions", "clustered_range", "segment_bounds", "spherical_kmeans_segment",
     "Index", "finalize_index", "build_index", "decode", "decode_head", "decode_gated",
-    "query_cosine",
+    "query_cosine", "BoundData", "bound_data", "sum_roundoff", "bound_terms", "prior_bounds",
+    "decode_bounded",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -493,3 +503,163 @@ def decode_gated(Q: np.ndarray, Q_prev: np.ndarray, sel_prev: np.ndarray, idx: I
                     Rh = _select(sigma, idx.sizes[b, g], k)
                 sel[b, h, :Rh.size] = Rh
     return o, lse, sel, reused
+
+
+# --------------------------------------------------------------------------------------------
+# Accuracy-bounded estimation.  The pages promise a controlled error bound for the estimation
+# zone [RI-es 2.A item 3; RI-ar 2.a, "accuracy-bound attention estimation"] but state no formula;
+# the bound below is derived here (reading R29).  For a query q, scale s, a cluster c with stored
+# mean key mu_c, n_c members, radius r_c = max ||k_i - mu_c|| and largest value norm V_c:
+#   every member's weight e_i = exp(s <q, k_i>) lies within exp(+-s ||q|| r_c) of
+#   e_c = exp(s <q, mu_c>), so |e_i - e_c| <= e_c (exp(x_c) - 1) with x_c = s ||q|| r_c, and
+#   e_i >= e_c exp(-x_c).
+# With E the estimated clusters, D_x the exact part's denominator, o the dense output and o^ the
+# method's, o - o^ = [sum_E sum_i (e_i - e_c)(v_i - o^) + sum_E e_c (SumV_c - SV_c)] / D, hence
+#   ||o - o^|| <= sum_E [n_c e_c (exp(x_c) - 1)(V_c + ||o^||) + e_c u n_c V_c]
+#                 / (D_x + sum_E n_c e_c exp(-x_c))
+# where u is the unit roundoff of the stored value sums SV_c (2^-8 bf16, 2^-24 fp32).  Before the
+# attention, D_x >= sum over the retrieved clusters of n_c e_c exp(-x_c) and ||o^|| <=
+# (1 + u) V_all (the largest value norm of the context) give the a-priori bound A(k) of the zone
+# made of the k first clusters in the selection order; the zone size is the smallest k with
+# A(k) <= eps, capped at top_k (reading R30).
+# --------------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class BoundData:
+    """Per-cluster data of the bound, float64 arrays holding float32 values rounded up."""
+    radius: np.ndarray        # [B,Hkv,C]  max ||k_i - mu_c|| over the members (0 if empty)
+    vnorm: np.ndarray         # [B,Hkv,C]  max ||v_i|| over the members (0 if empty)
+    vmax: np.ndarray          # [B,Hkv]    max ||v|| over every token, steady zone included
+
+
+def _round_up_f32(x: np.ndarray) -> np.ndarray:
+    """Smallest float32 >= x (x >= 0, float64), returned as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    below = f.astype(np.float64) < x
+    f = np.where(below, np.nextafter(f, np.float32(np.inf)), f)
+    return f.astype(np.float64)
+
+
+def _seq_sq_norms(X: np.ndarray) -> np.ndarray:
+    """Row-wise sum over j ascending of X[:, j]^2 in float64 (rounded square, then rounded add)."""
+    acc = np.zeros(X.shape[0])
+    for j in range(X.shape[1]):
+        acc = acc + X[:, j] * X[:, j]
+    return acc
+
+
+def bound_data(idx: Index) -> BoundData:
+    """Radius and value norms of every cluster, and the largest value norm of each (b, g): the
+    squared distances and norms are sums over coordinates in ascending order (differences and
+    squares rounded to float64), maximised over the members, then square-rooted and rounded up to
+    float32."""
+    B, Hkv, C = idx.sizes.shape
+    radius = np.zeros((B, Hkv, C))
+    vnorm = np.zeros((B, Hkv, C))
+    vmax = np.zeros((B, Hkv))
+    for b in range(B):
+        for g in range(Hkv):
+            off = idx.offsets[b, g]
+            dk = np.zeros(idx.Nc)
+            for c in np.nonzero(idx.sizes[b, g] > 0)[0]:
+                rows = slice(off[c], off[c + 1])
+                dk[rows] = _seq_sq_norms(idx.k_perm[b, g, rows] - idx.centroids[b, g, c][None, :])
+            dv = _seq_sq_norms(idx.v_perm[b, g])
+            for c in np.nonzero(idx.sizes[b, g] > 0)[0]:
+                rows = slice(off[c], off[c + 1])
+                radius[b, g, c] = _round_up_f32(math.sqrt(dk[rows].max()))
+                vnorm[b, g, c] = _round_up_f32(math.sqrt(dv[rows].max()))
+            ds = _seq_sq_norms(idx.v_steady[b, g])
+            top = max(dv.max() if dv.size else 0.0, ds.max() if ds.size else 0.0)
+            vmax[b, g] = _round_up_f32(math.sqrt(top))
+    return BoundData(radius=radius, vnorm=vnorm, vmax=vmax)
+
+
+def sum_roundoff(dtype: str) -> float:
+    """Unit roundoff of the stored value sums."""
+    return {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}[dtype]
+
+
+def bound_terms(q: np.ndarray, idx: Index, bd: BoundData, b: int, g: int, scale: float, dtype: str):
+    """Per-cluster terms of the bound for one query head, in the frame m* = max over non-empty
+    clusters of s sigma_c: w_c = n_c exp(s sigma_c - m*), a_c = w_c (exp(x_c) - 1),
+    err_c = a_c (V_c + (1 + u) V_all) + w_c u V_c, lo_c = w_c exp(-x_c); zero for empty clusters.
+    Returns (sigma, order, m*, w, a, err, lo) with ``order`` the non-empty clusters in the
+    selection order (-sigma_c, c)."""
+    sizes = idx.sizes[b, g]
+    sigma = canonical_scores(q[None, :], idx.centroids[b, g])[0] if idx.C > 0 else np.zeros(0)
+    ne = np.nonzero(sizes > 0)[0]
+    order = ne[np.lexsort((ne, -sigma[ne]))]
+    qn = math.sqrt(canonical_scores(q[None, :], q[None, :])[0, 0])
+    u = sum_roundoff(dtype)
+    w = np.zeros(idx.C)
+    a = np.zeros(idx.C)
+    err = np.zeros(idx.C)
+    lo = np.zeros(idx.C)
+    mstar = float((scale * sigma[ne]).max()) if ne.size else 0.0
+    if ne.size:
+        x = scale * qn * bd.radius[b, g, ne]
+        w[ne] = sizes[ne] * np.exp(scale * sigma[ne] - mstar)
+        a[ne] = w[ne] * np.expm1(x)
+        err[ne] = a[ne] * (bd.vnorm[b, g, ne] + (1 + u) * bd.vmax[b, g]) + w[ne] * u * bd.vnorm[b, g, ne]
+        lo[ne] = w[ne] * np.exp(-x)
+    return sigma, order, mstar, w, a, err, lo
+
+
+def prior_bounds(err: np.ndarray, lo: np.ndarray, order: np.ndarray) -> np.ndarray:
+    """A(k) for k = 0 .. len(order): the err_c of the clusters after the first k of ``order``,
+    summed, over the sum of every lo_c."""
+    den = lo[order].sum()
+    tail = err[order][::-1].cumsum()[::-1]            # tail[k] = sum of err over order[k:]
+    A = np.zeros(order.size + 1)
+    if order.size:
+        A[:-1] = tail / den
+    return A
+
+
+def decode_bounded(Q: np.ndarray, idx: Index, bd: BoundData, Hq: int, k_max: int, eps: float,
+                   dtype: str, scale: Optional[float] = None, k_force: Optional[np.ndarray] = None):
+    """Decode with accuracy-bounded zone sizing: each head retrieves the k first clusters of its
+    selection order, k the smallest in [0, min(k_max, #non-empty)] with A(k) <= eps (else the
+    cap).  ``k_force`` [B,Hq] imposes k instead.  Returns (o, lse, sel [B,Hq,k_max], k [B,Hq],
+    A(k) [B,Hq], bound [B,Hq]) with bound the a-posteriori bound on ||o - dense attention||."""
+    Q = np.asarray(Q, dtype=np.float64)
+    B, _, d = Q.shape
+    Hkv = idx.centroids.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    u = sum_roundoff(dtype)
+    o = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    sel = np.full((B, Hq, k_max), -1, dtype=np.int64)
+    ks = np.zeros((B, Hq), dtype=np.int64)
+    prior = np.zeros((B, Hq))
+    post = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            q = Q[b, h]
+            sigma, order, mstar, w, a, err, lo = bound_terms(q, idx, bd, b, g, scale, dtype)
+            A = prior_bounds(err, lo, order)
+            cap = min(int(k_max), order.size)
+            if k_force is not None:
+                k = int(k_force[b, h])
+            else:
+                ok = np.nonzero(A[:cap + 1] <= eps)[0]
+                k = int(ok[0]) if ok.size else cap
+            R = np.sort(order[:k])
+            oh, lh, _ = decode_head(q, idx, b, g, k, scale, R)
+            o[b, h], lse[b, h] = oh, lh
+            sel[b, h, :k] = R
+            ks[b, h] = k
+            prior[b, h] = A[k]
+            # exact part's denominator in the frame m*: steady rows and the zone's rows
+            off = idx.offsets[b, g]
+            rows = np.concatenate([np.arange(off[c], off[c + 1]) for c in R]) if k else np.zeros(0, np.int64)
+            Kx = np.concatenate([idx.k_steady[b, g], idx.k_perm[b, g][rows]])
+            Dx = float(np.exp((Kx @ q) * scale - mstar).sum()) if Kx.shape[0] else 0.0
+            E = order[k:]
+            num = (a[E] * (bd.vnorm[b, g, E] + np.linalg.norm(oh))).sum() + (w[E] * u * bd.vnorm[b, g, E]).sum()
+            post[b, h] = num / (Dx + lo[E].sum()) if E.size else 0.0
+    return o, lse, sel, ks, prior, post

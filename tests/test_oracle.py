@@ -502,3 +502,129 @@ def test_gated_refresh_postpones_rather_than_skips_the_selection():
     np.testing.assert_array_equal(fl, gl)
     np.testing.assert_array_equal(fs, sel)
     assert not np.array_equal(gs, sel)
+
+
+# ------------------------------------------------------------------ accuracy-bounded estimation
+def _bounded_setup(seed=0, dtype="bf16", q_scale=1.5, key_noise=0.3):
+    w = _small_workload(dtype=dtype, q_scale=q_scale, key_noise=key_noise)
+    K, V, Q = _inputs(w, seed)
+    idx = oracle.build_index(K, V, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 3, dtype)
+    return w, K, V, Q, idx, oracle.bound_data(idx)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bound_data_matches_a_brute_force_norm(dtype):
+    # radius and value norms from numpy's own norm (another summation): within one float32 ulp,
+    # and never below the exact distance
+    w, K, V, Q, idx, bd = _bounded_setup(1, dtype)
+    for g in range(w.Hkv):
+        off = idx.offsets[0, g]
+        for c in np.nonzero(idx.sizes[0, g])[0]:
+            kr = idx.k_perm[0, g, off[c]:off[c + 1]]
+            r = np.linalg.norm(kr - idx.centroids[0, g, c], axis=1).max()
+            vn = np.linalg.norm(idx.v_perm[0, g, off[c]:off[c + 1]], axis=1).max()
+            for got, ref in ((bd.radius[0, g, c], r), (bd.vnorm[0, g, c], vn)):
+                assert got >= ref * (1 - 1e-15)
+                assert got <= np.nextafter(np.float32(ref), np.float32(np.inf)) * (1 + 1e-7)
+        allv = np.concatenate([idx.v_perm[0, g], idx.v_steady[0, g]])
+        vm = np.linalg.norm(allv, axis=1).max()
+        assert vm * (1 - 1e-15) <= bd.vmax[0, g] <= np.nextafter(np.float32(vm), np.float32(np.inf)) * (1 + 1e-7)
+        assert bd.vmax[0, g] >= bd.vnorm[0, g].max()
+        assert (bd.radius[0, g][idx.sizes[0, g] == 0] == 0).all()
+
+
+def test_cluster_of_identical_keys_has_radius_zero():
+    rng = np.random.default_rng(2)
+    d, C = 128, 4
+    u = oracle.round_to_dtype(rng.standard_normal(d) / math.sqrt(d), "bf16")
+    K = oracle.round_to_dtype(rng.standard_normal((1, 1, 12, d)) / math.sqrt(d), "bf16")
+    V = oracle.round_to_dtype(rng.standard_normal((1, 1, 12, d)), "bf16")
+    labels = np.array([[[0, 1, 0, 2, 0, 3, 0, 1]]])
+    K[0, 0, 2:10][labels[0, 0] == 0] = u          # clustered positions 2..9 (sink 2, window 2)
+    idx = oracle.finalize_index(K, V, labels, 2, 2, C, "bf16")
+    bd = oracle.bound_data(idx)
+    assert bd.radius[0, 0, 0] == 0.0 and (bd.radius[0, 0, 1:] > 0).all()
+    _, _, _, w_, a_, err, _ = oracle.bound_terms(rng.standard_normal(d), idx, bd, 0, 0, 1 / math.sqrt(d), "bf16")
+    assert a_[0] == 0.0 and err[0] == w_[0] * 2.0 ** -8 * bd.vnorm[0, 0, 0]
+
+
+@pytest.mark.parametrize("seed,dtype,q_scale,key_noise", [(3, "bf16", 1.5, 0.3), (4, "f32", 1.5, 0.3),
+                                                          (5, "bf16", 6.0, 0.1), (6, "bf16", 1.0, 1.0)])
+@pytest.mark.parametrize("eps", [0.02, 0.3, 3.0])
+def test_bounded_decode_error_is_within_its_bound(seed, dtype, q_scale, key_noise, eps):
+    # the derived bound against dense softmax attention over the same stored keys and values
+    w, K, V, Q, idx, bd = _bounded_setup(seed, dtype, q_scale, key_noise)
+    k_max = idx.C
+    o, lse, sel, ks, prior, post = oracle.decode_bounded(Q, idx, bd, w.Hq, k_max, eps, dtype)
+    G = w.Hq // w.Hkv
+    scale = 1 / math.sqrt(w.d)
+    for h in range(w.Hq):
+        ro, _ = _dense(Q[0, h], K[0, h // G], V[0, h // G], scale)
+        err = float(np.linalg.norm(o[0, h] - ro))
+        assert err <= post[0, h] * (1 + 1e-9) + 1e-12, (h, err, post[0, h])
+        assert post[0, h] <= prior[0, h] * (1 + 1e-12) + 1e-300
+        assert prior[0, h] <= eps                   # k_max covers every cluster: never capped
+
+
+def test_bounded_zone_is_the_smallest_that_meets_eps():
+    w, K, V, Q, idx, bd = _bounded_setup(7)
+    G = w.Hq // w.Hkv
+    scale = 1 / math.sqrt(w.d)
+    for eps in (0.0, 0.05, 0.5, 5.0, np.inf):
+        o, lse, sel, ks, prior, post = oracle.decode_bounded(Q, idx, bd, w.Hq, idx.C, eps, "bf16")
+        for h in range(w.Hq):
+            sigma, order, mstar, w_, a_, err, lo = oracle.bound_terms(Q[0, h], idx, bd, 0, h // G, scale, "bf16")
+            A = oracle.prior_bounds(err, lo, order)
+            assert (np.diff(A) <= 0).all()
+            k = ks[0, h]
+            assert A[k] <= eps and (k == 0 or A[k - 1] > eps)
+            assert list(sel[0, h][:k]) == sorted(order[:k]) and (sel[0, h][k:] == -1).all()
+        if eps == 0.0:                              # everything retrieved: dense, bound 0
+            assert (ks == (idx.sizes[0] > 0).sum(axis=1).repeat(G)[None]).all() and (post == 0).all()
+        if eps == np.inf:
+            assert (ks == 0).all()
+
+
+def test_bounded_zone_is_capped_by_top_k_and_forced_k_reproduces_decode():
+    w, K, V, Q, idx, bd = _bounded_setup(8)
+    o, lse, sel, ks, prior, post = oracle.decode_bounded(Q, idx, bd, w.Hq, 3, 0.0, "bf16")
+    assert (ks == 3).all() and (prior > 0).all()
+    ro, rl, rs = oracle.decode(Q, idx, w.Hq, 3)
+    np.testing.assert_array_equal(sel, rs)
+    np.testing.assert_array_equal(o, ro)
+    kf = np.array([[0, 1, 2, 5]])
+    o2, _, sel2, ks2, _, _ = oracle.decode_bounded(Q, idx, bd, w.Hq, 5, 0.0, "bf16", k_force=kf)
+    np.testing.assert_array_equal(ks2, kf)
+    for h in range(w.Hq):
+        ro, rl, rs = oracle.decode(Q, idx, w.Hq, int(kf[0, h]))
+        np.testing.assert_array_equal(o2[0, h], ro[0, h])
+        np.testing.assert_array_equal(sel2[0, h][:kf[0, h]], rs[0, h])
+
+
+def test_bound_is_nearly_attained_by_two_opposite_members():
+    # one cluster {mu + r e0, mu - r e0} with values +e2 and -e2 (their sum is 0), two steady
+    # tokens with zero key and zero value, q = t e0: the cluster's estimate contributes nothing to
+    # the numerator while the exact attention leans towards +e2.  Exact error (in closed form)
+    # sinh-like / (2 + 2 cosh x), the bound 2 (e^x - 1 + u) / (2 + 2 e^-x); the ratio is about
+    # 0.64 at x = 0.44, so a bound off by a factor of 2 either way fails
+    d = 128
+    s = 1 / math.sqrt(d)
+    K = np.zeros((1, 1, 4, d))
+    V = np.zeros((1, 1, 4, d))
+    K[0, 0, 1, 1], K[0, 0, 1, 0] = 0.5, 0.25
+    K[0, 0, 2, 1], K[0, 0, 2, 0] = 0.5, -0.25
+    V[0, 0, 1, 2], V[0, 0, 2, 2] = 1.0, -1.0
+    idx = oracle.finalize_index(K, V, np.zeros((1, 1, 2), dtype=np.int64), 1, 1, 1, "bf16")
+    bd = oracle.bound_data(idx)
+    assert bd.radius[0, 0, 0] == 0.25 and bd.vnorm[0, 0, 0] == 1.0 and bd.vmax[0, 0] == 1.0
+    q = np.zeros(d)
+    q[0] = 20.0
+    o, lse, sel, ks, prior, post = oracle.decode_bounded(q[None, None], idx, bd, 1, 1, np.inf, "bf16")
+    assert ks[0, 0] == 0 and np.abs(o).max() == 0.0
+    x = s * 20.0 * 0.25
+    exact = (math.exp(x) - math.exp(-x)) / (2 + math.exp(x) + math.exp(-x))
+    ro, _ = _dense(q, K[0, 0], V[0, 0], s)
+    assert abs(np.linalg.norm(ro) - exact) < 1e-12
+    bound = 2 * (math.expm1(x) + 2.0 ** -8) / (2 + 2 * math.exp(-x))
+    assert abs(post[0, 0] - bound) < 1e-12
+    assert 0.5 * post[0, 0] < exact <= post[0, 0]
