@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--refresh", action="store_true",
                     help="with --gated: each step also runs wi_select_refresh (the postponed top-k of the "
                          "reused groups, which the next step keeps), as in FreeKV")
+    ap.add_argument("--bounded", type=float, default=None, metavar="EPS",
+                    help="time wi_decode_bounded: each head's zone (at most top_k clusters) sized to "
+                         "meet the error bound EPS; the bound data is computed once beforehand")
     ap.add_argument("--build-only", action="store_true",
                     help="time the index build (segmented spherical k-means) instead of the decode step")
     args = ap.parse_args()
@@ -292,6 +295,26 @@ def main():
         wi.wi_decode(p, views[j], qs[i % len(qs)].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
                      ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
 
+    bounded_info = None
+    if args.bounded is not None:
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        bound = wi.bound_data(idx, w.B, w.Hkv, Qt.dtype)
+        b1.record()
+        torch.cuda.synchronize()
+        bounded_info = {"eps": args.bounded, "bound_data_ms": b0.elapsed_time(b1)}
+        bounds = [bound] + [tuple(t.clone() for t in bound) for _ in range(len(insts) - 1)]
+        k_used = torch.empty((w.B, w.Hq), dtype=torch.int32, device=dev)
+        err_b = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+
+        def step(i):
+            j = i % len(insts)
+            r_, vn_, vm_ = bounds[j]
+            wi.wi_decode_bounded(p, views[j], r_.data_ptr(), vn_.data_ptr(), vm_.data_ptr(),
+                                 qs[i % len(qs)].data_ptr(), args.bounded, out.data_ptr(), lse.data_ptr(),
+                                 sel.data_ptr(), k_used.data_ptr(), err_b.data_ptr(), ws.data_ptr(), ws_bytes,
+                                 torch.cuda.current_stream().cuda_stream)
+
     if args.gated is not None:
         # step i reads the zones step i-1 wrote (two buffers: sel_prev and sel_ids may not alias)
         sels = [sel, torch.empty_like(sel)]
@@ -322,6 +345,12 @@ def main():
         reuse_log = None
         sel = sels[(args.warmup - 1) % 2]
     sel_np = sel.cpu().numpy()
+    if bounded_info is not None:
+        kk = k_used.float()
+        eb = err_b.float()
+        bounded_info.update({"k_mean": float(kk.mean()), "k_min": int(kk.min()), "k_max": int(kk.max()),
+                             "top_k_cap": w.top_k, "err_bound_mean": float(eb.mean()),
+                             "err_bound_max": float(eb.max())})
     off_np = idx.offsets.cpu().numpy()
     per_bytes, union_rows = algorithmic_bytes(w, off_np, sel_np)
     step_bytes = sum(per_bytes.values())
@@ -409,6 +438,7 @@ def main():
                    "head_dim": w.d, "context": w.N, "clusters": idx.C, "top_k": w.top_k,
                    "sink": w.sink, "window": w.window, "instances": len(insts),
                    "timing": "eager" if args.no_graph else "hip-graph replay"},
+        "bounded": bounded_info,
         "gated": None if args.gated is None else {"tau": args.gated, "refresh": args.refresh,
                                                   "reused_kv_head_frac": reuse_frac,
                                                   "out_ready_us": 1e3 * sum(avg_ms[k] for k in ("score", "select", "attend", "merge")),

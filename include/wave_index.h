@@ -201,6 +201,49 @@ wi_status wi_decode_gated(const wi_decode_params *p, const wi_index_view *idx, c
 wi_status wi_select_refresh(const wi_decode_params *p, const wi_index_view *idx, const void *q,
                             int32_t *sel_ids, void *workspace, size_t ws_bytes, void *stream);
 
+/* Per-cluster data of the estimation error bound of an index (the pages promise a controlled
+ * error for the estimation zone without a formula: RetroInfer technical summary, section 2.A
+ * item 3; Arabic summary, section 2.a).  With |x|^2 the sum over coordinates in ascending order
+ * of fp64 squares (differences rounded to fp64 first, no fused multiply-add) and sqrt_up(y) the
+ * smallest float f >= 0 with f * f >= y:
+ *   radius [B,Hkv,C] float  sqrt_up(max over the members i of c of |k_i - mu_c|^2), mu_c the
+ *                           stored centroid; 0 for an empty cluster (nullable when C = 0)
+ *   vnorm  [B,Hkv,C] float  sqrt_up(max over the members of |v_i|^2); 0 for an empty cluster
+ *                           (nullable when C = 0)
+ *   vmax   [B,Hkv]   float  sqrt_up(max |v|^2 over every token, steady zone included)
+ * p gives B, Hkv, d, dtype, n_steady, C and Nc as for wi_decode (Hq, top_k and scale are not
+ * read).  The index is only read; the outputs are caller-allocated device buffers.  Errors:
+ * WI_ERR_INVALID_ARG for null pointers or inconsistent sizes, WI_ERR_UNSUPPORTED as wi_decode. */
+wi_status wi_bound_data(const wi_decode_params *p, const wi_index_view *idx, float *radius,
+                        float *vnorm, float *vmax, void *stream);
+
+/* One decode step whose retrieval zone is sized per query head to meet an error bound (the
+ * pages promise a controlled error for the estimation zone without a formula: RetroInfer
+ * technical summary, section 2.A item 3; Arabic summary, section 2.a).  With s = scale, |q| the
+ * query norm, sigma_c the query-centroid score, m* the largest s sigma_c of the head, and the
+ * bound data of wi_bound_data (r_c = radius, V_c = vnorm, V_all = vmax), every non-empty cluster
+ * has w_c = n_c exp(s sigma_c - m*), x_c = s |q| r_c and
+ *   err_c = w_c (exp(x_c) - 1) (V_c + (1 + u) V_all) + w_c u V_c,   lo_c = w_c exp(-x_c),
+ * u the relative rounding bound of the stored value sums (2^-8 + 2^-23 for bf16, 2^-24 for
+ * fp32).  A zone made of the k first non-empty clusters in the order (-sigma_c, c) bounds
+ * |out - dense attention| by A(k) = (sum of err_c outside the zone) / (sum of every lo_c).  The
+ * zone is the smallest k in [0, min(top_k, #non-empty)] with A(k) <= eps (the cap if none); its
+ * clusters are then the top k exactly as wi_decode selects them.  The decisions are taken on
+ * fp32 scores, so a k whose A(k) lies within fp32 rounding of eps may come out one off.
+ *   radius, vnorm [B,Hkv,C], vmax [B,Hkv]  float  from wi_bound_data for this index
+ *   eps                                     >= 0 (inf: the smallest zone, k = 0)
+ *   sel_ids   [B,Hq,top_k] int32  the zone, ascending, -1 padded (nullable)
+ *   k_used    [B,Hq]       int32  the zone size of each head (nullable)
+ *   err_bound [B,Hq]       float  the bound after attention (nullable): the same sums outside
+ *             the zone with |out| in place of (1 + u) V_all and, in the denominator, the exact
+ *             part's total plus the estimated clusters' lo_c; 0 when nothing is estimated
+ * Everything else, and the errors, as wi_decode; also WI_ERR_INVALID_ARG for a null radius,
+ * vnorm (C > 0) or vmax, or eps < 0 or NaN, and WI_ERR_UNSUPPORTED for top_k > 2048. */
+wi_status wi_decode_bounded(const wi_decode_params *p, const wi_index_view *idx, const float *radius,
+                            const float *vnorm, const float *vmax, const void *q, float eps,
+                            float *out, float *lse, int32_t *sel_ids, int32_t *k_used,
+                            float *err_bound, void *workspace, size_t ws_bytes, void *stream);
+
 /* Stages timed by the profiling hook below (one entry per kernel the entry points launch). */
 typedef enum {
   WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA) and the estimation over all

@@ -147,6 +147,7 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_band_key = o;   o = align256(o + BH * C * 8);
   L.off_all_sel = o;    o = align256(o + BH * 4);
   L.off_gate = o;       o = align256(o + BG * 4);
+  L.off_bnd = o;        o = align256(o + BH * 4 * 4);
   L.off_hl_cid = o;     o = align256(o + BH * K * 4);
   L.off_hl_row = o;     o = align256(o + BH * K * 4);
   L.off_hl_pre = o;     o = align256(o + BH * (K + 1) * 4);
@@ -264,6 +265,15 @@ wi_status wi_decode_workspace_bytes(const wi_decode_params* p, size_t* bytes) {
   return WI_OK;
 }
 
+struct Bounded {
+  const float* radius;
+  const float* vnorm;
+  const float* vmax;
+  float eps;
+  int32_t* k_used;
+  float* err_bound;
+};
+
 struct Gate {
   const void* q_prev;
   const int32_t* sel_prev;
@@ -274,7 +284,7 @@ struct Gate {
 
 static wi_status decode_common(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
                                float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream,
-                               const Gate* gate) {
+                               const Gate* gate, const Bounded* bnd = nullptr) {
   if (!p || !idx || !q || !out) return fail(WI_ERR_INVALID_ARG, "params, index, q and out must be non-null");
   if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
     return fail(WI_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and Hkv dividing Hq");
@@ -322,6 +332,7 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
   a.band_key = reinterpret_cast<uint64_t*>(base + L.off_band_key);
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
   a.gate = reinterpret_cast<int32_t*>(base + L.off_gate);
+  a.bnd = reinterpret_cast<float*>(base + L.off_bnd);
   a.hl_cid = reinterpret_cast<int32_t*>(base + L.off_hl_cid);
   a.hl_row = reinterpret_cast<int32_t*>(base + L.off_hl_row);
   a.hl_pre = reinterpret_cast<int32_t*>(base + L.off_hl_pre);
@@ -344,7 +355,13 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
     a.gated = 1; a.q_prev = gate->q_prev; a.sel_prev = gate->sel_prev; a.reused = gate->reused;
     a.tau = gate->tau;
   }
-  return check_hip(wi::launch_decode(*p, a, st), gate ? "wi_decode_gated launch" : "wi_decode launch", st);
+  if (bnd) {
+    a.bounded = 1; a.radius = bnd->radius; a.vnorm = bnd->vnorm; a.vmax = bnd->vmax; a.eps = bnd->eps;
+    a.k_used = bnd->k_used; a.err_bound = bnd->err_bound;
+    a.u = p->dtype == WI_BF16 ? 0x1.0002p-8f : 0x1p-24f;     // 2^-8 + 2^-23 for bfloat16 sums
+  }
+  return check_hip(wi::launch_decode(*p, a, st),
+                   gate ? "wi_decode_gated launch" : bnd ? "wi_decode_bounded launch" : "wi_decode launch", st);
 }
 
 wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
@@ -365,6 +382,19 @@ wi_status wi_decode_gated(const wi_decode_params* p, const wi_index_view* idx, c
   }
   const Gate gate{q_prev, sel_prev, reused, tau, false};
   return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, &gate);
+}
+
+wi_status wi_decode_bounded(const wi_decode_params* p, const wi_index_view* idx, const float* radius,
+                            const float* vnorm, const float* vmax, const void* q, float eps, float* out, float* lse,
+                            int32_t* sel_ids, int32_t* k_used, float* err_bound, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  if (p && p->C > 0 && (!radius || !vnorm)) return fail(WI_ERR_INVALID_ARG, "radius and vnorm must be non-null");
+  if (!vmax) return fail(WI_ERR_INVALID_ARG, "vmax must be non-null");
+  if (!(eps >= 0.f)) return fail(WI_ERR_INVALID_ARG, "eps must be >= 0 (got %g)", (double)eps);
+  if (p && p->top_k > wi::kBoundedMaxTopK)
+    return fail(WI_ERR_UNSUPPORTED, "top_k %d > %d for bounded zone sizing", p->top_k, wi::kBoundedMaxTopK);
+  const Bounded bnd{radius, vnorm, vmax, eps, k_used, err_bound};
+  return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, nullptr, &bnd);
 }
 
 wi_status wi_select_refresh(const wi_decode_params* p, const wi_index_view* idx, const void* q,
@@ -389,6 +419,25 @@ const char* wi_status_string(wi_status s) {
 }
 
 const char* wi_last_error(void) { return g_err; }
+
+wi_status wi_bound_data(const wi_decode_params* p, const wi_index_view* idx, float* radius, float* vnorm,
+                        float* vmax, void* stream) {
+  if (!p || !idx || !vmax) return fail(WI_ERR_INVALID_ARG, "params, index and vmax must be non-null");
+  if (p->B < 1 || p->Hkv < 1) return fail(WI_ERR_INVALID_ARG, "need B, Hkv >= 1");
+  if (p->d != wi::kD) return fail(WI_ERR_UNSUPPORTED, "head dim %d unsupported (only 128)", p->d);
+  if (p->dtype != WI_F32 && p->dtype != WI_BF16) return fail(WI_ERR_INVALID_ARG, "bad dtype %d", p->dtype);
+  if (p->C < 0 || p->Nc < 0 || p->n_steady < 0) return fail(WI_ERR_INVALID_ARG, "negative C, Nc or n_steady");
+  if ((p->C == 0) != (p->Nc == 0)) return fail(WI_ERR_INVALID_ARG, "C and Nc must be both zero or both positive");
+  const int64_t BG = (int64_t)p->B * p->Hkv;
+  if (BG > wi::kMaxGroupsPerDecode) return fail(WI_ERR_UNSUPPORTED, "B * Hkv = %lld > %d", (long long)BG, wi::kMaxGroupsPerDecode);
+  if (BG * ((int64_t)p->Nc + p->n_steady) >= kMaxRows || BG * ((int64_t)p->C + 1) >= kMaxRows)
+    return fail(WI_ERR_UNSUPPORTED, "a buffer would exceed 2^31 rows");
+  if (p->n_steady > 0 && !idx->v_steady) return fail(WI_ERR_INVALID_ARG, "index view has a null v_steady");
+  if (p->C > 0 && (!idx->centroids || !idx->offsets || !idx->k_perm || !idx->v_perm || !radius || !vnorm))
+    return fail(WI_ERR_INVALID_ARG, "null index buffer, radius or vnorm");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return check_hip(wi::launch_bound_data(*p, *idx, radius, vnorm, vmax, st), "wi_bound_data launch", st);
+}
 
 static void prof_clear() {
   for (auto& r : wi::g_prof_recs) {

@@ -500,10 +500,12 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
 // and the split by a second pass.  The head's list (ascending id: cluster, first row, first
 // token, score key) and the entry of every attention workgroup's first token are published last.
 static_assert(kMaxGroup * kD <= kCandCap, "a KV group's queries are staged in the candidate arrays");
+static_assert(kBoundedMaxTopK <= kCandCap && kBoundedMaxTopK <= kSumCap && kBoundedMaxTopK <= kBins,
+              "the bounded select lists its zone in LDS");
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
-  __shared__ uint32_t skey[kSumCap];                 // tile summaries: score keys
+  __shared__ __attribute__((aligned(16))) uint32_t skey[kSumCap];   // tile summaries: score keys
   __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
                                                      // ascending retrieved list
   __shared__ __attribute__((aligned(16))) uint32_t ckey[kCandCap];   // candidates: score keys
@@ -637,6 +639,39 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
   };
 
+  // delta bounds |fp32 score - canonical fp64 score| for every cluster: fp32 accumulation of d
+  // exact-or-rounded products, doubled for an unspecified MFMA summation order
+  const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qv * (1.0 + 1.0 / 1024) *
+                           (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
+
+  // ---- accuracy-bounded zone sizing: error terms of the non-empty clusters in the frame of the
+  // largest logit m*: w = n exp(l - m*), a = w (exp(x) - 1) with x = s |q| r_c, lo = w exp(-x),
+  // err = a (V_c + (1 + u) V_all) + w u V_c.  A zone Z bounds the error of the output by
+  // (sum over the non-empty clusters outside Z of err) / (sum of every lo) before attention.
+  float b_mstar = 0.f;
+  const float b_vall = a.bounded ? a.vmax[bg] : 0.f;
+  // the terms of cluster c from its score key, size n, radius r and value norm vc
+  struct BTerms { float err, lo, ea, eav; };
+  auto bound_terms = [&](uint32_t k, float n, float r, float vc) -> BTerms {
+    const float x = a.scale * qv * r;
+    const float w = n * __expf(f32_from_order_key(k) * a.scale - b_mstar);
+    const float ea = w * expm1f(x);
+    return {ea * (vc + (1.f + a.u) * b_vall) + w * a.u * vc, w * __expf(-x), ea, ea * vc + w * a.u * vc};
+  };
+  if (a.bounded && n_ne > 0) {
+    // m*: the largest score, from the tiles' best scores when they are staged
+    float m = -INFINITY;
+    if (use_sum) {
+      for (int t = tid; t < tiles; t += NT) {
+        const uint32_t k = skey[t * kTileTop];
+        if (k != 0u) m = fmaxf(m, f32_from_order_key(k));
+      }
+    } else {
+      visit_keys([&](int c, uint32_t k) { if (k != 0u) m = fmaxf(m, f32_from_order_key(k)); });
+    }
+    b_mstar = block_max<NT>(m, fred) * a.scale;
+  }
+
   bool fast_pub = false;            // the retrieved clusters are all LDS candidates
   int co[kCandCap / NT], ce[kCandCap / NT];
   if (reuse) {
@@ -654,10 +689,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   } else if (k_eff > 0 && k_eff == n_ne) {
     visit_keys([&](int c, uint32_t k) { if (k != 0u) atomicOr(&bits[c >> 5], 1u << (c & 31)); });
   } else if (k_eff > 0) {
-    // delta bounds |fp32 score - canonical fp64 score| for every cluster: fp32 accumulation of d
-    // exact-or-rounded products, doubled for an unspecified MFMA summation order
-    const double delta = 2.0 * (kD + 2) * 5.9604644775390625e-08 * (double)qv * (1.0 + 1.0 / 1024) *
-                             (double)mxn * (1.0 + 1.0 / 1024) + 1e-30;
     // ---- L = the k_eff-th largest of the tile summaries: a lower bound of t, and t itself
     // when no tile has its 8th best within 2 delta of L (every score >= L is then a summary)
     float thr_f = -INFINITY;
@@ -813,6 +844,161 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   __syncthreads();
   WI_TP(8);
 
+  int k_zone = reuse ? n_reused_ne : k_eff;
+  if (a.bounded) {
+    // the k_eff selected clusters, ascending id, with score keys and error terms (the summary,
+    // candidate, histogram and publish arrays are free until publishing, which rebuilds them)
+    // zo: (score key, id) packed so that a larger value comes first in the order (-score, id)
+    uint64_t* zo = reinterpret_cast<uint64_t*>(skey);
+    int* zi = sid;
+    float* ze = reinterpret_cast<float*>(rl_off);      // err
+    float* zl = reinterpret_cast<float*>(ckey);        // lo
+    float* za = reinterpret_cast<float*>(cidl);        // a
+    float* zv = reinterpret_cast<float*>(hist);        // a V_c + w u V_c
+    const int32_t* szg = a.sizes + (size_t)bg * C;
+    const float* rdg = a.radius + (size_t)bg * C;
+    const float* vng = a.vnorm + (size_t)bg * C;
+    {
+      const int perw = (W32 + NT - 1) / NT;
+      const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+      int n = 0;
+      for (int w = w0; w < w1; ++w) n += __popc(bits[w]);
+      int tot;
+      int p = block_exclusive_scan<NT>(n, iscr, &tot);
+      for (int w = w0; w < w1; ++w) {
+        uint32_t m = bits[w];
+        while (m) { zi[p++] = w * 32 + __ffs(m) - 1; m &= m - 1; }
+      }
+    }
+    __syncthreads();
+    WI_TP(17);
+    // the list's terms: every load of an entry issued before the first is used
+    for (int i0 = 0; i0 < k_eff; i0 += 2 * NT) {
+      int c[2];
+      uint32_t kk[2];
+      float nn[2], rr[2], vv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        c[u] = zi[min(i0 + u * NT + tid, k_eff - 1)];
+        kk[u] = keys[c[u]]; nn[u] = (float)szg[c[u]]; rr[u] = rdg[c[u]]; vv[u] = vng[c[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * NT + tid;
+        if (i < k_eff) {
+          const BTerms t = bound_terms(kk[u], nn[u], rr[u], vv[u]);
+          zo[i] = ((uint64_t)kk[u] << 32) | (uint32_t)(0xffffffffu - (uint32_t)c[u]);
+          ze[i] = t.err; zl[i] = t.lo; za[i] = t.ea; zv[i] = t.eav;
+        }
+      }
+    }
+    // the terms of the non-empty clusters outside the list, summed directly in one pass (a
+    // difference of totals would cancel); loads unconditional (indices clamped), then masked
+    float so = 0.f, slo = 0.f, sa_o = 0.f, sv_o = 0.f;
+    for (int j0 = 0; j0 < KPT; j0 += 8) {
+      uint32_t kk[8];
+      float nn[8], rr[8], vv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = min((j0 + i) * NT + tid, C - 1);
+        kk[i] = keys[c]; nn[i] = (float)szg[c]; rr[i] = rdg[c]; vv[i] = vng[c];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = (j0 + i) * NT + tid;
+        const bool live = c < C && kk[i] != 0u && !((bits[min(c, C - 1) >> 5] >> (c & 31)) & 1u);
+        if (live) {
+          const BTerms t = bound_terms(kk[i], nn[i], rr[i], vv[i]);
+          so += t.err; slo += t.lo; sa_o += t.ea; sv_o += t.eav;
+        }
+      }
+    }
+    const float e_out = block_sum<NT>(so, fred);       // includes barriers: the list is visible
+    WI_TP(18);
+    float le = 0.f, ll = 0.f;
+    for (int i = tid; i < k_eff; i += NT) { le += ze[i]; ll += zl[i]; }
+    const float b_err = e_out + block_sum<NT>(le, fred);
+    const float b_lo = block_sum<NT>(slo, fred) + block_sum<NT>(ll, fred);
+    // k = the smallest zone size whose first clusters (in the order (-score, id)) leave an error
+    // sum <= eps * sum lo: for each entry, its rank and the error of the entries after it come
+    // from one pass over the list
+    const float lim = a.eps * b_lo;
+    int kb = b_err <= lim ? 0 : k_eff;
+    for (int i = tid; i < k_eff; i += NT) {
+      const uint64_t oi = zo[i];
+      int rank = 0;
+      float after = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < k_eff; ++j) {
+        const uint64_t oj = zo[j];
+        const float ej = ze[j];
+        rank += oj > oi ? 1 : 0;
+        after += oj < oi ? ej : 0.f;
+      }
+      rl_sz[i] = rank;
+      if (e_out + after <= lim) kb = min(kb, rank + 1);
+    }
+    k_zone = (int)-block_max<NT>(-(float)kb, fred);
+    WI_TP(19);
+    if (k_zone < k_eff) {
+      // the canonical top k_zone of the list: in above t + 2 delta, out below t - 2 delta, the
+      // band between them ranked by (-canonical score, id); t = the k_zone-th fp32 score
+      for (int w = tid; w < W32; w += NT) bits[w] = 0u;
+      if (tid == 0) { sh_i[7] = 0; sh_i[2] = 0; }
+      __syncthreads();
+      if (k_zone > 0) {
+        for (int i = tid; i < k_eff; i += NT)
+          if (rl_sz[i] == k_zone - 1) sh_i[7] = i;
+        __syncthreads();
+        const double that = (double)f32_from_order_key((uint32_t)(zo[sh_i[7]] >> 32));
+        const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
+        int nin = 0;
+        int32_t* band = a.band_ids + (size_t)bh * C;
+        for (int i = tid; i < k_eff; i += NT) {
+          const double v = (double)f32_from_order_key((uint32_t)(zo[i] >> 32));
+          if (v > hi) { const int c = zi[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
+          else if (v >= lo) band[atomicAdd(&sh_i[2], 1)] = zi[i];
+        }
+        const int need = k_zone - block_isum<NT>(nin, iscr);     // includes a barrier
+        const int n_band = sh_i[2];
+        uint64_t* bkey = a.band_key + (size_t)bh * C;
+        for (int i = tid; i < n_band; i += NT)
+          bkey[i] = f64_order_key(canonical_score_row<T>(qd, mu + (size_t)band[i] * kD));
+        __syncthreads();
+        for (int i = tid; i < n_band; i += NT) {
+          const uint64_t ki = bkey[i];
+          const int ci = band[i];
+          int rank = 0;
+          for (int j = 0; j < n_band; ++j) {
+            const uint64_t kj = bkey[j];
+            rank += (kj > ki || (kj == ki && band[j] < ci)) ? 1 : 0;
+          }
+          if (rank < need) atomicOr(&bits[ci >> 5], 1u << (ci & 31));
+        }
+      }
+      __syncthreads();
+    }
+    WI_TP(24);
+    // sums over the estimated clusters (outside the zone) for the bound after attention: the
+    // clusters outside the list, plus the list entries the zone left out
+    float sa = 0.f, sv = 0.f, sl = 0.f;
+    for (int i = tid; i < k_eff; i += NT) {
+      const int c = zi[i];
+      if ((bits[c >> 5] >> (c & 31)) & 1u) continue;
+      sa += za[i]; sv += zv[i]; sl += zl[i];
+    }
+    sa = block_sum<NT>(sa_o, fred) + block_sum<NT>(sa, fred);
+    sv = block_sum<NT>(sv_o, fred) + block_sum<NT>(sv, fred);
+    sl = block_sum<NT>(slo, fred) + block_sum<NT>(sl, fred);
+    if (tid == 0) {
+      float* bd = a.bnd + (size_t)bh * 4;
+      bd[0] = b_mstar; bd[1] = sa; bd[2] = sv; bd[3] = sl;
+      if (a.k_used) a.k_used[bh] = k_zone;
+    }
+    WI_TP(25);
+    fast_pub = false;
+  }
+
   // ---- publish, in ascending id: sel_ids and the head's list (id, first k_perm row, first
   // token after the steady zone, score key), padded to top_k; then, for every token workgroup
   // of the attention kernel, the list entry that holds its first retrieved token
@@ -931,7 +1117,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     if (tid == 0) a.hl_pre[pb + K] = (int)ntok;
     if (tot == 0) for (int x = tid; x < S; x += NT) bounds[x] = 0;
   }
-  if (tid == 0) a.all_sel[bh] = (reuse ? n_reused_ne == n_ne : k_eff == n_ne) ? 1 : 0;
+  if (tid == 0) a.all_sel[bh] = k_zone == n_ne ? 1 : 0;
   WI_TP(9);
 }
 
@@ -1396,15 +1582,35 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
   }
   sh_acc[rep][col] = acc;
   __syncthreads();
+  float o2 = 0.f;
   if (tid < 32) {
     float4 s = sh_acc[0][tid];
     for (int r = 1; r < RP; ++r) {
       const float4 t = sh_acc[r][tid];
       s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
     }
-    *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * tid) = make_float4(s.x / den, s.y / den, s.z / den, s.w / den);
+    const float4 o = make_float4(s.x / den, s.y / den, s.z / den, s.w / den);
+    *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * tid) = o;
+    o2 = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
   }
   if (tid == 0 && a.lse) a.lse[bh] = M + __logf(den);
+  if (a.bounded) {
+    // error bound of the output: (sum a (V_c + |o|) + w u V_c) / (D_x + sum lo) over the estimated
+    // clusters, their sums taken by the select in the frame m*, D_x = the exact partials' total
+    float dx = 0.f;
+    for (int p = PE + tid; p < PE + S; p += NT) dx += factor(p) * md_of(p)[1];
+    const float Dx = block_sum<NT>(dx, sh_red);
+    const float on = sqrtf(block_sum<NT>(o2, sh_red));
+    if (tid == 0 && a.err_bound) {
+      const float* bd = a.bnd + (size_t)bh * 4;
+      float e = 0.f;
+      if (bd[1] != 0.f || bd[2] != 0.f || bd[3] != 0.f) {
+        const float f = __expf(bd[0] - M);
+        e = (bd[2] + on * bd[1]) * f / (Dx + bd[3] * f);
+      }
+      a.err_bound[bh] = e;
+    }
+  }
   WI_TP(41);
 }
 

@@ -21,6 +21,7 @@ constexpr int kMaxGroupsPerDecode = 65535;  // B * Hkv of one decode call (a gri
 constexpr int kCorrEntries = 64;    // retrieved clusters per correction workgroup
 constexpr int kSelectBitmapLds = 65536;   // dynamic LDS of the select kernel: 2 bitmaps over C
 constexpr int kMaxDecodeClusters = kSelectBitmapLds / 8 * 32;   // C per KV head (262144)
+constexpr int kBoundedMaxTopK = 2048;    // clusters the bounded select ranks in LDS
 constexpr int kAttTarget = 1024;    // attention workgroups one wave of the grid holds (4 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -29,7 +30,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
   int BG, BH, G, W32, est_tiles_g, att_split, att_items;
-  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate,
+  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate, off_bnd,
       off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
 };
@@ -78,6 +79,16 @@ struct DecodeArgs {
   float tau;
   int gated;
   int refresh;             // select only: fresh zones for the groups gate[] marks, into sel_ids
+  // accuracy-bounded zone sizing (bounded == 0 otherwise)
+  const float* radius;     // [BG, C] cluster radius around the stored centroid
+  const float* vnorm;      // [BG, C] largest member value norm
+  const float* vmax;       // [BG]    largest value norm of the context
+  float eps;               // error bound the zone must meet
+  float u;                 // relative rounding bound of the stored value sums
+  int bounded;
+  int32_t* k_used;         // [BH] or null: zone size chosen
+  float* err_bound;        // [BH] or null: bound on |out - dense attention|
+  float* bnd;              // [BH, 4] workspace: m*, sum a, sum (a V + w u V), sum lo over the estimation zone
   // shapes
   int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, est_tiles_g, att_split, att_items;
   float scale;
@@ -85,6 +96,8 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_refresh(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_bound_data(const wi_decode_params& p, const wi_index_view& idx, float* radius, float* vnorm,
+                             float* vmax, hipStream_t s);
 
 // ------------------------------------------------------------------ profiling hook
 extern bool g_prof_on;

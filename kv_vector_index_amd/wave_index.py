@@ -23,6 +23,7 @@ WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0,
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
             "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated", "wi_select_refresh",
+            "wi_bound_data", "wi_decode_bounded",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
           "final", "refresh")
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         L.wi_select_refresh.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, sz,
                                         vp]
+        L.wi_bound_data.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp]
+        L.wi_decode_bounded.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp,
+                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]
         L.wi_status_string.argtypes = [ctypes.c_int]
         L.wi_profile_enable.argtypes = [ctypes.c_int]
         L.wi_profile_enable.restype = ctypes.c_int
@@ -93,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
                      "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated",
-                     "wi_select_refresh"):
+                     "wi_select_refresh", "wi_bound_data", "wi_decode_bounded"):
             getattr(L, name).restype = ctypes.c_int
         L.wi_status_string.restype = ctypes.c_char_p
         L.wi_last_error.restype = ctypes.c_char_p
@@ -156,6 +160,20 @@ def wi_decode_gated(p: DecodeParams, view: IndexView, q_ptr: int, q_prev_ptr: in
 def wi_select_refresh(p: DecodeParams, view: IndexView, q_ptr: int, sel_ptr: Optional[int], ws_ptr: int,
                       ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_select_refresh(ctypes.byref(p), ctypes.byref(view), q_ptr, sel_ptr, ws_ptr, ws_bytes,
+                                          stream))
+
+
+def wi_bound_data(p: DecodeParams, view: IndexView, radius_ptr: Optional[int], vnorm_ptr: Optional[int],
+                  vmax_ptr: int, stream: int) -> int:
+    return _check(lib().wi_bound_data(ctypes.byref(p), ctypes.byref(view), radius_ptr, vnorm_ptr, vmax_ptr, stream))
+
+
+def wi_decode_bounded(p: DecodeParams, view: IndexView, radius_ptr: Optional[int], vnorm_ptr: Optional[int],
+                      vmax_ptr: int, q_ptr: int, eps: float, out_ptr: int, lse_ptr: Optional[int],
+                      sel_ptr: Optional[int], k_ptr: Optional[int], err_ptr: Optional[int], ws_ptr: int,
+                      ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_decode_bounded(ctypes.byref(p), ctypes.byref(view), radius_ptr, vnorm_ptr, vmax_ptr,
+                                          q_ptr, eps, out_ptr, lse_ptr, sel_ptr, k_ptr, err_ptr, ws_ptr, ws_bytes,
                                           stream))
 
 
@@ -342,3 +360,45 @@ def decode_gated(index: Index, q, q_prev, sel_prev, top_k: int, tau: float, scal
         wi_select_refresh(p, view, q.data_ptr(), sel.data_ptr(), workspace.data_ptr(), workspace.numel(),
                           _stream(q.device))
     return out, lse, sel, reused
+
+
+def bound_data(index: Index, B: int, Hkv: int, dtype):
+    """Radius [B,Hkv,C], value norms [B,Hkv,C] and largest value norm [B,Hkv] (float32) of an
+    index: the per-cluster data of the estimation error bound."""
+    import torch
+    dev = index.centroids.device
+    p = decode_params(index, B, Hkv, Hkv, 0, dtype)
+    p.d = index.centroids.shape[-1]
+    p.dtype = WI_BF16 if dtype == torch.bfloat16 else WI_F32
+    radius = torch.empty((B, Hkv, index.C), dtype=torch.float32, device=dev)
+    vnorm = torch.empty((B, Hkv, index.C), dtype=torch.float32, device=dev)
+    vmax = torch.empty((B, Hkv), dtype=torch.float32, device=dev)
+    wi_bound_data(p, index.view(), _ptr(radius) if index.C else None, _ptr(vnorm) if index.C else None,
+                  vmax.data_ptr(), _stream(dev))
+    return radius, vnorm, vmax
+
+
+def decode_bounded(index: Index, q, bound, top_k: int, eps: float, scale: Optional[float] = None,
+                   workspace=None):
+    """Decode with the zone of each head sized to meet an error bound eps; ``bound`` is the
+    (radius, vnorm, vmax) of bound_data.  Returns (out, lse, sel, k_used [B,Hq], err_bound [B,Hq])."""
+    import torch
+    assert q.is_cuda and q.is_contiguous()
+    B, Hq, d = q.shape
+    Hkv = index.centroids.shape[1]
+    radius, vnorm, vmax = bound
+    p = decode_params(index, B, Hq, Hkv, top_k, q.dtype, scale)
+    p.d = d
+    p.dtype = _dtype_code(q)
+    need = wi_decode_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sel = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    k_used = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    err = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    wi_decode_bounded(p, index.view(), _ptr(radius) if index.C else None, _ptr(vnorm) if index.C else None,
+                      vmax.data_ptr(), q.data_ptr(), float(eps), out.data_ptr(), lse.data_ptr(), _ptr(sel),
+                      k_used.data_ptr(), err.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    return out, lse, sel, k_used, err

@@ -517,7 +517,7 @@ def decode_gated(Q: np.ndarray, Q_prev: np.ndarray, sel_prev: np.ndarray, idx: I
 # method's, o - o^ = [sum_E sum_i (e_i - e_c)(v_i - o^) + sum_E e_c (SumV_c - SV_c)] / D, hence
 #   ||o - o^|| <= sum_E [n_c e_c (exp(x_c) - 1)(V_c + ||o^||) + e_c u n_c V_c]
 #                 / (D_x + sum_E n_c e_c exp(-x_c))
-# where u is the unit roundoff of the stored value sums SV_c (2^-8 bf16, 2^-24 fp32).  Before the
+# where u bounds the relative rounding of the stored value sums SV_c (sum_roundoff).  Before the
 # attention, D_x >= sum over the retrieved clusters of n_c e_c exp(-x_c) and ||o^|| <=
 # (1 + u) V_all (the largest value norm of the context) give the a-priori bound A(k) of the zone
 # made of the k first clusters in the selection order; the zone size is the smallest k with
@@ -531,13 +531,19 @@ class BoundData:
     vmax: np.ndarray          # [B,Hkv]    max ||v|| over every token, steady zone included
 
 
-def _round_up_f32(x: np.ndarray) -> np.ndarray:
-    """Smallest float32 >= x (x >= 0, float64), returned as float64."""
-    x = np.asarray(x, dtype=np.float64)
-    f = x.astype(np.float32)
-    below = f.astype(np.float64) < x
-    f = np.where(below, np.nextafter(f, np.float32(np.inf)), f)
-    return f.astype(np.float64)
+def _sqrt_up_f32(d2: float) -> float:
+    """Smallest float32 f >= 0 with f * f >= d2: the square root of d2 >= 0 rounded up to float32
+    (f * f is exact in float64, so the test is exact)."""
+    f = np.float32(math.sqrt(d2))
+    if float(f) * float(f) < d2:
+        f = np.nextafter(f, np.float32(np.inf))
+    else:
+        while f > 0:
+            p = np.nextafter(f, np.float32(0))
+            if float(p) * float(p) < d2:
+                break
+            f = p
+    return float(f)
 
 
 def _seq_sq_norms(X: np.ndarray) -> np.ndarray:
@@ -552,7 +558,7 @@ def bound_data(idx: Index) -> BoundData:
     """Radius and value norms of every cluster, and the largest value norm of each (b, g): the
     squared distances and norms are sums over coordinates in ascending order (differences and
     squares rounded to float64), maximised over the members, then square-rooted and rounded up to
-    float32."""
+    float32 (reading R31)."""
     B, Hkv, C = idx.sizes.shape
     radius = np.zeros((B, Hkv, C))
     vnorm = np.zeros((B, Hkv, C))
@@ -567,17 +573,18 @@ def bound_data(idx: Index) -> BoundData:
             dv = _seq_sq_norms(idx.v_perm[b, g])
             for c in np.nonzero(idx.sizes[b, g] > 0)[0]:
                 rows = slice(off[c], off[c + 1])
-                radius[b, g, c] = _round_up_f32(math.sqrt(dk[rows].max()))
-                vnorm[b, g, c] = _round_up_f32(math.sqrt(dv[rows].max()))
+                radius[b, g, c] = _sqrt_up_f32(dk[rows].max())
+                vnorm[b, g, c] = _sqrt_up_f32(dv[rows].max())
             ds = _seq_sq_norms(idx.v_steady[b, g])
             top = max(dv.max() if dv.size else 0.0, ds.max() if ds.size else 0.0)
-            vmax[b, g] = _round_up_f32(math.sqrt(top))
+            vmax[b, g] = _sqrt_up_f32(top)
     return BoundData(radius=radius, vnorm=vnorm, vmax=vmax)
 
 
 def sum_roundoff(dtype: str) -> float:
-    """Unit roundoff of the stored value sums."""
-    return {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}[dtype]
+    """Relative rounding bound of the stored value sums: float64 -> float32 (2^-24), then for
+    bf16 float32 -> bfloat16 (2^-8), compounded (2^-8 + 2^-24 + 2^-32 < 2^-8 + 2^-23)."""
+    return {"bf16": 2.0 ** -8 + 2.0 ** -23, "f32": 2.0 ** -24}[dtype]
 
 
 def bound_terms(q: np.ndarray, idx: Index, bd: BoundData, b: int, g: int, scale: float, dtype: str):

@@ -222,6 +222,33 @@ def test_select_refresh_rejects_null_sel_ids_and_does_nothing_for_top_k_zero():
     assert wi.wi_select_refresh(_dparams(top_k=0), _view(), FAKE, None, FAKE, need, 0) == wi.WI_OK
 
 
+def test_bound_data_and_bounded_decode_reject_bad_arguments():
+    p = _dparams()
+    with pytest.raises(wi.WaveIndexError) as e:            # vmax is required
+        wi.wi_bound_data(p, _view(), FAKE, FAKE, None, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:            # radius is required when C > 0
+        wi.wi_bound_data(p, _view(), None, FAKE, FAKE, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_bound_data(_dparams(d=64), _view(), FAKE, FAKE, FAKE, 0)
+    assert e.value.status == wi.WI_ERR_UNSUPPORTED
+    need = wi.wi_decode_workspace_bytes(p)
+
+    def bounded(pp=p, radius=FAKE, vmax=FAKE, eps=0.1, ws_bytes=need):
+        with pytest.raises(wi.WaveIndexError) as e:
+            wi.wi_decode_bounded(pp, _view(), radius, FAKE, vmax, FAKE, eps, FAKE, None, None, None, None,
+                                 FAKE, ws_bytes, 0)
+        return e.value.status
+
+    assert bounded(radius=None) == wi.WI_ERR_INVALID_ARG
+    assert bounded(vmax=None) == wi.WI_ERR_INVALID_ARG
+    assert bounded(eps=-1.0) == wi.WI_ERR_INVALID_ARG
+    assert bounded(eps=float("nan")) == wi.WI_ERR_INVALID_ARG
+    assert bounded(pp=_dparams(top_k=2049)) == wi.WI_ERR_UNSUPPORTED
+    assert bounded(ws_bytes=need - 1) == wi.WI_ERR_WORKSPACE
+
+
 def test_build_rejects_null_inputs_and_small_workspace():
     p = wi.BuildParams(1, 8, 4096, 128, 4, 64, 1024, 64, 3, wi.WI_BF16, 1)
     need = wi.wi_index_shapes_for(p).build_workspace_bytes

@@ -1,0 +1,155 @@
+"""GPU parity of the accuracy-bounded estimation: wi_bound_data (per-cluster radius and value
+norms, bit-exact against oracle.bound_data) and wi_decode_bounded (the zone of each head sized
+to meet an error bound).
+
+The zone size is decided on fp32 scores on the device and on canonical fp64 scores in the
+oracle, so the device's k is checked for validity against the oracle's A(k) (A(k) <= eps and
+A(k - 1) > eps, each within a relative 1e-3, unless k is 0 or the cap); given that k, the zone
+(bit-exact ids), the outputs (the decode tolerances) and the bound after attention (relative
+1e-3) are compared with the oracle run at the same k.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_vector_index_amd import synth
+from kv_vector_index_amd import wave_index as wi
+from wi_testutil import assert_decode_parity, device, upload_index
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+K_TOL = 1e-3
+
+
+def _workload_index(dtype, seed, N=2048, Hq=8, Hkv=2, seg_len=512, cps=32, key_noise=0.3, q_scale=1.5):
+    w = synth.Workload("b", 1, Hq, Hkv, D, N, dtype, 24, 4, 32, seg_len, cps, 4, 16,
+                       key_noise=key_noise, q_scale=q_scale)
+    K, V, Q = synth.make_instance(w, seed)
+    dev = device()
+    Kt, Vt, Qt = (synth.cast(x, dtype, dev) for x in (K, V, Q))
+    K64, V64, Q64 = (synth.as_float64(t) for t in (Kt, Vt, Qt))
+    idx = oracle.build_index(K64, V64, w.sink, w.window, seg_len, cps, w.iters, 5, dtype)
+    return w, idx, Qt, Q64
+
+
+def _random_label_index(dtype, seed, C=1024, tpc=2, Hkv=2, empty_frac=0.3):
+    rng = np.random.default_rng(seed)
+    Nc = C * tpc
+    N = Nc + 4 + 16
+    K = rng.standard_normal((1, Hkv, N, D))
+    K /= np.linalg.norm(K, axis=-1, keepdims=True)
+    V = rng.standard_normal((1, Hkv, N, D))
+    labels = np.empty((1, Hkv, Nc), dtype=np.int64)
+    for g in range(Hkv):
+        live = np.nonzero(rng.random(C) >= empty_frac)[0]
+        lab = np.concatenate([live, rng.choice(live, Nc - live.size)])
+        rng.shuffle(lab)
+        labels[0, g] = lab
+    dev = device()
+    Kt, Vt = (synth.cast(x, dtype, dev) for x in (K, V))
+    K64, V64 = (synth.as_float64(t) for t in (Kt, Vt))
+    return oracle.finalize_index(K64, V64, labels, 4, 16, C, dtype)
+
+
+def _bound_on_device(gi, idx, dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    radius, vnorm, vmax = wi.bound_data(gi, idx.sizes.shape[0], idx.sizes.shape[1], tdt)
+    torch.cuda.synchronize()
+    return radius, vnorm, vmax
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bound_data_bit_exact(dtype):
+    for idx in (_workload_index(dtype, 1)[1], _random_label_index(dtype, 2)):
+        gi = upload_index(idx, dtype, device())
+        radius, vnorm, vmax = _bound_on_device(gi, idx, dtype)
+        ref = oracle.bound_data(idx)
+        np.testing.assert_array_equal(radius.cpu().numpy().astype(np.float64), ref.radius)
+        np.testing.assert_array_equal(vnorm.cpu().numpy().astype(np.float64), ref.vnorm)
+        np.testing.assert_array_equal(vmax.cpu().numpy().astype(np.float64), ref.vmax)
+
+
+def _check_bounded(idx, Qt, Q64, Hq, top_k, eps, dtype):
+    gi = upload_index(idx, dtype, device())
+    bound = _bound_on_device(gi, idx, dtype)
+    bd = oracle.bound_data(idx)
+    o, lse, sel, k_used, err = wi.decode_bounded(gi, Qt, bound, top_k, eps)
+    torch.cuda.synchronize()
+    k_dev = k_used.cpu().numpy().astype(np.int64)
+    B, G = Q64.shape[0], Hq // idx.sizes.shape[1]
+    scale = 1 / math.sqrt(D)
+    for b in range(B):
+        for h in range(Hq):
+            _, order, _, _, _, errc, lo = oracle.bound_terms(Q64[b, h], idx, bd, b, h // G, scale, dtype)
+            A = oracle.prior_bounds(errc, lo, order)
+            cap = min(top_k, order.size)
+            k = int(k_dev[b, h])
+            assert 0 <= k <= cap, (b, h, k, cap)
+            if k < cap:
+                assert A[k] <= eps * (1 + K_TOL) + 1e-30, (b, h, k, A[k], eps)
+            if k > 0:
+                assert A[k - 1] > eps * (1 - K_TOL), (b, h, k, A[k - 1], eps)
+    ro, rl, rs, rk, rprior, rpost = oracle.decode_bounded(Q64, idx, bd, Hq, top_k, eps, dtype, k_force=k_dev)
+    assert_decode_parity(o, lse, sel, ro, rl, rs, dtype)
+    e = err.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(e, rpost, rtol=2e-3, atol=1e-30)
+    return k_dev, e
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bounded_decode_over_a_range_of_eps(dtype):
+    w, idx, Qt, Q64 = _workload_index(dtype, 3)
+    ks = []
+    for eps in (0.0, 0.01, 0.1, 1.0, 10.0, float("inf")):
+        k, e = _check_bounded(idx, Qt, Q64, w.Hq, idx.C, eps, dtype)
+        ks.append(k)
+        assert (e <= eps * (1 + K_TOL) + 1e-30).all() or eps == 0.0
+    n_ne = (idx.sizes[0] > 0).sum(axis=1).repeat(w.Hq // w.Hkv)
+    assert (ks[0][0] == n_ne).all() and (ks[-1] == 0).all()
+    for a, b in zip(ks, ks[1:]):                  # a larger eps never needs a larger zone
+        assert (b <= a).all()
+    assert len({int(k.sum()) for k in ks}) >= 4  # the sweep really moves the zone
+
+
+def test_bounded_decode_capped_and_sharp_queries():
+    # sharp queries on tight clusters (|q| ~ 70: exp(s |q| r_c) makes the bound demanding); then
+    # top_k caps every head
+    w, idx, Qt, Q64 = _workload_index("bf16", 4, key_noise=0.1, q_scale=6.0)
+    for eps in (0.05, 5.0):
+        _check_bounded(idx, Qt, Q64, w.Hq, idx.C, eps, "bf16")
+    k, _ = _check_bounded(idx, Qt, Q64, w.Hq, 3, 0.0, "bf16")
+    assert (k == 3).all()
+
+
+def test_bounded_decode_with_empty_clusters_and_many_heads():
+    idx = _random_label_index("bf16", 5, C=512, tpc=3, Hkv=34)
+    rng = np.random.default_rng(5)
+    Hq = 272
+    Qt = synth.cast(3.0 * rng.standard_normal((1, Hq, D)), "bf16", device())
+    Q64 = synth.as_float64(Qt)
+    for eps in (0.5, 5.0):
+        _check_bounded(idx, Qt, Q64, Hq, 200, eps, "bf16")
+
+
+def test_bounded_decode_bound_covers_dense_attention():
+    # the device's own bound against dense softmax attention over the stored keys and values
+    w, idx, Qt, Q64 = _workload_index("bf16", 6)
+    gi = upload_index(idx, "bf16", device())
+    bound = _bound_on_device(gi, idx, "bf16")
+    G = w.Hq // w.Hkv
+    K = np.concatenate([idx.k_steady, idx.k_perm], axis=2)
+    V = np.concatenate([idx.v_steady, idx.v_perm], axis=2)
+    for eps in (0.05, 1.0, float("inf")):
+        o, lse, sel, k_used, err = wi.decode_bounded(gi, Qt, bound, idx.C, eps)
+        torch.cuda.synchronize()
+        o = o.cpu().numpy().astype(np.float64)
+        err = err.cpu().numpy().astype(np.float64)
+        for h in range(w.Hq):
+            lg = (K[0, h // G] @ Q64[0, h]) / math.sqrt(D)
+            p = np.exp(lg - lg.max())
+            dense = (p @ V[0, h // G]) / p.sum()
+            assert np.linalg.norm(o[0, h] - dense) <= err[0, h] * (1 + 1e-3) + 2e-5, (eps, h)

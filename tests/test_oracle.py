@@ -547,7 +547,7 @@ def test_cluster_of_identical_keys_has_radius_zero():
     assert bd.radius[0, 0, 0] == 0.0 and bd.radius[0, 0, 1] > 0
     assert bd.radius[0, 0, 2] == 0.0 and bd.radius[0, 0, 3] == 0.0
     _, _, _, w_, a_, err, _ = oracle.bound_terms(rng.standard_normal(d), idx, bd, 0, 0, 1 / math.sqrt(d), "bf16")
-    assert a_[0] == 0.0 and err[0] == w_[0] * 2.0 ** -8 * bd.vnorm[0, 0, 0]
+    assert a_[0] == 0.0 and err[0] == w_[0] * oracle.sum_roundoff("bf16") * bd.vnorm[0, 0, 0]
 
 
 @pytest.mark.parametrize("seed,dtype,q_scale,key_noise", [(3, "bf16", 1.5, 0.3), (4, "f32", 1.5, 0.3),
@@ -627,6 +627,6 @@ def test_bound_is_nearly_attained_by_two_opposite_members():
     exact = (math.exp(x) - math.exp(-x)) / (2 + math.exp(x) + math.exp(-x))
     ro, _ = _dense(q, K[0, 0], V[0, 0], s)
     assert abs(np.linalg.norm(ro) - exact) < 1e-12
-    bound = 2 * (math.expm1(x) + 2.0 ** -8) / (2 + 2 * math.exp(-x))
+    bound = 2 * (math.expm1(x) + oracle.sum_roundoff("bf16")) / (2 + 2 * math.exp(-x))
     assert abs(post[0, 0] - bound) < 1e-12
     assert 0.5 * post[0, 0] < exact <= post[0, 0]
