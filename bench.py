@@ -230,6 +230,9 @@ def main():
     ap.add_argument("--bounded", type=float, default=None, metavar="EPS",
                     help="time wi_decode_bounded: each head's zone (at most top_k clusters) sized to "
                          "meet the error bound EPS; the bound data is computed once beforehand")
+    ap.add_argument("--wavebuf", type=float, default=None, metavar="FRAC",
+                    help="time wi_decode_wavebuf: the clustered K/V in pinned host memory, a GPU block cache "
+                         "of FRAC of all blocks, eager steps over drifting queries")
     ap.add_argument("--build-only", action="store_true",
                     help="time the index build (segmented spherical k-means) instead of the decode step")
     args = ap.parse_args()
@@ -274,8 +277,11 @@ def main():
     # ---- instances at distinct HBM addresses (so that a step's bytes miss the 256 MB MALL) and
     # the queries of the steps (a drifting sequence for multi-step workloads)
     n_inst = args.instances if args.instances else (8 if w.B * w.Hkv * idx.C * w.d * 4 < (64 << 20) else 2 if w.B == 1 else 1)
+    if args.wavebuf is not None:
+        args.no_graph = True          # the host manages the cache between steps
+        n_inst = 1                    # one index, one cache
     insts = [idx] + [idx.clone() for _ in range(n_inst - 1)]
-    if w.steps > 1 or args.gated is not None:
+    if w.steps > 1 or args.gated is not None or args.wavebuf is not None:
         n_q, drift = (w.steps, w.drift) if w.steps > 1 else (64, 0.1)
         qm = synth.drift_queries_device(Qt, n_q, drift, args.seed)
         qs = [qm[t].to(torch.float32).to(Qt.dtype).contiguous() for t in range(n_q)]
@@ -294,6 +300,21 @@ def main():
         j = i % len(insts)
         wi.wi_decode(p, views[j], qs[i % len(qs)].data_ptr(), out.data_ptr(), lse.data_ptr(), sel.data_ptr(),
                      ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
+
+    wavebuf_info = None
+    if args.wavebuf is not None:
+        host_idx = wi.with_host_kv(idx)
+        nblk = -(-idx.Nc // wi.WB_BLOCK)
+        total_blocks = w.B * w.Hkv * nblk
+        cache_blocks = int(args.wavebuf * total_blocks)
+        exec_blocks = min(total_blocks, w.B * w.Hq * w.top_k * 2)
+        wb = wi.WaveBuffer(host_idx, w.B, w.Hq, w.Hkv, w.top_k, Qt.dtype, cache_blocks, exec_blocks)
+        blk_bytes = wi.WB_BLOCK * w.d * (2 if w.dtype == "bf16" else 4) * 2
+        wavebuf_info = {"cache_frac": args.wavebuf, "cache_blocks": cache_blocks, "exec_blocks": exec_blocks,
+                        "block_bytes": blk_bytes, "host_kv_bytes": 2 * host_idx.k_perm.numel() * host_idx.k_perm.element_size()}
+
+        def step(i):
+            wb.decode(qs[i % len(qs)], out, lse, sel)
 
     bounded_info = None
     if args.bounded is not None:
@@ -355,6 +376,8 @@ def main():
     per_bytes, union_rows = algorithmic_bytes(w, off_np, sel_np)
     step_bytes = sum(per_bytes.values())
 
+    if wavebuf_info is not None:
+        st0 = wb.stats()
     # ---- timed region: K steps
     K_steps = args.steps
     if args.no_graph:
@@ -389,6 +412,14 @@ def main():
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K_steps
+    if wavebuf_info is not None:
+        st1 = wb.stats()
+        d = {k: st1[k] - st0[k] for k in st1}
+        touched = d["hits"] + d["staged"] + d["host_reads"]
+        wavebuf_info.update({"hit_rate": d["hits"] / max(touched, 1), "blocks_per_step": touched / K_steps,
+                             "pcie_bytes_per_step": (d["staged"] + d["host_reads"]) * blk_bytes / K_steps,
+                             "host_reads_per_step": d["host_reads"] / K_steps,
+                             "evictions_per_step": d["evicted"] / K_steps})
 
     # ---- per-kernel timing (eager, HIP events on the launch stream around PROF_REPS back-to-back
     # launches of each kernel, so that the event records themselves do not count).  A long matrix
@@ -439,6 +470,7 @@ def main():
                    "sink": w.sink, "window": w.window, "instances": len(insts),
                    "timing": "eager" if args.no_graph else "hip-graph replay"},
         "bounded": bounded_info,
+        "wavebuf": wavebuf_info,
         "gated": None if args.gated is None else {"tau": args.gated, "refresh": args.refresh,
                                                   "reused_kv_head_frac": reuse_frac,
                                                   "out_ready_us": 1e3 * sum(avg_ms[k] for k in ("score", "select", "attend", "merge")),

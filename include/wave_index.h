@@ -244,6 +244,55 @@ wi_status wi_decode_bounded(const wi_decode_params *p, const wi_index_view *idx,
                             float *out, float *lse, int32_t *sel_ids, int32_t *k_used,
                             float *err_bound, void *workspace, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Wave buffer (RetroInfer technical summary, section 2.B; Arabic summary, section 2.b): decode
+ * over an index whose cluster-major K/V copies (wi_index_view.k_perm / v_perm) live in host
+ * memory, with a GPU cache of KV blocks managed from the host off the attention's critical path
+ * and an execution buffer for the blocks the cache misses.
+ *
+ * The clustered rows of each (b, KV head) are cut into blocks of 16 rows.  One device pool holds
+ * cache_blocks cached blocks and exec_blocks execution-buffer blocks.  Each wi_decode_wavebuf
+ * call, in stream order: applies the admissions the host decided from the previous call (copying
+ * the previous call's staged misses into cache slots); scores and selects as wi_decode; for every
+ * block a head's retrieval zone touches, uses the cached copy, or copies the block from host
+ * memory into the execution buffer, or, when the execution buffer is full, leaves it in host
+ * memory for the attention kernel to read there; attends and merges.  The call's access log goes
+ * back to the host on a stream of the wave buffer's own while attention runs.  The host decides
+ * from each call's log two calls later (logs and execution buffer are double-buffered, so the
+ * host never waits for the call just enqueued), in call order: it updates the LRU order, the
+ * hits first, then the staged misses, each in ascending (b, KV head, block) order; every staged
+ * miss not cached since is admitted, into a free slot or in place of the least recently used
+ * block.  The admissions decided from call t take effect at call t + 2.  Blocks read from host
+ * memory in place are not admitted.  Results equal wi_decode's bit for bit whatever the cache
+ * holds.
+ *
+ * Requirements: k_perm and v_perm must be host memory the device can read (hipHostMalloc);
+ * every other index buffer, q, out, lse, sel_ids and the workspace are device memory.  The
+ * device memory of the wave buffer (wi_wavebuf_device_bytes: the cache, two execution-buffer
+ * regions of exec_blocks, directory, logs; 256-byte aligned) is caller-
+ * allocated and must outlive it; the host state (the LRU, a pinned copy of the log, a stream
+ * and two events) is allocated by wi_wavebuf_create and freed by wi_wavebuf_destroy.  One
+ * wave buffer serves one index (same B, Hkv, Nc and dtype) and one stream at a time; its calls
+ * must not overlap and cannot be captured in a graph (the host acts between them).  The pool
+ * holds at most 2^29 rows.  Errors: WI_ERR_INVALID_ARG for null or negative arguments or a
+ * wave buffer of another index, WI_ERR_UNSUPPORTED as wi_decode and for a pool beyond 2^29
+ * rows, WI_ERR_WORKSPACE for too little device memory. */
+typedef struct wi_wavebuf wi_wavebuf;
+
+wi_status wi_wavebuf_device_bytes(const wi_decode_params *p, int32_t cache_blocks,
+                                  int32_t exec_blocks, size_t *bytes);
+wi_status wi_wavebuf_create(const wi_decode_params *p, int32_t cache_blocks, int32_t exec_blocks,
+                            void *device_mem, size_t bytes, void *stream, wi_wavebuf **out);
+wi_status wi_decode_wavebuf(wi_wavebuf *wb, const wi_decode_params *p, const wi_index_view *idx,
+                            const void *q, float *out, float *lse, int32_t *sel_ids,
+                            void *workspace, size_t ws_bytes, void *stream);
+/* (host) Waits for every pending log and decides from them (the decisions still take effect two
+ * calls after the call they come from), then fills stats[6]: calls, hits, misses staged in the
+ * execution buffer, blocks read from host memory in place, admissions, evictions (blocks are
+ * counted once per call however many heads touch them). */
+wi_status wi_wavebuf_stats(wi_wavebuf *wb, int64_t *stats);
+wi_status wi_wavebuf_destroy(wi_wavebuf *wb);
+
 /* Stages timed by the profiling hook below (one entry per kernel the entry points launch). */
 typedef enum {
   WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA) and the estimation over all

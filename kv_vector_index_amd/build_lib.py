@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["wi_api.hip", "wi_decode.hip", "wi_build.hip", "wi_bound.hip"]
+SOURCES = ["wi_api.hip", "wi_decode.hip", "wi_build.hip", "wi_bound.hip", "wi_wavebuf.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -284,7 +284,7 @@ struct Gate {
 
 static wi_status decode_common(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
                                float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream,
-                               const Gate* gate, const Bounded* bnd = nullptr) {
+                               const Gate* gate, const Bounded* bnd = nullptr, wi::WaveBuf* wb = nullptr) {
   if (!p || !idx || !q || !out) return fail(WI_ERR_INVALID_ARG, "params, index, q and out must be non-null");
   if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
     return fail(WI_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and Hkv dividing Hq");
@@ -355,13 +355,32 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
     a.gated = 1; a.q_prev = gate->q_prev; a.sel_prev = gate->sel_prev; a.reused = gate->reused;
     a.tau = gate->tau;
   }
+  if (wb) {
+    if (!wi::wavebuf_matches(wb, *p)) return fail(WI_ERR_INVALID_ARG, "wave buffer made for other B, Hkv, Nc or dtype");
+    if (p->Nc > 0) {
+      // the device's view of the host copies; memory the device cannot read is an error here
+      // rather than a fault in the attention kernel
+      void* dk = nullptr;
+      void* dv = nullptr;
+      if (hipHostGetDevicePointer(&dk, idx->k_perm, 0) != hipSuccess ||
+          hipHostGetDevicePointer(&dv, idx->v_perm, 0) != hipSuccess || !dk || !dv) {
+        (void)hipGetLastError();
+        return fail(WI_ERR_INVALID_ARG, "k_perm and v_perm must be pinned host memory (hipHostMalloc)");
+      }
+      a.k_perm = dk;
+      a.v_perm = dv;
+    }
+    const hipError_t e = wi::wavebuf_begin(wb, st, a);
+    if (e != hipSuccess) return check_hip(e, "wave buffer admission", st);
+  }
   if (bnd) {
     a.bounded = 1; a.radius = bnd->radius; a.vnorm = bnd->vnorm; a.vmax = bnd->vmax; a.eps = bnd->eps;
     a.k_used = bnd->k_used; a.err_bound = bnd->err_bound;
     a.u = p->dtype == WI_BF16 ? 0x1.0002p-8f : 0x1p-24f;     // 2^-8 + 2^-23 for bfloat16 sums
   }
   return check_hip(wi::launch_decode(*p, a, st),
-                   gate ? "wi_decode_gated launch" : bnd ? "wi_decode_bounded launch" : "wi_decode launch", st);
+                   gate ? "wi_decode_gated launch" : bnd ? "wi_decode_bounded launch"
+                   : wb ? "wi_decode_wavebuf launch" : "wi_decode launch", st);
 }
 
 wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
@@ -437,6 +456,67 @@ wi_status wi_bound_data(const wi_decode_params* p, const wi_index_view* idx, flo
     return fail(WI_ERR_INVALID_ARG, "null index buffer, radius or vnorm");
   hipStream_t st = static_cast<hipStream_t>(stream);
   return check_hip(wi::launch_bound_data(*p, *idx, radius, vnorm, vmax, st), "wi_bound_data launch", st);
+}
+
+static wi_status wavebuf_check(const wi_decode_params* p, int32_t cache_blocks, int32_t exec_blocks) {
+  if (!p) return fail(WI_ERR_INVALID_ARG, "null params");
+  if (p->B < 1 || p->Hkv < 1) return fail(WI_ERR_INVALID_ARG, "need B, Hkv >= 1");
+  if (p->d != wi::kD) return fail(WI_ERR_UNSUPPORTED, "head dim %d unsupported (only 128)", p->d);
+  if (p->dtype != WI_F32 && p->dtype != WI_BF16) return fail(WI_ERR_INVALID_ARG, "bad dtype %d", p->dtype);
+  if (p->Nc < 0 || cache_blocks < 0 || exec_blocks < 0)
+    return fail(WI_ERR_INVALID_ARG, "negative Nc, cache_blocks or exec_blocks");
+  if (((int64_t)cache_blocks + exec_blocks) * wi::kWbBlock > wi::kWbMaxPoolRows)
+    return fail(WI_ERR_UNSUPPORTED, "a wave-buffer pool holds at most 2^29 rows");
+  if ((int64_t)p->B * p->Hkv * wi::ceil_div(std::max(p->Nc, 1), wi::kWbBlock) >= kMaxRows)
+    return fail(WI_ERR_UNSUPPORTED, "too many blocks");
+  return WI_OK;
+}
+
+wi_status wi_wavebuf_device_bytes(const wi_decode_params* p, int32_t cache_blocks, int32_t exec_blocks,
+                                  size_t* bytes) {
+  const wi_status st = wavebuf_check(p, cache_blocks, exec_blocks);
+  if (st != WI_OK) return st;
+  if (!bytes) return fail(WI_ERR_INVALID_ARG, "null output");
+  *bytes = wi::wavebuf_device_bytes(*p, cache_blocks, exec_blocks);
+  return WI_OK;
+}
+
+wi_status wi_wavebuf_create(const wi_decode_params* p, int32_t cache_blocks, int32_t exec_blocks, void* device_mem,
+                            size_t bytes, void* stream, wi_wavebuf** out) {
+  const wi_status st = wavebuf_check(p, cache_blocks, exec_blocks);
+  if (st != WI_OK) return st;
+  if (!out) return fail(WI_ERR_INVALID_ARG, "null output");
+  const size_t need = wi::wavebuf_device_bytes(*p, cache_blocks, exec_blocks);
+  if (!device_mem || bytes < need) return fail(WI_ERR_WORKSPACE, "wave buffer memory of %zu bytes given, %zu needed", bytes, need);
+  if (reinterpret_cast<uintptr_t>(device_mem) & 255) return fail(WI_ERR_WORKSPACE, "wave buffer memory must be 256-byte aligned");
+  wi::WaveBuf* w = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const wi_status r = check_hip(wi::wavebuf_create(*p, cache_blocks, exec_blocks, device_mem, s, &w), "wi_wavebuf_create", s);
+  if (r != WI_OK) return r;
+  *out = reinterpret_cast<wi_wavebuf*>(w);
+  return WI_OK;
+}
+
+wi_status wi_decode_wavebuf(wi_wavebuf* wb, const wi_decode_params* p, const wi_index_view* idx, const void* q,
+                            float* out, float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  if (!wb) return fail(WI_ERR_INVALID_ARG, "null wave buffer");
+  return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, nullptr, nullptr,
+                       reinterpret_cast<wi::WaveBuf*>(wb));
+}
+
+wi_status wi_wavebuf_stats(wi_wavebuf* wb, int64_t* stats) {
+  if (!wb || !stats) return fail(WI_ERR_INVALID_ARG, "null wave buffer or output");
+  wi::WaveBuf* w = reinterpret_cast<wi::WaveBuf*>(wb);
+  const hipError_t e = wi::wavebuf_sync_log(w);
+  if (e != hipSuccess) return fail(WI_ERR_HIP, "wave buffer log: %s", hipGetErrorString(e));
+  std::memcpy(stats, wi::wavebuf_stats(w), 6 * sizeof(int64_t));
+  return WI_OK;
+}
+
+wi_status wi_wavebuf_destroy(wi_wavebuf* wb) {
+  wi::wavebuf_destroy(reinterpret_cast<wi::WaveBuf*>(wb));
+  return WI_OK;
 }
 
 static void prof_clear() {

@@ -1342,13 +1342,13 @@ template <> struct QkTile<float> {
 // against the 16 key rows on MFMA, the running max comes from a DPP row reduction, and the
 // probabilities go through a 64-byte LDS slot of the wave to the lanes that hold the value rows
 // (lane (lr, lg) holds dims 8 lr .. 8 lr + 7 of tokens 4 i + lg), which accumulate P V.
-template <typename T>
+template <typename T, bool PG>
 __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   constexpr int R = AttRows<T>::R;
   constexpr int PASS = 16 * R;                 // corrections: 4 waves x 4 lane groups x R rows
   __shared__ float sh_m[4], sh_den[4];
   __shared__ float sh_num[4 * kD];
-  __shared__ uint32_t sh_ent[kAttStage];       // token -> row | steady flag (bit 23) | valid (bit 24)
+  __shared__ uint32_t sh_ent[kAttStage];       // token -> row | host (bit 29) | steady (30) | valid (31)
   __shared__ int spre[kAttStage + 1];          // first token of list entries e_cur + x
   __shared__ int srow[kAttStage];              // first k_perm row of list entries e_cur + x
   __shared__ float sh_p[4][16];
@@ -1369,15 +1369,20 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     const int32_t* rowl = a.hl_row + (size_t)bh * K;
     QkTile<T> qk;
     qk.load_q(static_cast<const T*>(a.q) + (size_t)bh * kD, lr, lg);
-    const T* kp = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
-    const T* vp = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
+    // retrieved rows: the index's cluster-major copy, or with a wave buffer the block pool (cache
+    // and execution buffer) and, for blocks it could not stage, the copy in host memory
+    const T* hk = static_cast<const T*>(a.k_perm) + (size_t)bg * a.Nc * kD;
+    const T* hv = static_cast<const T*>(a.v_perm) + (size_t)bg * a.Nc * kD;
+    const T* kp = PG ? static_cast<const T*>(a.pool_k) : hk;
+    const T* vp = PG ? static_cast<const T*>(a.pool_v) : hv;
+    const int32_t* wloc = PG ? a.wb_loc + (size_t)bg * a.wb_nblk : nullptr;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * NS * kD;
     const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * NS * kD;
     WI_TP(21);
     for (int z0 = t0; z0 < t1; z0 += kAttStage) {
       const int z1 = min(t1, z0 + kAttStage);
       if (z0 > t0) __syncthreads();            // the previous chunk's map is no longer read
-      for (int t = z0 + tid; t < min(z1, NS); t += kAttThreads) sh_ent[t - z0] = (uint32_t)t | (3u << 23);
+      for (int t = z0 + tid; t < min(z1, NS); t += kAttThreads) sh_ent[t - z0] = (uint32_t)t | (3u << 30);
       const int u0 = max(z0, NS);
       if (u0 < z1) {
         // the at most z1 - u0 <= kAttStage entries that hold tokens [u0, z1) start at e_cur
@@ -1393,7 +1398,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
             const int mid = (lo + hi) >> 1;
             if (spre[mid] <= t) lo = mid; else hi = mid;
           }
-          sh_ent[t - z0] = (uint32_t)(srow[lo] + (t - spre[lo])) | (1u << 24);
+          const int row = srow[lo] + (t - spre[lo]);
+          uint32_t ent = (uint32_t)row | (1u << 31);
+          if constexpr (PG) {
+            const int loc = wloc[row >> 4];        // pool block, or -1: read from host memory
+            ent = loc >= 0 ? ((uint32_t)(loc * kWbBlock + (row & (kWbBlock - 1))) | (1u << 31)) : (ent | (1u << 29));
+          }
+          sh_ent[t - z0] = ent;
           if (t == z1 - 1) sh_next = e_cur + lo;
         }
       }
@@ -1405,18 +1416,20 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
         // key row of token base + lr (MFMA operand), value rows of tokens base + 4 i + lg
         const int tk = base + lr;
         const uint32_t eK = tk < z1 ? sh_ent[tk - z0] : 0u;
-        if ((eK >> 24) != 0u) qk.load_k((((eK >> 23) & 1u) ? ks : kp) + (size_t)(eK & 0x7fffffu) * kD, lg);
+        if ((eK >> 31) != 0u)
+          qk.load_k((((eK >> 30) & 1u) ? ks : (PG && ((eK >> 29) & 1u)) ? hk : kp) + (size_t)(eK & 0x1fffffffu) * kD, lg);
         else qk.zero_k();
         Piece<T> vr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tv = base + 4 * i + lg;
           const uint32_t eV = tv < z1 ? sh_ent[tv - z0] : 0u;
-          if ((eV >> 24) != 0u) vr[i].load((((eV >> 23) & 1u) ? vs : vp) + (size_t)(eV & 0x7fffffu) * kD + 8 * lr);
+          if ((eV >> 31) != 0u)
+            vr[i].load((((eV >> 30) & 1u) ? vs : (PG && ((eV >> 29) & 1u)) ? hv : vp) + (size_t)(eV & 0x1fffffffu) * kD + 8 * lr);
           else vr[i].zero();
         }
         const f32x4_t acc = qk.scores();
-        const float sc = (lg == 0 && (eK >> 24) != 0u) ? acc[0] * a.scale : -INFINITY;
+        const float sc = (lg == 0 && (eK >> 31) != 0u) ? acc[0] * a.scale : -INFINITY;
         const float hm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_max(sc)), 0));
         const float mn = fmaxf(st.m[0], hm);
         const float alpha = (st.m[0] == mn) ? 1.f : __expf(st.m[0] - mn);
@@ -1637,9 +1650,13 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   }
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.paged && (e = launch_wb_resolve(a, s)) != hipSuccess) return e;   // blocks of the zones
   prof_begin(WI_STAGE_ATTEND, s);
   for (int r = 0; r < prof_reps(); ++r) {
-    hipLaunchKernelGGL(k_attend<T>, dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
+    if (a.paged)
+      hipLaunchKernelGGL((k_attend<T, true>), dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attend<T, false>), dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
   }
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -22,6 +22,8 @@ constexpr int kCorrEntries = 64;    // retrieved clusters per correction workgro
 constexpr int kSelectBitmapLds = 65536;   // dynamic LDS of the select kernel: 2 bitmaps over C
 constexpr int kMaxDecodeClusters = kSelectBitmapLds / 8 * 32;   // C per KV head (262144)
 constexpr int kBoundedMaxTopK = 2048;    // clusters the bounded select ranks in LDS
+constexpr int kWbBlock = 16;        // rows per wave-buffer block
+constexpr int64_t kWbMaxPoolRows = (int64_t)1 << 29;   // rows a wave-buffer pool may hold
 constexpr int kAttTarget = 1024;    // attention workgroups one wave of the grid holds (4 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -89,6 +91,13 @@ struct DecodeArgs {
   int32_t* k_used;         // [BH] or null: zone size chosen
   float* err_bound;        // [BH] or null: bound on |out - dense attention|
   float* bnd;              // [BH, 4] workspace: m*, sum a, sum (a V + w u V), sum lo over the estimation zone
+  // wave buffer (paged == 0 otherwise): k_perm / v_perm are then the copies in host memory
+  int paged;
+  int wb_nblk;             // blocks of kWbBlock rows per (b, KV head)
+  const int32_t* wb_loc;   // [BG, wb_nblk] this step's pool block of every needed block, -1: host
+  const void* pool_k;      // [pool blocks, kWbBlock, d] cache and execution buffer
+  const void* pool_v;
+  void* wb;                // the wave buffer's host state (read by the launcher only)
   // shapes
   int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, est_tiles_g, att_split, att_items;
   float scale;
@@ -96,6 +105,16 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_refresh(const wi_decode_params& p, const DecodeArgs& a, hipStream_t s);
+struct WaveBuf;
+size_t wavebuf_device_bytes(const wi_decode_params& p, int cache_blocks, int exec_blocks);
+hipError_t wavebuf_create(const wi_decode_params& p, int cache_blocks, int exec_blocks, void* mem, hipStream_t s,
+                          WaveBuf** out);
+void wavebuf_destroy(WaveBuf* w);
+hipError_t wavebuf_sync_log(WaveBuf* w);
+const int64_t* wavebuf_stats(WaveBuf* w);
+bool wavebuf_matches(const WaveBuf* w, const wi_decode_params& p);
+hipError_t wavebuf_begin(WaveBuf* w, hipStream_t s, DecodeArgs& a);
+hipError_t launch_wb_resolve(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_bound_data(const wi_decode_params& p, const wi_index_view& idx, float* radius, float* vnorm,
                              float* vmax, hipStream_t s);
 

@@ -23,7 +23,8 @@ WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0,
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
             "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated", "wi_select_refresh",
-            "wi_bound_data", "wi_decode_bounded",
+            "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes", "wi_wavebuf_create",
+            "wi_decode_wavebuf", "wi_wavebuf_stats", "wi_wavebuf_destroy",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
           "final", "refresh")
@@ -90,6 +91,14 @@ def lib() -> ctypes.CDLL:
         L.wi_bound_data.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp]
         L.wi_decode_bounded.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp,
                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.wi_wavebuf_device_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.wi_wavebuf_create.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_int32, ctypes.c_int32, vp, sz, vp,
+                                        ctypes.POINTER(ctypes.c_void_p)]
+        L.wi_decode_wavebuf.argtypes = [vp, ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp,
+                                        vp, sz, vp]
+        L.wi_wavebuf_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
+        L.wi_wavebuf_destroy.argtypes = [vp]
         L.wi_status_string.argtypes = [ctypes.c_int]
         L.wi_profile_enable.argtypes = [ctypes.c_int]
         L.wi_profile_enable.restype = ctypes.c_int
@@ -97,7 +106,8 @@ def lib() -> ctypes.CDLL:
         L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
                      "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated",
-                     "wi_select_refresh", "wi_bound_data", "wi_decode_bounded"):
+                     "wi_select_refresh", "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes",
+                     "wi_wavebuf_create", "wi_decode_wavebuf", "wi_wavebuf_stats", "wi_wavebuf_destroy"):
             getattr(L, name).restype = ctypes.c_int
         L.wi_status_string.restype = ctypes.c_char_p
         L.wi_last_error.restype = ctypes.c_char_p
@@ -175,6 +185,35 @@ def wi_decode_bounded(p: DecodeParams, view: IndexView, radius_ptr: Optional[int
     return _check(lib().wi_decode_bounded(ctypes.byref(p), ctypes.byref(view), radius_ptr, vnorm_ptr, vmax_ptr,
                                           q_ptr, eps, out_ptr, lse_ptr, sel_ptr, k_ptr, err_ptr, ws_ptr, ws_bytes,
                                           stream))
+
+
+def wi_wavebuf_device_bytes(p: DecodeParams, cache_blocks: int, exec_blocks: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().wi_wavebuf_device_bytes(ctypes.byref(p), cache_blocks, exec_blocks, ctypes.byref(n)))
+    return n.value
+
+
+def wi_wavebuf_create(p: DecodeParams, cache_blocks: int, exec_blocks: int, mem_ptr: Optional[int], nbytes: int,
+                      stream: int) -> int:
+    h = ctypes.c_void_p(0)
+    _check(lib().wi_wavebuf_create(ctypes.byref(p), cache_blocks, exec_blocks, mem_ptr, nbytes, stream, ctypes.byref(h)))
+    return h.value
+
+
+def wi_decode_wavebuf(handle: int, p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_ptr: Optional[int],
+                      sel_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    return _check(lib().wi_decode_wavebuf(handle, ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr, sel_ptr,
+                                          ws_ptr, ws_bytes, stream))
+
+
+def wi_wavebuf_stats(handle: int) -> dict:
+    st = (ctypes.c_int64 * 6)()
+    _check(lib().wi_wavebuf_stats(handle, st))
+    return dict(zip(("calls", "hits", "staged", "host_reads", "admitted", "evicted"), list(st)))
+
+
+def wi_wavebuf_destroy(handle: int) -> int:
+    return _check(lib().wi_wavebuf_destroy(handle))
 
 
 def wi_profile_enable(enable, repeats: int = 1) -> int:
@@ -402,3 +441,63 @@ def decode_bounded(index: Index, q, bound, top_k: int, eps: float, scale: Option
                       vmax.data_ptr(), q.data_ptr(), float(eps), out.data_ptr(), lse.data_ptr(), _ptr(sel),
                       k_used.data_ptr(), err.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device))
     return out, lse, sel, k_used, err
+
+
+WB_BLOCK = 16   # rows per wave-buffer block
+
+
+def with_host_kv(index: Index) -> Index:
+    """The same index with its cluster-major K/V copies moved to pinned host memory."""
+    import torch
+    hk = torch.empty(index.k_perm.shape, dtype=index.k_perm.dtype, pin_memory=True)
+    hv = torch.empty(index.v_perm.shape, dtype=index.v_perm.dtype, pin_memory=True)
+    hk.copy_(index.k_perm)
+    hv.copy_(index.v_perm)
+    return Index(centroids=index.centroids, value_sums=index.value_sums, sizes=index.sizes, offsets=index.offsets,
+                 perm=index.perm, k_perm=hk, v_perm=hv, k_steady=index.k_steady, v_steady=index.v_steady,
+                 C=index.C, Nc=index.Nc, n_steady=index.n_steady)
+
+
+class WaveBuffer:
+    """A GPU block cache and execution buffer over an index whose K/V copies are in host memory
+    (with_host_kv).  decode() runs wi_decode_wavebuf; stats() returns the running counters."""
+
+    def __init__(self, index: Index, B: int, Hq: int, Hkv: int, top_k: int, dtype, cache_blocks: int,
+                 exec_blocks: int, device=None):
+        import torch
+        self.index = index
+        self.device = device if device is not None else index.centroids.device
+        self.p = decode_params(index, B, Hq, Hkv, top_k, dtype)
+        nbytes = wi_wavebuf_device_bytes(self.p, cache_blocks, exec_blocks)
+        self.mem = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.handle = wi_wavebuf_create(self.p, cache_blocks, exec_blocks, self.mem.data_ptr(), self.mem.numel(),
+                                        _stream(self.device))
+        self.view = index.view()
+        self.ws = torch.empty(max(wi_decode_workspace_bytes(self.p), 256), dtype=torch.uint8, device=self.device)
+
+    def decode(self, q, out=None, lse=None, sel=None):
+        import torch
+        B, Hq, d = q.shape
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        if sel is None:
+            sel = torch.empty((B, Hq, self.p.top_k), dtype=torch.int32, device=q.device)
+        wi_decode_wavebuf(self.handle, self.p, self.view, q.data_ptr(), out.data_ptr(), lse.data_ptr(), _ptr(sel),
+                          self.ws.data_ptr(), self.ws.numel(), _stream(q.device))
+        return out, lse, sel
+
+    def stats(self) -> dict:
+        return wi_wavebuf_stats(self.handle)
+
+    def close(self):
+        if self.handle:
+            wi_wavebuf_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

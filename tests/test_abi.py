@@ -249,6 +249,24 @@ def test_bound_data_and_bounded_decode_reject_bad_arguments():
     assert bounded(ws_bytes=need - 1) == wi.WI_ERR_WORKSPACE
 
 
+def test_wavebuf_rejects_bad_sizes_and_small_memory():
+    p = _dparams()
+    for cache, exe, status in ((-1, 8, wi.WI_ERR_INVALID_ARG), (8, -1, wi.WI_ERR_INVALID_ARG),
+                               (1 << 25, 1, wi.WI_ERR_UNSUPPORTED)):
+        with pytest.raises(wi.WaveIndexError) as e:
+            wi.wi_wavebuf_device_bytes(p, cache, exe)
+        assert e.value.status == status
+    need = wi.wi_wavebuf_device_bytes(p, 1000, 100)
+    # pool blocks of 16 rows of K and V, directory, claims and locations per block, the log
+    assert need >= 1100 * 16 * 128 * 2 * 2 + 3 * 8 * -(-131004 // 16) * 4
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_wavebuf_create(p, 1000, 100, FAKE, need - 1, 0)
+    assert e.value.status == wi.WI_ERR_WORKSPACE
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode_wavebuf(None, p, _view(), FAKE, FAKE, None, None, FAKE, 1 << 40, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
+
+
 def test_build_rejects_null_inputs_and_small_workspace():
     p = wi.BuildParams(1, 8, 4096, 128, 4, 64, 1024, 64, 3, wi.WI_BF16, 1)
     need = wi.wi_index_shapes_for(p).build_workspace_bytes
