@@ -502,7 +502,7 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
 static_assert(kMaxGroup * kD <= kCandCap, "a KV group's queries are staged in the candidate arrays");
 static_assert(kBoundedMaxTopK <= kCandCap && kBoundedMaxTopK <= kSumCap && kBoundedMaxTopK <= kBins,
               "the bounded select lists its zone in LDS");
-template <typename T, int NT>
+template <typename T, int NT, bool EXT>
 __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ __attribute__((aligned(16))) uint32_t skey[kSumCap];   // tile summaries: score keys
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / a.G, bg = b * a.Hkv + g;
   // refresh: only the heads whose group attended over its previous zones select again
-  if (a.refresh && a.gate[bg] == 0) return;
+  if (EXT && a.refresh && a.gate[bg] == 0) return;
   const int C = a.C, W32 = a.W32, tiles = a.est_tiles_g;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   // candidate arrays, which are not used before the zone is decided
   float* gq = reinterpret_cast<float*>(ckey);
   float* gp = reinterpret_cast<float*>(cidl);
-  if (a.gated) {
+  if (EXT && a.gated) {
     const size_t row0 = ((size_t)b * a.Hq + (size_t)g * a.G) * kD;
     for (int i = tid; i < a.G * kD; i += NT) {
       gq[i] = St<T>::f(static_cast<const T*>(a.q)[row0 + i]);
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   // coordinate order) with IEEE square roots and division, 0 when either query is zero.  Every
   // head of the group takes the same decision from the same sums.
   bool reuse = false;
-  if (a.gated) {
+  if (EXT && a.gated) {
     if (tid < 3 * a.G) {                      // thread 3 j + {0, 1, 2}: <q_j, q'_j>, |q_j|^2, |q'_j|^2
       const int j = tid / 3, kind = tid - 3 * j;
       const f32x4_t* x = reinterpret_cast<const f32x4_t*>((kind == 2 ? gp : gq) + j * kD);
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
     __syncthreads();
     reuse = sh_i[6] != 0;
-  } else if (!a.refresh && tid == 0 && h == g * a.G) {
+  } else if (!(EXT && a.refresh) && tid == 0 && h == g * a.G) {
     a.gate[bg] = 0;                           // a refresh after a plain decode has nothing to do
   }
   int n_reused_ne = 0;              // non-empty clusters of a reused zone
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   // err = a (V_c + (1 + u) V_all) + w u V_c.  A zone Z bounds the error of the output by
   // (sum over the non-empty clusters outside Z of err) / (sum of every lo) before attention.
   float b_mstar = 0.f;
-  const float b_vall = a.bounded ? a.vmax[bg] : 0.f;
+  const float b_vall = EXT && a.bounded ? a.vmax[bg] : 0.f;
   // the terms of cluster c from its score key, size n, radius r and value norm vc
   struct BTerms { float err, lo, ea, eav; };
   auto bound_terms = [&](uint32_t k, float n, float r, float vc) -> BTerms {
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     const float ea = w * expm1f(x);
     return {ea * (vc + (1.f + a.u) * b_vall) + w * a.u * vc, w * __expf(-x), ea, ea * vc + w * a.u * vc};
   };
-  if (a.bounded && n_ne > 0) {
+  if (EXT && a.bounded && n_ne > 0) {
     // m*: the largest score, from the tiles' best scores when they are staged
     float m = -INFINITY;
     if (use_sum) {
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   WI_TP(8);
 
   int k_zone = reuse ? n_reused_ne : k_eff;
-  if (a.bounded) {
+  if (EXT && a.bounded) {
     // the k_eff selected clusters, ascending id, with score keys and error terms (the summary,
     // candidate, histogram and publish arrays are free until publishing, which rebuilds them)
     // zo: (score key, id) packed so that a larger value comes first in the order (-score, id)
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   // of the attention kernel, the list entry that holds its first retrieved token
   {
     const int K = a.top_k, S = a.att_split;
-    const bool lists = !a.refresh;            // refresh: sel_ids only (attention may read the lists)
+    const bool lists = !(EXT && a.refresh);   // refresh: sel_ids only (attention may read the lists)
     // ascending retrieved ids (LDS when they fit); on the candidate path each retrieved
     // candidate also drops its prefetched first row, size and key at its rank
     int32_t* rl = K <= kSumCap ? sid : a.band_ids + (size_t)bh * C;
@@ -1628,6 +1628,22 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
 }
 
 // ============================================================================ launcher
+// the select: half-size blocks beyond kSelHeadsPerRound heads; the gated, refresh and bounded
+// modes in their own instantiation, so that the plain decode's kernel carries none of their code
+template <typename T>
+static void launch_select(const DecodeArgs& a, hipStream_t s) {
+  const int BH = a.B * a.Hq;
+  const bool ext = a.gated || a.refresh || a.bounded;
+  const size_t lds = (size_t)a.W32 * 8;
+  if (BH > kSelHeadsPerRound) {
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, true>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, false>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);
+  } else {
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, true>), dim3(BH), dim3(kSelThreadsFew), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsFew, false>), dim3(BH), dim3(kSelThreadsFew), lds, s, a);
+  }
+}
+
 template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
@@ -1642,12 +1658,7 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  for (int r = 0; r < prof_reps(); ++r) {
-    if (BH > kSelHeadsPerRound)
-      hipLaunchKernelGGL((k_select<T, kSelThreadsMany>), dim3(BH), dim3(kSelThreadsMany), (size_t)a.W32 * 8, s, a);
-    else
-      hipLaunchKernelGGL((k_select<T, kSelThreadsFew>), dim3(BH), dim3(kSelThreadsFew), (size_t)a.W32 * 8, s, a);
-  }
+  for (int r = 0; r < prof_reps(); ++r) launch_select<T>(a, s);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.paged && (e = launch_wb_resolve(a, s)) != hipSuccess) return e;   // blocks of the zones
@@ -1671,14 +1682,8 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
 
 template <typename T>
 static hipError_t launch_refresh_t(const DecodeArgs& a, hipStream_t s) {
-  const int BH = a.B * a.Hq;
   prof_begin(WI_STAGE_REFRESH, s);
-  for (int r = 0; r < prof_reps(); ++r) {
-    if (BH > kSelHeadsPerRound)
-      hipLaunchKernelGGL((k_select<T, kSelThreadsMany>), dim3(BH), dim3(kSelThreadsMany), (size_t)a.W32 * 8, s, a);
-    else
-      hipLaunchKernelGGL((k_select<T, kSelThreadsFew>), dim3(BH), dim3(kSelThreadsFew), (size_t)a.W32 * 8, s, a);
-  }
+  for (int r = 0; r < prof_reps(); ++r) launch_select<T>(a, s);
   prof_end(WI_STAGE_REFRESH, s);
   return hipGetLastError();
 }
@@ -1698,10 +1703,14 @@ static hipError_t set_select_lds() {
   static bool attr_set = false;
   if (!attr_set) {
     // the select kernel's two cluster bitmaps (2 * ceil(C / 32) words) live in dynamic LDS
-    const void* fns[4] = {reinterpret_cast<const void*>(k_select<float, kSelThreadsFew>),
-                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany>)};
+    const void* fns[8] = {reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, false>),
+                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, false>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, false>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, false>),
+                          reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, true>),
+                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, true>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, true>),
+                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, true>)};
     for (const void* f : fns) {
       const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
       if (e != hipSuccess) return e;
