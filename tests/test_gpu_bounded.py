@@ -153,3 +153,56 @@ def test_bounded_decode_bound_covers_dense_attention():
             p = np.exp(lg - lg.max())
             dense = (p @ V[0, h // G]) / p.sum()
             assert np.linalg.norm(o[0, h] - dense) <= err[0, h] * (1 + 1e-3) + 2e-5, (eps, h)
+
+
+def _slice_group(idx, g):
+    f = lambda a: a[:, g:g + 1]
+    return oracle.Index(centroids=f(idx.centroids), value_sums=f(idx.value_sums), sizes=f(idx.sizes),
+                        offsets=f(idx.offsets), perm=f(idx.perm), k_perm=f(idx.k_perm), v_perm=f(idx.v_perm),
+                        k_steady=f(idx.k_steady), v_steady=f(idx.v_steady), C=idx.C, Nc=idx.Nc)
+
+
+def test_bounded_full_size_sampled_groups():
+    """The benchmarked shape (B=1, 32/8 heads, 128K, top 164 of 8192 clusters) on an index the
+    oracle finalizes from the generator's blob labels: the bound data of two KV groups bit-exact,
+    and the sampled heads' zone sizes valid and their zones, outputs and bounds equal to the
+    oracle's at the same k."""
+    from wi_testutil import inputs
+    dev = device()
+    w = synth.WORKLOADS["gqa_128k_bf16"]
+    Kt, Vt, Qt, K64, V64, Q64, labels = inputs(w, 0, dev, with_labels=True)
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    lab = (np.arange(hi - lo) // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    idx = oracle.finalize_index(K64, V64, lab, w.sink, w.window, C, w.dtype)
+    gi = upload_index(idx, w.dtype, dev)
+    bound = _bound_on_device(gi, idx, "bf16")
+    G = w.Hq // w.Hkv
+    scale = 1 / math.sqrt(D)
+    for eps in (40.0, 400.0):
+        o, lse, sel, k_used, err = wi.decode_bounded(gi, Qt, bound, w.top_k, eps)
+        torch.cuda.synchronize()
+        k_dev = k_used.cpu().numpy().astype(np.int64)
+        for g in (2, 7):
+            sub = _slice_group(idx, g)
+            bd = oracle.bound_data(sub)
+            if eps == 40.0:
+                for got, ref in ((bound[0][:, g:g + 1], bd.radius), (bound[1][:, g:g + 1], bd.vnorm),
+                                 (bound[2][:, g:g + 1], bd.vmax)):
+                    np.testing.assert_array_equal(got.cpu().numpy().astype(np.float64), ref)
+            for h in (g * G, g * G + G - 1):
+                _, order, _, _, _, errc, lov = oracle.bound_terms(Q64[0, h], sub, bd, 0, 0, scale, "bf16")
+                A = oracle.prior_bounds(errc, lov, order)
+                k = int(k_dev[0, h])
+                cap = min(w.top_k, order.size)
+                assert 0 <= k <= cap
+                if k < cap:
+                    assert A[k] <= eps * (1 + K_TOL)
+                if k > 0:
+                    assert A[k - 1] > eps * (1 - K_TOL)
+                ro, rl, rs, _, _, rpost = oracle.decode_bounded(Q64[:, h:h + 1], sub, bd, 1, w.top_k, eps, "bf16",
+                                                                k_force=np.array([[k]]))
+                assert_decode_parity(o[:, h:h + 1], lse[:, h:h + 1], sel[:, h:h + 1], ro, rl, rs, "bf16")
+                np.testing.assert_allclose(float(err[0, h]), rpost[0, 0], rtol=2e-3)
+        if eps == 400.0:
+            assert (k_dev < w.top_k).any()            # a loose enough bound shrinks some zones

@@ -333,3 +333,47 @@ def test_refresh_long_lists_and_half_size_select_blocks():
         o, lse, sel, reused = wi.decode_gated(gi, Qt, Qpt, sp, k, 0.9, refresh=True)
         torch.cuda.synchronize()
         _check(o, lse, sel, reused, ro, rl, rs, rr, dtype)
+
+
+def test_gated_full_size_sampled_heads():
+    """The benchmarked shape (B=1, 32/8 heads, 128K, top 164 of 8192 clusters) on an index the
+    oracle finalizes from the generator's blob labels; the previous step's queries are the
+    generator's, the current ones drift by N(0, 0.1^2) per coordinate, and sel_prev is the
+    oracle's own top-k of the previous queries.  Sampled heads of a kept and (by moving one
+    group's queries far) a re-selected group are checked against the oracle one by one."""
+    dev = device()
+    w = synth.WORKLOADS["gqa_128k_bf16"]
+    from wi_testutil import inputs
+    Kt, Vt, Qpt, K64, V64, Qp64, labels = inputs(w, 0, dev, with_labels=True)
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    lab = (np.arange(hi - lo) // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    idx = oracle.finalize_index(K64, V64, lab, w.sink, w.window, C, w.dtype)
+    gi = upload_index(idx, w.dtype, dev)
+    G = w.Hq // w.Hkv
+    rng = np.random.default_rng(31)
+    Qn = Qp64 + 0.1 * rng.standard_normal(Qp64.shape)
+    Qn[0, 3 * G:4 * G] = 3.0 * rng.standard_normal((G, w.d))       # group 3 moves away
+    Qt, Q64 = _queries(Qn, w.dtype)
+    scale = 1 / math.sqrt(w.d)
+    # the oracle's top-k of the previous queries, for every head
+    sel_prev = np.full((1, w.Hq, w.top_k), -1, dtype=np.int64)
+    for h in range(w.Hq):
+        R = oracle.decode_head(Qp64[0, h], idx, 0, h // G, w.top_k, scale)[2]
+        sel_prev[0, h, :R.size] = R
+    o, lse, sel, reused = _run(gi, Qt, Qpt, sel_prev, w.top_k, 0.9)
+    r = reused.cpu().numpy()[0]
+    heads = [(0, 0), (0, 5), (0, 13), (0, 14), (0, 31)]
+    want_reuse = [all(oracle.query_cosine(Q64[0, j], Qp64[0, j]) >= 0.9 for j in range(g * G, (g + 1) * G))
+                  for g in range(w.Hkv)]
+    np.testing.assert_array_equal(r.astype(bool), want_reuse)
+    assert not want_reuse[3] and sum(want_reuse) >= 6
+    res = []
+    for b, h in heads:
+        g = h // G
+        R = np.unique(sel_prev[b, h][sel_prev[b, h] >= 0]) if want_reuse[g] else None
+        res.append(oracle.decode_head(Q64[b, h], idx, b, g, w.top_k, scale, R))
+    ro = np.stack([x[0] for x in res])
+    rl = np.array([x[1] for x in res])
+    rs = np.stack([np.concatenate([x[2], -np.ones(w.top_k - x[2].size, dtype=np.int64)]) for x in res])
+    assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)

@@ -177,3 +177,36 @@ def test_wavebuf_back_to_back_steps_without_waiting():
     assert st["calls"] == 2 * len(qs)
     assert (st["hits"], st["staged"], st["admitted"], st["evicted"]) == tuple(sum(x[i] for x in want) for i in range(4))
     wb.close()
+
+
+def test_wavebuf_full_size_equals_device_decode():
+    """The benchmarked shape (B=1, 32/8 heads, 128K, top 164 of 8192 clusters), the clustered K/V
+    in pinned host memory and a cache of 30% of the blocks: five drifting steps, each equal to
+    wi_decode on the device-resident index bit for bit; the third step onwards hits the cache."""
+    from wi_testutil import inputs
+    dev = device()
+    w = synth.WORKLOADS["gqa_128k_bf16"]
+    Kt, Vt, Qt, K64, V64, Q64, labels = inputs(w, 0, dev, with_labels=True)
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    lab = (np.arange(hi - lo) // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    idx = oracle.finalize_index(K64, V64, lab, w.sink, w.window, C, w.dtype)
+    gi = upload_index(idx, w.dtype, dev)
+    nblk = -(-idx.Nc // BLK)
+    host = wi.with_host_kv(gi)
+    wb = wi.WaveBuffer(host, w.B, w.Hq, w.Hkv, w.top_k, torch.bfloat16, int(0.3 * w.Hkv * nblk),
+                       w.Hq * w.top_k * 2)
+    qm = synth.drift_queries(Q64, 5, 0.1, 3)
+    prev = wb.stats()
+    for t in range(5):
+        q = synth.cast(qm[t], "bf16", dev)
+        o1, l1, s1 = wb.decode(q)
+        o2, l2, s2 = wi.decode(gi, q, w.top_k)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2), t
+        st = wb.stats()
+        if t >= 2:
+            assert st["hits"] - prev["hits"] > 0.5 * (st["hits"] - prev["hits"] + st["staged"] - prev["staged"])
+        prev = st
+    assert st["host_reads"] == 0
+    wb.close()
