@@ -16,12 +16,15 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are device pointers unless marked (host).  All device buffers are caller-allocated
- *     and caller-owned; the library never allocates or frees device memory and keeps no device
- *     state between calls.
+ *     and caller-owned; the library never allocates or frees device memory.  Only a wave buffer
+ *     (below) keeps state between calls: its cache lives in device memory the caller provides,
+ *     and its host state in memory wi_wavebuf_create allocates.
  *   - Layout is row-major and contiguous, heads-major: [B, H, tokens, d].  Query head h reads KV
  *     head h / (Hq / Hkv).
  *   - `stream` is a hipStream_t (0 = the null stream).  Calls enqueue work and return; they never
- *     synchronise.  Asynchronous faults surface at the caller's next synchronisation.
+ *     synchronise, except that a wave-buffer call waits for the access log of the call two
+ *     before it and wi_wavebuf_stats for every pending log.  Asynchronous faults surface at the
+ *     caller's next synchronisation.
  *   - d must be 128.  Element types are fp32 (WI_F32) or bfloat16 (WI_BF16); arithmetic is fp32
  *     (fast paths) and fp64 (every decision that must be reproducible: k-means assignments and
  *     sums, top-k ties).
@@ -274,7 +277,9 @@ wi_status wi_decode_bounded(const wi_decode_params *p, const wi_index_view *idx,
  * and two events) is allocated by wi_wavebuf_create and freed by wi_wavebuf_destroy.  One
  * wave buffer serves one index (same B, Hkv, Nc and dtype) and one stream at a time; its calls
  * must not overlap and cannot be captured in a graph (the host acts between them).  The pool
- * holds at most 2^29 rows.  Errors: WI_ERR_INVALID_ARG for null or negative arguments or a
+ * holds at most 2^29 rows.  After any error from wi_decode_wavebuf, destroy the wave buffer
+ * (its host state may have advanced past the device's).  Errors: WI_ERR_INVALID_ARG for null or
+ * negative arguments or a
  * wave buffer of another index, WI_ERR_UNSUPPORTED as wi_decode and for a pool beyond 2^29
  * rows, WI_ERR_WORKSPACE for too little device memory. */
 typedef struct wi_wavebuf wi_wavebuf;
