@@ -29,6 +29,7 @@
 
 #include "wi_device.h"
 #include "wi_internal.h"
+#include "wi_lru.h"
 
 namespace wi {
 
@@ -151,111 +152,16 @@ struct WaveBuf {
   int64_t enqueued = 0;                      // calls enqueued
   int64_t processed = 0;                     // calls whose log has been processed
   int epoch = 0;
-  // exact LRU: every access takes the next tick; the least recently used slot has the smallest
-  // tick.  queue holds (tick, slot) in tick order, stale entries skipped and compacted lazily.
-  std::vector<int64_t> slot_tick;
-  std::vector<std::pair<int64_t, int32_t>> queue;
-  size_t qhead = 0;
-  int64_t tick = 0;
-  std::vector<int32_t> slot_key, dir_h, free_slots;
-  std::vector<int32_t> slot_src;             // per slot within one batch of admissions
-  std::vector<int32_t> key_mark;             // per key: the last batch that changed its entry
-  int32_t batch = 0;
-  std::vector<uint64_t> ent, tmp;            // sort buffers
-  int64_t stats[6] = {0, 0, 0, 0, 0, 0};     // calls, hits, staged misses, host reads, admitted, evicted
+  WbLru* lru = nullptr;                      // the policy (and the counters)
 
-  void touch(int s) {
-    slot_tick[s] = ++tick;
-    queue.emplace_back(tick, s);
-  }
-  int pop_lru() {
-    for (;;) {
-      const auto x = queue[qhead++];
-      if (slot_tick[x.second] == x.first) return x.second;
-    }
-  }
-  void compact_queue() {
-    if (qhead < queue.size() / 2 && queue.size() < 4 * (size_t)std::max(cache_blocks, 1024)) return;
-    std::vector<std::pair<int64_t, int32_t>> q;
-    for (size_t i = qhead; i < queue.size(); ++i)
-      if (slot_tick[queue[i].second] == queue[i].first) q.push_back(queue[i]);
-    queue.swap(q);
-    qhead = 0;
-  }
-  // entries (key << 32 | (code + 2)) sorted by key: LSD radix sort, 11 bits a pass
-  void sort_entries(int n, int key_bits) {
-    tmp.resize(n);
-    for (int shift = 32; shift < 32 + key_bits; shift += 11) {
-      int cnt[2049] = {0};
-      for (int i = 0; i < n; ++i) ++cnt[((ent[i] >> shift) & 2047) + 1];
-      for (int b = 0; b < 2048; ++b) cnt[b + 1] += cnt[b];
-      for (int i = 0; i < n; ++i) tmp[cnt[(ent[i] >> shift) & 2047]++] = ent[i];
-      ent.swap(tmp);
-    }
-  }
-  // the log of call `processed` (parity q): LRU order and the admissions applied two calls later
+  // the log of call `processed` (parity q): the decisions applied two calls later
   void process_log(int q) {
     const int n = std::min(ctr_h[q][1], log_cap);
     if (n > copied[q])       // more entries than the copy brought back: fetch the rest now
       (void)hipMemcpy(log_h[q] + 2 * (size_t)copied[q], log[q] + 2 * (size_t)copied[q], (size_t)(n - copied[q]) * 8,
                       hipMemcpyDeviceToHost);
     last_count = n;
-    ent.resize(n);
-    for (int i = 0; i < n; ++i)
-      ent[i] = ((uint64_t)(uint32_t)log_h[q][2 * i] << 32) | (uint32_t)(log_h[q][2 * i + 1] + 2);
-    int key_bits = 1;
-    while (((int64_t)1 << key_bits) < (int64_t)BG * nblk) ++key_bits;
-    sort_entries(n, key_bits);
-    for (int i = 0; i < n; ++i) {
-      if ((int)(ent[i] & 0xffffffffu) - 2 != -1) continue;
-      ++stats[1];
-      const int s = dir_h[ent[i] >> 32];
-      if (s >= 0) touch(s);                 // (a block hit then may have been evicted since)
-    }
-    std::vector<int32_t> touched, changed;
-    ++batch;
-    auto mark = [&](int key) { if (key_mark[key] != batch) { key_mark[key] = batch; changed.push_back(key); } };
-    for (int i = 0; i < n; ++i) {
-      const int key = (int)(ent[i] >> 32), code = (int)(ent[i] & 0xffffffffu) - 2;
-      if (code == -1) continue;
-      if (code == -2) { ++stats[3]; continue; }
-      ++stats[2];
-      if (cache_blocks == 0) continue;
-      if (dir_h[key] >= 0) { touch(dir_h[key]); continue; }   // admitted from an earlier log
-      int s;
-      if (!free_slots.empty()) {
-        s = free_slots.back();
-        free_slots.pop_back();
-      } else {
-        s = pop_lru();
-        dir_h[slot_key[s]] = -1;
-        mark(slot_key[s]);
-        ++stats[5];
-      }
-      if (slot_src[s] < 0) touched.push_back(s);
-      slot_src[s] = cache_blocks + q * exec_blocks + code;
-      slot_key[s] = key;
-      dir_h[key] = s;
-      mark(key);
-      touch(s);
-      ++stats[4];
-    }
-    // a slot filled more than once in this batch is copied once, with its last block; every
-    // directory entry the batch changed is sent once, with its final value
-    int32_t* cp = adm_h[q];
-    int32_t* up = adm_h[q] + 2 * (size_t)std::max(exec_blocks, 1);
-    int m = 0;
-    for (const int s : touched) {
-      cp[2 * m] = slot_src[s];
-      cp[2 * m + 1] = s;
-      ++m;
-      slot_src[s] = -1;
-    }
-    int u = 0;
-    for (const int key : changed) { up[2 * u] = key; up[2 * u + 1] = dir_h[key]; ++u; }
-    n_cp[q] = m;
-    n_up[q] = u;
-    compact_queue();
+    lru->decide(log_h[q], n, q, adm_h[q], &n_cp[q], adm_h[q] + 2 * (size_t)std::max(exec_blocks, 1), &n_up[q]);
     ++processed;
   }
   hipError_t process_through(int64_t last) {  // every log up to call `last` (inclusive)
@@ -319,11 +225,7 @@ hipError_t wavebuf_create(const wi_decode_params& p, int cache_blocks, int exec_
     w->log[q] = reinterpret_cast<int32_t*>(base + L.log) + 2 * (size_t)w->log_cap * q;
     w->adm[q] = reinterpret_cast<int32_t*>(base + L.adm) + 6 * ea * q;
   }
-  w->slot_tick.assign(cache_blocks, 0); w->slot_key.assign(cache_blocks, -1);
-  w->slot_src.assign(cache_blocks, -1);
-  w->key_mark.assign((size_t)w->BG * w->nblk, 0);
-  w->dir_h.assign((size_t)w->BG * w->nblk, -1);
-  for (int i = cache_blocks - 1; i >= 0; --i) w->free_slots.push_back(i);
+  w->lru = new WbLru(cache_blocks, exec_blocks, (int64_t)w->BG * w->nblk);
   hipError_t e = hipSuccess;
   for (int q = 0; q < 2 && e == hipSuccess; ++q) {
     e = hipHostMalloc(reinterpret_cast<void**>(&w->log_h[q]), (size_t)w->log_cap * 8 + 16, hipHostMallocDefault);
@@ -354,12 +256,13 @@ void wavebuf_destroy(WaveBuf* w) {
   }
   if (w->resolved) (void)hipEventDestroy(w->resolved);
   if (w->copy_stream) (void)hipStreamDestroy(w->copy_stream);
+  delete w->lru;
   delete w;
 }
 
 hipError_t wavebuf_sync_log(WaveBuf* w) { return w->process_through(w->enqueued - 1); }
 
-const int64_t* wavebuf_stats(WaveBuf* w) { return w->stats; }
+const int64_t* wavebuf_stats(WaveBuf* w) { return w->lru->stats; }
 
 bool wavebuf_matches(const WaveBuf* w, const wi_decode_params& p) {
   return w->B == p.B && w->Hkv == p.Hkv && w->Nc == p.Nc && w->dtype == p.dtype;
@@ -395,7 +298,7 @@ hipError_t wavebuf_begin(WaveBuf* w, hipStream_t s, DecodeArgs& a) {
   w->n_cp[q] = 0;
   w->n_up[q] = 0;
   ++w->epoch;
-  ++w->stats[0];
+  ++w->lru->stats[0];
   ++w->enqueued;
   a.paged = 1;
   a.wb_nblk = w->nblk;
