@@ -510,9 +510,9 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
                                                      // ascending retrieved list
   __shared__ __attribute__((aligned(16))) uint32_t ckey[kCandCap];   // candidates: score keys
   __shared__ __attribute__((aligned(16))) int cidl[kCandCap];        // candidates: cluster ids
-  __shared__ int tfull[kFullCap];                    // tiles whose 8 best pass the threshold
-  __shared__ int rl_off[kCandCap];                   // retrieved list, by rank: first row, size
-  __shared__ int rl_sz[kCandCap];
+  __shared__ __attribute__((aligned(16))) int tfull[kFullCap];   // tiles whose 8 best pass the threshold
+  __shared__ __attribute__((aligned(16))) int rl_off[kCandCap];  // retrieved list, by rank: first row, size
+  __shared__ __attribute__((aligned(16))) int rl_sz[kCandCap];
   __shared__ uint32_t hist[kBins];
   __shared__ int iscr[48];
   __shared__ float fred[32];
@@ -763,10 +763,19 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
     }
     WI_TP(5);
-    // ---- t = k_eff-th largest score: L itself when no tile was scanned in full, else from the
-    // candidates, else over all scores
+    // ---- t = k_eff-th largest score: L itself when no cluster outside the summaries scores above
+    // L (every cluster above L is then a summary entry, at most k_eff - 1 of them, so the k_eff-th
+    // largest is L): true when no tile was scanned in full, and checked by counting otherwise
+    // (the candidates hold every cluster above L); else from the candidates, else over all scores
+    bool t_is_L = listed && L != 0u && !scan_all && sh_i[5] == 0;
+    if (listed && L != 0u && !t_is_L) {
+      int d = 0;
+      for (int i = tid; i < n_c; i += NT) d += ckey[i] > L ? 1 : 0;
+      for (int i = tid; i < nsum; i += NT) d -= skey[i] > L ? 1 : 0;
+      t_is_L = block_isum<NT>(d, iscr) == 0;
+    }
     uint32_t thr;
-    if (listed && !scan_all && sh_i[5] == 0 && L != 0u) {
+    if (t_is_L) {
       thr = L;
     } else if (listed) {
       thr = kth_largest_key<NT>(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
@@ -806,11 +815,32 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     if (need >= n_band) {
       for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
     } else if (n_band <= kSmallBand) {
-      // one wave: canonical scores, then rank by (-sigma, id); the band is in ascending id order
+      // canonical scores, one wave per band cluster: the lanes form the 128 exact products (two
+      // each) in a row of LDS scratch (the publish arrays, free until publishing), then lane 0
+      // adds them in ascending coordinate order -- the roundings of canonical_score_row.  Then
+      // one wave ranks by (-sigma, id); the band is in ascending id order.
+      static_assert((NT / 64) * kD * 8 <= 2 * kCandCap * 4, "a row of fp64 products per wave");
+      static_assert(kSmallBand * 8 <= kFullCap * 4, "the band's score keys");
+      double* prow = (wv < 8 ? reinterpret_cast<double*>(rl_off) : reinterpret_cast<double*>(rl_sz)) + (wv & 7) * kD;
+      uint64_t* bk = reinterpret_cast<uint64_t*>(tfull);
+      for (int j = wv; j < n_band; j += NT / 64) {
+        const T* m = mu + (size_t)band[j] * kD + 2 * lane;
+        prow[2 * lane] = qd[2 * lane] * (double)St<T>::f(m[0]);
+        prow[2 * lane + 1] = qd[2 * lane + 1] * (double)St<T>::f(m[1]);
+        wave_lds_sync();
+        if (lane == 0) {
+          double acc = 0.0;
+#pragma unroll 16
+          for (int e = 0; e < kD; ++e) acc = acc + prow[e];
+          bk[j] = f64_order_key(acc);
+        }
+        wave_lds_sync();
+      }
+      __syncthreads();
       if (wv == 0) {
         const bool live = lane < n_band;
         const int c = live ? band[lane] : 0;
-        const uint64_t key = live ? f64_order_key(canonical_score_row<T>(qd, mu + (size_t)c * kD)) : 0ull;
+        const uint64_t key = live ? bk[lane] : 0ull;
         int rank = 0;
         for (int j = 0; j < n_band; ++j) {
           const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
@@ -1258,14 +1288,6 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));  // row half mirror
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));  // row mirror
   return v;
-}
-
-// Orders this wave's LDS writes before its later LDS reads (and the reverse) without a block
-// barrier: the lanes of one wave hand values to each other through LDS.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Scores of a query against 16 key rows on MFMA: A = the query (row 0; rows 1-15 zero), B = the

@@ -77,6 +77,14 @@ __device__ __forceinline__ uint64_t f64_order_key(double x) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Orders this wave's LDS writes before its later LDS reads (and the reverse) without a block
+// barrier: the lanes of one wave hand values to each other through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------------ wave / block reductions
 // Lane exchanges inside a DPP row of 16 lanes (VALU operand modifiers, no LDS traffic):
 // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
