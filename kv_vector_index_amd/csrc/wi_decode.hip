@@ -314,7 +314,8 @@ constexpr int kSumCap = 4096;       // tile summaries (8 per 128-cluster tile) s
 constexpr int kCandCap = 2048;      // candidate clusters ranked in LDS
 constexpr int kFullCap = 256;       // tiles scanned in full
 constexpr int kBins = 2048;         // histogram bins over [min, max] of the ranked scores
-constexpr int kPubPT = 8;           // retrieved clusters per thread in one publishing round
+constexpr int kPubPT = 1;           // retrieved clusters per thread in one publishing round (lanes
+                                    // take consecutive entries, so the list stores coalesce)
 
 // Radix bin of the k-th largest key: each thread owns 256 / NT consecutive bins in
 // descending order, so an exclusive scan over the threads gives the count above each thread's
@@ -1124,9 +1125,11 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
       t_run += csum;
     }
+    WI_TP(26);
     // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); the entry holding its
     // first retrieved token max(that start, NS): the last entry whose first token is <= it
     __syncthreads();
+    WI_TP(27);
     if (lists && tot > 0) {
       for (int x = tid; x < S; x += NT) {
         const int u = max((int)(((int64_t)x * ntok) / S), a.NS);
@@ -1139,6 +1142,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
         bounds[x] = lo;
       }
     }
+    WI_TP(28);
     for (int i = tot + tid; i < K; i += NT) {
       if (out) out[i] = -1;
       if (lists) { a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok; }
