@@ -1108,6 +1108,14 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       int t = t_run + block_exclusive_scan<NT>(ssum, iscr, &csum);
       WI_TP(11);
       if (tot <= chunk) ntok = (int64_t)a.NS + csum;
+      // token workgroup x covers [floor(x ntok / S), floor((x+1) ntok / S)); its first retrieved
+      // token is u_x = max(that start, NS), and its entry the last one whose first token is
+      // <= u_x.  u_x >= p holds for every x when p <= NS, else for x >= ceil(p S / ntok), so
+      // entry i (tokens [t_i, t_i + size)) is the entry of x in [x_first(t_i), x_first(t_i +
+      // size)), the last entry also of every later x
+      auto x_first = [&](int p) -> int {
+        return p <= a.NS ? 0 : (int)min<int64_t>(S, ((int64_t)p * S + ntok - 1) / ntok);
+      };
 #pragma unroll
       for (int u = 0; u < kPubPT; ++u) {
         const int i = i0 + u;
@@ -1118,31 +1126,15 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
             a.hl_row[lb + i] = r_[u];
             a.hl_pre[pb + i] = t;
             a.hl_key[lb + i] = k_[u];
+            const int x1 = i == tot - 1 ? S : x_first(t + z_[u]);
+            for (int x = x_first(t); x < x1; ++x) bounds[x] = i;
           }
-          if (tot <= kSumCap) skey[i] = (uint32_t)t;
           t += z_[u];
         }
       }
       t_run += csum;
     }
     WI_TP(26);
-    // token workgroup s covers [floor(s ntok / S), floor((s+1) ntok / S)); the entry holding its
-    // first retrieved token max(that start, NS): the last entry whose first token is <= it
-    __syncthreads();
-    WI_TP(27);
-    if (lists && tot > 0) {
-      for (int x = tid; x < S; x += NT) {
-        const int u = max((int)(((int64_t)x * ntok) / S), a.NS);
-        int lo = 0, hi = tot;                      // first token of entry lo <= u < that of hi
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          const int pm = tot <= kSumCap ? (int)skey[mid] : a.hl_pre[pb + mid];
-          if (pm <= u) lo = mid; else hi = mid;
-        }
-        bounds[x] = lo;
-      }
-    }
-    WI_TP(28);
     for (int i = tot + tid; i < K; i += NT) {
       if (out) out[i] = -1;
       if (lists) { a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok; }
