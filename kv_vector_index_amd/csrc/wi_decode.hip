@@ -702,7 +702,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
         if ((double)thr_f > thr_d) thr_f = nextafterf(thr_f, -INFINITY);
       }
     }
-    if (tid == 0) { sh_i[2] = 0; sh_i[5] = 0; }
+    if (tid == 0) { sh_i[2] = 0; sh_i[5] = 0; sh_i[7] = 0; }
     __syncthreads();
     WI_TP(4);
     // ---- candidates: the non-empty clusters scoring >= L - 2 delta (appends wave-aggregated)
@@ -788,30 +788,38 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     // ---- in / band / out
     const double that = (double)f32_from_order_key(thr);
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
+    // the band goes to a bitmap and, while it has at most kSmallBand members, straight to a list
+    // in LDS (in no particular order); a longer band is listed from the bitmap in ascending id
     int nin = 0;
     auto classify = [&](int c, uint32_t k) {
       if (k == 0u) return;
       const double v = (double)f32_from_order_key(k);
       if (v > hi) { atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
-      else if (v >= lo) atomicOr(&bbits[c >> 5], 1u << (c & 31));
+      else if (v >= lo) {
+        atomicOr(&bbits[c >> 5], 1u << (c & 31));
+        const int p = atomicAdd(&sh_i[7], 1);
+        if (p < kSmallBand) band_lds[p] = c;
+      }
     };
     if (listed) for (int i = tid; i < n_c; i += NT) classify(cidl[i], ckey[i]);
     else visit_keys(classify);
     const int n_in = block_isum<NT>(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
-    // band list in ascending id order from the band bitmap
-    const int perw = (W32 + NT - 1) / NT;
-    const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
-    int nb = 0;
-    for (int w = w0; w < w1; ++w) nb += __popc(bbits[w]);
-    int n_band;
-    int pos = block_exclusive_scan<NT>(nb, iscr, &n_band);
-    int32_t* band = n_band <= kSmallBand ? band_lds : a.band_ids + (size_t)bh * C;
-    for (int w = w0; w < w1; ++w) {
-      uint32_t m = bbits[w];
-      while (m) { const int bit = __ffs(m) - 1; m &= m - 1; band[pos++] = w * 32 + bit; }
+    int n_band = sh_i[7];
+    int32_t* band = band_lds;
+    if (n_band > kSmallBand) {
+      const int perw = (W32 + NT - 1) / NT;
+      const int w0 = min(W32, tid * perw), w1 = min(W32, w0 + perw);
+      int nb = 0;
+      for (int w = w0; w < w1; ++w) nb += __popc(bbits[w]);
+      int pos = block_exclusive_scan<NT>(nb, iscr, &n_band);
+      band = a.band_ids + (size_t)bh * C;
+      for (int w = w0; w < w1; ++w) {
+        uint32_t m = bbits[w];
+        while (m) { const int bit = __ffs(m) - 1; m &= m - 1; band[pos++] = w * 32 + bit; }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     WI_TP(7);
     if (need >= n_band) {
       for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
@@ -819,7 +827,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       // canonical scores, one wave per band cluster: the lanes form the 128 exact products (two
       // each) in a row of LDS scratch (the publish arrays, free until publishing), then lane 0
       // adds them in ascending coordinate order -- the roundings of canonical_score_row.  Then
-      // one wave ranks by (-sigma, id); the band is in ascending id order.
+      // one wave ranks by (-sigma, id).
       static_assert((NT / 64) * kD * 8 <= 2 * kCandCap * 4, "a row of fp64 products per wave");
       static_assert(kSmallBand * 8 <= kFullCap * 4, "the band's score keys");
       double* prow = (wv < 8 ? reinterpret_cast<double*>(rl_off) : reinterpret_cast<double*>(rl_sz)) + (wv & 7) * kD;
@@ -844,9 +852,8 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
         const uint64_t key = live ? bk[lane] : 0ull;
         int rank = 0;
         for (int j = 0; j < n_band; ++j) {
-          const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
-                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, j);
-          rank += (kj > key) || (kj == key && j < lane);
+          const uint64_t kj = bk[j];
+          rank += (kj > key) || (kj == key && band[j] < c);
         }
         if (live && rank < need) atomicOr(&bits[c >> 5], 1u << (c & 31));
       }
