@@ -463,6 +463,70 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
   return block_radix_select<NT, uint32_t>(n, k, get, hist, iscr, &rr);
 }
 
+// For one wave (no block barriers): the k-th largest (k >= 1) of n <= 64 KR order keys get(i),
+// given that at least k of them are >= L > 0.  Returns L when fewer than k keys exceed L.
+// Otherwise the k-th largest is the e-th smallest key above L, e = #(keys > L) - k + 1: a
+// 256-bin histogram over (L, max] names its bin, and the bin's keys are ranked directly.  The
+// keys are read once, KR per lane, and kept in registers.  Returns 0 when n > 64 KR or when that
+// bin holds more than 64 keys (the caller then searches with the whole block).  `hist` holds
+// >= 256 counters and `bl` >= 64 keys of LDS that no other wave touches meanwhile.
+template <int KR, typename Get>
+__device__ uint32_t wave_kth_above(int n, int k, uint32_t L, Get get, uint32_t* hist, uint32_t* bl) {
+  constexpr int NB = 256;
+  if (n > 64 * KR) return 0u;
+  const int lane = threadIdx.x & 63;
+  uint32_t kr[KR];
+#pragma unroll
+  for (int r = 0; r < KR; ++r) { const int i = lane + 64 * r; kr[r] = i < n ? get(i) : 0u; }
+#pragma unroll
+  for (int j = 0; j < NB / 64; ++j) hist[lane + 64 * j] = 0u;
+  int d = 0;
+  uint32_t mk = 0u;
+#pragma unroll
+  for (int r = 0; r < KR; ++r) if (kr[r] > L) { ++d; mk = max(mk, kr[r]); }
+  d = wave_isum(d);
+  if (d < k) return L;
+  mk = wave_umax(mk);
+  const int e = d - k + 1;
+  const float lo = f32_from_order_key(L), hi = f32_from_order_key(mk);
+  const float inv = hi > lo ? (float)NB / (hi - lo) : 0.f;
+  auto bin_of_key = [&](uint32_t key) { return min(NB - 1, max(0, (int)((f32_from_order_key(key) - lo) * inv))); };
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < KR; ++r) if (kr[r] > L) atomicAdd(&hist[bin_of_key(kr[r])], 1u);
+  wave_lds_sync();
+  // lane j holds bins 4 j .. 4 j + 3, ascending; the bin holding the e-th smallest
+  const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const int v = (int)(h0 + h1 + h2 + h3);
+  const int inc = wave_inclusive_scan(v), exc = inc - v;
+  const uint64_t own = __ballot(exc < e && e <= inc);
+  const int owner = __ffsll((unsigned long long)own) - 1;
+  int bin = 0, below = exc, nb = (int)h0;
+  if (below + (int)h0 < e) { below += (int)h0; bin = 1; nb = (int)h1;
+    if (below + (int)h1 < e) { below += (int)h1; bin = 2; nb = (int)h2;
+      if (below + (int)h2 < e) { below += (int)h2; bin = 3; nb = (int)h3; } } }
+  bin = __builtin_amdgcn_readlane(4 * lane + bin, owner);
+  below = __builtin_amdgcn_readlane(below, owner);
+  nb = __builtin_amdgcn_readlane(nb, owner);
+  if (nb > 64) return 0u;
+  int run = 0;
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    const bool take = kr[r] > L && bin_of_key(kr[r]) == bin;
+    const uint64_t m = __ballot(take);
+    if (take) bl[run + __popcll(m & ((1ull << lane) - 1ull))] = kr[r];
+    run += __popcll(m);
+  }
+  wave_lds_sync();
+  // the rem-th smallest key of the bin
+  const int rem = e - below;
+  const uint32_t key = lane < nb ? bl[lane] : 0u;
+  int lt = 0, le = 0;
+  for (int j = 0; j < nb; ++j) { const uint32_t kj = bl[j]; lt += kj < key; le += kj <= key; }
+  const uint64_t hit = __ballot(lane < nb && lt < rem && rem <= le);
+  return (uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((unsigned long long)hit) - 1);
+}
+
 // Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
 // summed in ascending coordinate order, no contraction.  The row is fetched in four batches.
 template <typename T>
@@ -537,22 +601,37 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
   const int KPT = (C + NT - 1) / NT;          // thread t visits clusters j * NT + t, j < KPT
 
-  // ---- set-up: query, largest centroid norm, non-empty count, tile summaries
-  float qv = 0.f;                             // this thread's part of |q|^2
-  for (int i = tid; i < kD; i += NT) { const float x = St<T>::f(qh[i]); qd[i] = (double)x; qv += x * x; }
-  float mxn = 0.f;
-  int ne = 0;
-  for (int i = tid; i < tiles; i += NT) {
-    mxn = fmaxf(mxn, a.tile_norm[(size_t)bg * tiles + i]);
-    ne += a.tile_cnt[(size_t)bg * tiles + i];
-  }
+  // ---- set-up: query, largest centroid norm, non-empty count, tile summaries.  Each thread's
+  // first element of each is loaded before any of them is used (indices clamped in range, the
+  // value kept only where in range), so that the loads share one round trip; any further
+  // elements follow in loops.
   const int nsum = tiles * kTileTop;
   const bool use_sum = nsum <= kSumCap;
-  if (use_sum)
-    for (int i = tid; i < nsum; i += NT) {
-      skey[i] = a.tile_top[(size_t)bh * nsum + i];
-      sid[i] = a.tile_top_id[(size_t)bh * nsum + i];
-    }
+  const float* tnorm = a.tile_norm + (size_t)bg * tiles;
+  const int* tcnt = a.tile_cnt + (size_t)bg * tiles;
+  const uint32_t* ttop = a.tile_top + (size_t)bh * nsum;
+  const int* ttid = a.tile_top_id + (size_t)bh * nsum;
+  const float q0 = St<T>::f(qh[min(tid, kD - 1)]);
+  float tn0 = 0.f;
+  int tc0 = 0;
+  if (tiles > 0) { tn0 = tnorm[min(tid, tiles - 1)]; tc0 = tcnt[min(tid, tiles - 1)]; }
+  uint32_t sk0 = 0u;
+  int si0 = 0;
+  if (use_sum && nsum > 0) { sk0 = ttop[min(tid, nsum - 1)]; si0 = ttid[min(tid, nsum - 1)]; }
+  float qv = 0.f;                             // this thread's part of |q|^2
+  if (tid < kD) { qd[tid] = (double)q0; qv = q0 * q0; }
+  for (int i = tid + NT; i < kD; i += NT) { const float x = St<T>::f(qh[i]); qd[i] = (double)x; qv += x * x; }
+  float mxn = tid < tiles ? tn0 : 0.f;
+  int ne = tid < tiles ? tc0 : 0;
+  for (int i = tid + NT; i < tiles; i += NT) { mxn = fmaxf(mxn, tnorm[i]); ne += tcnt[i]; }
+  if (use_sum) {
+    if (tid < nsum) { skey[tid] = sk0; sid[tid] = si0; }
+    for (int i = tid + NT; i < nsum; i += NT) { skey[i] = ttop[i]; sid[i] = ttid[i]; }
+  }
+  // every set-up load has landed: say so to the compiler (vmcnt(0) expcnt(7) lgkmcnt(15)), whose
+  // bookkeeping would otherwise keep a conditionally loaded register pending on some paths and,
+  // at its next reuse, wait for every later load (the candidates' first rows in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   for (int w = tid; w < 2 * W32; w += NT) dynl[w] = 0u;
   // gated decode: the KV group's current and previous queries, staged (exact in fp32) in the
   // candidate arrays, which are not used before the zone is decided
@@ -637,6 +716,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
         const int c = (j0 + i) * NT + tid;
         if (c < C) fn(c, k[i]);
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);         // every load above has landed (as at set-up)
     }
   };
 
@@ -755,29 +835,37 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     const int n_c = sh_i[2];
     const bool listed = n_c <= kCandCap;
     fast_pub = listed;
-    // first rows and sizes of the candidates, fetched now and used when publishing
-    if (listed) {
-#pragma unroll
-      for (int j = 0; j < kCandCap / NT; ++j) {
-        const int i = tid + j * NT;
-        if (i < n_c) { const int c = cidl[i]; co[j] = a.offsets[(size_t)bg * (C + 1) + c]; ce[j] = a.offsets[(size_t)bg * (C + 1) + c + 1]; }
-      }
-    }
     WI_TP(5);
-    // ---- t = k_eff-th largest score: L itself when no cluster outside the summaries scores above
-    // L (every cluster above L is then a summary entry, at most k_eff - 1 of them, so the k_eff-th
-    // largest is L): true when no tile was scanned in full, and checked by counting otherwise
-    // (the candidates hold every cluster above L); else from the candidates, else over all scores
+    // ---- t = k_eff-th largest score.  The candidates hold every cluster above L and at least
+    // k_eff of them score >= L, so t = L when fewer than k_eff candidates score above L; always so
+    // when no tile was scanned in full (every cluster above L is then one of the fewer than k_eff
+    // summary entries above L).  Otherwise one wave finds t among the candidates above L when
+    // there are at most 512 candidates (the block counts them when there are more); the whole
+    // block searches the candidates when there are more or that wave's histogram bin is crowded,
+    // and every score when the candidates overflowed.
     bool t_is_L = listed && L != 0u && !scan_all && sh_i[5] == 0;
-    if (listed && L != 0u && !t_is_L) {
+    uint32_t thr = 0u;
+    if (listed && L != 0u && !t_is_L && n_c > 64 * 8) {
       int d = 0;
       for (int i = tid; i < n_c; i += NT) d += ckey[i] > L ? 1 : 0;
-      for (int i = tid; i < nsum; i += NT) d -= skey[i] > L ? 1 : 0;
-      t_is_L = block_isum<NT>(d, iscr) == 0;
+      t_is_L = block_isum<NT>(d, iscr) < k_eff;
+    } else if (listed && L != 0u && !t_is_L) {
+      if (wv == 0) {
+        const uint32_t r = wave_kth_above<8>(n_c, k_eff, L, [&](int i) { return ckey[i]; }, hist,
+                                             reinterpret_cast<uint32_t*>(band_lds));
+        if (lane == 0) sh_i[3] = (int)r;
+      }
+      __syncthreads();
+      thr = (uint32_t)sh_i[3];
+      t_is_L = thr == L;
     }
-    uint32_t thr;
+    WI_TV(50, n_c);
+    WI_TV(51, sh_i[5]);
+    WI_TV(52, t_is_L ? 1 : (listed && thr != 0u) ? 2 : listed ? 3 : 4);
     if (t_is_L) {
       thr = L;
+    } else if (listed && thr != 0u) {
+      // found by the wave
     } else if (listed) {
       thr = kth_largest_key<NT>(n_c, k_eff, [&](int i) { return ckey[i]; }, hist, reinterpret_cast<uint32_t*>(band_lds), iscr, fred, sh_i);
     } else {
@@ -785,6 +873,15 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       thr = block_radix_select<NT, uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
     }
     WI_TP(6);
+    // first rows and sizes of the candidates, fetched now (in flight while the band is classified
+    // and re-scored) and used when publishing
+    if (listed) {
+#pragma unroll
+      for (int j = 0; j < kCandCap / NT; ++j) {
+        const int i = tid + j * NT;
+        if (i < n_c) { const int c = cidl[i]; co[j] = a.offsets[(size_t)bg * (C + 1) + c]; ce[j] = a.offsets[(size_t)bg * (C + 1) + c + 1]; }
+      }
+    }
     // ---- in / band / out
     const double that = (double)f32_from_order_key(thr);
     const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
@@ -806,6 +903,8 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     const int n_in = block_isum<NT>(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
     int n_band = sh_i[7];
+    WI_TV(53, n_band);
+    WI_TV(54, need);
     int32_t* band = band_lds;
     if (n_band > kSmallBand) {
       const int perw = (W32 + NT - 1) / NT;
@@ -821,8 +920,14 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       __syncthreads();
     }
     WI_TP(7);
+    // (a band listed in LDS is read through band_lds itself: through the generic pointer the
+    // reads would be flat loads, which wait for every global load in flight)
     if (need >= n_band) {
-      for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+      if (n_band <= kSmallBand) {
+        for (int i = tid; i < n_band; i += NT) { const int c = band_lds[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+      } else {
+        for (int i = tid; i < n_band; i += NT) { const int c = band[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+      }
     } else if (n_band <= kSmallBand) {
       // canonical scores, one wave per band cluster: the lanes form the 128 exact products (two
       // each) in a row of LDS scratch (the publish arrays, free until publishing), then lane 0
@@ -833,7 +938,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       double* prow = (wv < 8 ? reinterpret_cast<double*>(rl_off) : reinterpret_cast<double*>(rl_sz)) + (wv & 7) * kD;
       uint64_t* bk = reinterpret_cast<uint64_t*>(tfull);
       for (int j = wv; j < n_band; j += NT / 64) {
-        const T* m = mu + (size_t)band[j] * kD + 2 * lane;
+        const T* m = mu + (size_t)band_lds[j] * kD + 2 * lane;
         prow[2 * lane] = qd[2 * lane] * (double)St<T>::f(m[0]);
         prow[2 * lane + 1] = qd[2 * lane + 1] * (double)St<T>::f(m[1]);
         wave_lds_sync();
@@ -848,12 +953,12 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       __syncthreads();
       if (wv == 0) {
         const bool live = lane < n_band;
-        const int c = live ? band[lane] : 0;
+        const int c = live ? band_lds[lane] : 0;
         const uint64_t key = live ? bk[lane] : 0ull;
         int rank = 0;
         for (int j = 0; j < n_band; ++j) {
           const uint64_t kj = bk[j];
-          rank += (kj > key) || (kj == key && band[j] < c);
+          rank += (kj > key) || (kj == key && band_lds[j] < c);
         }
         if (live && rank < need) atomicOr(&bits[c >> 5], 1u << (c & 31));
       }

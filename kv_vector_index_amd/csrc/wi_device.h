@@ -11,8 +11,11 @@ namespace wi {
 #ifdef WI_TRACE
 extern __device__ unsigned long long g_trace[64][8192];
 #define WI_TP(ev) do { const unsigned wi_tp_i = blockIdx.x + blockIdx.y * gridDim.x; if (threadIdx.x == 0 && wi_tp_i < 8192u) ::wi::g_trace[ev][wi_tp_i] = wall_clock64(); } while (0)
+// a value (one per workgroup) instead of a time
+#define WI_TV(ev, v) do { const unsigned wi_tp_i = blockIdx.x + blockIdx.y * gridDim.x; if (threadIdx.x == 0 && wi_tp_i < 8192u) ::wi::g_trace[ev][wi_tp_i] = (unsigned long long)(v) + 1ull; } while (0)
 #else
 #define WI_TP(ev) do { } while (0)
+#define WI_TV(ev, v) do { } while (0)
 #endif
 
 constexpr int kD = 128;     // head dimension the kernels are written for

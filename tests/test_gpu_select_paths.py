@@ -28,10 +28,11 @@ pytestmark = pytest.mark.gpu
 SINK, WINDOW = 4, 16
 
 
-def _case(C, tokens_per_cluster, Hq, Hkv, dtype, seed, empty_frac=0.1, crowd=0, crowd_heads=1):
+def _case(C, tokens_per_cluster, Hq, Hkv, dtype, seed, empty_frac=0.1, crowd=0, crowd_heads=1, crowd_noise=0.05):
     """Random unit keys, Gaussian values, random labels with ~empty_frac empty clusters.  With
     crowd > 0, clusters 0 .. crowd-1 (all in the first tiles) hold keys close to one direction u
-    and the first `crowd_heads` query heads of every group point at u."""
+    (exactly u with crowd_noise 0: equal mean keys, so equal scores) and the first `crowd_heads`
+    query heads of every group point at u."""
     rng = np.random.default_rng(seed)
     d = 128
     Nc = C * tokens_per_cluster
@@ -54,7 +55,7 @@ def _case(C, tokens_per_cluster, Hq, Hkv, dtype, seed, empty_frac=0.1, crowd=0, 
             u = rng.standard_normal(d)
             u /= np.linalg.norm(u)
             pos = SINK + np.nonzero(lab < crowd)[0]
-            K[0, g, pos] = u + 0.05 * rng.standard_normal((pos.size, d))
+            K[0, g, pos] = u + crowd_noise * rng.standard_normal((pos.size, d))
             for j in range(crowd_heads):
                 Q[0, g * G + j] = 6.0 * u + 0.1 * rng.standard_normal(d)
     K /= np.linalg.norm(K, axis=-1, keepdims=True)
@@ -77,6 +78,32 @@ def test_select_crowded_tile_is_scanned_in_full():
     # 40 of the best clusters sit in the first tile: its 8th best passes the bound
     idx, Qt, Q64 = _case(C=1024, tokens_per_cluster=3, Hq=8, Hkv=2, dtype="bf16", seed=1, crowd=40)
     _check(idx, Qt, Q64, Hq=8, k=50, dtype="bf16")
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_select_threshold_above_the_summary_bound(seed):
+    # crowded first tiles scanned in full: the k-th largest lies above the summaries' bound (more
+    # than k - 1 clusters above it) or is the bound itself (nothing beyond the summaries above it)
+    idx, Qt, Q64 = _case(C=1024, tokens_per_cluster=3, Hq=8, Hkv=2, dtype="bf16", seed=seed, crowd=40,
+                         crowd_heads=4)
+    for k in (6, 20, 45, 60):
+        _check(idx, Qt, Q64, Hq=8, k=k, dtype="bf16")
+
+
+def test_select_threshold_above_the_bound_among_many_candidates():
+    # 700 crowded clusters and k = 600: more candidates than one wave ranks from its registers
+    idx, Qt, Q64 = _case(C=2048, tokens_per_cluster=2, Hq=4, Hkv=1, dtype="bf16", seed=15, crowd=700,
+                         crowd_heads=2)
+    _check(idx, Qt, Q64, Hq=4, k=600, dtype="bf16")
+
+
+def test_select_threshold_among_many_equal_scores():
+    # 200 clusters with equal mean keys, the k-th largest among them: more than a wave's worth of
+    # candidates share its histogram bin (the whole block searches), and the ties are broken by id
+    idx, Qt, Q64 = _case(C=1024, tokens_per_cluster=3, Hq=8, Hkv=2, dtype="bf16", seed=14, crowd=200,
+                         crowd_heads=2, crowd_noise=0.0)
+    for k in (150, 230):
+        _check(idx, Qt, Q64, Hq=8, k=k, dtype="bf16")
 
 
 def test_select_candidates_overflow_to_radix_over_all_scores():
