@@ -141,7 +141,8 @@ struct WaveBuf {
   void *pool_k = nullptr, *pool_v = nullptr;
   int32_t *dir = nullptr, *claim = nullptr, *loc = nullptr;
   int32_t *ctr[2] = {nullptr, nullptr}, *log[2] = {nullptr, nullptr}, *adm[2] = {nullptr, nullptr};
-  // host (pinned) copies
+  // host (pinned) copies; the counters sit right before the log on both sides, so that one copy
+  // brings both back
   int32_t *log_h[2] = {nullptr, nullptr}, *ctr_h[2] = {nullptr, nullptr}, *adm_h[2] = {nullptr, nullptr};
   int copied[2] = {0, 0};                    // log entries each pending copy brings back
   int n_cp[2] = {0, 0}, n_up[2] = {0, 0};    // pending admissions: copies, directory updates
@@ -176,7 +177,7 @@ struct WaveBuf {
 };
 
 struct WbLayout {
-  size_t pool_k, pool_v, dir, claim, loc, ctr, log, adm, total;
+  size_t pool_k, pool_v, dir, claim, loc, log, log_stride, adm, total;
 };
 
 static WbLayout wb_layout(int64_t BG, int64_t nblk, int64_t pool_blocks, int64_t exec_blocks, int esize,
@@ -189,8 +190,8 @@ static WbLayout wb_layout(int64_t BG, int64_t nblk, int64_t pool_blocks, int64_t
   L.dir = o;    o = align256(o + BG * nblk * 4);
   L.claim = o;  o = align256(o + BG * nblk * 4);
   L.loc = o;    o = align256(o + BG * nblk * 4);
-  L.ctr = o;    o = align256(o + 2 * 16);
-  L.log = o;    o = align256(o + 2 * log_cap * 8);
+  L.log_stride = align256(16 + (size_t)log_cap * 8);   // per parity: 4 counters, then the log
+  L.log = o;    o = align256(o + 2 * L.log_stride);
   L.adm = o;    o = align256(o + 2 * std::max<int64_t>(exec_blocks, 1) * 24);   // copies + updates
   L.total = o;
   return L;
@@ -221,16 +222,16 @@ hipError_t wavebuf_create(const wi_decode_params& p, int cache_blocks, int exec_
   w->loc = reinterpret_cast<int32_t*>(base + L.loc);
   const size_t ea = (size_t)std::max(exec_blocks, 1);
   for (int q = 0; q < 2; ++q) {
-    w->ctr[q] = reinterpret_cast<int32_t*>(base + L.ctr) + 4 * q;
-    w->log[q] = reinterpret_cast<int32_t*>(base + L.log) + 2 * (size_t)w->log_cap * q;
+    w->ctr[q] = reinterpret_cast<int32_t*>(base + L.log + L.log_stride * q);
+    w->log[q] = w->ctr[q] + 4;
     w->adm[q] = reinterpret_cast<int32_t*>(base + L.adm) + 6 * ea * q;
   }
   w->lru = new WbLru(cache_blocks, exec_blocks, (int64_t)w->BG * w->nblk);
   hipError_t e = hipSuccess;
   for (int q = 0; q < 2 && e == hipSuccess; ++q) {
-    e = hipHostMalloc(reinterpret_cast<void**>(&w->log_h[q]), (size_t)w->log_cap * 8 + 16, hipHostMallocDefault);
+    e = hipHostMalloc(reinterpret_cast<void**>(&w->ctr_h[q]), (size_t)w->log_cap * 8 + 16, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&w->adm_h[q]), ea * 24, hipHostMallocDefault);
-    if (e == hipSuccess) { w->ctr_h[q] = w->log_h[q] + 2 * (size_t)w->log_cap; std::memset(w->ctr_h[q], 0, 16); }
+    if (e == hipSuccess) { std::memset(w->ctr_h[q], 0, 16); w->log_h[q] = w->ctr_h[q] + 4; }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&w->log_ready[q], hipEventDisableTiming);
   }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&w->copy_stream, hipStreamNonBlocking);
@@ -250,7 +251,7 @@ void wavebuf_destroy(WaveBuf* w) {
   if (!w) return;
   if (w->copy_stream) (void)hipStreamSynchronize(w->copy_stream);
   for (int q = 0; q < 2; ++q) {
-    if (w->log_h[q]) (void)hipHostFree(w->log_h[q]);
+    if (w->ctr_h[q]) (void)hipHostFree(w->ctr_h[q]);
     if (w->adm_h[q]) (void)hipHostFree(w->adm_h[q]);
     if (w->log_ready[q]) (void)hipEventDestroy(w->log_ready[q]);
   }
@@ -277,14 +278,14 @@ hipError_t wavebuf_begin(WaveBuf* w, hipStream_t s, DecodeArgs& a) {
   if (e != hipSuccess) return e;
   const int ncp = w->n_cp[q], nup = w->n_up[q];
   const size_t ea = (size_t)std::max(w->exec_blocks, 1);
-  // the copies at the front of the list, the directory updates after 2 ea ints
-  if (ncp > 0 && (e = hipMemcpyAsync(w->adm[q], w->adm_h[q], (size_t)ncp * 8, hipMemcpyHostToDevice, s)) != hipSuccess)
-    return e;
-  if (nup > 0 && (e = hipMemcpyAsync(w->adm[q] + 2 * ea, w->adm_h[q] + 2 * ea, (size_t)nup * 8, hipMemcpyHostToDevice,
-                                     s)) != hipSuccess)
+  // the block copies, then the directory updates (decided after 2 ea ints, moved up to follow the
+  // copies), in one transfer
+  if (nup > 0 && ncp < (int)ea) std::memmove(w->adm_h[q] + 2 * (size_t)ncp, w->adm_h[q] + 2 * ea, (size_t)nup * 8);
+  if (ncp + nup > 0 &&
+      (e = hipMemcpyAsync(w->adm[q], w->adm_h[q], (size_t)(ncp + nup) * 8, hipMemcpyHostToDevice, s)) != hipSuccess)
     return e;
   const int32_t* cp = w->adm[q];
-  const int32_t* up = w->adm[q] + 2 * ea;
+  const int32_t* up = w->adm[q] + 2 * (size_t)ncp;
   if (w->dtype == WI_BF16)
     hipLaunchKernelGGL(k_wb_admit<uint16_t>, dim3(std::max(ncp, 1)), dim3(kWbThreads), 0, s, cp, ncp, up, nup,
                        static_cast<uint16_t*>(w->pool_k), static_cast<uint16_t*>(w->pool_v), w->dir, w->ctr[q]);
@@ -327,15 +328,15 @@ hipError_t launch_wb_resolve(const DecodeArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // the counters and the log go back on the copy stream while the attention runs: as many
-  // entries as the last processed log held, with room to spare (a longer log is fetched in full
-  // when it is processed)
+  // the counters and the log (right after them) go back in one copy on the copy stream while the
+  // attention runs: as many entries as the last processed log held, with room to spare (a longer
+  // log is fetched in full when it is processed)
   const int ncopy = std::min(w->log_cap, 2 * w->last_count + 4096);
   w->copied[q] = ncopy;
   hipError_t e = hipEventRecord(w->resolved, s);
   if (e == hipSuccess) e = hipStreamWaitEvent(w->copy_stream, w->resolved, 0);
-  if (e == hipSuccess) e = hipMemcpyAsync(w->ctr_h[q], w->ctr[q], 16, hipMemcpyDeviceToHost, w->copy_stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(w->log_h[q], w->log[q], (size_t)ncopy * 8, hipMemcpyDeviceToHost, w->copy_stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(w->ctr_h[q], w->ctr[q], 16 + (size_t)ncopy * 8, hipMemcpyDeviceToHost, w->copy_stream);
   if (e == hipSuccess) e = hipEventRecord(w->log_ready[q], w->copy_stream);
   return e;
 }
