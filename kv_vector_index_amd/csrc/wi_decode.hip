@@ -465,9 +465,10 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
 
 // For one wave (no block barriers): the k-th largest (k >= 1) of n <= 64 KR order keys get(i),
 // given that at least k of them are >= L > 0.  Returns L when fewer than k keys exceed L.
-// Otherwise the k-th largest is the e-th smallest key above L, e = #(keys > L) - k + 1: a
-// 256-bin histogram over (L, max] names its bin, and the bin's keys are ranked directly.  The
-// keys are read once, KR per lane, and kept in registers.  Returns 0 when n > 64 KR or when that
+// Otherwise the k-th largest is the e-th smallest key above L, e = #(keys > L) - k + 1: for e <= 8
+// by walking up the distinct keys above L (a wave minimum and a tie count each), else a 256-bin
+// histogram over (L, max] names its bin and the bin's keys are ranked directly.  The keys are
+// read once, KR per lane, and kept in registers.  Returns 0 when n > 64 KR or when that
 // bin holds more than 64 keys (the caller then searches with the whole block).  `hist` holds
 // >= 256 counters and `bl` >= 64 keys of LDS that no other wave touches meanwhile.
 template <int KR, typename Get>
@@ -488,6 +489,24 @@ __device__ uint32_t wave_kth_above(int n, int k, uint32_t L, Get get, uint32_t* 
   if (d < k) return L;
   mk = wave_umax(mk);
   const int e = d - k + 1;
+  if (e <= 8) {
+    // few keys to pass over: walk up the distinct keys above L, smallest first, counting ties
+    uint32_t v = L;
+    int left = e;
+    for (int it = 0; it < 8; ++it) {
+      uint32_t mn = 0xffffffffu;
+#pragma unroll
+      for (int r = 0; r < KR; ++r) if (kr[r] > v) mn = min(mn, kr[r]);
+      mn = ~wave_umax(~mn);
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < KR; ++r) c += kr[r] == mn ? 1 : 0;
+      c = wave_isum(c);
+      if (c >= left) return mn;
+      left -= c;
+      v = mn;
+    }
+  }
   const float lo = f32_from_order_key(L), hi = f32_from_order_key(mk);
   const float inv = hi > lo ? (float)NB / (hi - lo) : 0.f;
   auto bin_of_key = [&](uint32_t key) { return min(NB - 1, max(0, (int)((f32_from_order_key(key) - lo) * inv))); };
