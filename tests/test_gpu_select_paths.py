@@ -97,6 +97,16 @@ def test_select_threshold_above_the_bound_among_many_candidates():
     _check(idx, Qt, Q64, Hq=4, k=600, dtype="bf16")
 
 
+def test_select_threshold_within_a_few_equal_scores():
+    # 12 clusters with equal mean keys lead two heads of each group: the k-th largest is their
+    # common score a few keys above the summaries' bound (found by walking up the distinct keys),
+    # and the ties are broken by id
+    idx, Qt, Q64 = _case(C=1024, tokens_per_cluster=3, Hq=8, Hkv=2, dtype="bf16", seed=16, crowd=12,
+                         crowd_heads=2, crowd_noise=0.0)
+    for k in (5, 10, 14):
+        _check(idx, Qt, Q64, Hq=8, k=k, dtype="bf16")
+
+
 def test_select_threshold_among_many_equal_scores():
     # 200 clusters with equal mean keys, the k-th largest among them: more than a wave's worth of
     # candidates share its histogram bin (the whole block searches), and the ties are broken by id
