@@ -277,11 +277,11 @@ wi_status wi_decode_bounded(const wi_decode_params *p, const wi_index_view *idx,
  * and two events) is allocated by wi_wavebuf_create and freed by wi_wavebuf_destroy.  One
  * wave buffer serves one index (same B, Hkv, Nc and dtype) and one stream at a time; its calls
  * must not overlap and cannot be captured in a graph (the host acts between them).  The pool
- * holds at most 2^29 rows.  After any error from wi_decode_wavebuf, destroy the wave buffer
- * (its host state may have advanced past the device's).  Errors: WI_ERR_INVALID_ARG for null or
- * negative arguments or a
- * wave buffer of another index, WI_ERR_UNSUPPORTED as wi_decode and for a pool beyond 2^29
- * rows, WI_ERR_WORKSPACE for too little device memory. */
+ * (cache_blocks + 2 * exec_blocks blocks of 16 rows) holds at most 2^29 rows.  After any error
+ * from wi_decode_wavebuf, destroy the wave buffer (its host state may have advanced past the
+ * device's).  Errors: WI_ERR_INVALID_ARG for null or negative arguments or a wave buffer of
+ * another index, WI_ERR_UNSUPPORTED as wi_decode and for a pool beyond 2^29 rows,
+ * WI_ERR_WORKSPACE for too little device memory. */
 typedef struct wi_wavebuf wi_wavebuf;
 
 wi_status wi_wavebuf_device_bytes(const wi_decode_params *p, int32_t cache_blocks,

@@ -465,8 +465,10 @@ static wi_status wavebuf_check(const wi_decode_params* p, int32_t cache_blocks, 
   if (p->dtype != WI_F32 && p->dtype != WI_BF16) return fail(WI_ERR_INVALID_ARG, "bad dtype %d", p->dtype);
   if (p->Nc < 0 || cache_blocks < 0 || exec_blocks < 0)
     return fail(WI_ERR_INVALID_ARG, "negative Nc, cache_blocks or exec_blocks");
-  if (((int64_t)cache_blocks + exec_blocks) * wi::kWbBlock > wi::kWbMaxPoolRows)
-    return fail(WI_ERR_UNSUPPORTED, "a wave-buffer pool holds at most 2^29 rows");
+  // the pool holds the cache and two execution-buffer regions (one per call parity); the
+  // attention kernel addresses its rows with 29 bits
+  if (((int64_t)cache_blocks + 2 * (int64_t)exec_blocks) * wi::kWbBlock > wi::kWbMaxPoolRows)
+    return fail(WI_ERR_UNSUPPORTED, "a wave-buffer pool (cache + 2 x execution buffer) holds at most 2^29 rows");
   if ((int64_t)p->B * p->Hkv * wi::ceil_div(std::max(p->Nc, 1), wi::kWbBlock) >= kMaxRows)
     return fail(WI_ERR_UNSUPPORTED, "too many blocks");
   return WI_OK;

@@ -33,10 +33,6 @@
 
 namespace wi {
 
-#ifdef WI_TRACE
-__device__ unsigned long long g_trace[64][8192];
-#endif
-
 constexpr int kScoreThreads = 256;
 
 // ============================================================================ k_score_est
@@ -48,7 +44,6 @@ template <typename T, int G> struct ScoreWaves { static constexpr int v = (sizeo
 
 template <typename T, int G>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(ScoreWaves<T, G>::v))) void k_score_est(DecodeArgs a) {
-  WI_TP(30);
   __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
   __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
   __shared__ float sh_n[kScoreThreads];     // cluster sizes (entries >= nrows are 0)
@@ -121,7 +116,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)min(lr, G - 1) * kD + 32 * s + 8 * lg);
     load_sv();
     __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
-    WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -155,7 +149,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     }
     load_sv();
     __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
-    WI_TP(31);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float mb[32];
@@ -177,7 +170,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   }
   sh_n[tid] = tid < nrows ? (float)n_raw : 0.f;
   __syncthreads();
-  WI_TP(32);
 
   const size_t slot = (size_t)bg * a.est_tiles_g + tile;
   if (w == 0) {
@@ -230,7 +222,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       a.tile_top_id[ti] = best_id;
     }
   }
-  WI_TP(33);
   __syncthreads();
   float acc[G][8];
 #pragma unroll
@@ -301,7 +292,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     a.est_md[(slot * G + tid) * 2] = sh_m[tid];
     a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
   }
-  WI_TP(34);
 }
 
 // ============================================================================ k_select
@@ -392,7 +382,6 @@ __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, floa
   if (lane == 0) { fred[2 * wv] = mx; fred[2 * wv + 1] = mn; }
   if (tid == 0) sh_i[4] = 0;                       // key counter of kth_largest_key's small bin
   __syncthreads();
-  WI_TP(12);
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) { mx = fmaxf(mx, fred[2 * i]); mn = fminf(mn, fred[2 * i + 1]); }
   KthBin r;
@@ -405,14 +394,12 @@ __device__ KthBin kth_bin(int n, int k, Get get, uint32_t* hist, int* iscr, floa
     atomicAdd(&hist[min(kBins - 1, max(0, (int)((s - r.mn) * r.inv)))], 1u);
   }
   __syncthreads();
-  WI_TP(13);
   // threshold bin: thread t owns bins kBins-1-BPT*t .. (descending)
   constexpr int BPT = (kBins + NT - 1) / NT;
   int v = 0;
   for (int j = 0; j < BPT; ++j) { const int bin = kBins - 1 - BPT * tid - j; if (bin >= 0) v += (int)hist[bin]; }
   int tot;
   int run = block_exclusive_scan<NT>(v, iscr, &tot);
-  WI_TP(14);
   if (run < k && k <= run + v) {
     for (int j = 0; j < BPT; ++j) {
       const int bin = kBins - 1 - BPT * tid - j;
@@ -439,7 +426,6 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
                                     float* fred, int* sh_i) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const KthBin kb = kth_bin<NT>(n, k, get, hist, iscr, fred, sh_i);
-  WI_TP(15);
   if (kb.bin < 0) return 0u;
   const int rem = k - kb.above;
   const int nb = (int)hist[kb.bin];
@@ -449,7 +435,6 @@ __device__ uint32_t kth_largest_key(int n, int k, Get get, uint32_t* hist, uint3
       if (key != 0u && bin_of(kb, key) == kb.bin) bl[atomicAdd(&sh_i[4], 1)] = key;
     }
     __syncthreads();
-    WI_TP(16);
     if (wv == 0) {
       const uint32_t key = lane < nb ? bl[lane] : 0u;
       int gt = 0, ge = 0;
@@ -604,7 +589,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   __shared__ int band_lds[kSmallBand];
   __shared__ double gdd[3 * kMaxGroup];              // gated decode: <q, q'>, |q|^2, |q'|^2 per head
   __shared__ int sh_i[8];
-  WI_TP(0);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
@@ -673,7 +657,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     ne = (int)r0; mxn = r1; qv = sqrtf(r2);
     __syncthreads();
   }
-  WI_TP(3);
   const int n_ne = ne;
   const int k_eff = min(a.top_k, n_ne);
   // gated decode: the KV group keeps its heads' previous zones when every one of its query heads
@@ -803,7 +786,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
     if (tid == 0) { sh_i[2] = 0; sh_i[5] = 0; sh_i[7] = 0; }
     __syncthreads();
-    WI_TP(4);
     // ---- candidates: the non-empty clusters scoring >= L - 2 delta (appends wave-aggregated)
     auto append = [&](bool take, uint32_t key, int id) {
       const uint64_t m = __ballot(take);
@@ -854,7 +836,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     const int n_c = sh_i[2];
     const bool listed = n_c <= kCandCap;
     fast_pub = listed;
-    WI_TP(5);
     // ---- t = k_eff-th largest score.  The candidates hold every cluster above L and at least
     // k_eff of them score >= L, so t = L when fewer than k_eff candidates score above L; always so
     // when no tile was scanned in full (every cluster above L is then one of the fewer than k_eff
@@ -878,9 +859,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       thr = (uint32_t)sh_i[3];
       t_is_L = thr == L;
     }
-    WI_TV(50, n_c);
-    WI_TV(51, sh_i[5]);
-    WI_TV(52, t_is_L ? 1 : (listed && thr != 0u) ? 2 : listed ? 3 : 4);
     if (t_is_L) {
       thr = L;
     } else if (listed && thr != 0u) {
@@ -891,7 +869,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       int rr;
       thr = block_radix_select<NT, uint32_t>(C, k_eff, [&](int c) { return keys[c]; }, hist, iscr, &rr);
     }
-    WI_TP(6);
     // first rows and sizes of the candidates, fetched now (in flight while the band is classified
     // and re-scored) and used when publishing
     if (listed) {
@@ -922,8 +899,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     const int n_in = block_isum<NT>(nin, iscr);          // includes a barrier
     const int need = k_eff - n_in;
     int n_band = sh_i[7];
-    WI_TV(53, n_band);
-    WI_TV(54, need);
     int32_t* band = band_lds;
     if (n_band > kSmallBand) {
       const int perw = (W32 + NT - 1) / NT;
@@ -938,7 +913,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
       __syncthreads();
     }
-    WI_TP(7);
     // (a band listed in LDS is read through band_lds itself: through the generic pointer the
     // reads would be flat loads, which wait for every global load in flight)
     if (need >= n_band) {
@@ -1004,7 +978,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
   }
   __syncthreads();
-  WI_TP(8);
 
   int k_zone = reuse ? n_reused_ne : k_eff;
   if (EXT && a.bounded) {
@@ -1033,7 +1006,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
     }
     __syncthreads();
-    WI_TP(17);
     // the list's terms: every load of an entry issued before the first is used
     for (int i0 = 0; i0 < k_eff; i0 += 2 * NT) {
       int c[2];
@@ -1076,7 +1048,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
     }
     const float e_out = block_sum<NT>(so, fred);       // includes barriers: the list is visible
-    WI_TP(18);
     float le = 0.f, ll = 0.f;
     for (int i = tid; i < k_eff; i += NT) { le += ze[i]; ll += zl[i]; }
     const float b_err = e_out + block_sum<NT>(le, fred);
@@ -1101,7 +1072,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       if (e_out + after <= lim) kb = min(kb, rank + 1);
     }
     k_zone = (int)-block_max<NT>(-(float)kb, fred);
-    WI_TP(19);
     if (k_zone < k_eff) {
       // the canonical top k_zone of the list: in above t + 2 delta, out below t - 2 delta, the
       // band between them ranked by (-canonical score, id); t = the k_zone-th fp32 score
@@ -1140,7 +1110,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
       __syncthreads();
     }
-    WI_TP(24);
     // sums over the estimated clusters (outside the zone) for the bound after attention: the
     // clusters outside the list, plus the list entries the zone left out
     float sa = 0.f, sv = 0.f, sl = 0.f;
@@ -1157,7 +1126,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       bd[0] = b_mstar; bd[1] = sa; bd[2] = sv; bd[3] = sl;
       if (a.k_used) a.k_used[bh] = k_zone;
     }
-    WI_TP(25);
     fast_pub = false;
   }
 
@@ -1200,7 +1168,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     }
     tot = min(tot, K);
     __syncthreads();
-    WI_TP(10);
     const int32_t* off = a.offsets + (size_t)bg * (C + 1);
     int32_t* out = a.sel_ids ? a.sel_ids + (size_t)bh * K : nullptr;
     const size_t lb = (size_t)bh * K, pb = (size_t)bh * (K + 1);
@@ -1237,7 +1204,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
       int csum;
       int t = t_run + block_exclusive_scan<NT>(ssum, iscr, &csum);
-      WI_TP(11);
       if (tot <= chunk) ntok = (int64_t)a.NS + csum;
       // token workgroup x covers [floor(x ntok / S), floor((x+1) ntok / S)); its first retrieved
       // token is u_x = max(that start, NS), and its entry the last one whose first token is
@@ -1265,7 +1231,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       }
       t_run += csum;
     }
-    WI_TP(26);
     for (int i = tot + tid; i < K; i += NT) {
       if (out) out[i] = -1;
       if (lists) { a.hl_cid[lb + i] = 0; a.hl_row[lb + i] = 0; a.hl_key[lb + i] = 0u; a.hl_pre[pb + i] = (int)ntok; }
@@ -1275,7 +1240,6 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
     if (tot == 0) for (int x = tid; x < S; x += NT) bounds[x] = 0;
   }
   if (tid == 0) a.all_sel[bh] = k_zone == n_ne ? 1 : 0;
-  WI_TP(9);
 }
 
 // ============================================================================ k_attend
@@ -1502,7 +1466,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ int srow[kAttStage];              // first k_perm row of list entries e_cur + x
   __shared__ float sh_p[4][16];
   __shared__ int sh_next;
-  WI_TP(20);
   const int items = a.att_items, S = a.att_split, K = a.top_k;
   const int bh = blockIdx.x / items, s = blockIdx.x - bh * items;
   const int b = bh / a.Hq, h = bh - b * a.Hq, bg = b * a.Hkv + h / a.G;
@@ -1527,7 +1490,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
     const int32_t* wloc = PG ? a.wb_loc + (size_t)bg * a.wb_nblk : nullptr;
     const T* ks = static_cast<const T*>(a.k_steady) + (size_t)bg * NS * kD;
     const T* vs = static_cast<const T*>(a.v_steady) + (size_t)bg * NS * kD;
-    WI_TP(21);
     for (int z0 = t0; z0 < t1; z0 += kAttStage) {
       const int z1 = min(t1, z0 + kAttStage);
       if (z0 > t0) __syncthreads();            // the previous chunk's map is no longer read
@@ -1624,9 +1586,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
       st.template add<R>(l, wd, vr);
     }
   }
-  WI_TP(22);
   write_partial<1>(st, (size_t)bh * items + s, a.att_md, a.att_num, sh_m, sh_den, sh_num);
-  WI_TP(23);
 }
 
 // ============================================================================ k_merge
@@ -1644,7 +1604,6 @@ constexpr int kMergeU = 12;
 template <int NT>
 __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
   constexpr int kMergeMdU = NT >= 1024 ? 1 : 2;   // md pairs per thread loaded in the first round
-  WI_TP(40);
   __shared__ float sh_f[kMergeLds];
   __shared__ float sh_red[32];
   __shared__ float4 sh_acc[NT / 32][32];
@@ -1773,7 +1732,6 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
       a.err_bound[bh] = e;
     }
   }
-  WI_TP(41);
 }
 
 // ============================================================================ launcher
@@ -1883,8 +1841,3 @@ hipError_t launch_refresh(const wi_decode_params& p, const DecodeArgs& a, hipStr
 
 }  // namespace wi
 
-#ifdef WI_TRACE
-extern "C" int wi_trace_read(void* dst, size_t bytes) {
-  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(wi::g_trace), bytes, 0, hipMemcpyDeviceToHost);
-}
-#endif

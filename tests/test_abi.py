@@ -252,10 +252,15 @@ def test_bound_data_and_bounded_decode_reject_bad_arguments():
 def test_wavebuf_rejects_bad_sizes_and_small_memory():
     p = _dparams()
     for cache, exe, status in ((-1, 8, wi.WI_ERR_INVALID_ARG), (8, -1, wi.WI_ERR_INVALID_ARG),
-                               (1 << 25, 1, wi.WI_ERR_UNSUPPORTED)):
+                               (1 << 25, 1, wi.WI_ERR_UNSUPPORTED),
+                               # cache + both execution-buffer regions past 2^29 rows, although
+                               # cache + one region is within it
+                               ((1 << 24), (1 << 23) + 1, wi.WI_ERR_UNSUPPORTED)):
         with pytest.raises(wi.WaveIndexError) as e:
             wi.wi_wavebuf_device_bytes(p, cache, exe)
         assert e.value.status == status
+    # exactly 2^29 rows: cache 2^24 blocks + 2 x 2^23 blocks of 16 rows
+    assert wi.wi_wavebuf_device_bytes(p, 1 << 24, 1 << 23) > 0
     need = wi.wi_wavebuf_device_bytes(p, 1000, 100)
     # pool blocks of 16 rows of K and V, directory, claims and locations per block, the log
     assert need >= 1100 * 16 * 128 * 2 * 2 + 3 * 8 * -(-131004 // 16) * 4
