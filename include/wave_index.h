@@ -166,6 +166,17 @@ wi_status wi_decode(const wi_decode_params *p, const wi_index_view *idx, const v
                     float *out, float *lse, int32_t *sel_ids, void *workspace, size_t ws_bytes,
                     void *stream);
 
+/* wi_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is a static array of the
+ * library's own, 64 MiB on every device the library runs on (held until the process ends), so
+ * the call takes no workspace argument and allocates nothing.  Every other argument, the result
+ * and the errors are those of wi_decode; also WI_ERR_UNSUPPORTED when wi_decode_workspace_bytes
+ * exceeds 64 MiB (e.g. batch 16 at 128K tokens).  All calls on one device share its array:
+ * calls that overlap on one device (on different streams, or from different threads without
+ * ordering) race and give wrong results. */
+wi_status wi_decode_noalloc(const wi_decode_params *p, const wi_index_view *idx, const void *q,
+                            float *out, float *lse, int32_t *sel_ids, void *stream);
+
 /* One decode step that attends over the previous step's zones where the queries barely moved
  * (FreeKV Spanish summary, section A items 1-2: speculative retrieval, and a fine-grained
  * correction that selects again for the KV heads whose consecutive queries have a cosine below a

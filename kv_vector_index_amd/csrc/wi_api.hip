@@ -163,6 +163,35 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
 
 }  // namespace wi
 
+// ---- allocation-free decode: the workspace is this file's static device array.  Host code never
+// names the array itself (its host-side name is only a registration handle): the device address
+// comes from hipGetSymbolAddress, once per device with that device current, and is kept per device.
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+
+wi_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(WI_ERR_UNSUPPORTED, "device %d: the static workspace serves devices 0..%d", dev, kScratchMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(WI_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return WI_OK;
+}
+}  // namespace
+
 extern "C" {
 
 wi_status wi_index_shapes_for(const wi_build_params* p, wi_index_shapes* out) {
@@ -386,6 +415,19 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
 wi_status wi_decode(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
                     float* lse, int32_t* sel_ids, void* workspace, size_t ws_bytes, void* stream) {
   return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, nullptr);
+}
+
+wi_status wi_decode_noalloc(const wi_decode_params* p, const wi_index_view* idx, const void* q, float* out,
+                            float* lse, int32_t* sel_ids, void* stream) {
+  size_t need = 0;
+  wi_status s = wi_decode_workspace_bytes(p, &need);
+  if (s != WI_OK) return s;
+  if (need > kScratchBytes)
+    return fail(WI_ERR_UNSUPPORTED, "this decode needs %zu workspace bytes; the static workspace holds %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != WI_OK) return s;
+  return decode_common(p, idx, q, out, lse, sel_ids, ws, kScratchBytes, stream, nullptr);
 }
 
 wi_status wi_decode_gated(const wi_decode_params* p, const wi_index_view* idx, const void* q,

@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libwave_index.so")
 WI_OK, WI_ERR_INVALID_ARG, WI_ERR_UNSUPPORTED, WI_ERR_WORKSPACE, WI_ERR_HIP = 0, -1, -2, -3, -4
 WI_F32, WI_BF16 = 0, 1
 EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
-            "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated", "wi_select_refresh",
-            "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes", "wi_wavebuf_create",
+            "wi_decode_workspace_bytes", "wi_decode", "wi_decode_noalloc", "wi_decode_gated",
+            "wi_select_refresh", "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes", "wi_wavebuf_create",
             "wi_decode_wavebuf", "wi_wavebuf_stats", "wi_wavebuf_destroy",
             "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.wi_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
         L.wi_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
                                 vp, vp, sz, vp]
+        L.wi_decode_noalloc.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
+                                        vp, vp]
         L.wi_decode_gated.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp,
                                       ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         L.wi_select_refresh.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, sz,
@@ -105,7 +107,7 @@ def lib() -> ctypes.CDLL:
         L.wi_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
-                     "wi_decode_workspace_bytes", "wi_decode", "wi_decode_gated",
+                     "wi_decode_workspace_bytes", "wi_decode", "wi_decode_noalloc", "wi_decode_gated",
                      "wi_select_refresh", "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes",
                      "wi_wavebuf_create", "wi_decode_wavebuf", "wi_wavebuf_stats", "wi_wavebuf_destroy"):
             getattr(L, name).restype = ctypes.c_int
@@ -158,6 +160,12 @@ def wi_decode(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_pt
               sel_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_decode(ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr,
                                   sel_ptr, ws_ptr, ws_bytes, stream))
+
+
+def wi_decode_noalloc(p: DecodeParams, view: IndexView, q_ptr: int, out_ptr: int, lse_ptr: Optional[int],
+                      sel_ptr: Optional[int], stream: int) -> int:
+    return _check(lib().wi_decode_noalloc(ctypes.byref(p), ctypes.byref(view), q_ptr, out_ptr, lse_ptr,
+                                          sel_ptr, stream))
 
 
 def wi_decode_gated(p: DecodeParams, view: IndexView, q_ptr: int, q_prev_ptr: int, sel_prev_ptr: int,

@@ -296,3 +296,16 @@ def test_profile_hook_modes():
     stages = wi.wi_profile_read()                         # nothing recorded yet
     assert all(v == (0.0, 0) for v in stages.values())
     assert L.wi_profile_enable(0) == wi.WI_OK
+
+
+def test_decode_noalloc_rejects_workspaces_beyond_its_static_array():
+    # batch 16 at 128K needs ~86 MiB of workspace, more than the 64 MiB static array; the call is
+    # rejected on the host, before the device is looked up
+    p = _dparams(B=16)
+    assert wi.wi_decode_workspace_bytes(p) > 64 << 20
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode_noalloc(p, _view(), FAKE, FAKE, None, None, 0)
+    assert e.value.status == wi.WI_ERR_UNSUPPORTED
+    with pytest.raises(wi.WaveIndexError) as e:
+        wi.wi_decode_noalloc(_dparams(top_k=-1), _view(), FAKE, FAKE, None, None, 0)
+    assert e.value.status == wi.WI_ERR_INVALID_ARG
