@@ -20,8 +20,11 @@ With --gated TAU a step is one wi_decode_gated call over a drifting query stream
 queries and zones are the next step's q_prev and sel_prev), and with --refresh also the
 wi_select_refresh call that computes the postponed selection (FreeKV's scheme).
 
-Prints one JSON line (rank 0) with the throughput, the roofline position of the dominant kernel
-(per-kernel HIP-event timing over a second, eager pass), and the CPU oracle timed on the host.
+Prints one JSON line (rank 0) with the throughput, the roofline position of the kernel that moves
+the most HBM bytes (per-kernel HIP-event timing over a second, eager pass in which every kernel is
+launched 20 times back to back, each repeat reading another copy of the index so that it misses
+the Infinity Cache as the graph-replayed steps do), and the CPU oracle timed on the host's cores
+on the same inputs (whole decode steps; the default workload only).
 """
 import argparse
 import json
@@ -40,6 +43,9 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_{}.json")   # per workload
 PROF_REPS = 20                  # launches of each decode kernel between its timing events
 KERNEL_NAMES = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
+STREAMING = ("score", "attend")  # the decode kernels that stream HBM; select and merge are latency
+CPU_MAX_WORKERS = 16            # the host share of one GPU
+_CPU = {}                       # host inputs of the CPU baseline, inherited by its forked workers
 
 
 def log(*a):
@@ -47,12 +53,15 @@ def log(*a):
 
 
 def algorithmic_bytes(w, idx_offsets_np, sel_np):
-    """Bytes each decode kernel must move per step (every byte counted once):
-      score  : centroids, value sums and sizes of every cluster, queries
+    """Bytes each decode kernel must move per step, every byte counted once (the per-step formula
+    of the measurement plan, split by the kernel that moves it):
+      score  : centroids and value sums of every cluster, offsets (C + 1 per KV head), queries
       select : the retrieved ids it writes
-      attend : steady rows, the union of the rows retrieved by a KV group's query heads, and the
-               value sum of each retrieved cluster (for its estimation term)
-      merge  : outputs and lse"""
+      attend : steady rows and the union of the rows retrieved by a KV group's query heads (K + V)
+      merge  : outputs and lse
+    Returns (per-kernel bytes, union rows, correction bytes): the last are what the attention
+    kernel's correction workgroups re-read (a value sum and a score key per retrieved cluster and
+    head), an implementation cost reported apart."""
     import numpy as np
     e = 2 if w.dtype == "bf16" else 4
     d = w.d
@@ -61,6 +70,7 @@ def algorithmic_bytes(w, idx_offsets_np, sel_np):
     NS = min(w.N, w.sink + w.window)
     per = {"score": 0, "select": 0, "attend": 0, "merge": 0}
     union_rows = 0
+    corr = 0
     for b in range(w.B):
         for g in range(w.Hkv):
             off = idx_offsets_np[b, g]
@@ -68,63 +78,132 @@ def algorithmic_bytes(w, idx_offsets_np, sel_np):
             ids = ids[ids >= 0]
             u = int((off[ids + 1] - off[ids]).sum())
             union_rows += u
-            per["score"] += C * (2 * d * e + 4)
-            per["attend"] += NS * 2 * d * e + u * 2 * d * e + ids.size * (d * e + 4)
+            per["score"] += C * 2 * d * e + 4 * (C + 1)
+            per["attend"] += NS * 2 * d * e + u * 2 * d * e
+            corr += int((sel_np[b, g * G:(g + 1) * G] >= 0).sum()) * (d * e + 4)
     per["score"] += w.B * w.Hq * d * e
     per["select"] += w.B * w.Hq * w.top_k * 4
     per["merge"] += w.B * w.Hq * (4 * d + 4)
-    return per, union_rows
+    return per, union_rows, corr
 
 
-def cpu_baseline(w, seed, budget_s):
-    """The oracle's decode on the host, on a bounded sample of the workload: the query heads of one
-    KV group of sequence 0 (the seeded generator draws that group exactly as in the full
-    workload), on an oracle-finalized index of that group, repeated within the time budget and
-    scaled to whole steps (B x Hq heads)."""
+def _cpu_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_MAX_WORKERS))
+
+
+def host_inputs(w, seed):
+    """The workload's inputs drawn on the host (numpy float64, cast to the storage dtype): the
+    torch tensors the GPU leg uploads, and the exact float64 copies and blob labels the oracle
+    reads, kept for the forked CPU workers."""
+    from kv_vector_index_amd import synth
+    K, V, Q, labels = synth.make_instance(w, seed, with_labels=True)
+    Kt, Vt, Qt = (synth.cast(x, w.dtype) for x in (K, V, Q))
+    del K, V, Q
+    _CPU.update(K64=synth.as_float64(Kt), V64=synth.as_float64(Vt), Q64=synth.as_float64(Qt),
+                labels=labels, w=w)
+    return Kt, Vt, Qt
+
+
+def _cpu_index(g):
+    """The oracle's index of KV group g of sequence 0, finalized from the generator's blob labels
+    (folded into the segments' cluster ids): a clustering of the right shape without the oracle's
+    k-means, whose cost is timed on its own."""
     import numpy as np
+
+    import oracle
+    w = _CPU["w"]
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    ci = np.arange(hi - lo)
+    lab = (ci // w.seg_len) * w.clusters_per_seg + _CPU["labels"][0:1, g:g + 1, lo:hi] % w.clusters_per_seg
+    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
+    return oracle.finalize_index(_CPU["K64"][0:1, g:g + 1], _CPU["V64"][0:1, g:g + 1], lab, w.sink, w.window,
+                                 C, w.dtype)
+
+
+def _cpu_decode_worker(task):
+    """One worker: the oracle's decode of the listed query heads (all of KV group g), repeated until
+    `budget` seconds have passed; returns (rounds, seconds)."""
+    g, heads, budget = task
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from kv_vector_index_amd import synth
-
-    G = w.Hq // w.Hkv
-    ws = w.replace(B=1, Hkv=1, Hq=G, steps=1)
-    K, V, Q, labels = synth.make_instance(ws, seed, with_labels=True)
-    K = synth.as_float64(synth.cast(K, w.dtype))
-    V = synth.as_float64(synth.cast(V, w.dtype))
-    Q = synth.as_float64(synth.cast(Q, w.dtype))
-    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
-    ci = np.arange(hi - lo)
-    lab = (ci // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
-    C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
-    idx = oracle.finalize_index(K, V, lab, w.sink, w.window, C, w.dtype)
+    w = _CPU["w"]
+    idx = _cpu_index(g)
     scale = 1 / math.sqrt(w.d)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        heads = 0
+        rounds = 0
         while True:
-            for h in range(G):
-                oracle.decode_head(Q[0, h], idx, 0, 0, w.top_k, scale)
-                heads += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
-        steps = heads / (w.B * w.Hq)
-        # build: one segment of spherical k-means, scaled to every segment of every (b, g)
-        segs = oracle.segment_bounds(hi - lo, w.seg_len)
-        t1 = time.perf_counter()
-        a0, a1 = segs[0]
-        oracle.spherical_kmeans_segment(K[0, 0, lo + a0:lo + a1], w.clusters_per_seg, w.iters,
-                                        w.dtype, oracle.segment_state(1, 0, 0, 0))
-        seg_s = time.perf_counter() - t1
+            for h in heads:
+                oracle.decode_head(_CPU["Q64"][0, h], idx, 0, 0, w.top_k, scale)
+            rounds += 1
+            dt = time.perf_counter() - t0
+            if dt > budget:
+                return rounds, dt
+
+
+def _cpu_build_worker(task):
+    """One worker: the oracle's spherical k-means of one segment of KV group g; returns seconds."""
+    g, s = task
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    w = _CPU["w"]
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    a0, a1 = oracle.segment_bounds(hi - lo, w.seg_len)[s]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.spherical_kmeans_segment(_CPU["K64"][0, g, lo + a0:lo + a1], w.clusters_per_seg, w.iters,
+                                        w.dtype, oracle.segment_state(1, 0, g, s))
+        return time.perf_counter() - t0
+
+
+def cpu_pool():
+    """A pool of forked workers, made before the GPU is touched (the workers inherit the host
+    inputs and never use the GPU)."""
+    import multiprocessing as mp
+    return mp.get_context("fork").Pool(_cpu_cores())
+
+
+def cpu_baseline(pool, w, budget_s):
+    """The oracle's decode of whole steps (every query head of the batch) on the inputs the GPU leg
+    decodes, spread over the pool's workers (one BLAS thread each): steps/s of the slowest worker,
+    which a step has to wait for.  Also the oracle's k-means on one segment per worker, scaled to
+    the whole index build (an estimate)."""
+    import oracle
+    cores = pool._processes
+    G = w.Hq // w.Hkv
+    # query heads dealt to the workers by KV group: each worker decodes heads of one group
+    per_group = max(1, cores // w.Hkv)
+    tasks = []
+    for g in range(w.Hkv):
+        heads = list(range(g * G, (g + 1) * G))
+        parts = [heads[i::per_group] for i in range(per_group)]
+        tasks += [(g, p, budget_s) for p in parts if p]
+    res = pool.map(_cpu_decode_worker, tasks, chunksize=1)
+    used = min(cores, len(tasks))
+    waves = -(-len(tasks) // cores)          # tasks a worker runs one after the other
+    rate = min(r / t for r, t in res) / waves
+    lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
+    nseg = len(oracle.segment_bounds(hi - lo, w.seg_len))
+    btasks = [(g % w.Hkv, (g // w.Hkv) % nseg) for g in range(min(cores, w.Hkv * nseg))]
+    t0 = time.perf_counter()
+    bt = pool.map(_cpu_build_worker, btasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    segs_total = w.B * w.Hkv * nseg
     return {
-        "value": steps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
-        "sample": f"{heads} query-head decodes ({G} heads of KV group 0, sequence 0) of {w.name} on an "
-                  f"oracle-finalized index, NumPy float64, BLAS pinned to 1 thread, {dt:.1f} s; "
-                  f"value = heads/s / ({w.B} x {w.Hq} heads per step)",
-        "build_s_estimate": seg_s * len(segs) * w.B * w.Hkv,
-        "build_sample": f"one {a1 - a0}-token segment x {w.iters} iterations in {seg_s:.1f} s, "
-                        f"scaled to {len(segs) * w.B * w.Hkv} segments",
+        "value": rate, "unit": "steps/s", "cores": used, "kind": "oracle",
+        "sample": f"whole decode steps ({w.B} x {w.Hq} query heads) of {w.name} on the inputs the GPU leg "
+                  f"decodes, NumPy float64, {len(tasks)} workers over {used} cores (one BLAS thread each), "
+                  f"each repeating its heads for {budget_s:.0f} s; value = the slowest worker's rounds/s; "
+                  f"the oracle index is finalized from the generator's blob labels",
+        "build_s_estimate": wall * -(-segs_total // len(btasks)),
+        "build_sample": f"{len(btasks)} segments of spherical k-means ({w.iters} iterations) in parallel in "
+                        f"{wall:.1f} s, scaled to {segs_total} segments (an estimate)",
         "cpu_model": _cpu_model(),
     }
 
@@ -218,7 +297,8 @@ def main():
     ap.add_argument("--workload", default="gqa_128k_bf16")
     ap.add_argument("--instances", type=int, default=0, help="index copies cycled through (0: by footprint)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds each CPU worker repeats its query heads for")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--gated", type=float, default=None, metavar="TAU",
@@ -248,11 +328,25 @@ def main():
     from kv_vector_index_amd import wave_index as wi
 
     w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
     if args.build_only or w.top_k <= 0:
-        return bench_build(w, args, dev)
-    log(f"[bench] workload {w.name}: generating inputs on the device")
-    Kt, Vt, Qt = synth.make_instance_device(w, args.seed, dev)
+        return bench_build(w, args, torch.device("cuda:0"))
+    # The CPU baseline decodes whole steps on the very inputs the GPU leg decodes: for a batch-1
+    # workload of at most 128K tokens they are drawn on the host (before the GPU is touched, so
+    # that the oracle's worker processes can be forked with them); larger workloads draw on the
+    # device and carry no CPU baseline.
+    with_cpu = not args.no_cpu_baseline and w.B == 1 and w.N <= 131072 and args.wavebuf is None
+    pool = None
+    if with_cpu:
+        log(f"[bench] workload {w.name}: generating inputs on the host")
+        Kh, Vh, Qh = host_inputs(w, args.seed)
+        pool = cpu_pool()
+    dev = torch.device("cuda:0")
+    if with_cpu:
+        Kt, Vt, Qt = (x.to(dev) for x in (Kh, Vh, Qh))
+        del Kh, Vh, Qh
+    else:
+        log(f"[bench] workload {w.name}: generating inputs on the device")
+        Kt, Vt, Qt = synth.make_instance_device(w, args.seed, dev)
 
     # ---- index build (timed on its own, with per-kernel events)
     log("[bench] building the index")
@@ -276,7 +370,12 @@ def main():
 
     # ---- instances at distinct HBM addresses (so that a step's bytes miss the 256 MB MALL) and
     # the queries of the steps (a drifting sequence for multi-step workloads)
-    n_inst = args.instances if args.instances else (8 if w.B * w.Hkv * idx.C * w.d * 4 < (64 << 20) else 2 if w.B == 1 else 1)
+    # enough copies that the bytes one kernel reads from the other copies between two reads of the
+    # same copy exceed the 256 MB Infinity Cache (also in the profiling pass, whose repeats of one
+    # kernel rotate through the copies)
+    e_b = 2 if w.dtype == "bf16" else 4
+    score_bytes = w.B * w.Hkv * idx.C * w.d * 2 * e_b
+    n_inst = args.instances if args.instances else max(1 if w.B > 1 else 2, min(16, -(-(512 << 20) // max(score_bytes, 1))))
     if args.wavebuf is not None:
         args.no_graph = True          # the host manages the cache between steps
         n_inst = 1                    # one index, one cache
@@ -373,7 +472,7 @@ def main():
                              "top_k_cap": w.top_k, "err_bound_mean": float(eb.mean()),
                              "err_bound_max": float(eb.max())})
     off_np = idx.offsets.cpu().numpy()
-    per_bytes, union_rows = algorithmic_bytes(w, off_np, sel_np)
+    per_bytes, union_rows, corr_bytes = algorithmic_bytes(w, off_np, sel_np)
     step_bytes = sum(per_bytes.values())
 
     if wavebuf_info is not None:
@@ -429,6 +528,7 @@ def main():
     prof_steps = min(K_steps, 20)
     a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    wi.wi_profile_rotate([] if args.wavebuf is not None else views)   # repeats read other copies
     wi.wi_profile_enable(True, PROF_REPS)
     for _ in range(30):
         a = a @ a
@@ -438,18 +538,20 @@ def main():
     torch.cuda.synchronize()
     stages = wi.wi_profile_read()
     wi.wi_profile_enable(False)
+    wi.wi_profile_rotate([])
     del a
     avg_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()
               if k in ("score", "select", "attend", "merge") or (k == "refresh" and v[1])}
-    dominant = max(("score", "attend"), key=lambda k: avg_ms[k] or 0.0)
-    achieved = {k: per_bytes[k] / (avg_ms[k] / 1e3) / 1e9 for k in ("score", "attend") if avg_ms[k]}
+    # the roofline kernel: the streaming kernel that moves the most algorithmic bytes
+    dominant = max(STREAMING, key=lambda k: per_bytes[k])
+    achieved = {k: per_bytes[k] / (avg_ms[k] / 1e3) / 1e9 for k in STREAMING if avg_ms[k]}
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE.format(w.name)):
         with open(TRAFFIC_FILE.format(w.name)) as f:
             tr = json.load(f)
         from kv_vector_index_amd.traffic import decode_source_hash
-        if tr.get("kernel_source_sha256_16") == decode_source_hash():
+        if tr.get("kernel_source_sha256_16") == decode_source_hash() and tr.get("instances") == len(insts):
             traffic = tr.get("hbm_bytes_per_launch", {}).get(dominant)
 
     result = {
@@ -482,10 +584,15 @@ def main():
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "retrieved_union_rows": union_rows,
         "kernel_avg_us": {k: (v * 1e3 if v is not None else None) for k, v in avg_ms.items()},
+        "kernel_latency_us": {k: avg_ms[k] * 1e3 for k in ("select", "merge") if avg_ms.get(k)},
         "kernel_algorithmic_bytes": per_bytes,
+        "correction_reread_bytes": corr_bytes,
         "roofline": {"kernel": KERNEL_NAMES[dominant], "bound": "hbm", "achieved": achieved[dominant],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved[dominant] / HBM_PEAK_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic, "bytes_per_launch": per_bytes[dominant],
+                     "avg_launch_us": avg_ms[dominant] * 1e3,
+                     "timing": f"HIP events around {PROF_REPS} back-to-back launches per step, each reading "
+                               f"another of {len(insts)} index copies, {prof_steps} steps"},
         "kernel_hbm_gbps": achieved,
         "build": {"ms": build_ms,
                   "stage_ms": {k: v[0] for k, v in build_stages.items() if v[1]},
@@ -506,9 +613,11 @@ def main():
     torch.cuda.synchronize()
     result["hbm_copy_gbps"] = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
     del src, dst
-    if not args.no_cpu_baseline:
+    if pool is not None:
         log("[bench] CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(pool, w, args.cpu_budget)
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
 
 

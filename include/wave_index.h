@@ -339,6 +339,15 @@ typedef enum {
  * WI_ERR_INVALID_ARG. */
 wi_status wi_profile_enable(int enable);
 
+/* (host) Profiling hook for measurement tools: while wi_profile_enable(R) with R > 1 repeats each
+ * decode kernel, repeat r reads the index through views[r mod n] instead of the call's own index
+ * (the queries, workspace and outputs stay the call's).  The views must be bit-identical copies
+ * of the index the calls decode, so that every repeat computes the same results; placed at other
+ * HBM addresses, they keep a repeat's reads from hitting in the last-level cache, as they would
+ * not in a run that decodes many sequences.  The array is copied; n = 0 clears the list.
+ * Wave-buffer calls ignore it.  Errors: WI_ERR_INVALID_ARG for n < 0, or null views with n > 0. */
+wi_status wi_profile_rotate(const wi_index_view *views, int n);
+
 /* (host) Wait for the recorded events and return, per stage, the summed kernel time in
  * milliseconds and the number of launches (repeats included) since the hook was enabled.  Both arrays hold
  * WI_NUM_STAGES entries.  Synchronises on the recorded events only. */

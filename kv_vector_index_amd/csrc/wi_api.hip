@@ -77,6 +77,16 @@ namespace wi {
 
 bool g_prof_on = false;
 int g_prof_reps = 1;
+static std::vector<wi_index_view> g_prof_views;   // rotation list of the repeats (host copies)
+
+DecodeArgs prof_args(const DecodeArgs& a, int r) {
+  if (!g_prof_on || g_prof_views.empty() || a.paged) return a;
+  const wi_index_view& v = g_prof_views[(size_t)r % g_prof_views.size()];
+  DecodeArgs x = a;
+  x.mu = v.centroids; x.sv = v.value_sums; x.offsets = v.offsets; x.sizes = v.sizes;
+  x.k_perm = v.k_perm; x.v_perm = v.v_perm; x.k_steady = v.k_steady; x.v_steady = v.v_steady;
+  return x;
+}
 
 namespace {
 struct ProfRec {
@@ -579,6 +589,13 @@ wi_status wi_profile_enable(int enable) {
   if (enable) prof_clear();
   wi::g_prof_on = enable != 0;
   wi::g_prof_reps = enable > 1 ? enable : 1;
+  return WI_OK;
+}
+
+wi_status wi_profile_rotate(const wi_index_view* views, int n) {
+  std::lock_guard<std::mutex> lk(wi::g_prof_mu);
+  if (n < 0 || (n > 0 && !views)) return fail(WI_ERR_INVALID_ARG, "rotation list: need n >= 0 and views for n > 0");
+  wi::g_prof_views.assign(views, views + n);
   return WI_OK;
 }
 

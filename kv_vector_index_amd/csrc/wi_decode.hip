@@ -1758,14 +1758,15 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
                          a.est_tiles_g + a.att_items > (kMergeThreadsMany / 32) * kMergeU;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
-  // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent)
+  // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent, and
+  // repeat r may read a copy of the index at other addresses: prof_args)
   for (int r = 0; r < prof_reps(); ++r) {
-    hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, a);
+    hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, prof_args(a, r));
   }
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_SELECT, s);
-  for (int r = 0; r < prof_reps(); ++r) launch_select<T>(a, s);
+  for (int r = 0; r < prof_reps(); ++r) launch_select<T>(prof_args(a, r), s);
   prof_end(WI_STAGE_SELECT, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.paged && (e = launch_wb_resolve(a, s)) != hipSuccess) return e;   // blocks of the zones
@@ -1774,7 +1775,7 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
     if (a.paged)
       hipLaunchKernelGGL((k_attend<T, true>), dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((k_attend<T, false>), dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, a);
+      hipLaunchKernelGGL((k_attend<T, false>), dim3((unsigned)BH * (unsigned)a.att_items), dim3(kAttThreads), 0, s, prof_args(a, r));
   }
   prof_end(WI_STAGE_ATTEND, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -122,6 +122,10 @@ hipError_t launch_bound_data(const wi_decode_params& p, const wi_index_view& idx
 extern bool g_prof_on;
 extern int g_prof_reps;   // decode kernels launched this many times back to back while profiling
 inline int prof_reps() { return g_prof_on ? g_prof_reps : 1; }
+// The arguments of repeat r of a decode kernel while profiling: with a rotation list set
+// (wi_profile_rotate), the index pointers of list entry r mod n (copies of the call's index at
+// other addresses); otherwise, and for a wave-buffer decode, the call's own arguments.
+DecodeArgs prof_args(const DecodeArgs& a, int r);
 void prof_record(int stage, bool begin, hipStream_t s);
 inline void prof_begin(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, true, s); }
 inline void prof_end(int stage, hipStream_t s) { if (g_prof_on) prof_record(stage, false, s); }

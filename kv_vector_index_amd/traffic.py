@@ -7,7 +7,7 @@ Two sub-commands:
         FETCH_SIZE / WRITE_SIZE counters;
 
     python -m kv_vector_index_amd.traffic record --fetch DIR --write DIR \\
-            --copy-fetch DIR --copy-write DIR --copy-mib 512 --out FILE
+            --copy-fetch DIR --copy-write DIR --copy-mib 512 --workload W --instances N --out FILE
         reads the counter CSVs that `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` wrote
         for a decode run and for the copy run, scales every kernel's per-dispatch KiB by the
         factor that makes the copy kernel read and write exactly its known size, and writes a
@@ -26,9 +26,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DECODE_KERNELS = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
+DECODE_SOURCES = ("wi_decode.hip", "wi_device.h", "wi_internal.h", "wi_api.hip")
+
+
 def decode_source_hash() -> str:
-    with open(os.path.join(ROOT, "kv_vector_index_amd", "csrc", "wi_decode.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) over every source the decode kernels and their launch
+    configuration are compiled from."""
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "kv_vector_index_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def per_kernel_kib(directory: str, counter: str) -> dict:
@@ -88,7 +96,8 @@ def cmd_record(args):
     f_write = nbytes / (cw[copy_name]["kib"] * 1024.0)
     df = per_kernel_kib(args.fetch, "FETCH_SIZE")
     dw = per_kernel_kib(args.write, "WRITE_SIZE")
-    out = {"kernel_source_sha256_16": decode_source_hash(),
+    out = {"kernel_source_sha256_16": decode_source_hash(), "kernel_sources": list(DECODE_SOURCES),
+           "workload": args.workload, "instances": args.instances,
            "calibration": {"kernel": copy_name, "bytes": nbytes,
                            "fetch_kib": cf[copy_name]["kib"], "write_kib": cw[copy_name]["kib"],
                            "fetch_factor": f_fetch, "write_factor": f_write},
@@ -118,6 +127,8 @@ def main(argv=None):
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     r.add_argument("--copy-mib", type=int, default=512)
+    r.add_argument("--workload", required=True, help="the bench workload the decode run measured")
+    r.add_argument("--instances", type=int, required=True, help="index copies that bench run cycled through")
     r.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     return cmd_copy(args) if args.cmd == "copy" else cmd_record(args)

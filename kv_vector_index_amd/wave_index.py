@@ -25,7 +25,7 @@ EXPORTED = ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
             "wi_decode_workspace_bytes", "wi_decode", "wi_decode_noalloc", "wi_decode_gated",
             "wi_select_refresh", "wi_bound_data", "wi_decode_bounded", "wi_wavebuf_device_bytes", "wi_wavebuf_create",
             "wi_decode_wavebuf", "wi_wavebuf_stats", "wi_wavebuf_destroy",
-            "wi_profile_enable", "wi_profile_read", "wi_status_string", "wi_last_error")
+            "wi_profile_enable", "wi_profile_rotate", "wi_profile_read", "wi_status_string", "wi_last_error")
 STAGES = ("score", "select", "attend", "merge", "prep", "init", "assign", "rescore", "csr", "update",
           "final", "refresh")
 
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.wi_status_string.argtypes = [ctypes.c_int]
         L.wi_profile_enable.argtypes = [ctypes.c_int]
         L.wi_profile_enable.restype = ctypes.c_int
+        L.wi_profile_rotate.argtypes = [ctypes.POINTER(IndexView), ctypes.c_int]
+        L.wi_profile_rotate.restype = ctypes.c_int
         L.wi_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.wi_profile_read.restype = ctypes.c_int
         for name in ("wi_index_shapes_for", "wi_build_index", "wi_index_append_segment",
@@ -228,6 +230,13 @@ def wi_profile_enable(enable, repeats: int = 1) -> int:
     """Turn the per-kernel timing hook on or off; with repeats > 1 every decode kernel is
     launched that many times back to back between its events."""
     return _check(lib().wi_profile_enable(max(1, int(repeats)) if enable else 0))
+
+
+def wi_profile_rotate(views) -> int:
+    """Rotation list of the profiling hook's repeats: IndexViews of bit-identical copies of the
+    decoded index (an empty list clears it)."""
+    arr = (IndexView * max(1, len(views)))(*views)
+    return _check(lib().wi_profile_rotate(arr, len(views)))
 
 
 def wi_profile_read() -> dict:

@@ -35,7 +35,10 @@ Parity pins (tests/test_oracle.py), per function:
   spherical_kmeans_segment pinned: zero-noise blobs recover the labels, sizes and directions;
                           objective non-decreasing; fixed-point consistency; brute-force Lloyd on
                           tiny inputs against exhaustive-search cluster labels
-  finalize_index ........ pinned: CSR invariants, bit copies, recomputed sums
+  finalize_index ........ pinned: CSR invariants, bit copies, recomputed sums; exactly: the
+                          ascending-position float64 sum on a cancellation case where pairwise
+                          and reversed orders differ, and the two-step float64 -> float32 ->
+                          bfloat16 rounding on a double-rounding case
   build_index ........... pinned: segment independence, single-segment equivalence
   decode ................ pinned: all-retrieved equals dense softmax attention (textbook, and
                           torch SDPA in float64); keys equal to centroids make the estimate exact;

@@ -296,6 +296,10 @@ def test_profile_hook_modes():
     stages = wi.wi_profile_read()                         # nothing recorded yet
     assert all(v == (0.0, 0) for v in stages.values())
     assert L.wi_profile_enable(0) == wi.WI_OK
+    assert L.wi_profile_rotate(None, -1) == wi.WI_ERR_INVALID_ARG
+    assert L.wi_profile_rotate(None, 2) == wi.WI_ERR_INVALID_ARG
+    assert wi.wi_profile_rotate([_view(), _view()]) == wi.WI_OK
+    assert wi.wi_profile_rotate([]) == wi.WI_OK
 
 
 def test_decode_noalloc_rejects_workspaces_beyond_its_static_array():

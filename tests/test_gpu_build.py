@@ -99,38 +99,84 @@ def test_build_and_decode_single_head_8k_f32_end_to_end():
 
 @pytest.mark.parametrize("name,segments", [
     ("build_128k_bf16", [(0, 0, 0), (0, 7, 15)]),
-    ("gqa_128k_bf16", [(0, 3, 15)]),          # the ragged last segment (8124 tokens)
+    ("gqa_128k_bf16", [(0, 3, 15)]),                        # the ragged last segment (8124 tokens)
+    ("gqa_1m_bf16", [(0, 7, 127), (0, 0, 64)]),             # 128 segments per KV head
+    ("gqa_128k_b16_bf16", [(15, 2, 7), (15, 7, 15)]),      # the last sequence of the batch
 ])
 def test_build_full_size_sampled_segments(name, segments):
+    """The full-size build of a workload, with the oracle's k-means and finalize run on sampled
+    segments (segments are clustered independently): sizes, offsets, perm, mean keys, value sums
+    and the cluster-major K and V rows of the segment bit for bit, and whole-index invariants."""
     dev = device()
     w = synth.WORKLOADS[name]
-    Kt, Vt, Qt, K64, V64, Q64 = inputs(w, 0, dev)
+    if w.B * w.N <= 131072:
+        Kt, Vt, _ = inputs(w, 0, dev)[:3]
+    else:       # host float64 generation of 1M tokens or 16 sequences is slow: the device recipe
+        Kt, Vt, _ = synth.make_instance_device(w, 0, dev)
     seed = 12345
     gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, seed)
     torch.cuda.synchronize()
-    g_np = index_to_numpy(gi)
     lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
     segs = oracle.segment_bounds(hi - lo, w.seg_len)
     Cs = w.clusters_per_seg
+    f64 = lambda t: t.detach().cpu().to(torch.float64).numpy()
     for b, g, s in segments:
+        print(f"[build {name}] segment (b={b}, g={g}, s={s})", flush=True)
         a0, a1 = segs[s]
-        assign, sums, counts = oracle.spherical_kmeans_segment(
-            K64[b, g, lo + a0:lo + a1], Cs, w.iters, w.dtype, oracle.segment_state(seed, b, g, s))
-        c0 = s * Cs
-        np.testing.assert_array_equal(g_np["sizes"][b, g, c0:c0 + Cs], counts)
-        off = g_np["offsets"][b, g, c0:c0 + Cs + 1]
+        Kseg = f64(Kt[b, g, lo + a0:lo + a1])
+        Vseg = f64(Vt[b, g, lo + a0:lo + a1])
+        assign, _, counts = oracle.spherical_kmeans_segment(Kseg, Cs, w.iters, w.dtype,
+                                                            oracle.segment_state(seed, b, g, s))
+        ref = oracle.finalize_index(Kseg[None, None], Vseg[None, None], assign[None, None], 0, 0, Cs, w.dtype)
+        c0, c1 = s * Cs, (s + 1) * Cs
+        off = gi.offsets[b, g, c0:c1 + 1].cpu().numpy().astype(np.int64)
         assert off[0] == a0 and off[-1] == a1
-        for j in range(Cs):
-            run = g_np["perm"][b, g, off[j]:off[j + 1]]
-            want = lo + a0 + np.nonzero(assign == j)[0]
-            np.testing.assert_array_equal(run, want)
-            if counts[j]:
-                mu = oracle.round_to_dtype(sums[j] / counts[j], w.dtype)
-                np.testing.assert_array_equal(g_np["centroids"][b, g, c0 + j], mu)
-                np.testing.assert_array_equal(g_np["k_perm"][b, g, off[j]:off[j + 1]], K64[b, g, want])
+        np.testing.assert_array_equal(gi.sizes[b, g, c0:c1].cpu().numpy(), counts)
+        np.testing.assert_array_equal(off - a0, ref.offsets[0, 0])
+        np.testing.assert_array_equal(gi.perm[b, g, a0:a1].cpu().numpy(), lo + a0 + ref.perm[0, 0])
+        for f, want in (("centroids", ref.centroids[0, 0]), ("value_sums", ref.value_sums[0, 0])):
+            got = f64(getattr(gi, f)[b, g, c0:c1])
+            np.testing.assert_array_equal(got.view(np.uint64), want.view(np.uint64), err_msg=f)
+        for f, want in (("k_perm", ref.k_perm[0, 0]), ("v_perm", ref.v_perm[0, 0])):
+            np.testing.assert_array_equal(f64(getattr(gi, f)[b, g, a0:a1]), want, err_msg=f)
     # whole-index invariants at full size
+    sizes, offs, perm = gi.sizes.cpu().numpy(), gi.offsets.cpu().numpy(), gi.perm.cpu().numpy()
     for b in range(w.B):
         for g in range(w.Hkv):
-            assert g_np["sizes"][b, g].sum() == hi - lo
-            np.testing.assert_array_equal(np.diff(g_np["offsets"][b, g]), g_np["sizes"][b, g])
-            assert np.array_equal(np.sort(g_np["perm"][b, g]), np.arange(lo, hi))
+            assert sizes[b, g].sum() == hi - lo
+            np.testing.assert_array_equal(np.diff(offs[b, g]), sizes[b, g])
+            assert np.array_equal(np.sort(perm[b, g]), np.arange(lo, hi))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_build_value_sums_ascending_order_and_two_step_rounding(dtype):
+    """Values do not move the clustering, so members of chosen clusters can carry values whose
+    float64 sum depends on the order (f32: 2^60, 1, -2^60, 1 sums to 1 left to right, 0 pairwise
+    or right to left) or whose rounding depends on the float32 step (bf16: 1 + 2^-8 + 2^-30 stores
+    as 1, not 1 + 2^-7).  The clusters are chosen from the oracle's build; both sides must give
+    exactly those values."""
+    dev = device()
+    w = synth.Workload("b", 1, 2, 2, 128, 3000, dtype, 20, 4, 16, 1000, 24, 3, 5)
+    K, V, _ = synth.make_instance(w, 8)
+    Kt = synth.cast(K, dtype, dev)
+    K64 = synth.as_float64(Kt)
+    V64 = synth.as_float64(synth.cast(V, dtype))
+    ref0 = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 4, dtype)
+    pattern = [2.0 ** 60, 1.0, -(2.0 ** 60), 1.0] if dtype == "f32" else [1.0, 2.0 ** -8, 2.0 ** -30]
+    planted = []
+    for b, h in ((0, 0), (0, 1)):
+        sz = ref0.sizes[b, h]
+        for c in np.nonzero(sz >= len(pattern))[0][:3]:
+            run = ref0.perm[b, h, ref0.offsets[b, h, c]:ref0.offsets[b, h, c + 1]]   # ascending positions
+            V64[b, h, run] = 0.0
+            V64[b, h, run[:len(pattern)]] = np.asarray(pattern)[:, None]
+            planted.append((b, h, c))
+    assert len(planted) == 6
+    Vt = synth.cast(V64, dtype, dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 4)
+    torch.cuda.synchronize()
+    g = index_to_numpy(gi)
+    ref = oracle.build_index(K64, V64, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 4, dtype)
+    for b, h, c in planted:
+        assert np.all(ref.value_sums[b, h, c] == 1.0), (b, h, c)
+    _assert_index_equal(g, ref)

@@ -125,34 +125,34 @@ def test_decode_single_head_8k_f32_workload():
     _run(w, seed=0, build_seed=0)
 
 
-def test_decode_gqa_128k_bf16_full_size_sampled_heads():
+@pytest.mark.parametrize("q_scale", [1.5, 12.0])
+def test_decode_gqa_128k_bf16_full_size_every_head(q_scale):
     """The benchmarked launch (B=1, 32/8 heads, 128K, top 164 of 8192 clusters), on an index the
     oracle finalizes from the generator's blob labels (folded into 512 clusters per segment);
-    the oracle checks a sample of query heads one by one."""
+    every query head is checked against the oracle.  q_scale 12 sharpens the queries (max logit
+    about 12) so that the 1e-2 output gate bites."""
     dev = device()
-    w = synth.WORKLOADS["gqa_128k_bf16"]
+    w = synth.WORKLOADS["gqa_128k_bf16"].replace(q_scale=q_scale)
     Kt, Vt, Qt, K64, V64, Q64, labels = inputs(w, 0, dev, with_labels=True)
+    del Kt, Vt
     lo, hi = oracle.clustered_range(w.N, w.sink, w.window)
     ci = np.arange(hi - lo)
     lab = (ci // w.seg_len) * w.clusters_per_seg + labels[:, :, lo:hi] % w.clusters_per_seg
     C = len(oracle.segment_bounds(hi - lo, w.seg_len)) * w.clusters_per_seg
     idx = oracle.finalize_index(K64, V64, lab, w.sink, w.window, C, w.dtype)
+    del K64, V64
     gi = upload_index(idx, w.dtype, dev)
     o, lse, sel = wi.decode(gi, Qt, w.top_k)
     torch.cuda.synchronize()
-    heads = [(0, 0), (0, 5), (0, 14), (0, 31)]
+    ro, rl, rs = oracle.decode(Q64, idx, w.Hq, w.top_k, 1 / math.sqrt(w.d))
+    err, _, _ = assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype)
+    if q_scale > 2:
+        assert float(np.abs(ro).max()) > 0.1, "sharpened queries should give outputs above the gate"
     G = w.Hq // w.Hkv
-    res = [oracle.decode_head(Q64[b, h], idx, b, h // G, w.top_k, 1 / math.sqrt(w.d)) for b, h in heads]
-    ro = np.stack([r[0] for r in res])
-    rl = np.array([r[1] for r in res])
-    rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
-    assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
-    # every head: the selected ids are ascending, distinct, non-empty clusters
     s = sel.cpu().numpy()
-    sizes = idx.sizes
     for h in range(w.Hq):
         ids = s[0, h][s[0, h] >= 0]
-        assert ids.size == w.top_k and np.all(np.diff(ids) > 0) and np.all(sizes[0, h // G, ids] > 0)
+        assert ids.size == w.top_k and np.all(np.diff(ids) > 0) and np.all(idx.sizes[0, h // G, ids] > 0)
 
 
 def _oracle_index_slice(gi, b, g):
@@ -165,39 +165,55 @@ def _oracle_index_slice(gi, b, g):
                         k_steady=f(gi.k_steady), v_steady=f(gi.v_steady), C=gi.C, Nc=gi.Nc)
 
 
-def test_decode_gqa_128k_b16_drifting_steps_sampled_heads():
+def _check_every_head(gi, w, results):
+    """results: list of (Q64 [B,Hq,d], o, lse, sel) device results of decode steps on index gi;
+    every (b, query head) of every step is decoded by the oracle on the same index, one KV group
+    at a time, and held to the parity gates."""
+    G = w.Hq // w.Hkv
+    scale = 1 / math.sqrt(w.d)
+    got = [(o.cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
+            s.cpu().numpy().astype(np.int64)) for _, o, l, s in results]
+    ro = np.zeros((len(results), w.B, w.Hq, w.d))
+    rl = np.zeros((len(results), w.B, w.Hq))
+    rs = np.full((len(results), w.B, w.Hq, w.top_k), -1, dtype=np.int64)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            sl = _oracle_index_slice(gi, b, g)
+            for t, (Q64, _, _, _) in enumerate(results):
+                for h in range(g * G, (g + 1) * G):
+                    oh, lh, R = oracle.decode_head(Q64[b, h], sl, 0, 0, w.top_k, scale)
+                    ro[t, b, h], rl[t, b, h] = oh, lh
+                    rs[t, b, h, :R.size] = R
+            del sl
+    for t, (o, l, s) in enumerate(got):
+        assert_decode_parity(torch.from_numpy(o), torch.from_numpy(l), torch.from_numpy(s),
+                             ro[t], rl[t], rs[t], w.dtype)
+
+
+def test_decode_gqa_128k_b16_drifting_steps_every_head():
     """Batch 16 at 128K context, 100 decode steps whose queries drift by N(0, 0.1) per step, on
-    the device-built index of the full batch; the oracle checks sampled query heads at the first,
-    a middle and the last step, on the same index (build parity is tested on its own)."""
+    the device-built index of the full batch; the oracle checks all 16 x 32 query heads at the
+    first, a middle and the last step, on the same index (build parity is tested on its own)."""
     dev = device()
     w = synth.WORKLOADS["gqa_128k_b16_bf16"]
     Kt, Vt, Qt = synth.make_instance_device(w, 0, dev)
     gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 1)
     del Kt, Vt
     qm = synth.drift_queries_device(Qt, w.steps, w.drift, 0)
-    G = w.Hq // w.Hkv
-    heads = [(0, 0), (7, 13), (15, 31)]
     checks = {0: None, 50: None, w.steps - 1: None}
     for t in range(w.steps):
         q = qm[t].to(torch.float32).to(Qt.dtype)
         o, lse, sel = wi.decode(gi, q, w.top_k)
         if t in checks:
-            checks[t] = (q.clone(), o.clone(), lse.clone(), sel.clone())
+            checks[t] = (synth.as_float64(q), o.clone(), lse.clone(), sel.clone())
     torch.cuda.synchronize()
-    slices = {(b, h // G): _oracle_index_slice(gi, b, h // G) for b, h in heads}
-    for t, (q, o, lse, sel) in checks.items():
-        Q64 = synth.as_float64(q)
-        res = [oracle.decode_head(Q64[b, h], slices[(b, h // G)], 0, 0, w.top_k, 1 / math.sqrt(w.d))
-               for b, h in heads]
-        ro = np.stack([r[0] for r in res])
-        rl = np.array([r[1] for r in res])
-        rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
-        assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
+    print(f"[decode b16] 100 steps done; oracle over {w.B * w.Hq} heads x 3 steps", flush=True)
+    _check_every_head(gi, w, list(checks.values()))
 
 
-def test_decode_gqa_1m_bf16_sampled_heads():
+def test_decode_gqa_1m_bf16_every_head():
     """One million tokens per KV head (65536 clusters, top 656): the device-built index decoded
-    once, sampled query heads checked against the oracle on the same index."""
+    once, every query head checked against the oracle on the same index."""
     dev = device()
     w = synth.WORKLOADS["gqa_1m_bf16"]
     Kt, Vt, Qt = synth.make_instance_device(w, 0, dev)
@@ -205,15 +221,7 @@ def test_decode_gqa_1m_bf16_sampled_heads():
     del Kt, Vt
     o, lse, sel = wi.decode(gi, Qt, w.top_k)
     torch.cuda.synchronize()
-    G = w.Hq // w.Hkv
-    heads = [(0, 0), (0, 9), (0, 30)]
-    Q64 = synth.as_float64(Qt)
-    res = [oracle.decode_head(Q64[b, h], _oracle_index_slice(gi, b, h // G), 0, 0, w.top_k, 1 / math.sqrt(w.d))
-           for b, h in heads]
-    ro = np.stack([r[0] for r in res])
-    rl = np.array([r[1] for r in res])
-    rs = np.stack([np.concatenate([r[2], -np.ones(w.top_k - r[2].size, dtype=np.int64)]) for r in res])
-    assert_decode_parity(o, lse, sel, ro, rl, rs, w.dtype, heads=heads)
+    _check_every_head(gi, w, [(synth.as_float64(Qt), o, lse, sel)])
 
 
 def test_decode_graph_replay_matches_eager():
@@ -271,11 +279,14 @@ def test_decode_repeated_launches_and_back_to_back_calls_agree():
                              w.dtype)
     gi = upload_index(idx, w.dtype, dev)
     o1, l1, s1 = wi.decode(gi, Qt, w.top_k)
+    copies = [gi.clone(), gi.clone()]
+    wi.wi_profile_rotate([c.view() for c in copies])       # repeats read copies at other addresses
     wi.wi_profile_enable(True, 3)
     o2, l2, s2 = wi.decode(gi, Qt, w.top_k)
     torch.cuda.synchronize()
     launches = wi.wi_profile_read()["attend"][1]
     wi.wi_profile_enable(False)
+    wi.wi_profile_rotate([])
     o3, l3, s3 = wi.decode(gi, Qt, w.top_k)
     torch.cuda.synchronize()
     assert launches == 3

@@ -1,7 +1,8 @@
 """GPU tests of the wave buffer (wi_decode_wavebuf): decode over an index whose cluster-major K/V
 copies are in pinned host memory, through a GPU block cache and an execution buffer.
 
-Where the rows come from must not change what is computed: every step's out, lse and sel_ids
+Every step's out, lse and sel_ids meet the oracle's gates on the same index (the oracle decodes
+every head of every step), and where the rows come from must not change what is computed: they
 equal wi_decode's on the same index in device memory, bit for bit, whatever the cache holds.
 The cache's behaviour is checked against a plain LRU model fed with the blocks that the oracle's
 retrieval zones touch (16-row blocks of the cluster-major rows, once per (b, KV head) and step):
@@ -16,7 +17,7 @@ import torch
 import oracle
 from kv_vector_index_amd import synth
 from kv_vector_index_amd import wave_index as wi
-from wi_testutil import device, upload_index
+from wi_testutil import assert_decode_parity, device, upload_index
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +96,9 @@ def _run(w, idx, gi, qs, cache_blocks, exec_blocks, dtype):
         o1, l1, s1 = wb.decode(q)
         o2, l2, s2 = wi.decode(gi, q, w.top_k)
         torch.cuda.synchronize()
+        # the oracle's decode on the same index, then the device-resident decode bit for bit
+        ro, rl, rs = oracle.decode(synth.as_float64(q), idx, w.Hq, w.top_k)
+        assert_decode_parity(o1, l1, s1, ro, rl, rs, dtype)
         assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
         st = wb.stats()
         per_step.append({k: st[k] - prev[k] for k in st})
@@ -170,6 +174,8 @@ def test_wavebuf_back_to_back_steps_without_waiting():
     res = [wb.decode(q) for q in qs + qs]
     torch.cuda.synchronize()
     for q, (o1, l1, s1) in zip(qs + qs, res):
+        ro, rl, rs = oracle.decode(synth.as_float64(q), idx, w.Hq, w.top_k)
+        assert_decode_parity(o1, l1, s1, ro, rl, rs, "bf16")
         o2, l2, s2 = wi.decode(gi, q, w.top_k)
         assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
     st = wb.stats()
@@ -203,6 +209,8 @@ def test_wavebuf_full_size_equals_device_decode():
         o1, l1, s1 = wb.decode(q)
         o2, l2, s2 = wi.decode(gi, q, w.top_k)
         torch.cuda.synchronize()
+        ro, rl, rs = oracle.decode(synth.as_float64(q), idx, w.Hq, w.top_k)
+        assert_decode_parity(o1, l1, s1, ro, rl, rs, "bf16")
         assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2), t
         st = wb.stats()
         if t >= 2:

@@ -255,6 +255,45 @@ def test_csr_invariants():
             np.testing.assert_array_equal(idx.k_steady[b, g], K[b, g, st])
 
 
+def _one_cluster_index(K_rows, V_rows, dtype):
+    """finalize_index over a context of len(K_rows) clustered tokens (no steady zone), all in
+    cluster 0 of 2 (cluster 1 stays empty)."""
+    n = len(K_rows)
+    K = np.zeros((1, 1, n, 128))
+    V = np.zeros((1, 1, n, 128))
+    K[0, 0] = np.asarray(K_rows)[:, None]
+    V[0, 0] = np.asarray(V_rows)[:, None]
+    return oracle.finalize_index(K, V, np.zeros((1, 1, n), dtype=np.int64), 0, 0, 2, dtype)
+
+
+def test_finalize_sums_members_in_ascending_position_order_f32():
+    # members at positions 0..3 holding 2^60, 1, -2^60, 1 (all exact in float32).  Left to right in
+    # float64: 2^60 + 1 rounds to 2^60, minus 2^60 gives 0, plus 1 gives 1.  Other orders give
+    # other values: pairwise (2^60 + 1) + (-2^60 + 1) = 0, right to left 0, exact 2.  So the value
+    # sum must be exactly 1 and the mean key exactly 1/4.
+    big = 2.0 ** 60
+    idx = _one_cluster_index([big, 1.0, -big, 1.0], [big, 1.0, -big, 1.0], "f32")
+    assert idx.sizes[0, 0, 0] == 4 and idx.sizes[0, 0, 1] == 0
+    assert np.all(idx.value_sums[0, 0, 0] == 1.0)
+    assert np.all(idx.centroids[0, 0, 0] == 0.25)
+    assert not idx.value_sums[0, 0, 1].any() and not idx.centroids[0, 0, 1].any()
+
+
+def test_finalize_rounds_float64_to_float32_to_bfloat16_in_two_steps():
+    # bf16 storage of x = 1 + 2^-8 + 2^-30: x is just above the midpoint of the bf16 neighbours 1
+    # and 1 + 2^-7, so rounding it directly would give 1 + 2^-7; rounded to float32 first it becomes
+    # exactly the midpoint 1 + 2^-8 (2^-30 is below half a float32 ulp), which then rounds to the
+    # even neighbour 1.  Value sum: members 1, 2^-8, 2^-30; mean key: members 4, 2^-6, 2^-28, 0
+    # (sum 4 x, so the mean is x).  Every member is exact in bf16 and the float64 sums are exact.
+    idx = _one_cluster_index([4.0, 2.0 ** -6, 2.0 ** -28, 0.0], [1.0, 2.0 ** -8, 2.0 ** -30, 0.0], "bf16")
+    assert np.all(idx.value_sums[0, 0, 0] == 1.0)
+    assert np.all(idx.centroids[0, 0, 0] == 1.0)
+    # a float32-exact value past the midpoint rounds up, as plain round-to-nearest does
+    idx = _one_cluster_index([4.0, 2.0 ** -6, 2.0 ** -20, 0.0], [1.0, 2.0 ** -8, 2.0 ** -22, 0.0], "bf16")
+    assert np.all(idx.value_sums[0, 0, 0] == 1.0 + 2.0 ** -7)
+    assert np.all(idx.centroids[0, 0, 0] == 1.0 + 2.0 ** -7)
+
+
 def test_segments_are_independent_and_single_segment_matches_unsegmented():
     w = _small_workload(B=1, Hkv=1, Hq=1, N=300, seg_len=100, clusters_per_seg=6)
     K, V, _ = _inputs(w)
