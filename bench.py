@@ -42,8 +42,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_MFMA_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_{}.json")   # per workload
 PROF_REPS = 20                  # launches of each decode kernel between its timing events
-KERNEL_NAMES = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
-STREAMING = ("score", "attend")  # the decode kernels that stream HBM; select and merge are latency
+KERNEL_NAMES = {"score": "k_score", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
+STREAMING = ("score", "select", "attend")   # kernels that stream HBM (the select's estimation
+                                             # workgroups stream the value sums); merge is latency
 CPU_MAX_WORKERS = 16            # the host share of one GPU
 _CPU = {}                       # host inputs of the CPU baseline, inherited by its forked workers
 
@@ -55,8 +56,8 @@ def log(*a):
 def algorithmic_bytes(w, idx_offsets_np, sel_np):
     """Bytes each decode kernel must move per step, every byte counted once (the per-step formula
     of the measurement plan, split by the kernel that moves it):
-      score  : centroids and value sums of every cluster, offsets (C + 1 per KV head), queries
-      select : the retrieved ids it writes
+      score  : centroids of every cluster, offsets (C + 1 per KV head), queries
+      select : value sums of every cluster (its estimation workgroups), the retrieved ids it writes
       attend : steady rows and the union of the rows retrieved by a KV group's query heads (K + V)
       merge  : outputs and lse
     Returns (per-kernel bytes, union rows, correction bytes): the last are what the attention
@@ -78,7 +79,8 @@ def algorithmic_bytes(w, idx_offsets_np, sel_np):
             ids = ids[ids >= 0]
             u = int((off[ids + 1] - off[ids]).sum())
             union_rows += u
-            per["score"] += C * 2 * d * e + 4 * (C + 1)
+            per["score"] += C * d * e + 4 * (C + 1)
+            per["select"] += C * d * e
             per["attend"] += NS * 2 * d * e + u * 2 * d * e
             corr += int((sel_np[b, g * G:(g + 1) * G] >= 0).sum()) * (d * e + 4)
     per["score"] += w.B * w.Hq * d * e
@@ -334,14 +336,15 @@ def main():
     # workload of at most 128K tokens they are drawn on the host (before the GPU is touched, so
     # that the oracle's worker processes can be forked with them); larger workloads draw on the
     # device and carry no CPU baseline.
-    with_cpu = not args.no_cpu_baseline and w.B == 1 and w.N <= 131072 and args.wavebuf is None
+    host_gen = w.B == 1 and w.N <= 131072
     pool = None
-    if with_cpu:
+    if host_gen:
         log(f"[bench] workload {w.name}: generating inputs on the host")
         Kh, Vh, Qh = host_inputs(w, args.seed)
-        pool = cpu_pool()
+        if not args.no_cpu_baseline and args.wavebuf is None:
+            pool = cpu_pool()
     dev = torch.device("cuda:0")
-    if with_cpu:
+    if host_gen:
         Kt, Vt, Qt = (x.to(dev) for x in (Kh, Vh, Qh))
         del Kh, Vh, Qh
     else:

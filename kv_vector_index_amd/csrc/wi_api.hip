@@ -136,7 +136,10 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.BH = p.B * p.Hq;
   L.G = p.Hq / p.Hkv;
   L.W32 = (int)ceil_div(p.C, 32);
-  L.est_tiles_g = (int)ceil_div(p.C, kEstTile);
+  L.tiles_g = (int)ceil_div(p.C, kScoreTile);
+  // estimation workgroups per KV group: about kEstTarget in all, each over whole score tiles
+  const int64_t est_target = L.BH > 256 ? kEstTargetMany : kEstTarget;
+  L.est_blocks_g = (int)std::max<int64_t>(std::min<int64_t>(L.tiles_g, ceil_div(est_target, L.BG)), p.C > 0 ? 1 : 0);
   // Attention workgroups per query head: Sc fold the retrieved clusters' estimation terms (64
   // each); S split the head's exact tokens (steady zone + retrieved clusters, estimated from
   // the mean cluster size).  S fills about one resident wave of the grid (kAttTarget in all)
@@ -149,10 +152,10 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G, K = p.top_k;
   size_t o = 0;
   L.off_keys = o;       o = align256(o + BH * C * 4);
-  L.off_tile_norm = o;  o = align256(o + BG * L.est_tiles_g * 4);
-  L.off_tile_cnt = o;   o = align256(o + BG * L.est_tiles_g * 4);
-  L.off_tile_top = o;   o = align256(o + BH * L.est_tiles_g * kTileTop * 4);
-  L.off_tile_top_id = o; o = align256(o + BH * L.est_tiles_g * kTileTop * 4);
+  L.off_tile_norm = o;  o = align256(o + BG * L.tiles_g * 4);
+  L.off_tile_cnt = o;   o = align256(o + BG * L.tiles_g * 4);
+  L.off_tile_top = o;   o = align256(o + BH * L.tiles_g * kTileTop * 4);
+  L.off_tile_top_id = o; o = align256(o + BH * L.tiles_g * kTileTop * 4);
   L.off_band_ids = o;   o = align256(o + BH * C * 4);
   L.off_band_key = o;   o = align256(o + BH * C * 8);
   L.off_all_sel = o;    o = align256(o + BH * 4);
@@ -163,8 +166,8 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_hl_pre = o;     o = align256(o + BH * (K + 1) * 4);
   L.off_hl_key = o;     o = align256(o + BH * K * 4);
   L.off_att_bounds = o; o = align256(o + BH * L.att_split * 4);
-  L.off_est_md = o;     o = align256(o + BG * L.est_tiles_g * G * 2 * 4);
-  L.off_est_num = o;    o = align256(o + BG * L.est_tiles_g * G * kD * 4);
+  L.off_est_md = o;     o = align256(o + BG * L.est_blocks_g * G * 2 * 4);
+  L.off_est_num = o;    o = align256(o + BG * L.est_blocks_g * G * kD * 4);
   L.off_att_md = o;     o = align256(o + BH * L.att_items * 2 * 4);
   L.off_att_num = o;    o = align256(o + BH * L.att_items * kD * 4);
   L.total = o;
@@ -382,7 +385,7 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
   a.att_md = reinterpret_cast<float*>(base + L.off_att_md);
   a.att_num = reinterpret_cast<float*>(base + L.off_att_num);
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.G = G; a.C = p->C; a.Nc = p->Nc; a.NS = p->n_steady;
-  a.top_k = p->top_k; a.W32 = L.W32; a.est_tiles_g = L.est_tiles_g;
+  a.top_k = p->top_k; a.W32 = L.W32; a.tiles_g = L.tiles_g; a.est_blocks_g = L.est_blocks_g;
   a.att_split = L.att_split; a.att_items = L.att_items;
   a.scale = p->scale;
   hipStream_t st = static_cast<hipStream_t>(stream);

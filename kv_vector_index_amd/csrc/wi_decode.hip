@@ -1,5 +1,4 @@
-// Wave-index decode step on gfx950: score + estimate -> select -> work lists -> exact attention
-// -> LSE merge.
+// Wave-index decode step on gfx950: score -> select + estimate -> exact attention -> LSE merge.
 //
 // Method: RetroInfer's tripartite attention (technical summary, gist.science Spanish page,
 // section 2.A items 1-3; Arabic page section 2.a).  Per query head, the steady zone (sinks and
@@ -8,22 +7,23 @@
 // denominator and n_c * exp(s_c) * SV_c / n_c to the numerator; the partial softmax states are
 // merged with log-sum-exp.
 //
-// The estimation is computed over *all* non-empty clusters in the same pass that scores them
-// (mu and SV stream together, before the selection is known), and the terms of the retrieved
-// clusters are subtracted at the merge: sum over E = sum over all - sum over R.  The subtracted
-// terms never exceed the exact mass of the same tokens (exp is convex, so n_c exp(mean logit) is
-// at most the sum of the members' exp(logit)), so the cancellation costs O(eps_fp32) relative to
-// the merged denominator.  When a head retrieves every non-empty cluster both terms are dropped.
+// The estimation is computed over *all* non-empty clusters, before the selection is known, and
+// the terms of the retrieved clusters are subtracted at the merge: sum over E = sum over all -
+// sum over R.  The subtracted terms never exceed the exact mass of the same tokens (exp is
+// convex, so n_c exp(mean logit) is at most the sum of the members' exp(logit)), so the
+// cancellation costs O(eps_fp32) relative to the merged denominator.  When a head retrieves every
+// non-empty cluster both terms are dropped.
 //
 // Kernels (one stream, in order):
-//   k_score_est  grid (ceil(C/128), B*Hkv): MFMA scores of the KV group's query heads against 128
+//   k_score      grid (ceil(C/128), B*Hkv): MFMA scores of the KV group's query heads against 128
 //                centroids (one pass over mu serves all heads of the group), the score keys, the
-//                tile's 8 best keys per head, fp32 centroid norms, and the tile's estimation
-//                partial per head from SV and the sizes.
-//   k_select     grid (B*Hq): exact top-k per head (a threshold bounded from the tile summaries
-//                and found on the fp32 scores, canonical fp64 re-scoring of the certified
-//                uncertainty band, ties to the lower id), published as the head's ascending list
-//                of clusters with their first rows and token offsets.
+//                tile's 8 best keys per head, fp32 centroid norms and non-empty counts.
+//   k_select     grid (B*Hq + B*Hkv*ceil(C/512)): workgroup bh < B*Hq finds the exact top-k of
+//                query head bh (a threshold bounded from the tile summaries and found on the fp32
+//                scores, canonical fp64 re-scoring of the certified uncertainty band, ties to the
+//                lower id), published as the head's ascending list of clusters with their first
+//                rows and token offsets; the other workgroups stream the value sums and fold the
+//                estimation partials of 512 clusters each, on the CUs the select leaves idle.
 //   k_attend     grid (B*Hq * (S + Sc)): S workgroups per head split its token list (steady zone,
 //                then the rows of its retrieved clusters) with an online softmax; Sc workgroups
 //                fold the retrieved clusters' estimation terms.
@@ -35,56 +35,36 @@ namespace wi {
 
 constexpr int kScoreThreads = 256;
 
-// ============================================================================ k_score_est
-// grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid or value
-// sum row (256 B in bf16) is read as four 64-byte pieces by four lanes in one instruction.
-// Four waves per SIMD where the tile's registers fit in 128 VGPRs without spilling (bf16, up to
-// four heads per group); otherwise the compiler's choice.
+// ============================================================================ k_score
+// grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid row (256 B
+// in bf16) is read as four 64-byte pieces by four lanes in one instruction.  Four waves per SIMD
+// where the tile's registers fit in 128 VGPRs without spilling (bf16, up to four heads per
+// group); otherwise the compiler's choice.
 template <typename T, int G> struct ScoreWaves { static constexpr int v = (sizeof(T) == 2 && G <= 4) ? 4 : 1; };
 
 template <typename T, int G>
-__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(ScoreWaves<T, G>::v))) void k_score_est(DecodeArgs a) {
-  __shared__ float sh_s[G][kEstTile];       // logits (scaled), -inf for empty clusters
-  __shared__ float sh_w[G][kEstTile];       // exp(logit - m)
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(ScoreWaves<T, G>::v))) void k_score(DecodeArgs a) {
   __shared__ float sh_n[kScoreThreads];     // cluster sizes (entries >= nrows are 0)
-  __shared__ float sh_nrm[kEstTile];        // centroid norms
-  __shared__ uint32_t sh_k[G][kEstTile];    // order keys of the raw scores, 0 for empty clusters
-  __shared__ float sh_m[G], sh_den[G];
-  __shared__ float sh_num[G <= 4 ? 1 : 4][G][kD];          // G > 4: per-wave numerators
-  __shared__ __attribute__((aligned(16))) float sh_part[G <= 4 ? 16 : 1][G][kD];  // G <= 4: per lane group
+  __shared__ float sh_nrm[kScoreTile];      // centroid norms
+  __shared__ uint32_t sh_k[G][kScoreTile];  // order keys of the raw scores
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   if (C == 0) return;
-  const int nrows = min(kEstTile, C - tile * kEstTile);
-  const int cbase = tile * kEstTile + w * 32;
+  const int nrows = min(kScoreTile, C - tile * kScoreTile);
+  const int cbase = tile * kScoreTile + w * 32;
   const T* mu = static_cast<const T*>(a.mu) + (size_t)bg * C * kD;
-  const T* sv = static_cast<const T*>(a.sv) + ((size_t)bg * C + (size_t)tile * kEstTile) * kD;
   const int32_t* szs = a.sizes + (size_t)bg * C;
   const T* qg = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G) * kD;
 
   // Every global load of the tile is issued before the first wait: the sizes, the centroids and
-  // the queries, then the value sums (lane (lr, lg) of wave w owns rows w*32 + 4i + lg and dims
-  // [8 lr, 8 lr + 8)), so the tile costs one memory round trip and the scores, keys and
-  // summaries are computed while the value sums are still arriving.  The loads are unconditional
-  // (row indices clamped into the tile, query rows into the group) so that the wait before the
-  // first MFMA counts only the loads issued ahead of it; rows past the tile get weight 0 and
-  // query rows past the group are never read back.  Empty clusters are masked by their size in
-  // the per-head pass.
-  const int n_raw = szs[tile * kEstTile + min(tid, nrows - 1)];
-  u32x4_t svr[8];
-  [[maybe_unused]] u32x4_t svr_hi[8];
-  auto load_sv = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = min(w * 32 + 4 * i + lg, nrows - 1);
-      const T* p = sv + (size_t)r * kD + 8 * lr;
-      svr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-      if constexpr (sizeof(T) == 4) svr_hi[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
-    }
-  };
+  // the queries.  The loads are unconditional (row indices clamped into the tile, query rows
+  // into the group) so that the wait before the first MFMA counts only the loads issued ahead
+  // of it; query rows past the group are never read back.  Empty clusters are masked by their
+  // size in the per-head pass.
+  const int n_raw = szs[tile * kScoreTile + min(tid, nrows - 1)];
   // raw score of query head h (row h of the MFMA tile) against cluster row cl, and the norm of
   // that centroid
   auto put_scores = [&](const f32x4_t& acc, float n2, int t) {
@@ -92,10 +72,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
-      if (h < G) {
-        sh_s[h][cl] = acc[r];
-        sh_k[h][cl] = f32_order_key(acc[r]);
-      }
+      if (h < G) sh_k[h][cl] = f32_order_key(acc[r]);
     }
     if (lg == 0) sh_nrm[cl] = sqrtf(n2);
   };
@@ -114,7 +91,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)min(lr, G - 1) * kD + 32 * s + 8 * lg);
-    load_sv();
     __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -147,7 +123,6 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       qa[4 * j] = __uint_as_float(v.x); qa[4 * j + 1] = __uint_as_float(v.y);
       qa[4 * j + 2] = __uint_as_float(v.z); qa[4 * j + 3] = __uint_as_float(v.w);
     }
-    load_sv();
     __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -171,7 +146,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   sh_n[tid] = tid < nrows ? (float)n_raw : 0.f;
   __syncthreads();
 
-  const size_t slot = (size_t)bg * a.est_tiles_g + tile;
+  const size_t slot = (size_t)bg * a.tiles_g + tile;
   if (w == 0) {
     // largest norm among the tile's non-empty centroids, and how many are non-empty
     const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
@@ -179,26 +154,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     const int nc = __popcll(__ballot(e0)) + __popcll(__ballot(e1));
     if (lane == 0) { a.tile_norm[slot] = nm; a.tile_cnt[slot] = nc; }
   }
-  // per head: the raw-score keys (0 for empty clusters), then the estimation partial of the tile:
-  // m_h = max logit, den_h = sum n_c w, num_h = sum w SV_c
+  // per head: the raw-score keys (0 for empty clusters) and the head's 8 best scores of the tile
+  // (key 0 past the non-empty clusters) with their cluster ids: lane r keeps the r-th, found by
+  // repeated wave maxima, each time clearing the holder with the lowest id
   for (int h = w; h < G; h += kScoreThreads / 64) {
     const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
     const uint32_t k0 = e0 ? sh_k[h][lane] : 0u, k1 = e1 ? sh_k[h][lane + 64] : 0u;
-    uint32_t* keys_h = a.keys + ((size_t)b * a.Hq + (size_t)g * G + h) * C + (size_t)tile * kEstTile;
+    uint32_t* keys_h = a.keys + ((size_t)b * a.Hq + (size_t)g * G + h) * C + (size_t)tile * kScoreTile;
     if (lane < nrows) keys_h[lane] = k0;
     if (lane + 64 < nrows) keys_h[lane + 64] = k1;
-    const float x0 = e0 ? sh_s[h][lane] * a.scale : -INFINITY;
-    const float x1 = e1 ? sh_s[h][lane + 64] * a.scale : -INFINITY;
-    const float m = wave_max(fmaxf(x0, x1));
-    const float w0 = x0 == -INFINITY ? 0.f : __expf(x0 - m);
-    const float w1 = x1 == -INFINITY ? 0.f : __expf(x1 - m);
-    sh_w[h][lane] = w0;
-    sh_w[h][lane + 64] = w1;
-    const float dn = wave_sum(w0 * sh_n[lane] + w1 * sh_n[lane + 64]);
-    if (lane == 0) { sh_m[h] = m; sh_den[h] = dn; }
-    // the head's 8 best scores of the tile (key 0 past the non-empty clusters) with their cluster
-    // ids: lane r keeps the r-th, found by repeated wave maxima, each time clearing the holder
-    // with the lowest id
     uint32_t c0 = k0, c1 = k1, best = 0u;
     int best_id = 0;
 #pragma unroll
@@ -214,83 +178,223 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
         holder = __ffsll((unsigned long long)b1) - 1 + 64;
         if (lane == holder - 64) c1 = 0u;
       }
-      if (lane == r) { best = m8; best_id = tile * kEstTile + holder; }
+      if (lane == r) { best = m8; best_id = tile * kScoreTile + holder; }
     }
     if (lane < kTileTop) {
-      const size_t ti = (((size_t)b * a.Hq + (size_t)g * G + h) * a.est_tiles_g + tile) * kTileTop + lane;
+      const size_t ti = (((size_t)b * a.Hq + (size_t)g * G + h) * a.tiles_g + tile) * kTileTop + lane;
       a.tile_top[ti] = best;
       a.tile_top_id[ti] = best_id;
     }
   }
-  __syncthreads();
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 32 + 4 * i + lg;
-    float v[8];
-    if constexpr (sizeof(T) == 2) {
-      const u32x4_t u = svr[i];
-      v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-      v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-      v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
-      v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
-    } else {
-      v[0] = __uint_as_float(svr[i].x); v[1] = __uint_as_float(svr[i].y);
-      v[2] = __uint_as_float(svr[i].z); v[3] = __uint_as_float(svr[i].w);
-      v[4] = __uint_as_float(svr_hi[i].x); v[5] = __uint_as_float(svr_hi[i].y);
-      v[6] = __uint_as_float(svr_hi[i].z); v[7] = __uint_as_float(svr_hi[i].w);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float wt = sh_w[h][r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += wt * v[e];
-    }
+}
+
+// Packed row piece: 8 elements of one row (16 B of bf16 or 32 B of fp32).
+template <typename T> struct Piece;
+template <> struct Piece<uint16_t> {
+  u32x4_t v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ void load_nt(const uint16_t* p) { v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)); }
+  __device__ void zero() { v = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
   }
-  // sum over the 16 lane groups of the block (4 waves x 4 row groups) that hold the same dims
-  if constexpr (G <= 4) {
-    // every lane group writes its partial numerators to LDS; 16-way sums read them back
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = &sh_part[w * 4 + lg][h][8 * lr];
-      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-    }
-    __syncthreads();
-    for (int i = tid; i < G * kD; i += kScoreThreads) {
-      const int h = i / kD, d = i - h * kD;
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sum += sh_part[j][h][d];
-      a.est_num[(slot * G + h) * kD + d] = sum;
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[h][e] += __shfl_xor(acc[h][e], 16);
-        acc[h][e] += __shfl_xor(acc[h][e], 32);
+};
+template <> struct Piece<float> {
+  u32x4_t v0, v1;
+  __device__ void load(const float* p) {
+    v0 = *reinterpret_cast<const u32x4_t*>(p);
+    v1 = *reinterpret_cast<const u32x4_t*>(p + 4);
+  }
+  __device__ void load_nt(const float* p) {
+    v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
+  }
+  __device__ void zero() { v0 = u32x4_t{0u, 0u, 0u, 0u}; v1 = v0; }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v0.x); o[1] = __uint_as_float(v0.y); o[2] = __uint_as_float(v0.z); o[3] = __uint_as_float(v0.w);
+    o[4] = __uint_as_float(v1.x); o[5] = __uint_as_float(v1.y); o[6] = __uint_as_float(v1.z); o[7] = __uint_as_float(v1.w);
+  }
+};
+
+// ============================================================================ estimation
+// Workgroups of the select launch past the B*Hq select workgroups: estimation workgroup x takes
+// the score tiles [e T / E, (e + 1) T / E) of KV group bg (x = bg E + e; T tiles of 128 clusters,
+// E = est_blocks_g workgroups per group) and folds, for every query head h of the group,
+// m = max over the non-empty clusters of l_c = scale <q_h, mu_c>, den = sum n_c exp(l_c - m) and
+// num = sum exp(l_c - m) SV_c (n_c exp(l_c) SV_c / n_c per cluster).  The scores are the score
+// kernel's fp32 scores (decoded from their order keys) and m comes from its per-tile maxima.
+// These workgroups need no selection, so they stream the value sums while the select
+// workgroups, one per query head, leave most CUs idle; each keeps two passes of rows in flight
+// and writes one partial per head.
+// Buffer resource of a byte range (gfx9 descriptor: raw buffer, no stride, dword 3 0x00020000):
+// loads address it with 32-bit offsets from a scalar base, and reads past its end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kStreamNT = 2;        // buffer-load cache policy: non-temporal (streamed once)
+
+// Eight elements of one value-sum row (16 B of bf16, two 16 B pieces of fp32), as raw bits,
+// read through a buffer resource with a 32-bit offset.
+template <typename T> struct Oct;
+template <> struct Oct<uint16_t> {
+  u32x4_t v;
+  __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+    v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kStreamNT));
+  }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+};
+template <> struct Oct<float> {
+  u32x4_t v0, v1;
+  __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+    v0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kStreamNT));
+    v1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16u, so, kStreamNT));
+  }
+  __device__ void unpack(float (&o)[8]) const {
+    o[0] = __uint_as_float(v0.x); o[1] = __uint_as_float(v0.y); o[2] = __uint_as_float(v0.z); o[3] = __uint_as_float(v0.w);
+    o[4] = __uint_as_float(v1.x); o[5] = __uint_as_float(v1.y); o[6] = __uint_as_float(v1.z); o[7] = __uint_as_float(v1.w);
+  }
+};
+
+template <typename T, int NT>
+__device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2][kD] */,
+                          float* sh /* >= 4 + 4 (NT / 64) floats */) {
+  // lane (lr = lane & 15, lg = lane >> 4) of wave wv holds dims [8 lr, 8 lr + 8) of row
+  // p0 + 4 wv + lg of each pass, NBUF passes in flight: 64 KB per 1024-thread workgroup in bf16
+  // (the select kernel runs one such workgroup per CU, or two of 512 threads)
+  constexpr int NW = NT / 64, PASS = NW * 4, NBUF = 4;
+  constexpr uint32_t kRow = kD * sizeof(T);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int E = a.est_blocks_g, tiles = a.tiles_g;
+  const int bg = x / E, e = x - bg * E;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv, G = a.G, C = a.C;
+  const int t0 = (int)((int64_t)e * tiles / E), t1 = (int)((int64_t)(e + 1) * tiles / E);
+  const int c0 = t0 * kScoreTile, n = min(C, t1 * kScoreTile) - c0;      // n >= 1 (E <= tiles)
+  // the range's value sums, the group's score keys and the range's sizes, as buffer resources:
+  // rows past the range read 0 (value sums, sizes) or other clusters' keys, all weighted 0
+  const __amdgpu_buffer_rsrc_t r_sv = byte_range(static_cast<const T*>(a.sv) + ((size_t)bg * C + c0) * kD, (uint32_t)n * kRow);
+  const __amdgpu_buffer_rsrc_t r_key = byte_range(a.keys + ((size_t)b * a.Hq + (size_t)g * G) * C, (uint32_t)(G * C) * 4u);
+  const __amdgpu_buffer_rsrc_t r_sz = byte_range(a.sizes + (size_t)bg * C + c0, (uint32_t)n * 4u);
+  const size_t slot = (size_t)bg * E + e;
+  for (int h0 = 0; h0 < G; h0 += 4) {
+    // m of each head of the chunk: the largest of its tiles' best scores (key 0: no cluster)
+    if (wv < 4) {
+      float mx = -INFINITY;
+      if (h0 + wv < G) {
+        const uint32_t* tt = a.tile_top + ((size_t)b * a.Hq + (size_t)g * G + h0 + wv) * tiles * kTileTop;
+        for (int t = t0 + lane; t < t1; t += 64) {
+          const uint32_t k = tt[(size_t)t * kTileTop];
+          if (k != 0u) mx = fmaxf(mx, f32_from_order_key(k) * a.scale);
+        }
       }
-    if (lg == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sh_num[w][h][8 * lr + e] = acc[h][e];
+      mx = wave_max(mx);
+      if (lane == 0) sh[wv] = mx;
     }
     __syncthreads();
-    for (int i = tid; i < G * kD; i += kScoreThreads) {
-      const int h = i / kD, d = i - h * kD;
-      a.est_num[(slot * G + h) * kD + d] = sh_num[0][h][d] + sh_num[1][h][d] + sh_num[2][h][d] + sh_num[3][h][d];
+    // Lane lr < 4 of a row group also weighs the row for head h0 + lr (the other lanes copy its
+    // weight), so that a lane holds one score key per row.
+    const int hl = lr & 3;
+    const float m_own = sh[hl];
+    const bool head_live = h0 + hl < G;
+    const uint32_t vo_sv = (uint32_t)(4 * wv + lg) * kRow + 8u * sizeof(T) * lr;
+    const uint32_t vo_key = ((uint32_t)min(h0 + hl, G - 1) * (uint32_t)C + (uint32_t)c0 + (uint32_t)(4 * wv + lg)) * 4u;
+    const uint32_t vo_sz = (uint32_t)(4 * wv + lg) * 4u;
+    Oct<T> vr[NBUF];
+    uint32_t kk[NBUF];
+    float nn[NBUF];
+    auto issue = [&](auto buf, int p0) {
+      vr[buf].load(r_sv, vo_sv, p0 * (int)kRow);
+      kk[buf] = __builtin_amdgcn_raw_buffer_load_b32(r_key, vo_key, p0 * 4, 0);
+      nn[buf] = (float)(int)__builtin_amdgcn_raw_buffer_load_b32(r_sz, vo_sz, p0 * 4, 0);
+    };
+    float acc[4][8], den = 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    auto consume = [&](auto buf, int p0) {
+      const bool live = p0 + 4 * wv + lg < n;
+      const uint32_t k = kk[buf];
+      // exp(-inf) = 0 for rows past the range, empty clusters and heads past the group (no branch)
+      const float w_own = __expf((live && k != 0u && head_live) ? f32_from_order_key(k) * a.scale - m_own : -INFINITY);
+      if (lr < 4) den += w_own * nn[buf];
+      float v[8];
+      vr[buf].unpack(v);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float wt = __shfl(w_own, (lane & 48) + h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] += wt * v[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);     // keep each pass's weights from being hoisted into the last
+    };
+    // a ring of NBUF passes: the loads of pass p + 3 are issued before pass p is folded; passes
+    // past the range read zeros (no memory access) and are weighted 0
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    using B3 = std::integral_constant<int, 3>;
+    issue(B0{}, 0);
+    issue(B1{}, PASS);
+    issue(B2{}, 2 * PASS);
+    for (int p0 = 0; p0 < n; p0 += 4 * PASS) {
+      issue(B3{}, p0 + 3 * PASS);
+      consume(B0{}, p0);
+      issue(B0{}, p0 + 4 * PASS);
+      consume(B1{}, p0 + PASS);
+      issue(B1{}, p0 + 5 * PASS);
+      consume(B2{}, p0 + 2 * PASS);
+      issue(B2{}, p0 + 6 * PASS);
+      consume(B3{}, p0 + 3 * PASS);
     }
-  }
-  if (tid < G) {
-    a.est_md[(slot * G + tid) * 2] = sh_m[tid];
-    a.est_md[(slot * G + tid) * 2 + 1] = sh_den[tid];
+    // den of head h0 + h: the lanes lr = h of the row groups; the numerators over the four row
+    // groups of a wave (lane shuffles), then over the waves through LDS, two heads a round
+    float dh[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) dh[h] = wave_sum(lr == h ? den : 0.f);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[h][j] += __shfl_xor(acc[h][j], 16);
+        acc[h][j] += __shfl_xor(acc[h][j], 32);
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sh[4 + 4 * wv + h] = dh[h];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; hh += 2) {
+      if (lg == 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part[(wv * 2 + u) * kD + 8 * lr + j] = acc[hh + u][j];
+      }
+      __syncthreads();
+      if (tid < 2 * kD) {
+        const int u = tid / kD, d = tid - u * kD, h = h0 + hh + u;
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) sum += part[(ww * 2 + u) * kD + d];
+        if (h < G) a.est_num[(slot * G + h) * kD + d] = sum;
+      }
+      if (hh == 0 && tid < 4 && h0 + tid < G) {
+        float dn = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) dn += sh[4 + 4 * ww + tid];
+        a.est_md[(slot * G + h0 + tid) * 2] = sh[tid];
+        a.est_md[(slot * G + h0 + tid) * 2 + 1] = dn;
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -572,7 +676,7 @@ static_assert(kMaxGroup * kD <= kCandCap, "a KV group's queries are staged in th
 static_assert(kBoundedMaxTopK <= kCandCap && kBoundedMaxTopK <= kSumCap && kBoundedMaxTopK <= kBins,
               "the bounded select lists its zone in LDS");
 template <typename T, int NT, bool EXT>
-__global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_select(DecodeArgs a) {
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ __attribute__((aligned(16))) uint32_t skey[kSumCap];   // tile summaries: score keys
   __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
@@ -589,6 +693,11 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   __shared__ int band_lds[kSmallBand];
   __shared__ double gdd[3 * kMaxGroup];              // gated decode: <q, q'>, |q|^2, |q'|^2 per head
   __shared__ int sh_i[8];
+  static_assert((NT / 64) * 2 * kD <= kSumCap && 4 + 4 * (NT / 64) <= kSumCap, "estimation scratch");
+  if (blockIdx.x >= (unsigned)(a.B * a.Hq)) {      // an estimation workgroup (uniform branch)
+    est_block<T, NT>(a, (int)blockIdx.x - a.B * a.Hq, reinterpret_cast<float*>(skey), reinterpret_cast<float*>(sid));
+    return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x;
@@ -596,7 +705,7 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
   const int g = h / a.G, bg = b * a.Hkv + g;
   // refresh: only the heads whose group attended over its previous zones select again
   if (EXT && a.refresh && a.gate[bg] == 0) return;
-  const int C = a.C, W32 = a.W32, tiles = a.est_tiles_g;
+  const int C = a.C, W32 = a.W32, tiles = a.tiles_g;
   uint32_t* bits = dynl;
   uint32_t* bbits = dynl + W32;
   const uint32_t* keys = a.keys + (size_t)bh * C;
@@ -823,8 +932,8 @@ __global__ __launch_bounds__(NT) void k_select(DecodeArgs a) {
       } else {
         for (int j = wv; j < n_full; j += NT / 64) {
           const int t = tfull[j];
-          for (int r = lane; r < kEstTile; r += 64) {
-            const int c = t * kEstTile + r;
+          for (int r = lane; r < kScoreTile; r += 64) {
+            const int c = t * kScoreTile + r;
             const uint32_t key = c < C ? keys[c] : 0u;
             append(passes(key), key, c);
           }
@@ -1250,32 +1359,6 @@ constexpr int kAttStage = 512;      // row-map entries staged in LDS at a time
 template <typename T> struct AttRows { static constexpr int R = 4; };
 template <> struct AttRows<float> { static constexpr int R = 2; };
 
-// Packed row piece: 8 elements of one row (16 B of bf16 or 32 B of fp32).
-template <typename T> struct Piece;
-template <> struct Piece<uint16_t> {
-  u32x4_t v;
-  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4_t*>(p); }
-  __device__ void zero() { v = u32x4_t{0u, 0u, 0u, 0u}; }
-  __device__ void unpack(float (&o)[8]) const {
-    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
-    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
-    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
-    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
-  }
-};
-template <> struct Piece<float> {
-  u32x4_t v0, v1;
-  __device__ void load(const float* p) {
-    v0 = *reinterpret_cast<const u32x4_t*>(p);
-    v1 = *reinterpret_cast<const u32x4_t*>(p + 4);
-  }
-  __device__ void zero() { v0 = u32x4_t{0u, 0u, 0u, 0u}; v1 = v0; }
-  __device__ void unpack(float (&o)[8]) const {
-    o[0] = __uint_as_float(v0.x); o[1] = __uint_as_float(v0.y); o[2] = __uint_as_float(v0.z); o[3] = __uint_as_float(v0.w);
-    o[4] = __uint_as_float(v1.x); o[5] = __uint_as_float(v1.y); o[6] = __uint_as_float(v1.z); o[7] = __uint_as_float(v1.w);
-  }
-};
-
 // Online softmax state of one lane group.
 template <int G>
 struct OState {
@@ -1615,17 +1698,17 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
   // of them are loaded at once, before the head's all-retrieved flag is known; when it is set
   // the estimation and correction partials are dead (not used, whatever they hold).
   const int all_sel = a.all_sel[bh];
-  const int PE = a.est_tiles_g;
+  const int PE = a.est_blocks_g;
   const int S = a.att_split, items = a.att_items;
   const int P = PE + items;
   auto md_of = [&](int p) -> const float* {
-    if (p < PE) return a.est_md + (((size_t)bg * a.est_tiles_g + p) * G + hi) * 2;
+    if (p < PE) return a.est_md + (((size_t)bg * a.est_blocks_g + p) * G + hi) * 2;
     return a.att_md + ((size_t)bh * items + (p - PE)) * 2;
   };
   const int col = tid & 31, rep = tid >> 5;
   constexpr int RP = NT / 32;
   // numerator columns [4 col, 4 col + 4) of partial p; past P the last partial is read and unused
-  const float* est_col = a.est_num + ((size_t)bg * a.est_tiles_g * G + hi) * kD + 4 * col;
+  const float* est_col = a.est_num + ((size_t)bg * a.est_blocks_g * G + hi) * kD + 4 * col;
   const float* att_col = a.att_num + (size_t)bh * items * kD + 4 * col;
   auto num_col = [&](int p) -> float4 {
     p = min(p, P - 1);
@@ -1735,19 +1818,22 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
 }
 
 // ============================================================================ launcher
-// the select: half-size blocks beyond kSelHeadsPerRound heads; the gated, refresh and bounded
-// modes in their own instantiation, so that the plain decode's kernel carries none of their code
+// the select: one workgroup per query head, followed by the estimation workgroups (none for a
+// refresh, which only selects); half-size blocks beyond kSelHeadsPerRound heads; the gated,
+// refresh and bounded modes in their own instantiation, so that the plain decode's kernel
+// carries none of their code
 template <typename T>
 static void launch_select(const DecodeArgs& a, hipStream_t s) {
   const int BH = a.B * a.Hq;
+  const unsigned grid = (unsigned)BH + (a.refresh ? 0u : (unsigned)(a.B * a.Hkv) * (unsigned)a.est_blocks_g);
   const bool ext = a.gated || a.refresh || a.bounded;
   const size_t lds = (size_t)a.W32 * 8;
   if (BH > kSelHeadsPerRound) {
-    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, true>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);
-    else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, false>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, true>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, false>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
   } else {
-    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, true>), dim3(BH), dim3(kSelThreadsFew), lds, s, a);
-    else hipLaunchKernelGGL((k_select<T, kSelThreadsFew, false>), dim3(BH), dim3(kSelThreadsFew), lds, s, a);
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, true>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsFew, false>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
   }
 }
 
@@ -1755,13 +1841,13 @@ template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
   const bool merge_big = BH <= kSelHeadsPerRound &&
-                         a.est_tiles_g + a.att_items > (kMergeThreadsMany / 32) * kMergeU;
+                         a.est_blocks_g + a.att_items > (kMergeThreadsMany / 32) * kMergeU;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
   // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent, and
   // repeat r may read a copy of the index at other addresses: prof_args)
   for (int r = 0; r < prof_reps(); ++r) {
-    hipLaunchKernelGGL((k_score_est<T, G>), dim3(std::max(1, a.est_tiles_g), BG), dim3(kScoreThreads), 0, s, prof_args(a, r));
+    hipLaunchKernelGGL((k_score<T, G>), dim3(std::max(1, a.tiles_g), BG), dim3(kScoreThreads), 0, s, prof_args(a, r));
   }
   prof_end(WI_STAGE_SCORE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;

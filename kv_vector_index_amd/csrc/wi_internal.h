@@ -12,7 +12,10 @@
 
 namespace wi {
 
-constexpr int kEstTile = 128;       // clusters per estimation work item
+constexpr int kScoreTile = 128;     // clusters per workgroup of the score kernel
+constexpr int kEstTarget = 224;     // estimation workgroups a decode aims for: the CUs the select's
+                                    // B*Hq workgroups leave free at batch 1 (256 - 32), or, when
+constexpr int kEstTargetMany = 512; // the select fills every CU, two workgroups per CU after it
 constexpr int kTileTop = 8;         // best scores per head the score kernel keeps of each tile
 constexpr int kMaxGroup = 8;        // query heads per KV head supported by the decode kernels
 constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
@@ -31,7 +34,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
-  int BG, BH, G, W32, est_tiles_g, att_split, att_items;
+  int BG, BH, G, W32, tiles_g, est_blocks_g, att_split, att_items;
   size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate, off_bnd,
       off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
@@ -54,10 +57,10 @@ struct DecodeArgs {
   int32_t* sel_ids;        // [BH, top_k] or null
   // workspace
   uint32_t* keys;          // [BH, C] order key of the fp32 score <q, mu_c> (0: empty cluster)
-  float* tile_norm;        // [BG, est_tiles_g] largest centroid norm of each 128-cluster tile
-  int32_t* tile_cnt;       // [BG, est_tiles_g] non-empty clusters of each tile
-  uint32_t* tile_top;      // [BH, est_tiles_g, kTileTop] best score keys of each tile, descending
-  int32_t* tile_top_id;    // [BH, est_tiles_g, kTileTop] their cluster ids
+  float* tile_norm;        // [BG, tiles_g] largest centroid norm of each 128-cluster tile
+  int32_t* tile_cnt;       // [BG, tiles_g] non-empty clusters of each tile
+  uint32_t* tile_top;      // [BH, tiles_g, kTileTop] best score keys of each tile, descending
+  int32_t* tile_top_id;    // [BH, tiles_g, kTileTop] their cluster ids
   int32_t* band_ids;       // [BH, C]
   uint64_t* band_key;      // [BH, C]
   int32_t* all_sel;        // [BH] 1 when every non-empty cluster was retrieved
@@ -69,8 +72,8 @@ struct DecodeArgs {
   uint32_t* hl_key;        // [BH, top_k]    order key of the fp32 score
   int32_t* att_bounds;     // [BH, S]        list entry holding the first retrieved token of
                            //                token workgroup s
-  float* est_md;           // [BG, est_tiles_g, G, 2] (m, den)
-  float* est_num;          // [BG, est_tiles_g, G, d]
+  float* est_md;           // [BG, est_blocks_g, G, 2] (m, den) of each estimation workgroup's tiles
+  float* est_num;          // [BG, est_blocks_g, G, d]
   float* att_md;           // [BH, S + Sc, 2]
   float* att_num;          // [BH, S + Sc, d]
   // selection reuse (gated decode; gated == 0 otherwise)
@@ -99,7 +102,7 @@ struct DecodeArgs {
   const void* pool_v;
   void* wb;                // the wave buffer's host state (read by the launcher only)
   // shapes
-  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, est_tiles_g, att_split, att_items;
+  int B, Hq, Hkv, G, C, Nc, NS, top_k, W32, tiles_g, est_blocks_g, att_split, att_items;
   float scale;
 };
 
