@@ -35,6 +35,15 @@ namespace wi {
 
 constexpr int kScoreThreads = 256;
 
+// Workgroups of the attention and merge launches are numbered group-fastest: workgroup j serves
+// query head (j mod BG) G + j / BG, so that consecutive numbers cycle through the KV groups.
+// Workgroups are dispatched to the XCDs round-robin, so with BG a multiple of the 8 XCDs a
+// group's attention workgroups and the merge of its heads share an XCD (and its L2).
+__device__ __forceinline__ int head_of_block(const DecodeArgs& a, int j) {
+  const int BG = a.B * a.Hkv, bg = j % BG;
+  return bg * a.G + j / BG;
+}
+
 // ============================================================================ k_score
 // grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid row (256 B
 // in bf16) is read as four 64-byte pieces by four lanes in one instruction.  Four waves per SIMD
@@ -1550,7 +1559,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
   __shared__ float sh_p[4][16];
   __shared__ int sh_next;
   const int items = a.att_items, S = a.att_split, K = a.top_k;
-  const int bh = blockIdx.x / items, s = blockIdx.x - bh * items;
+  // group-fastest numbering: every workgroup of a KV group's heads runs on the group's XCD
+  const int BG = a.B * a.Hkv, j = blockIdx.x / BG, bgx = blockIdx.x - j * BG;
+  const int hix = j % a.G, s = j / a.G;
+  const int bh = bgx * a.G + hix;
   const int b = bh / a.Hq, h = bh - b * a.Hq, bg = b * a.Hkv + h / a.G;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int NS = a.NS;
@@ -1691,7 +1703,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
   __shared__ float sh_red[32];
   __shared__ float4 sh_acc[NT / 32][32];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
+  const int bh = head_of_block(a, blockIdx.x);
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
   // Partials in order: PE estimation tiles, S token workgroups, PC correction workgroups.  All
