@@ -256,7 +256,7 @@ def bench_build(w, args, dev):
     # index maintenance: the same context one segment shorter, grown by that segment
     append = None
     L = w.seg_len
-    if L > 0 and idx.Nc >= 2 * L and idx.Nc % L == 0:
+    if L > 0 and idx.Nc >= 2 * L and idx.Nc % L == 0 and not args.no_append:
         n0 = w.N - L
         K0, V0 = Kt[:, :, :n0].contiguous(), Vt[:, :, :n0].contiguous()
         prev = wi.build_index(K0, V0, w.sink, w.window, L, w.clusters_per_seg, w.iters, 1)
@@ -317,6 +317,9 @@ def main():
                          "of FRAC of all blocks, eager steps over drifting queries")
     ap.add_argument("--build-only", action="store_true",
                     help="time the index build (segmented spherical k-means) instead of the decode step")
+    ap.add_argument("--no-append", action="store_true",
+                    help="with --build-only: skip timing the index maintenance (one appended segment), so "
+                         "that every k-means kernel launched covers the whole context")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would hold its "

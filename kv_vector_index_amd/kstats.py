@@ -15,6 +15,10 @@
         for the kernels whose name contains NAME it reports the matrix operations the counters
         saw (MOPS x 512 flops) against the algorithmic F flops per launch, the duration, the
         achieved rate against the peak, and the matrix cores' busy share of the busy CU cycles.
+
+    python -m kv_vector_index_amd.kstats build --trace DIR --bench FILE [--cmd "..."] --out FILE.md
+        reads the kernel trace of a `bench.py --build-only` run and lists every library kernel
+        with its calls, average and total duration.
 """
 import argparse
 import csv
@@ -23,7 +27,7 @@ import json
 import os
 import sys
 
-DECODE_KERNELS = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
+DECODE_KERNELS = {"score": "k_score", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
 def _rows(directory: str, suffix: str):
@@ -60,6 +64,16 @@ def _find(table: dict, frag: str):
     return vals, names
 
 
+def kernel_stats(trace_dir: str):
+    """[(kernel name, calls, average us, min us, max us)] from the --stats summary of a trace."""
+    try:
+        rows = list(_rows(trace_dir, "kernel_stats.csv"))
+    except FileNotFoundError:
+        return []
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+             float(r["MaxNs"]) / 1e3) for r in rows]
+
+
 def cmd_times(args):
     with open(args.bench) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
@@ -90,6 +104,35 @@ def cmd_times(args):
     rl = bench["roofline"]
     lines += ["", f"Bench roofline line: kernel {rl['kernel']}, {rl['achieved']:.0f} GB/s, frac {rl['frac']:.3f} "
               f"({rl.get('bytes_per_launch')} bytes / {rl.get('avg_launch_us', float('nan')):.2f} us)."]
+    stats = kernel_stats(args.trace)
+    if stats:
+        lines += ["", "rocprofv3 --stats (every dispatch of the run, decode kernels):", "",
+                  "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for name, calls, avg, mn, mx in stats:
+            if any(frag in name for frag in DECODE_KERNELS.values()):
+                lines.append(f"| `{name}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_build(args):
+    """Every library kernel of an index-build bench run: calls, average and total duration."""
+    with open(args.bench) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    cfg = bench["config"]
+    lines = [f"# Index build kernels, {cfg['workload']} (rocprofv3 kernel trace)", ""]
+    if args.cmd:
+        lines += ["Command (repo root, one MI355X):", "", "    " + args.cmd, ""]
+    lines += [f"Build: {bench['ms_per_step']:.3f} ms per index ({cfg['batch']} x {cfg['kv_heads']} KV heads, "
+              f"{cfg['context']} tokens, segments of {cfg['segment']}, {cfg['clusters_per_segment']} clusters each, "
+              f"{cfg['iterations']} iterations); k_assign {bench['roofline']['achieved']:.0f} TFLOP/s on the "
+              f"algorithmic flops (frac {bench['roofline']['frac']:.3f} of {bench['roofline']['peak']:.0f}).", "",
+              "| kernel | calls | average us | total us | share of the library's kernel time |", "|---|---|---|---|---|"]
+    stats = [s for s in kernel_stats(args.trace) if s[0].startswith(("void wi::", "wi::"))]
+    total = sum(c * a for _, c, a, _, _ in stats)
+    for name, calls, avg, _, _ in stats:
+        lines.append(f"| `{name}` | {calls} | {avg:.2f} | {calls * avg:.1f} | {calls * avg / total:.3f} |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -158,8 +201,13 @@ def main(argv=None):
     m.add_argument("--peak-tflops", type=float, required=True)
     m.add_argument("--cmd", action="append", default=[])
     m.add_argument("--out", required=True)
+    bl = sub.add_parser("build")
+    bl.add_argument("--trace", required=True)
+    bl.add_argument("--bench", required=True)
+    bl.add_argument("--cmd", default="")
+    bl.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    return cmd_times(args) if args.cmd_name == "times" else cmd_mfma(args)
+    return {"times": cmd_times, "mfma": cmd_mfma, "build": cmd_build}[args.cmd_name](args)
 
 
 if __name__ == "__main__":

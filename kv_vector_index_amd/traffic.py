@@ -23,7 +23,7 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DECODE_KERNELS = {"score": "k_score_est", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
+DECODE_KERNELS = {"score": "k_score", "select": "k_select", "attend": "k_attend", "merge": "k_merge"}
 
 
 DECODE_SOURCES = ("wi_decode.hip", "wi_device.h", "wi_internal.h", "wi_api.hip")
@@ -115,6 +115,36 @@ def cmd_record(args):
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out["hbm_bytes_per_launch"]))
+    if args.md:
+        write_md(out, args)
+
+
+def write_md(rec: dict, args):
+    """A markdown summary of a record: measured HBM bytes per launch of each decode kernel beside
+    the algorithmic bytes the bench run of the same workload reported."""
+    algo = {}
+    if args.bench:
+        with open(args.bench) as f:
+            algo = json.loads(f.read().strip().splitlines()[-1]).get("kernel_algorithmic_bytes", {})
+    cal = rec["calibration"]
+    lines = [f"# HBM traffic of the decode kernels, {rec['workload']} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", ""]
+    if args.cmd:
+        lines += ["Commands (repo root, one MI355X):", ""] + ["    " + c for c in args.cmd] + [""]
+    lines += [f"Decode kernel sources sha256/16: {rec['kernel_source_sha256_16']}; index copies cycled: "
+              f"{rec['instances']}.", "",
+              f"Calibration: `{cal['kernel']}` copying {cal['bytes']} bytes reads {cal['fetch_kib']:.0f} KiB "
+              f"(FETCH_SIZE) and writes {cal['write_kib']:.0f} KiB (WRITE_SIZE) per dispatch: factors "
+              f"{cal['fetch_factor']:.4f} and {cal['write_factor']:.4f} turn the counters into bytes.", "",
+              "| kernel | dispatches | FETCH bytes | WRITE bytes | HBM bytes / launch | algorithmic bytes / launch | "
+              "HBM / algorithmic |", "|---|---|---|---|---|---|---|"]
+    for key, r in rec["raw"].items():
+        tot = rec["hbm_bytes_per_launch"][key]
+        a = algo.get(key)
+        ratio = f"{tot / a:.3f}" if a else "-"
+        lines.append(f"| {key} | {r['dispatches']} | {r['fetch_bytes']:.4g} | {r['write_bytes']:.4g} | {tot:.4g} | "
+                     f"{a if a is not None else '-'} | {ratio} |")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def main(argv=None):
@@ -130,6 +160,9 @@ def main(argv=None):
     r.add_argument("--workload", required=True, help="the bench workload the decode run measured")
     r.add_argument("--instances", type=int, required=True, help="index copies that bench run cycled through")
     r.add_argument("--out", required=True)
+    r.add_argument("--md", default="", help="also write a markdown summary here")
+    r.add_argument("--bench", default="", help="a bench.py JSON line of the same workload (algorithmic bytes)")
+    r.add_argument("--cmd", action="append", default=[], help="commands to list in the summary")
     args = ap.parse_args(argv)
     return cmd_copy(args) if args.cmd == "copy" else cmd_record(args)
 
