@@ -432,14 +432,15 @@ def main():
         bounds = [bound] + [tuple(t.clone() for t in bound) for _ in range(len(insts) - 1)]
         k_used = torch.empty((w.B, w.Hq), dtype=torch.int32, device=dev)
         err_b = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        n_exact = torch.zeros(1, dtype=torch.int32, device=dev)     # heads that decided in fp64
 
         def step(i):
             j = i % len(insts)
             r_, vn_, vm_ = bounds[j]
             wi.wi_decode_bounded(p, views[j], r_.data_ptr(), vn_.data_ptr(), vm_.data_ptr(),
                                  qs[i % len(qs)].data_ptr(), args.bounded, out.data_ptr(), lse.data_ptr(),
-                                 sel.data_ptr(), k_used.data_ptr(), err_b.data_ptr(), ws.data_ptr(), ws_bytes,
-                                 torch.cuda.current_stream().cuda_stream)
+                                 sel.data_ptr(), k_used.data_ptr(), err_b.data_ptr(), n_exact.data_ptr(),
+                                 ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
 
     if args.gated is not None:
         # step i reads the zones step i-1 wrote (two buffers: sel_prev and sel_ids may not alias)
@@ -476,7 +477,8 @@ def main():
         eb = err_b.float()
         bounded_info.update({"k_mean": float(kk.mean()), "k_min": int(kk.min()), "k_max": int(kk.max()),
                              "top_k_cap": w.top_k, "err_bound_mean": float(eb.mean()),
-                             "err_bound_max": float(eb.max())})
+                             "err_bound_max": float(eb.max()),
+                             "fp64_decided_head_frac": int(n_exact.item()) / max(1, args.warmup * w.B * w.Hq)})
     off_np = idx.offsets.cpu().numpy()
     per_bytes, union_rows, corr_bytes = algorithmic_bytes(w, off_np, sel_np)
     step_bytes = sum(per_bytes.values())

@@ -241,9 +241,13 @@ wi_status wi_bound_data(const wi_decode_params *p, const wi_index_view *idx, flo
  * u the relative rounding bound of the stored value sums (2^-8 + 2^-23 for bf16, 2^-24 for
  * fp32).  A zone made of the k first non-empty clusters in the order (-sigma_c, c) bounds
  * |out - dense attention| by A(k) = (sum of err_c outside the zone) / (sum of every lo_c).  The
- * zone is the smallest k in [0, min(top_k, #non-empty)] with A(k) <= eps (the cap if none); its
- * clusters are then the top k exactly as wi_decode selects them.  The decisions are taken on
- * fp32 scores, so a k whose A(k) lies within fp32 rounding of eps may come out one off.
+ * zone is the smallest k in [0, min(top_k, #non-empty)] with A(k) <= eps (the cap if none), with
+ * every term and A(k) taken on canonical fp64 scores; its clusters are then the top k exactly as
+ * wi_decode selects them.  Each head first decides on fp32 scores and terms and keeps that
+ * decision when rigorous bounds on their rounding (and on the clusters whose fp32 order may
+ * differ from the canonical one) show A(k) <= eps and A(k - 1) > eps; otherwise it recomputes
+ * every non-empty cluster's terms in fp64 from canonical scores and decides on those.  The size
+ * is therefore the fp64 decision unless some A(j) lies within fp64 rounding of eps.
  *   radius, vnorm [B,Hkv,C], vmax [B,Hkv]  float  from wi_bound_data for this index
  *   eps                                     >= 0 (inf: the smallest zone, k = 0)
  *   sel_ids   [B,Hq,top_k] int32  the zone, ascending, -1 padded (nullable)
@@ -251,12 +255,15 @@ wi_status wi_bound_data(const wi_decode_params *p, const wi_index_view *idx, flo
  *   err_bound [B,Hq]       float  the bound after attention (nullable): the same sums outside
  *             the zone with |out| in place of (1 + u) V_all and, in the denominator, the exact
  *             part's total plus the estimated clusters' lo_c; 0 when nothing is estimated
+ *   n_exact   [1]          uint32 device counter (nullable), incremented once for every head
+ *             that decided in fp64; the caller zeroes it
  * Everything else, and the errors, as wi_decode; also WI_ERR_INVALID_ARG for a null radius,
  * vnorm (C > 0) or vmax, or eps < 0 or NaN, and WI_ERR_UNSUPPORTED for top_k > 2048. */
 wi_status wi_decode_bounded(const wi_decode_params *p, const wi_index_view *idx, const float *radius,
                             const float *vnorm, const float *vmax, const void *q, float eps,
                             float *out, float *lse, int32_t *sel_ids, int32_t *k_used,
-                            float *err_bound, void *workspace, size_t ws_bytes, void *stream);
+                            float *err_bound, uint32_t *n_exact, void *workspace, size_t ws_bytes,
+                            void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * Wave buffer (RetroInfer technical summary, section 2.B; Arabic summary, section 2.b): decode

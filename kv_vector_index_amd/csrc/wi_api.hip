@@ -314,6 +314,7 @@ struct Bounded {
   float eps;
   int32_t* k_used;
   float* err_bound;
+  uint32_t* n_exact;
 };
 
 struct Gate {
@@ -417,7 +418,7 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
   }
   if (bnd) {
     a.bounded = 1; a.radius = bnd->radius; a.vnorm = bnd->vnorm; a.vmax = bnd->vmax; a.eps = bnd->eps;
-    a.k_used = bnd->k_used; a.err_bound = bnd->err_bound;
+    a.k_used = bnd->k_used; a.err_bound = bnd->err_bound; a.bnd_fallback = bnd->n_exact;
     a.u = p->dtype == WI_BF16 ? 0x1.0002p-8f : 0x1p-24f;     // 2^-8 + 2^-23 for bfloat16 sums
   }
   return check_hip(wi::launch_decode(*p, a, st),
@@ -460,14 +461,14 @@ wi_status wi_decode_gated(const wi_decode_params* p, const wi_index_view* idx, c
 
 wi_status wi_decode_bounded(const wi_decode_params* p, const wi_index_view* idx, const float* radius,
                             const float* vnorm, const float* vmax, const void* q, float eps, float* out, float* lse,
-                            int32_t* sel_ids, int32_t* k_used, float* err_bound, void* workspace, size_t ws_bytes,
-                            void* stream) {
+                            int32_t* sel_ids, int32_t* k_used, float* err_bound, uint32_t* n_exact,
+                            void* workspace, size_t ws_bytes, void* stream) {
   if (p && p->C > 0 && (!radius || !vnorm)) return fail(WI_ERR_INVALID_ARG, "radius and vnorm must be non-null");
   if (!vmax) return fail(WI_ERR_INVALID_ARG, "vmax must be non-null");
   if (!(eps >= 0.f)) return fail(WI_ERR_INVALID_ARG, "eps must be >= 0 (got %g)", (double)eps);
   if (p && p->top_k > wi::kBoundedMaxTopK)
     return fail(WI_ERR_UNSUPPORTED, "top_k %d > %d for bounded zone sizing", p->top_k, wi::kBoundedMaxTopK);
-  const Bounded bnd{radius, vnorm, vmax, eps, k_used, err_bound};
+  const Bounded bnd{radius, vnorm, vmax, eps, k_used, err_bound, n_exact};
   return decode_common(p, idx, q, out, lse, sel_ids, workspace, ws_bytes, stream, nullptr, &bnd);
 }
 

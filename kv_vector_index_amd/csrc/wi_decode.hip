@@ -644,6 +644,118 @@ __device__ uint32_t wave_kth_above(int n, int k, uint32_t L, Get get, uint32_t* 
   return (uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((unsigned long long)hit) - 1);
 }
 
+// ---- ranking and fp64 reductions of the accuracy-bounded select
+// A key of the canonical order of the bounded zone: (-sigma, id) as (order key of sigma, id).
+struct CanonKey {
+  uint64_t k;
+  int id;
+};
+__device__ __forceinline__ bool canon_gt(const CanonKey& x, const CanonKey& y) {
+  return x.k > y.k || (x.k == y.k && x.id < y.id);
+}
+__device__ __forceinline__ uint64_t bcast_lane(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ CanonKey bcast_lane(const CanonKey& v, int l) {
+  return {bcast_lane(v.k, l), __builtin_amdgcn_readlane(v.id, l)};
+}
+
+// Ranks in descending order (under gt, a strict total order; the keys are distinct) of n <=
+// EPT * NT keys, thread t holding keys e * NT + t.  Every run of 64 consecutive keys belongs to
+// one wave: its keys are ranked among themselves from lane broadcasts and stored in that order
+// through put(position, key); a key's rank is its rank in its run plus, for every other run, the
+// number of keys above it, found by a binary search through get(position).  O(n log 64) LDS reads
+// per key against O(n) for direct counting.
+template <int NT, int EPT, typename K, typename Gt, typename Put, typename Get>
+__device__ __forceinline__ void block_rank_desc(int n, const K (&key)[EPT], int (&rank)[EPT], Gt gt,
+                                                Put put, Get get) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int rr[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = e * NT + tid, base = i - lane;
+    int r = 0;
+    if (base < n) {                                  // uniform over the wave
+      const int len = min(64, n - base);
+      for (int l = 0; l < len; ++l) r += gt(bcast_lane(key[e], l), key[e]) ? 1 : 0;
+      if (i < n) put(base + r, key[e]);
+    }
+    rr[e] = r;
+  }
+  __syncthreads();
+  const int runs = (n + 63) / 64;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = e * NT + tid;
+    rank[e] = 0;
+    if (i >= n) continue;
+    const int own = i >> 6;
+    int tot = rr[e];
+    for (int r = 0; r < runs; ++r) {
+      if (r == own) continue;
+      const int len = min(64, n - 64 * r);
+      int pos = 0;                                   // keys [0, pos) of run r are above key[e]
+#pragma unroll
+      for (int st = 32; st >= 1; st >>= 1) {
+        const int q = pos + st - 1;
+        if (q < len && gt(get(64 * r + q), key[e])) pos += st;
+      }
+      if (pos < len && gt(get(64 * r + pos), key[e])) ++pos;
+      tot += pos;
+    }
+    rank[e] = tot;
+  }
+  __syncthreads();
+}
+
+// Block-wide exclusive prefix sum of any arithmetic type (lane shifts, then the wave totals in
+// LDS scratch of NT / 64 entries); *total receives the block sum.
+template <int NT, typename V>
+__device__ __forceinline__ V block_exclusive_scan_any(V v, V* scratch, V* total) {
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  V inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const V o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  V before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < nw; ++i) {
+    const V t = scratch[i];
+    before += i < w ? t : V(0);
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + inc - v;
+}
+template <int NT>
+__device__ __forceinline__ double block_sum_d(double v, double* scratch) {
+  double tot;
+  block_exclusive_scan_any<NT, double>(v, scratch, &tot);
+  return tot;
+}
+template <int NT>
+__device__ __forceinline__ double block_max_d(double v, double* scratch) {
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmax(v, __shfl_xor(v, m));
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < nw; ++i) r = fmax(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
 // Canonical fp64 score of the query (fp64 copy in LDS) and one centroid row: exact products
 // summed in ascending coordinate order, no contraction.  The row is fetched in four batches.
 template <typename T>
@@ -667,6 +779,120 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
     }
   }
   return acc;
+}
+
+// canonical_score_row with 8 coordinates in flight instead of 32: fewer registers, for the
+// out-of-line fp64 decision below (the same products and the same order of additions).
+template <typename T>
+__device__ __forceinline__ double canonical_score_row_lean(const double* qd, const T* row) {
+#pragma clang fp contract(off)
+  double acc = 0.0;
+#pragma unroll 1
+  for (int j0 = 0; j0 < kD; j0 += 8) {
+    float x[8];
+    St<T>::load8(row + j0, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = acc + qd[j0 + e] * (double)x[e];
+  }
+  return acc;
+}
+
+// The zone size of the accuracy-bounded select decided in fp64, when the fp32 decision could not
+// be certified: every non-empty cluster's err and lo from its canonical score, term by term as the
+// bound defines them; the selected list (the canonical top k_eff, ids zi[0 .. k_eff)) ranked by
+// (-sigma, id); and the smallest j with A(j) = (err summed after the first j) / (sum of every lo)
+// <= eps, the cap k_eff when none.  Leaves the first j of the canonical order in `bits` (which
+// holds the list on entry) and returns j.  zo (k_eff 8-byte slots) and run_ids (k_eff ints) are
+// LDS scratch; every thread of the block calls it.
+template <typename T, int NT>
+__device__ __attribute__((noinline)) int bounded_zone_fp64(
+    const uint32_t* keys, const T* mu, const int32_t* szg, const float* rdg, const float* vng, double vall,
+    double sc, double uu, double eps, int C, int W32, int k_eff, const double* qd, const int* zi, uint64_t* zo,
+    int* run_ids, uint32_t* bits, double* dscr, float* fred) {
+#pragma clang fp contract(off)
+  constexpr int EPT = kBoundedMaxTopK / NT;
+  const int tid = threadIdx.x;
+  double qn2 = 0.0;
+  for (int j = 0; j < kD; ++j) qn2 = qn2 + qd[j] * qd[j];
+  const double qn = sqrt(qn2);
+  double s64[EPT];
+  CanonKey ck[EPT];
+  double smax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = e * NT + tid;
+    s64[e] = 0.0;
+    ck[e] = CanonKey{0ull, 0x7fffffff};
+    if (p < k_eff) {
+      s64[e] = canonical_score_row_lean<T>(qd, mu + (size_t)zi[p] * kD);
+      ck[e] = CanonKey{f64_order_key(s64[e]), zi[p]};
+      smax = fmax(smax, s64[e]);
+    }
+  }
+  const double mstar = sc * block_max_d<NT>(smax, dscr);
+  auto terms64 = [&](double s, int c, double& err, double& lo) {
+#pragma clang fp contract(off)
+    const double x = sc * qn * (double)rdg[c];
+    const double w = (double)szg[c] * exp(sc * s - mstar);
+    const double av = w * expm1(x);
+    err = av * ((double)vng[c] + (1.0 + uu) * vall) + w * uu * (double)vng[c];
+    lo = w * exp(-x);
+  };
+  double tout = 0.0, dsum = 0.0;
+  for (int c = tid; c < C; c += NT) {
+    if (keys[c] == 0u || ((bits[c >> 5] >> (c & 31)) & 1u)) continue;
+    double e1, l1;
+    terms64(canonical_score_row_lean<T>(qd, mu + (size_t)c * kD), c, e1, l1);
+    tout = tout + e1;
+    dsum = dsum + l1;
+  }
+  double el[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    el[e] = 0.0;
+    if (e * NT + tid < k_eff) {
+      double l1;
+      terms64(s64[e], ck[e].id, el[e], l1);
+      dsum = dsum + l1;
+    }
+  }
+  const double t_out = block_sum_d<NT>(tout, dscr);
+  const double d_all = block_sum_d<NT>(dsum, dscr);
+  int rk[EPT];
+  block_rank_desc<NT, EPT>(k_eff, ck, rk, [](const CanonKey& x, const CanonKey& y) { return canon_gt(x, y); },
+                           [&](int p, const CanonKey& k) { zo[p] = k.k; run_ids[p] = k.id; },
+                           [&](int p) { return CanonKey{zo[p], run_ids[p]}; });
+  double* ez = reinterpret_cast<double*>(zo);           // err in canonical order
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) if (e * NT + tid < k_eff) ez[rk[e]] = el[e];
+  __syncthreads();
+  // T(j) = t_out + the err of canonical positions j .. k_eff - 1 (thread t: positions
+  // k_eff - 1 - (t EPT + e)), then A(j) = T(j) / d_all
+  double dl[EPT], drun = 0.0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = k_eff - 1 - (tid * EPT + e);
+    drun = drun + (p >= 0 ? ez[p] : 0.0);
+    dl[e] = drun;
+  }
+  double dtot;
+  const double dbefore = block_exclusive_scan_any<NT, double>(drun, dscr, &dtot);
+  int kb = k_eff;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = k_eff - 1 - (tid * EPT + e);
+    if (p >= 0 && (t_out + (dbefore + dl[e])) / d_all <= eps) kb = min(kb, p);
+  }
+  const int kz = (int)-block_max<NT>(-(float)kb, fred);
+  if (kz < k_eff) {
+    for (int w = tid; w < W32; w += NT) bits[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (e * NT + tid < k_eff && rk[e] < kz) { const int c = ck[e].id; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+    __syncthreads();
+  }
+  return kz;
 }
 
 // Per query head: the retrieval zone is the k_eff = min(top_k, #non-empty) non-empty clusters
@@ -701,6 +927,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ double qd[kD];
   __shared__ int band_lds[kSmallBand];
   __shared__ double gdd[3 * kMaxGroup];              // gated decode: <q, q'>, |q|^2, |q'|^2 per head
+  __shared__ double dscr[16];                        // bounded decode: fp64 reduction scratch
   __shared__ int sh_i[8];
   static_assert((NT / 64) * 2 * kD <= kSumCap && 4 + 4 * (NT / 64) <= kSumCap, "estimation scratch");
   if (blockIdx.x >= (unsigned)(a.B * a.Hq)) {      // an estimation workgroup (uniform branch)
@@ -1099,15 +1326,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
   int k_zone = reuse ? n_reused_ne : k_eff;
   if (EXT && a.bounded) {
-    // the k_eff selected clusters, ascending id, with score keys and error terms (the summary,
-    // candidate, histogram and publish arrays are free until publishing, which rebuilds them)
-    // zo: (score key, id) packed so that a larger value comes first in the order (-score, id)
+    // the k_eff selected clusters (the canonical top k_eff) with score keys and error terms (the
+    // summary, candidate, histogram and publish arrays are free until publishing, which rebuilds
+    // them); zo packs (score key, id) so that a larger value comes first in the order (-score, id)
     uint64_t* zo = reinterpret_cast<uint64_t*>(skey);
     int* zi = sid;
     float* ze = reinterpret_cast<float*>(rl_off);      // err
     float* zl = reinterpret_cast<float*>(ckey);        // lo
     float* za = reinterpret_cast<float*>(cidl);        // a
     float* zv = reinterpret_cast<float*>(hist);        // a V_c + w u V_c
+    float* zt = reinterpret_cast<float*>(rl_sz);       // T(j): err summed over the clusters after the first j
     const int32_t* szg = a.sizes + (size_t)bg * C;
     const float* rdg = a.radius + (size_t)bg * C;
     const float* vng = a.vnorm + (size_t)bg * C;
@@ -1124,6 +1352,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       }
     }
     __syncthreads();
+    float rmax = 0.f;                                  // largest radius of a non-empty cluster
     // the list's terms: every load of an entry issued before the first is used
     for (int i0 = 0; i0 < k_eff; i0 += 2 * NT) {
       int c[2];
@@ -1141,6 +1370,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           const BTerms t = bound_terms(kk[u], nn[u], rr[u], vv[u]);
           zo[i] = ((uint64_t)kk[u] << 32) | (uint32_t)(0xffffffffu - (uint32_t)c[u]);
           ze[i] = t.err; zl[i] = t.lo; za[i] = t.ea; zv[i] = t.eav;
+          rmax = fmaxf(rmax, rr[u]);
         }
       }
     }
@@ -1162,71 +1392,136 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         if (live) {
           const BTerms t = bound_terms(kk[i], nn[i], rr[i], vv[i]);
           so += t.err; slo += t.lo; sa_o += t.ea; sv_o += t.eav;
+          rmax = fmaxf(rmax, rr[i]);
         }
       }
     }
     const float e_out = block_sum<NT>(so, fred);       // includes barriers: the list is visible
-    float le = 0.f, ll = 0.f;
-    for (int i = tid; i < k_eff; i += NT) { le += ze[i]; ll += zl[i]; }
-    const float b_err = e_out + block_sum<NT>(le, fred);
+    float ll = 0.f;
+    for (int i = tid; i < k_eff; i += NT) ll += zl[i];
     const float b_lo = block_sum<NT>(slo, fred) + block_sum<NT>(ll, fred);
-    // k = the smallest zone size whose first clusters (in the order (-score, id)) leave an error
-    // sum <= eps * sum lo: for each entry, its rank and the error of the entries after it come
-    // from one pass over the list
+    const float r_hi = block_max<NT>(rmax, fred);
     const float lim = a.eps * b_lo;
-    int kb = b_err <= lim ? 0 : k_eff;
-    for (int i = tid; i < k_eff; i += NT) {
-      const uint64_t oi = zo[i];
-      int rank = 0;
-      float after = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < k_eff; ++j) {
-        const uint64_t oj = zo[j];
-        const float ej = ze[j];
-        rank += oj > oi ? 1 : 0;
-        after += oj < oi ? ej : 0.f;
+    constexpr int EPT = kBoundedMaxTopK / NT;           // list entries per thread
+    static_assert(EPT * NT == kBoundedMaxTopK && 2 * kBoundedMaxTopK <= kSumCap, "the bounded list's layout");
+    // kf = the smallest zone size j whose first clusters in the order (-fp32 score, id) leave an
+    // error sum T(j) <= eps * (sum of every lo); the cap k_eff when none does
+    int kf = k_eff;
+    if (k_eff > 0) {
+      // ---- the list sorted: ranks (runs of 64 ranked in their waves, merged by binary search),
+      // then every array permuted to them through registers
+      uint64_t kv[EPT];
+      int rk[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) { const int i = e * NT + tid; kv[e] = i < k_eff ? zo[i] : 0ull; }
+      block_rank_desc<NT, EPT>(k_eff, kv, rk, [](uint64_t x, uint64_t y) { return x > y; },
+                               [&](int p, uint64_t k) { zo[p] = k; }, [&](int p) { return zo[p]; });
+      float pe[EPT], pl[EPT], pa[EPT], pv[EPT];
+      int pc[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = min(e * NT + tid, k_eff - 1);
+        pe[e] = ze[i]; pl[e] = zl[i]; pa[e] = za[i]; pv[e] = zv[i]; pc[e] = zi[i];
       }
-      rl_sz[i] = rank;
-      if (e_out + after <= lim) kb = min(kb, rank + 1);
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        if (e * NT + tid < k_eff) {
+          const int r = rk[e];
+          zo[r] = kv[e]; ze[r] = pe[e]; zl[r] = pl[e]; za[r] = pa[e]; zv[r] = pv[e]; zi[r] = pc[e];
+        }
+      }
+      __syncthreads();
+      // ---- T(j) = e_out + the err of positions j .. k_eff - 1: thread t sums positions
+      // k_eff - 1 - (t EPT + e), e < EPT, and an exclusive scan adds those of the threads before
+      float loc[EPT], run = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int p = k_eff - 1 - (tid * EPT + e);
+        run += p >= 0 ? ze[p] : 0.f;
+        loc[e] = run;
+      }
+      float tot;
+      const float before = block_exclusive_scan_any<NT, float>(run, fred, &tot);
+      int kb = k_eff;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int p = k_eff - 1 - (tid * EPT + e);
+        if (p >= 0) {
+          const float t = e_out + (before + loc[e]);
+          zt[p] = t;
+          if (t <= lim) kb = min(kb, p);
+        }
+      }
+      kf = (int)-block_max<NT>(-(float)kb, fred);      // includes barriers: zt is visible
     }
-    k_zone = (int)-block_max<NT>(-(float)kb, fred);
-    if (k_zone < k_eff) {
-      // the canonical top k_zone of the list: in above t + 2 delta, out below t - 2 delta, the
-      // band between them ranked by (-canonical score, id); t = the k_zone-th fp32 score
-      for (int w = tid; w < W32; w += NT) bits[w] = 0u;
-      if (tid == 0) { sh_i[7] = 0; sh_i[2] = 0; }
-      __syncthreads();
-      if (k_zone > 0) {
-        for (int i = tid; i < k_eff; i += NT)
-          if (rl_sz[i] == k_zone - 1) sh_i[7] = i;
-        __syncthreads();
-        const double that = (double)f32_from_order_key((uint32_t)(zo[sh_i[7]] >> 32));
-        const double hi = that + 2.0 * delta, lo = that - 2.0 * delta;
-        int nin = 0;
-        int32_t* band = a.band_ids + (size_t)bh * C;
-        for (int i = tid; i < k_eff; i += NT) {
-          const double v = (double)f32_from_order_key((uint32_t)(zo[i] >> 32));
-          if (v > hi) { const int c = zi[i]; atomicOr(&bits[c >> 5], 1u << (c & 31)); ++nin; }
-          else if (v >= lo) band[atomicAdd(&sh_i[2], 1)] = zi[i];
-        }
-        const int need = k_zone - block_isum<NT>(nin, iscr);     // includes a barrier
-        const int n_band = sh_i[2];
-        uint64_t* bkey = a.band_key + (size_t)bh * C;
-        for (int i = tid; i < n_band; i += NT)
-          bkey[i] = f64_order_key(canonical_score_row<T>(qd, mu + (size_t)band[i] * kD));
-        __syncthreads();
-        for (int i = tid; i < n_band; i += NT) {
-          const uint64_t ki = bkey[i];
-          const int ci = band[i];
-          int rank = 0;
-          for (int j = 0; j < n_band; ++j) {
-            const uint64_t kj = bkey[j];
-            rank += (kj > ki || (kj == ki && band[j] < ci)) ? 1 : 0;
-          }
-          if (rank < need) atomicOr(&bits[ci >> 5], 1u << (ci & 31));
-        }
+    // ---- certification: kf is the decision the canonical fp64 terms give when A(kf) <= eps and
+    // A(kf - 1) > eps hold for every value within the fp32 error of the terms and sums.  The fp32
+    // order's prefixes are the canonical ones up to clusters whose fp32 scores lie within 2 delta
+    // of the boundary: the canonical first j hold positions [0, L_j) and lie within [0, U_j), so
+    // T(U_j) <= T_canonical(j) <= T(L_j).  A certified A(kf) <= eps through T(L_kf) makes
+    // T(L_kf) <= lim, hence L_kf = kf by the minimality of kf: no near tie straddles the
+    // boundary, and the zone is the first kf positions.
+    bool cert = true;
+    if (k_eff > 0) {
+      auto sc_at = [&](int p) { return (double)f32_from_order_key((uint32_t)(zo[p] >> 32)); };
+      auto t_at = [&](int p) { return p < k_eff ? (double)zt[p] : (double)e_out; };
+      auto len_L = [&](int j) {
+        if (j <= 0 || j >= k_eff) return j;
+        const double s = sc_at(j) + 2.0 * delta;
+        int L = j;
+        while (L > 0 && sc_at(L - 1) <= s) --L;
+        return L;
+      };
+      auto len_U = [&](int j) {
+        if (j <= 0 || j >= k_eff) return j;
+        const double s = sc_at(j - 1) - 2.0 * delta;
+        int U = j;
+        while (U < k_eff && sc_at(U) >= s) ++U;
+        return U;
+      };
+      // relative error budgets (u = 2^-24): the weights' exponent is off by scale delta from the
+      // scores plus the roundings of scale s - m* and of the exponential's argument; x = scale |q|
+      // r carries |q|'s rounding into expm1 and exp(-x); each term adds a few roundings, and each
+      // sum at most one per addition on its longest path.  Doubled, plus an absolute allowance for
+      // terms that underflow.
+      const double u32 = 5.9604644775390625e-08, sc = (double)a.scale;
+      const double amax = sc * ((double)qv * (1.0 + 1.0 / 1024) * (double)mxn * (1.0 + 1.0 / 1024) + delta);
+      const double rw = expm1(sc * delta + 6.0 * u32 * amax + 4.0 * u32) + 2.0 * u32;
+      const double xh = sc * (double)qv * (double)r_hi * (1.0 + 1.0 / 1024);
+      const double rx = (kD + 8) * u32;
+      const double depth = (double)(KPT + 2 * EPT + 64) * u32;
+      const double rT = 2.0 * (rw + (1.0 + xh) * rx + 12.0 * u32 + depth);
+      const double rD = 2.0 * (rw + xh * rx + 2.0 * u32 * xh + 6.0 * u32 + depth);
+      const double tiny = (double)n_ne * 0x1p-100;
+      const double tauT = tiny * (exp(fmin(xh, 80.0)) + 1.0) * (1.0 + 3.0 * (double)b_vall);
+      const double Dlo = (double)b_lo * (1.0 - rD) - tiny, Dhi = (double)b_lo * (1.0 + rD) + tiny;
+      const double eps = (double)a.eps;
+      cert = xh < 80.0 && Dlo > 0.0 && isfinite((double)b_lo) && isfinite((double)e_out);
+      if (cert && kf < k_eff) {                       // A(kf) <= eps
+        const double hiA = (t_at(len_L(kf)) * (1.0 + rT) + tauT) / Dlo;
+        cert = isfinite(hiA) && hiA * (1.0 + 1e-9) < eps;
       }
-      __syncthreads();
+      if (cert && kf > 0) {                           // A(kf - 1) > eps
+        const double loA = (t_at(len_U(kf - 1)) * (1.0 - rT) - tauT) / Dhi;
+        cert = loA * (1.0 - 1e-9) > eps;
+      }
+    }
+    if (cert) {
+      if (kf < k_eff) {
+        for (int w = tid; w < W32; w += NT) bits[w] = 0u;
+        __syncthreads();
+        for (int p = tid; p < kf; p += NT) { const int c = zi[p]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+        __syncthreads();
+      }
+      k_zone = kf;
+    } else {
+      // ---- undecided in fp32: the decision in fp64 (out of line, so that its registers do not
+      // weigh on the rest of the select)
+      k_zone = bounded_zone_fp64<T, NT>(keys, mu, szg, rdg, vng, (double)b_vall, (double)a.scale, (double)a.u,
+                                        (double)a.eps, C, W32, k_eff, qd, zi, zo, sid + kBoundedMaxTopK, bits,
+                                        dscr, fred);
+      if (tid == 0 && a.bnd_fallback) atomicAdd(a.bnd_fallback, 1u);
     }
     // sums over the estimated clusters (outside the zone) for the bound after attention: the
     // clusters outside the list, plus the list entries the zone left out

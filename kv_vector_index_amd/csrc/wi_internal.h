@@ -92,6 +92,7 @@ struct DecodeArgs {
   float u;                 // relative rounding bound of the stored value sums
   int bounded;
   int32_t* k_used;         // [BH] or null: zone size chosen
+  uint32_t* bnd_fallback;  // [1] or null: incremented once per head whose zone size was decided in fp64
   float* err_bound;        // [BH] or null: bound on |out - dense attention|
   float* bnd;              // [BH, 4] workspace: m*, sum a, sum (a V + w u V), sum lo over the estimation zone
   // wave buffer (paged == 0 otherwise): k_perm / v_perm are then the copies in host memory

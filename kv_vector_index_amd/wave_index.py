@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
                                         vp]
         L.wi_bound_data.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp]
         L.wi_decode_bounded.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(IndexView), vp, vp, vp, vp,
-                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]
+                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.wi_wavebuf_device_bytes.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_size_t)]
         L.wi_wavebuf_create.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_int32, ctypes.c_int32, vp, sz, vp,
@@ -190,11 +190,11 @@ def wi_bound_data(p: DecodeParams, view: IndexView, radius_ptr: Optional[int], v
 
 def wi_decode_bounded(p: DecodeParams, view: IndexView, radius_ptr: Optional[int], vnorm_ptr: Optional[int],
                       vmax_ptr: int, q_ptr: int, eps: float, out_ptr: int, lse_ptr: Optional[int],
-                      sel_ptr: Optional[int], k_ptr: Optional[int], err_ptr: Optional[int], ws_ptr: int,
-                      ws_bytes: int, stream: int) -> int:
+                      sel_ptr: Optional[int], k_ptr: Optional[int], err_ptr: Optional[int],
+                      n_exact_ptr: Optional[int], ws_ptr: int, ws_bytes: int, stream: int) -> int:
     return _check(lib().wi_decode_bounded(ctypes.byref(p), ctypes.byref(view), radius_ptr, vnorm_ptr, vmax_ptr,
-                                          q_ptr, eps, out_ptr, lse_ptr, sel_ptr, k_ptr, err_ptr, ws_ptr, ws_bytes,
-                                          stream))
+                                          q_ptr, eps, out_ptr, lse_ptr, sel_ptr, k_ptr, err_ptr, n_exact_ptr, ws_ptr,
+                                          ws_bytes, stream))
 
 
 def wi_wavebuf_device_bytes(p: DecodeParams, cache_blocks: int, exec_blocks: int) -> int:
@@ -435,9 +435,10 @@ def bound_data(index: Index, B: int, Hkv: int, dtype):
 
 
 def decode_bounded(index: Index, q, bound, top_k: int, eps: float, scale: Optional[float] = None,
-                   workspace=None):
+                   workspace=None, n_exact=None):
     """Decode with the zone of each head sized to meet an error bound eps; ``bound`` is the
-    (radius, vnorm, vmax) of bound_data.  Returns (out, lse, sel, k_used [B,Hq], err_bound [B,Hq])."""
+    (radius, vnorm, vmax) of bound_data.  Returns (out, lse, sel, k_used [B,Hq], err_bound [B,Hq]).
+    ``n_exact``, a one-element int32 device tensor, counts the heads that decided in fp64."""
     import torch
     assert q.is_cuda and q.is_contiguous()
     B, Hq, d = q.shape
@@ -456,7 +457,8 @@ def decode_bounded(index: Index, q, bound, top_k: int, eps: float, scale: Option
     err = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     wi_decode_bounded(p, index.view(), _ptr(radius) if index.C else None, _ptr(vnorm) if index.C else None,
                       vmax.data_ptr(), q.data_ptr(), float(eps), out.data_ptr(), lse.data_ptr(), _ptr(sel),
-                      k_used.data_ptr(), err.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device))
+                      k_used.data_ptr(), err.data_ptr(), None if n_exact is None else n_exact.data_ptr(),
+                      workspace.data_ptr(), workspace.numel(), _stream(q.device))
     return out, lse, sel, k_used, err
 
 

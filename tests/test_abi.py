@@ -238,7 +238,7 @@ def test_bound_data_and_bounded_decode_reject_bad_arguments():
     def bounded(pp=p, radius=FAKE, vmax=FAKE, eps=0.1, ws_bytes=need):
         with pytest.raises(wi.WaveIndexError) as e:
             wi.wi_decode_bounded(pp, _view(), radius, FAKE, vmax, FAKE, eps, FAKE, None, None, None, None,
-                                 FAKE, ws_bytes, 0)
+                                 None, FAKE, ws_bytes, 0)
         return e.value.status
 
     assert bounded(radius=None) == wi.WI_ERR_INVALID_ARG
