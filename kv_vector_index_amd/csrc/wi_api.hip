@@ -161,6 +161,7 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.off_all_sel = o;    o = align256(o + BH * 4);
   L.off_gate = o;       o = align256(o + BG * 4);
   L.off_bnd = o;        o = align256(o + BH * 4 * 4);
+  L.off_bnd_redo = o;   o = align256(o + BH * 4);
   L.off_hl_cid = o;     o = align256(o + BH * K * 4);
   L.off_hl_row = o;     o = align256(o + BH * K * 4);
   L.off_hl_pre = o;     o = align256(o + BH * (K + 1) * 4);
@@ -376,6 +377,7 @@ static wi_status decode_common(const wi_decode_params* p, const wi_index_view* i
   a.all_sel = reinterpret_cast<int32_t*>(base + L.off_all_sel);
   a.gate = reinterpret_cast<int32_t*>(base + L.off_gate);
   a.bnd = reinterpret_cast<float*>(base + L.off_bnd);
+  a.bnd_redo = reinterpret_cast<int32_t*>(base + L.off_bnd_redo);
   a.hl_cid = reinterpret_cast<int32_t*>(base + L.off_hl_cid);
   a.hl_row = reinterpret_cast<int32_t*>(base + L.off_hl_row);
   a.hl_pre = reinterpret_cast<int32_t*>(base + L.off_hl_pre);

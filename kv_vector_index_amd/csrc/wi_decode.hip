@@ -710,6 +710,35 @@ __device__ __forceinline__ void block_rank_desc(int n, const K (&key)[EPT], int 
   __syncthreads();
 }
 
+// NS sums and one maximum over the block with a single pair of barriers; scratch holds
+// (NS + 1) * NT / 64 floats.
+template <int NT, int NS>
+__device__ __forceinline__ void block_sums_max(float (&v)[NS], float& mx, float* scratch) {
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) v[i] = wave_sum(v[i]);
+  mx = wave_max(mx);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) scratch[i * nw + w] = v[i];
+    scratch[NS * nw + w] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < nw; ++j) r += scratch[i * nw + j];
+    v[i] = r;
+  }
+  float m = scratch[NS * nw];
+#pragma unroll
+  for (int j = 1; j < nw; ++j) m = fmaxf(m, scratch[NS * nw + j]);
+  mx = m;
+  __syncthreads();
+}
+
 // Block-wide exclusive prefix sum of any arithmetic type (lane shifts, then the wave totals in
 // LDS scratch of NT / 64 entries); *total receives the block sum.
 template <int NT, typename V>
@@ -781,38 +810,101 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const T*
   return acc;
 }
 
-// canonical_score_row with 8 coordinates in flight instead of 32: fewer registers, for the
-// out-of-line fp64 decision below (the same products and the same order of additions).
-template <typename T>
-__device__ __forceinline__ double canonical_score_row_lean(const double* qd, const T* row) {
-#pragma clang fp contract(off)
-  double acc = 0.0;
-#pragma unroll 1
-  for (int j0 = 0; j0 < kD; j0 += 8) {
-    float x[8];
-    St<T>::load8(row + j0, x);
+// Visits the coordinates of one centroid row in ascending order, f(j, value), with the row's
+// loads issued in batches of kPieces raw 16-byte pieces, kept packed until used: one memory round
+// trip per batch and 4 kPieces registers of row data.
+template <typename T, int kPieces, typename F>
+__device__ __forceinline__ void row_visit(const T* row, F&& f) {
+  constexpr int kPer = 16 / (int)sizeof(T);             // elements per piece
+  constexpr int kBatch = kPieces * kPer;                // elements per batch
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = acc + qd[j0 + e] * (double)x[e];
+  for (int j0 = 0; j0 < kD; j0 += kBatch) {
+    u32x4_t r[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(row + j0 + i * kPer);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          f(j0 + i * 8 + 2 * e, __uint_as_float(w[e] << 16));
+          f(j0 + i * 8 + 2 * e + 1, __uint_as_float(w[e] & 0xffff0000u));
+        } else {
+          f(j0 + i * 4 + e, __uint_as_float(w[e]));
+        }
+      }
+    }
   }
+}
+
+// <q, row> in fp64 with four partial sums: not the canonical rounding, but within d 2^-53
+// sum |q_j row_j| of it (about 1e-13 of the score here), which moves a cluster's weight by a
+// relative 1e-13 -- for sums of terms, where the value matters and not the rounding.
+template <typename T>
+__device__ __forceinline__ double score_row_f64(const double* qd, const T* row) {
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  row_visit<T, 16>(row, [&](int j, float x) { acc[j & 3] = fma(qd[j], (double)x, acc[j & 3]); });
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// canonical_score_row with the row loaded by row_visit (same products, same order of additions).
+template <typename T>
+__device__ __forceinline__ double canonical_score_row_unrolled(const double* qd, const T* row) {
+  double acc = 0.0;
+  row_visit<T, 8>(row, [&](int j, float x) {
+#pragma clang fp contract(off)
+    acc = acc + qd[j] * (double)x;
+  });
   return acc;
 }
 
+// A zero the compiler cannot see through: indexing the query's LDS copy with it per row keeps
+// the 128 query values from being hoisted out of a loop over rows (they would not fit in
+// registers and would be spilled to scratch memory).
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
+// Pointers into LDS (address space 3) and global memory (1) for the parameters of an out-of-line
+// function: through plain pointers its accesses would be flat ones, which wait for every memory
+// operation in flight.
+template <typename X> using lds_ptr = __attribute__((address_space(3))) X*;
+template <typename X> using gbl_ptr = __attribute__((address_space(1))) X*;
+
 // The zone size of the accuracy-bounded select decided in fp64, when the fp32 decision could not
-// be certified: every non-empty cluster's err and lo from its canonical score, term by term as the
-// bound defines them; the selected list (the canonical top k_eff, ids zi[0 .. k_eff)) ranked by
-// (-sigma, id); and the smallest j with A(j) = (err summed after the first j) / (sum of every lo)
-// <= eps, the cap k_eff when none.  Leaves the first j of the canonical order in `bits` (which
-// holds the list on entry) and returns j.  zo (k_eff 8-byte slots) and run_ids (k_eff ints) are
-// LDS scratch; every thread of the block calls it.
+// be certified: every non-empty cluster's err and lo in fp64, term by term as the bound defines
+// them (the list's clusters from their canonical scores, the others' from score_row_f64); the
+// selected list (the canonical top k_eff, ids zi[0 .. k_eff)) ranked by (-sigma, id); and the
+// smallest j with A(j) = (err summed after the first j) / (sum of every lo) <= eps, the cap k_eff
+// when none.  Leaves the first j of the canonical order in `bits` (which holds the list on entry)
+// and returns j.  zo (k_eff 8-byte slots) and run_ids (k_eff ints) are LDS scratch; every thread
+// of the block calls it.  Out of line, so that its registers do not weigh on the select.
 template <typename T, int NT>
 __device__ __attribute__((noinline)) int bounded_zone_fp64(
-    const uint32_t* keys, const T* mu, const int32_t* szg, const float* rdg, const float* vng, double vall,
-    double sc, double uu, double eps, int C, int W32, int k_eff, const double* qd, const int* zi, uint64_t* zo,
-    int* run_ids, uint32_t* bits, double* dscr, float* fred) {
+    gbl_ptr<const uint32_t> keys_g, gbl_ptr<const T> mu_g, gbl_ptr<const int32_t> szg_g, gbl_ptr<const float> rdg_g,
+    gbl_ptr<const float> vng_g, double vall, double sc, double uu, double eps, int C, int W32, int k_eff,
+    lds_ptr<const double> qd_l, lds_ptr<const int> zi_l, lds_ptr<uint64_t> zo_l, lds_ptr<int> run_ids_l,
+    lds_ptr<uint32_t> bits_l, lds_ptr<double> dscr_l, lds_ptr<float> fred_l) {
 #pragma clang fp contract(off)
+  const uint32_t* keys = (const uint32_t*)keys_g;
+  const T* mu = (const T*)mu_g;
+  const int32_t* szg = (const int32_t*)szg_g;
+  const float* rdg = (const float*)rdg_g;
+  const float* vng = (const float*)vng_g;
+  const double* qd = (const double*)qd_l;
+  const int* zi = (const int*)zi_l;
+  uint64_t* zo = (uint64_t*)zo_l;
+  int* run_ids = (int*)run_ids_l;
+  uint32_t* bits = (uint32_t*)bits_l;
+  double* dscr = (double*)dscr_l;
+  float* fred = (float*)fred_l;
   constexpr int EPT = kBoundedMaxTopK / NT;
   const int tid = threadIdx.x;
   double qn2 = 0.0;
+#pragma unroll 8
   for (int j = 0; j < kD; ++j) qn2 = qn2 + qd[j] * qd[j];
   const double qn = sqrt(qn2);
   double s64[EPT];
@@ -824,25 +916,33 @@ __device__ __attribute__((noinline)) int bounded_zone_fp64(
     s64[e] = 0.0;
     ck[e] = CanonKey{0ull, 0x7fffffff};
     if (p < k_eff) {
-      s64[e] = canonical_score_row_lean<T>(qd, mu + (size_t)zi[p] * kD);
+      s64[e] = canonical_score_row_unrolled<T>(qd + opaque_zero(), mu + (size_t)zi[p] * kD);
       ck[e] = CanonKey{f64_order_key(s64[e]), zi[p]};
       smax = fmax(smax, s64[e]);
     }
   }
   const double mstar = sc * block_max_d<NT>(smax, dscr);
-  auto terms64 = [&](double s, int c, double& err, double& lo) {
+  auto terms64 = [&](double s, double n, double r, double vc, double& err, double& lo) {
 #pragma clang fp contract(off)
-    const double x = sc * qn * (double)rdg[c];
-    const double w = (double)szg[c] * exp(sc * s - mstar);
+    const double x = sc * qn * r;
+    const double w = n * exp(sc * s - mstar);
     const double av = w * expm1(x);
-    err = av * ((double)vng[c] + (1.0 + uu) * vall) + w * uu * (double)vng[c];
+    err = av * (vc + (1.0 + uu) * vall) + w * uu * vc;
     lo = w * exp(-x);
   };
+  // the clusters outside the list; each cluster's key, size, radius and value norm are fetched
+  // one iteration ahead, so that a live cluster costs the one round trip of its row
   double tout = 0.0, dsum = 0.0;
+  uint32_t kn = 0u;
+  float nn = 0.f, rn = 0.f, vn = 0.f;
+  if (tid < C) { kn = keys[tid]; nn = (float)szg[tid]; rn = rdg[tid]; vn = vng[tid]; }
   for (int c = tid; c < C; c += NT) {
-    if (keys[c] == 0u || ((bits[c >> 5] >> (c & 31)) & 1u)) continue;
+    const uint32_t kc = kn;
+    const float nc = nn, rc = rn, vc = vn;
+    if (c + NT < C) { kn = keys[c + NT]; nn = (float)szg[c + NT]; rn = rdg[c + NT]; vn = vng[c + NT]; }
+    if (kc == 0u || ((bits[c >> 5] >> (c & 31)) & 1u)) continue;
     double e1, l1;
-    terms64(canonical_score_row_lean<T>(qd, mu + (size_t)c * kD), c, e1, l1);
+    terms64(score_row_f64<T>(qd + opaque_zero(), mu + (size_t)c * kD), (double)nc, (double)rc, (double)vc, e1, l1);
     tout = tout + e1;
     dsum = dsum + l1;
   }
@@ -851,8 +951,9 @@ __device__ __attribute__((noinline)) int bounded_zone_fp64(
   for (int e = 0; e < EPT; ++e) {
     el[e] = 0.0;
     if (e * NT + tid < k_eff) {
+      const int c = ck[e].id;
       double l1;
-      terms64(s64[e], ck[e].id, el[e], l1);
+      terms64(s64[e], (double)szg[c], (double)rdg[c], (double)vng[c], el[e], l1);
       dsum = dsum + l1;
     }
   }
@@ -910,8 +1011,13 @@ __device__ __attribute__((noinline)) int bounded_zone_fp64(
 static_assert(kMaxGroup * kD <= kCandCap, "a KV group's queries are staged in the candidate arrays");
 static_assert(kBoundedMaxTopK <= kCandCap && kBoundedMaxTopK <= kSumCap && kBoundedMaxTopK <= kBins,
               "the bounded select lists its zone in LDS");
-template <typename T, int NT, bool EXT>
+// MODE 0: plain decode; 1: the gated, refresh and bounded modes; 2: the bounded mode's second
+// launch, for the heads whose zone size the first could not certify in fp32 (it decides them in
+// fp64).  Each mode is its own instantiation, so that the plain decode, and the first bounded
+// launch, carry no registers of the modes they do not run.
+template <typename T, int NT, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_select(DecodeArgs a) {
+  constexpr bool EXT = MODE != 0, EXACT = MODE == 2;
   extern __shared__ uint32_t dynl[];                 // [W32] retrieved bitmap, [W32] band bitmap
   __shared__ __attribute__((aligned(16))) uint32_t skey[kSumCap];   // tile summaries: score keys
   __shared__ int sid[kSumCap];                       // tile summaries: cluster ids; then the
@@ -930,6 +1036,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ double dscr[16];                        // bounded decode: fp64 reduction scratch
   __shared__ int sh_i[8];
   static_assert((NT / 64) * 2 * kD <= kSumCap && 4 + 4 * (NT / 64) <= kSumCap, "estimation scratch");
+  if (EXACT && a.bnd_redo[blockIdx.x] == 0) return;   // decided by the first launch
   if (blockIdx.x >= (unsigned)(a.B * a.Hq)) {      // an estimation workgroup (uniform branch)
     est_block<T, NT>(a, (int)blockIdx.x - a.B * a.Hq, reinterpret_cast<float*>(skey), reinterpret_cast<float*>(sid));
     return;
@@ -1396,11 +1503,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
       }
     }
-    const float e_out = block_sum<NT>(so, fred);       // includes barriers: the list is visible
-    float ll = 0.f;
-    for (int i = tid; i < k_eff; i += NT) ll += zl[i];
-    const float b_lo = block_sum<NT>(slo, fred) + block_sum<NT>(ll, fred);
-    const float r_hi = block_max<NT>(rmax, fred);
+    float* red = reinterpret_cast<float*>(tfull);      // reduction scratch (free here)
+    const float slo_o = slo;                           // lo outside the list (this thread's part)
+    __syncthreads();                                   // the list's terms are visible
+    for (int i = tid; i < k_eff; i += NT) slo += zl[i];
+    float tot2[2] = {so, slo};
+    block_sums_max<NT, 2>(tot2, rmax, red);
+    const float e_out = tot2[0], b_lo = tot2[1], r_hi = rmax;
     const float lim = a.eps * b_lo;
     constexpr int EPT = kBoundedMaxTopK / NT;           // list entries per thread
     static_assert(EPT * NT == kBoundedMaxTopK && 2 * kBoundedMaxTopK <= kSumCap, "the bounded list's layout");
@@ -1458,12 +1567,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     // ---- certification: kf is the decision the canonical fp64 terms give when A(kf) <= eps and
     // A(kf - 1) > eps hold for every value within the fp32 error of the terms and sums.  The fp32
     // order's prefixes are the canonical ones up to clusters whose fp32 scores lie within 2 delta
-    // of the boundary: the canonical first j hold positions [0, L_j) and lie within [0, U_j), so
-    // T(U_j) <= T_canonical(j) <= T(L_j).  A certified A(kf) <= eps through T(L_kf) makes
-    // T(L_kf) <= lim, hence L_kf = kf by the minimality of kf: no near tie straddles the
-    // boundary, and the zone is the first kf positions.
-    bool cert = true;
-    if (k_eff > 0) {
+    // of the boundary: the canonical first j hold positions [0, L_j), lie within [0, U_j) and
+    // leave out U_j - j of the band [L_j, U_j), so T_canonical(j) lies between T(U_j) plus U_j - j
+    // times the band's smallest err and T(U_j) plus U_j - j times its largest.
+    bool cert = !EXACT;
+    int zL = kf, zU = kf;                              // the band at the zone's boundary
+    if (!EXACT && k_eff > 0) {
       auto sc_at = [&](int p) { return (double)f32_from_order_key((uint32_t)(zo[p] >> 32)); };
       auto t_at = [&](int p) { return p < k_eff ? (double)zt[p] : (double)e_out; };
       auto len_L = [&](int j) {
@@ -1479,6 +1588,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         int U = j;
         while (U < k_eff && sc_at(U) >= s) ++U;
         return U;
+      };
+      auto t_bound = [&](int j, bool upper) {
+        const int L = len_L(j), U = len_U(j);
+        float m = upper ? 0.f : INFINITY;
+        for (int p = L; p < U; ++p) m = upper ? fmaxf(m, ze[p]) : fminf(m, ze[p]);
+        return t_at(U) + (U > j ? (double)(U - j) * (double)m : 0.0);
       };
       // relative error budgets (u = 2^-24): the weights' exponent is off by scale delta from the
       // scores plus the roundings of scale s - m* and of the exponential's argument; x = scale |q|
@@ -1499,44 +1614,66 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       const double eps = (double)a.eps;
       cert = xh < 80.0 && Dlo > 0.0 && isfinite((double)b_lo) && isfinite((double)e_out);
       if (cert && kf < k_eff) {                       // A(kf) <= eps
-        const double hiA = (t_at(len_L(kf)) * (1.0 + rT) + tauT) / Dlo;
+        const double hiA = (t_bound(kf, true) * (1.0 + rT) + tauT) / Dlo;
         cert = isfinite(hiA) && hiA * (1.0 + 1e-9) < eps;
       }
       if (cert && kf > 0) {                           // A(kf - 1) > eps
-        const double loA = (t_at(len_U(kf - 1)) * (1.0 - rT) - tauT) / Dhi;
+        const double loA = (t_bound(kf - 1, false) * (1.0 - rT) - tauT) / Dhi;
         cert = loA * (1.0 - 1e-9) > eps;
       }
+      if (cert) { zL = len_L(kf); zU = len_U(kf); }
+    }
+    if constexpr (!EXACT) {
+      // an uncertified head leaves its outputs to the second launch
+      if (tid == 0) a.bnd_redo[bh] = cert ? 0 : 1;
+      if (!cert) return;
     }
     if (cert) {
       if (kf < k_eff) {
+        // the zone: positions [0, zL), and the best kf - zL of the band [zL, zU) by (-canonical
+        // score, id)
         for (int w = tid; w < W32; w += NT) bits[w] = 0u;
         __syncthreads();
-        for (int p = tid; p < kf; p += NT) { const int c = zi[p]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+        for (int p = tid; p < zL; p += NT) { const int c = zi[p]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+        if (zU > zL) {
+          uint64_t* bkey = a.band_key + (size_t)bh * C;
+          for (int p = zL + tid; p < zU; p += NT)
+            bkey[p - zL] = f64_order_key(canonical_score_row<T>(qd, mu + (size_t)zi[p] * kD));
+          __syncthreads();
+          const int nb = zU - zL, need = kf - zL;
+          for (int p = zL + tid; p < zU; p += NT) {
+            const CanonKey me{bkey[p - zL], zi[p]};
+            int r = 0;
+            for (int j = 0; j < nb; ++j) r += canon_gt(CanonKey{bkey[j], zi[zL + j]}, me) ? 1 : 0;
+            if (r < need) { const int c = zi[p]; atomicOr(&bits[c >> 5], 1u << (c & 31)); }
+          }
+        }
         __syncthreads();
       }
       k_zone = kf;
-    } else {
-      // ---- undecided in fp32: the decision in fp64 (out of line, so that its registers do not
-      // weigh on the rest of the select)
-      k_zone = bounded_zone_fp64<T, NT>(keys, mu, szg, rdg, vng, (double)b_vall, (double)a.scale, (double)a.u,
-                                        (double)a.eps, C, W32, k_eff, qd, zi, zo, sid + kBoundedMaxTopK, bits,
-                                        dscr, fred);
+    } else if constexpr (EXACT) {
+      // ---- the second launch: the decision in fp64
+      k_zone = bounded_zone_fp64<T, NT>(
+          (gbl_ptr<const uint32_t>)keys, (gbl_ptr<const T>)mu, (gbl_ptr<const int32_t>)szg,
+          (gbl_ptr<const float>)rdg, (gbl_ptr<const float>)vng, (double)b_vall, (double)a.scale, (double)a.u,
+          (double)a.eps, C, W32, k_eff, (lds_ptr<const double>)qd, (lds_ptr<const int>)zi, (lds_ptr<uint64_t>)zo,
+          (lds_ptr<int>)(sid + kBoundedMaxTopK), (lds_ptr<uint32_t>)bits, (lds_ptr<double>)dscr,
+          (lds_ptr<float>)fred);
       if (tid == 0 && a.bnd_fallback) atomicAdd(a.bnd_fallback, 1u);
     }
     // sums over the estimated clusters (outside the zone) for the bound after attention: the
     // clusters outside the list, plus the list entries the zone left out
-    float sa = 0.f, sv = 0.f, sl = 0.f;
+    float s3[3] = {sa_o, sv_o, slo_o};
     for (int i = tid; i < k_eff; i += NT) {
       const int c = zi[i];
       if ((bits[c >> 5] >> (c & 31)) & 1u) continue;
-      sa += za[i]; sv += zv[i]; sl += zl[i];
+      s3[0] += za[i]; s3[1] += zv[i]; s3[2] += zl[i];
     }
-    sa = block_sum<NT>(sa_o, fred) + block_sum<NT>(sa, fred);
-    sv = block_sum<NT>(sv_o, fred) + block_sum<NT>(sv, fred);
-    sl = block_sum<NT>(slo, fred) + block_sum<NT>(sl, fred);
+    float unused = 0.f;
+    block_sums_max<NT, 3>(s3, unused, red);
     if (tid == 0) {
       float* bd = a.bnd + (size_t)bh * 4;
-      bd[0] = b_mstar; bd[1] = sa; bd[2] = sv; bd[3] = sl;
+      bd[0] = b_mstar; bd[1] = s3[0]; bd[2] = s3[1]; bd[3] = s3[2];
       if (a.k_used) a.k_used[bh] = k_zone;
     }
     fast_pub = false;
@@ -2136,11 +2273,13 @@ static void launch_select(const DecodeArgs& a, hipStream_t s) {
   const bool ext = a.gated || a.refresh || a.bounded;
   const size_t lds = (size_t)a.W32 * 8;
   if (BH > kSelHeadsPerRound) {
-    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, true>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
-    else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, false>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 1>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 0>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
+    if (a.bounded) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 2>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);
   } else {
-    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, true>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
-    else hipLaunchKernelGGL((k_select<T, kSelThreadsFew, false>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
+    if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, 1>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
+    else hipLaunchKernelGGL((k_select<T, kSelThreadsFew, 0>), dim3(grid), dim3(kSelThreadsFew), lds, s, a);
+    if (a.bounded) hipLaunchKernelGGL((k_select<T, kSelThreadsFew, 2>), dim3(BH), dim3(kSelThreadsFew), lds, s, a);
   }
 }
 
@@ -2204,14 +2343,18 @@ static hipError_t set_select_lds() {
   static bool attr_set = false;
   if (!attr_set) {
     // the select kernel's two cluster bitmaps (2 * ceil(C / 32) words) live in dynamic LDS
-    const void* fns[8] = {reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, false>),
-                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, false>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, false>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, false>),
-                          reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, true>),
-                          reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, true>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, true>),
-                          reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, true>)};
+    const void* fns[12] = {reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, 0>),
+                           reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, 0>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, 0>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, 0>),
+                           reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, 1>),
+                           reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, 1>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, 1>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, 1>),
+                           reinterpret_cast<const void*>(k_select<float, kSelThreadsFew, 2>),
+                           reinterpret_cast<const void*>(k_select<float, kSelThreadsMany, 2>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsFew, 2>),
+                           reinterpret_cast<const void*>(k_select<uint16_t, kSelThreadsMany, 2>)};
     for (const void* f : fns) {
       const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSelectBitmapLds);
       if (e != hipSuccess) return e;

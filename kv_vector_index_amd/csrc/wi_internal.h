@@ -35,7 +35,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ decode workspace
 struct DecodeLayout {
   int BG, BH, G, W32, tiles_g, est_blocks_g, att_split, att_items;
-  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate, off_bnd,
+  size_t off_keys, off_tile_norm, off_tile_cnt, off_tile_top, off_tile_top_id, off_band_ids, off_band_key, off_all_sel, off_gate, off_bnd, off_bnd_redo,
       off_hl_cid, off_hl_row, off_hl_pre, off_hl_key, off_att_bounds, off_est_md, off_est_num,
       off_att_md, off_att_num, total;
 };
@@ -93,6 +93,7 @@ struct DecodeArgs {
   int bounded;
   int32_t* k_used;         // [BH] or null: zone size chosen
   uint32_t* bnd_fallback;  // [1] or null: incremented once per head whose zone size was decided in fp64
+  int32_t* bnd_redo;       // [BH] workspace: 1 where the bounded select left the head to its fp64 launch
   float* err_bound;        // [BH] or null: bound on |out - dense attention|
   float* bnd;              // [BH, 4] workspace: m*, sum a, sum (a V + w u V), sum lo over the estimation zone
   // wave buffer (paged == 0 otherwise): k_perm / v_perm are then the copies in host memory
