@@ -121,42 +121,92 @@ __device__ void store_unit_direction(double x0, double x1, T* dst, double* buf, 
 
 constexpr int kInitThreads = 512;
 
+// The seed rows of one segment's clusters, one cluster per thread.  The partial Fisher-Yates
+// shuffle swaps position r with j_r >= r for r = 0, 1, ..., and cluster r takes the row that ends
+// at position r.  That row is the one at position j_r just before step r: the row an earlier step
+// r' < r moved there (the last with j_r' = j_r; it brought the row then at position r'), else j_r
+// itself.  So each cluster follows that chain back through the draws, with no sequential pass
+// over the swaps.  Then the thread loads its seed row whole, sums its squares in fp64 in ascending
+// coordinate order and stores round(x / ||x||) (a zero row for a zero norm).
 template <typename T>
 __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
-  extern __shared__ uint32_t init_lds[];      // draws j_r [Cs], then the row array [n_s] (u16)
-  __shared__ double buf[kInitThreads / 64][kD];
+  extern __shared__ uint32_t init_lds[];      // draws j_r [Cs]
   const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
   uint32_t* draw = init_lds;
-  uint16_t* rows = reinterpret_cast<uint16_t*>(init_lds + a.Cs);
   const uint64_t st0 = segment_state0(a.seed, b, g, s);
   // the draws do not depend on the shuffle state: j_r = r + (x_r mod (n_s - r))
   for (int r = threadIdx.x; r < cs_eff; r += kInitThreads)
     draw[r] = (uint32_t)r + (uint32_t)(splitmix64_nth(st0, (uint64_t)r) % (uint64_t)(n_s - r));
-  for (int i = threadIdx.x; i < n_s; i += kInitThreads) rows[i] = (uint16_t)i;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int r = 0; r < cs_eff; ++r) {
-      const int j = (int)draw[r];
-      const uint16_t t = rows[r];
-      rows[r] = rows[j];
-      rows[j] = t;
-    }
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
   T* mh = static_cast<T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
-  for (int j = w; j < a.Cs; j += kInitThreads / 64) {
-    if (j < cs_eff) {
-      const T* row = K + (size_t)rows[j] * kD;
-      store_unit_direction<T>((double)St<T>::f(row[2 * lane]), (double)St<T>::f(row[2 * lane + 1]),
-                              mh + (size_t)j * kD, buf[w], false);
-    } else {
-      mh[(size_t)j * kD + 2 * lane] = St<T>::from_f64(0.0);
-      mh[(size_t)j * kD + 2 * lane + 1] = St<T>::from_f64(0.0);
+  constexpr int kPer = 16 / (int)sizeof(T);          // elements per 16-byte piece
+  constexpr int kPieces = kD / kPer;
+  for (int j = threadIdx.x; j < a.Cs; j += kInitThreads) {
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(mh + (size_t)j * kD);
+    if (j >= cs_eff) {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+      continue;
+    }
+    int p = (int)draw[j], t = j;
+    for (;;) {
+      int q = -1;
+      for (int x = t - 1; x >= 0; --x)
+        if ((int)draw[x] == p) { q = x; break; }
+      if (q < 0) break;
+      p = q;
+      t = q;
+    }
+    const u32x4_t* row = reinterpret_cast<const u32x4_t*>(K + (size_t)p * kD);
+    u32x4_t r[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) r[i] = row[i];
+    auto elem = [&](int e) -> double {               // coordinate e of the row
+      const u32x4_t& v = r[e / kPer];
+      if constexpr (sizeof(T) == 2) {
+        const int k = (e % kPer) >> 1;               // the 32-bit word holding it
+        const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+        return (double)__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+      } else {
+        const int k = e % kPer;
+        return (double)__uint_as_float(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+      }
+    };
+    double nrm2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < kD; ++e) {
+#pragma clang fp contract(off)
+      const double x = elem(e);
+      const double sq = x * x;
+      nrm2 = nrm2 + sq;
+    }
+    if (!(nrm2 > 0.0)) {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+      continue;
+    }
+    const double nrm = __builtin_sqrt(nrm2);
+    // the row's bits are re-read for the divisions below rather than 128 fp64 values kept live
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t lo = St<T>::from_f64(elem(i * kPer + 2 * q) / nrm);
+          const uint32_t hi = St<T>::from_f64(elem(i * kPer + 2 * q + 1) / nrm);
+          w[q] = lo | (hi << 16);
+        } else {
+          w[q] = __float_as_uint(St<T>::from_f64(elem(i * kPer + q) / nrm));
+        }
+      }
+      dst[i] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
   }
 }
@@ -665,7 +715,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   if (a.Nc == 0 || a.seg0 >= a.nseg) return hipSuccess;
   const int nseg_b = a.nseg - a.seg0;        // segments built by this call
   {
-    const size_t lds = (size_t)a.Cs * 4 + (((size_t)a.L * 2 + 3) & ~size_t(3));
+    const size_t lds = (size_t)a.Cs * 4;
     prof_begin(WI_STAGE_INIT, st);
     hipLaunchKernelGGL(k_init<T>, dim3(nseg_b, BG), dim3(kInitThreads), lds, st, a);
     prof_end(WI_STAGE_INIT, st);

@@ -664,13 +664,15 @@ __device__ __forceinline__ CanonKey bcast_lane(const CanonKey& v, int l) {
 
 // Ranks in descending order (under gt, a strict total order; the keys are distinct) of n <=
 // EPT * NT keys, thread t holding keys e * NT + t.  Every run of 64 consecutive keys belongs to
-// one wave: its keys are ranked among themselves from lane broadcasts and stored in that order
-// through put(position, key); a key's rank is its rank in its run plus, for every other run, the
-// number of keys above it, found by a binary search through get(position).  O(n log 64) LDS reads
-// per key against O(n) for direct counting.
-template <int NT, int EPT, typename K, typename Gt, typename Put, typename Get>
+// one wave: its keys are ranked among themselves and stored in that order through put(position,
+// key); a key's rank is its rank in its run plus, for every other run, the number of keys above
+// it, found by a binary search through get(position).  O(n log 64) LDS reads per key against
+// O(n) for direct counting.  Within a run the keys are compared either from lane broadcasts or,
+// when orig(i) reads key i from LDS (kOrig), from broadcast LDS reads, which pipeline; the sorted
+// runs may then overwrite those keys (a barrier separates the two).
+template <int NT, int EPT, bool kOrig, typename K, typename Gt, typename Put, typename Get, typename Orig>
 __device__ __forceinline__ void block_rank_desc(int n, const K (&key)[EPT], int (&rank)[EPT], Gt gt,
-                                                Put put, Get get) {
+                                                Put put, Get get, Orig orig) {
   const int tid = threadIdx.x, lane = tid & 63;
   int rr[EPT];
 #pragma unroll
@@ -679,10 +681,20 @@ __device__ __forceinline__ void block_rank_desc(int n, const K (&key)[EPT], int 
     int r = 0;
     if (base < n) {                                  // uniform over the wave
       const int len = min(64, n - base);
-      for (int l = 0; l < len; ++l) r += gt(bcast_lane(key[e], l), key[e]) ? 1 : 0;
-      if (i < n) put(base + r, key[e]);
+      if constexpr (kOrig) {
+#pragma unroll 8
+        for (int l = 0; l < len; ++l) r += gt(orig(base + l), key[e]) ? 1 : 0;
+      } else {
+        for (int l = 0; l < len; ++l) r += gt(bcast_lane(key[e], l), key[e]) ? 1 : 0;
+      }
     }
     rr[e] = r;
+  }
+  if constexpr (kOrig) __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = e * NT + tid;
+    if (i < n) put((i - lane) + rr[e], key[e]);
   }
   __syncthreads();
   const int runs = (n + 63) / 64;
@@ -960,9 +972,9 @@ __device__ __attribute__((noinline)) int bounded_zone_fp64(
   const double t_out = block_sum_d<NT>(tout, dscr);
   const double d_all = block_sum_d<NT>(dsum, dscr);
   int rk[EPT];
-  block_rank_desc<NT, EPT>(k_eff, ck, rk, [](const CanonKey& x, const CanonKey& y) { return canon_gt(x, y); },
-                           [&](int p, const CanonKey& k) { zo[p] = k.k; run_ids[p] = k.id; },
-                           [&](int p) { return CanonKey{zo[p], run_ids[p]}; });
+  block_rank_desc<NT, EPT, false>(k_eff, ck, rk, [](const CanonKey& x, const CanonKey& y) { return canon_gt(x, y); },
+                                  [&](int p, const CanonKey& k) { zo[p] = k.k; run_ids[p] = k.id; },
+                                  [&](int p) { return CanonKey{zo[p], run_ids[p]}; }, [](int) { return CanonKey{}; });
   double* ez = reinterpret_cast<double*>(zo);           // err in canonical order
 #pragma unroll
   for (int e = 0; e < EPT; ++e) if (e * NT + tid < k_eff) ez[rk[e]] = el[e];
@@ -1523,8 +1535,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       int rk[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e) { const int i = e * NT + tid; kv[e] = i < k_eff ? zo[i] : 0ull; }
-      block_rank_desc<NT, EPT>(k_eff, kv, rk, [](uint64_t x, uint64_t y) { return x > y; },
-                               [&](int p, uint64_t k) { zo[p] = k; }, [&](int p) { return zo[p]; });
+      block_rank_desc<NT, EPT, true>(k_eff, kv, rk, [](uint64_t x, uint64_t y) { return x > y; },
+                                     [&](int p, uint64_t k) { zo[p] = k; }, [&](int p) { return zo[p]; },
+                                     [&](int p) { return zo[p]; });
       float pe[EPT], pl[EPT], pa[EPT], pv[EPT];
       int pc[EPT];
 #pragma unroll
