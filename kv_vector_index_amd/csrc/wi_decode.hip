@@ -1564,7 +1564,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         loc[e] = run;
       }
       float tot;
-      const float before = block_exclusive_scan_any<NT, float>(run, fred, &tot);
+      const float before = block_exclusive_scan_f<NT>(run, fred, &tot);
       int kb = k_eff;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
@@ -1615,17 +1615,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       // terms that underflow.
       const double u32 = 5.9604644775390625e-08, sc = (double)a.scale;
       const double amax = sc * ((double)qv * (1.0 + 1.0 / 1024) * (double)mxn * (1.0 + 1.0 / 1024) + delta);
-      const double rw = expm1(sc * delta + 6.0 * u32 * amax + 4.0 * u32) + 2.0 * u32;
+      // e^y - 1 <= y (1 + y) for 0 <= y <= 1/2 (the series' tail is below y^2 e^y / 2)
+      const double yw = sc * delta + 6.0 * u32 * amax + 4.0 * u32;
+      const double rw = yw * (1.0 + yw) + 2.0 * u32;
       const double xh = sc * (double)qv * (double)r_hi * (1.0 + 1.0 / 1024);
       const double rx = (kD + 8) * u32;
       const double depth = (double)(KPT + 2 * EPT + 64) * u32;
       const double rT = 2.0 * (rw + (1.0 + xh) * rx + 12.0 * u32 + depth);
       const double rD = 2.0 * (rw + xh * rx + 2.0 * u32 * xh + 6.0 * u32 + depth);
       const double tiny = (double)n_ne * 0x1p-100;
-      const double tauT = tiny * (exp(fmin(xh, 80.0)) + 1.0) * (1.0 + 3.0 * (double)b_vall);
+      const double tauT = tiny * ((double)__expf((float)fmin(xh, 80.0)) * 1.01 + 1.0) * (1.0 + 3.0 * (double)b_vall);
       const double Dlo = (double)b_lo * (1.0 - rD) - tiny, Dhi = (double)b_lo * (1.0 + rD) + tiny;
       const double eps = (double)a.eps;
-      cert = xh < 80.0 && Dlo > 0.0 && isfinite((double)b_lo) && isfinite((double)e_out);
+      cert = yw <= 0.5 && xh < 80.0 && Dlo > 0.0 && isfinite((double)b_lo) && isfinite((double)e_out);
       if (cert && kf < k_eff) {                       // A(kf) <= eps
         const double hiA = (t_bound(kf, true) * (1.0 + rT) + tauT) / Dlo;
         cert = isfinite(hiA) && hiA * (1.0 + 1e-9) < eps;

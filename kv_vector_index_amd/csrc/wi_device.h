@@ -134,6 +134,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v + (row >= 1 ? s1 : 0) + (row >= 2 ? s2 : 0) + (row >= 3 ? s3 : 0);
 }
 
+// The same for floats (the additions of a scan: any order is fine where this is used).
+__device__ __forceinline__ float wave_inclusive_scan_f(float v) {
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  const float s1 = readlane_f(v, 15);
+  const float s2 = readlane_f(v, 31);
+  const float s3 = readlane_f(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? s1 : 0.f) + (row >= 2 ? s2 : 0.f) + (row >= 3 ? s3 : 0.f);
+}
+
 // Block-wide scans and reductions over NT threads (a multiple of 64, <= 1024; NT is the launch
 // block size, a compile-time constant so that no work-group size is read at run time).  `scratch`
 // holds >= NT / 64 entries of LDS; every thread reads all per-wave partials itself.
@@ -156,6 +169,25 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   *total = tot;
   __syncthreads();
   return before + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_exclusive_scan_f(float v, float* scratch, float* total) {
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float inc = wave_inclusive_scan_f(v);
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  float before = 0.f, tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < nw; ++i) {
+    const float t = scratch[i];
+    before += i < w ? t : 0.f;
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + (inc - v);
 }
 
 template <int NT>
