@@ -506,48 +506,76 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
 }
 
 // ============================================================================ k_rescore
+// The keys the assignment could not certify, one per workgroup at a time: the key row is staged in
+// LDS in fp64, each thread forms the canonical scores of its centroids (c = t, t + 256, ...), every
+// one with its row's loads issued at once and the 128 exact products added in ascending
+// coordinate order, and a block argmax (ties to the lower id) names the cluster.
+constexpr int kRescoreThreads = 256;
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_rescore(BuildArgs a, int it) {
+__global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it) {
 #pragma clang fp contract(off)
-  __shared__ double kx[4][kD];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ double kx[kD];
+  __shared__ double rb[kRescoreThreads / 64];
+  __shared__ int rj[kRescoreThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t n = a.flag_cnt[it];
-  for (uint32_t e = blockIdx.x * 4 + w; e < n; e += gridDim.x * 4) {
+  constexpr int kPer = 16 / (int)sizeof(T);           // elements per 16-byte piece
+  for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
     const int packed = a.flag_list[e];
     const int bg = packed / a.Nc, ci = packed - bg * a.Nc;
     const int s = ci / a.L;
     const int cs_eff = min(a.Cs, seg_len_of(a, s));
     const T* krow = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + ci) * kD;
-    kx[w][2 * lane] = (double)St<T>::f(krow[2 * lane]);
-    kx[w][2 * lane + 1] = (double)St<T>::f(krow[2 * lane + 1]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (tid < kD) kx[tid] = (double)St<T>::f(krow[tid]);
+    __syncthreads();
     const T* mh = static_cast<const T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
     double best = -INFINITY;
     int bj = 0x7fffffff;
-    for (int j = lane; j < cs_eff; j += 64) {
-      const T* crow = mh + (size_t)j * kD;
+    for (int j = tid; j < cs_eff; j += kRescoreThreads) {
+      const u32x4_t* crow = reinterpret_cast<const u32x4_t*>(mh + (size_t)j * kD);
+      const double* kq = kx + opaque_zero();          // the key's values re-read per centroid
       double acc = 0.0;
-      for (int d0 = 0; d0 < kD; d0 += 8) {
-        float cv[8];
-        St<T>::load8(crow + d0, cv);
-        for (int e2 = 0; e2 < 8; ++e2) {
-          const double p = kx[w][d0 + e2] * (double)cv[e2];
-          acc = acc + p;
+#pragma unroll
+      for (int h = 0; h < kD / (16 * kPer); ++h) {     // batches of 16 pieces: 1 (bf16) or 2 (fp32)
+        u32x4_t r[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r[i] = crow[h * 16 + i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t wd[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d0 = (h * 16 + i) * kPer;
+            if constexpr (sizeof(T) == 2) {
+              const double p0 = kq[d0 + 2 * q] * (double)__uint_as_float(wd[q] << 16);
+              acc = acc + p0;
+              const double p1 = kq[d0 + 2 * q + 1] * (double)__uint_as_float(wd[q] & 0xffff0000u);
+              acc = acc + p1;
+            } else {
+              const double p = kq[d0 + q] * (double)__uint_as_float(wd[q]);
+              acc = acc + p;
+            }
+          }
         }
       }
       if (acc > best || bj == 0x7fffffff) { best = acc; bj = j; }
     }
-    // wave argmax, ties to the lower id
+    // block argmax, ties to the lower id
 #pragma unroll
     for (int m = 32; m > 0; m >>= 1) {
       const double ob = __shfl_xor(best, m);
       const int oj = __shfl_xor(bj, m);
       if (ob > best || (ob == best && oj < bj)) { best = ob; bj = oj; }
     }
-    if (lane == 0) a.assign[(size_t)bg * a.Nc + ci] = bj;
-    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) { rb[w] = best; rj[w] = bj; }
+    __syncthreads();
+    if (tid == 0) {
+      for (int i = 1; i < kRescoreThreads / 64; ++i)
+        if (rb[i] > best || (rb[i] == best && rj[i] < bj)) { best = rb[i]; bj = rj[i]; }
+      a.assign[(size_t)bg * a.Nc + ci] = bj;
+    }
+    __syncthreads();
   }
 }
 
@@ -555,7 +583,7 @@ __global__ __launch_bounds__(256) void k_rescore(BuildArgs a, int it) {
 constexpr int kCsrThreads = 1024;
 
 __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
-  extern __shared__ uint32_t csr_lds[];   // cnt[Cs], loc[Cs], run[Cs], tbl[16][Cs] (u8)
+  extern __shared__ uint32_t csr_lds[];   // cnt[Cs], loc[Cs], run[Cs], tbl[16][Cs] (u8), keys[1024]
   __shared__ int iscr[32];
   const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int n_s = seg_len_of(a, s);
@@ -564,6 +592,7 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
   uint32_t* loc = csr_lds + Cs;
   uint32_t* run = csr_lds + 2 * Cs;
   uint8_t* tbl = reinterpret_cast<uint8_t*>(csr_lds + 3 * Cs);
+  int* rkeys = reinterpret_cast<int*>(csr_lds + 3 * Cs + 4 * Cs);   // a round's keys, 64 per wave
   const int32_t* asg = a.assign + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
@@ -586,23 +615,29 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
     a.offsets[(size_t)bg * (a.C + 1) + cbase + j] = s * a.L + (int32_t)loc[j];
   }
   // stable scatter: rounds of 1024 tokens in order; within a wave, lanes with equal ids are
-  // ranked by lane; across waves of a round by the per-wave count table; across rounds by run[].
+  // ranked by lane (each lane reads the wave's 64 ids back from LDS, broadcast reads that
+  // pipeline); across waves of a round by the per-wave count table; across rounds by run[].
   int32_t* perm = a.perm + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int pos0 = a.lo + s * a.L;
+  int key_next = tid < n_s ? asg[tid] : -1;          // each round's ids are loaded a round ahead
   for (int r0 = 0; r0 < n_s; r0 += kCsrThreads) {
-    for (int x = tid; x < 16 * Cs / 4; x += kCsrThreads) reinterpret_cast<uint32_t*>(tbl)[x] = 0u;
-    __syncthreads();
     const int i = r0 + tid;
     const bool valid = i < n_s;
-    const int key = valid ? asg[i] : -1;
-    uint64_t mine = 0;
+    const int key = key_next;
+    key_next = i + kCsrThreads < n_s ? asg[i + kCsrThreads] : -1;
+    for (int x = tid; x < 16 * Cs / 4; x += kCsrThreads) reinterpret_cast<uint32_t*>(tbl)[x] = 0u;
+    __syncthreads();
+    int* wk = rkeys + w * 64;
+    wk[lane] = key;
+    wave_lds_sync();
+    int rank = 0, count = 0;
+#pragma unroll 8
     for (int j = 0; j < 64; ++j) {
-      const int sk = __builtin_amdgcn_readlane(key, j);
-      const uint64_t m = __ballot(key == sk);
-      if (key == sk) mine = m;
+      const bool eq = wk[j] == key;
+      rank += (eq && j < lane) ? 1 : 0;
+      count += eq ? 1 : 0;
     }
-    const int rank = __popcll(mine & ((1ull << lane) - 1ull));
-    if (valid && rank == 0) tbl[w * Cs + key] = (uint8_t)__popcll(mine);
+    if (valid && rank == 0) tbl[w * Cs + key] = (uint8_t)count;
     __syncthreads();
     if (valid) {
       int p = (int)loc[key] + (int)run[key] + rank;
@@ -723,7 +758,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const size_t alds = (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride;
-  const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs;
+  const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs + (size_t)4 * kCsrThreads;
   // assignment blocks per segment: about one block per CU in all (each stages the segment's
   // centroids once and loops over 64-key-per-wave passes), at least one pass each
   const unsigned assign_px = (unsigned)std::max<int64_t>(1, std::min<int64_t>(
@@ -738,7 +773,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
                          alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
-    hipLaunchKernelGGL(k_rescore<T>, dim3(1024), dim3(256), 0, st, a, it);
+    hipLaunchKernelGGL(k_rescore<T>, dim3(2048), dim3(kRescoreThreads), 0, st, a, it);
     prof_end(WI_STAGE_RESCORE, st);
     prof_begin(WI_STAGE_CSR, st);
     hipLaunchKernelGGL(k_csr, dim3(nseg_b, BG), dim3(kCsrThreads), clds, st, a);

@@ -871,15 +871,6 @@ __device__ __forceinline__ double canonical_score_row_unrolled(const double* qd,
   return acc;
 }
 
-// A zero the compiler cannot see through: indexing the query's LDS copy with it per row keeps
-// the 128 query values from being hoisted out of a loop over rows (they would not fit in
-// registers and would be spilled to scratch memory).
-__device__ __forceinline__ int opaque_zero() {
-  int z = 0;
-  asm volatile("" : "+v"(z));
-  return z;
-}
-
 // Pointers into LDS (address space 3) and global memory (1) for the parameters of an out-of-line
 // function: through plain pointers its accesses would be flat ones, which wait for every memory
 // operation in flight.

@@ -76,6 +76,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A zero the compiler cannot see through.  Indexing an LDS array of loop-invariant values with it
+// inside a loop keeps the compiler from hoisting all of those values into registers ahead of the
+// loop (they would not fit and would be spilled to scratch memory).
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
 // ------------------------------------------------------------------ wave / block reductions
 // Lane exchanges inside a DPP row of 16 lanes (VALU operand modifiers, no LDS traffic):
 // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
