@@ -139,7 +139,8 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.tiles_g = (int)ceil_div(p.C, kScoreTile);
   // estimation workgroups per KV group: about kEstTarget in all, each over whole score tiles
   const int64_t est_target = L.BH > 256 ? kEstTargetMany : kEstTarget;
-  L.est_blocks_g = (int)std::max<int64_t>(std::min<int64_t>(L.tiles_g, ceil_div(est_target, L.BG)), p.C > 0 ? 1 : 0);
+  L.est_blocks_g = (int)std::max<int64_t>(
+      std::min<int64_t>({L.tiles_g, ceil_div(est_target, L.BG), ceil_div(p.C, kEstMinClusters)}), p.C > 0 ? 1 : 0);
   // Attention workgroups per query head: Sc fold the retrieved clusters' estimation terms (64
   // each); S split the head's exact tokens (steady zone + retrieved clusters, estimated from
   // the mean cluster size).  S fills about one resident wave of the grid (kAttTarget in all)

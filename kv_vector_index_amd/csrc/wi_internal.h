@@ -16,6 +16,8 @@ constexpr int kScoreTile = 128;     // clusters per workgroup of the score kerne
 constexpr int kEstTarget = 224;     // estimation workgroups a decode aims for: the CUs the select's
                                     // B*Hq workgroups leave free at batch 1 (256 - 32), or, when
 constexpr int kEstTargetMany = 512; // the select fills every CU, two workgroups per CU after it
+constexpr int kEstMinClusters = 512; // clusters an estimation workgroup streams at least (fewer,
+                                     // longer workgroups leave the merge fewer partials)
 constexpr int kTileTop = 8;         // best scores per head the score kernel keeps of each tile
 constexpr int kMaxGroup = 8;        // query heads per KV head supported by the decode kernels
 constexpr int kMaxSegLen = 65536;   // tokens per k-means segment
@@ -27,7 +29,7 @@ constexpr int kMaxDecodeClusters = kSelectBitmapLds / 8 * 32;   // C per KV head
 constexpr int kBoundedMaxTopK = 2048;    // clusters the bounded select ranks in LDS
 constexpr int kWbBlock = 16;        // rows per wave-buffer block
 constexpr int64_t kWbMaxPoolRows = (int64_t)1 << 29;   // rows a wave-buffer pool may hold
-constexpr int kAttTarget = 1024;    // attention workgroups one wave of the grid holds (4 per CU)
+constexpr int kAttTarget = 768;     // attention workgroups a batch-1 step aims for (3 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
