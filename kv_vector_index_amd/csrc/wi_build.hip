@@ -221,15 +221,6 @@ template <> struct AssignCfg<float> { static constexpr int kChunk = 256, kStride
 template <typename T> constexpr int assign_threads() { return 64 * AssignCfg<T>::kWaves; }
 constexpr int64_t kAssignBlocksTarget = 256;       // one block per CU
 
-// a.lo * b.lo + a.hi * b.hi + c for packed bfloat16 pairs: both products are exact in fp32, the
-// sums round as fp32 additions.  Emitted directly: the compiler's builtin for this instruction
-// picks the wrong 32-bit pieces of a 128-bit register here.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
-
 // Running state of one key over the 4-centroid groups seen so far: the largest and second-largest
 // group maximum of the fp32 scores, and the group holding the largest.  Every centroid outside
 // the best group scores at most b2; the best group's own four scores are recomputed at the end.
@@ -506,30 +497,57 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
 }
 
 // ============================================================================ k_rescore
-// The keys the assignment could not certify, one per workgroup at a time: the key row is staged in
-// LDS in fp64, each thread forms the canonical scores of its centroids (c = t, t + 256, ...), every
-// one with its row's loads issued at once and the 128 exact products added in ascending
-// coordinate order, and a block argmax (ties to the lower id) names the cluster.
-constexpr int kRescoreThreads = 256;
+// The keys the assignment could not certify, one per workgroup at a time: each thread forms the
+// canonical scores of its centroids (c = t, t + 512, ...) with the 128 exact products added in
+// ascending coordinate order, and a block argmax (ties to the lower id) names the cluster.  The
+// dependent memory round trips are few: the list count and the workgroup's first entry are read
+// together, then the key row (staged in LDS in fp64) and the first centroid row of every thread
+// are requested together.
+constexpr int kRescoreThreads = 512;
 
 template <typename T>
 __global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it) {
 #pragma clang fp contract(off)
+  constexpr int NW = kRescoreThreads / 64;
+  constexpr int kPer = 16 / (int)sizeof(T);            // elements per 16-byte piece
+  constexpr int kBatches = kD / (16 * kPer);            // 16-piece batches per row: 1 (bf16), 2 (fp32)
   __shared__ double kx[kD];
-  __shared__ double rb[kRescoreThreads / 64];
-  __shared__ int rj[kRescoreThreads / 64];
+  __shared__ double rb[NW];
+  __shared__ int rj[NW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t cap = (uint32_t)a.BG * (uint32_t)a.Nc;  // list slots (one per clustered token)
+  uint32_t e = blockIdx.x;
   const uint32_t n = a.flag_cnt[it];
-  constexpr int kPer = 16 / (int)sizeof(T);           // elements per 16-byte piece
-  for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
-    const int packed = a.flag_list[e];
+  int packed = a.flag_list[min(e, cap - 1u)];           // read beside the count; used only if e < n
+  while (e < n) {
     const int bg = packed / a.Nc, ci = packed - bg * a.Nc;
     const int s = ci / a.L;
     const int cs_eff = min(a.Cs, seg_len_of(a, s));
     const T* krow = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + ci) * kD;
-    if (tid < kD) kx[tid] = (double)St<T>::f(krow[tid]);
-    __syncthreads();
     const T* mh = static_cast<const T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
+    // the key's 16-byte pieces (threads < kD / kPer) and the first batch of this thread's first
+    // centroid row (clamped into the segment's rows; unused past cs_eff) go out together
+    u32x4_t kpc = {0u, 0u, 0u, 0u};
+    if (tid < kD / kPer) kpc = reinterpret_cast<const u32x4_t*>(krow)[tid];
+    u32x4_t r[16];
+    {
+      const u32x4_t* crow = reinterpret_cast<const u32x4_t*>(mh + (size_t)min(tid, cs_eff - 1) * kD);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = crow[i];
+    }
+    if (tid < kD / kPer) {
+      const uint32_t wd[4] = {kpc.x, kpc.y, kpc.z, kpc.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (sizeof(T) == 2) {
+          kx[tid * kPer + 2 * q] = (double)__uint_as_float(wd[q] << 16);
+          kx[tid * kPer + 2 * q + 1] = (double)__uint_as_float(wd[q] & 0xffff0000u);
+        } else {
+          kx[tid * kPer + q] = (double)__uint_as_float(wd[q]);
+        }
+      }
+    }
+    __syncthreads();
     double best = -INFINITY;
     int bj = 0x7fffffff;
     for (int j = tid; j < cs_eff; j += kRescoreThreads) {
@@ -537,10 +555,11 @@ __global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it
       const double* kq = kx + opaque_zero();          // the key's values re-read per centroid
       double acc = 0.0;
 #pragma unroll
-      for (int h = 0; h < kD / (16 * kPer); ++h) {     // batches of 16 pieces: 1 (bf16) or 2 (fp32)
-        u32x4_t r[16];
+      for (int h = 0; h < kBatches; ++h) {
+        if (j != tid || h > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = crow[h * 16 + i];
+          for (int i = 0; i < 16; ++i) r[i] = crow[h * 16 + i];
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t wd[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
@@ -571,10 +590,12 @@ __global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it
     if (lane == 0) { rb[w] = best; rj[w] = bj; }
     __syncthreads();
     if (tid == 0) {
-      for (int i = 1; i < kRescoreThreads / 64; ++i)
+      for (int i = 1; i < NW; ++i)
         if (rb[i] > best || (rb[i] == best && rj[i] < bj)) { best = rb[i]; bj = rj[i]; }
       a.assign[(size_t)bg * a.Nc + ci] = bj;
     }
+    e += gridDim.x;
+    if (e < n) packed = a.flag_list[e];
     __syncthreads();
   }
 }

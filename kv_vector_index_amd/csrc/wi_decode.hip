@@ -272,13 +272,27 @@ template <> struct Oct<float> {
   }
 };
 
+// Passes of value-sum rows in flight per estimation wave.  Deeper rings (6, 8) measured slower:
+// the extra requests in flight lengthen the memory round trips of the select workgroups that
+// share the launch more than they speed up the stream.
+constexpr int kEstRing = 4;
+
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <typename T, int NT>
 __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2][kD] */,
                           float* sh /* >= 4 + 4 (NT / 64) floats */) {
   // lane (lr = lane & 15, lg = lane >> 4) of wave wv holds dims [8 lr, 8 lr + 8) of row
-  // p0 + 4 wv + lg of each pass, NBUF passes in flight: 64 KB per 1024-thread workgroup in bf16
+  // p0 + 4 wv + lg of each pass, NBUF passes in flight (16 KB each per 1024-thread workgroup in bf16)
   // (the select kernel runs one such workgroup per CU, or two of 512 threads)
-  constexpr int NW = NT / 64, PASS = NW * 4, NBUF = 4;
+  constexpr int NW = NT / 64, PASS = NW * 4, NBUF = kEstRing;
   constexpr uint32_t kRow = kD * sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int E = a.est_blocks_g, tiles = a.tiles_g;
@@ -293,24 +307,9 @@ __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2
   const __amdgpu_buffer_rsrc_t r_sz = byte_range(a.sizes + (size_t)bg * C + c0, (uint32_t)n * 4u);
   const size_t slot = (size_t)bg * E + e;
   for (int h0 = 0; h0 < G; h0 += 4) {
-    // m of each head of the chunk: the largest of its tiles' best scores (key 0: no cluster)
-    if (wv < 4) {
-      float mx = -INFINITY;
-      if (h0 + wv < G) {
-        const uint32_t* tt = a.tile_top + ((size_t)b * a.Hq + (size_t)g * G + h0 + wv) * tiles * kTileTop;
-        for (int t = t0 + lane; t < t1; t += 64) {
-          const uint32_t k = tt[(size_t)t * kTileTop];
-          if (k != 0u) mx = fmaxf(mx, f32_from_order_key(k) * a.scale);
-        }
-      }
-      mx = wave_max(mx);
-      if (lane == 0) sh[wv] = mx;
-    }
-    __syncthreads();
     // Lane lr < 4 of a row group also weighs the row for head h0 + lr (the other lanes copy its
     // weight), so that a lane holds one score key per row.
     const int hl = lr & 3;
-    const float m_own = sh[hl];
     const bool head_live = h0 + hl < G;
     const uint32_t vo_sv = (uint32_t)(4 * wv + lg) * kRow + 8u * sizeof(T) * lr;
     const uint32_t vo_key = ((uint32_t)min(h0 + hl, G - 1) * (uint32_t)C + (uint32_t)c0 + (uint32_t)(4 * wv + lg)) * 4u;
@@ -323,6 +322,26 @@ __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2
       kk[buf] = __builtin_amdgcn_raw_buffer_load_b32(r_key, vo_key, p0 * 4, 0);
       nn[buf] = (float)(int)__builtin_amdgcn_raw_buffer_load_b32(r_sz, vo_sz, p0 * 4, 0);
     };
+    // m of each head of the chunk: the largest of its tiles' best scores (key 0: no cluster).
+    // The first tile maxima are requested before the ring's first passes, which need no m and
+    // are in flight while m is formed.
+    const uint32_t* tt = a.tile_top + ((size_t)b * a.Hq + (size_t)g * G + h0 + (wv & 3)) * tiles * kTileTop;
+    const bool m_lane = wv < 4 && h0 + wv < G;
+    const uint32_t k_first = (m_lane && t0 + lane < t1) ? tt[(size_t)(t0 + lane) * kTileTop] : 0u;
+    static_for<0, NBUF - 1>([&](auto i) { issue(i, i * PASS); });
+    if (wv < 4) {
+      float mx = (k_first != 0u) ? f32_from_order_key(k_first) * a.scale : -INFINITY;
+      if (m_lane) {
+        for (int t = t0 + lane + 64; t < t1; t += 64) {
+          const uint32_t k = tt[(size_t)t * kTileTop];
+          if (k != 0u) mx = fmaxf(mx, f32_from_order_key(k) * a.scale);
+        }
+      }
+      mx = wave_max(mx);
+      if (lane == 0) sh[wv] = mx;
+    }
+    __syncthreads();
+    const float m_own = sh[hl];
     float acc[4][8], den = 0.f;
 #pragma unroll
     for (int h = 0; h < 4; ++h)
@@ -344,24 +363,15 @@ __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2
       }
       __builtin_amdgcn_sched_barrier(0);     // keep each pass's weights from being hoisted into the last
     };
-    // a ring of NBUF passes: the loads of pass p + 3 are issued before pass p is folded; passes
-    // past the range read zeros (no memory access) and are weighted 0
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    using B2 = std::integral_constant<int, 2>;
-    using B3 = std::integral_constant<int, 3>;
-    issue(B0{}, 0);
-    issue(B1{}, PASS);
-    issue(B2{}, 2 * PASS);
-    for (int p0 = 0; p0 < n; p0 += 4 * PASS) {
-      issue(B3{}, p0 + 3 * PASS);
-      consume(B0{}, p0);
-      issue(B0{}, p0 + 4 * PASS);
-      consume(B1{}, p0 + PASS);
-      issue(B1{}, p0 + 5 * PASS);
-      consume(B2{}, p0 + 2 * PASS);
-      issue(B2{}, p0 + 6 * PASS);
-      consume(B3{}, p0 + 3 * PASS);
+    // a ring of NBUF passes (the first NBUF - 1 issued above): the loads of pass p + NBUF - 1 are
+    // issued before pass p is folded; passes past the range read zeros (no memory access) and
+    // are weighted 0
+    for (int p0 = 0; p0 < n; p0 += NBUF * PASS) {
+      static_for<0, NBUF>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        issue(std::integral_constant<int, (I + NBUF - 1) % NBUF>{}, p0 + (I + NBUF - 1) * PASS);
+        consume(i, p0 + i * PASS);
+      });
     }
     // den of head h0 + h: the lanes lr = h of the row groups; the numerators over the four row
     // groups of a wave (lane shuffles), then over the waves through LDS, two heads a round

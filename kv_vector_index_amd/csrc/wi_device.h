@@ -56,6 +56,15 @@ template <> struct St<uint16_t> {
 };
 
 // fp32 -> uint32 whose unsigned order is the float order (-NaN < -Inf < ... < +Inf < +NaN).
+// a.lo * b.lo + a.hi * b.hi + c for packed bfloat16 pairs: both products are exact in fp32, the
+// sums round as fp32 additions.  Emitted directly: the compiler's builtin for this instruction
+// picks the wrong 32-bit pieces of a 128-bit register.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
