@@ -291,7 +291,9 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   Best2 tk[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) { tk[kt].b1 = -INFINITY; tk[kt].b2 = -INFINITY; tk[kt].grp = 0; }
-  // key (lane & 15) of tile kt; lane group lg holds dims 32 lg .. 32 lg + 31
+  // key (lane & 15) of tile kt.  bf16: matrix step st takes dims 32 st + 8 lg .. +8 of keys and
+  // centroids, so that one load reads 64 contiguous bytes of each of 16 key rows; fp32: lane
+  // group lg holds dims 32 lg .. 32 lg + 31
   constexpr int KE = sizeof(T) == 2 ? 4 : 32;      // bf16: 4 x 8 elements; fp32: 32 elements
   typedef typename std::conditional<sizeof(T) == 2, bf16x8_t, float>::type KElem;
   KElem kb[4][KE];
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     const int i = min(key0 + w * 64 + kt * 16 + lr, n_s - 1);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kb[kt][st] = *reinterpret_cast<const bf16x8_t*>(K + (size_t)i * kD + 32 * lg + 8 * st);
+      for (int st = 0; st < 4; ++st) kb[kt][st] = *reinterpret_cast<const bf16x8_t*>(K + (size_t)i * kD + 32 * st + 8 * lg);
     } else {
 #pragma unroll
       for (int st = 0; st < 32; st += 8) {
@@ -328,12 +330,12 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
       f32x4_t acc[4];
       if constexpr (sizeof(T) == 2) {
         // one 32-dim slice of the 16 centroid rows at a time, against the four key tiles
-        const unsigned char* rp = clds + (ct * 16 + lr) * STR + 64 * lg;
+        const unsigned char* rp = clds + (ct * 16 + lr) * STR + 16 * lg;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const bf16x8_t ca = *reinterpret_cast<const bf16x8_t*>(rp + 16 * st);
+          const bf16x8_t ca = *reinterpret_cast<const bf16x8_t*>(rp + 64 * st);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca, kb[kt][st], acc[kt], 0, 0, 0);
         }
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * lg + 16 * st);
+        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(clds + c * STR + 64 * st + 16 * lg);
         const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
         acc = dot2_bf16(cv.x, kw.x, acc);
         acc = dot2_bf16(cv.y, kw.y, acc);
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * lg + 8 * st);
+        const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(mh + (size_t)c * kD + 32 * st + 8 * lg);
         const u32x4_t kw = __builtin_bit_cast(u32x4_t, kb[kt][st]);
         acc = dot2_bf16(cv.x, kw.x, acc);
         acc = dot2_bf16(cv.y, kw.y, acc);
@@ -444,11 +446,11 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
       // (after the merges every lane of key lr holds its group)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const unsigned char* rp = clds + min(4 * grp + r, cs_eff - 1) * STR + 64 * lg;
+        const unsigned char* rp = clds + min(4 * grp + r, cs_eff - 1) * STR + 16 * lg;
         f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 4; ++st)
-          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(rp + 16 * st), kb[kt][st], dd, 0, 0, 0);
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(rp + 64 * st), kb[kt][st], dd, 0, 0, 0);
         p[r] = 4 * grp + r < cs_eff ? diag_of(dd) : -INFINITY;
       }
     } else {
