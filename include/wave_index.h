@@ -318,9 +318,9 @@ wi_status wi_wavebuf_destroy(wi_wavebuf *wb);
 
 /* Stages timed by the profiling hook below (one entry per kernel the entry points launch). */
 typedef enum {
-  WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA) and the estimation over all
-                             non-empty clusters                                              */
-  WI_STAGE_SELECT = 1,    /* decode: per-head top-k and the per-group work lists            */
+  WI_STAGE_SCORE = 0,     /* decode: query-centroid scores (MFMA), per-tile summaries       */
+  WI_STAGE_SELECT = 1,    /* decode: per-head top-k and retrieval lists, and beside them the
+                             estimation over all non-empty clusters                          */
   WI_STAGE_ATTEND = 2,    /* decode: exact attention over steady + retrieved rows and the
                              retrieved clusters' estimation terms                            */
   WI_STAGE_MERGE = 3,     /* decode: log-sum-exp merge into out and lse                      */
