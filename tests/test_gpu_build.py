@@ -80,6 +80,28 @@ def test_build_parity_duplicate_keys_force_ties():
     _assert_index_equal(index_to_numpy(gi), ref)
 
 
+def test_build_parity_more_uncertain_keys_than_rescore_workgroups():
+    # 3000 copies of one key in a 4096-key segment: the seeded init picks several of them, whose
+    # clusters share one direction, so every copy ties between them in every iteration and goes
+    # to the fp64 re-decision -- more keys than the 2048 workgroups of that launch, so that its
+    # workgroups take several list entries each.  The lower cluster id must win every tie.
+    dev = device()
+    w = synth.Workload("b", 1, 1, 1, 128, 4096 + 12, "bf16", 16, 4, 8, 4096, 64, 3, 4)
+    K, V, _ = synth.make_instance(w, 8)
+    K[0, 0, 4:3004] = K[0, 0, 2000]
+    state = oracle.segment_state(13, 0, 0, 0)
+    seeds = oracle.init_rows(4096, 64, state)
+    assert sum(1 for r in seeds if r < 3000) >= 2      # tied centroids exist from the start
+    Kt, Vt = synth.cast(K, "bf16", dev), synth.cast(V, "bf16", dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 13)
+    torch.cuda.synchronize()
+    ref = oracle.build_index(synth.as_float64(Kt), synth.as_float64(Vt), w.sink, w.window,
+                             w.seg_len, w.clusters_per_seg, w.iters, 13, "bf16")
+    got = index_to_numpy(gi)
+    _assert_index_equal(got, ref)
+    assert int(got["sizes"].max()) >= 3000
+
+
 def test_build_steady_only():
     w = synth.Workload("b", 1, 2, 2, 128, 40, "f32", 8, 16, 32, 64, 8, 2, 1)
     gi, ref, _, _ = _build_both(w, 3, 1)
