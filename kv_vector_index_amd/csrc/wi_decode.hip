@@ -45,10 +45,14 @@ __device__ __forceinline__ int head_of_block(const DecodeArgs& a, int j) {
 }
 
 // ============================================================================ k_score
-// grid (ceil(C/128), B*Hkv), 256 threads.  Every global load is coalesced: a centroid row (256 B
-// in bf16) is read as four 64-byte pieces by four lanes in one instruction.  Four waves per SIMD
-// where the tile's registers fit in 128 VGPRs without spilling (bf16, up to four heads per
-// group); otherwise the compiler's choice.
+// grid (ceil(C/128), B*Hkv), 256 threads.  bf16: each wave copies its 32 centroid rows from HBM
+// into LDS with direct global-to-LDS loads, one kilobyte (four whole rows) per instruction, and
+// reads them back in the MFMA operand layout; a row's sixteen 16-byte pieces are stored rotated
+// by an XOR with the row index, so that the 16 lanes of a read phase hit 16 different bank
+// groups.  fp32: a centroid row (512 B) is read straight into the operand registers, as eight
+// 64-byte pieces of 16 rows per instruction.  Four waves per SIMD where the tile's registers fit
+// in 128 VGPRs without spilling (bf16, up to four heads per group); otherwise the compiler's
+// choice.
 template <typename T, int G> struct ScoreWaves { static constexpr int v = (sizeof(T) == 2 && G <= 4) ? 4 : 1; };
 
 template <typename T, int G>
@@ -56,6 +60,9 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   __shared__ float sh_n[kScoreThreads];     // cluster sizes (entries >= nrows are 0)
   __shared__ float sh_nrm[kScoreTile];      // centroid norms
   __shared__ uint32_t sh_k[G][kScoreTile];  // order keys of the raw scores
+  // bf16: the tile's centroid rows, 16 pieces of 16 B per row, piece c of row r at r * 16 +
+  // (c ^ (r & 15))
+  __shared__ __attribute__((aligned(16))) u32x4_t sh_mu[sizeof(T) == 2 ? kScoreTile * 16 : 1];
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int C = a.C;
@@ -91,16 +98,30 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
     // dims 32 s + 8 lg .. +8 on both operands, so the four lanes of a row read 64 contiguous bytes.
     bf16x8_t qa[4];
     bf16x8_t mb[2][4];
+    // load i of the wave copies rows 4 i .. 4 i + 3 of its 32 (clamped into the group's rows):
+    // lane L reads piece (L & 15) ^ (r & 15) of row r = 4 i + (L >> 4), which lands in LDS slot
+    // L of the load's 64
+    u32x4_t* wrows = sh_mu + w * 32 * 16;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const T* row = mu + (size_t)min(cbase + 16 * t + lr, C - 1) * kD + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(row + 32 * s));
+    for (int i = 0; i < 8; ++i) {
+      const int rl = 4 * i + (lane >> 4);                 // row within the wave's 32
+      const int r = min(cbase + rl, C - 1);
+      const int c = (lane & 15) ^ (rl & 15);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4_t*>(mu + (size_t)r * kD) + c,
+                                       (__attribute__((address_space(3))) void*)(wrows + 64 * i), 16, 0, 0);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qa[s] = *reinterpret_cast<const bf16x8_t*>(qg + (size_t)min(lr, G - 1) * kD + 32 * s + 8 * lg);
-    __builtin_amdgcn_sched_barrier(0);      // every load is in flight before the first wait
+    // the wave's own rows have landed in LDS (no other wave reads them)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int rl = 16 * t + lr;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_bit_cast(bf16x8_t, wrows[rl * 16 + ((4 * s + lg) ^ (rl & 15))]);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
