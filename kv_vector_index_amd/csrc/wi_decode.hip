@@ -2154,10 +2154,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
 }
 
 // ============================================================================ k_merge
-// Block size of the merge: 512 threads, or 1024 when every head has a CU to itself and has more
-// partials than 512 threads fetch in one round.  Each thread keeps kMergeU numerator columns in
-// flight (12 fits either size without spills).
-constexpr int kMergeThreadsFew = 1024, kMergeThreadsMany = 512;
+// Block size of the merge: 256 threads (fewer waves to synchronise than 512, which measured
+// slower, and 128 would need a second round of loads at 1M tokens), or 1024 when every head has a
+// CU to itself and has more partials than 256 threads fetch in one round.  Each thread keeps
+// kMergeU numerator columns in flight (12 fits either size without spills).
+constexpr int kMergeThreadsFew = 1024, kMergeThreadsMany = 256;
 constexpr int kMergeLds = 8192;
 constexpr int kMergeU = 12;
 
