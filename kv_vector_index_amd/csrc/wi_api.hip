@@ -138,7 +138,7 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   L.W32 = (int)ceil_div(p.C, 32);
   L.tiles_g = (int)ceil_div(p.C, kScoreTile);
   // estimation workgroups per KV group: about kEstTarget in all, each over whole score tiles
-  const int64_t est_target = L.BH > 256 ? kEstTargetMany : kEstTarget;
+  const int64_t est_target = select_half_blocks(L.BH, p.C) ? kEstTargetMany : kEstTarget;
   L.est_blocks_g = (int)std::max<int64_t>(
       std::min<int64_t>({L.tiles_g, ceil_div(est_target, L.BG), ceil_div(p.C, kEstMinClusters)}), p.C > 0 ? 1 : 0);
   // Attention workgroups per query head: Sc fold the retrieved clusters' estimation terms (64

@@ -439,8 +439,8 @@ __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2
 }
 
 // ============================================================================ k_select
-// Block size of the select: 1024 threads while every head has a CU to itself, 512 beyond that
-// (two heads per CU then run at once).
+// Block size of the select: 512 threads beyond 256 heads (two heads per CU then run at once) or
+// when two blocks fit one CU's LDS (select_half_blocks), otherwise 1024.
 constexpr int kSelThreadsFew = 1024, kSelThreadsMany = 512;
 constexpr int kSelHeadsPerRound = 256;
 constexpr int kSmallBand = 64;      // bands up to one wave are resolved by direct ranking
@@ -2301,7 +2301,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
 
 // ============================================================================ launcher
 // the select: one workgroup per query head, followed by the estimation workgroups (none for a
-// refresh, which only selects); half-size blocks beyond kSelHeadsPerRound heads; the gated,
+// refresh, which only selects); half-size blocks where select_half_blocks says so; the gated,
 // refresh and bounded modes in their own instantiation, so that the plain decode's kernel
 // carries none of their code
 template <typename T>
@@ -2310,7 +2310,7 @@ static void launch_select(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)BH + (a.refresh ? 0u : (unsigned)(a.B * a.Hkv) * (unsigned)a.est_blocks_g);
   const bool ext = a.gated || a.refresh || a.bounded;
   const size_t lds = (size_t)a.W32 * 8;
-  if (BH > kSelHeadsPerRound) {
+  if (select_half_blocks(BH, a.C)) {
     if (ext) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 1>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
     else hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 0>), dim3(grid), dim3(kSelThreadsMany), lds, s, a);
     if (a.bounded) hipLaunchKernelGGL((k_select<T, kSelThreadsMany, 2>), dim3(BH), dim3(kSelThreadsMany), lds, s, a);

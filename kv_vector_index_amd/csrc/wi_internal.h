@@ -14,8 +14,8 @@ namespace wi {
 
 constexpr int kScoreTile = 128;     // clusters per workgroup of the score kernel
 constexpr int kEstTarget = 224;     // estimation workgroups a decode aims for: the CUs the select's
-                                    // B*Hq workgroups leave free at batch 1 (256 - 32), or, when
-constexpr int kEstTargetMany = 512; // the select fills every CU, two workgroups per CU after it
+                                    // 1024-thread workgroups leave free at batch 1 (256 - 32), or,
+constexpr int kEstTargetMany = 512; // with 512-thread select blocks, two workgroups per CU
 constexpr int kEstMinClusters = 512; // clusters an estimation workgroup streams at least (fewer,
                                      // longer workgroups leave the merge fewer partials)
 constexpr int kTileTop = 8;         // best scores per head the score kernel keeps of each tile
@@ -32,6 +32,13 @@ constexpr int64_t kWbMaxPoolRows = (int64_t)1 << 29;   // rows a wave-buffer poo
 constexpr int kAttTarget = 768;     // attention workgroups a batch-1 step aims for (3 per CU)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The select launch runs 512-thread workgroups beyond 256 query heads (two heads a CU), and also
+// at fewer heads when two of its workgroups fit one CU's LDS (the static arrays and the
+// bitmaps over at most 16384 clusters): smaller blocks synchronise faster (128K tokens, batch 1:
+// select 12.1 -> 10.6 us).  With more clusters a workgroup needs most of a CU's LDS, and the
+// 1024-thread form streams the estimation faster (1M tokens: 30.9 against 41.3 us).
+inline bool select_half_blocks(int BH, int C) { return BH > 256 || C <= 16384; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ decode workspace
