@@ -144,11 +144,13 @@ DecodeLayout decode_layout(const wi_decode_params& p) {
   // Attention workgroups per query head: Sc fold the retrieved clusters' estimation terms (64
   // each); S split the head's exact tokens (steady zone + retrieved clusters, estimated from
   // the mean cluster size).  S fills about one resident wave of the grid (kAttTarget in all)
-  // but gives no workgroup fewer than 64 or, when the grid must queue anyway, 512 tokens.
+  // but gives no workgroup fewer than 64 or, when the grid must queue anyway, 336 tokens (1M
+  // tokens, batch 1: 32 token workgroups per head, four per CU; attend 34.1 us with 512-token
+  // workgroups, 32.9 us with these).
   const int Sc = p.top_k > 0 ? (int)ceil_div(p.top_k, kCorrEntries) : 0;
   const int64_t tok_est = (int64_t)p.n_steady + (p.C > 0 ? ceil_div((int64_t)p.top_k * p.Nc, p.C) : 0);
   const int64_t fill = (int64_t)kAttTarget / L.BH - Sc;
-  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(tok_est, 64), std::max<int64_t>(ceil_div(tok_est, 512), fill)));
+  L.att_split = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(tok_est, 64), std::max<int64_t>(ceil_div(tok_est, 336), fill)));
   L.att_items = L.att_split + Sc;
   const size_t BG = L.BG, BH = L.BH, C = p.C, G = L.G, K = p.top_k;
   size_t o = 0;
