@@ -446,7 +446,6 @@ __device__ void est_block(const DecodeArgs& a, int x, float* part /* [NT / 64][2
 // Block size of the select: 512 threads beyond 256 heads (two heads per CU then run at once) or
 // when two blocks fit one CU's LDS (select_half_blocks), otherwise 1024.
 constexpr int kSelThreadsFew = 1024, kSelThreadsMany = 512;
-constexpr int kSelHeadsPerRound = 256;
 constexpr int kSmallBand = 64;      // bands up to one wave are resolved by direct ranking
 constexpr int kSumCap = 4096;       // tile summaries (8 per 128-cluster tile) staged in LDS
 constexpr int kCandCap = 2048;      // candidate clusters ranked in LDS
@@ -2159,145 +2158,161 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
 }
 
 // ============================================================================ k_merge
-// Block size of the merge: 256 threads (fewer waves to synchronise than 512, which measured
-// slower, and 128 would need a second round of loads at 1M tokens), or 1024 when every head has a
-// CU to itself and has more partials than 256 threads fetch in one round.  Each thread keeps
-// kMergeU numerator columns in flight (12 fits either size without spills).
-constexpr int kMergeThreadsFew = 1024, kMergeThreadsMany = 256;
-constexpr int kMergeLds = 8192;
+// One workgroup per query head, with no block barrier (except for the bound of the bounded
+// decode): wave w takes columns [128 w / NW, 128 (w + 1) / NW) of every partial, as QPW float4
+// quads; lane (q, sl) = q + QPW sl folds quad q of partials sl, sl + SPW, sl + 2 SPW, ...  Every
+// wave reads all the (m, den) pairs itself (64 per lane round), forms the largest partial max and
+// the denominator with wave reductions, and hands each lane the merge factors of its partials by
+// lane shuffles; the slices are summed by a butterfly over the slice bits.  256 threads while
+// the first round of loads covers every partial (at most 96), else 1024.  The pairs of the first
+// kMergeMd rounds and the numerators of the first kMergeU partials per lane are requested
+// together, before anything is known; any further partials are read in later rounds.
+constexpr int kMergeThreadsFew = 256, kMergeThreadsMany = 1024;
+constexpr int kMergeMd = 4;
 constexpr int kMergeU = 12;
+template <int NT> struct MergeShape {
+  static constexpr int NW = NT / 64, QPW = 32 / NW, SPW = 64 / QPW;
+  static constexpr int kFirst = SPW * kMergeU;     // partials the first round of numerators covers
+};
 
 // out = num / den, lse = M + log(den) with M the largest partial max, den = sum_p s_p f_p den_p,
 // num = sum_p s_p f_p num_p, f_p = exp(m_p - M): estimation tiles (s = +1), exact splits (+1),
 // retrieved-cluster corrections (s = -1).  A head that retrieved every non-empty cluster takes
-// only its exact splits.  The first batch of numerators is fetched before the maximum is known.
+// only its exact splits.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_merge(DecodeArgs a) {
-  constexpr int kMergeMdU = NT >= 1024 ? 1 : 2;   // md pairs per thread loaded in the first round
-  __shared__ float sh_f[kMergeLds];
-  __shared__ float sh_red[32];
-  __shared__ float4 sh_acc[NT / 32][32];
-  const int tid = threadIdx.x;
+  using SH = MergeShape<NT>;
+  constexpr int NW = SH::NW, QPW = SH::QPW, SPW = SH::SPW;
+  __shared__ float sh_red[2 * NW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sl = lane / QPW, quad = w * QPW + (lane - sl * QPW);
   const int bh = head_of_block(a, blockIdx.x);
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int G = a.G, g = h / G, hi = h - g * G, bg = b * a.Hkv + g;
-  // Partials in order: PE estimation tiles, S token workgroups, PC correction workgroups.  All
-  // of them are loaded at once, before the head's all-retrieved flag is known; when it is set
-  // the estimation and correction partials are dead (not used, whatever they hold).
+  // partials in order: PE estimation tiles, S token workgroups, PC correction workgroups; when
+  // the head's all-retrieved flag is set the estimation and correction partials are dead (not
+  // used, whatever they hold)
   const int all_sel = a.all_sel[bh];
   const int PE = a.est_blocks_g;
   const int S = a.att_split, items = a.att_items;
   const int P = PE + items;
-  auto md_of = [&](int p) -> const float* {
-    if (p < PE) return a.est_md + (((size_t)bg * a.est_blocks_g + p) * G + hi) * 2;
-    return a.att_md + ((size_t)bh * items + (p - PE)) * 2;
+  auto md_of = [&](int p) -> const float2* {
+    if (p < PE) return reinterpret_cast<const float2*>(a.est_md + (((size_t)bg * a.est_blocks_g + p) * G + hi) * 2);
+    return reinterpret_cast<const float2*>(a.att_md + ((size_t)bh * items + (p - PE)) * 2);
   };
-  const int col = tid & 31, rep = tid >> 5;
-  constexpr int RP = NT / 32;
-  // numerator columns [4 col, 4 col + 4) of partial p; past P the last partial is read and unused
-  const float* est_col = a.est_num + ((size_t)bg * a.est_blocks_g * G + hi) * kD + 4 * col;
-  const float* att_col = a.att_num + (size_t)bh * items * kD + 4 * col;
+  const float* est_col = a.est_num + ((size_t)bg * a.est_blocks_g * G + hi) * kD + 4 * quad;
+  const float* att_col = a.att_num + (size_t)bh * items * kD + 4 * quad;
+  // quad of partial p; past P the last partial is read and unused
   auto num_col = [&](int p) -> float4 {
     p = min(p, P - 1);
     const float* q = p < PE ? est_col + (size_t)p * G * kD : att_col + (size_t)(p - PE) * kD;
     return *reinterpret_cast<const float4*>(q);
   };
+  float2 md[kMergeMd];
+#pragma unroll
+  for (int u = 0; u < kMergeMd; ++u) md[u] = *md_of(min(lane + 64 * u, P - 1));
   float4 v[kMergeU];
 #pragma unroll
-  for (int u = 0; u < kMergeU; ++u) v[u] = num_col(rep + u * RP);
-  float2 md[kMergeMdU];
-#pragma unroll
-  for (int u = 0; u < kMergeMdU; ++u) md[u] = *reinterpret_cast<const float2*>(md_of(min(tid + u * NT, P - 1)));
+  for (int j = 0; j < kMergeU; ++j) v[j] = num_col(sl + SPW * j);
   const bool use_est = all_sel == 0;
   auto live = [&](int p, float den) { return den > 0.f && (use_est || (p >= PE && p < PE + S)); };
   float mx = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < kMergeMdU; ++u) {
-    const int p = tid + u * NT;
+  for (int u = 0; u < kMergeMd; ++u) {
+    const int p = lane + 64 * u;
     if (p < PE + S && live(p, md[u].y)) mx = fmaxf(mx, md[u].x);
   }
-  for (int p = tid + kMergeMdU * NT; p < PE + S; p += NT) {
-    const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
+  for (int p = lane + 64 * kMergeMd; p < PE + S; p += 64) {
+    const float2 m2 = *md_of(p);
     if (live(p, m2.y)) mx = fmaxf(mx, m2.x);
   }
-  const float M = block_max<NT>(mx, sh_red);
+  const float M = wave_max(mx);
   // merge factor of a live partial, negated for the corrections; 0 for a dead one
   auto factor_of = [&](int p, float2 m2) -> float {
     if (!live(p, m2.y)) return 0.f;
     const float f = __expf(m2.x - M);
     return p >= PE + S ? -f : f;
   };
-  const bool f_lds = P <= kMergeLds;
-  float dn = 0.f;
+  float f[kMergeMd];
+  float dn = 0.f, dx = 0.f;                      // dx: the exact partials (bounded decode)
 #pragma unroll
-  for (int u = 0; u < kMergeMdU; ++u) {
-    const int p = tid + u * NT;
-    if (p < P) {
-      const float f = factor_of(p, md[u]);
-      if (f_lds) sh_f[p] = f;
-      if (f != 0.f) dn += f * md[u].y;
+  for (int u = 0; u < kMergeMd; ++u) {
+    const int p = lane + 64 * u;
+    f[u] = p < P ? factor_of(p, md[u]) : 0.f;
+    if (f[u] != 0.f) {
+      dn += f[u] * md[u].y;
+      if (p >= PE && p < PE + S) dx += f[u] * md[u].y;
     }
   }
-  for (int p = tid + kMergeMdU * NT; p < P; p += NT) {
-    const float2 m2 = *reinterpret_cast<const float2*>(md_of(p));
-    const float f = factor_of(p, m2);
-    if (f_lds) sh_f[p] = f;
-    if (f != 0.f) dn += f * m2.y;
+  for (int p = lane + 64 * kMergeMd; p < P; p += 64) {
+    const float2 m2 = *md_of(p);
+    const float fp = factor_of(p, m2);
+    if (fp != 0.f) {
+      dn += fp * m2.y;
+      if (p >= PE && p < PE + S) dx += fp * m2.y;
+    }
   }
-  const float den = block_sum<NT>(dn, sh_red);
-  __syncthreads();
-  auto factor = [&](int p) -> float {
-    if (f_lds) return sh_f[p];
-    return factor_of(p, *reinterpret_cast<const float2*>(md_of(p)));
-  };
+  const float den = wave_sum(dn);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fold = [&](float fp, const float4& x) {
+    if (fp != 0.f) { acc.x += fp * x.x; acc.y += fp * x.y; acc.z += fp * x.z; acc.w += fp * x.w; }
+  };
+  // the first round: partial p = sl + SPW j takes its factor from lane p mod 64 of round p / 64
+  // (the same round for every lane of the wave, since SPW divides 64)
 #pragma unroll
-  for (int u = 0; u < kMergeU; ++u) {
-    const int p = rep + u * RP;
-    if (p < P) {
-      const float f = factor(p);
-      if (f != 0.f) { acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w; }
+  for (int j = 0; j < kMergeU; ++j) {
+    const int p = sl + SPW * j;
+    const int u = (SPW * j) >> 6;
+    float fp;
+    if (u < kMergeMd) {
+      float fu = f[0];
+#pragma unroll
+      for (int uu = 1; uu < kMergeMd; ++uu) if (uu == u) fu = f[uu];
+      fp = __shfl(fu, p & 63);
+    } else {
+      fp = p < P ? factor_of(p, *md_of(p)) : 0.f;
+    }
+    if (p < P) fold(fp, v[j]);
+  }
+  // any further partials, kMergeU per lane a round, their factors recomputed from their pairs
+  for (int p0 = SPW * kMergeU; p0 < P; p0 += SPW * kMergeU) {
+#pragma unroll
+    for (int j = 0; j < kMergeU; ++j) v[j] = num_col(p0 + sl + SPW * j);
+#pragma unroll
+    for (int j = 0; j < kMergeU; ++j) {
+      const int p = p0 + sl + SPW * j;
+      if (p < P) fold(factor_of(p, *md_of(p)), v[j]);
     }
   }
-  for (int p0 = rep + kMergeU * RP; p0 < P; p0 += kMergeU * RP) {
+  // sum over the slices (lanes q + QPW sl, sl = 0 .. SPW - 1)
 #pragma unroll
-    for (int u = 0; u < kMergeU; ++u) v[u] = num_col(p0 + u * RP);
-#pragma unroll
-    for (int u = 0; u < kMergeU; ++u) {
-      const int p = p0 + u * RP;
-      if (p < P) {
-        const float f = factor(p);
-        if (f != 0.f) { acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w; }
-      }
-    }
+  for (int m = QPW; m < 64; m <<= 1) {
+    acc.x += __shfl_xor(acc.x, m); acc.y += __shfl_xor(acc.y, m);
+    acc.z += __shfl_xor(acc.z, m); acc.w += __shfl_xor(acc.w, m);
   }
-  sh_acc[rep][col] = acc;
-  __syncthreads();
   float o2 = 0.f;
-  if (tid < 32) {
-    float4 s = sh_acc[0][tid];
-    for (int r = 1; r < RP; ++r) {
-      const float4 t = sh_acc[r][tid];
-      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-    }
-    const float4 o = make_float4(s.x / den, s.y / den, s.z / den, s.w / den);
-    *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * tid) = o;
+  if (sl == 0) {
+    const float4 o = make_float4(acc.x / den, acc.y / den, acc.z / den, acc.w / den);
+    *reinterpret_cast<float4*>(a.out + (size_t)bh * kD + 4 * quad) = o;
     o2 = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
   }
   if (tid == 0 && a.lse) a.lse[bh] = M + __logf(den);
   if (a.bounded) {
     // error bound of the output: (sum a (V_c + |o|) + w u V_c) / (D_x + sum lo) over the estimated
     // clusters, their sums taken by the select in the frame m*, D_x = the exact partials' total
-    float dx = 0.f;
-    for (int p = PE + tid; p < PE + S; p += NT) dx += factor(p) * md_of(p)[1];
-    const float Dx = block_sum<NT>(dx, sh_red);
-    const float on = sqrtf(block_sum<NT>(o2, sh_red));
+    const float Dx = wave_sum(dx);
+    const float ow = wave_sum(o2);
+    if (lane == 0) sh_red[w] = ow;
+    __syncthreads();
     if (tid == 0 && a.err_bound) {
+      float on2 = 0.f;
+      for (int i = 0; i < NW; ++i) on2 += sh_red[i];
+      const float on = sqrtf(on2);
       const float* bd = a.bnd + (size_t)bh * 4;
       float e = 0.f;
       if (bd[1] != 0.f || bd[2] != 0.f || bd[3] != 0.f) {
-        const float f = __expf(bd[0] - M);
-        e = (bd[2] + on * bd[1]) * f / (Dx + bd[3] * f);
+        const float fb = __expf(bd[0] - M);
+        e = (bd[2] + on * bd[1]) * fb / (Dx + bd[3] * fb);
       }
       a.err_bound[bh] = e;
     }
@@ -2329,8 +2344,7 @@ static void launch_select(const DecodeArgs& a, hipStream_t s) {
 template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
-  const bool merge_big = BH <= kSelHeadsPerRound &&
-                         a.est_blocks_g + a.att_items > (kMergeThreadsMany / 32) * kMergeU;
+  const bool merge_big = a.est_blocks_g + a.att_items > MergeShape<kMergeThreadsFew>::kFirst;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
   // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent, and
@@ -2356,8 +2370,8 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
   for (int r = 0; r < prof_reps(); ++r) {
-    if (merge_big) hipLaunchKernelGGL(k_merge<kMergeThreadsFew>, dim3(BH), dim3(kMergeThreadsFew), 0, s, a);
-    else hipLaunchKernelGGL(k_merge<kMergeThreadsMany>, dim3(BH), dim3(kMergeThreadsMany), 0, s, a);
+    if (merge_big) hipLaunchKernelGGL(k_merge<kMergeThreadsMany>, dim3(BH), dim3(kMergeThreadsMany), 0, s, a);
+    else hipLaunchKernelGGL(k_merge<kMergeThreadsFew>, dim3(BH), dim3(kMergeThreadsFew), 0, s, a);
   }
   prof_end(WI_STAGE_MERGE, s);
   return hipGetLastError();
