@@ -603,77 +603,110 @@ __global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it
 }
 
 // ============================================================================ k_csr
+// One workgroup per segment, whose tokens are split into 16 contiguous ranges of whole 64-token
+// steps, one per wave.  (1) Each wave counts its range's ids into its own row of a [16][Cs] table
+// of 16-bit counts; (2) the thread owning cluster c turns column c into exclusive prefixes over
+// the waves (the tokens of id c in earlier ranges) and the total; (3) a block scan of the totals
+// gives the offsets; (4) each wave walks its range in order, 64 tokens a step: a token's slot is
+// its id's offset, plus the id's tokens before this step (its entry in the wave's table row,
+// which the first lane of each id in the step then advances), plus its rank among the equal ids
+// of the step (each lane reads the step's 64 ids back from LDS, broadcast reads that pipeline).
+// Only (1)-(3) need block barriers.  Counts fit 16 bits: a segment holds at most 65536 tokens,
+// and a prefix before a wave's range at most 15/16 of them.
 constexpr int kCsrThreads = 1024;
+constexpr int kCsrWaves = kCsrThreads / 64;
+constexpr int kCsrRegSteps = 8;     // steps of ids a lane keeps in registers from (1) to (4)
+inline size_t csr_lds_bytes(int Cs) {
+  const size_t cs2 = (size_t)((Cs + 1) & ~1);
+  return (size_t)kCsrWaves * cs2 * 2 + (size_t)Cs * 4 + (size_t)kCsrWaves * 64 * 4;
+}
 
 __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
-  extern __shared__ uint32_t csr_lds[];   // cnt[Cs], loc[Cs], run[Cs], tbl[16][Cs] (u8), keys[1024]
+  extern __shared__ uint32_t csr_lds[];   // tbl[16][Cs2] (u16), loc[Cs], ids[16][64]
   __shared__ int iscr[32];
   const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int n_s = seg_len_of(a, s);
-  const int Cs = a.Cs;
-  uint32_t* cnt = csr_lds;
-  uint32_t* loc = csr_lds + Cs;
-  uint32_t* run = csr_lds + 2 * Cs;
-  uint8_t* tbl = reinterpret_cast<uint8_t*>(csr_lds + 3 * Cs);
-  int* rkeys = reinterpret_cast<int*>(csr_lds + 3 * Cs + 4 * Cs);   // a round's keys, 64 per wave
+  const int Cs = a.Cs, Cs2 = (Cs + 1) & ~1;
+  uint16_t* tbl = reinterpret_cast<uint16_t*>(csr_lds);
+  uint32_t* loc = csr_lds + kCsrWaves * Cs2 / 2;
+  int* rkeys = reinterpret_cast<int*>(loc + Cs);
   const int32_t* asg = a.assign + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int R = (n_s + 64 * kCsrWaves - 1) / (64 * kCsrWaves) * 64;   // tokens per wave
+  const int t0 = min(n_s, w * R), t1 = min(n_s, t0 + R);
 
-  for (int j = tid; j < Cs; j += kCsrThreads) { cnt[j] = 0u; run[j] = 0u; }
+  for (int x = tid; x < kCsrWaves * Cs2 / 2; x += kCsrThreads) csr_lds[x] = 0u;
+  int kr[kCsrRegSteps];
+#pragma unroll
+  for (int u = 0; u < kCsrRegSteps; ++u) {
+    const int i = t0 + 64 * u + lane;
+    kr[u] = i < t1 ? asg[i] : -1;
+  }
   __syncthreads();
-  for (int i = tid; i < n_s; i += kCsrThreads) atomicAdd(&cnt[asg[i]], 1u);
+  // (1) the wave's counts; two 16-bit counts share a word, added to with 32-bit atomics
+  auto count = [&](int key) {
+    if (key >= 0) atomicAdd(&csr_lds[(w * Cs2 + key) >> 1], 1u << (16 * (key & 1)));
+  };
+#pragma unroll
+  for (int u = 0; u < kCsrRegSteps; ++u) count(kr[u]);
+  for (int i = t0 + 64 * kCsrRegSteps + lane; i < t1; i += 64) count(asg[i]);
   __syncthreads();
-  // exclusive scan of the counts (each thread owns a contiguous run of ids)
+  // (2) prefixes over the waves, totals (kept in loc until the scan)
   const int per = (Cs + kCsrThreads - 1) / kCsrThreads;
   const int j0 = min(Cs, tid * per), j1 = min(Cs, j0 + per);
   int my = 0;
-  for (int j = j0; j < j1; ++j) my += (int)cnt[j];
+  for (int j = j0; j < j1; ++j) {
+    int run = 0;
+    for (int ww = 0; ww < kCsrWaves; ++ww) {
+      const int x = tbl[ww * Cs2 + j];
+      tbl[ww * Cs2 + j] = (uint16_t)run;
+      run += x;
+    }
+    loc[j] = (uint32_t)run;
+    my += run;
+  }
+  // (3) offsets
   int tot;
   int ex = block_exclusive_scan<kCsrThreads>(my, iscr, &tot);
-  for (int j = j0; j < j1; ++j) { loc[j] = (uint32_t)ex; ex += (int)cnt[j]; }
-  __syncthreads();
   const int cbase = s * Cs;
-  for (int j = tid; j < Cs; j += kCsrThreads) {
-    a.sizes[(size_t)bg * a.C + cbase + j] = (int32_t)cnt[j];
-    a.offsets[(size_t)bg * (a.C + 1) + cbase + j] = s * a.L + (int32_t)loc[j];
+  for (int j = j0; j < j1; ++j) {
+    const int c = (int)loc[j];
+    a.sizes[(size_t)bg * a.C + cbase + j] = (int32_t)c;
+    a.offsets[(size_t)bg * (a.C + 1) + cbase + j] = s * a.L + ex;
+    loc[j] = (uint32_t)ex;
+    ex += c;
   }
-  // stable scatter: rounds of 1024 tokens in order; within a wave, lanes with equal ids are
-  // ranked by lane (each lane reads the wave's 64 ids back from LDS, broadcast reads that
-  // pipeline); across waves of a round by the per-wave count table; across rounds by run[].
+  __syncthreads();
+  // (4) the wave's range in order
   int32_t* perm = a.perm + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int pos0 = a.lo + s * a.L;
-  int key_next = tid < n_s ? asg[tid] : -1;          // each round's ids are loaded a round ahead
-  for (int r0 = 0; r0 < n_s; r0 += kCsrThreads) {
-    const int i = r0 + tid;
-    const bool valid = i < n_s;
-    const int key = key_next;
-    key_next = i + kCsrThreads < n_s ? asg[i + kCsrThreads] : -1;
-    for (int x = tid; x < 16 * Cs / 4; x += kCsrThreads) reinterpret_cast<uint32_t*>(tbl)[x] = 0u;
-    __syncthreads();
-    int* wk = rkeys + w * 64;
+  int* wk = rkeys + w * 64;
+  uint16_t* mine = tbl + w * Cs2;
+  auto step = [&](int i, int key) {
     wk[lane] = key;
     wave_lds_sync();
-    int rank = 0, count = 0;
+    int rank = 0, cnt = 0;
 #pragma unroll 8
     for (int j = 0; j < 64; ++j) {
       const bool eq = wk[j] == key;
       rank += (eq && j < lane) ? 1 : 0;
-      count += eq ? 1 : 0;
+      cnt += eq ? 1 : 0;
     }
-    if (valid && rank == 0) tbl[w * Cs + key] = (uint8_t)count;
-    __syncthreads();
-    if (valid) {
-      int p = (int)loc[key] + (int)run[key] + rank;
-      for (int ww = 0; ww < w; ++ww) p += tbl[ww * Cs + key];
-      perm[p] = pos0 + i;
+    int before = 0;
+    if (key >= 0) {
+      before = mine[key];
+      perm[(int)loc[key] + before + rank] = pos0 + i;
     }
-    __syncthreads();
-    for (int j = tid; j < Cs; j += kCsrThreads) {
-      uint32_t add = 0;
-      for (int ww = 0; ww < 16; ++ww) add += tbl[ww * Cs + j];
-      run[j] += add;
-    }
-    __syncthreads();
+    wave_lds_sync();
+    if (key >= 0 && rank == 0) mine[key] = (uint16_t)(before + cnt);
+    wave_lds_sync();
+  };
+#pragma unroll
+  for (int u = 0; u < kCsrRegSteps; ++u)
+    if (t0 + 64 * u < t1) step(t0 + 64 * u + lane, kr[u]);
+  for (int b0 = t0 + 64 * kCsrRegSteps; b0 < t1; b0 += 64) {
+    const int i = b0 + lane;
+    step(i, i < t1 ? asg[i] : -1);
   }
 }
 
@@ -781,7 +814,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const size_t alds = (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride;
-  const size_t clds = (size_t)a.Cs * 12 + (size_t)16 * a.Cs + (size_t)4 * kCsrThreads;
+  const size_t clds = csr_lds_bytes(a.Cs);
   // assignment blocks per segment: about one block per CU in all (each stages the segment's
   // centroids once and loops over 64-key-per-wave passes), at least one pass each
   const unsigned assign_px = (unsigned)std::max<int64_t>(1, std::min<int64_t>(
