@@ -14,8 +14,9 @@
 //               directions = rounded unit seed keys
 //   then `iters` times:
 //     k_assign  MFMA keys x centroid directions (centroids staged in LDS, keys in registers)
-//               with a fused running top-2 per key; uncertain keys go to a list
-//     k_rescore fp64 canonical argmax for the listed keys
+//               with a fused running top-2 per key; uncertain keys go to a list, which a block
+//               holding every centroid of its segment re-decides itself in fp64
+//     k_rescore fp64 canonical argmax for the listed keys (centroids not resident in LDS)
 //     k_csr     per segment: counts, offsets and a stable counting scatter -> sizes/offsets/perm
 //     k_update  (all but the last iteration) fp64 member sums -> new unit directions
 //     k_final   (last iteration) mean keys, value sums, cluster-major K/V copies
@@ -220,6 +221,12 @@ template <> struct AssignCfg<uint16_t> { static constexpr int kChunk = 512, kStr
 template <> struct AssignCfg<float> { static constexpr int kChunk = 256, kStride = 528, kWaves = 8; };
 template <typename T> constexpr int assign_threads() { return 64 * AssignCfg<T>::kWaves; }
 constexpr int64_t kAssignBlocksTarget = 256;       // one block per CU
+constexpr int kAssignListCap = 2048;   // uncertain keys a resident block re-decides from its LDS list
+constexpr int kAssignKeyWaves = 8;     // waves that re-decide one key (one centroid per thread)
+template <typename T> constexpr size_t assign_lds_bytes(bool resident) {
+  return (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride +
+         (resident ? (size_t)kAssignListCap * 4 + (size_t)(AssignCfg<T>::kWaves / kAssignKeyWaves) * kD * 8 : 0);
+}
 
 // Running state of one key over the 4-centroid groups seen so far: the largest and second-largest
 // group maximum of the fp32 scores, and the group holding the largest.  Every centroid outside
@@ -256,11 +263,17 @@ __device__ __forceinline__ void best2_merge_xor(Best2& t, int m) {
 // of the best group are recomputed, which names the best centroid; the choice is certified when
 // it leads every other centroid (the group's other three, and the second-best group maximum) by
 // more than twice the fp32 error bound, otherwise the key goes to the fp64 re-decision list.
+// With every centroid resident in LDS the block re-decides its own listed keys after its last
+// pass (no separate launch: the build's assignment steps took 1.44 + 0.13 ms in two kernels,
+// 1.51 ms in one); otherwise k_rescore takes the list.
 template <typename T, bool kResident>
 __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int it) {
   extern __shared__ __attribute__((aligned(16))) unsigned char clds[];
   constexpr int CH = AssignCfg<T>::kChunk, STR = AssignCfg<T>::kStride;
   constexpr int NT = assign_threads<T>();          // 64 keys per wave and pass
+  __shared__ int f_cnt;                            // resident: keys on the block's re-decision list
+  __shared__ double rd_best[AssignCfg<T>::kWaves];
+  __shared__ int rd_id[AssignCfg<T>::kWaves];
   const int s = a.seg0 + blockIdx.y, bg = blockIdx.z;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
@@ -280,6 +293,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     }
   };
   if constexpr (resident) {
+    if (threadIdx.x == 0) f_cnt = 0;
     stage(0, cs_eff, (cs_eff + 15) & ~15);
     __syncthreads();
   }
@@ -487,19 +501,112 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
     const uint64_t m = __ballot(flagged[kt]);
     if (m == 0) continue;
     uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&a.flag_cnt[it], (uint32_t)__popcll(m));
+    if (lane == 0) base = resident ? (uint32_t)atomicAdd(&f_cnt, __popcll(m)) : atomicAdd(&a.flag_cnt[it], (uint32_t)__popcll(m));
     base = __builtin_amdgcn_readlane(base, 0);
     if (flagged[kt]) {
       const uint32_t pos = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
       const int i = key0 + w * 64 + kt * 16 + lr;
-      a.flag_list[pos] = (int32_t)((size_t)bg * a.Nc + (size_t)s * a.L + i);
+      const size_t gi = (size_t)bg * a.Nc + (size_t)s * a.L + i;
+      if constexpr (resident) {
+        // the block's list in LDS; past its capacity the key is marked in place (-1)
+        if (pos < (uint32_t)kAssignListCap) reinterpret_cast<int*>(clds + CH * STR)[pos] = i;
+        else a.assign[gi] = -1;
+      } else {
+        a.flag_list[pos] = (int32_t)gi;
+      }
     }
   }
   }  // passes
+
+  if constexpr (resident) {
+    // The fp64 re-decision of the block's uncertain keys, against the centroids still in LDS:
+    // kAssignKeyWaves waves per key, one centroid per thread, the canonical score (exact products
+    // added in ascending coordinate order in fp64), the block argmax with ties to the lower id.
+    // Keys past the list's capacity were marked in place; the block then finds them by reading
+    // back its own keys' assignments, one pass of keys at a time.
+    int* flist = reinterpret_cast<int*>(clds + CH * STR);
+    double* fkey = reinterpret_cast<double*>(clds + CH * STR + kAssignListCap * 4);
+    constexpr int KPR = AssignCfg<T>::kWaves / kAssignKeyWaves;     // keys per round
+    const int kg = w / kAssignKeyWaves, gt = threadIdx.x - kg * kAssignKeyWaves * 64;
+    auto redecide = [&](int n_list) {
+      for (int r0 = 0; r0 < n_list; r0 += KPR) {
+        const int e = r0 + kg;
+        const int i = e < n_list ? flist[e] : -1;
+        if (i >= 0 && gt < kD) fkey[kg * kD + gt] = (double)St<T>::f(K[(size_t)i * kD + gt]);
+        __syncthreads();
+        double best = -INFINITY;
+        int bj = 0x7fffffff;
+        if (i >= 0 && gt < cs_eff) {
+#pragma clang fp contract(off)
+          const double* kq = fkey + kg * kD;
+          const unsigned char* crow = clds + gt * STR;
+          double acc = 0.0;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll 4
+            for (int q = 0; q < kD / 8; ++q) {
+              const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(crow + 16 * q);
+              const uint32_t wd[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const double p0 = kq[8 * q + 2 * h] * (double)__uint_as_float(wd[h] << 16);
+                acc = acc + p0;
+                const double p1 = kq[8 * q + 2 * h + 1] * (double)__uint_as_float(wd[h] & 0xffff0000u);
+                acc = acc + p1;
+              }
+            }
+          } else {
+#pragma unroll 4
+            for (int q = 0; q < kD / 4; ++q) {
+              const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(crow + 16 * q);
+              const uint32_t wd[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const double pp = kq[4 * q + h] * (double)__uint_as_float(wd[h]);
+                acc = acc + pp;
+              }
+            }
+          }
+          best = acc;
+          bj = gt;
+        }
+#pragma unroll
+        for (int m = 32; m > 0; m >>= 1) {
+          const double ob = __shfl_xor(best, m);
+          const int oj = __shfl_xor(bj, m);
+          if (ob > best || (ob == best && oj < bj)) { best = ob; bj = oj; }
+        }
+        if (lane == 0) { rd_best[w] = best; rd_id[w] = bj; }
+        __syncthreads();
+        if (gt == 0 && i >= 0) {
+          for (int x = 1; x < kAssignKeyWaves; ++x) {
+            const double ob = rd_best[w + x];
+            const int oj = rd_id[w + x];
+            if (ob > best || (ob == best && oj < bj)) { best = ob; bj = oj; }
+          }
+          a.assign[(size_t)bg * a.Nc + (size_t)s * a.L + i] = bj;
+        }
+        __syncthreads();                       // fkey and the partials are reused next round
+      }
+    };
+    __syncthreads();
+    const int n_flag = f_cnt;
+    redecide(min(n_flag, kAssignListCap));
+    if (n_flag > kAssignListCap) {
+      for (int key0 = blockIdx.x * NT; key0 < n_s; key0 += gridDim.x * NT) {
+        if (threadIdx.x == 0) f_cnt = 0;
+        __syncthreads();
+        const int i = key0 + (int)threadIdx.x;
+        if (i < n_s && a.assign[(size_t)bg * a.Nc + (size_t)s * a.L + i] < 0) flist[atomicAdd(&f_cnt, 1)] = i;
+        __syncthreads();
+        redecide(f_cnt);
+      }
+    }
+  }
 }
 
 // ============================================================================ k_rescore
-// The keys the assignment could not certify, one per workgroup at a time: each thread forms the
+// The keys the assignment could not certify when the centroids did not fit in LDS, one per
+// workgroup at a time: each thread forms the
 // canonical scores of its centroids (c = t, t + 512, ...) with the 128 exact products added in
 // ascending coordinate order, and a block argmax (ties to the lower id) names the cluster.  The
 // dependent memory round trips are few: the list count and the workgroup's first entry are read
@@ -813,7 +920,8 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t alds = (size_t)AssignCfg<T>::kChunk * AssignCfg<T>::kStride;
+  const bool resident = a.Cs <= AssignCfg<T>::kChunk;   // every centroid of a segment fits in LDS
+  const size_t alds = assign_lds_bytes<T>(resident);
   const size_t clds = csr_lds_bytes(a.Cs);
   // assignment blocks per segment: about one block per CU in all (each stages the segment's
   // centroids once and loops over 64-key-per-wave passes), at least one pass each
@@ -821,7 +929,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
       ceil_div(a.L, assign_threads<T>()), ceil_div(kAssignBlocksTarget, (int64_t)nseg_b * BG)));
   for (int it = 0; it < a.iters; ++it) {
     prof_begin(WI_STAGE_ASSIGN, st);
-    if (a.Cs <= AssignCfg<T>::kChunk)
+    if (resident)
       hipLaunchKernelGGL((k_assign<T, true>), dim3(assign_px, nseg_b, BG), dim3(assign_threads<T>()),
                          alds, st, a, it);
     else
@@ -829,7 +937,8 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
                          alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
     prof_begin(WI_STAGE_RESCORE, st);
-    hipLaunchKernelGGL(k_rescore<T>, dim3(2048), dim3(kRescoreThreads), 0, st, a, it);
+    if (!resident)      // a resident assignment re-decides its uncertain keys itself
+      hipLaunchKernelGGL(k_rescore<T>, dim3(2048), dim3(kRescoreThreads), 0, st, a, it);
     prof_end(WI_STAGE_RESCORE, st);
     prof_begin(WI_STAGE_CSR, st);
     hipLaunchKernelGGL(k_csr, dim3(nseg_b, BG), dim3(kCsrThreads), clds, st, a);
