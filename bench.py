@@ -289,7 +289,9 @@ def bench_build(w, args, dev):
         "roofline": {"kernel": "k_assign", "bound": "mfma", "achieved": tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None},
         "assign_rescore": {"achieved": tflops_ar, "frac": tflops_ar / peak,
-                           "note": "the assignment's algorithmic flops over the time of k_assign and k_rescore together"},
+                           "note": "the assignment's algorithmic flops over the time of k_assign and k_rescore together "
+                                   "(k_rescore runs only when a segment's centroids do not fit in LDS; "
+                                   "otherwise k_assign re-decides its uncertain keys itself)"},
         "append_segment": append,
     }
     print(json.dumps(result), flush=True)

@@ -936,10 +936,11 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((k_assign<T, false>), dim3(assign_px, nseg_b, BG), dim3(assign_threads<T>()),
                          alds, st, a, it);
     prof_end(WI_STAGE_ASSIGN, st);
-    prof_begin(WI_STAGE_RESCORE, st);
-    if (!resident)      // a resident assignment re-decides its uncertain keys itself
+    if (!resident) {    // a resident assignment re-decides its uncertain keys itself
+      prof_begin(WI_STAGE_RESCORE, st);
       hipLaunchKernelGGL(k_rescore<T>, dim3(2048), dim3(kRescoreThreads), 0, st, a, it);
-    prof_end(WI_STAGE_RESCORE, st);
+      prof_end(WI_STAGE_RESCORE, st);
+    }
     prof_begin(WI_STAGE_CSR, st);
     hipLaunchKernelGGL(k_csr, dim3(nseg_b, BG), dim3(kCsrThreads), clds, st, a);
     prof_end(WI_STAGE_CSR, st);
