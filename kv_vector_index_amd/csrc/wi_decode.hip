@@ -58,12 +58,20 @@ template <typename T, int G> struct ScoreWaves { static constexpr int v = (sizeo
 
 template <typename T, int G>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(ScoreWaves<T, G>::v))) void k_score(DecodeArgs a) {
-  __shared__ float sh_n[kScoreThreads];     // cluster sizes (entries >= nrows are 0)
-  __shared__ float sh_nrm[kScoreTile];      // centroid norms
-  __shared__ uint32_t sh_k[G][kScoreTile];  // order keys of the raw scores
-  // bf16: the tile's centroid rows, 16 pieces of 16 B per row, piece c of row r at r * 16 +
-  // (c ^ (r & 15))
-  __shared__ __attribute__((aligned(16))) u32x4_t sh_mu[sizeof(T) == 2 ? kScoreTile * 16 : 1];
+  constexpr bool kBf = sizeof(T) == 2;
+  // fp32: per cluster of the tile its size (0 past nrows), its centroid's norm and the order keys
+  // of its raw scores.  bf16: the tile's centroid rows, 16 pieces of 16 B per row, piece c of row
+  // r at r * 16 + (c ^ (r & 15)); once a wave holds its 32 rows in registers, the same three
+  // per-cluster values of its clusters go into the first 1280 bytes of its 8 KB of rows, so that
+  // a workgroup needs 32 KB of LDS and five fit one CU.
+  __shared__ float sh_n[kBf ? 1 : kScoreThreads];
+  __shared__ float sh_nrm[kBf ? 1 : kScoreTile];
+  __shared__ uint32_t sh_k[kBf ? 1 : G][kBf ? 1 : kScoreTile];
+  __shared__ __attribute__((aligned(16))) u32x4_t sh_mu[kBf ? kScoreTile * 16 : 1];
+  auto wreg = [&](int c) -> uint32_t* { return reinterpret_cast<uint32_t*>(sh_mu + (c >> 5) * 32 * 16); };
+  auto key_at = [&](int h, int c) -> uint32_t& { if constexpr (kBf) return wreg(c)[h * 32 + (c & 31)]; else return sh_k[h][c]; };
+  auto nrm_at = [&](int c) -> float& { if constexpr (kBf) return reinterpret_cast<float*>(wreg(c))[256 + (c & 31)]; else return sh_nrm[c]; };
+  auto n_at = [&](int c) -> float& { if constexpr (kBf) return reinterpret_cast<float*>(wreg(c))[288 + (c & 31)]; else return sh_n[c]; };
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int C = a.C;
@@ -81,7 +89,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   // into the group) so that the wait before the first MFMA counts only the loads issued ahead
   // of it; query rows past the group are never read back.  Empty clusters are masked by their
   // size in the per-head pass.
-  const int n_raw = szs[tile * kScoreTile + min(tid, nrows - 1)];
+  // the size of cluster ncl: bf16, lane l < 32 of wave w takes cluster 32 w + l (its wave's own
+  // clusters); fp32, thread t takes cluster t
+  const int ncl = kBf ? w * 32 + (lane & 31) : tid;
+  const int n_raw = szs[tile * kScoreTile + min(ncl, nrows - 1)];
   // raw score of query head h (row h of the MFMA tile) against cluster row cl, and the norm of
   // that centroid
   auto put_scores = [&](const f32x4_t& acc, float n2, int t) {
@@ -89,9 +100,9 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
-      if (h < G) sh_k[h][cl] = f32_order_key(acc[r]);
+      if (h < G) key_at(h, cl) = f32_order_key(acc[r]);
     }
-    if (lg == 0) sh_nrm[cl] = sqrtf(n2);
+    if (lg == 0) nrm_at(cl) = sqrtf(n2);
   };
 
   if constexpr (sizeof(T) == 2) {
@@ -123,6 +134,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
 #pragma unroll
       for (int s = 0; s < 4; ++s) mb[t][s] = __builtin_bit_cast(bf16x8_t, wrows[rl * 16 + ((4 * s + lg) ^ (rl & 15))]);
     }
+    // every row is in registers before the wave writes its per-cluster values over them
+    __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -174,14 +187,14 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
       put_scores(acc, n2, t);
     }
   }
-  sh_n[tid] = tid < nrows ? (float)n_raw : 0.f;
+  if (!kBf || lane < 32) n_at(ncl) = ncl < nrows ? (float)n_raw : 0.f;
   __syncthreads();
 
   const size_t slot = (size_t)bg * a.tiles_g + tile;
   if (w == 0) {
     // largest norm among the tile's non-empty centroids, and how many are non-empty
-    const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
-    const float nm = wave_max(fmaxf(e0 ? sh_nrm[lane] : 0.f, e1 ? sh_nrm[lane + 64] : 0.f));
+    const bool e0 = n_at(lane) > 0.f, e1 = n_at(lane + 64) > 0.f;
+    const float nm = wave_max(fmaxf(e0 ? nrm_at(lane) : 0.f, e1 ? nrm_at(lane + 64) : 0.f));
     const int nc = __popcll(__ballot(e0)) + __popcll(__ballot(e1));
     if (lane == 0) { a.tile_norm[slot] = nm; a.tile_cnt[slot] = nc; }
   }
@@ -189,8 +202,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(S
   // (key 0 past the non-empty clusters) with their cluster ids: lane r keeps the r-th, found by
   // repeated wave maxima, each time clearing the holder with the lowest id
   for (int h = w; h < G; h += kScoreThreads / 64) {
-    const bool e0 = sh_n[lane] > 0.f, e1 = sh_n[lane + 64] > 0.f;
-    const uint32_t k0 = e0 ? sh_k[h][lane] : 0u, k1 = e1 ? sh_k[h][lane + 64] : 0u;
+    const bool e0 = n_at(lane) > 0.f, e1 = n_at(lane + 64) > 0.f;
+    const uint32_t k0 = e0 ? key_at(h, lane) : 0u, k1 = e1 ? key_at(h, lane + 64) : 0u;
     uint32_t* keys_h = a.keys + ((size_t)b * a.Hq + (size_t)g * G + h) * C + (size_t)tile * kScoreTile;
     if (lane < nrows) keys_h[lane] = k0;
     if (lane + 64 < nrows) keys_h[lane + 64] = k1;
