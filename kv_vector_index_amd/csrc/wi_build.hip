@@ -716,8 +716,9 @@ __global__ __launch_bounds__(kRescoreThreads) void k_rescore(BuildArgs a, int it
 // the waves (the tokens of id c in earlier ranges) and the total; (3) a block scan of the totals
 // gives the offsets; (4) each wave walks its range in order, 64 tokens a step: a token's slot is
 // its id's offset, plus the id's tokens before this step (its entry in the wave's table row,
-// which the first lane of each id in the step then advances), plus its rank among the equal ids
-// of the step (each lane reads the step's 64 ids back from LDS, broadcast reads that pipeline).
+// which every lane then advances with an LDS atomic, so that the entry read back gives the id's
+// count in the step), plus its rank among the equal ids of the step (0 for an id that occurs
+// once; one ballot for each id that occurs more than once).
 // Only (1)-(3) need block barriers.  Counts fit 16 bits: a segment holds at most 65536 tokens,
 // and a prefix before a wave's range at most 15/16 of them.
 constexpr int kCsrThreads = 1024;
@@ -725,18 +726,17 @@ constexpr int kCsrWaves = kCsrThreads / 64;
 constexpr int kCsrRegSteps = 8;     // steps of ids a lane keeps in registers from (1) to (4)
 inline size_t csr_lds_bytes(int Cs) {
   const size_t cs2 = (size_t)((Cs + 1) & ~1);
-  return (size_t)kCsrWaves * cs2 * 2 + (size_t)Cs * 4 + (size_t)kCsrWaves * 64 * 4;
+  return (size_t)kCsrWaves * cs2 * 2 + (size_t)Cs * 4;
 }
 
 __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
-  extern __shared__ uint32_t csr_lds[];   // tbl[16][Cs2] (u16), loc[Cs], ids[16][64]
+  extern __shared__ uint32_t csr_lds[];   // tbl[16][Cs2] (u16), loc[Cs]
   __shared__ int iscr[32];
   const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int n_s = seg_len_of(a, s);
   const int Cs = a.Cs, Cs2 = (Cs + 1) & ~1;
   uint16_t* tbl = reinterpret_cast<uint16_t*>(csr_lds);
   uint32_t* loc = csr_lds + kCsrWaves * Cs2 / 2;
-  int* rkeys = reinterpret_cast<int*>(loc + Cs);
   const int32_t* asg = a.assign + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = (n_s + 64 * kCsrWaves - 1) / (64 * kCsrWaves) * 64;   // tokens per wave
@@ -787,26 +787,27 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
   // (4) the wave's range in order
   int32_t* perm = a.perm + (size_t)bg * a.Nc + (size_t)s * a.L;
   const int pos0 = a.lo + s * a.L;
-  int* wk = rkeys + w * 64;
   uint16_t* mine = tbl + w * Cs2;
   auto step = [&](int i, int key) {
-    wk[lane] = key;
+    const bool v = key >= 0;
+    const int before = v ? (int)mine[key] : 0;
+    wave_lds_sync();                  // every lane has read its id's count before any is added to
+    if (v) atomicAdd(&csr_lds[(w * Cs2 + key) >> 1], 1u << (16 * (key & 1)));
     wave_lds_sync();
-    int rank = 0, cnt = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) {
-      const bool eq = wk[j] == key;
-      rank += (eq && j < lane) ? 1 : 0;
-      cnt += eq ? 1 : 0;
+    // the step's tokens of this id (16-bit difference: the count reaches 65536 only at the last
+    // step of a segment that is one cluster), and the rank among them in lane order, found by one
+    // ballot per id that occurs more than once
+    const int cnt = v ? (int)(uint16_t)(mine[key] - (uint16_t)before) : 0;
+    int rank = 0;
+    uint64_t dup = __ballot(cnt > 1);
+    while (dup != 0ull) {
+      const int l = __ffsll((unsigned long long)dup) - 1;
+      const int k = __builtin_amdgcn_readlane(key, l);
+      const uint64_t m = __ballot(key == k);
+      if (key == k) rank = __popcll(m & ((1ull << lane) - 1ull));
+      dup &= ~m;
     }
-    int before = 0;
-    if (key >= 0) {
-      before = mine[key];
-      perm[(int)loc[key] + before + rank] = pos0 + i;
-    }
-    wave_lds_sync();
-    if (key >= 0 && rank == 0) mine[key] = (uint16_t)(before + cnt);
-    wave_lds_sync();
+    if (v) perm[(int)loc[key] + before + rank] = pos0 + i;
   };
 #pragma unroll
   for (int u = 0; u < kCsrRegSteps; ++u)
