@@ -820,7 +820,8 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr(BuildArgs a) {
 
 // ============================================================================ k_update / k_final
 // One wave per cluster; lane owns dims 2*lane, 2*lane+1.  Members are summed in fp64 in
-// ascending position (the CSR order), 16 rows fetched ahead of the sums.
+// ascending position (the CSR order), 16 rows fetched ahead of the sums; the positions of 64
+// members come in one load.
 template <typename T, bool kFinal>
 __global__ __launch_bounds__(512) void k_sums(BuildArgs a) {
   __shared__ double buf[8][kD];
@@ -849,14 +850,14 @@ __global__ __launch_bounds__(512) void k_sums(BuildArgs a) {
   T* kp = static_cast<T*>(a.kp) + (size_t)bg * a.Nc * kD;
   T* vp = static_cast<T*>(a.vp) + (size_t)bg * a.Nc * kD;
   double k0 = 0.0, k1 = 0.0, v0 = 0.0, v1 = 0.0;
+  int p = 0;                          // member positions, 64 at a time (one per lane)
   for (int m0 = 0; m0 < n; m0 += 16) {
     const int cnt = min(16, n - m0);
-    int p = 0;
-    if (lane < cnt) p = perm[start + m0 + lane];
+    if ((m0 & 63) == 0 && m0 + lane < n) p = perm[start + m0 + lane];
     T kx[16][2], vx[16][2];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int pos = __shfl(p, u);
+      const int pos = __shfl(p, (m0 & 63) + u);
       if (u < cnt) {
         kx[u][0] = K[(size_t)pos * kD + 2 * lane];
         kx[u][1] = K[(size_t)pos * kD + 2 * lane + 1];
