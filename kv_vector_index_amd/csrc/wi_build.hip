@@ -490,7 +490,8 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   if constexpr (resident) {
     // The fp64 re-decision of the block's uncertain keys, against the centroids still in LDS:
     // kAssignKeyWaves waves per key, one centroid per thread, the canonical score (exact products
-    // added in ascending coordinate order in fp64), the block argmax with ties to the lower id.
+    // added in ascending coordinate order in fp64: a fused multiply-add of an exact product rounds
+    // as the addition does), the block argmax with ties to the lower id.
     // Keys past the list's capacity were marked in place; the block then finds them by reading
     // back its own keys' assignments, one pass of keys at a time.
     int* flist = reinterpret_cast<int*>(clds + CH * STR);
@@ -517,10 +518,8 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
               const uint32_t wd[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
               for (int h = 0; h < 4; ++h) {
-                const double p0 = kq[8 * q + 2 * h] * (double)__uint_as_float(wd[h] << 16);
-                acc = acc + p0;
-                const double p1 = kq[8 * q + 2 * h + 1] * (double)__uint_as_float(wd[h] & 0xffff0000u);
-                acc = acc + p1;
+                acc = __builtin_fma(kq[8 * q + 2 * h], (double)__uint_as_float(wd[h] << 16), acc);
+                acc = __builtin_fma(kq[8 * q + 2 * h + 1], (double)__uint_as_float(wd[h] & 0xffff0000u), acc);
               }
             }
           } else {
@@ -529,10 +528,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
               const u32x4_t cv = *reinterpret_cast<const u32x4_t*>(crow + 16 * q);
               const uint32_t wd[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-              for (int h = 0; h < 4; ++h) {
-                const double pp = kq[4 * q + h] * (double)__uint_as_float(wd[h]);
-                acc = acc + pp;
-              }
+              for (int h = 0; h < 4; ++h) acc = __builtin_fma(kq[4 * q + h], (double)__uint_as_float(wd[h]), acc);
             }
           }
           best = acc;
