@@ -83,8 +83,8 @@ def test_build_parity_duplicate_keys_force_ties():
 def test_build_parity_more_uncertain_keys_than_rescore_workgroups():
     # 3000 copies of one key in a 4096-key segment: the seeded init picks several of them, whose
     # clusters share one direction, so every copy ties between them in every iteration and goes
-    # to the fp64 re-decision -- more keys than the 2048 workgroups of that launch, so that its
-    # workgroups take several list entries each.  The lower cluster id must win every tie.
+    # to the fp64 re-decision (about 750 keys for each of the segment's four assignment blocks).
+    # The lower cluster id must win every tie.
     dev = device()
     w = synth.Workload("b", 1, 1, 1, 128, 4096 + 12, "bf16", 16, 4, 8, 4096, 64, 3, 4)
     K, V, _ = synth.make_instance(w, 8)
@@ -100,6 +100,28 @@ def test_build_parity_more_uncertain_keys_than_rescore_workgroups():
     got = index_to_numpy(gi)
     _assert_index_equal(got, ref)
     assert int(got["sizes"].max()) >= 3000
+
+
+def test_build_parity_uncertain_keys_past_the_block_list():
+    # 8 KV heads x 16 segments of 8192 tokens: two assignment blocks per segment, each over 4096
+    # keys.  8000 copies of one key in head 0's first segment, among which the init picks 15 of
+    # the 16 seeds: every copy ties in every iteration, so each of that segment's blocks has about
+    # 4000 keys to re-decide, more than its 2048-entry LDS list holds; the rest are marked in place
+    # and found again by the block.
+    dev = device()
+    w = synth.Workload("b", 1, 8, 8, 128, 16 * 8192 + 12, "bf16", 16, 4, 8, 8192, 16, 2, 4)
+    K, V, _ = synth.make_instance(w, 9)
+    K[0, 0, 4:8004] = K[0, 0, 3000]
+    seeds = oracle.init_rows(8192, 16, oracle.segment_state(13, 0, 0, 0))
+    assert sum(1 for r in seeds if r < 8000) >= 2
+    Kt, Vt = synth.cast(K, "bf16", dev), synth.cast(V, "bf16", dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 13)
+    torch.cuda.synchronize()
+    ref = oracle.build_index(synth.as_float64(Kt), synth.as_float64(Vt), w.sink, w.window,
+                             w.seg_len, w.clusters_per_seg, w.iters, 13, "bf16")
+    got = index_to_numpy(gi)
+    _assert_index_equal(got, ref)
+    assert int(got["sizes"].max()) >= 8000
 
 
 def test_build_steady_only():

@@ -47,6 +47,15 @@ def test_decode_parity_top_k_range(top_k):
     _run(_small(B=1, Hq=8), seed=3, top_k=top_k)
 
 
+@pytest.mark.parametrize("top_k", [1000, 3000])
+def test_decode_many_partials_per_head(top_k):
+    # one query head per KV group over 60 000 tokens (59 segments x 48 = 2832 clusters): with this
+    # many retrieved tokens a head gets 354 (top 1000) or 390 (all) partials, past the merge's
+    # 256 (m, den) pairs held in registers and, for 390, past its first round of numerators
+    w = synth.Workload("many", 1, 2, 2, 128, 60000, "bf16", 40, 4, 32, 1024, 48, 3, top_k)
+    _run(w, seed=17)
+
+
 def test_decode_sharpened_queries_bf16():
     # a query scale of 12 concentrates attention (max logit ~ 12) so that the 1e-2 gate bites
     _run(_small(q_scale=12.0, q_noise=0.5), seed=4)
