@@ -124,6 +124,23 @@ def test_build_parity_uncertain_keys_past_the_block_list():
     assert int(got["sizes"].max()) >= 8000
 
 
+def test_build_parity_one_cluster_holds_a_whole_65536_token_segment():
+    # every key of a segment of the largest supported length is the same: all 65536 tokens go to
+    # cluster 0 (ties to the lower id), the largest count the CSR's 16-bit per-wave tables reach
+    dev = device()
+    w = synth.Workload("b", 1, 1, 1, 128, 65536 + 12, "bf16", 4, 4, 8, 65536, 4, 2, 1)
+    K, V, _ = synth.make_instance(w, 3)
+    K[0, 0, :] = K[0, 0, 100]
+    Kt, Vt = synth.cast(K, "bf16", dev), synth.cast(V, "bf16", dev)
+    gi = wi.build_index(Kt, Vt, w.sink, w.window, w.seg_len, w.clusters_per_seg, w.iters, 2)
+    torch.cuda.synchronize()
+    ref = oracle.build_index(synth.as_float64(Kt), synth.as_float64(Vt), w.sink, w.window,
+                             w.seg_len, w.clusters_per_seg, w.iters, 2, "bf16")
+    got = index_to_numpy(gi)
+    _assert_index_equal(got, ref)
+    assert int(got["sizes"].max()) == 65536
+
+
 def test_build_steady_only():
     w = synth.Workload("b", 1, 2, 2, 128, 40, "f32", 8, 16, 32, 64, 8, 2, 1)
     gi, ref, _, _ = _build_both(w, 3, 1)
