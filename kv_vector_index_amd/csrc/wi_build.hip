@@ -90,27 +90,54 @@ __device__ __forceinline__ uint64_t segment_state0(uint64_t seed, int b, int g, 
 }
 
 constexpr int kInitThreads = 512;
+// hash slots of the seed search: a power of two, at least twice the clusters of a segment
+inline __host__ __device__ int init_hash_slots(int cs) {
+  int h = 2;
+  while (h < 2 * cs) h <<= 1;
+  return h;
+}
 
 // The seed rows of one segment's clusters, one cluster per thread.  The partial Fisher-Yates
 // shuffle swaps position r with j_r >= r for r = 0, 1, ..., and cluster r takes the row that ends
 // at position r.  That row is the one at position j_r just before step r: the row an earlier step
 // r' < r moved there (the last with j_r' = j_r; it brought the row then at position r'), else j_r
 // itself.  So each cluster follows that chain back through the draws, with no sequential pass
-// over the swaps.  Then the thread loads its seed row whole, sums its squares in fp64 in ascending
+// over the swaps; the draws equal to a position are found through an open-addressing hash table
+// of draw indices keyed by their draw (in LDS, at most half full), not by scanning the earlier
+// draws.  Then the thread loads its seed row whole, sums its squares in fp64 in ascending
 // coordinate order and stores round(x / ||x||) (a zero row for a zero norm).
 template <typename T>
 __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
-  extern __shared__ uint32_t init_lds[];      // draws j_r [Cs]
+  extern __shared__ uint32_t init_lds[];      // draws j_r [Cs], hash slots [init_hash_slots(Cs)]
   const int s = a.seg0 + blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
   uint32_t* draw = init_lds;
+  int* slot = reinterpret_cast<int*>(init_lds + a.Cs);
+  const int HS = init_hash_slots(a.Cs), hshift = 32 - __builtin_ctz((unsigned)HS);
+  auto hash = [&](uint32_t v) -> int { return hshift >= 32 ? 0 : (int)((v * 0x9E3779B1u) >> hshift); };
+  for (int i = threadIdx.x; i < HS; i += kInitThreads) slot[i] = -1;
   const uint64_t st0 = segment_state0(a.seed, b, g, s);
   // the draws do not depend on the shuffle state: j_r = r + (x_r mod (n_s - r))
   for (int r = threadIdx.x; r < cs_eff; r += kInitThreads)
     draw[r] = (uint32_t)r + (uint32_t)(splitmix64_nth(st0, (uint64_t)r) % (uint64_t)(n_s - r));
   __syncthreads();
+  for (int r = threadIdx.x; r < cs_eff; r += kInitThreads) {
+    int h = hash(draw[r]);
+    while (atomicCAS(&slot[h], -1, r) != -1) h = (h + 1) & (HS - 1);
+  }
+  __syncthreads();
+  // the largest draw index x < t with draw x equal to v, or -1 (the probe ends at an empty slot)
+  auto last_draw_before = [&](uint32_t v, int t) -> int {
+    int best = -1;
+    for (int h = hash(v);; h = (h + 1) & (HS - 1)) {
+      const int x = slot[h];
+      if (x < 0) break;
+      if (draw[x] == v && x < t && x > best) best = x;
+    }
+    return best;
+  };
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
   T* mh = static_cast<T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
   constexpr int kPer = 16 / (int)sizeof(T);          // elements per 16-byte piece
@@ -124,9 +151,7 @@ __global__ __launch_bounds__(kInitThreads) void k_init(BuildArgs a) {
     }
     int p = (int)draw[j], t = j;
     for (;;) {
-      int q = -1;
-      for (int x = t - 1; x >= 0; --x)
-        if ((int)draw[x] == p) { q = x; break; }
+      const int q = last_draw_before((uint32_t)p, t);
       if (q < 0) break;
       p = q;
       t = q;
@@ -955,7 +980,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   if (a.Nc == 0 || a.seg0 >= a.nseg) return hipSuccess;
   const int nseg_b = a.nseg - a.seg0;        // segments built by this call
   {
-    const size_t lds = (size_t)a.Cs * 4;
+    const size_t lds = (size_t)a.Cs * 4 + (size_t)init_hash_slots(a.Cs) * 4;
     prof_begin(WI_STAGE_INIT, st);
     hipLaunchKernelGGL(k_init<T>, dim3(nseg_b, BG), dim3(kInitThreads), lds, st, a);
     prof_end(WI_STAGE_INIT, st);
