@@ -271,7 +271,7 @@ __global__ __launch_bounds__(assign_threads<T>()) void k_assign(BuildArgs a, int
   const int s = a.seg0 + blockIdx.y, bg = blockIdx.z;
   const int n_s = seg_len_of(a, s);
   const int cs_eff = min(a.Cs, n_s);
-  if (blockIdx.x * NT >= n_s) return;
+  if ((int)blockIdx.x * NT >= n_s) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
   const T* K = static_cast<const T*>(a.k) + ((size_t)bg * a.N + a.lo + (size_t)s * a.L) * kD;
   const T* mh = static_cast<const T*>(a.mhat) + ((size_t)bg * a.C + (size_t)s * a.Cs) * kD;
