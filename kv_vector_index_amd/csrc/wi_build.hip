@@ -9,7 +9,7 @@
 // -> bf16 with round-to-nearest-even.
 //
 // Kernels (one stream, in order):
-//   k_prep      steady-zone copies, fp32 key norms for the error band, counter reset
+//   k_prep      steady-zone copies, re-decision counter reset
 //   k_init      per segment: SplitMix64-driven partial Fisher-Yates picks the seed rows;
 //               directions = rounded unit seed keys
 //   then `iters` times:
