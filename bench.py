@@ -328,7 +328,7 @@ def main():
                          "that every k-means kernel launched covers the whole context")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would hold its "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would hold its "
               "own sequences and KV heads with no communication); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -23,7 +23,7 @@ the sequence [RI-es 3, "Clustering Segmentado"; RI-ar 2.a, last paragraph].  The
 for a cluster of n_c tokens with mean key mu_c and value sum SV_c is n_c * exp(<q, mu_c>/sqrt(d))
 * (SV_c / n_c) in the numerator and n_c * exp(<q, mu_c>/sqrt(d)) in the denominator, and the zone
 results are merged with log-sum-exp.  Everything the pages leave open is a "reading", marked R<n>
-below and listed in DESIGN.md.
+below where the code takes it.
 
 Parity pins (tests/test_oracle.py), per function:
   round_to_dtype ........ pinned: torch's float->bfloat16 conversion on random and edge values
