@@ -2180,11 +2180,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(DecodeArgs a) {
 // quads; lane (q, sl) = q + QPW sl folds quad q of partials sl, sl + SPW, sl + 2 SPW, ...  Every
 // wave reads all the (m, den) pairs itself (64 per lane round), forms the largest partial max and
 // the denominator with wave reductions, and hands each lane the merge factors of its partials by
-// lane shuffles; the slices are summed by a butterfly over the slice bits.  256 threads while
-// the first round of loads covers every partial (at most 96), else 1024.  The pairs of the first
-// kMergeMd rounds and the numerators of the first kMergeU partials per lane are requested
-// together, before anything is known; any further partials are read in later rounds.
-constexpr int kMergeThreadsFew = 256, kMergeThreadsMany = 1024;
+// lane shuffles; the slices are summed by a butterfly over the slice bits.  The smallest of 128
+// and 256 threads whose first round of loads covers every partial (at most 48 or 96), else 1024
+// (128K tokens, batch 1, 43 partials per head: 4.28 us with 256 threads, 4.11 with 128).  The
+// pairs of the first kMergeMd rounds and the numerators of the first kMergeU partials per lane
+// are requested together, before anything is known; any further partials are read in later
+// rounds.
+constexpr int kMergeThreadsSmall = 128, kMergeThreadsFew = 256, kMergeThreadsMany = 1024;
 constexpr int kMergeMd = 4;
 constexpr int kMergeU = 12;
 template <int NT> struct MergeShape {
@@ -2361,7 +2363,9 @@ static void launch_select(const DecodeArgs& a, hipStream_t s) {
 template <typename T, int G>
 static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
-  const bool merge_big = a.est_blocks_g + a.att_items > MergeShape<kMergeThreadsFew>::kFirst;
+  const int merge_parts = a.est_blocks_g + a.att_items;
+  const int merge_nt = merge_parts <= MergeShape<kMergeThreadsSmall>::kFirst ? kMergeThreadsSmall
+                     : merge_parts <= MergeShape<kMergeThreadsFew>::kFirst ? kMergeThreadsFew : kMergeThreadsMany;
   hipError_t e;
   prof_begin(WI_STAGE_SCORE, s);
   // (while profiling with repeats, every kernel runs prof_reps() times: each is idempotent, and
@@ -2387,8 +2391,9 @@ static hipError_t launch_groups(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(WI_STAGE_MERGE, s);
   for (int r = 0; r < prof_reps(); ++r) {
-    if (merge_big) hipLaunchKernelGGL(k_merge<kMergeThreadsMany>, dim3(BH), dim3(kMergeThreadsMany), 0, s, a);
-    else hipLaunchKernelGGL(k_merge<kMergeThreadsFew>, dim3(BH), dim3(kMergeThreadsFew), 0, s, a);
+    if (merge_nt == kMergeThreadsSmall) hipLaunchKernelGGL(k_merge<kMergeThreadsSmall>, dim3(BH), dim3(kMergeThreadsSmall), 0, s, a);
+    else if (merge_nt == kMergeThreadsFew) hipLaunchKernelGGL(k_merge<kMergeThreadsFew>, dim3(BH), dim3(kMergeThreadsFew), 0, s, a);
+    else hipLaunchKernelGGL(k_merge<kMergeThreadsMany>, dim3(BH), dim3(kMergeThreadsMany), 0, s, a);
   }
   prof_end(WI_STAGE_MERGE, s);
   return hipGetLastError();
